@@ -1,0 +1,190 @@
+/*
+ * oscar.h - C ABI of the OSCAR split-cache INT2 decode path on MI355X (gfx950).
+ *
+ * The method (pages: the m.th-motor.com repost of the OSCAR authors' article,
+ * the arddev.tech summary "OSCAR 2bit KV cache", and the snilld.dk post on
+ * OSCAR making 2-bit KV cache practical):
+ *   - the first 64 tokens (attention sinks) and the last 256 tokens (recent
+ *     window) of each sequence stay in BF16 (thmotor: split-cache paragraph;
+ *     arddev: analytics section and the launch flags in "how to apply today");
+ *   - the long middle history is stored rotated by R = U . Hadamard .
+ *     bit-reversal and quantised to INT2 per group of channels with a bf16
+ *     scale and zero point and a clipping ratio, four 2-bit codes per byte
+ *     (thmotor: rotation formula after Fig. 1; split-cache paragraph);
+ *   - each decode step the oldest recent token is rotated, clipped, quantised,
+ *     packed and demoted into the history (thmotor: split-cache paragraph);
+ *   - decode attends the BF16 segment and the INT2 segment separately and merges
+ *     them with an online-softmax merge (thmotor: decode-stage sentence of the
+ *     split-cache paragraph).
+ *
+ * Conventions
+ *   - Pointers are DEVICE pointers unless marked [host].  bf16 values are passed
+ *     as their uint16_t bit patterns.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronises; all work is enqueued on `stream` (a hipStream_t passed as
+ *     void*; NULL = the null stream).  Buffers must stay valid until the stream
+ *     has executed the work.
+ *   - Every call validates its arguments on the host before any HIP call.  On
+ *     failure it returns a negative oscar_status, enqueues nothing, leaves all
+ *     outputs untouched and records a message readable by oscar_last_error().
+ *     A failed kernel launch returns OSCAR_EHIP.  Device-side faults surface at
+ *     the caller's next synchronisation (HIP semantics).
+ *   - Calls are re-entrant; the only library state is a thread-local error
+ *     string.  Calls that write the same cache records from several streams
+ *     concurrently race.
+ *
+ * Cache layout (HBM)
+ *   INT2 history pool: uint8 [num_int2_pages][Hkv][oscar_record_bytes(D, G)].
+ *   One record holds 16 tokens of one KV head:
+ *     K codes   [16][D/4]      token-major, 4 codes per byte, channel c in bits
+ *                              2*(c%4) of byte c/4 (LSB first)
+ *     V codes   [D][4]         channel-major, token t in bits 2*(t%4) of byte t/4
+ *     K (s, z)  [16][D/G][2]   bf16 scale, bf16 zero per (token, group)
+ *     V (s, z)  [16][D/G][2]
+ *   Codes are in {0,1,2,3}; the dequantised rotated value is code*scale + zero.
+ *   BF16 pools: uint16 [num_bf16_pages][Hkv][16][D], one for K and one for V.
+ *   A token slot is page*16 + offset within the page.
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  OSCAR_OK = 0,
+  OSCAR_EINVAL = -1,        /* bad pointer, size, range or combination        */
+  OSCAR_EUNSUPPORTED = -2,  /* valid but not built (head_dim, group size, ...) */
+  OSCAR_EWORKSPACE = -3,    /* workspace smaller than required                 */
+  OSCAR_EHIP = -4           /* a HIP runtime call or kernel launch failed      */
+} oscar_status;
+
+enum {
+  OSCAR_PAGE_TOKENS = 16,
+  OSCAR_SINK_TOKENS = 64,
+  OSCAR_RECENT_TOKENS = 256,
+  OSCAR_MAX_BF16_TOKENS = 320,   /* sink + recent                              */
+  OSCAR_MAX_Q_HEADS = 256
+};
+
+/* Which kernel computes the INT2 segment. */
+enum {
+  OSCAR_INT2_AUTO = 0,
+  OSCAR_INT2_VALU = 1,      /* vector-ALU dot products                         */
+  OSCAR_INT2_MFMA = 2       /* matrix-core contraction                         */
+};
+
+typedef struct {
+  int32_t num_kv_heads;      /* Hkv >= 1                                        */
+  int32_t head_dim;          /* D in {64, 128}                                  */
+  int32_t group_size;        /* G in {32, 64, 128}, G divides D                 */
+  int32_t page_size;         /* must be 16                                      */
+  uint8_t *int2_pool;        /* [num_int2_pages][Hkv][record]                   */
+  int64_t num_int2_pages;
+  uint16_t *bf16_k_pool;     /* [num_bf16_pages][Hkv][16][D]                    */
+  uint16_t *bf16_v_pool;
+  int64_t num_bf16_pages;
+} oscar_cache;
+
+typedef struct {
+  int32_t batch;             /* B >= 1                                          */
+  int32_t num_q_heads;       /* Hq, a multiple of Hkv, <= OSCAR_MAX_Q_HEADS     */
+  const int32_t *kv_head_of_q; /* [host][Hq] KV head of each q head, every KV
+                                  head used by exactly Hq/Hkv q heads; NULL means
+                                  h -> h / (Hq/Hkv)                             */
+  const int32_t *hist_pages; /* [B][hist_stride] physical INT2 page ids in token
+                                order; entries past ceil(hist_len/16) unread     */
+  int32_t hist_stride;
+  const int32_t *hist_len;   /* [B] INT2 history tokens, 0 <= len <= max_hist_len */
+  const int32_t *bf16_pages; /* [B][bf16_stride] physical BF16 page ids         */
+  int32_t bf16_stride;
+  const int32_t *bf16_len;   /* [B] BF16 tokens (sink + recent), 0..320; slots
+                                0..len-1 of the listed pages are attended (their
+                                order does not matter)                          */
+  int32_t max_hist_len;      /* [host] upper bound on every hist_len; sizes the
+                                grid without a device-to-host read               */
+  float sm_scale;            /* softmax scale; 0 means 1/sqrt(D)                */
+  int32_t num_splits;        /* history chunks per (sequence, KV head); 0 = auto */
+  int32_t int2_kernel;       /* OSCAR_INT2_AUTO / _VALU / _MFMA                  */
+} oscar_decode_args;
+
+/* Bytes of one INT2 page record: 2*16*(D/4) + 2*16*(D/G)*4. */
+size_t oscar_record_bytes(int32_t head_dim, int32_t group_size);
+
+/* Text for the last non-OK status returned on this thread ("" if none). */
+const char *oscar_last_error(void);
+
+/*
+ * oscar_write_bf16 - store n new tokens' K and V into BF16 slots (the new
+ * decode token goes into the recent window; thmotor split-cache paragraph).
+ *   dst_slot [n]       BF16 slot page*16+off, or -1 to skip the entry
+ *   k_new, v_new       [n][Hkv][D] bf16
+ * Errors: EINVAL for NULL pointers with n > 0, n < 0, bad cache descriptor.
+ */
+int oscar_write_bf16(const oscar_cache *cache, int32_t n, const int32_t *dst_slot,
+                     const uint16_t *k_new, const uint16_t *v_new, void *stream);
+
+/*
+ * oscar_demote_pack - rotate, clip, quantise and pack n tokens from BF16 slots
+ * into INT2 history slots (thmotor: split-cache paragraph, rotate/clip/
+ * quantize/pack at demotion, four 2-bit values per byte).
+ *   src_slot [n]   BF16 slot (page*16+off) read for every KV head, or -1 to skip
+ *   dst_slot [n]   INT2 slot (page*16+off) written for every KV head
+ *   R_k, R_v       [Hkv][D][D] fp32, row-vector convention x = k . R;
+ *                  R_v == NULL means identity (value rotation folded upstream)
+ *   clip_k, clip_v [Hkv] fp32 clipping ratios in (0, 1]
+ * Per (token, KV head, K|V): x = k . R in fp64; per group of G consecutive
+ * channels mx, mn = max, min; scale = (c*mx - c*mn)/3 and zero = c*mn rounded
+ * to bf16 (nearest even, from fp64); code = clamp(rint((x - zero)/scale), 0, 3)
+ * (0 when scale == 0).  The other tokens' bits in a shared record are
+ * preserved, so any set of distinct destination slots may be demoted in one
+ * call; two entries with the same destination race.
+ * Errors: EINVAL (NULL pointers with n > 0, clip outside (0,1] is not checked
+ * on the device: pass validated values), EUNSUPPORTED (D, G), EHIP.
+ */
+int oscar_demote_pack(const oscar_cache *cache, int32_t n, const int32_t *src_slot,
+                      const int32_t *dst_slot, const float *R_k, const float *R_v,
+                      const float *clip_k, const float *clip_v, void *stream);
+
+/* Workspace bytes oscar_decode_attn needs for these arguments (host only). */
+int oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_args *args,
+                                 size_t *bytes);
+
+/*
+ * oscar_decode_attn - attend every q head over both segments, producing partial
+ * results in `workspace` (thmotor: decode stage of the split-cache paragraph).
+ *   q          [B][Hq][D] bf16
+ *   R_k        [Hkv][D][D] fp32: the history is attended with q . R_k
+ *   workspace  >= oscar_decode_workspace_bytes; contents valid for a following
+ *              oscar_merge with the same cache/args on the same stream
+ * Partials per (sequence, q head): one for the BF16 segment (unrotated q and
+ * K/V) and one per history chunk (rotated basis), each (max logit, sum of
+ * exponentials, unnormalised output), fp32.
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP.
+ */
+int oscar_decode_attn(const oscar_cache *cache, const oscar_decode_args *args,
+                      const uint16_t *q, const float *R_k, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
+ * oscar_merge - log-sum-exp merge of the history chunks, un-rotation of the
+ * history output by R_v^T, and online-softmax merge with the BF16 segment
+ * (thmotor: online softmax merge of the two segments).
+ *   R_v  [Hkv][D][D] fp32 or NULL (identity)
+ *   out  [B][Hq][D] fp32 attention output
+ *   lse  [B][Hq] fp32 natural-log softmax denominator, or NULL
+ * A (sequence, head) with no tokens at all gets out = 0 and lse = -inf.
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP.
+ */
+int oscar_merge(const oscar_cache *cache, const oscar_decode_args *args,
+                const void *workspace, size_t workspace_bytes, const float *R_v,
+                float *out, float *lse, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OSCAR_H */

@@ -1,0 +1,273 @@
+// Host side of liboscar: argument validation, workspace layout, launches.
+// Validation never calls the HIP runtime, so every argument error is reported
+// the same way with or without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "common.hpp"
+
+namespace oscar {
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(OSCAR_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int check_cache(const oscar_cache *c) {
+  if (c == nullptr) return fail(OSCAR_EINVAL, "cache is NULL");
+  if (c->page_size != OSCAR_PAGE_TOKENS)
+    return fail(OSCAR_EINVAL, "page_size must be %d (got %d)", OSCAR_PAGE_TOKENS, c->page_size);
+  if (c->num_kv_heads < 1 || c->num_kv_heads > OSCAR_MAX_Q_HEADS)
+    return fail(OSCAR_EINVAL, "num_kv_heads out of range (got %d)", c->num_kv_heads);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(OSCAR_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c->head_dim);
+  const int G = c->group_size;
+  if (G != 32 && G != 64 && G != 128)
+    return fail(OSCAR_EUNSUPPORTED, "group_size must be 32, 64 or 128 (got %d)", G);
+  if (G > c->head_dim || c->head_dim % G != 0)
+    return fail(OSCAR_EUNSUPPORTED, "group_size %d does not divide head_dim %d", G, c->head_dim);
+  if (c->num_int2_pages < 0 || c->num_bf16_pages < 0)
+    return fail(OSCAR_EINVAL, "negative page count");
+  if (c->num_int2_pages > 0 && (c->int2_pool == nullptr || !aligned(c->int2_pool, 16)))
+    return fail(OSCAR_EINVAL, "int2_pool is NULL or not 16-byte aligned");
+  if (c->num_bf16_pages > 0 &&
+      (c->bf16_k_pool == nullptr || c->bf16_v_pool == nullptr || !aligned(c->bf16_k_pool, 16) ||
+       !aligned(c->bf16_v_pool, 16)))
+    return fail(OSCAR_EINVAL, "bf16 pools are NULL or not 16-byte aligned");
+  return OSCAR_OK;
+}
+
+// Fills kv_of_q / q_of_kv; checks every KV head is used by exactly g q heads.
+int build_head_map(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p) {
+  const int Hq = a->num_q_heads, Hkv = c->num_kv_heads;
+  if (Hq < 1 || Hq > OSCAR_MAX_Q_HEADS)
+    return fail(OSCAR_EINVAL, "num_q_heads out of range (got %d)", Hq);
+  if (Hq % Hkv != 0)
+    return fail(OSCAR_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", Hq, Hkv);
+  const int g = Hq / Hkv;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(OSCAR_EUNSUPPORTED, "q heads per KV head must be 1, 2, 4 or 8 (got %d)", g);
+  int cnt[OSCAR_MAX_Q_HEADS] = {0};
+  for (int h = 0; h < Hq; ++h) {
+    const int j = a->kv_head_of_q ? a->kv_head_of_q[h] : h / g;
+    if (j < 0 || j >= Hkv)
+      return fail(OSCAR_EINVAL, "kv_head_of_q[%d] = %d outside [0, %d)", h, j, Hkv);
+    if (cnt[j] >= g)
+      return fail(OSCAR_EINVAL, "KV head %d is used by more than %d q heads", j, g);
+    p->kv_of_q[h] = (int16_t)j;
+    p->q_of_kv[j * g + cnt[j]] = (int16_t)h;
+    ++cnt[j];
+  }
+  p->g = g;
+  return OSCAR_OK;
+}
+
+int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p) {
+  int st = check_cache(c);
+  if (st) return st;
+  if (a == nullptr) return fail(OSCAR_EINVAL, "args is NULL");
+  if (a->batch < 1) return fail(OSCAR_EINVAL, "batch must be >= 1 (got %d)", a->batch);
+  st = build_head_map(c, a, p);
+  if (st) return st;
+  if (a->max_hist_len < 0) return fail(OSCAR_EINVAL, "max_hist_len < 0");
+  if (a->hist_len == nullptr || a->bf16_len == nullptr)
+    return fail(OSCAR_EINVAL, "hist_len / bf16_len must not be NULL");
+  const int need_hist = (a->max_hist_len + OSCAR_PAGE_TOKENS - 1) / OSCAR_PAGE_TOKENS;
+  if (need_hist > 0) {
+    if (a->hist_pages == nullptr) return fail(OSCAR_EINVAL, "hist_pages is NULL");
+    if (a->hist_stride < need_hist)
+      return fail(OSCAR_EINVAL, "hist_stride %d < ceil(max_hist_len/16) = %d", a->hist_stride,
+                  need_hist);
+    if (c->num_int2_pages <= 0) return fail(OSCAR_EINVAL, "max_hist_len > 0 but no INT2 pages");
+  }
+  if (a->bf16_pages == nullptr || a->bf16_stride < 1)
+    return fail(OSCAR_EINVAL, "bf16_pages is NULL or bf16_stride < 1");
+  if (!(a->sm_scale >= 0.f) || !std::isfinite(a->sm_scale))
+    return fail(OSCAR_EINVAL, "sm_scale must be finite and >= 0");
+  if (a->num_splits < 0) return fail(OSCAR_EINVAL, "num_splits < 0");
+  if (a->int2_kernel < OSCAR_INT2_AUTO || a->int2_kernel > OSCAR_INT2_MFMA)
+    return fail(OSCAR_EINVAL, "int2_kernel must be 0, 1 or 2");
+
+  p->B = a->batch;
+  p->Hq = a->num_q_heads;
+  p->Hkv = c->num_kv_heads;
+  p->D = c->head_dim;
+  p->G = c->group_size;
+  p->int2_pool = c->int2_pool;
+  p->num_int2_pages = c->num_int2_pages;
+  p->bf16_k = c->bf16_k_pool;
+  p->bf16_v = c->bf16_v_pool;
+  p->num_bf16_pages = c->num_bf16_pages;
+  p->hist_pages = a->hist_pages;
+  p->hist_stride = a->hist_stride;
+  p->hist_len = a->hist_len;
+  p->bf16_pages = a->bf16_pages;
+  p->bf16_stride = a->bf16_stride;
+  p->bf16_len = a->bf16_len;
+  p->max_hist_len = a->max_hist_len;
+  const float sm = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt((float)c->head_dim);
+  p->sm_log2 = sm * kLog2e;
+
+  // history split: enough blocks to fill the chip, but each block streams
+  // enough pages that the chunk partials stay ~2% of the history bytes
+  const int npages = need_hist;
+  int S = 1;
+  if (npages > 0) {
+    if (a->num_splits > 0) {
+      S = a->num_splits < npages ? a->num_splits : npages;
+    } else {
+      const int units = a->batch * c->num_kv_heads;
+      const int target_blocks = 2048;
+      const double rec = (double)RecLayout(p->D, p->G).bytes();
+      const double part_bytes = 2.0 * p->g * (p->D + 2) * 4.0;   // write + read back
+      int min_pages = (int)std::ceil(50.0 * part_bytes / rec);
+      min_pages = min_pages < 16 ? 16 : min_pages;
+      int s_fill = (target_blocks + units - 1) / units;
+      int s_cap = npages / min_pages;
+      S = s_fill < s_cap ? s_fill : s_cap;
+      S = S < 1 ? 1 : S;
+    }
+  }
+  const int pps = npages > 0 ? (npages + S - 1) / S : 0;
+  if (npages > 0) S = (npages + pps - 1) / pps;
+  p->splits = S;
+  p->pages_per_split = pps;
+
+  WsLayout &L = p->L;
+  const size_t BH = (size_t)a->batch * a->num_q_heads;
+  size_t off = 0;
+  L.qrot = off; off = align256(off + BH * p->D * 4);
+  L.qpiece = off; off = align256(off + BH * 4 * p->D);
+  L.qexp = off; off = align256(off + BH * 4);
+  L.part_o = off; off = align256(off + BH * S * p->D * 4);
+  L.part_ml = off; off = align256(off + BH * S * 2 * 4);
+  L.bf_o = off; off = align256(off + BH * p->D * 4);
+  L.bf_ml = off; off = align256(off + BH * 2 * 4);
+  L.total = off;
+  L.splits = S;
+  L.pages_per_split = pps;
+  return OSCAR_OK;
+}
+
+}  // namespace
+}  // namespace oscar
+
+using namespace oscar;
+
+extern "C" {
+
+size_t oscar_record_bytes(int32_t head_dim, int32_t group_size) {
+  if (head_dim <= 0 || group_size <= 0 || head_dim % 4 || head_dim % group_size) return 0;
+  return (size_t)RecLayout(head_dim, group_size).bytes();
+}
+
+const char *oscar_last_error(void) { return g_err.c_str(); }
+
+int oscar_write_bf16(const oscar_cache *cache, int32_t n, const int32_t *dst_slot,
+                     const uint16_t *k_new, const uint16_t *v_new, void *stream) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (n < 0) return fail(OSCAR_EINVAL, "n < 0");
+  if (n == 0) return OSCAR_OK;
+  if (!dst_slot || !k_new || !v_new) return fail(OSCAR_EINVAL, "NULL slot or token pointer");
+  if (cache->num_bf16_pages <= 0) return fail(OSCAR_EINVAL, "cache has no BF16 pages");
+  hipError_t e = launch_write_bf16(*cache, n, dst_slot, k_new, v_new, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "oscar_write_bf16 launch");
+  return OSCAR_OK;
+}
+
+int oscar_demote_pack(const oscar_cache *cache, int32_t n, const int32_t *src_slot,
+                      const int32_t *dst_slot, const float *R_k, const float *R_v,
+                      const float *clip_k, const float *clip_v, void *stream) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (n < 0) return fail(OSCAR_EINVAL, "n < 0");
+  if (n == 0) return OSCAR_OK;
+  if (!src_slot || !dst_slot) return fail(OSCAR_EINVAL, "NULL slot list");
+  if (!R_k) return fail(OSCAR_EINVAL, "R_k is NULL");
+  if (!clip_k || !clip_v) return fail(OSCAR_EINVAL, "NULL clip ratios");
+  if (cache->num_bf16_pages <= 0 || cache->num_int2_pages <= 0)
+    return fail(OSCAR_EINVAL, "cache needs BF16 and INT2 pages");
+  hipError_t e = launch_demote(*cache, n, src_slot, dst_slot, R_k, R_v, clip_k, clip_v,
+                               (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "oscar_demote_pack launch");
+  return OSCAR_OK;
+}
+
+int oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_args *args,
+                                 size_t *bytes) {
+  DecodeParams p{};
+  int st = check_args(cache, args, &p);
+  if (st) return st;
+  if (!bytes) return fail(OSCAR_EINVAL, "bytes is NULL");
+  *bytes = p.L.total;
+  return OSCAR_OK;
+}
+
+int oscar_decode_attn(const oscar_cache *cache, const oscar_decode_args *args, const uint16_t *q,
+                      const float *R_k, void *workspace, size_t workspace_bytes, void *stream) {
+  DecodeParams p{};
+  int st = check_args(cache, args, &p);
+  if (st) return st;
+  if (!q || !aligned(q, 16)) return fail(OSCAR_EINVAL, "q is NULL or not 16-byte aligned");
+  if (!R_k) return fail(OSCAR_EINVAL, "R_k is NULL");
+  if (!workspace || !aligned(workspace, 256))
+    return fail(OSCAR_EINVAL, "workspace is NULL or not 256-byte aligned");
+  if (workspace_bytes < p.L.total)
+    return fail(OSCAR_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
+                p.L.total);
+  p.ws = static_cast<uint8_t *>(workspace);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_qrot(p, q, R_k, s);
+  if (e != hipSuccess) return hip_fail(e, "q rotation launch");
+  e = launch_bf16_seg(p, q, s);
+  if (e != hipSuccess) return hip_fail(e, "BF16 segment launch");
+  if (args->max_hist_len > 0) {
+    const int kind = args->int2_kernel == OSCAR_INT2_AUTO ? OSCAR_INT2_VALU : args->int2_kernel;
+    if (kind == OSCAR_INT2_MFMA)
+      return fail(OSCAR_EUNSUPPORTED, "the matrix-core INT2 kernel is not built in this library");
+    e = launch_int2_valu(p, s);
+    if (e != hipSuccess) return hip_fail(e, "INT2 segment launch");
+  }
+  return OSCAR_OK;
+}
+
+int oscar_merge(const oscar_cache *cache, const oscar_decode_args *args, const void *workspace,
+                size_t workspace_bytes, const float *R_v, float *out, float *lse, void *stream) {
+  DecodeParams p{};
+  int st = check_args(cache, args, &p);
+  if (st) return st;
+  if (!out) return fail(OSCAR_EINVAL, "out is NULL");
+  if (!workspace || !aligned(workspace, 256))
+    return fail(OSCAR_EINVAL, "workspace is NULL or not 256-byte aligned");
+  if (workspace_bytes < p.L.total)
+    return fail(OSCAR_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
+                p.L.total);
+  p.ws = static_cast<uint8_t *>(const_cast<void *>(workspace));
+  if (args->max_hist_len == 0) p.splits = 0;   // no history chunk was produced
+  hipError_t e = launch_merge(p, R_v, out, lse, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return OSCAR_OK;
+}
+
+}  // extern "C"

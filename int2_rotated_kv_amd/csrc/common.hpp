@@ -1,0 +1,90 @@
+// Internal helpers shared by the HIP translation units of liboscar.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "oscar.h"
+
+namespace oscar {
+
+constexpr int kPage = OSCAR_PAGE_TOKENS;
+constexpr int kMaxBf16 = OSCAR_MAX_BF16_TOKENS;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Byte offsets of the four sections of one INT2 page record (16 tokens, one KV
+// head): K codes [16][D/4] | V codes [D][4] | K (s,z) [16][D/G] dwords | V (s,z).
+struct RecLayout {
+  int D, G;
+  __host__ __device__ constexpr RecLayout(int d, int g) : D(d), G(g) {}
+  __host__ __device__ constexpr int kcodes() const { return 0; }
+  __host__ __device__ constexpr int vcodes() const { return kPage * (D / 4); }
+  __host__ __device__ constexpr int ksz() const { return 2 * kPage * (D / 4); }
+  __host__ __device__ constexpr int vsz() const { return 2 * kPage * (D / 4) + kPage * (D / G) * 4; }
+  __host__ __device__ constexpr int bytes() const { return 2 * kPage * (D / 4) + 2 * kPage * (D / G) * 4; }
+};
+
+// bf16 bit pattern -> float (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Workspace partition used by decode_attn and merge.
+struct WsLayout {
+  size_t qrot;      // fp32 [B][Hq][D]     q . R_k (unscaled)
+  size_t qpiece;    // int8 [B][Hq][4][D] + per-head exponent (MFMA path)
+  size_t qexp;      // int32 [B][Hq]
+  size_t part_o;    // fp32 [B][Hq][S][D]  history chunk partial outputs (rotated basis)
+  size_t part_ml;   // fp32 [B][Hq][S][2]  (max logit in log2 units, sum of exponentials)
+  size_t bf_o;      // fp32 [B][Hq][D]     BF16 segment partial output
+  size_t bf_ml;     // fp32 [B][Hq][2]
+  size_t total;
+  int splits;       // S
+  int pages_per_split;
+};
+
+// Kernel-side description of a decode call (passed by value).
+struct DecodeParams {
+  int B, Hq, Hkv, g, D, G;
+  const uint8_t *int2_pool;
+  int64_t num_int2_pages;
+  const uint16_t *bf16_k, *bf16_v;
+  int64_t num_bf16_pages;
+  const int32_t *hist_pages;
+  int hist_stride;
+  const int32_t *hist_len;
+  const int32_t *bf16_pages;
+  int bf16_stride;
+  const int32_t *bf16_len;
+  int max_hist_len;
+  float sm_log2;       // softmax scale * log2(e)
+  int splits, pages_per_split;
+  uint8_t *ws;
+  WsLayout L;
+  int16_t q_of_kv[OSCAR_MAX_Q_HEADS];  // [Hkv][g] q heads of each KV head
+  int16_t kv_of_q[OSCAR_MAX_Q_HEADS];  // [Hq] KV head of each q head
+};
+
+// Wave-local ordering of LDS traffic between lanes of one wavefront.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Launchers (defined next to their kernels).
+hipError_t launch_write_bf16(const oscar_cache &c, int n, const int32_t *dst, const uint16_t *k,
+                             const uint16_t *v, hipStream_t s);
+hipError_t launch_demote(const oscar_cache &c, int n, const int32_t *src, const int32_t *dst,
+                         const float *Rk, const float *Rv, const float *ck, const float *cv,
+                         hipStream_t s);
+hipError_t launch_qrot(const DecodeParams &p, const uint16_t *q, const float *Rk, hipStream_t s);
+hipError_t launch_bf16_seg(const DecodeParams &p, const uint16_t *q, hipStream_t s);
+hipError_t launch_int2_valu(const DecodeParams &p, hipStream_t s);
+hipError_t launch_int2_mfma(const DecodeParams &p, hipStream_t s);
+hipError_t launch_merge(const DecodeParams &p, const float *Rv, float *out, float *lse,
+                        hipStream_t s);
+
+}  // namespace oscar

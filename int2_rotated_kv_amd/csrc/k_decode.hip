@@ -1,0 +1,389 @@
+// Decode-attention kernels over the split cache: query rotation, the BF16
+// (sink + recent) segment, and the vector-ALU variant of the INT2 history
+// segment (m.th-motor.com repost of the OSCAR article, decode stage of the
+// split-cache paragraph: the INT2 kernel unpacks, restores scale/zero point
+// and accumulates in floating point; the BF16 kernel handles sink/recent; an
+// online-softmax merge combines them).
+//
+// Logits are carried in log2 units: s = (q . k) * sm_scale * log2(e), so every
+// exponential is exp2.  Partials per (sequence, q head, chunk) are
+// (m = max s, l = sum 2^(s - m), o = sum 2^(s - m) v) in fp32.
+#include "common.hpp"
+
+namespace oscar {
+
+// ---------------------------------------------------------------------------
+// q . R_k for every (sequence, q head): the history keys are stored as k . R_k,
+// so (q . R_k) . (k . R_k) = q . k for an orthogonal R_k.  fp64 accumulation,
+// one rounding to fp32.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(D) void k_qrot(DecodeParams p, const uint16_t *__restrict__ q,
+                                            const float *__restrict__ Rk) {
+  const int bh = blockIdx.x;
+  const int h = bh % p.Hq;
+  const int j = p.kv_of_q[h];
+  const int c = threadIdx.x;
+  __shared__ double qs[D];
+  qs[c] = (double)bf16_to_f32(q[(size_t)bh * D + c]);
+  __syncthreads();
+  const float *R = Rk + (size_t)j * D * D;
+  double acc = 0.0;
+  for (int i = 0; i < D; ++i) acc = fma(qs[i], (double)R[(size_t)i * D + c], acc);
+  reinterpret_cast<float *>(p.ws + p.L.qrot)[(size_t)bh * D + c] = (float)acc;
+}
+
+hipError_t launch_qrot(const DecodeParams &p, const uint16_t *q, const float *Rk, hipStream_t s) {
+  const int nb = p.B * p.Hq;
+  if (p.D == 64) hipLaunchKernelGGL(k_qrot<64>, dim3(nb), dim3(64), 0, s, p, q, Rk);
+  else hipLaunchKernelGGL(k_qrot<128>, dim3(nb), dim3(128), 0, s, p, q, Rk);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// BF16 segment: up to 320 unrotated tokens per sequence in BF16 pages.  One
+// block per (sequence, KV head); the g q heads of the KV head share every load.
+// ---------------------------------------------------------------------------
+template <int D, int GQ>
+__global__ __launch_bounds__(256) void k_bf16_seg(DecodeParams p, const uint16_t *__restrict__ q) {
+  constexpr int NT = 256;
+  constexpr int NP = NT / D;          // token partitions in the PV phase
+  const int b = blockIdx.x / p.Hkv;
+  const int j = blockIdx.x % p.Hkv;
+  const int tid = threadIdx.x;
+
+  __shared__ float qs[GQ][D];
+  __shared__ float sp[GQ][kMaxBf16];
+  __shared__ int pages[kMaxBf16 / kPage];
+  __shared__ float hm[GQ], hl[GQ];
+  __shared__ float po[NP][GQ][D];
+
+  int T = p.bf16_len[b];
+  T = T < 0 ? 0 : T;
+  T = T > kMaxBf16 ? kMaxBf16 : T;
+  T = T > kPage * p.bf16_stride ? kPage * p.bf16_stride : T;
+
+  for (int i = tid; i < GQ * D; i += NT) {
+    const int h = i / D, c = i % D;
+    const int hq = p.q_of_kv[j * GQ + h];
+    qs[h][c] = bf16_to_f32(q[((size_t)b * p.Hq + hq) * D + c]) * p.sm_log2;
+  }
+  if (tid < (T + kPage - 1) / kPage) pages[tid] = p.bf16_pages[(size_t)b * p.bf16_stride + tid];
+  __syncthreads();
+
+  // logits: one token per thread
+  for (int t = tid; t < T; t += NT) {
+    const int64_t page = pages[t / kPage];
+    float acc[GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) acc[h] = 0.f;
+    const bool ok = page >= 0 && page < p.num_bf16_pages;
+    if (ok) {
+      const uint4 *kp = reinterpret_cast<const uint4 *>(
+          p.bf16_k + ((page * p.Hkv + j) * kPage + (t % kPage)) * D);
+#pragma unroll 4
+      for (int c8 = 0; c8 < D / 8; ++c8) {
+        const uint4 v = kp[c8];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float k0 = bf16_lo(w4[e]), k1 = bf16_hi(w4[e]);
+          const int c = c8 * 8 + 2 * e;
+#pragma unroll
+          for (int h = 0; h < GQ; ++h) acc[h] = fmaf(qs[h][c + 1], k1, fmaf(qs[h][c], k0, acc[h]));
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) sp[h][t] = ok ? acc[h] : -INFINITY;
+  }
+  __syncthreads();
+
+  // per-head max and sum, one wave per head (4 waves)
+  const int lane = tid & 63, w = tid >> 6;
+  for (int h = w; h < GQ; h += NT / 64) {
+    float m = -INFINITY;
+    for (int t = lane; t < T; t += 64) m = fmaxf(m, sp[h][t]);
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float l = 0.f;
+    for (int t = lane; t < T; t += 64) {
+      const float e = (m == -INFINITY) ? 0.f : exp2f(sp[h][t] - m);
+      sp[h][t] = e;
+      l += e;
+    }
+    for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+    if (lane == 0) { hm[h] = m; hl[h] = l; }
+  }
+  __syncthreads();
+
+  // PV: thread (part, c), tokens part, part + NP, ...
+  {
+    const int c = tid % D, part = tid / D;
+    float acc[GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) acc[h] = 0.f;
+    for (int t = part; t < T; t += NP) {
+      const int64_t page = pages[t / kPage];
+      if (page < 0 || page >= p.num_bf16_pages) continue;
+      const float v = bf16_to_f32(p.bf16_v[((page * p.Hkv + j) * kPage + (t % kPage)) * D + c]);
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) acc[h] = fmaf(sp[h][t], v, acc[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) po[part][h][c] = acc[h];
+  }
+  __syncthreads();
+  float *bo = reinterpret_cast<float *>(p.ws + p.L.bf_o);
+  float *bml = reinterpret_cast<float *>(p.ws + p.L.bf_ml);
+  for (int i = tid; i < GQ * D; i += NT) {
+    const int h = i / D, c = i % D;
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) s += po[k][h][c];
+    const int hq = p.q_of_kv[j * GQ + h];
+    bo[((size_t)b * p.Hq + hq) * D + c] = s;
+    if (c == 0) {
+      bml[((size_t)b * p.Hq + hq) * 2 + 0] = hm[h];
+      bml[((size_t)b * p.Hq + hq) * 2 + 1] = hl[h];
+    }
+  }
+}
+
+template <int D>
+static void launch_bf16_d(const DecodeParams &p, const uint16_t *q, hipStream_t s) {
+  const dim3 grid(p.B * p.Hkv), blk(256);
+  switch (p.g) {
+    case 1: hipLaunchKernelGGL((k_bf16_seg<D, 1>), grid, blk, 0, s, p, q); break;
+    case 2: hipLaunchKernelGGL((k_bf16_seg<D, 2>), grid, blk, 0, s, p, q); break;
+    case 4: hipLaunchKernelGGL((k_bf16_seg<D, 4>), grid, blk, 0, s, p, q); break;
+    default: hipLaunchKernelGGL((k_bf16_seg<D, 8>), grid, blk, 0, s, p, q); break;
+  }
+}
+
+hipError_t launch_bf16_seg(const DecodeParams &p, const uint16_t *q, hipStream_t s) {
+  if (p.D == 64) launch_bf16_d<64>(p, q, s);
+  else launch_bf16_d<128>(p, q, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// INT2 history segment, vector-ALU variant.  One block (4 waves) per
+// (sequence, KV head, chunk of pages); each wave walks every 4th page of the
+// chunk.  Per page (16 tokens):
+//   QK:  lane (t = lane%16, part = lane/16) dots q_rot with the codes of token
+//        t's channel quarter `part`, then applies that group's scale/zero:
+//        s_part = scale * sum(q*code) + zero * sum(q); the four quarters are
+//        summed across lanes.
+//   softmax: running max per head over the 16 token lanes; p = 2^(s - m).
+//   PV:  lane owns channels lane + 64k and accumulates
+//        sum_t (p*scale_v) * code_v; the zero-point part sum_t p*zero_v depends
+//        only on (head, group) and is accumulated on the token lanes.
+// ---------------------------------------------------------------------------
+template <int D, int G, int GQ>
+__global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
+  constexpr RecLayout RL(D, G);
+  constexpr int NG = D / G;       // groups per token
+  constexpr int PART = D / 4;     // channels per QK quarter
+  constexpr int CPL = D / 64;     // PV channels per lane
+  constexpr int KW = D / 64;      // K-code dwords per QK lane
+  static_assert(PART <= G, "a QK quarter must lie inside one group");
+
+  const int S = p.splits;
+  const int unit = blockIdx.x / S;
+  const int split = blockIdx.x % S;
+  const int b = unit / p.Hkv;
+  const int j = unit % p.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t = lane & 15, part = lane >> 4;
+
+  __shared__ float qs[D][GQ];                 // q_rot * sm_log2, heads innermost
+  __shared__ float qpart[4][GQ];              // sum of each quarter's q
+  __shared__ float pw[4][NG][16][GQ];         // per wave: p * scale_v per (group, token, head)
+  __shared__ float zred[4][NG][GQ];           // per wave: sum_t p * zero_v
+  __shared__ float wm[4][GQ], wl[4][GQ];
+  __shared__ float wo[4][GQ][D];
+
+  const float *qrot = reinterpret_cast<const float *>(p.ws + p.L.qrot);
+  for (int i = tid; i < GQ * D; i += 256) {
+    const int h = i / D, c = i % D;
+    const int hq = p.q_of_kv[j * GQ + h];
+    qs[c][h] = qrot[((size_t)b * p.Hq + hq) * D + c] * p.sm_log2;
+  }
+  __syncthreads();
+  if (tid < 4 * GQ) {
+    const int pt = tid / GQ, h = tid % GQ;
+    float s = 0.f;
+    for (int i = 0; i < PART; ++i) s += qs[pt * PART + i][h];
+    qpart[pt][h] = s;
+  }
+  __syncthreads();
+
+  int hl = p.hist_len[b];
+  hl = hl < 0 ? 0 : hl;
+  hl = hl > p.max_hist_len ? p.max_hist_len : hl;
+  hl = hl > kPage * p.hist_stride ? kPage * p.hist_stride : hl;
+  const int npages = (hl + kPage - 1) / kPage;
+  const int p0 = split * p.pages_per_split;
+  int p1 = p0 + p.pages_per_split;
+  p1 = p1 > npages ? npages : p1;
+
+  const int grp_qk = (part * PART) / G;
+  float m[GQ], lsum[GQ], zacc[GQ], o[GQ][CPL];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    m[h] = -INFINITY;
+    lsum[h] = 0.f;
+    zacc[h] = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) o[h][k] = 0.f;
+  }
+
+  for (int pg = p0 + w; pg < p1; pg += 4) {
+    const int phys = p.hist_pages[(size_t)b * p.hist_stride + pg];
+    if (phys < 0 || phys >= p.num_int2_pages) continue;
+    const uint8_t *rec = p.int2_pool + ((size_t)phys * p.Hkv + j) * RL.bytes();
+    const int ntok = hl - pg * kPage < kPage ? hl - pg * kPage : kPage;
+
+    // ---- QK ----
+    const uint32_t *kr = reinterpret_cast<const uint32_t *>(rec + RL.kcodes() + t * (D / 4)) + part * KW;
+    uint32_t kw[KW];
+#pragma unroll
+    for (int i = 0; i < KW; ++i) kw[i] = kr[i];
+    const uint32_t ksz = reinterpret_cast<const uint32_t *>(rec + RL.ksz())[t * NG + grp_qk];
+    const uint32_t vszw = reinterpret_cast<const uint32_t *>(rec + RL.vsz())[t * NG + grp_qk];
+    uint32_t vcw[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) vcw[k] = reinterpret_cast<const uint32_t *>(rec + RL.vcodes())[lane + 64 * k];
+
+    float dot[GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) dot[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < KW; ++i) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float cf = (float)((kw[i] >> (2 * k)) & 3u);
+        const int c = part * PART + i * 16 + k;
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) dot[h] = fmaf(qs[c][h], cf, dot[h]);
+      }
+    }
+    const float ksc = bf16_lo(ksz), kze = bf16_hi(ksz);
+    float sv[GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      float v = fmaf(ksc, dot[h], kze * qpart[part][h]);
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      sv[h] = t < ntok ? v : -INFINITY;
+    }
+
+    // ---- online softmax ----
+    // (scale, zero) of tokens not yet written are never used: unwritten record
+    // bytes may hold any bit pattern
+    const float vsc = t < ntok ? bf16_lo(vszw) : 0.f;
+    const float vze = t < ntok ? bf16_hi(vszw) : 0.f;
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      float pm = sv[h];
+#pragma unroll
+      for (int o2 = 1; o2 < 16; o2 <<= 1) pm = fmaxf(pm, __shfl_xor(pm, o2));
+      const float mn = fmaxf(m[h], pm);
+      const float alpha = (m[h] == -INFINITY) ? 0.f : exp2f(m[h] - mn);
+      const float pr = (sv[h] == -INFINITY) ? 0.f : exp2f(sv[h] - mn);
+      m[h] = mn;
+      lsum[h] = fmaf(lsum[h], alpha, pr);
+      zacc[h] = fmaf(zacc[h], alpha, pr * vze);
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) o[h][k] *= alpha;
+      // one lane per (group, token) publishes p * scale_v
+      if ((part * PART) % G == 0) pw[w][grp_qk][t][h] = pr * vsc;
+    }
+    wave_lds_sync();
+
+    // ---- PV ----
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int c = lane + 64 * k;
+      const int gc = c / G;
+#pragma unroll 4
+      for (int tt = 0; tt < 16; ++tt) {
+        const float cf = (float)((vcw[k] >> (2 * tt)) & 3u);
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) o[h][k] = fmaf(pw[w][gc][tt][h], cf, o[h][k]);
+      }
+    }
+    wave_lds_sync();
+  }
+
+  // ---- wave epilogue: sum the per-token-lane partial sums ----
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    float l = lsum[h], z = zacc[h];
+#pragma unroll
+    for (int o2 = 1; o2 < 16; o2 <<= 1) {
+      l += __shfl_xor(l, o2);
+      z += __shfl_xor(z, o2);
+    }
+    lsum[h] = l;
+    if (t == 0 && (part * PART) % G == 0) zred[w][grp_qk][h] = z;
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) wo[w][h][lane + 64 * k] = o[h][k] + zred[w][(lane + 64 * k) / G][h];
+    if (lane == 0) { wm[w][h] = m[h]; wl[w][h] = lsum[h]; }
+  }
+  __syncthreads();
+
+  // ---- combine the 4 waves, write the chunk partial ----
+  float *po = reinterpret_cast<float *>(p.ws + p.L.part_o);
+  float *pml = reinterpret_cast<float *>(p.ws + p.L.part_ml);
+  for (int i = tid; i < GQ * D; i += 256) {
+    const int h = i / D, c = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) M = fmaxf(M, wm[k][h]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (wm[k][h] == -INFINITY) continue;
+        const float a = exp2f(wm[k][h] - M);
+        L = fmaf(wl[k][h], a, L);
+        O = fmaf(wo[k][h][c], a, O);
+      }
+    }
+    const int hq = p.q_of_kv[j * GQ + h];
+    const size_t row = ((size_t)b * p.Hq + hq) * S + split;
+    po[row * D + c] = O;
+    if (c == 0) {
+      pml[row * 2 + 0] = M;
+      pml[row * 2 + 1] = L;
+    }
+  }
+}
+
+template <int D, int G>
+static void launch_int2_valu_dg(const DecodeParams &p, hipStream_t s) {
+  const dim3 grid(p.B * p.Hkv * p.splits), blk(256);
+  switch (p.g) {
+    case 1: hipLaunchKernelGGL((k_int2_valu<D, G, 1>), grid, blk, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((k_int2_valu<D, G, 2>), grid, blk, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((k_int2_valu<D, G, 4>), grid, blk, 0, s, p); break;
+    default: hipLaunchKernelGGL((k_int2_valu<D, G, 8>), grid, blk, 0, s, p); break;
+  }
+}
+
+hipError_t launch_int2_valu(const DecodeParams &p, hipStream_t s) {
+  if (p.D == 64 && p.G == 32) launch_int2_valu_dg<64, 32>(p, s);
+  else if (p.D == 64 && p.G == 64) launch_int2_valu_dg<64, 64>(p, s);
+  else if (p.D == 128 && p.G == 32) launch_int2_valu_dg<128, 32>(p, s);
+  else if (p.D == 128 && p.G == 64) launch_int2_valu_dg<128, 64>(p, s);
+  else if (p.D == 128 && p.G == 128) launch_int2_valu_dg<128, 128>(p, s);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace oscar

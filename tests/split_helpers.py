@@ -1,0 +1,153 @@
+"""Shared helpers of the GPU parity tests: build a split cache on the device
+through the library, and compute the same step with the CPU oracle.
+
+Inputs come only from synth; expected values only from oracle.  The two sides
+meet here and nowhere else."""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+import synth
+from oracle import oscar_oracle as orc
+
+PAGE, SINK, RECENT = 16, 64, 256
+
+
+def to_dev_bf16(bits, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+@dataclass
+class DeviceRun:
+    sc: object            # SplitCache
+    out: np.ndarray       # [B][Hq][D] float32
+    lse: np.ndarray       # [B][Hq]
+    pool: np.ndarray      # INT2 pool bytes [pages][Hkv][rec]
+    hist_len: np.ndarray  # per sequence after the steps
+
+
+def hist_capacity_pages(L: int, steps: int) -> int:
+    s, h, r = synth.split_lengths(L)
+    return max(1, -(-(h + steps) // PAGE))
+
+
+def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_splits=0,
+                   R_v_none=False, head_map=None, device="cuda", seed_perm=None):
+    """Build the initial split cache of every sequence, run `steps` decode steps
+    (demote oldest recent -> write new token -> attend -> merge), return the
+    outputs of the last step and the INT2 pool."""
+    import torch
+    from int2_rotated_kv_amd import binding as ob
+    from int2_rotated_kv_amd.splitcache import SplitCache
+
+    wl = inp.wl
+    B = wl.B
+    caps = [hist_capacity_pages(L, steps) for L in wl.lengths]
+    stride = max(caps)
+    n_int2 = sum(caps)
+    perm = synth.page_permutation(wl.seed if seed_perm is None else seed_perm, n_int2, extra=3)
+    table = np.zeros((B, stride), dtype=np.int32)
+    o = 0
+    for b in range(B):
+        table[b, :caps[b]] = perm[o:o + caps[b]]
+        o += caps[b]
+    sc = SplitCache(B, wl.Hkv, wl.Hq, wl.D, wl.G, table, n_int2 + 3, staging_pages=64, device=device)
+    Rk = torch.from_numpy(inp.R_k).to(device)
+    Rv = None if R_v_none else torch.from_numpy(inp.R_v).to(device)
+    ck = torch.from_numpy(inp.clip_k).to(device)
+    cv = torch.from_numpy(inp.clip_v).to(device)
+    entries = []
+    for b in range(B):
+        L = wl.lengths[b]
+        s, h, r = synth.split_lengths(L)
+        K, V = inp.K[b], inp.V[b]
+        bidx = list(range(0, s)) + list(range(s + h, L))
+        sc.load_bf16(b, to_dev_bf16(K[bidx]), to_dev_bf16(V[bidx]))
+        if h:
+            entries.append((b, 0, to_dev_bf16(K[s:s + h]), to_dev_bf16(V[s:s + h])))
+    sc.fill_history(entries, Rk, Rv, ck, cv)
+
+    out = torch.zeros((B, wl.Hq, wl.D), dtype=torch.float32, device=device)
+    lse = torch.zeros((B, wl.Hq), dtype=torch.float32, device=device)
+    for st in range(steps):
+        dsrc, ddst, wdst = sc.plan_step()
+        ob.demote_pack(sc.cache, torch.from_numpy(dsrc).to(device), torch.from_numpy(ddst).to(device),
+                       Rk, Rv, ck, cv)
+        newk = np.stack([inp.K[b][wl.lengths[b] + st] for b in range(B)])
+        newv = np.stack([inp.V[b][wl.lengths[b] + st] for b in range(B)])
+        ob.write_bf16(sc.cache, torch.from_numpy(wdst).to(device),
+                      to_dev_bf16(newk).view(torch.int16), to_dev_bf16(newv).view(torch.int16))
+        sc.commit_step()
+        sc.sync_lengths()
+        args = sc.decode_args(kv_head_of_q=head_map, num_splits=num_splits, int2_kernel=int2_kernel)
+        q = to_dev_bf16(inp.q[st])
+        ob.decode(sc.cache, args, q.view(torch.int16), Rk, Rv, out, lse)
+    torch.cuda.synchronize()
+    return DeviceRun(sc, out.cpu().numpy(), lse.cpu().numpy(), sc.cache.int2.cpu().numpy(),
+                     sc.hist_len_h.copy())
+
+
+def oracle_step(inp: synth.SmallInputs, steps: int = 1, R_v_none=False, head_map=None,
+                seqs=None, heads=None):
+    """Oracle view after `steps` decode steps: history quantised from the
+    original tokens, BF16 = sink + current recent window.  Returns per sequence
+    (out [Hq][D], lse [Hq], quantised history dict)."""
+    wl = inp.wl
+    D, G = wl.D, wl.G
+    hm = np.array(head_map) if head_map is not None else orc.default_head_map(wl.Hq, wl.Hkv)
+    res = {}
+    for b in (range(wl.B) if seqs is None else seqs):
+        L = wl.lengths[b] + steps
+        s, h, r = synth.split_lengths(L)
+        K = synth.bf16_bits_to_f64(inp.K[b][:L])
+        V = synth.bf16_bits_to_f64(inp.V[b][:L])
+        kc = np.zeros((h, wl.Hkv, D), np.uint8); vc = np.zeros_like(kc)
+        ks = np.zeros((h, wl.Hkv, D // G)); kz = np.zeros_like(ks); vs = np.zeros_like(ks); vz = np.zeros_like(ks)
+        khat = np.zeros((h, wl.Hkv, D)); vhat = np.zeros_like(khat)
+        for j in range(wl.Hkv):
+            if h == 0:
+                break
+            Rv = np.eye(D) if R_v_none else inp.R_v[j]
+            c1, s1, z1 = orc.quantize_tokens(K[s:s + h, j], inp.R_k[j], G, float(inp.clip_k[j]))
+            c2, s2, z2 = orc.quantize_tokens(V[s:s + h, j], Rv, G, float(inp.clip_v[j]))
+            kc[:, j], ks[:, j], kz[:, j] = c1, s1, z1
+            vc[:, j], vs[:, j], vz[:, j] = c2, s2, z2
+            khat[:, j] = orc.dequant(c1, s1, z1, G)
+            vhat[:, j] = orc.dequant(c2, s2, z2, G)
+        bidx = list(range(0, s)) + list(range(s + h, L))
+        q = synth.bf16_bits_to_f64(inp.q[steps - 1][b])
+        out, lse = orc.decode_attention(q, hm, K[bidx], V[bidx], khat, vhat, inp.R_k,
+                                        None if R_v_none else inp.R_v)
+        res[b] = dict(out=out, lse=lse, h=h, kc=kc, ks=ks, kz=kz, vc=vc, vs=vs, vz=vz)
+    return res
+
+
+def oracle_records(r, D, G, Hkv):
+    """Expected bytes of every history page of one sequence: [pages][Hkv][rec]."""
+    h = r["h"]
+    npg = -(-h // PAGE)
+    rec = orc.record_bytes(D, G)
+    out = np.zeros((npg, Hkv, rec), np.uint8)
+    for p in range(npg):
+        a, e = p * PAGE, min(h, p * PAGE + PAGE)
+        n = e - a
+        for j in range(Hkv):
+            def pad(x, fill_shape):
+                y = np.zeros(fill_shape, dtype=x.dtype)
+                y[:n] = x[a:e, j]
+                return y
+            kc = pad(r["kc"], (PAGE, D)); vc = pad(r["vc"], (PAGE, D))
+            ks = pad(r["ks"], (PAGE, D // G)); kz = pad(r["kz"], (PAGE, D // G))
+            vs = pad(r["vs"], (PAGE, D // G)); vz = pad(r["vz"], (PAGE, D // G))
+            out[p, j] = orc.encode_record(kc, ks, kz, vc, vs, vz, D, G)
+    return out
+
+
+def row_rel_err(got, ref):
+    """max_c |got - ref| / max_c |ref| per row (the last axis)."""
+    den = np.maximum(np.abs(ref).max(axis=-1), 1e-30)
+    return np.abs(got - ref).max(axis=-1) / den

@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/oscar.h declares, and rejects invalid arguments on the host before any
+HIP call (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from int2_rotated_kv_amd import binding as ob
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "oscar.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(oscar_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 7
+    lib = ob.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in ob._SIGS, f"{n} has no binding signature"
+
+
+def test_record_bytes():
+    assert ob.record_bytes(128, 64) == 1280
+    assert ob.record_bytes(128, 128) == 1152
+    assert ob.record_bytes(64, 32) == 768
+    assert ob.record_bytes(100, 64) == 0
+
+
+class _FakeTensor:
+    """Stands in for a device tensor: only a pointer value (never dereferenced,
+    since every call below fails validation before launching anything)."""
+
+    def __init__(self, ptr=0x100000, shape=(1, 64), numel=64):
+        self._p, self.shape, self._n = ptr, shape, numel
+
+    def data_ptr(self):
+        return self._p
+
+    def numel(self):
+        return self._n
+
+    def dim(self):
+        return len(self.shape)
+
+
+def _cache(**kw):
+    c = dict(num_kv_heads=8, head_dim=128, group_size=64, page_size=16, int2_pool=0x10000,
+             num_int2_pages=10, bf16_k_pool=0x20000, bf16_v_pool=0x30000, num_bf16_pages=40)
+    c.update(kw)
+    return ob.OscarCache(**c)
+
+
+def _args(**kw):
+    a = dict(batch=2, num_q_heads=32, kv_head_of_q=None, hist_pages=0x40000, hist_stride=10,
+             hist_len=0x50000, bf16_pages=0x60000, bf16_stride=20, bf16_len=0x70000,
+             max_hist_len=100, sm_scale=0.0, num_splits=0, int2_kernel=0)
+    a.update(kw)
+    return ob.OscarDecodeArgs(**a)
+
+
+def _ws(c, a):
+    out = ctypes.c_size_t(0)
+    st = ob.lib().oscar_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(a), ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_bytes_valid():
+    st, n = _ws(_cache(), _args())
+    assert st == ob.OSCAR_OK and n > 0
+    # more splits -> more workspace
+    st2, n2 = _ws(_cache(), _args(num_splits=7))
+    assert st2 == 0 and n2 > n or n2 >= n
+
+
+@pytest.mark.parametrize("ckw,akw,want", [
+    (dict(page_size=32), {}, ob.OSCAR_EINVAL),
+    (dict(head_dim=96), {}, ob.OSCAR_EUNSUPPORTED),
+    (dict(group_size=48), {}, ob.OSCAR_EUNSUPPORTED),
+    (dict(head_dim=64, group_size=128), {}, ob.OSCAR_EUNSUPPORTED),
+    (dict(num_kv_heads=0), {}, ob.OSCAR_EINVAL),
+    (dict(int2_pool=0x10001), {}, ob.OSCAR_EINVAL),
+    (dict(bf16_v_pool=0), {}, ob.OSCAR_EINVAL),
+    ({}, dict(batch=0), ob.OSCAR_EINVAL),
+    ({}, dict(num_q_heads=30), ob.OSCAR_EINVAL),
+    ({}, dict(num_q_heads=24), ob.OSCAR_EUNSUPPORTED),
+    ({}, dict(max_hist_len=-1), ob.OSCAR_EINVAL),
+    ({}, dict(hist_stride=6), ob.OSCAR_EINVAL),
+    ({}, dict(hist_pages=0), ob.OSCAR_EINVAL),
+    ({}, dict(hist_len=0), ob.OSCAR_EINVAL),
+    ({}, dict(bf16_stride=0), ob.OSCAR_EINVAL),
+    ({}, dict(sm_scale=-1.0), ob.OSCAR_EINVAL),
+    ({}, dict(sm_scale=float("nan")), ob.OSCAR_EINVAL),
+    ({}, dict(num_splits=-2), ob.OSCAR_EINVAL),
+    ({}, dict(int2_kernel=7), ob.OSCAR_EINVAL),
+])
+def test_invalid_arguments_rejected(ckw, akw, want):
+    st, _ = _ws(_cache(**ckw), _args(**akw))
+    assert st == want, ob.last_error()
+    assert ob.last_error() != ""
+
+
+def test_bad_head_map_rejected():
+    m = (ctypes.c_int32 * 32)(*([0] * 5 + list(range(1, 8)) * 3 + [7] * 6))
+    st, _ = _ws(_cache(), _args(kv_head_of_q=ctypes.cast(m, ctypes.c_void_p)))
+    assert st == ob.OSCAR_EINVAL and "KV head" in ob.last_error()
+    m = (ctypes.c_int32 * 32)(*([9] + [0] * 31))
+    st, _ = _ws(_cache(), _args(kv_head_of_q=ctypes.cast(m, ctypes.c_void_p)))
+    assert st == ob.OSCAR_EINVAL
+
+
+def test_calls_fail_before_launch_on_bad_input():
+    lib = ob.lib()
+    c = _cache()
+    a = _args()
+    # workspace too small
+    st = lib.oscar_decode_attn(ctypes.byref(c), ctypes.byref(a), 0x1000, 0x2000, 0x3000, 16, None)
+    assert st == ob.OSCAR_EWORKSPACE
+    st = lib.oscar_merge(ctypes.byref(c), ctypes.byref(a), 0x3000, 16, None, 0x4000, None, None)
+    assert st == ob.OSCAR_EWORKSPACE
+    # unaligned / NULL pointers
+    st = lib.oscar_decode_attn(ctypes.byref(c), ctypes.byref(a), 0x1001, 0x2000, 0x3000, 1 << 30, None)
+    assert st == ob.OSCAR_EINVAL
+    st = lib.oscar_merge(ctypes.byref(c), ctypes.byref(a), 0x3000, 1 << 30, None, None, None, None)
+    assert st == ob.OSCAR_EINVAL
+    # demote: negative count, NULL lists, NULL R_k; n == 0 is a no-op
+    assert lib.oscar_demote_pack(ctypes.byref(c), -1, 1, 1, 1, 1, 1, 1, None) == ob.OSCAR_EINVAL
+    assert lib.oscar_demote_pack(ctypes.byref(c), 4, None, 1, 1, 1, 1, 1, None) == ob.OSCAR_EINVAL
+    assert lib.oscar_demote_pack(ctypes.byref(c), 4, 1, 1, None, 1, 1, 1, None) == ob.OSCAR_EINVAL
+    assert lib.oscar_demote_pack(ctypes.byref(c), 0, None, None, None, None, None, None, None) == ob.OSCAR_OK
+    assert lib.oscar_write_bf16(ctypes.byref(c), 3, None, 1, 1, None) == ob.OSCAR_EINVAL
+    assert lib.oscar_write_bf16(None, 3, 1, 1, 1, None) == ob.OSCAR_EINVAL
+    assert lib.oscar_write_bf16(ctypes.byref(c), 0, None, None, None, None) == ob.OSCAR_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ob, "_LIB", None)
+    monkeypatch.setattr(ob, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        ob.lib()

@@ -1,0 +1,91 @@
+"""GPU parity of the split-cache decode path against the CPU oracle.
+
+Bars: INT2 page bytes (codes, packing, bf16 scale/zero) bit-exact; attention
+outputs within 2e-3 max relative error per row (max |err| / max |ref|)."""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+import split_helpers as sh
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _check_bytes(run, inp, ref):
+    wl = inp.wl
+    for b, r in ref.items():
+        want = sh.oracle_records(r, wl.D, wl.G, wl.Hkv)
+        phys = run.sc.hist_table_h[b, :want.shape[0]]
+        got = run.pool[phys]
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, f"seq {b}: {len(bad)} byte mismatches, first {bad[:5].tolist()}"
+
+
+def _check_out(run, ref, tol=TOL):
+    worst = 0.0
+    for b, r in ref.items():
+        e = sh.row_rel_err(run.out[b].astype(np.float64), r["out"])
+        worst = max(worst, float(e.max()))
+        assert np.all(e <= tol), f"seq {b}: row errors {np.sort(e)[-4:]}"
+        lerr = np.abs(run.lse[b] - r["lse"]).max()
+        assert lerr < 1e-3, f"seq {b}: lse error {lerr}"
+    return worst
+
+
+@pytest.mark.parametrize("kernel", [1])
+def test_tiny_one_step(kernel):
+    _say("case: tiny one step, kernel", kernel)
+    inp = synth.make_small(synth.workload("tiny"))
+    run = sh.build_and_step(inp, steps=1, int2_kernel=kernel)
+    ref = sh.oracle_step(inp, steps=1)
+    _check_bytes(run, inp, ref)
+    w = _check_out(run, ref)
+    _say("tiny worst row rel err", w)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 0])
+def test_tiny_splits_and_rotations(splits):
+    """Different history chunkings, R_v != R_k, and R_v = identity."""
+    _say("case: tiny splits", splits)
+    wl = synth.workload("tiny", B=2, lengths=(1024, 777), steps=2, seed=5)
+    inp = synth.make_small(wl, distinct_rv=True)
+    run = sh.build_and_step(inp, steps=2, int2_kernel=1, num_splits=splits)
+    ref = sh.oracle_step(inp, steps=2)
+    _check_bytes(run, inp, ref)
+    _check_out(run, ref)
+    run = sh.build_and_step(inp, steps=2, int2_kernel=1, num_splits=splits, R_v_none=True)
+    ref = sh.oracle_step(inp, steps=2, R_v_none=True)
+    _check_bytes(run, inp, ref)
+    _check_out(run, ref)
+
+
+def test_edge_lengths_and_head_map():
+    """Sequences with no history, a partial sink, one history token; a
+    non-contiguous GQA head map."""
+    _say("case: edge lengths")
+    wl = synth.workload("tiny", B=5, Hkv=2, Hq=8, lengths=(10, 64, 320, 321, 400), steps=1, seed=6)
+    inp = synth.make_small(wl)
+    hm = [1, 0, 1, 0, 0, 1, 1, 0]
+    run = sh.build_and_step(inp, steps=1, int2_kernel=1, head_map=hm)
+    ref = sh.oracle_step(inp, steps=1, head_map=hm)
+    _check_bytes(run, inp, ref)
+    _check_out(run, ref)
+
+
+def test_qwen3_8b_32k_one_step():
+    """Qwen3-8B-shaped layer at 32K context, every history page and output."""
+    _say("case: qwen3-8b-32k")
+    inp = synth.make_small(synth.workload("qwen3-8b-32k"))
+    run = sh.build_and_step(inp, steps=1, int2_kernel=1)
+    ref = sh.oracle_step(inp, steps=1)
+    _check_bytes(run, inp, ref)
+    w = _check_out(run, ref)
+    _say("32k worst row rel err", w)
