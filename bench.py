@@ -1,0 +1,393 @@
+"""Decode-step benchmark of the split-cache INT2 path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--int2-kernel auto|valu|mfma]
+
+One step = the whole hot path for every sequence of the batch: demote the
+oldest recent token into the INT2 history (oscar_demote_pack), write the new
+token into the freed BF16 slot (oscar_write_bf16), attend both segments
+(oscar_decode_attn: query rotation, BF16 segment, INT2 history chunks) and
+merge (oscar_merge).  Inputs are synthetic and already resident in HBM when
+timing starts.  Prints ONE JSON line.
+
+The default workload is the Qwen3-8B-shaped batch-32 cache at ~100K context
+(8 KV heads, 32 q heads, head_dim 128, INT2 group 64, lengths uniform in
+[90000, 100000]): the largest 100K-context configuration on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PAGE, SINK, RECENT = 16, 64, 256
+HBM_PEAK_GBS = 8000.0
+
+
+# --------------------------------------------------------------------------
+# workload construction (device side, through the library)
+# --------------------------------------------------------------------------
+
+class BenchState:
+    pass
+
+
+def build_workload(name: str, total_steps: int, device="cuda", log=print):
+    """Build the split cache of a 100K-class workload on the device and plan
+    `total_steps` decode steps.  History pages are quantised by
+    oscar_demote_pack from generated BF16 tokens."""
+    import torch
+    from int2_rotated_kv_amd import binding as ob
+    from int2_rotated_kv_amd.splitcache import SplitCache
+
+    wl = synth.workload(name, steps=total_steps)
+    gen = synth.LargeGen(wl, device=device)
+    t0 = time.time()
+    sc = SplitCache(wl.B, wl.Hkv, wl.Hq, wl.D, wl.G, gen.hist_table, gen.n_unique,
+                    staging_pages=synth.LargeGen.PAGES_PER_BLOCK, device=device)
+    Rk = torch.from_numpy(gen.R_k).to(device)
+    Rv = torch.from_numpy(gen.R_v).to(device)
+    ck = torch.from_numpy(gen.clip_k).to(device)
+    cv = torch.from_numpy(gen.clip_v).to(device)
+
+    # unique pages that hold prompt history
+    prompt = np.zeros(gen.n_unique, dtype=bool)
+    for b in range(wl.B):
+        npg = -(-int(gen.hist_len0[b]) // PAGE)
+        prompt[gen.unique_of[b, :npg]] = True
+    ppb = synth.LargeGen.PAGES_PER_BLOCK
+    for blk in range(-(-gen.n_unique // ppb)):
+        us = np.arange(blk * ppb, min((blk + 1) * ppb, gen.n_unique))
+        sel = us[prompt[us]]
+        if sel.size == 0:
+            continue
+        k, v = gen.history_block(blk)
+        k = k.view(ppb, PAGE, wl.Hkv, wl.D)[torch.from_numpy(sel - blk * ppb).to(device)]
+        v = v.view(ppb, PAGE, wl.Hkv, wl.D)[torch.from_numpy(sel - blk * ppb).to(device)]
+        sc.fill_history_pages(gen.phys_of_unique[sel], k.reshape(-1, wl.Hkv, wl.D),
+                              v.reshape(-1, wl.Hkv, wl.D), Rk, Rv, ck, cv)
+    for b in range(wl.B):
+        k, v = gen.bf16_tokens(b)
+        sc.load_bf16(b, k, v)
+    sc.hist_len_h[:] = gen.hist_len0
+    torch.cuda.synchronize()
+    log(f"[bench] built {name}: {gen.n_unique} unique INT2 pages "
+        f"({gen.n_unique * wl.Hkv * sc.cache.rec / 1e9:.2f} GB) in {time.time() - t0:.1f}s")
+
+    # plan every step on the host; upload the slot lists and lengths once
+    T = total_steps
+    dsrc = np.zeros((T, wl.B), np.int32)
+    ddst = np.zeros((T, wl.B), np.int32)
+    wdst = np.zeros((T, wl.B), np.int32)
+    hl = np.zeros((T, wl.B), np.int32)
+    bl = np.zeros((T, wl.B), np.int32)
+    h0 = sc.hist_len_h.copy()
+    b0 = sc.bf16_len_h.copy()
+    r0 = sc.ring_head.copy()
+    for s in range(T):
+        a, d, w = sc.plan_step()
+        sc.commit_step()
+        dsrc[s], ddst[s], wdst[s] = a, d, w
+        hl[s], bl[s] = sc.hist_len_h, sc.bf16_len_h
+    sc.hist_len_h[:], sc.bf16_len_h[:], sc.ring_head[:] = h0, b0, r0
+    st = BenchState()
+    st.wl, st.gen, st.sc = wl, gen, sc
+    st.Rk, st.Rv, st.ck, st.cv = Rk, Rv, ck, cv
+    dev = lambda x: torch.from_numpy(x).to(device)
+    st.dsrc, st.ddst, st.wdst, st.hl, st.bl = dev(dsrc), dev(ddst), dev(wdst), dev(hl), dev(bl)
+    st.hl_h, st.bl_h = hl, bl
+    toks = [gen.step_tokens(s) for s in range(T)]
+    st.knew = torch.stack([t[0] for t in toks]).view(torch.int16)
+    st.vnew = torch.stack([t[1] for t in toks]).view(torch.int16)
+    st.q = torch.stack([t[2] for t in toks]).view(torch.int16)
+    return st
+
+
+def step_args(st, s: int, int2_kernel: int):
+    from int2_rotated_kv_amd import binding as ob
+    return ob.DecodeArgs(st.wl.B, st.wl.Hq, st.sc.hist_pages, st.hl[s], st.sc.bf16_pages, st.bl[s],
+                         int(st.hl_h[s].max()), int2_kernel=int2_kernel)
+
+
+def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False):
+    import torch
+    from int2_rotated_kv_amd import binding as ob
+    T = steps + warmup
+    args = [step_args(st, s, int2_kernel) for s in range(T)]
+    a_qb = [a.with_phases(ob.PHASE_QROT | ob.PHASE_BF16) for a in args]
+    a_i2 = [a.with_phases(ob.PHASE_INT2) for a in args]
+    ws = ob.alloc_workspace(st.sc.cache, args[-1])
+    wl = st.wl
+    out = torch.zeros((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=st.q.device)
+    lse = torch.zeros((wl.B, wl.Hq), dtype=torch.float32, device=st.q.device)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    first_out = None
+    cache = st.sc.cache
+
+    def one(s, e=None):
+        if e: e[0].record()
+        ob.demote_pack(cache, st.dsrc[s], st.ddst[s], st.Rk, st.Rv, st.ck, st.cv)
+        ob.write_bf16(cache, st.wdst[s], st.knew[s], st.vnew[s])
+        if e: e[1].record()
+        ob.decode_attn(cache, a_qb[s], st.q[s], st.Rk, ws)
+        if e: e[2].record()
+        ob.decode_attn(cache, a_i2[s], st.q[s], st.Rk, ws)
+        if e: e[3].record()
+        ob.merge(cache, args[s], ws, st.Rv, out, lse)
+        if e: e[4].record()
+
+    for s in range(warmup):
+        one(s)
+        if s == 0 and keep_first_out:
+            torch.cuda.synchronize()
+            first_out = (out.cpu().numpy().copy(), lse.cpu().numpy().copy())
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one(warmup + i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    seg = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in ev])  # ms
+    return dict(wall_s=wall, seg_ms=seg, first_out=first_out, out=out, args=args)
+
+
+# --------------------------------------------------------------------------
+# byte accounting (algorithmic: what the method must move)
+# --------------------------------------------------------------------------
+
+def hist_bytes_per_token_head(D, G):
+    return 2 * (D // 4) + 2 * (D // G) * 4
+
+
+def int2_alg_bytes(wl, hl_row, splits):
+    units = int(hl_row.sum()) * wl.Hkv
+    pages = int(sum(-(-int(h) // PAGE) for h in hl_row))
+    return (units * hist_bytes_per_token_head(wl.D, wl.G) + pages * 4
+            + wl.B * wl.Hq * wl.D * 4 + wl.B * wl.Hq * splits * (wl.D + 2) * 4), units
+
+
+def step_alg_bytes(wl, hl_row, bl_row, splits):
+    i2, _ = int2_alg_bytes(wl, hl_row, splits)
+    bf = int(bl_row.sum()) * wl.Hkv * wl.D * 2 * 2
+    demote = wl.B * wl.Hkv * 2 * (wl.D * 2 + wl.D // 4 + (wl.D // wl.G) * 4)
+    write = wl.B * wl.Hkv * 2 * wl.D * 2 * 2
+    merge = wl.B * wl.Hq * (splits * (wl.D + 2) * 4 + (wl.D + 2) * 4 + wl.D * 4)
+    q = wl.B * wl.Hq * wl.D * 2 * 2
+    return i2 + bf + demote + write + merge + q
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle, timed on this host
+# --------------------------------------------------------------------------
+
+def cpu_baseline(st, first_out, budget_s=12.0, max_seqs=4, log=print):
+    """Time the CPU oracle on the first decode step of a few sequences: unpack
+    every INT2 page record of the sequence, dequantise, quantise the demoted
+    token, and attend all q heads over the split cache.  The oracle's records
+    come from its own quantisation of the generated tokens.  Returns the
+    baseline dict and the oracle-vs-GPU error of the sampled sequences."""
+    import torch
+    from oracle import oscar_oracle as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    wl, gen = st.wl, st.gen
+    D, G, Hkv, g = wl.D, wl.G, wl.Hkv, wl.g
+    ppb = synth.LargeGen.PAGES_PER_BLOCK
+    knew0, vnew0, q0 = gen.step_tokens(0)
+    timed, units, worst = 0.0, 0, 0.0
+    seqs = 0
+    for b in range(wl.B):
+        if seqs >= max_seqs or (seqs > 0 and timed >= budget_s):
+            break
+        hl0 = int(gen.hist_len0[b])
+        npg = -(-hl0 // PAGE)
+        us = gen.unique_of[b, :npg]
+        blocks = {}
+        kh = np.empty((npg * PAGE, Hkv, D), np.uint16)
+        vh = np.empty_like(kh)
+        for i, u in enumerate(us):
+            blk = int(u) // ppb
+            if blk not in blocks:
+                blocks.clear()
+                k, v = gen.history_block(blk)
+                blocks[blk] = (k.view(torch.int16).cpu().numpy().view(np.uint16),
+                               v.view(torch.int16).cpu().numpy().view(np.uint16))
+            k, v = blocks[blk]
+            o = (int(u) % ppb) * PAGE
+            kh[i * PAGE:(i + 1) * PAGE] = k[o:o + PAGE]
+            vh[i * PAGE:(i + 1) * PAGE] = v[o:o + PAGE]
+        kh, vh = kh[:hl0], vh[:hl0]
+        kb, vb = gen.bf16_tokens(b)
+        kb = kb.view(torch.int16).cpu().numpy().view(np.uint16)
+        vb = vb.view(torch.int16).cpu().numpy().view(np.uint16)
+        # after step 0: token 64 (oldest recent) is demoted, the new token appended
+        dem_k, dem_v = kb[SINK], vb[SINK]
+        bf_k = np.concatenate([kb[:SINK], kb[SINK + 1:], knew0[b:b + 1].view(torch.int16).cpu().numpy().view(np.uint16)])
+        bf_v = np.concatenate([vb[:SINK], vb[SINK + 1:], vnew0[b:b + 1].view(torch.int16).cpu().numpy().view(np.uint16)])
+        q = synth.bf16_bits_to_f64(q0[b].view(torch.int16).cpu().numpy().view(np.uint16))
+        out_ref = np.zeros((wl.Hq, D))
+        for j in range(Hkv):
+            # oracle-side cache: records of its own quantisation (setup, untimed)
+            K = synth.bf16_bits_to_f64(kh[:, j])
+            V = synth.bf16_bits_to_f64(vh[:, j])
+            kc, ks, kz = orc.quantize_tokens(K, gen.R_k[j], G, float(gen.clip_k[j]))
+            vc, vs, vz = orc.quantize_tokens(V, gen.R_v[j], G, float(gen.clip_v[j]))
+            recs = []
+            for p in range(npg):
+                a, e = p * PAGE, min(hl0, p * PAGE + PAGE)
+                pad = lambda x, w: np.concatenate([x[a:e], np.zeros((PAGE - (e - a), w), x.dtype)])
+                recs.append(orc.encode_record(pad(kc, D), pad(ks, D // G), pad(kz, D // G),
+                                              pad(vc, D), pad(vs, D // G), pad(vz, D // G), D, G))
+            heads = [h for h in range(wl.Hq) if h // g == j]
+            t0 = time.perf_counter()
+            # --- timed: one decode step of this (sequence, KV head) ---
+            dk = orc.quantize_tokens(synth.bf16_bits_to_f64(dem_k[j])[None], gen.R_k[j], G, float(gen.clip_k[j]))
+            dv = orc.quantize_tokens(synth.bf16_bits_to_f64(dem_v[j])[None], gen.R_v[j], G, float(gen.clip_v[j]))
+            parts = [orc.decode_record(r, D, G) for r in recs]
+            khat = np.concatenate([orc.dequant(p_[0], p_[1], p_[2], G) for p_ in parts])[:hl0]
+            vhat = np.concatenate([orc.dequant(p_[3], p_[4], p_[5], G) for p_ in parts])[:hl0]
+            khat = np.concatenate([khat, orc.dequant(*dk, G)])
+            vhat = np.concatenate([vhat, orc.dequant(*dv, G)])
+            o, _ = orc.decode_attention(q[heads], np.zeros(len(heads), int),
+                                        synth.bf16_bits_to_f64(bf_k[:, j])[:, None],
+                                        synth.bf16_bits_to_f64(bf_v[:, j])[:, None],
+                                        khat[:, None], vhat[:, None], gen.R_k[j:j + 1], gen.R_v[j:j + 1])
+            timed += time.perf_counter() - t0
+            out_ref[heads] = o
+        units += (hl0 + 1 + SINK + RECENT) * Hkv
+        seqs += 1
+        if first_out is not None:
+            got = first_out[0][b].astype(np.float64)
+            den = np.maximum(np.abs(out_ref).max(axis=1), 1e-30)
+            worst = max(worst, float((np.abs(got - out_ref).max(axis=1) / den).max()))
+        log(f"[bench] cpu oracle: sequence {b} done, {timed:.1f}s timed so far")
+    return dict(value=units / timed, unit="KV-token-heads/s", cores=int(blas_threads), kind="oracle",
+                sample=f"first decode step of {seqs} of {wl.B} sequences (all {Hkv} KV heads, "
+                       f"{wl.Hq} q heads): unpack + dequantise every INT2 record, quantise the "
+                       f"demoted token, fp64 attention; {timed:.1f}s timed",
+                seconds=timed), worst
+
+
+# --------------------------------------------------------------------------
+
+def traffic_from_profile(kernel_name: str):
+    """HBM bytes per dispatch of `kernel_name` from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel_name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "int2_rotated_kv_amd", "csrc", kv.get("source", ""))
+    if not os.path.exists(src):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if sha != kv.get("source_sha256_16"):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3-8b-b32-100k")
+    ap.add_argument("--int2-kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run 5 plain device-to-device copies of BYTES bytes (the "
+                         "reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE) and exit")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {a.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from int2_rotated_kv_amd import binding as ob
+
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+    if a.calibrate_copy:
+        src = torch.ones(a.calibrate_copy, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {a.calibrate_copy} bytes 5 times")
+        return
+    kern = {"auto": ob.INT2_AUTO, "valu": ob.INT2_VALU, "mfma": ob.INT2_MFMA}[a.int2_kernel]
+    torch.cuda.set_device(0)
+    st = build_workload(a.workload, a.steps + a.warmup, log=log)
+    wl = st.wl
+    r = run_steps(st, a.steps, a.warmup, kern, keep_first_out=not a.no_cpu_baseline)
+    log(f"[bench] timed {a.steps} steps in {r['wall_s']:.3f}s")
+
+    # per-step quantities over the timed steps
+    timed = range(a.warmup, a.warmup + a.steps)
+    ms_step = 1000.0 * r["wall_s"] / a.steps
+    kvth = np.mean([int(st.hl_h[s].sum() + st.bl_h[s].sum()) * wl.Hkv for s in timed])
+    splits = ob.decode_plan(st.sc.cache, r["args"][a.warmup])[0]
+    step_bytes = np.mean([step_alg_bytes(wl, st.hl_h[s], st.bl_h[s], splits) for s in timed])
+    i2_bytes = np.mean([int2_alg_bytes(wl, st.hl_h[s], splits)[0] for s in timed])
+    seg = r["seg_ms"]
+    int2_ms = float(seg[:, 2].mean())
+    achieved = i2_bytes / (int2_ms * 1e-3) / 1e9
+    kname = "k_int2_mfma" if kern == ob.INT2_MFMA else "k_int2_valu"
+    tr = traffic_from_profile(kname)
+    out = {
+        "metric": "decode attention: KV-tokens·heads/s and achieved HBM TB/s (% of peak) at 100K ctx",
+        "value": kvth / (ms_step * 1e-3),
+        "unit": "KV-token-heads/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "kv_heads": wl.Hkv, "q_heads": wl.Hq,
+                   "head_dim": wl.D, "group": wl.G, "mean_context": float(np.mean(wl.lengths)),
+                   "sink": SINK, "recent": RECENT, "page": PAGE, "int2_kernel": kname,
+                   "splits": splits, "parallelism": "single-gpu"},
+        "hbm_tbps": step_bytes / (ms_step * 1e-3) / 1e12,
+        "hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "step_ms_breakdown": {"demote+write": float(seg[:, 0].mean()), "qrot+bf16": float(seg[:, 1].mean()),
+                              "int2": int2_ms, "merge": float(seg[:, 3].mean())},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": tr, "kernel": kname,
+                     "alg_bytes_per_launch": i2_bytes},
+    }
+    if not a.no_cpu_baseline:
+        cb, worst = cpu_baseline(st, r["first_out"], budget_s=a.cpu_budget, log=log)
+        out["cpu_baseline"] = cb
+        out["sampled_parity_max_rel_err"] = worst
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -71,6 +71,14 @@ enum {
   OSCAR_MAX_Q_HEADS = 256
 };
 
+/* Parts of oscar_decode_attn (bit mask). */
+enum {
+  OSCAR_PHASE_QROT = 1,     /* q . R_k into the workspace                        */
+  OSCAR_PHASE_BF16 = 2,     /* BF16 sink/recent segment partial                  */
+  OSCAR_PHASE_INT2 = 4,     /* INT2 history chunk partials                       */
+  OSCAR_PHASE_ALL = 7
+};
+
 /* Which kernel computes the INT2 segment. */
 enum {
   OSCAR_INT2_AUTO = 0,
@@ -110,6 +118,11 @@ typedef struct {
   float sm_scale;            /* softmax scale; 0 means 1/sqrt(D)                */
   int32_t num_splits;        /* history chunks per (sequence, KV head); 0 = auto */
   int32_t int2_kernel;       /* OSCAR_INT2_AUTO / _VALU / _MFMA                  */
+  uint32_t phases;           /* oscar_decode_attn work: OR of OSCAR_PHASE_*; 0 means
+                                all.  Phases may be issued in separate calls (e.g.
+                                on two streams or between timing events); the
+                                INT2 phase reads the rotated query that the QROT
+                                phase writes into the workspace                 */
 } oscar_decode_args;
 
 /* Bytes of one INT2 page record: 2*16*(D/4) + 2*16*(D/G)*4. */
@@ -153,6 +166,16 @@ int oscar_demote_pack(const oscar_cache *cache, int32_t n, const int32_t *src_sl
 /* Workspace bytes oscar_decode_attn needs for these arguments (host only). */
 int oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_args *args,
                                  size_t *bytes);
+
+/*
+ * oscar_decode_plan - the history chunking oscar_decode_attn will use for these
+ * arguments (host only): num_splits chunks of pages_per_split pages per
+ * (sequence, KV head), and the workspace size.  Any output may be NULL.
+ * Automatic chunking (num_splits == 0) aims at 2048 blocks in flight while
+ * keeping every chunk at least 50x the bytes of its partial result.
+ */
+int oscar_decode_plan(const oscar_cache *cache, const oscar_decode_args *args,
+                      int32_t *num_splits, int32_t *pages_per_split, size_t *workspace_bytes);
 
 /*
  * oscar_decode_attn - attend every q head over both segments, producing partial

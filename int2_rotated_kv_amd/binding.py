@@ -21,6 +21,7 @@ OSCAR_EWORKSPACE = -3
 OSCAR_EHIP = -4
 
 INT2_AUTO, INT2_VALU, INT2_MFMA = 0, 1, 2
+PHASE_QROT, PHASE_BF16, PHASE_INT2, PHASE_ALL = 1, 2, 4, 7
 PAGE = 16
 SINK, RECENT = 64, 256
 MAX_BF16 = SINK + RECENT
@@ -57,6 +58,7 @@ class OscarDecodeArgs(ctypes.Structure):
         ("sm_scale", ctypes.c_float),
         ("num_splits", ctypes.c_int32),
         ("int2_kernel", ctypes.c_int32),
+        ("phases", ctypes.c_uint32),
     ]
 
 
@@ -80,6 +82,9 @@ _SIGS = {
     "oscar_decode_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(OscarCache),
                                                     ctypes.POINTER(OscarDecodeArgs),
                                                     ctypes.POINTER(ctypes.c_size_t)]),
+    "oscar_decode_plan": (ctypes.c_int, [ctypes.POINTER(OscarCache), ctypes.POINTER(OscarDecodeArgs),
+                                         ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                         ctypes.POINTER(ctypes.c_size_t)]),
     "oscar_decode_attn": (ctypes.c_int, [ctypes.POINTER(OscarCache), ctypes.POINTER(OscarDecodeArgs),
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]),
@@ -181,7 +186,8 @@ class DecodeArgs:
     """Host-side holder of oscar_decode_args plus the tensors it points at."""
 
     def __init__(self, batch, num_q_heads, hist_pages, hist_len, bf16_pages, bf16_len,
-                 max_hist_len, kv_head_of_q=None, sm_scale=0.0, num_splits=0, int2_kernel=INT2_AUTO):
+                 max_hist_len, kv_head_of_q=None, sm_scale=0.0, num_splits=0, int2_kernel=INT2_AUTO,
+                 phases=0):
         self.hist_pages, self.hist_len = hist_pages, hist_len
         self.bf16_pages, self.bf16_len = bf16_pages, bf16_len
         self._map = None
@@ -192,7 +198,15 @@ class DecodeArgs:
             _ptr(hist_pages) if hist_pages is not None and hist_pages.numel() else None,
             int(hist_pages.shape[1]) if hist_pages is not None and hist_pages.dim() == 2 else 0,
             _ptr(hist_len), _ptr(bf16_pages), int(bf16_pages.shape[1]), _ptr(bf16_len),
-            int(max_hist_len), float(sm_scale), int(num_splits), int(int2_kernel))
+            int(max_hist_len), float(sm_scale), int(num_splits), int(int2_kernel), int(phases))
+
+    def with_phases(self, phases: int) -> "DecodeArgs":
+        """A copy of these arguments restricted to some oscar_decode_attn phases."""
+        other = object.__new__(DecodeArgs)
+        other.__dict__.update(self.__dict__)
+        other.c = OscarDecodeArgs.from_buffer_copy(self.c)
+        other.c.phases = int(phases)
+        return other
 
 
 def workspace_bytes(cache: Cache, args: DecodeArgs) -> int:
@@ -200,6 +214,15 @@ def workspace_bytes(cache: Cache, args: DecodeArgs) -> int:
     out = ctypes.c_size_t(0)
     check(lib().oscar_decode_workspace_bytes(ctypes.byref(d), ctypes.byref(args.c), ctypes.byref(out)))
     return int(out.value)
+
+
+def decode_plan(cache: Cache, args: DecodeArgs):
+    """(num_splits, pages_per_split, workspace_bytes) oscar_decode_attn will use."""
+    d = cache.desc()
+    s, p, w = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_size_t(0)
+    check(lib().oscar_decode_plan(ctypes.byref(d), ctypes.byref(args.c), ctypes.byref(s),
+                                  ctypes.byref(p), ctypes.byref(w)))
+    return int(s.value), int(p.value), int(w.value)
 
 
 def alloc_workspace(cache: Cache, args: DecodeArgs, device="cuda"):

@@ -107,6 +107,7 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   if (a->num_splits < 0) return fail(OSCAR_EINVAL, "num_splits < 0");
   if (a->int2_kernel < OSCAR_INT2_AUTO || a->int2_kernel > OSCAR_INT2_MFMA)
     return fail(OSCAR_EINVAL, "int2_kernel must be 0, 1 or 2");
+  if (a->phases & ~(uint32_t)OSCAR_PHASE_ALL) return fail(OSCAR_EINVAL, "unknown phase bits");
 
   p->B = a->batch;
   p->Hq = a->num_q_heads;
@@ -224,6 +225,17 @@ int oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_ar
   return OSCAR_OK;
 }
 
+int oscar_decode_plan(const oscar_cache *cache, const oscar_decode_args *args,
+                      int32_t *num_splits, int32_t *pages_per_split, size_t *workspace_bytes) {
+  DecodeParams p{};
+  int st = check_args(cache, args, &p);
+  if (st) return st;
+  if (num_splits) *num_splits = p.splits;
+  if (pages_per_split) *pages_per_split = p.pages_per_split;
+  if (workspace_bytes) *workspace_bytes = p.L.total;
+  return OSCAR_OK;
+}
+
 int oscar_decode_attn(const oscar_cache *cache, const oscar_decode_args *args, const uint16_t *q,
                       const float *R_k, void *workspace, size_t workspace_bytes, void *stream) {
   DecodeParams p{};
@@ -238,11 +250,17 @@ int oscar_decode_attn(const oscar_cache *cache, const oscar_decode_args *args, c
                 p.L.total);
   p.ws = static_cast<uint8_t *>(workspace);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_qrot(p, q, R_k, s);
-  if (e != hipSuccess) return hip_fail(e, "q rotation launch");
-  e = launch_bf16_seg(p, q, s);
-  if (e != hipSuccess) return hip_fail(e, "BF16 segment launch");
-  if (args->max_hist_len > 0) {
+  const uint32_t ph = args->phases ? args->phases : (uint32_t)OSCAR_PHASE_ALL;
+  hipError_t e = hipSuccess;
+  if (ph & OSCAR_PHASE_QROT) {
+    e = launch_qrot(p, q, R_k, s);
+    if (e != hipSuccess) return hip_fail(e, "q rotation launch");
+  }
+  if (ph & OSCAR_PHASE_BF16) {
+    e = launch_bf16_seg(p, q, s);
+    if (e != hipSuccess) return hip_fail(e, "BF16 segment launch");
+  }
+  if ((ph & OSCAR_PHASE_INT2) && args->max_hist_len > 0) {
     const int kind = args->int2_kernel == OSCAR_INT2_AUTO ? OSCAR_INT2_VALU : args->int2_kernel;
     if (kind == OSCAR_INT2_MFMA)
       return fail(OSCAR_EUNSUPPORTED, "the matrix-core INT2 kernel is not built in this library");

@@ -50,6 +50,9 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
                                              const float *__restrict__ Rv,
                                              const float *__restrict__ clip_k,
                                              const float *__restrict__ clip_v) {
+  // every fp64 operation below is rounded on its own, as specified: no fusion
+  // of the clip products into the subtraction
+#pragma clang fp contract(off)
   constexpr int T = 16;
   constexpr RecLayout RL(D, G);
   constexpr int GW = G < 64 ? G : 64;       // lanes of a group inside one wave
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
   const bool isv = blockIdx.z != 0;
   const int e0 = blockIdx.x * T;
 
-  __shared__ double xs[T][D];
+  __shared__ __align__(16) double xs[T][D];
   __shared__ int s_src[T], s_dst[T];
   __shared__ double red_mx[2][T], red_mn[2][T];
 
@@ -94,10 +97,14 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
     R += (size_t)j * D * D;
 #pragma unroll
     for (int t = 0; t < T; ++t) x[t] = 0.0;
-    for (int i = 0; i < D; ++i) {
-      const double r = (double)R[(size_t)i * D + c];
+    for (int i = 0; i < D; i += 2) {
+      const double r0 = (double)R[(size_t)i * D + c];
+      const double r1 = (double)R[(size_t)(i + 1) * D + c];
 #pragma unroll
-      for (int t = 0; t < T; ++t) x[t] = fma(xs[t][i], r, x[t]);
+      for (int t = 0; t < T; ++t) {
+        const double2 kk = *reinterpret_cast<const double2 *>(&xs[t][i]);
+        x[t] = fma(kk.y, r1, fma(kk.x, r0, x[t]));
+      }
     }
   } else {
 #pragma unroll

@@ -61,7 +61,7 @@ def _cache(**kw):
 def _args(**kw):
     a = dict(batch=2, num_q_heads=32, kv_head_of_q=None, hist_pages=0x40000, hist_stride=10,
              hist_len=0x50000, bf16_pages=0x60000, bf16_stride=20, bf16_len=0x70000,
-             max_hist_len=100, sm_scale=0.0, num_splits=0, int2_kernel=0)
+             max_hist_len=100, sm_scale=0.0, num_splits=0, int2_kernel=0, phases=0)
     a.update(kw)
     return ob.OscarDecodeArgs(**a)
 
@@ -100,6 +100,7 @@ def test_workspace_bytes_valid():
     ({}, dict(sm_scale=float("nan")), ob.OSCAR_EINVAL),
     ({}, dict(num_splits=-2), ob.OSCAR_EINVAL),
     ({}, dict(int2_kernel=7), ob.OSCAR_EINVAL),
+    ({}, dict(phases=8), ob.OSCAR_EINVAL),
 ])
 def test_invalid_arguments_rejected(ckw, akw, want):
     st, _ = _ws(_cache(**ckw), _args(**akw))
