@@ -284,20 +284,22 @@ def cpu_baseline(st, first_out, budget_s=12.0, max_seqs=4, log=print):
 
 # --------------------------------------------------------------------------
 
-def traffic_from_profile(kernel_name: str):
-    """HBM bytes per dispatch of `kernel_name` from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
+def traffic_from_profile(kernel_name: str, workload: str):
+    """HBM bytes per dispatch of `kernel_name` on `workload` from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by what
+    the counter reads for a plain 1 GiB copy), or None when there is none or it
+    was taken on a different version of the kernel's source."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{kernel_name}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel_name}_{workload}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "int2_rotated_kv_amd", "csrc", kv.get("source", ""))
-    if not os.path.exists(src):
+            kv[k.strip()] = v.strip().split()[0] if v.strip() else ""
+    src = os.path.join(ROOT, "int2_rotated_kv_amd", "csrc", kv.get("source", "-"))
+    if kv.get("workload") != workload or not os.path.isfile(src):
         return None
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     if sha != kv.get("source_sha256_16"):
@@ -355,7 +357,7 @@ def main(argv=None):
     int2_ms = float(seg[:, 2].mean())
     achieved = i2_bytes / (int2_ms * 1e-3) / 1e9
     kname = "k_int2_mfma" if kern == ob.INT2_MFMA else "k_int2_valu"
-    tr = traffic_from_profile(kname)
+    tr = traffic_from_profile(kname, wl.name)
     out = {
         "metric": "decode attention: KV-tokens·heads/s and achieved HBM TB/s (% of peak) at 100K ctx",
         "value": kvth / (ms_step * 1e-3),
