@@ -36,9 +36,11 @@
  * Cache layout (HBM)
  *   INT2 history pool: uint8 [num_int2_pages][Hkv][oscar_record_bytes(D, G)].
  *   One record holds 16 tokens of one KV head:
- *     K codes   [16][D/4]      token-major, 4 codes per byte, channel c in bits
- *                              2*(c%4) of byte c/4 (LSB first)
- *     V codes   [D][4]         channel-major, token t in bits 2*(t%4) of byte t/4
+ *     K codes   [16][D/16]     per token D/16 little-endian 32-bit words; word
+ *                              kb*(D/64) + blk holds channels 64*blk + 16*kb + i
+ *                              in bits 2i (i = 0..15): 4 codes per byte
+ *     V codes   [D]            one 32-bit word per channel, token t in bits 2t;
+ *                              channel 16*nb + n stored at word n*(D/16) + nb
  *     K (s, z)  [16][D/G][2]   bf16 scale, bf16 zero per (token, group)
  *     V (s, z)  [16][D/G][2]
  *   Codes are in {0,1,2,3}; the dequantised rotated value is code*scale + zero.

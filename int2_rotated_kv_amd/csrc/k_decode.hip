@@ -170,10 +170,10 @@ hipError_t launch_bf16_seg(const DecodeParams &p, const uint16_t *q, hipStream_t
 // INT2 history segment, vector-ALU variant.  One block (4 waves) per
 // (sequence, KV head, chunk of pages); each wave walks every 4th page of the
 // chunk.  Per page (16 tokens):
-//   QK:  lane (t = lane%16, part = lane/16) dots q_rot with the codes of token
-//        t's channel quarter `part`, then applies that group's scale/zero:
-//        s_part = scale * sum(q*code) + zero * sum(q); the four quarters are
-//        summed across lanes.
+//   QK:  lane (t = lane%16, part = lane/16) takes K words part*KW .. +KW-1 of
+//        token t (16 channels each), dots them with q_rot and applies each
+//        word's group scale/zero: s = scale * sum(q*code) + zero * sum(q); the
+//        four parts are summed across lanes.
 //   softmax: running max per head over the 16 token lanes; p = 2^(s - m).
 //   PV:  lane owns channels lane + 64k and accumulates
 //        sum_t (p*scale_v) * code_v; the zero-point part sum_t p*zero_v depends
@@ -182,11 +182,11 @@ hipError_t launch_bf16_seg(const DecodeParams &p, const uint16_t *q, hipStream_t
 template <int D, int G, int GQ>
 __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
   constexpr RecLayout RL(D, G);
-  constexpr int NG = D / G;       // groups per token
-  constexpr int PART = D / 4;     // channels per QK quarter
+  constexpr int NG = D / G;       // groups per token (<= 4)
+  constexpr int NBLK = D / 64;    // 64-channel blocks per token
+  constexpr int KW = D / 64;      // K words per QK lane (D/16 words over 4 parts)
   constexpr int CPL = D / 64;     // PV channels per lane
-  constexpr int KW = D / 64;      // K-code dwords per QK lane
-  static_assert(PART <= G, "a QK quarter must lie inside one group");
+  static_assert(NG <= 4, "one QK part per group publishes its V scale");
 
   const int S = p.splits;
   const int unit = blockIdx.x / S;
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
   const int t = lane & 15, part = lane >> 4;
 
   __shared__ float qs[D][GQ];                 // q_rot * sm_log2, heads innermost
-  __shared__ float qpart[4][GQ];              // sum of each quarter's q
+  __shared__ float qword[D / 16][GQ];         // sum of q over each K word's 16 channels
   __shared__ float pw[4][NG][16][GQ];         // per wave: p * scale_v per (group, token, head)
   __shared__ float zred[4][NG][GQ];           // per wave: sum_t p * zero_v
   __shared__ float wm[4][GQ], wl[4][GQ];
@@ -210,11 +210,12 @@ __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
     qs[c][h] = qrot[((size_t)b * p.Hq + hq) * D + c] * p.sm_log2;
   }
   __syncthreads();
-  if (tid < 4 * GQ) {
-    const int pt = tid / GQ, h = tid % GQ;
+  if (tid < (D / 16) * GQ) {
+    const int q = tid / GQ, h = tid % GQ;
+    const int c0 = 64 * (q % NBLK) + 16 * (q / NBLK);
     float s = 0.f;
-    for (int i = 0; i < PART; ++i) s += qs[pt * PART + i][h];
-    qpart[pt][h] = s;
+    for (int i = 0; i < 16; ++i) s += qs[c0 + i][h];
+    qword[q][h] = s;
   }
   __syncthreads();
 
@@ -227,7 +228,6 @@ __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
   int p1 = p0 + p.pages_per_split;
   p1 = p1 > npages ? npages : p1;
 
-  const int grp_qk = (part * PART) / G;
   float m[GQ], lsum[GQ], zacc[GQ], o[GQ][CPL];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
@@ -244,35 +244,48 @@ __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
     const uint8_t *rec = p.int2_pool + ((size_t)phys * p.Hkv + j) * RL.bytes();
     const int ntok = hl - pg * kPage < kPage ? hl - pg * kPage : kPage;
 
-    // ---- QK ----
+    // ---- loads ----
     const uint32_t *kr = reinterpret_cast<const uint32_t *>(rec + RL.kcodes() + t * (D / 4)) + part * KW;
     uint32_t kw[KW];
 #pragma unroll
     for (int i = 0; i < KW; ++i) kw[i] = kr[i];
-    const uint32_t ksz = reinterpret_cast<const uint32_t *>(rec + RL.ksz())[t * NG + grp_qk];
-    const uint32_t vszw = reinterpret_cast<const uint32_t *>(rec + RL.vsz())[t * NG + grp_qk];
+    const uint32_t *kszp = reinterpret_cast<const uint32_t *>(rec + RL.ksz()) + t * NG;
+    uint32_t ksz[NG];
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) ksz[g2] = kszp[g2];
+    const uint32_t vszw = part < NG ? reinterpret_cast<const uint32_t *>(rec + RL.vsz())[t * NG + part] : 0u;
     uint32_t vcw[CPL];
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) vcw[k] = reinterpret_cast<const uint32_t *>(rec + RL.vcodes())[lane + 64 * k];
+    for (int k = 0; k < CPL; ++k) {
+      const int c = lane + 64 * k;
+      vcw[k] = reinterpret_cast<const uint32_t *>(rec + RL.vcodes())[(c & 15) * (D / 16) + (c >> 4)];
+    }
 
-    float dot[GQ];
+    // ---- QK ----
+    float sv[GQ];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) dot[h] = 0.f;
+    for (int h = 0; h < GQ; ++h) sv[h] = 0.f;
 #pragma unroll
     for (int i = 0; i < KW; ++i) {
+      const int q = part * KW + i;
+      const int c0 = 64 * (q % NBLK) + 16 * (q / NBLK);
+      const int gq = c0 / G;
+      float dot[GQ];
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) dot[h] = 0.f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const float cf = (float)((kw[i] >> (2 * k)) & 3u);
-        const int c = part * PART + i * 16 + k;
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) dot[h] = fmaf(qs[c][h], cf, dot[h]);
+        for (int h = 0; h < GQ; ++h) dot[h] = fmaf(qs[c0 + k][h], cf, dot[h]);
       }
+      const float ksc = bf16_lo(ksz[gq]), kze = bf16_hi(ksz[gq]);
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) sv[h] += fmaf(ksc, dot[h], kze * qword[q][h]);
     }
-    const float ksc = bf16_lo(ksz), kze = bf16_hi(ksz);
-    float sv[GQ];
 #pragma unroll
     for (int h = 0; h < GQ; ++h) {
-      float v = fmaf(ksc, dot[h], kze * qpart[part][h]);
+      float v = sv[h];
       v += __shfl_xor(v, 16);
       v += __shfl_xor(v, 32);
       sv[h] = t < ntok ? v : -INFINITY;
@@ -296,8 +309,8 @@ __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
       zacc[h] = fmaf(zacc[h], alpha, pr * vze);
 #pragma unroll
       for (int k = 0; k < CPL; ++k) o[h][k] *= alpha;
-      // one lane per (group, token) publishes p * scale_v
-      if ((part * PART) % G == 0) pw[w][grp_qk][t][h] = pr * vsc;
+      // lane (t, part < NG) publishes p * scale_v of group `part`
+      if (part < NG) pw[w][part][t][h] = pr * vsc;
     }
     wave_lds_sync();
 
@@ -326,7 +339,7 @@ __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
       z += __shfl_xor(z, o2);
     }
     lsum[h] = l;
-    if (t == 0 && (part * PART) % G == 0) zred[w][grp_qk][h] = z;
+    if (t == 0 && part < NG) zred[w][part][h] = z;
   }
   wave_lds_sync();
 #pragma unroll

@@ -164,7 +164,10 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
   }
 
   if (!isv) {
-    // K: token-major rows, 16 channels per dword, channel c at bits 2*(c%16)
+    // K: token-major rows of D/16 words; word kb*(D/64) + blk holds channels
+    // 64*blk + 16*kb + i at bits 2i
+    constexpr int NBLK = D / 64;
+    const int kword = ((c & 63) >> 4) * NBLK + (c >> 6);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       uint32_t w = codes[t] << (2 * (c & 15));
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
       if (d >= 0 && (c & 15) == 0) {
         const int64_t page = d >> 4, off = d & 15;
         uint8_t *rec = pool + ((size_t)page * Hkv + j) * RL.bytes();
-        reinterpret_cast<uint32_t *>(rec + RL.kcodes() + off * (D / 4))[c >> 4] = w;
+        reinterpret_cast<uint32_t *>(rec + RL.kcodes() + off * (D / 4))[kword] = w;
       }
     }
   } else {
@@ -198,7 +201,8 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
         }
       }
       uint8_t *rec = pool + ((size_t)page * Hkv + j) * RL.bytes();
-      uint32_t *wp = reinterpret_cast<uint32_t *>(rec + RL.vcodes()) + c;
+      // V word of channel c sits at position (c % 16) * (D/16) + c / 16
+      uint32_t *wp = reinterpret_cast<uint32_t *>(rec + RL.vcodes()) + (c & 15) * (D / 16) + (c >> 4);
       if (mask == 0xFFFFFFFFu) {
         *wp = bits;
       } else {

@@ -214,12 +214,42 @@ def unpack_rows(packed, D: int) -> np.ndarray:
 
 
 def pack_channel_major(codes16) -> np.ndarray:
-    """V-code layout of one 16-token page: for each channel, the 16 tokens' codes
-    in 4 bytes, token t at bits 2*(t%4) of byte t//4 (LSB first).  Input
-    codes [16, D]; output uint8 [D, 4]."""
-    c = np.asarray(codes16, dtype=np.uint8)
+    """V codes of one 16-token page, one 32-bit word per channel: token t's code
+    in bits 2t..2t+1 (LSB first, i.e. 4 codes per byte).  Input codes [16, D];
+    output uint32 [D] indexed by channel."""
+    c = np.asarray(codes16, dtype=np.uint32)
     assert c.shape[0] == 16
-    return pack_rows(c.T)
+    w = np.zeros(c.shape[1], dtype=np.uint32)
+    for t in range(16):
+        w |= c[t] << np.uint32(2 * t)
+    return w
+
+
+def k_row_words(codes_row) -> np.ndarray:
+    """K codes of one token as D/16 32-bit words.  Word q = kb*(D/64) + blk holds
+    channels 64*blk + 16*kb + i in bits 2i (i = 0..15): the row's 16-channel
+    slices taken slice-of-block-major, so that the slices a reader needs for
+    every 64-channel block are adjacent.  For D = 64 this is channel order."""
+    c = np.asarray(codes_row, dtype=np.uint32)
+    D = c.shape[0]
+    nblk = max(1, D // 64)
+    out = np.zeros(D // 16, dtype=np.uint32)
+    for blk in range(nblk):
+        for kb in range(min(4, D // 16)):
+            w = 0
+            for i in range(16):
+                w |= int(c[64 * blk + 16 * kb + i]) << (2 * i)
+            out[kb * nblk + blk] = w
+    return out
+
+
+def v_word_order(D: int) -> np.ndarray:
+    """Channel stored at each V-code word position: position n*(D/16) + nb holds
+    channel 16*nb + n."""
+    pos = np.empty(D, dtype=np.int64)
+    for c in range(D):
+        pos[(c % 16) * (D // 16) + c // 16] = c
+    return pos
 
 
 # ----------------------------------------------------------------------------
@@ -227,20 +257,24 @@ def pack_channel_major(codes16) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def record_bytes(D: int, G: int) -> int:
-    """K codes [16][D/4] | V codes [D][4] | K (scale,zero) [16][D/G][2] bf16 |
-    V (scale,zero) [16][D/G][2] bf16."""
+    """K codes [16][D/16 words] | V codes [D words] | K (scale,zero) [16][D/G][2]
+    bf16 | V (scale,zero) [16][D/G][2] bf16."""
     return 2 * 16 * (D // 4) + 2 * 16 * (D // G) * 4
 
 
 def encode_record(kc, ks, kz, vc, vs, vz, D: int, G: int) -> np.ndarray:
-    """Bytes of one page record from codes [16, D] and bf16 scale/zero [16, D/G]
-    for K and V.  Token rows not yet written are all-zero (pass zeros)."""
+    """Bytes of one page record (16 tokens of one KV head) from codes [16, D]
+    and bf16 scale/zero [16, D/G] for K and V.  Words are little-endian.
+    Token rows not yet written are all-zero (pass zeros)."""
     def sz(s, z):
         sb = f64_to_bf16_bits(s).astype(np.uint16)
         zb = f64_to_bf16_bits(z).astype(np.uint16)
         pair = np.stack([sb, zb], axis=-1)        # [16][D/G][2]
         return pair.astype("<u2").view(np.uint8).reshape(-1)
-    parts = [pack_rows(kc).reshape(-1), pack_channel_major(vc).reshape(-1), sz(ks, kz), sz(vs, vz)]
+    kwords = np.concatenate([k_row_words(kc[t]) for t in range(16)])
+    vwords = pack_channel_major(vc)[v_word_order(D)]
+    parts = [kwords.astype("<u4").view(np.uint8), vwords.astype("<u4").view(np.uint8),
+             sz(ks, kz), sz(vs, vz)]
     out = np.concatenate(parts)
     assert out.size == record_bytes(D, G)
     return out
@@ -249,10 +283,22 @@ def encode_record(kc, ks, kz, vc, vs, vz, D: int, G: int) -> np.ndarray:
 def decode_record(rec, D: int, G: int):
     """Inverse of encode_record: (kc, ks, kz, vc, vs, vz)."""
     rec = np.asarray(rec, dtype=np.uint8)
-    o = 0
-    kc = unpack_rows(rec[o:o + 16 * D // 4].reshape(16, D // 4), D); o += 16 * D // 4
-    vcm = unpack_rows(rec[o:o + 16 * D // 4].reshape(D, 4), 16); o += 16 * D // 4
-    vc = vcm.T.copy()
+    nw = D // 16
+    kw = rec[:16 * nw * 4].view("<u4").reshape(16, nw)
+    o = 16 * nw * 4
+    vw = rec[o:o + D * 4].view("<u4"); o += D * 4
+    nblk = max(1, D // 64)
+    kc = np.zeros((16, D), np.uint8)
+    for kb in range(min(4, nw)):
+        for blk in range(nblk):
+            w = kw[:, kb * nblk + blk]
+            for i in range(16):
+                kc[:, 64 * blk + 16 * kb + i] = (w >> np.uint32(2 * i)) & 3
+    vchan = np.zeros(D, np.uint32)
+    vchan[v_word_order(D)] = vw
+    vc = np.zeros((16, D), np.uint8)
+    for t in range(16):
+        vc[t] = (vchan >> np.uint32(2 * t)) & 3
     ng = D // G
     ksz = rec[o:o + 16 * ng * 4].view("<u2").reshape(16, ng, 2); o += 16 * ng * 4
     vsz = rec[o:o + 16 * ng * 4].view("<u2").reshape(16, ng, 2); o += 16 * ng * 4

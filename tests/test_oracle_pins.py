@@ -223,9 +223,21 @@ def test_pack_exhaustive_roundtrip():
 
 def test_channel_major_layout():
     c = np.zeros((16, 8), dtype=np.uint8)
-    c[5, 2] = 3          # token 5, channel 2 -> channel 2's byte 1, bits 2..3
-    b = orc.pack_channel_major(c)
-    assert b.shape == (8, 4) and b[2, 1] == 3 << 2 and b.sum() == 12
+    c[5, 2] = 3          # token 5, channel 2 -> channel 2's word, bits 10..11
+    w = orc.pack_channel_major(c)
+    assert w.shape == (8,) and w[2] == 3 << 10 and w.sum() == 3 << 10
+    # V words are stored channel 16*nb + n at position n*(D/16) + nb
+    order = orc.v_word_order(128)
+    assert order[9] == 17 and order[0] == 0 and order[1] == 16 and order[8] == 1
+
+
+def test_k_row_word_order():
+    """D = 128: word q = kb*2 + blk holds channels 64*blk + 16*kb .. +15."""
+    row = np.zeros(128, np.uint8)
+    row[70] = 1          # blk 1, kb 0, i 6 -> word 1, bits 12..13
+    row[16] = 3          # blk 0, kb 1, i 0 -> word 2, bits 0..1
+    w = orc.k_row_words(row)
+    assert w[1] == 1 << 12 and w[2] == 3 and w.sum() == (1 << 12) + 3
 
 
 @pytest.mark.parametrize("D,G", [(64, 32), (128, 64), (128, 128)])
@@ -402,22 +414,24 @@ def test_bits_per_element_printed_values():
 
 
 def test_record_layout_hand_placed():
-    """Byte positions of the page-record layout for D=8, G=4 (record = K codes
-    [16][2] | V codes channel-major [8][4] | K (scale,zero) [16][2][2] bf16 |
-    V (scale,zero) [16][2][2] bf16 = 32 + 32 + 128 + 128 bytes)."""
-    D, G = 8, 4
+    """Byte positions of the page-record layout for D=64, G=32 (record = K words
+    [16][4] | V words [64] | K (scale,zero) [16][2][2] bf16 | V (scale,zero)
+    [16][2][2] bf16 = 256 + 256 + 128 + 128 bytes), worked by hand."""
+    D, G = 64, 32
     kc = np.zeros((16, D), np.uint8); vc = np.zeros((16, D), np.uint8)
     ks = np.zeros((16, 2)); kz = np.zeros((16, 2)); vs = np.zeros((16, 2)); vz = np.zeros((16, 2))
-    kc[3, 5] = 2          # token 3, channel 5 -> byte 3*2 + 1, bits 2..3 -> 0x08
-    vc[9, 6] = 3          # token 9, channel 6 -> V block byte 6*4 + 2, bits 2..3 -> 0x0C
-    ks[2, 1] = 1.0        # token 2, group 1 scale -> 0x3F80 at 64 + (2*2+1)*4
+    kc[3, 37] = 2         # token 3, channel 37: word 3*4 + 2, bits 10..11 -> byte 57 = 0x08
+    vc[9, 6] = 3          # channel 6 at word 6*4 + 0 = 24, token 9 bits 18..19 -> byte 256+96+2 = 0x0C
+    vc[0, 17] = 1         # channel 17 at word 1*4 + 1 = 5, token 0 -> byte 256+20 = 0x01
+    ks[2, 1] = 1.0        # K (s, z) of token 2 group 1 at 512 + (2*2+1)*4 -> 0x3F80
     kz[2, 1] = -2.0       # zero -> 0xC000 right after
-    vz[15, 0] = 0.5       # V block: 192 + (15*2+0)*4 + 2 -> 0x3F00
+    vz[15, 0] = 0.5       # V block: 640 + (15*2+0)*4 + 2 -> 0x3F00
     rec = orc.encode_record(kc, ks, kz, vc, vs, vz, D, G)
-    assert rec.size == 320
-    want = np.zeros(320, np.uint8)
-    want[7] = 0x08
-    want[32 + 26] = 0x0C
-    want[64 + 20:64 + 24] = [0x80, 0x3F, 0x00, 0xC0]
-    want[192 + 120 + 2:192 + 120 + 4] = [0x00, 0x3F]
+    assert rec.size == 768
+    want = np.zeros(768, np.uint8)
+    want[57] = 0x08
+    want[256 + 96 + 2] = 0x0C
+    want[256 + 20] = 0x01
+    want[532:536] = [0x80, 0x3F, 0x00, 0xC0]
+    want[640 + 120 + 2:640 + 120 + 4] = [0x00, 0x3F]
     assert np.array_equal(rec, want)
