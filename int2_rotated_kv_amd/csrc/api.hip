@@ -261,10 +261,12 @@ int oscar_decode_attn(const oscar_cache *cache, const oscar_decode_args *args, c
     if (e != hipSuccess) return hip_fail(e, "BF16 segment launch");
   }
   if ((ph & OSCAR_PHASE_INT2) && args->max_hist_len > 0) {
-    const int kind = args->int2_kernel == OSCAR_INT2_AUTO ? OSCAR_INT2_VALU : args->int2_kernel;
-    if (kind == OSCAR_INT2_MFMA)
-      return fail(OSCAR_EUNSUPPORTED, "the matrix-core INT2 kernel is not built in this library");
-    e = launch_int2_valu(p, s);
+    const bool mfma_ok = p.g == 4 || p.g == 8;
+    int kind = args->int2_kernel;
+    if (kind == OSCAR_INT2_AUTO) kind = mfma_ok ? OSCAR_INT2_MFMA : OSCAR_INT2_VALU;
+    if (kind == OSCAR_INT2_MFMA && !mfma_ok)
+      return fail(OSCAR_EUNSUPPORTED, "matrix-core INT2 kernel needs 4 or 8 q heads per KV head (got %d)", p.g);
+    e = kind == OSCAR_INT2_MFMA ? launch_int2_mfma(p, s) : launch_int2_valu(p, s);
     if (e != hipSuccess) return hip_fail(e, "INT2 segment launch");
   }
   return OSCAR_OK;

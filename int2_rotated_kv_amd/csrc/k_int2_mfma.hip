@@ -1,0 +1,445 @@
+// INT2 history segment on the matrix cores (m.th-motor.com repost of the OSCAR
+// article, decode stage: the INT2 kernel unpacks the 2-bit codes, restores
+// scale/zero point and accumulates in floating point).
+//
+// The history is stored as per-token, per-group asymmetric codes:
+//   x_hat[t, c] = code[t, c] * scale[t, g(c)] + zero[t, g(c)],  code in {0..3}.
+// Both contractions of decode attention are split so that the 2-bit codes
+// enter a matrix instruction unchanged and the per-(token, group) scale/zero
+// are applied to its small outputs:
+//
+//   logits  s[h, t] = sum_g scale[t,g] * (q_h . code_t)_g + sum_g zero[t,g] * Q[h,g]
+//     (q_h . code_t)_g on v_mfma_i32_16x16x64_i8: B = codes (exact int8), A = the
+//     rotated query as a 21-bit integer split into three 7-bit pieces, one per
+//     A row; the three int32 results recombine exactly as p0*2^14 + p1*2^7 + p2.
+//   values  o[h, c] = sum_t w[h,t,g(c)] * code[t,c] + sum_t p[h,t] * zero[t,g(c)],
+//           w = p * scale_v
+//     sum_t w * code on v_mfma_f32_16x16x16_f16: B = codes as the exact f16
+//     values 1 + code/4, A = w in f16, fp32 accumulation; the "+1" part is
+//     removed with sum_t w (of the same f16 values).
+//
+// One block (4 waves) per (sequence, KV head, chunk of pages); each wave walks
+// every 4th page of the chunk with the next page's loads in flight, keeping an
+// exact running max per head (16-lane DPP reductions).  Requires 4 or 8 q heads
+// per KV head and V group scales below the f16 range (65504).
+#include "common.hpp"
+
+namespace oscar {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+namespace {
+
+// 16-lane (DPP row) reductions; every lane of the row receives the result.
+__device__ __forceinline__ float dpp_f(float x, int ctrl_id) {
+  const int v = __float_as_int(x);
+  int r;
+  switch (ctrl_id) {
+    case 0: r = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); break;   // quad [1,0,3,2]
+    case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); break;   // quad [2,3,0,1]
+    case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: r = __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); break; // row_mirror
+  }
+  return __int_as_float(r);
+}
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, dpp_f(x, 0));
+  x = fmaxf(x, dpp_f(x, 1));
+  x = fmaxf(x, dpp_f(x, 2));
+  x = fmaxf(x, dpp_f(x, 3));
+  return x;
+}
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp_f(x, 0);
+  x += dpp_f(x, 1);
+  x += dpp_f(x, 2);
+  x += dpp_f(x, 3);
+  return x;
+}
+
+__device__ __forceinline__ v4h as_v4h(uint32_t a, uint32_t b) {
+  v4h r;
+  __builtin_memcpy(&r, &a, 4);
+  __builtin_memcpy(reinterpret_cast<char *>(&r) + 4, &b, 4);
+  return r;
+}
+
+// k-slot order shared by the PV operands: lane group kb, element i <-> token
+// kb + {0, 8, 4, 12}[i]; token t sits in slot 4*(t%4) + e(t/4), e = {0,2,1,3}.
+__device__ __forceinline__ int pv_slot(int t) {
+  const int i = t >> 2;
+  return 4 * (t & 3) + (((i & 1) << 1) | (i >> 1));
+}
+
+template <int NW>
+__device__ __forceinline__ void load_words(uint32_t (&dst)[NW], const uint32_t *src) {
+  if constexpr (NW % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+      const uint4 v = reinterpret_cast<const uint4 *>(src)[i];
+      dst[4 * i] = v.x; dst[4 * i + 1] = v.y; dst[4 * i + 2] = v.z; dst[4 * i + 3] = v.w;
+    }
+  } else if constexpr (NW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(src);
+    dst[0] = v.x; dst[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) dst[i] = src[i];
+  }
+}
+
+}  // namespace
+
+template <int D, int G, int GQ>
+__global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
+  constexpr RecLayout RL(D, G);
+  constexpr int NG = D / G;            // groups per token
+  constexpr int NBLK = D / 64;         // 64-channel blocks (one int8 MFMA K each)
+  constexpr int GPB = G < 64 ? 64 / G : 1;   // groups inside one 64-channel block
+  constexpr int NQK = NBLK * GPB;      // QK MFMAs per head quad per page
+  constexpr int NNB = D / 16;          // 16-channel N blocks of PV
+  constexpr int NQ = GQ / 4;           // head quads
+  static_assert(GQ == 4 || GQ == 8, "4 or 8 q heads per KV head");
+
+  const int S = p.splits;
+  const int unit = blockIdx.x / S;
+  const int split = blockIdx.x % S;
+  const int b = unit / p.Hkv;
+  const int j = unit % p.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, kb = lane >> 4;     // row-in-16 and lane group
+
+  __shared__ float qf[GQ][D];                    // q_rot (unscaled)
+  __shared__ int qexp[GQ];                       // q_int = rint(q * 2^qexp)
+  __shared__ float qz[GQ][NG];                   // sm_log2 * sum of q over the group
+  __shared__ __align__(16) _Float16 wbuf[4][NG][16][16];       // per wave: w[grp][head row][slot]
+  __shared__ float wm[4][GQ], wl[4][GQ];
+  __shared__ float wo[4][GQ][D];
+
+  // ---------------- prologue: query as integer pieces ----------------
+  const float *qrot = reinterpret_cast<const float *>(p.ws + p.L.qrot);
+  for (int i = tid; i < GQ * D; i += 256) {
+    const int h = i / D, c = i % D;
+    qf[h][c] = qrot[((size_t)b * p.Hq + p.q_of_kv[j * GQ + h]) * D + c];
+  }
+  __syncthreads();
+  if (tid < GQ) {
+    float mx = 0.f;
+    for (int c = 0; c < D; ++c) mx = fmaxf(mx, fabsf(qf[tid][c]));
+    int e = 0;
+    if (mx > 0.f) (void)frexpf(mx, &e);          // mx < 2^e
+    int qe = mx > 0.f ? 20 - e : 0;              // |q| * 2^qexp < 2^20
+    qexp[tid] = qe > 126 ? 126 : (qe < -100 ? -100 : qe);
+  }
+  if (tid >= 64 && tid < 64 + GQ * NG) {
+    const int h = (tid - 64) / NG, g2 = (tid - 64) % NG;
+    float s = 0.f;
+    for (int c = g2 * G; c < (g2 + 1) * G; ++c) s += qf[h][c];
+    qz[h][g2] = s * p.sm_log2;
+  }
+  __syncthreads();
+
+  // A operands: row = 4*h + piece (piece 3 is zero), lane group kb, VGPR e,
+  // byte bb <-> channel 64*blk + 16*kb + 4*bb + e (the B unpack order).
+  v4i aq[NQ][NQK];
+  {
+    const int hrow = r16 >> 2, pc = r16 & 3;
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      const int h = qd * 4 + hrow;
+      const float sc = ldexpf(1.f, qexp[h]);
+#pragma unroll
+      for (int m = 0; m < NQK; ++m) {
+        const int blk = m / GPB, gsub = m % GPB;
+        const int g2 = (64 * blk) / G + gsub;
+        int vv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const int c = 64 * blk + 16 * kb + 4 * bb + e;
+            int piece = 0;
+            if (pc < 3 && c / G == g2) {
+              const int qi = (int)rintf(qf[h][c] * sc);
+              piece = pc == 0 ? (qi >> 14) : pc == 1 ? ((qi >> 7) & 127) : (qi & 127);
+            }
+            word |= ((uint32_t)piece & 0xFFu) << (8 * bb);
+          }
+          vv[e] = (int)word;
+        }
+        aq[qd][m] = v4i{vv[0], vv[1], vv[2], vv[3]};
+      }
+    }
+  }
+  // per-lane constants of the (head, token) layout of the QK result
+  float qscale[NQ], qzl[NQ][NG];
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) {
+    const int h = qd * 4 + kb;
+    qscale[qd] = ldexpf(1.f, -qexp[h]) * p.sm_log2;
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) qzl[qd][g2] = qz[h][g2];
+  }
+
+  int hl = p.hist_len[b];
+  hl = hl < 0 ? 0 : hl;
+  hl = hl > p.max_hist_len ? p.max_hist_len : hl;
+  hl = hl > kPage * p.hist_stride ? kPage * p.hist_stride : hl;
+  const int npages = (hl + kPage - 1) / kPage;
+  const int p0 = split * p.pages_per_split;
+  int p1 = p0 + p.pages_per_split;
+  p1 = p1 > npages ? npages : p1;
+
+  // running state; QK layout: lane = (head kb [+4 qd], token r16)
+  float m_run[NQ], lsum[NQ], zacc[NQ][NG];
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) {
+    m_run[qd] = -INFINITY;
+    lsum[qd] = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) zacc[qd][g2] = 0.f;
+  }
+  // PV accumulators: row = head (rows 0..GQ-1 real), column = channel 16*nb + r16
+  v4f acc[NNB];
+#pragma unroll
+  for (int nb = 0; nb < NNB; ++nb) acc[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const uint8_t *pool = p.int2_pool;
+  const int32_t *ptab = p.hist_pages + (size_t)b * p.hist_stride;
+  auto rec_of = [&](int pg) -> const uint8_t * {
+    const int phys = ptab[pg];
+    if (phys < 0 || phys >= p.num_int2_pages) return nullptr;
+    return pool + ((size_t)phys * p.Hkv + j) * RL.bytes();
+  };
+
+  // raw page data of one page for this lane
+  uint32_t kwd[NBLK], ksz[NG], vsz[NG], vwd[NNB];
+  uint32_t nkwd[NBLK], nksz[NG], nvsz[NG], nvwd[NNB];
+  auto load_page = [&](const uint8_t *rec, uint32_t (&k_)[NBLK], uint32_t (&ks_)[NG],
+                       uint32_t (&vs_)[NG], uint32_t (&v_)[NNB]) {
+    load_words<NBLK>(k_, reinterpret_cast<const uint32_t *>(rec + RL.kcodes()) + r16 * (D / 16) + kb * NBLK);
+    load_words<NG>(ks_, reinterpret_cast<const uint32_t *>(rec + RL.ksz()) + r16 * NG);
+    load_words<NG>(vs_, reinterpret_cast<const uint32_t *>(rec + RL.vsz()) + r16 * NG);
+    load_words<NNB>(v_, reinterpret_cast<const uint32_t *>(rec + RL.vcodes()) + r16 * NNB);
+  };
+
+  int pg = p0 + w;
+  const uint8_t *rec = pg < p1 ? rec_of(pg) : nullptr;
+  if (rec) load_page(rec, kwd, ksz, vsz, vwd);
+
+  for (; pg < p1; pg += 4) {
+    const int pgn = pg + 4;
+    const uint8_t *recn = pgn < p1 ? rec_of(pgn) : nullptr;
+    if (recn) load_page(recn, nkwd, nksz, nvsz, nvwd);
+    if (rec) {
+      const int ntok = hl - pg * kPage < kPage ? hl - pg * kPage : kPage;
+      const bool valid = r16 < ntok;
+
+      // ---------------- QK on int8 MFMA ----------------
+      v4i qacc[NQ][NG];
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+        for (int g2 = 0; g2 < NG; ++g2) qacc[qd][g2] = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) {
+        const uint32_t d = kwd[blk];
+        const v4i bq = v4i{(int)(d & 0x03030303u), (int)((d >> 2) & 0x03030303u),
+                           (int)((d >> 4) & 0x03030303u), (int)((d >> 6) & 0x03030303u)};
+#pragma unroll
+        for (int gs = 0; gs < GPB; ++gs) {
+          const int m = blk * GPB + gs;
+          const int g2 = (64 * blk) / G + gs;
+#pragma unroll
+          for (int qd = 0; qd < NQ; ++qd)
+            qacc[qd][g2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[qd][m], bq, qacc[qd][g2], 0, 0, 0);
+        }
+      }
+      float s[NQ];
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        float sc = 0.f, zt = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < NG; ++g2) {
+          const int dint = ((qacc[qd][g2][0] << 7) + qacc[qd][g2][1]) * 128 + qacc[qd][g2][2];
+          sc = fmaf(bf16_lo(ksz[g2]), (float)dint, sc);
+          zt = fmaf(bf16_hi(ksz[g2]), qzl[qd][g2], zt);
+        }
+        s[qd] = valid ? fmaf(sc, qscale[qd], zt) : -INFINITY;
+      }
+
+      // ---------------- online softmax (exact running max per head) ----------------
+      float pr[NQ];
+      bool grow = false;
+      float mnew[NQ];
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        mnew[qd] = fmaxf(m_run[qd], row_max(s[qd]));
+        grow |= mnew[qd] > m_run[qd];
+      }
+      if (__any(grow)) {
+        float alpha[NQ];
+#pragma unroll
+        for (int qd = 0; qd < NQ; ++qd) {
+          alpha[qd] = m_run[qd] == -INFINITY ? 0.f : exp2f(m_run[qd] - mnew[qd]);
+          m_run[qd] = mnew[qd];
+          lsum[qd] *= alpha[qd];
+#pragma unroll
+          for (int g2 = 0; g2 < NG; ++g2) zacc[qd][g2] *= alpha[qd];
+        }
+        // accumulator row r (head r) lives in lanes 16*(r/4) .. ; head h's alpha
+        // is uniform over lanes 16*(h%4) .. of quad h/4
+        float ar[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int hq = (kb == 0 ? 0 : 4) + r;     // head of accumulator row 4*kb + r
+          const int src = 16 * (hq & 3);
+          float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[0]), src));
+          float a1 = a0;
+          if constexpr (NQ > 1) a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[NQ - 1]), src));
+          ar[r] = hq < 4 ? a0 : a1;
+        }
+#pragma unroll
+        for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[nb][r] *= ar[r];
+      }
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        pr[qd] = valid ? exp2f(s[qd] - m_run[qd]) : 0.f;
+        lsum[qd] += pr[qd];
+      }
+
+      // ---------------- PV weights to LDS ----------------
+#pragma unroll
+      for (int g2 = 0; g2 < NG; ++g2) {
+        const float vs = valid ? bf16_lo(vsz[g2]) : 0.f;
+        const float vz = valid ? bf16_hi(vsz[g2]) : 0.f;
+#pragma unroll
+        for (int qd = 0; qd < NQ; ++qd) {
+          const _Float16 wh = (_Float16)(pr[qd] * vs);
+          zacc[qd][g2] = fmaf(pr[qd], vz, zacc[qd][g2]);
+          zacc[qd][g2] = fmaf(-4.f, (float)wh, zacc[qd][g2]);
+          wbuf[w][g2][qd * 4 + kb][pv_slot(r16)] = wh;
+        }
+      }
+      wave_lds_sync();
+      v4h apv[NG];
+#pragma unroll
+      for (int g2 = 0; g2 < NG; ++g2) {
+        if (r16 < GQ) {
+          const uint2 u = *reinterpret_cast<const uint2 *>(&wbuf[w][g2][r16][4 * kb]);
+          apv[g2] = as_v4h(u.x, u.y);
+        } else {
+          apv[g2] = as_v4h(0u, 0u);
+        }
+      }
+      wave_lds_sync();
+
+      // ---------------- PV on f16 MFMA ----------------
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb) {
+        const uint32_t y = vwd[nb] >> (2 * kb);
+        const v4h bv = as_v4h(((y << 8) & 0x03000300u) | 0x3C003C00u, (y & 0x03000300u) | 0x3C003C00u);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(apv[(16 * nb) / G], bv, acc[nb], 0, 0, 0);
+      }
+    }
+    rec = recn;
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) kwd[i] = nkwd[i];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) { ksz[i] = nksz[i]; vsz[i] = nvsz[i]; }
+#pragma unroll
+    for (int i = 0; i < NNB; ++i) vwd[i] = nvwd[i];
+  }
+
+  // ---------------- wave epilogue ----------------
+  // head h's sums: row sums over the 16 token lanes of quad h/4, lane group h%4
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) {
+    const float L = row_sum(lsum[qd]);
+    float Z[NG];
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) Z[g2] = row_sum(zacc[qd][g2]);
+    const int h = qd * 4 + kb;
+    if (r16 == 0) {
+      wm[w][h] = m_run[qd];
+      wl[w][h] = L;
+    }
+    // the zero-point / offset part is added to every channel of its group
+    if (r16 < NG) {
+      float zz = Z[0];
+#pragma unroll
+      for (int g2 = 1; g2 < NG; ++g2) zz = r16 == g2 ? Z[g2] : zz;
+      wo[w][h][0 + r16] = zz;          // staged in the first NG channels, moved below
+    }
+  }
+  wave_lds_sync();
+  float zst[GQ][NG];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h)
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) zst[h][g2] = wo[w][h][g2];
+  wave_lds_sync();
+  // accumulator element r of lane (kb, r16) is row 4*kb + r, channel 16*nb + r16
+#pragma unroll
+  for (int nb = 0; nb < NNB; ++nb) {
+    const int c = 16 * nb + r16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * kb + r;
+      if (h < GQ) wo[w][h][c] = 4.f * acc[nb][r] + zst[h][c / G];
+    }
+  }
+  __syncthreads();
+
+  // ---------------- combine the 4 waves, write the chunk partial ----------------
+  float *po = reinterpret_cast<float *>(p.ws + p.L.part_o);
+  float *pml = reinterpret_cast<float *>(p.ws + p.L.part_ml);
+  for (int i = tid; i < GQ * D; i += 256) {
+    const int h = i / D, c = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) M = fmaxf(M, wm[k][h]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (wm[k][h] == -INFINITY) continue;
+        const float a = exp2f(wm[k][h] - M);
+        L = fmaf(wl[k][h], a, L);
+        O = fmaf(wo[k][h][c], a, O);
+      }
+    }
+    const int hq = p.q_of_kv[j * GQ + h];
+    const size_t row = ((size_t)b * p.Hq + hq) * S + split;
+    po[row * D + c] = O;
+    if (c == 0) {
+      pml[row * 2 + 0] = M;
+      pml[row * 2 + 1] = L;
+    }
+  }
+}
+
+template <int D, int G>
+static void launch_mfma_dg(const DecodeParams &p, hipStream_t s) {
+  const dim3 grid(p.B * p.Hkv * p.splits), blk(256);
+  if (p.g == 8) hipLaunchKernelGGL((k_int2_mfma<D, G, 8>), grid, blk, 0, s, p);
+  else hipLaunchKernelGGL((k_int2_mfma<D, G, 4>), grid, blk, 0, s, p);
+}
+
+hipError_t launch_int2_mfma(const DecodeParams &p, hipStream_t s) {
+  if (p.g != 4 && p.g != 8) return hipErrorInvalidValue;
+  if (p.D == 64 && p.G == 32) launch_mfma_dg<64, 32>(p, s);
+  else if (p.D == 64 && p.G == 64) launch_mfma_dg<64, 64>(p, s);
+  else if (p.D == 128 && p.G == 32) launch_mfma_dg<128, 32>(p, s);
+  else if (p.D == 128 && p.G == 64) launch_mfma_dg<128, 64>(p, s);
+  else if (p.D == 128 && p.G == 128) launch_mfma_dg<128, 128>(p, s);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace oscar

@@ -40,7 +40,10 @@ def _check_out(run, ref, tol=TOL):
     return worst
 
 
-@pytest.mark.parametrize("kernel", [1])
+KERNELS = [1, 2]      # vector-ALU and matrix-core INT2 kernels
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
 def test_tiny_one_step(kernel):
     _say("case: tiny one step, kernel", kernel)
     inp = synth.make_small(synth.workload("tiny"))
@@ -51,41 +54,59 @@ def test_tiny_one_step(kernel):
     _say("tiny worst row rel err", w)
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("splits", [1, 3, 0])
-def test_tiny_splits_and_rotations(splits):
+def test_tiny_splits_and_rotations(splits, kernel):
     """Different history chunkings, R_v != R_k, and R_v = identity."""
-    _say("case: tiny splits", splits)
+    _say("case: tiny splits", splits, "kernel", kernel)
     wl = synth.workload("tiny", B=2, lengths=(1024, 777), steps=2, seed=5)
     inp = synth.make_small(wl, distinct_rv=True)
-    run = sh.build_and_step(inp, steps=2, int2_kernel=1, num_splits=splits)
+    run = sh.build_and_step(inp, steps=2, int2_kernel=kernel, num_splits=splits)
     ref = sh.oracle_step(inp, steps=2)
     _check_bytes(run, inp, ref)
     _check_out(run, ref)
-    run = sh.build_and_step(inp, steps=2, int2_kernel=1, num_splits=splits, R_v_none=True)
+    run = sh.build_and_step(inp, steps=2, int2_kernel=kernel, num_splits=splits, R_v_none=True)
     ref = sh.oracle_step(inp, steps=2, R_v_none=True)
     _check_bytes(run, inp, ref)
     _check_out(run, ref)
 
 
-def test_edge_lengths_and_head_map():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_edge_lengths_and_head_map(kernel):
     """Sequences with no history, a partial sink, one history token; a
     non-contiguous GQA head map."""
-    _say("case: edge lengths")
+    _say("case: edge lengths, kernel", kernel)
     wl = synth.workload("tiny", B=5, Hkv=2, Hq=8, lengths=(10, 64, 320, 321, 400), steps=1, seed=6)
     inp = synth.make_small(wl)
     hm = [1, 0, 1, 0, 0, 1, 1, 0]
-    run = sh.build_and_step(inp, steps=1, int2_kernel=1, head_map=hm)
+    run = sh.build_and_step(inp, steps=1, int2_kernel=kernel, head_map=hm)
     ref = sh.oracle_step(inp, steps=1, head_map=hm)
     _check_bytes(run, inp, ref)
     _check_out(run, ref)
 
 
-def test_qwen3_8b_32k_one_step():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_qwen3_8b_32k_one_step(kernel):
     """Qwen3-8B-shaped layer at 32K context, every history page and output."""
-    _say("case: qwen3-8b-32k")
+    _say("case: qwen3-8b-32k, kernel", kernel)
     inp = synth.make_small(synth.workload("qwen3-8b-32k"))
-    run = sh.build_and_step(inp, steps=1, int2_kernel=1)
+    run = sh.build_and_step(inp, steps=1, int2_kernel=kernel)
     ref = sh.oracle_step(inp, steps=1)
     _check_bytes(run, inp, ref)
     w = _check_out(run, ref)
     _say("32k worst row rel err", w)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("D,G,Hq,Hkv", [(128, 128, 16, 2), (128, 32, 8, 2), (64, 64, 8, 1)])
+def test_shapes(kernel, D, G, Hq, Hkv):
+    """Other head_dim / group / GQA shapes: G = 128 with 8 q heads per KV head
+    (Qwen3-32B-shaped), G = 32 at D = 128, G = 64 at D = 64; ragged history."""
+    _say("case: shape", D, G, Hq, Hkv, "kernel", kernel)
+    wl = synth.workload("tiny", B=2, Hkv=Hkv, Hq=Hq, D=D, G=G, lengths=(1500, 2077), steps=1, seed=11)
+    inp = synth.make_small(wl)
+    run = sh.build_and_step(inp, steps=1, int2_kernel=kernel, num_splits=2)
+    ref = sh.oracle_step(inp, steps=1)
+    _check_bytes(run, inp, ref)
+    w = _check_out(run, ref)
+    _say("worst row rel err", w)
