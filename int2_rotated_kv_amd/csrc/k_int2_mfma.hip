@@ -207,153 +207,174 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
   for (int nb = 0; nb < NNB; ++nb) acc[nb] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const uint8_t *pool = p.int2_pool;
+  // ---------------- page loop: 4-stage register ring ----------------
+  // stage data of one page for this lane: K words of token r16 / lane group kb,
+  // K and V (scale, zero) words of token r16, and VPL distinct V words
+  // (redistributed through LDS before use).
+  constexpr int NS = 4;
+  constexpr int VPL = D / 64;
+  struct Stage {
+    uint32_t k[NBLK], ks[NG], vs[NG], v[VPL];
+    int ok;
+  };
+  Stage st[NS];
+  const int nk = p1 - p0 - w > 0 ? (p1 - p0 - w + 3) / 4 : 0;   // pages of this wave
   const int32_t *ptab = p.hist_pages + (size_t)b * p.hist_stride;
-  auto rec_of = [&](int pg) -> const uint8_t * {
-    const int phys = ptab[pg];
-    if (phys < 0 || phys >= p.num_int2_pages) return nullptr;
-    return pool + ((size_t)phys * p.Hkv + j) * RL.bytes();
+  const size_t rec_stride = (size_t)p.Hkv * RL.bytes();
+  const uint8_t *pool_j = p.int2_pool + (size_t)j * RL.bytes();
+  int pid_vec = 0, pid_base = -64;
+
+  auto page_id = [&](int k) -> int {           // wave-uniform k
+    if (k - pid_base >= 64) {
+      pid_base = k;
+      const int kk = k + lane;
+      pid_vec = kk < nk ? ptab[p0 + w + 4 * kk] : -1;
+    }
+    return __builtin_amdgcn_readlane(pid_vec, k - pid_base);
   };
-
-  // raw page data of one page for this lane
-  uint32_t kwd[NBLK], ksz[NG], vsz[NG], vwd[NNB];
-  uint32_t nkwd[NBLK], nksz[NG], nvsz[NG], nvwd[NNB];
-  auto load_page = [&](const uint8_t *rec, uint32_t (&k_)[NBLK], uint32_t (&ks_)[NG],
-                       uint32_t (&vs_)[NG], uint32_t (&v_)[NNB]) {
-    load_words<NBLK>(k_, reinterpret_cast<const uint32_t *>(rec + RL.kcodes()) + r16 * (D / 16) + kb * NBLK);
-    load_words<NG>(ks_, reinterpret_cast<const uint32_t *>(rec + RL.ksz()) + r16 * NG);
-    load_words<NG>(vs_, reinterpret_cast<const uint32_t *>(rec + RL.vsz()) + r16 * NG);
-    load_words<NNB>(v_, reinterpret_cast<const uint32_t *>(rec + RL.vcodes()) + r16 * NNB);
+  auto issue = [&](Stage &sg, int k) {
+    int phys = k < nk ? page_id(k) : -1;
+    sg.ok = phys >= 0 && phys < p.num_int2_pages;
+    // out-of-range stages still load (from page 0) so every lane issues the
+    // same load sequence; their data is never used
+    const uint8_t *rec = pool_j + (sg.ok ? (size_t)phys : 0) * rec_stride;
+    load_words<NBLK>(sg.k, reinterpret_cast<const uint32_t *>(rec + RL.kcodes()) + r16 * (D / 16) + kb * NBLK);
+    load_words<NG>(sg.ks, reinterpret_cast<const uint32_t *>(rec + RL.ksz()) + r16 * NG);
+    load_words<NG>(sg.vs, reinterpret_cast<const uint32_t *>(rec + RL.vsz()) + r16 * NG);
+    load_words<VPL>(sg.v, reinterpret_cast<const uint32_t *>(rec + RL.vcodes()) + lane * VPL);
   };
+  __shared__ __align__(16) uint32_t vbuf[4][D];   // per wave: V words of the current page
 
-  int pg = p0 + w;
-  const uint8_t *rec = pg < p1 ? rec_of(pg) : nullptr;
-  if (rec) load_page(rec, kwd, ksz, vsz, vwd);
+  auto process = [&](Stage &sg, int k) {
+    if (!sg.ok) return;
+    const int pg = p0 + w + 4 * k;
+    const int ntok = hl - pg * kPage < kPage ? hl - pg * kPage : kPage;
+    const bool valid = r16 < ntok;
 
-  for (; pg < p1; pg += 4) {
-    const int pgn = pg + 4;
-    const uint8_t *recn = pgn < p1 ? rec_of(pgn) : nullptr;
-    if (recn) load_page(recn, nkwd, nksz, nvsz, nvwd);
-    if (rec) {
-      const int ntok = hl - pg * kPage < kPage ? hl - pg * kPage : kPage;
-      const bool valid = r16 < ntok;
+    // V words to LDS (read back after the QK / softmax work)
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) vbuf[w][lane * VPL + i] = sg.v[i];
 
-      // ---------------- QK on int8 MFMA ----------------
-      v4i qacc[NQ][NG];
+    // ---------------- QK on int8 MFMA ----------------
+    v4i qacc[NQ][NG];
 #pragma unroll
-      for (int qd = 0; qd < NQ; ++qd)
+    for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-        for (int g2 = 0; g2 < NG; ++g2) qacc[qd][g2] = v4i{0, 0, 0, 0};
+      for (int g2 = 0; g2 < NG; ++g2) qacc[qd][g2] = v4i{0, 0, 0, 0};
 #pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk) {
-        const uint32_t d = kwd[blk];
-        const v4i bq = v4i{(int)(d & 0x03030303u), (int)((d >> 2) & 0x03030303u),
-                           (int)((d >> 4) & 0x03030303u), (int)((d >> 6) & 0x03030303u)};
+    for (int blk = 0; blk < NBLK; ++blk) {
+      const uint32_t d = sg.k[blk];
+      const v4i bq = v4i{(int)(d & 0x03030303u), (int)((d >> 2) & 0x03030303u),
+                         (int)((d >> 4) & 0x03030303u), (int)((d >> 6) & 0x03030303u)};
 #pragma unroll
-        for (int gs = 0; gs < GPB; ++gs) {
-          const int m = blk * GPB + gs;
-          const int g2 = (64 * blk) / G + gs;
+      for (int gs = 0; gs < GPB; ++gs) {
+        const int m = blk * GPB + gs;
+        const int g2 = (64 * blk) / G + gs;
 #pragma unroll
-          for (int qd = 0; qd < NQ; ++qd)
-            qacc[qd][g2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[qd][m], bq, qacc[qd][g2], 0, 0, 0);
-        }
-      }
-      float s[NQ];
-#pragma unroll
-      for (int qd = 0; qd < NQ; ++qd) {
-        float sc = 0.f, zt = 0.f;
-#pragma unroll
-        for (int g2 = 0; g2 < NG; ++g2) {
-          const int dint = ((qacc[qd][g2][0] << 7) + qacc[qd][g2][1]) * 128 + qacc[qd][g2][2];
-          sc = fmaf(bf16_lo(ksz[g2]), (float)dint, sc);
-          zt = fmaf(bf16_hi(ksz[g2]), qzl[qd][g2], zt);
-        }
-        s[qd] = valid ? fmaf(sc, qscale[qd], zt) : -INFINITY;
-      }
-
-      // ---------------- online softmax (exact running max per head) ----------------
-      float pr[NQ];
-      bool grow = false;
-      float mnew[NQ];
-#pragma unroll
-      for (int qd = 0; qd < NQ; ++qd) {
-        mnew[qd] = fmaxf(m_run[qd], row_max(s[qd]));
-        grow |= mnew[qd] > m_run[qd];
-      }
-      if (__any(grow)) {
-        float alpha[NQ];
-#pragma unroll
-        for (int qd = 0; qd < NQ; ++qd) {
-          alpha[qd] = m_run[qd] == -INFINITY ? 0.f : exp2f(m_run[qd] - mnew[qd]);
-          m_run[qd] = mnew[qd];
-          lsum[qd] *= alpha[qd];
-#pragma unroll
-          for (int g2 = 0; g2 < NG; ++g2) zacc[qd][g2] *= alpha[qd];
-        }
-        // accumulator row r (head r) lives in lanes 16*(r/4) .. ; head h's alpha
-        // is uniform over lanes 16*(h%4) .. of quad h/4
-        float ar[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int hq = (kb == 0 ? 0 : 4) + r;     // head of accumulator row 4*kb + r
-          const int src = 16 * (hq & 3);
-          float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[0]), src));
-          float a1 = a0;
-          if constexpr (NQ > 1) a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[NQ - 1]), src));
-          ar[r] = hq < 4 ? a0 : a1;
-        }
-#pragma unroll
-        for (int nb = 0; nb < NNB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[nb][r] *= ar[r];
-      }
-#pragma unroll
-      for (int qd = 0; qd < NQ; ++qd) {
-        pr[qd] = valid ? exp2f(s[qd] - m_run[qd]) : 0.f;
-        lsum[qd] += pr[qd];
-      }
-
-      // ---------------- PV weights to LDS ----------------
-#pragma unroll
-      for (int g2 = 0; g2 < NG; ++g2) {
-        const float vs = valid ? bf16_lo(vsz[g2]) : 0.f;
-        const float vz = valid ? bf16_hi(vsz[g2]) : 0.f;
-#pragma unroll
-        for (int qd = 0; qd < NQ; ++qd) {
-          const _Float16 wh = (_Float16)(pr[qd] * vs);
-          zacc[qd][g2] = fmaf(pr[qd], vz, zacc[qd][g2]);
-          zacc[qd][g2] = fmaf(-4.f, (float)wh, zacc[qd][g2]);
-          wbuf[w][g2][qd * 4 + kb][pv_slot(r16)] = wh;
-        }
-      }
-      wave_lds_sync();
-      v4h apv[NG];
-#pragma unroll
-      for (int g2 = 0; g2 < NG; ++g2) {
-        if (r16 < GQ) {
-          const uint2 u = *reinterpret_cast<const uint2 *>(&wbuf[w][g2][r16][4 * kb]);
-          apv[g2] = as_v4h(u.x, u.y);
-        } else {
-          apv[g2] = as_v4h(0u, 0u);
-        }
-      }
-      wave_lds_sync();
-
-      // ---------------- PV on f16 MFMA ----------------
-#pragma unroll
-      for (int nb = 0; nb < NNB; ++nb) {
-        const uint32_t y = vwd[nb] >> (2 * kb);
-        const v4h bv = as_v4h(((y << 8) & 0x03000300u) | 0x3C003C00u, (y & 0x03000300u) | 0x3C003C00u);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(apv[(16 * nb) / G], bv, acc[nb], 0, 0, 0);
+        for (int qd = 0; qd < NQ; ++qd)
+          qacc[qd][g2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[qd][m], bq, qacc[qd][g2], 0, 0, 0);
       }
     }
-    rec = recn;
+    float s_[NQ];
 #pragma unroll
-    for (int i = 0; i < NBLK; ++i) kwd[i] = nkwd[i];
+    for (int qd = 0; qd < NQ; ++qd) {
+      float sc = 0.f, zt = 0.f;
 #pragma unroll
-    for (int i = 0; i < NG; ++i) { ksz[i] = nksz[i]; vsz[i] = nvsz[i]; }
+      for (int g2 = 0; g2 < NG; ++g2) {
+        const int dint = ((qacc[qd][g2][0] << 7) + qacc[qd][g2][1]) * 128 + qacc[qd][g2][2];
+        sc = fmaf(bf16_lo(sg.ks[g2]), (float)dint, sc);
+        zt = fmaf(bf16_hi(sg.ks[g2]), qzl[qd][g2], zt);
+      }
+      s_[qd] = valid ? fmaf(sc, qscale[qd], zt) : -INFINITY;
+    }
+
+    // ---------------- online softmax (exact running max per head) ----------------
+    bool grow = false;
+    float mnew[NQ];
 #pragma unroll
-    for (int i = 0; i < NNB; ++i) vwd[i] = nvwd[i];
+    for (int qd = 0; qd < NQ; ++qd) {
+      mnew[qd] = fmaxf(m_run[qd], row_max(s_[qd]));
+      grow |= mnew[qd] > m_run[qd];
+    }
+    if (__any(grow)) {
+      float alpha[NQ];
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        alpha[qd] = m_run[qd] == -INFINITY ? 0.f : exp2f(m_run[qd] - mnew[qd]);
+        m_run[qd] = mnew[qd];
+        lsum[qd] *= alpha[qd];
+#pragma unroll
+        for (int g2 = 0; g2 < NG; ++g2) zacc[qd][g2] *= alpha[qd];
+      }
+      // accumulator row 4*kb + r is head 4*kb + r; head h's alpha is uniform
+      // over the 16 lanes 16*(h%4) .. of head quad h/4
+      float ar[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[0]), 16 * r));
+        float a1 = a0;
+        if constexpr (NQ > 1) a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[NQ - 1]), 16 * r));
+        ar[r] = kb == 0 ? a0 : a1;
+      }
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nb][r] *= ar[r];
+    }
+    float pr[NQ];
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      pr[qd] = valid ? exp2f(s_[qd] - m_run[qd]) : 0.f;
+      lsum[qd] += pr[qd];
+    }
+
+    // ---------------- PV weights to LDS ----------------
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) {
+      const float vs = valid ? bf16_lo(sg.vs[g2]) : 0.f;
+      const float vz = valid ? bf16_hi(sg.vs[g2]) : 0.f;
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        const _Float16 wh = (_Float16)(pr[qd] * vs);
+        zacc[qd][g2] = fmaf(pr[qd], vz, zacc[qd][g2]);
+        zacc[qd][g2] = fmaf(-4.f, (float)wh, zacc[qd][g2]);
+        wbuf[w][g2][qd * 4 + kb][pv_slot(r16)] = wh;
+      }
+    }
+    wave_lds_sync();
+    v4h apv[NG];
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) {
+      if (r16 < GQ) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(&wbuf[w][g2][r16][4 * kb]);
+        apv[g2] = as_v4h(u.x, u.y);
+      } else {
+        apv[g2] = as_v4h(0u, 0u);
+      }
+    }
+    uint32_t vwd[NNB];
+    load_words<NNB>(vwd, &vbuf[w][r16 * NNB]);
+    wave_lds_sync();
+
+    // ---------------- PV on f16 MFMA ----------------
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb) {
+      const uint32_t y = vwd[nb] >> (2 * kb);
+      const v4h bv = as_v4h(((y << 8) & 0x03000300u) | 0x3C003C00u, (y & 0x03000300u) | 0x3C003C00u);
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(apv[(16 * nb) / G], bv, acc[nb], 0, 0, 0);
+    }
+  };
+
+  if (nk > 0) {
+#pragma unroll
+    for (int s2 = 0; s2 < NS - 1; ++s2) issue(st[s2], s2);
+    for (int k = 0; k < nk; k += NS) {
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) {
+        issue(st[(s2 + NS - 1) % NS], k + s2 + NS - 1);
+        if (k + s2 < nk) process(st[s2], k + s2);
+      }
+    }
   }
 
   // ---------------- wave epilogue ----------------
