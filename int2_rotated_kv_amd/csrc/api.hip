@@ -162,8 +162,8 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   L.qexp = off; off = align256(off + BH * 4);
   L.part_o = off; off = align256(off + BH * S * p->D * 4);
   L.part_ml = off; off = align256(off + BH * S * 2 * 4);
-  L.bf_o = off; off = align256(off + BH * p->D * 4);
-  L.bf_ml = off; off = align256(off + BH * 2 * 4);
+  L.bf_o = off; off = align256(off + BH * kBf16Splits * p->D * 4);
+  L.bf_ml = off; off = align256(off + BH * kBf16Splits * 2 * 4);
   L.total = off;
   L.splits = S;
   L.pages_per_split = pps;
@@ -191,6 +191,8 @@ int oscar_write_bf16(const oscar_cache *cache, int32_t n, const int32_t *dst_slo
   if (n < 0) return fail(OSCAR_EINVAL, "n < 0");
   if (n == 0) return OSCAR_OK;
   if (!dst_slot || !k_new || !v_new) return fail(OSCAR_EINVAL, "NULL slot or token pointer");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(OSCAR_EINVAL, "k_new / v_new must be 16-byte aligned");
   if (cache->num_bf16_pages <= 0) return fail(OSCAR_EINVAL, "cache has no BF16 pages");
   hipError_t e = launch_write_bf16(*cache, n, dst_slot, k_new, v_new, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "oscar_write_bf16 launch");
@@ -205,7 +207,8 @@ int oscar_demote_pack(const oscar_cache *cache, int32_t n, const int32_t *src_sl
   if (n < 0) return fail(OSCAR_EINVAL, "n < 0");
   if (n == 0) return OSCAR_OK;
   if (!src_slot || !dst_slot) return fail(OSCAR_EINVAL, "NULL slot list");
-  if (!R_k) return fail(OSCAR_EINVAL, "R_k is NULL");
+  if (!R_k || !aligned(R_k, 16)) return fail(OSCAR_EINVAL, "R_k is NULL or not 16-byte aligned");
+  if (R_v && !aligned(R_v, 16)) return fail(OSCAR_EINVAL, "R_v is not 16-byte aligned");
   if (!clip_k || !clip_v) return fail(OSCAR_EINVAL, "NULL clip ratios");
   if (cache->num_bf16_pages <= 0 || cache->num_int2_pages <= 0)
     return fail(OSCAR_EINVAL, "cache needs BF16 and INT2 pages");
@@ -242,7 +245,7 @@ int oscar_decode_attn(const oscar_cache *cache, const oscar_decode_args *args, c
   int st = check_args(cache, args, &p);
   if (st) return st;
   if (!q || !aligned(q, 16)) return fail(OSCAR_EINVAL, "q is NULL or not 16-byte aligned");
-  if (!R_k) return fail(OSCAR_EINVAL, "R_k is NULL");
+  if (!R_k || !aligned(R_k, 16)) return fail(OSCAR_EINVAL, "R_k is NULL or not 16-byte aligned");
   if (!workspace || !aligned(workspace, 256))
     return fail(OSCAR_EINVAL, "workspace is NULL or not 256-byte aligned");
   if (workspace_bytes < p.L.total)
@@ -278,6 +281,7 @@ int oscar_merge(const oscar_cache *cache, const oscar_decode_args *args, const v
   int st = check_args(cache, args, &p);
   if (st) return st;
   if (!out) return fail(OSCAR_EINVAL, "out is NULL");
+  if (R_v && !aligned(R_v, 16)) return fail(OSCAR_EINVAL, "R_v is not 16-byte aligned");
   if (!workspace || !aligned(workspace, 256))
     return fail(OSCAR_EINVAL, "workspace is NULL or not 256-byte aligned");
   if (workspace_bytes < p.L.total)

@@ -11,6 +11,8 @@ namespace oscar {
 
 constexpr int kPage = OSCAR_PAGE_TOKENS;
 constexpr int kMaxBf16 = OSCAR_MAX_BF16_TOKENS;
+constexpr int kBf16PagesPerSplit = 4;                              // one wave per page
+constexpr int kBf16Splits = kMaxBf16 / (kPage * kBf16PagesPerSplit); // 5 BF16 partials
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -38,8 +40,8 @@ struct WsLayout {
   size_t qexp;      // int32 [B][Hq]
   size_t part_o;    // fp32 [B][Hq][S][D]  history chunk partial outputs (rotated basis)
   size_t part_ml;   // fp32 [B][Hq][S][2]  (max logit in log2 units, sum of exponentials)
-  size_t bf_o;      // fp32 [B][Hq][D]     BF16 segment partial output
-  size_t bf_ml;     // fp32 [B][Hq][2]
+  size_t bf_o;      // fp32 [B][Hq][kBf16Splits][D]  BF16 segment partial outputs
+  size_t bf_ml;     // fp32 [B][Hq][kBf16Splits][2]
   size_t total;
   int splits;       // S
   int pages_per_split;

@@ -41,117 +41,148 @@ hipError_t launch_qrot(const DecodeParams &p, const uint16_t *q, const float *Rk
 }
 
 // ---------------------------------------------------------------------------
-// BF16 segment: up to 320 unrotated tokens per sequence in BF16 pages.  One
-// block per (sequence, KV head); the g q heads of the KV head share every load.
+// BF16 segment: up to 320 unrotated tokens per sequence in BF16 pages.  Grid
+// (sequence x KV head, 5 splits of 4 pages); one wave per page, the g q heads
+// of the KV head share every load.  Per page:
+//   QK: lane (t = lane%16, part = lane/16) dots channels 32*part .. +31 of token
+//       t with q; the parts are summed across lanes.
+//   PV: lane owns channels D/64*lane .. +D/64-1 and accumulates p * v over the
+//       16 tokens.
+// Each split writes one partial (m, l, o) per q head.
 // ---------------------------------------------------------------------------
 template <int D, int GQ>
 __global__ __launch_bounds__(256) void k_bf16_seg(DecodeParams p, const uint16_t *__restrict__ q) {
-  constexpr int NT = 256;
-  constexpr int NP = NT / D;          // token partitions in the PV phase
+  constexpr int CP = D / 4;            // channels per QK part
+  constexpr int NCH = D / 64;          // PV channels per lane
   const int b = blockIdx.x / p.Hkv;
   const int j = blockIdx.x % p.Hkv;
-  const int tid = threadIdx.x;
+  const int split = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t = lane & 15, part = lane >> 4;
 
-  __shared__ float qs[GQ][D];
-  __shared__ float sp[GQ][kMaxBf16];
-  __shared__ int pages[kMaxBf16 / kPage];
-  __shared__ float hm[GQ], hl[GQ];
-  __shared__ float po[NP][GQ][D];
+  __shared__ float qs[D][GQ];
+  __shared__ float pb[4][16][GQ];
+  __shared__ float wm[4][GQ], wl[4][GQ];
+  __shared__ float wo[4][GQ][D];
 
   int T = p.bf16_len[b];
   T = T < 0 ? 0 : T;
   T = T > kMaxBf16 ? kMaxBf16 : T;
   T = T > kPage * p.bf16_stride ? kPage * p.bf16_stride : T;
 
-  for (int i = tid; i < GQ * D; i += NT) {
+  for (int i = tid; i < GQ * D; i += 256) {
     const int h = i / D, c = i % D;
-    const int hq = p.q_of_kv[j * GQ + h];
-    qs[h][c] = bf16_to_f32(q[((size_t)b * p.Hq + hq) * D + c]) * p.sm_log2;
+    qs[c][h] = bf16_to_f32(q[((size_t)b * p.Hq + p.q_of_kv[j * GQ + h]) * D + c]) * p.sm_log2;
   }
-  if (tid < (T + kPage - 1) / kPage) pages[tid] = p.bf16_pages[(size_t)b * p.bf16_stride + tid];
   __syncthreads();
 
-  // logits: one token per thread
-  for (int t = tid; t < T; t += NT) {
-    const int64_t page = pages[t / kPage];
-    float acc[GQ];
+  const int pgi = split * kBf16PagesPerSplit + w;     // page index in the table
+  float m[GQ], o[GQ][NCH], lsum[GQ];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) acc[h] = 0.f;
-    const bool ok = page >= 0 && page < p.num_bf16_pages;
-    if (ok) {
-      const uint4 *kp = reinterpret_cast<const uint4 *>(
-          p.bf16_k + ((page * p.Hkv + j) * kPage + (t % kPage)) * D);
-#pragma unroll 4
-      for (int c8 = 0; c8 < D / 8; ++c8) {
+  for (int h = 0; h < GQ; ++h) {
+    m[h] = -INFINITY;
+    lsum[h] = 0.f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) o[h][k] = 0.f;
+  }
+  const int ntok = T - pgi * kPage;
+  if (ntok > 0) {
+    const int64_t page = p.bf16_pages[(size_t)b * p.bf16_stride + pgi];
+    if (page >= 0 && page < p.num_bf16_pages) {
+      const size_t base = ((page * p.Hkv + j) * kPage) * D;
+      // ---- QK ----
+      const uint4 *kp = reinterpret_cast<const uint4 *>(p.bf16_k + base + (size_t)t * D + part * CP);
+      float dot[GQ];
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) dot[h] = 0.f;
+#pragma unroll
+      for (int c8 = 0; c8 < CP / 8; ++c8) {
         const uint4 v = kp[c8];
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+          const int c = part * CP + c8 * 8 + 2 * e;
           const float k0 = bf16_lo(w4[e]), k1 = bf16_hi(w4[e]);
-          const int c = c8 * 8 + 2 * e;
 #pragma unroll
-          for (int h = 0; h < GQ; ++h) acc[h] = fmaf(qs[h][c + 1], k1, fmaf(qs[h][c], k0, acc[h]));
+          for (int h = 0; h < GQ; ++h) dot[h] = fmaf(qs[c + 1][h], k1, fmaf(qs[c][h], k0, dot[h]));
+        }
+      }
+      const bool valid = t < ntok;
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        float s = dot[h];
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        s = valid ? s : -INFINITY;
+        float mx = s;
+#pragma unroll
+        for (int o2 = 1; o2 < 16; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+        const float pr = valid ? exp2f(s - mx) : 0.f;
+        float l = pr;
+#pragma unroll
+        for (int o2 = 1; o2 < 16; o2 <<= 1) l += __shfl_xor(l, o2);
+        m[h] = mx;
+        lsum[h] = l;
+        if (part == 0) pb[w][t][h] = pr;
+      }
+      wave_lds_sync();
+      // ---- PV ----
+      const uint16_t *vp = p.bf16_v + base;
+      const int tmax = ntok < kPage ? ntok : kPage;
+      for (int tt = 0; tt < tmax; ++tt) {
+        float v[NCH];
+        if constexpr (NCH == 2) {
+          const uint32_t vv = reinterpret_cast<const uint32_t *>(vp)[(size_t)tt * (D / 2) + lane];
+          v[0] = bf16_lo(vv);
+          v[1] = bf16_hi(vv);
+        } else {
+          v[0] = bf16_to_f32(vp[(size_t)tt * D + lane]);
+        }
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+          const float pr = pb[w][tt][h];
+#pragma unroll
+          for (int k = 0; k < NCH; ++k) o[h][k] = fmaf(pr, v[k], o[h][k]);
         }
       }
     }
-#pragma unroll
-    for (int h = 0; h < GQ; ++h) sp[h][t] = ok ? acc[h] : -INFINITY;
   }
-  __syncthreads();
-
-  // per-head max and sum, one wave per head (4 waves)
-  const int lane = tid & 63, w = tid >> 6;
-  for (int h = w; h < GQ; h += NT / 64) {
-    float m = -INFINITY;
-    for (int t = lane; t < T; t += 64) m = fmaxf(m, sp[h][t]);
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    float l = 0.f;
-    for (int t = lane; t < T; t += 64) {
-      const float e = (m == -INFINITY) ? 0.f : exp2f(sp[h][t] - m);
-      sp[h][t] = e;
-      l += e;
-    }
-    for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
-    if (lane == 0) { hm[h] = m; hl[h] = l; }
-  }
-  __syncthreads();
-
-  // PV: thread (part, c), tokens part, part + NP, ...
-  {
-    const int c = tid % D, part = tid / D;
-    float acc[GQ];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) acc[h] = 0.f;
-    for (int t = part; t < T; t += NP) {
-      const int64_t page = pages[t / kPage];
-      if (page < 0 || page >= p.num_bf16_pages) continue;
-      const float v = bf16_to_f32(p.bf16_v[((page * p.Hkv + j) * kPage + (t % kPage)) * D + c]);
+  for (int h = 0; h < GQ; ++h) {
 #pragma unroll
-      for (int h = 0; h < GQ; ++h) acc[h] = fmaf(sp[h][t], v, acc[h]);
-    }
-#pragma unroll
-    for (int h = 0; h < GQ; ++h) po[part][h][c] = acc[h];
+    for (int k = 0; k < NCH; ++k) wo[w][h][lane * NCH + k] = o[h][k];
+    if (lane == 0) { wm[w][h] = m[h]; wl[w][h] = lsum[h]; }
   }
   __syncthreads();
   float *bo = reinterpret_cast<float *>(p.ws + p.L.bf_o);
   float *bml = reinterpret_cast<float *>(p.ws + p.L.bf_ml);
-  for (int i = tid; i < GQ * D; i += NT) {
+  for (int i = tid; i < GQ * D; i += 256) {
     const int h = i / D, c = i % D;
-    float s = 0.f;
+    float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < NP; ++k) s += po[k][h][c];
-    const int hq = p.q_of_kv[j * GQ + h];
-    bo[((size_t)b * p.Hq + hq) * D + c] = s;
+    for (int k = 0; k < 4; ++k) M = fmaxf(M, wm[k][h]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (wm[k][h] == -INFINITY) continue;
+        const float a = exp2f(wm[k][h] - M);
+        L = fmaf(wl[k][h], a, L);
+        O = fmaf(wo[k][h][c], a, O);
+      }
+    }
+    const size_t row = ((size_t)b * p.Hq + p.q_of_kv[j * GQ + h]) * kBf16Splits + split;
+    bo[row * D + c] = O;
     if (c == 0) {
-      bml[((size_t)b * p.Hq + hq) * 2 + 0] = hm[h];
-      bml[((size_t)b * p.Hq + hq) * 2 + 1] = hl[h];
+      bml[row * 2 + 0] = M;
+      bml[row * 2 + 1] = L;
     }
   }
 }
 
 template <int D>
 static void launch_bf16_d(const DecodeParams &p, const uint16_t *q, hipStream_t s) {
-  const dim3 grid(p.B * p.Hkv), blk(256);
+  const dim3 grid(p.B * p.Hkv, kBf16Splits), blk(256);
   switch (p.g) {
     case 1: hipLaunchKernelGGL((k_bf16_seg<D, 1>), grid, blk, 0, s, p, q); break;
     case 2: hipLaunchKernelGGL((k_bf16_seg<D, 2>), grid, blk, 0, s, p, q); break;

@@ -37,9 +37,10 @@ __device__ uint16_t f64_to_bf16_rne(double x) {
   return (uint16_t)(sign | (uint16_t)((E + 127) << 7) | (uint16_t)(q & 127));
 }
 
-// One block: up to 16 entries of the slot lists, one KV head (blockIdx.y), K or
-// V (blockIdx.z).  Thread c owns rotated channel c of all 16 tokens.
-template <int D, int G>
+// One block: up to T entries of the slot lists (16 for bulk fills, 1 for the
+// few tokens of a decode step), one KV head (blockIdx.y), K or V (blockIdx.z).
+// Thread c owns rotated channel c of the block's tokens.
+template <int D, int G, int T>
 __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
                                              const uint16_t *__restrict__ bf_v,
                                              uint8_t *__restrict__ pool, int Hkv, int n,
@@ -53,7 +54,6 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
   // every fp64 operation below is rounded on its own, as specified: no fusion
   // of the clip products into the subtraction
 #pragma clang fp contract(off)
-  constexpr int T = 16;
   constexpr RecLayout RL(D, G);
   constexpr int GW = G < 64 ? G : 64;       // lanes of a group inside one wave
   const int c = threadIdx.x;
@@ -97,6 +97,7 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
     R += (size_t)j * D * D;
 #pragma unroll
     for (int t = 0; t < T; ++t) x[t] = 0.0;
+#pragma unroll 4
     for (int i = 0; i < D; i += 2) {
       const double r0 = (double)R[(size_t)i * D + c];
       const double r1 = (double)R[(size_t)(i + 1) * D + c];
@@ -220,19 +221,19 @@ __global__ void k_write_bf16(uint16_t *__restrict__ pk, uint16_t *__restrict__ p
   const int d = dst[e];
   if (d < 0 || (d >> 4) >= n_pages) return;   // skipped entry
   const int64_t page = d >> 4, off = d & 15;
-  const int per = Hkv * D;  // elements per token
-  for (int i = threadIdx.x; i < per; i += blockDim.x) {
-    const int j = i / D, c = i - j * D;
-    const size_t o = ((page * Hkv + j) * kPage + off) * D + c;
-    pk[o] = kn[(size_t)e * per + i];
-    pv[o] = vn[(size_t)e * per + i];
+  const int per8 = Hkv * D / 8;               // 16-byte chunks per token
+  for (int i = threadIdx.x; i < per8; i += blockDim.x) {
+    const int j = i / (D / 8), c8 = i - j * (D / 8);
+    const size_t o = ((page * Hkv + j) * kPage + off) * D / 8 + c8;
+    reinterpret_cast<uint4 *>(pk)[o] = reinterpret_cast<const uint4 *>(kn)[(size_t)e * per8 + i];
+    reinterpret_cast<uint4 *>(pv)[o] = reinterpret_cast<const uint4 *>(vn)[(size_t)e * per8 + i];
   }
 }
 
 hipError_t launch_write_bf16(const oscar_cache &c, int n, const int32_t *dst, const uint16_t *k,
                              const uint16_t *v, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_write_bf16, dim3(n), dim3(256), 0, s, c.bf16_k_pool, c.bf16_v_pool,
+  hipLaunchKernelGGL(k_write_bf16, dim3(n), dim3(128), 0, s, c.bf16_k_pool, c.bf16_v_pool,
                      c.num_kv_heads, c.head_dim, c.num_bf16_pages, dst, k, v);
   return hipGetLastError();
 }
@@ -241,10 +242,19 @@ template <int D, int G>
 static void launch_demote_t(const oscar_cache &c, int n, const int32_t *src, const int32_t *dst,
                             const float *Rk, const float *Rv, const float *ck, const float *cv,
                             hipStream_t s) {
-  dim3 grid((n + 15) / 16, c.num_kv_heads, 2);
-  hipLaunchKernelGGL((k_demote<D, G>), grid, dim3(D), 0, s, c.bf16_k_pool, c.bf16_v_pool,
-                     c.int2_pool, c.num_kv_heads, n, c.num_bf16_pages, c.num_int2_pages, src, dst,
-                     Rk, Rv, ck, cv);
+  // few tokens (a decode step): one token per block for parallelism; bulk
+  // fills: 16 tokens per block so every R load serves 16 dot products
+  if ((n + 15) / 16 * c.num_kv_heads * 2 < 1024) {
+    dim3 grid(n, c.num_kv_heads, 2);
+    hipLaunchKernelGGL((k_demote<D, G, 1>), grid, dim3(D), 0, s, c.bf16_k_pool, c.bf16_v_pool,
+                       c.int2_pool, c.num_kv_heads, n, c.num_bf16_pages, c.num_int2_pages, src, dst,
+                       Rk, Rv, ck, cv);
+  } else {
+    dim3 grid((n + 15) / 16, c.num_kv_heads, 2);
+    hipLaunchKernelGGL((k_demote<D, G, 16>), grid, dim3(D), 0, s, c.bf16_k_pool, c.bf16_v_pool,
+                       c.int2_pool, c.num_kv_heads, n, c.num_bf16_pages, c.num_int2_pages, src, dst,
+                       Rk, Rv, ck, cv);
+  }
 }
 
 hipError_t launch_demote(const oscar_cache &c, int n, const int32_t *src, const int32_t *dst,
