@@ -36,7 +36,10 @@ def common_flags(debug: bool = False):
          "-I", INCLUDE, "-I", CSRC,
          # packed fp32 VALU instructions are disabled on purpose for all device code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-munsafe-fp-atomics"]
+         "-munsafe-fp-atomics",
+         # keep matrix-core accumulators in VGPRs: the online-softmax rescale
+         # multiplies them with VALU ops, which cannot read AGPRs
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
     f += ["-O1", "-g"] if debug else ["-O3"]
     return f
 

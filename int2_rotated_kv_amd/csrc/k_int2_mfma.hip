@@ -33,29 +33,32 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 namespace {
 
 // 16-lane (DPP row) reductions; every lane of the row receives the result.
-__device__ __forceinline__ float dpp_f(float x, int ctrl_id) {
-  const int v = __float_as_int(x);
-  int r;
-  switch (ctrl_id) {
-    case 0: r = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); break;   // quad [1,0,3,2]
-    case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); break;   // quad [2,3,0,1]
-    case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
-    default: r = __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); break; // row_mirror
-  }
-  return __int_as_float(r);
-}
+// Operands are finite or -inf, so no NaN canonicalisation is needed; the
+// s_nop covers the VALU-write -> DPP-read hazard.
 __device__ __forceinline__ float row_max(float x) {
-  x = fmaxf(x, dpp_f(x, 0));
-  x = fmaxf(x, dpp_f(x, 1));
-  x = fmaxf(x, dpp_f(x, 2));
-  x = fmaxf(x, dpp_f(x, 3));
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf"
+      : "+v"(x));
   return x;
 }
 __device__ __forceinline__ float row_sum(float x) {
-  x += dpp_f(x, 0);
-  x += dpp_f(x, 1);
-  x += dpp_f(x, 2);
-  x += dpp_f(x, 3);
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf"
+      : "+v"(x));
   return x;
 }
 
@@ -108,7 +111,8 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
   const int split = blockIdx.x % S;
   const int b = unit / p.Hkv;
   const int j = unit % p.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int r16 = lane & 15, kb = lane >> 4;     // row-in-16 and lane group
 
   __shared__ float qf[GQ][D];                    // q_rot (unscaled)
@@ -117,6 +121,8 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
   __shared__ __align__(16) _Float16 wbuf[4][NG][16][16];       // per wave: w[grp][head row][slot]
   __shared__ float wm[4][GQ], wl[4][GQ];
   __shared__ float wo[4][GQ][D];
+
+  for (int i = tid; i < 4 * NG * 16 * 16; i += 256) (&wbuf[0][0][0][0])[i] = (_Float16)0.f;
 
   // ---------------- prologue: query as integer pieces ----------------
   const float *qrot = reinterpret_cast<const float *>(p.ws + p.L.qrot);
@@ -245,11 +251,21 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
   };
   __shared__ __align__(16) uint32_t vbuf[4][D];   // per wave: V words of the current page
 
+  // code -> f16 (1 + code/4) masks, held in registers (opaque to the compiler)
+  // so that (x & m) | c selects one v_and_or_b32
+  uint32_t m_code, f16one;
+  asm volatile("s_mov_b32 %0, 0x3000300" : "=s"(m_code));
+  asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(f16one));
+  const int pvs = pv_slot(r16);
+
   auto process = [&](Stage &sg, int k) {
     if (!sg.ok) return;
     const int pg = p0 + w + 4 * k;
     const int ntok = hl - pg * kPage < kPage ? hl - pg * kPage : kPage;
+    // tokens past the history length: logit -inf, (scale, zero) read as 0
     const bool valid = r16 < ntok;
+    const float sinv = valid ? 0.f : -INFINITY;
+    const uint32_t vmask = valid ? 0xFFFFFFFFu : 0u;
 
     // V words to LDS (read back after the QK / softmax work)
 #pragma unroll
@@ -282,10 +298,11 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
       for (int g2 = 0; g2 < NG; ++g2) {
         const int dint = ((qacc[qd][g2][0] << 7) + qacc[qd][g2][1]) * 128 + qacc[qd][g2][2];
-        sc = fmaf(bf16_lo(sg.ks[g2]), (float)dint, sc);
-        zt = fmaf(bf16_hi(sg.ks[g2]), qzl[qd][g2], zt);
+        const uint32_t kz = sg.ks[g2] & vmask;
+        sc = fmaf(bf16_lo(kz), (float)dint, sc);
+        zt = fmaf(bf16_hi(kz), qzl[qd][g2], zt);
       }
-      s_[qd] = valid ? fmaf(sc, qscale[qd], zt) : -INFINITY;
+      s_[qd] = fmaf(sc, qscale[qd], zt) + sinv;
     }
 
     // ---------------- online softmax (exact running max per head) ----------------
@@ -296,7 +313,7 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
       mnew[qd] = fmaxf(m_run[qd], row_max(s_[qd]));
       grow |= mnew[qd] > m_run[qd];
     }
-    if (__any(grow)) {
+    if (__builtin_expect(__any(grow), 0)) {
       float alpha[NQ];
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
@@ -324,33 +341,30 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
     float pr[NQ];
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
-      pr[qd] = valid ? exp2f(s_[qd] - m_run[qd]) : 0.f;
+      pr[qd] = exp2f(s_[qd] - m_run[qd]);     // 0 for masked tokens
       lsum[qd] += pr[qd];
     }
 
     // ---------------- PV weights to LDS ----------------
 #pragma unroll
     for (int g2 = 0; g2 < NG; ++g2) {
-      const float vs = valid ? bf16_lo(sg.vs[g2]) : 0.f;
-      const float vz = valid ? bf16_hi(sg.vs[g2]) : 0.f;
+      const uint32_t vz_ = sg.vs[g2] & vmask;
+      const float vs = bf16_lo(vz_), vz = bf16_hi(vz_);
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
         const _Float16 wh = (_Float16)(pr[qd] * vs);
         zacc[qd][g2] = fmaf(pr[qd], vz, zacc[qd][g2]);
         zacc[qd][g2] = fmaf(-4.f, (float)wh, zacc[qd][g2]);
-        wbuf[w][g2][qd * 4 + kb][pv_slot(r16)] = wh;
+        wbuf[w][g2][qd * 4 + kb][pvs] = wh;
       }
     }
     wave_lds_sync();
     v4h apv[NG];
 #pragma unroll
     for (int g2 = 0; g2 < NG; ++g2) {
-      if (r16 < GQ) {
-        const uint2 u = *reinterpret_cast<const uint2 *>(&wbuf[w][g2][r16][4 * kb]);
-        apv[g2] = as_v4h(u.x, u.y);
-      } else {
-        apv[g2] = as_v4h(0u, 0u);
-      }
+      // rows >= GQ of wbuf stay zero: heads beyond GQ contribute nothing
+      const uint2 u = *reinterpret_cast<const uint2 *>(&wbuf[w][g2][r16][4 * kb]);
+      apv[g2] = as_v4h(u.x, u.y);
     }
     uint32_t vwd[NNB];
     load_words<NNB>(vwd, &vbuf[w][r16 * NNB]);
@@ -360,7 +374,7 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
     for (int nb = 0; nb < NNB; ++nb) {
       const uint32_t y = vwd[nb] >> (2 * kb);
-      const v4h bv = as_v4h(((y << 8) & 0x03000300u) | 0x3C003C00u, (y & 0x03000300u) | 0x3C003C00u);
+      const v4h bv = as_v4h(((y << 8) & m_code) | f16one, (y & m_code) | f16one);
       acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(apv[(16 * nb) / G], bv, acc[nb], 0, 0, 0);
     }
   };
