@@ -113,17 +113,17 @@ def build_workload(name: str, total_steps: int, device="cuda", log=print):
     return st
 
 
-def step_args(st, s: int, int2_kernel: int):
+def step_args(st, s: int, int2_kernel: int, num_splits: int = 0):
     from int2_rotated_kv_amd import binding as ob
     return ob.DecodeArgs(st.wl.B, st.wl.Hq, st.sc.hist_pages, st.hl[s], st.sc.bf16_pages, st.bl[s],
-                         int(st.hl_h[s].max()), int2_kernel=int2_kernel)
+                         int(st.hl_h[s].max()), int2_kernel=int2_kernel, num_splits=num_splits)
 
 
-def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False):
+def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0):
     import torch
     from int2_rotated_kv_amd import binding as ob
     T = steps + warmup
-    args = [step_args(st, s, int2_kernel) for s in range(T)]
+    args = [step_args(st, s, int2_kernel, num_splits) for s in range(T)]
     a_qb = [a.with_phases(ob.PHASE_QROT | ob.PHASE_BF16) for a in args]
     a_i2 = [a.with_phases(ob.PHASE_INT2) for a in args]
     ws = ob.alloc_workspace(st.sc.cache, args[-1])
@@ -318,6 +318,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="qwen3-8b-b32-100k")
     ap.add_argument("--int2-kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="history chunks per (sequence, KV head); 0 = the library's choice")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run 5 plain device-to-device copies of BYTES bytes (the "
@@ -343,7 +345,8 @@ def main(argv=None):
     torch.cuda.set_device(0)
     st = build_workload(a.workload, a.steps + a.warmup, log=log)
     wl = st.wl
-    r = run_steps(st, a.steps, a.warmup, kern, keep_first_out=not a.no_cpu_baseline)
+    r = run_steps(st, a.steps, a.warmup, kern, keep_first_out=not a.no_cpu_baseline,
+                  num_splits=a.splits)
     log(f"[bench] timed {a.steps} steps in {r['wall_s']:.3f}s")
 
     # per-step quantities over the timed steps

@@ -40,7 +40,7 @@
  *                              kb*(D/64) + blk holds channels 64*blk + 16*kb + i
  *                              in bits 2i (i = 0..15): 4 codes per byte
  *     V codes   [D]            one 32-bit word per channel, token t in bits 2t;
- *                              channel 16*nb + n stored at word n*(D/16) + nb
+ *                              channel c stored at word (c%64)*(D/64) + c/64
  *     K (s, z)  [16][D/G][2]   bf16 scale, bf16 zero per (token, group)
  *     V (s, z)  [16][D/G][2]
  *   Codes are in {0,1,2,3}; the dequantised rotated value is code*scale + zero.

@@ -287,10 +287,8 @@ __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
     const uint32_t vszw = part < NG ? reinterpret_cast<const uint32_t *>(rec + RL.vsz())[t * NG + part] : 0u;
     uint32_t vcw[CPL];
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-      const int c = lane + 64 * k;
-      vcw[k] = reinterpret_cast<const uint32_t *>(rec + RL.vcodes())[(c & 15) * (D / 16) + (c >> 4)];
-    }
+    for (int k = 0; k < CPL; ++k)   // channel lane + 64k at word lane*CPL + k
+      vcw[k] = reinterpret_cast<const uint32_t *>(rec + RL.vcodes())[lane * CPL + k];
 
     // ---- QK ----
     float sv[GQ];

@@ -202,8 +202,8 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
         }
       }
       uint8_t *rec = pool + ((size_t)page * Hkv + j) * RL.bytes();
-      // V word of channel c sits at position (c % 16) * (D/16) + c / 16
-      uint32_t *wp = reinterpret_cast<uint32_t *>(rec + RL.vcodes()) + (c & 15) * (D / 16) + (c >> 4);
+      // V word of channel c sits at position (c % 64) * (D/64) + c / 64
+      uint32_t *wp = reinterpret_cast<uint32_t *>(rec + RL.vcodes()) + (c & 63) * (D / 64) + (c >> 6);
       if (mask == 0xFFFFFFFFu) {
         *wp = bits;
       } else {

@@ -14,9 +14,10 @@
 //     A row; the three int32 results recombine exactly as p0*2^14 + p1*2^7 + p2.
 //   values  o[h, c] = sum_t w[h,t,g(c)] * code[t,c] + sum_t p[h,t] * zero[t,g(c)],
 //           w = p * scale_v
-//     sum_t w * code on v_mfma_f32_16x16x16_f16: B = codes as the exact f16
-//     values 1 + code/4, A = w in f16, fp32 accumulation; the "+1" part is
-//     removed with sum_t w (of the same f16 values).
+//     sum_t w * code on v_mfma_f32_4x4x4_16b_f16 (16 blocks of 4 heads x 4
+//     channels x 4 tokens, so lane l owns channels l, l+64): B = codes as the
+//     exact f16 values 1 + code/4, A = w in f16, fp32 accumulation; the "+1"
+//     part is removed with sum_t w (of the same f16 values).
 //
 // One block (4 waves) per (sequence, KV head, chunk of pages); each wave walks
 // every 4th page of the chunk with the next page's loads in flight, keeping an
@@ -47,6 +48,12 @@ __device__ __forceinline__ float row_max(float x) {
       "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf"
       : "+v"(x));
   return x;
+}
+// max of two floats that are finite or -inf (no NaN handling needed)
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 __device__ __forceinline__ float row_sum(float x) {
   asm volatile(
@@ -102,7 +109,7 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
   constexpr int NBLK = D / 64;         // 64-channel blocks (one int8 MFMA K each)
   constexpr int GPB = G < 64 ? 64 / G : 1;   // groups inside one 64-channel block
   constexpr int NQK = NBLK * GPB;      // QK MFMAs per head quad per page
-  constexpr int NNB = D / 16;          // 16-channel N blocks of PV
+  constexpr int NH = D / 64;           // 64-channel halves of PV (lane owns l + 64*h2)
   constexpr int NQ = GQ / 4;           // head quads
   static_assert(GQ == 4 || GQ == 8, "4 or 8 q heads per KV head");
 
@@ -118,11 +125,9 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
   __shared__ float qf[GQ][D];                    // q_rot (unscaled)
   __shared__ int qexp[GQ];                       // q_int = rint(q * 2^qexp)
   __shared__ float qz[GQ][NG];                   // sm_log2 * sum of q over the group
-  __shared__ __align__(16) _Float16 wbuf[4][NG][16][16];       // per wave: w[grp][head row][slot]
+  __shared__ __align__(16) _Float16 wbuf[4][NG][GQ][16];       // per wave: w[grp][head][slot]
   __shared__ float wm[4][GQ], wl[4][GQ];
   __shared__ float wo[4][GQ][D];
-
-  for (int i = tid; i < 4 * NG * 16 * 16; i += 256) (&wbuf[0][0][0][0])[i] = (_Float16)0.f;
 
   // ---------------- prologue: query as integer pieces ----------------
   const float *qrot = reinterpret_cast<const float *>(p.ws + p.L.qrot);
@@ -208,15 +213,17 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
     for (int g2 = 0; g2 < NG; ++g2) zacc[qd][g2] = 0.f;
   }
-  // PV accumulators: row = head (rows 0..GQ-1 real), column = channel 16*nb + r16
-  v4f acc[NNB];
+  // PV accumulators: acc[qd][h2][i] = o[head 4*qd + i][channel lane + 64*h2]
+  v4f acc[NQ][NH];
 #pragma unroll
-  for (int nb = 0; nb < NNB; ++nb) acc[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+    for (int h2 = 0; h2 < NH; ++h2) acc[qd][h2] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // ---------------- page loop: 4-stage register ring ----------------
   // stage data of one page for this lane: K words of token r16 / lane group kb,
-  // K and V (scale, zero) words of token r16, and VPL distinct V words
-  // (redistributed through LDS before use).
+  // K and V (scale, zero) words of token r16, and the V words of channels
+  // lane + 64*h2 (adjacent in the record).
   constexpr int NS = 4;
   constexpr int VPL = D / 64;
   struct Stage {
@@ -249,8 +256,6 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
     load_words<NG>(sg.vs, reinterpret_cast<const uint32_t *>(rec + RL.vsz()) + r16 * NG);
     load_words<VPL>(sg.v, reinterpret_cast<const uint32_t *>(rec + RL.vcodes()) + lane * VPL);
   };
-  __shared__ __align__(16) uint32_t vbuf[4][D];   // per wave: V words of the current page
-
   // code -> f16 (1 + code/4) masks, held in registers (opaque to the compiler)
   // so that (x & m) | c selects one v_and_or_b32
   uint32_t m_code, f16one;
@@ -262,14 +267,16 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
     if (!sg.ok) return;
     const int pg = p0 + w + 4 * k;
     const int ntok = hl - pg * kPage < kPage ? hl - pg * kPage : kPage;
-    // tokens past the history length: logit -inf, (scale, zero) read as 0
-    const bool valid = r16 < ntok;
-    const float sinv = valid ? 0.f : -INFINITY;
-    const uint32_t vmask = valid ? 0xFFFFFFFFu : 0u;
-
-    // V words to LDS (read back after the QK / softmax work)
+    // tokens past the history length (only on a sequence's last, partial page):
+    // logit -inf and (scale, zero) read as 0, since unwritten record bytes may
+    // hold any bit pattern
+    const bool partial = ntok < kPage;           // wave-uniform
+    if (partial) {
+      const uint32_t vmask = r16 < ntok ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) vbuf[w][lane * VPL + i] = sg.v[i];
+      for (int g2 = 0; g2 < NG; ++g2) { sg.ks[g2] &= vmask; sg.vs[g2] &= vmask; }
+    }
+    const float sinv = r16 < ntok ? 0.f : -INFINITY;
 
     // ---------------- QK on int8 MFMA ----------------
     v4i qacc[NQ][NG];
@@ -298,9 +305,8 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
       for (int g2 = 0; g2 < NG; ++g2) {
         const int dint = ((qacc[qd][g2][0] << 7) + qacc[qd][g2][1]) * 128 + qacc[qd][g2][2];
-        const uint32_t kz = sg.ks[g2] & vmask;
-        sc = fmaf(bf16_lo(kz), (float)dint, sc);
-        zt = fmaf(bf16_hi(kz), qzl[qd][g2], zt);
+        sc = fmaf(bf16_lo(sg.ks[g2]), (float)dint, sc);
+        zt = fmaf(bf16_hi(sg.ks[g2]), qzl[qd][g2], zt);
       }
       s_[qd] = fmaf(sc, qscale[qd], zt) + sinv;
     }
@@ -310,46 +316,41 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
     float mnew[NQ];
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
-      mnew[qd] = fmaxf(m_run[qd], row_max(s_[qd]));
+      mnew[qd] = max_raw(m_run[qd], row_max(s_[qd]));
       grow |= mnew[qd] > m_run[qd];
     }
     if (__builtin_expect(__any(grow), 0)) {
       float alpha[NQ];
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
-        alpha[qd] = m_run[qd] == -INFINITY ? 0.f : exp2f(m_run[qd] - mnew[qd]);
+        alpha[qd] = m_run[qd] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qd] - mnew[qd]);
         m_run[qd] = mnew[qd];
         lsum[qd] *= alpha[qd];
 #pragma unroll
         for (int g2 = 0; g2 < NG; ++g2) zacc[qd][g2] *= alpha[qd];
       }
-      // accumulator row 4*kb + r is head 4*kb + r; head h's alpha is uniform
-      // over the 16 lanes 16*(h%4) .. of head quad h/4
-      float ar[4];
+      // accumulator element i of head quad qd is head 4*qd + i, whose alpha is
+      // uniform over the 16 lanes 16*i .. of quad qd
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[0]), 16 * r));
-        float a1 = a0;
-        if constexpr (NQ > 1) a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[NQ - 1]), 16 * r));
-        ar[r] = kb == 0 ? a0 : a1;
-      }
+      for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-      for (int nb = 0; nb < NNB; ++nb)
+        for (int i = 0; i < 4; ++i) {
+          const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[qd]), 16 * i));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[nb][r] *= ar[r];
+          for (int h2 = 0; h2 < NH; ++h2) acc[qd][h2][i] *= a;
+        }
     }
     float pr[NQ];
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
-      pr[qd] = exp2f(s_[qd] - m_run[qd]);     // 0 for masked tokens
+      pr[qd] = __builtin_amdgcn_exp2f(s_[qd] - m_run[qd]);   // 0 for masked tokens
       lsum[qd] += pr[qd];
     }
 
     // ---------------- PV weights to LDS ----------------
 #pragma unroll
     for (int g2 = 0; g2 < NG; ++g2) {
-      const uint32_t vz_ = sg.vs[g2] & vmask;
-      const float vs = bf16_lo(vz_), vz = bf16_hi(vz_);
+      const float vs = bf16_lo(sg.vs[g2]), vz = bf16_hi(sg.vs[g2]);
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
         const _Float16 wh = (_Float16)(pr[qd] * vs);
@@ -359,24 +360,26 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
       }
     }
     wave_lds_sync();
-    v4h apv[NG];
-#pragma unroll
-    for (int g2 = 0; g2 < NG; ++g2) {
-      // rows >= GQ of wbuf stay zero: heads beyond GQ contribute nothing
-      const uint2 u = *reinterpret_cast<const uint2 *>(&wbuf[w][g2][r16][4 * kb]);
-      apv[g2] = as_v4h(u.x, u.y);
-    }
-    uint32_t vwd[NNB];
-    load_words<NNB>(vwd, &vbuf[w][r16 * NNB]);
-    wave_lds_sync();
 
-    // ---------------- PV on f16 MFMA ----------------
+    // ---------------- PV on f16 MFMA, 4 token quads ----------------
+    // quad ti: tokens (ti, ti+8, ti+4, ti+12) as k = 0..3; token t of a V word
+    // sits in bits 2t, so v << (8 - 2ti) and v >> 2ti put each pair at f16
+    // mantissa bits 8..9 / 24..25
 #pragma unroll
-    for (int nb = 0; nb < NNB; ++nb) {
-      const uint32_t y = vwd[nb] >> (2 * kb);
-      const v4h bv = as_v4h(((y << 8) & m_code) | f16one, (y & m_code) | f16one);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(apv[(16 * nb) / G], bv, acc[nb], 0, 0, 0);
+    for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+      for (int h2 = 0; h2 < NH; ++h2) {
+        const uint32_t v = sg.v[h2];
+        const v4h bv = as_v4h(((v << (8 - 2 * ti)) & m_code) | f16one, ((v >> (2 * ti)) & m_code) | f16one);
+        const int g2 = (lane + 64 * h2) / G;
+#pragma unroll
+        for (int qd = 0; qd < NQ; ++qd) {
+          const uint2 u = *reinterpret_cast<const uint2 *>(&wbuf[w][g2][qd * 4 + (lane & 3)][4 * ti]);
+          acc[qd][h2] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_v4h(u.x, u.y), bv, acc[qd][h2], 0, 0, 0);
+        }
+      }
     }
+    wave_lds_sync();
   };
 
   if (nk > 0) {
@@ -419,16 +422,15 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
     for (int g2 = 0; g2 < NG; ++g2) zst[h][g2] = wo[w][h][g2];
   wave_lds_sync();
-  // accumulator element r of lane (kb, r16) is row 4*kb + r, channel 16*nb + r16
+  // accumulator element i of quad qd, half h2: head 4*qd + i, channel lane + 64*h2
 #pragma unroll
-  for (int nb = 0; nb < NNB; ++nb) {
-    const int c = 16 * nb + r16;
+  for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * kb + r;
-      if (h < GQ) wo[w][h][c] = 4.f * acc[nb][r] + zst[h][c / G];
+    for (int h2 = 0; h2 < NH; ++h2) {
+      const int c = lane + 64 * h2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wo[w][4 * qd + i][c] = 4.f * acc[qd][h2][i] + zst[4 * qd + i][c / G];
     }
-  }
   __syncthreads();
 
   // ---------------- combine the 4 waves, write the chunk partial ----------------

@@ -244,11 +244,13 @@ def k_row_words(codes_row) -> np.ndarray:
 
 
 def v_word_order(D: int) -> np.ndarray:
-    """Channel stored at each V-code word position: position n*(D/16) + nb holds
-    channel 16*nb + n."""
+    """Channel stored at each V-code word position: position (c % 64)*(D/64) + c//64
+    holds channel c, so the D/64 channels c, c+64, ... of one reader lane are
+    adjacent.  For D = 64 this is channel order."""
+    nh = max(1, D // 64)
     pos = np.empty(D, dtype=np.int64)
     for c in range(D):
-        pos[(c % 16) * (D // 16) + c // 16] = c
+        pos[(c % 64) * nh + c // 64] = c
     return pos
 
 

@@ -226,9 +226,10 @@ def test_channel_major_layout():
     c[5, 2] = 3          # token 5, channel 2 -> channel 2's word, bits 10..11
     w = orc.pack_channel_major(c)
     assert w.shape == (8,) and w[2] == 3 << 10 and w.sum() == 3 << 10
-    # V words are stored channel 16*nb + n at position n*(D/16) + nb
+    # V words: channel c at position (c % 64) * (D/64) + c // 64
     order = orc.v_word_order(128)
-    assert order[9] == 17 and order[0] == 0 and order[1] == 16 and order[8] == 1
+    assert order[0] == 0 and order[1] == 64 and order[2] == 1 and order[35] == 81
+    assert list(orc.v_word_order(64)) == list(range(64))
 
 
 def test_k_row_word_order():
@@ -415,14 +416,14 @@ def test_bits_per_element_printed_values():
 
 def test_record_layout_hand_placed():
     """Byte positions of the page-record layout for D=64, G=32 (record = K words
-    [16][4] | V words [64] | K (scale,zero) [16][2][2] bf16 | V (scale,zero)
+    [16][4] | V words [64] (channel order at D = 64) | K (scale,zero) [16][2][2] bf16 | V (scale,zero)
     [16][2][2] bf16 = 256 + 256 + 128 + 128 bytes), worked by hand."""
     D, G = 64, 32
     kc = np.zeros((16, D), np.uint8); vc = np.zeros((16, D), np.uint8)
     ks = np.zeros((16, 2)); kz = np.zeros((16, 2)); vs = np.zeros((16, 2)); vz = np.zeros((16, 2))
     kc[3, 37] = 2         # token 3, channel 37: word 3*4 + 2, bits 10..11 -> byte 57 = 0x08
-    vc[9, 6] = 3          # channel 6 at word 6*4 + 0 = 24, token 9 bits 18..19 -> byte 256+96+2 = 0x0C
-    vc[0, 17] = 1         # channel 17 at word 1*4 + 1 = 5, token 0 -> byte 256+20 = 0x01
+    vc[9, 6] = 3          # channel 6 at word 6, token 9 bits 18..19 -> byte 256+24+2 = 0x0C
+    vc[0, 17] = 1         # channel 17 at word 17, token 0 -> byte 256+68 = 0x01
     ks[2, 1] = 1.0        # K (s, z) of token 2 group 1 at 512 + (2*2+1)*4 -> 0x3F80
     kz[2, 1] = -2.0       # zero -> 0xC000 right after
     vz[15, 0] = 0.5       # V block: 640 + (15*2+0)*4 + 2 -> 0x3F00
@@ -430,8 +431,8 @@ def test_record_layout_hand_placed():
     assert rec.size == 768
     want = np.zeros(768, np.uint8)
     want[57] = 0x08
-    want[256 + 96 + 2] = 0x0C
-    want[256 + 20] = 0x01
+    want[256 + 24 + 2] = 0x0C
+    want[256 + 68] = 0x01
     want[532:536] = [0x80, 0x3F, 0x00, 0xC0]
     want[640 + 120 + 2:640 + 120 + 4] = [0x00, 0x3F]
     assert np.array_equal(rec, want)
