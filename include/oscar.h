@@ -35,14 +35,16 @@
  *
  * Cache layout (HBM)
  *   INT2 history pool: uint8 [num_int2_pages][Hkv][oscar_record_bytes(D, G)].
- *   One record holds 16 tokens of one KV head:
- *     K codes   [16][D/16]     per token D/16 little-endian 32-bit words; word
- *                              kb*(D/64) + blk holds channels 64*blk + 16*kb + i
- *                              in bits 2i (i = 0..15): 4 codes per byte
- *     V codes   [D]            one 32-bit word per channel, token t in bits 2t;
- *                              channel c stored at word (c%64)*(D/64) + c/64
- *     K (s, z)  [16][D/G][2]   bf16 scale, bf16 zero per (token, group)
- *     V (s, z)  [16][D/G][2]
+ *   One record holds 16 tokens of one KV head, as little-endian 32-bit words:
+ *     code region   64 lane slots of D/32 words.  Slot l = 16*kb + t holds
+ *                   the D/64 K words of token t, part kb (word blk: channels
+ *                   64*blk + 16*kb + i in bits 2i, i = 0..15), then the D/64
+ *                   V words of channels l, l+64, ... (token t in bits 2t)
+ *     (s, z) region 16 token slots of 2*D/G words: the K words of groups
+ *                   0..D/G-1, then the V words; each word is bf16 scale in
+ *                   bits 0..15 and bf16 zero in bits 16..31
+ *   A reader lane l takes slot l and token slot l % 16 with one 16-byte load
+ *   each (D = 128, G = 64).
  *   Codes are in {0,1,2,3}; the dequantised rotated value is code*scale + zero.
  *   BF16 pools: uint16 [num_bf16_pages][Hkv][16][D], one for K and one for V.
  *   A token slot is page*16 + offset within the page.
@@ -81,7 +83,9 @@ enum {
   OSCAR_PHASE_ALL = 7
 };
 
-/* Which kernel computes the INT2 segment. */
+/* Which kernel computes the INT2 segment.  AUTO picks MFMA when every KV head
+ * serves 4 or 8 q heads, else VALU; asking for MFMA with another ratio is
+ * EUNSUPPORTED from every call that takes the arguments. */
 enum {
   OSCAR_INT2_AUTO = 0,
   OSCAR_INT2_VALU = 1,      /* vector-ALU dot products                         */
@@ -173,8 +177,9 @@ int oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_ar
  * oscar_decode_plan - the history chunking oscar_decode_attn will use for these
  * arguments (host only): num_splits chunks of pages_per_split pages per
  * (sequence, KV head), and the workspace size.  Any output may be NULL.
- * Automatic chunking (num_splits == 0) aims at 2048 blocks in flight while
- * keeping every chunk at least 50x the bytes of its partial result.
+ * Automatic chunking (num_splits == 0) aims at 8192 (MFMA kernel) or 2048
+ * (VALU kernel) (sequence, KV head, chunk) units while keeping every chunk at
+ * least 50x the bytes of its partial result and 16 pages long.
  */
 int oscar_decode_plan(const oscar_cache *cache, const oscar_decode_args *args,
                       int32_t *num_splits, int32_t *pages_per_split, size_t *workspace_bytes);

@@ -129,8 +129,18 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   const float sm = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt((float)c->head_dim);
   p->sm_log2 = sm * kLog2e;
 
-  // history split: enough blocks to fill the chip, but each block streams
-  // enough pages that the chunk partials stay ~2% of the history bytes
+  // INT2 kernel: the matrix-core one needs 4 or 8 q heads per KV head
+  const bool mfma_ok = p->g == 4 || p->g == 8;
+  int kind = a->int2_kernel;
+  if (kind == OSCAR_INT2_AUTO) kind = mfma_ok ? OSCAR_INT2_MFMA : OSCAR_INT2_VALU;
+  if (kind == OSCAR_INT2_MFMA && !mfma_ok)
+    return fail(OSCAR_EUNSUPPORTED,
+                "matrix-core INT2 kernel needs 4 or 8 q heads per KV head (got %d)", p->g);
+  p->int2_kind = kind;
+
+  // history split: enough waves to fill the chip (the vector-ALU kernel runs
+  // 4 waves per (sequence, KV head, chunk), the matrix-core one 1), but each
+  // chunk streams enough pages that its partials stay ~2% of its history bytes
   const int npages = need_hist;
   int S = 1;
   if (npages > 0) {
@@ -138,7 +148,7 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
       S = a->num_splits < npages ? a->num_splits : npages;
     } else {
       const int units = a->batch * c->num_kv_heads;
-      const int target_blocks = 2048;
+      const int target_blocks = kind == OSCAR_INT2_MFMA ? 8192 : 2048;
       const double rec = (double)RecLayout(p->D, p->G).bytes();
       const double part_bytes = 2.0 * p->g * (p->D + 2) * 4.0;   // write + read back
       int min_pages = (int)std::ceil(50.0 * part_bytes / rec);
@@ -264,12 +274,7 @@ int oscar_decode_attn(const oscar_cache *cache, const oscar_decode_args *args, c
     if (e != hipSuccess) return hip_fail(e, "BF16 segment launch");
   }
   if ((ph & OSCAR_PHASE_INT2) && args->max_hist_len > 0) {
-    const bool mfma_ok = p.g == 4 || p.g == 8;
-    int kind = args->int2_kernel;
-    if (kind == OSCAR_INT2_AUTO) kind = mfma_ok ? OSCAR_INT2_MFMA : OSCAR_INT2_VALU;
-    if (kind == OSCAR_INT2_MFMA && !mfma_ok)
-      return fail(OSCAR_EUNSUPPORTED, "matrix-core INT2 kernel needs 4 or 8 q heads per KV head (got %d)", p.g);
-    e = kind == OSCAR_INT2_MFMA ? launch_int2_mfma(p, s) : launch_int2_valu(p, s);
+    e = p.int2_kind == OSCAR_INT2_MFMA ? launch_int2_mfma(p, s) : launch_int2_valu(p, s);
     if (e != hipSuccess) return hip_fail(e, "INT2 segment launch");
   }
   return OSCAR_OK;

@@ -19,13 +19,22 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Byte offsets of the four sections of one INT2 page record (16 tokens, one KV
 // head): K codes [16][D/4] | V codes [D][4] | K (s,z) [16][D/G] dwords | V (s,z).
 struct RecLayout {
+  // One (page, KV head) record: a code region of 64 lane slots of D/32 words
+  // (slot l = 16*kb + t: the D/64 K words of token t, part kb, then the D/64 V
+  // words of channels l, l + 64, ...) and a scale/zero region of 16 token
+  // slots of 2*D/G words (K groups, then V groups; scale | zero << 16).
   int D, G;
   __host__ __device__ constexpr RecLayout(int d, int g) : D(d), G(g) {}
-  __host__ __device__ constexpr int kcodes() const { return 0; }
-  __host__ __device__ constexpr int vcodes() const { return kPage * (D / 4); }
-  __host__ __device__ constexpr int ksz() const { return 2 * kPage * (D / 4); }
-  __host__ __device__ constexpr int vsz() const { return 2 * kPage * (D / 4) + kPage * (D / G) * 4; }
-  __host__ __device__ constexpr int bytes() const { return 2 * kPage * (D / 4) + 2 * kPage * (D / G) * 4; }
+  __host__ __device__ constexpr int slot_words() const { return D / 32; }
+  __host__ __device__ constexpr int codes_bytes() const { return 64 * (D / 32) * 4; }
+  __host__ __device__ constexpr int tok_words() const { return 2 * (D / G); }
+  // byte offsets
+  __host__ __device__ constexpr int kword(int slot, int blk) const { return (slot * (D / 32) + blk) * 4; }
+  __host__ __device__ constexpr int vword(int slot, int h2) const { return (slot * (D / 32) + D / 64 + h2) * 4; }
+  __host__ __device__ constexpr int tok_sz(int t) const { return codes_bytes() + t * tok_words() * 4; }
+  __host__ __device__ constexpr int ksz(int t, int g) const { return tok_sz(t) + g * 4; }
+  __host__ __device__ constexpr int vsz(int t, int g) const { return tok_sz(t) + (D / G + g) * 4; }
+  __host__ __device__ constexpr int bytes() const { return codes_bytes() + kPage * tok_words() * 4; }
 };
 
 // bf16 bit pattern -> float (exact)
@@ -62,6 +71,7 @@ struct DecodeParams {
   const int32_t *bf16_len;
   int max_hist_len;
   float sm_log2;       // softmax scale * log2(e)
+  int int2_kind;       // resolved INT2 kernel: OSCAR_INT2_VALU or OSCAR_INT2_MFMA
   int splits, pages_per_split;
   uint8_t *ws;
   WsLayout L;

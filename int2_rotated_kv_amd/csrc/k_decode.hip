@@ -201,8 +201,8 @@ hipError_t launch_bf16_seg(const DecodeParams &p, const uint16_t *q, hipStream_t
 // INT2 history segment, vector-ALU variant.  One block (4 waves) per
 // (sequence, KV head, chunk of pages); each wave walks every 4th page of the
 // chunk.  Per page (16 tokens):
-//   QK:  lane (t = lane%16, part = lane/16) takes K words part*KW .. +KW-1 of
-//        token t (16 channels each), dots them with q_rot and applies each
+//   QK:  lane (t = lane%16, part = lane/16) takes the KW K words of token t,
+//        part `part` (16 channels each), dots them with q_rot and applies each
 //        word's group scale/zero: s = scale * sum(q*code) + zero * sum(q); the
 //        four parts are summed across lanes.
 //   softmax: running max per head over the 16 token lanes; p = 2^(s - m).
@@ -276,19 +276,18 @@ __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
     const int ntok = hl - pg * kPage < kPage ? hl - pg * kPage : kPage;
 
     // ---- loads ----
-    const uint32_t *kr = reinterpret_cast<const uint32_t *>(rec + RL.kcodes() + t * (D / 4)) + part * KW;
+    // lane slot `lane` (= 16*part + t) holds this lane's K and V words
     uint32_t kw[KW];
 #pragma unroll
-    for (int i = 0; i < KW; ++i) kw[i] = kr[i];
-    const uint32_t *kszp = reinterpret_cast<const uint32_t *>(rec + RL.ksz()) + t * NG;
+    for (int i = 0; i < KW; ++i) kw[i] = *reinterpret_cast<const uint32_t *>(rec + RL.kword(lane, i));
     uint32_t ksz[NG];
 #pragma unroll
-    for (int g2 = 0; g2 < NG; ++g2) ksz[g2] = kszp[g2];
-    const uint32_t vszw = part < NG ? reinterpret_cast<const uint32_t *>(rec + RL.vsz())[t * NG + part] : 0u;
+    for (int g2 = 0; g2 < NG; ++g2) ksz[g2] = *reinterpret_cast<const uint32_t *>(rec + RL.ksz(t, g2));
+    const uint32_t vszw = part < NG ? *reinterpret_cast<const uint32_t *>(rec + RL.vsz(t, part)) : 0u;
     uint32_t vcw[CPL];
 #pragma unroll
-    for (int k = 0; k < CPL; ++k)   // channel lane + 64k at word lane*CPL + k
-      vcw[k] = reinterpret_cast<const uint32_t *>(rec + RL.vcodes())[lane * CPL + k];
+    for (int k = 0; k < CPL; ++k)   // channel lane + 64k
+      vcw[k] = *reinterpret_cast<const uint32_t *>(rec + RL.vword(lane, k));
 
     // ---- QK ----
     float sv[GQ];

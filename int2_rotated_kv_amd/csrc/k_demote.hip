@@ -159,16 +159,15 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
     if (d >= 0 && (c % G) == 0) {
       const int64_t page = d >> 4, off = d & 15;
       uint8_t *rec = pool + ((size_t)page * Hkv + j) * RL.bytes();
-      uint32_t *sz = reinterpret_cast<uint32_t *>(rec + (isv ? RL.vsz() : RL.ksz()));
-      sz[off * (D / G) + c / G] = (uint32_t)sb | ((uint32_t)zb << 16);
+      const int o = isv ? RL.vsz((int)off, c / G) : RL.ksz((int)off, c / G);
+      *reinterpret_cast<uint32_t *>(rec + o) = (uint32_t)sb | ((uint32_t)zb << 16);
     }
   }
 
   if (!isv) {
-    // K: token-major rows of D/16 words; word kb*(D/64) + blk holds channels
-    // 64*blk + 16*kb + i at bits 2i
-    constexpr int NBLK = D / 64;
-    const int kword = ((c & 63) >> 4) * NBLK + (c >> 6);
+    // K: word blk of lane slot 16*kb + t holds channels 64*blk + 16*kb + i of
+    // token t at bits 2i
+    const int kb = (c & 63) >> 4, blk = c >> 6;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       uint32_t w = codes[t] << (2 * (c & 15));
@@ -178,7 +177,7 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
       if (d >= 0 && (c & 15) == 0) {
         const int64_t page = d >> 4, off = d & 15;
         uint8_t *rec = pool + ((size_t)page * Hkv + j) * RL.bytes();
-        reinterpret_cast<uint32_t *>(rec + RL.kcodes() + off * (D / 4))[kword] = w;
+        *reinterpret_cast<uint32_t *>(rec + RL.kword(16 * kb + (int)off, blk)) = w;
       }
     }
   } else {
@@ -202,8 +201,8 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
         }
       }
       uint8_t *rec = pool + ((size_t)page * Hkv + j) * RL.bytes();
-      // V word of channel c sits at position (c % 64) * (D/64) + c / 64
-      uint32_t *wp = reinterpret_cast<uint32_t *>(rec + RL.vcodes()) + (c & 63) * (D / 64) + (c >> 6);
+      // V word of channel c: lane slot c % 64, V word c / 64
+      uint32_t *wp = reinterpret_cast<uint32_t *>(rec + RL.vword(c & 63, c >> 6));
       if (mask == 0xFFFFFFFFu) {
         *wp = bits;
       } else {

@@ -16,13 +16,19 @@
 //           w = p * scale_v
 //     sum_t w * code on v_mfma_f32_4x4x4_16b_f16 (16 blocks of 4 heads x 4
 //     channels x 4 tokens, so lane l owns channels l, l+64): B = codes as the
-//     exact f16 values 1 + code/4, A = w in f16, fp32 accumulation; the "+1"
-//     part is removed with sum_t w (of the same f16 values).
+//     exact f16 values 1 + code * 2^(b-10), the code masked into mantissa bit
+//     b in {4, 6, 8} of its half straight from the packed word or one of two
+//     shifted copies; A = w * 2^(8-b) in f16, so A * B = A + w * code / 4;
+//     fp32 accumulation; the A part is removed with sum_t A (same f16 values).
 //
-// One block (4 waves) per (sequence, KV head, chunk of pages); each wave walks
-// every 4th page of the chunk with the next page's loads in flight, keeping an
-// exact running max per head (16-lane DPP reductions).  Requires 4 or 8 q heads
-// per KV head and V group scales below the f16 range (65504).
+// One block per (sequence, chunk of pages, group of up to 8 KV heads), one wave
+// per KV head.  The waves of a block walk the same pages, so the records of all
+// KV heads of a page (adjacent in the pool) are read together; each wave keeps
+// 3 pages in flight in a register ring and writes its own chunk partial.  The
+// running max per head is lazy: it is raised (16-lane DPP reductions, rescale
+// of the partial sums) only when a logit exceeds it by more than 2 (log2
+// units), so unnormalised weights stay below 4.  Requires 4 or 8 q heads per KV
+// head and V group scales below 1024 (A = w * 16 must stay in f16 range).
 #include "common.hpp"
 
 namespace oscar {
@@ -76,11 +82,16 @@ __device__ __forceinline__ v4h as_v4h(uint32_t a, uint32_t b) {
   return r;
 }
 
-// k-slot order shared by the PV operands: lane group kb, element i <-> token
-// kb + {0, 8, 4, 12}[i]; token t sits in slot 4*(t%4) + e(t/4), e = {0,2,1,3}.
-__device__ __forceinline__ int pv_slot(int t) {
-  const int i = t >> 2;
-  return 4 * (t & 3) + (((i & 1) << 1) | (i >> 1));
+// k-slot order shared by the PV operands: token pair u = 0..7 is (u, u + 8),
+// held by the two f16 halves of one B register; MFMA ti takes pairs 2ti and
+// 2ti + 1, so token t sits in A slot 2 * (t % 8) + t / 8.
+__device__ __forceinline__ int pv_slot(int t) { return 2 * (t & 7) + (t >> 3); }
+// mantissa bit b of token pair u in its B register (x1 = v << 4, x0 = v,
+// x2 = v >> 6): u = 0, 1, 2 from x1 at 4, 6, 8; u = 3, 4 from x0 at 6, 8;
+// u = 5, 6, 7 from x2 at 4, 6, 8.  A carries the factor 2^(8 - b).
+__device__ __forceinline__ float pv_factor(int t) {
+  const int u = t & 7;
+  return (u == 0 || u == 5) ? 16.f : (u == 1 || u == 3 || u == 6) ? 4.f : 1.f;
 }
 
 template <int NW>
@@ -102,8 +113,10 @@ __device__ __forceinline__ void load_words(uint32_t (&dst)[NW], const uint32_t *
 
 }  // namespace
 
+constexpr int kMfmaHeadsPerBlock = 8;
+
 template <int D, int G, int GQ>
-__global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
+__global__ __launch_bounds__(64 * kMfmaHeadsPerBlock) void k_int2_mfma(DecodeParams p) {
   constexpr RecLayout RL(D, G);
   constexpr int NG = D / G;            // groups per token
   constexpr int NBLK = D / 64;         // 64-channel blocks (one int8 MFMA K each)
@@ -111,46 +124,59 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
   constexpr int NQK = NBLK * GPB;      // QK MFMAs per head quad per page
   constexpr int NH = D / 64;           // 64-channel halves of PV (lane owns l + 64*h2)
   constexpr int NQ = GQ / 4;           // head quads
+  constexpr int HB = kMfmaHeadsPerBlock;
   static_assert(GQ == 4 || GQ == 8, "4 or 8 q heads per KV head");
 
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave (uniform)
+  const int nwav = blockDim.x >> 6;
+  const int ngrp = (p.Hkv + nwav - 1) / nwav;
   const int S = p.splits;
-  const int unit = blockIdx.x / S;
-  const int split = blockIdx.x % S;
-  const int b = unit / p.Hkv;
-  const int j = unit % p.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
-  const int r16 = lane & 15, kb = lane >> 4;     // row-in-16 and lane group
+  const int hg = blockIdx.x % ngrp;
+  const int split = (blockIdx.x / ngrp) % S;
+  const int b = blockIdx.x / (ngrp * S);
+  const int j = hg * nwav + w;                    // this wave's KV head
+  if (j >= p.Hkv) return;                         // no block-level barrier follows
+  const int r16 = lane & 15, kb = lane >> 4;      // row-in-16 and lane group
 
-  __shared__ float qf[GQ][D];                    // q_rot (unscaled)
-  __shared__ int qexp[GQ];                       // q_int = rint(q * 2^qexp)
-  __shared__ float qz[GQ][NG];                   // sm_log2 * sum of q over the group
-  __shared__ __align__(16) _Float16 wbuf[4][NG][GQ][16];       // per wave: w[grp][head][slot]
-  __shared__ float wm[4][GQ], wl[4][GQ];
-  __shared__ float wo[4][GQ][D];
+  __shared__ float qf_all[HB][GQ][D];             // per wave: q_rot (unscaled)
+  __shared__ __align__(16) _Float16 wbuf_all[HB][NG][GQ][16];   // per wave: w[grp][head][slot]
+  float (*qf)[D] = qf_all[w];
+  _Float16 (*wbuf)[GQ][16] = wbuf_all[w];
 
-  // ---------------- prologue: query as integer pieces ----------------
+  // ---------------- prologue: the wave's q heads as integer pieces ----------------
   const float *qrot = reinterpret_cast<const float *>(p.ws + p.L.qrot);
-  for (int i = tid; i < GQ * D; i += 256) {
-    const int h = i / D, c = i % D;
-    qf[h][c] = qrot[((size_t)b * p.Hq + p.q_of_kv[j * GQ + h]) * D + c];
-  }
-  __syncthreads();
-  if (tid < GQ) {
+  int qexp[GQ];
+  float qz[GQ][NG];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    const float *src = qrot + ((size_t)b * p.Hq + p.q_of_kv[j * GQ + h]) * D;
     float mx = 0.f;
-    for (int c = 0; c < D; ++c) mx = fmaxf(mx, fabsf(qf[tid][c]));
+    float gs[NG];
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) gs[g2] = 0.f;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      const float v = src[lane + 64 * k];
+      qf[h][lane + 64 * k] = v;
+      mx = fmaxf(mx, fabsf(v));
+      gs[(lane + 64 * k) / G] += v;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) {
+      float t = gs[g2];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+      qz[h][g2] = t * p.sm_log2;
+    }
     int e = 0;
     if (mx > 0.f) (void)frexpf(mx, &e);          // mx < 2^e
     int qe = mx > 0.f ? 20 - e : 0;              // |q| * 2^qexp < 2^20
-    qexp[tid] = qe > 126 ? 126 : (qe < -100 ? -100 : qe);
+    qexp[h] = qe > 126 ? 126 : (qe < -100 ? -100 : qe);
   }
-  if (tid >= 64 && tid < 64 + GQ * NG) {
-    const int h = (tid - 64) / NG, g2 = (tid - 64) % NG;
-    float s = 0.f;
-    for (int c = g2 * G; c < (g2 + 1) * G; ++c) s += qf[h][c];
-    qz[h][g2] = s * p.sm_log2;
-  }
-  __syncthreads();
+  wave_lds_sync();
 
   // A operands: row = 4*h + piece (piece 3 is zero), lane group kb, VGPR e,
   // byte bb <-> channel 64*blk + 16*kb + 4*bb + e (the B unpack order).
@@ -159,8 +185,11 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
     const int hrow = r16 >> 2, pc = r16 & 3;
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
+      int qe_row = qexp[0];
+#pragma unroll
+      for (int h = 1; h < GQ; ++h) qe_row = (h == qd * 4 + hrow) ? qexp[h] : qe_row;
+      const float sc = ldexpf(1.f, qe_row);
       const int h = qd * 4 + hrow;
-      const float sc = ldexpf(1.f, qexp[h]);
 #pragma unroll
       for (int m = 0; m < NQK; ++m) {
         const int blk = m / GPB, gsub = m % GPB;
@@ -185,14 +214,25 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
       }
     }
   }
-  // per-lane constants of the (head, token) layout of the QK result
+  // per-lane constants of the (head, token) layout of the QK result:
+  // lane (kb, r16) holds head 4*qd + kb, token r16
   float qscale[NQ], qzl[NQ][NG];
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
-    const int h = qd * 4 + kb;
-    qscale[qd] = ldexpf(1.f, -qexp[h]) * p.sm_log2;
+    int qe_l = qexp[0];
+    float z_l[NG];
 #pragma unroll
-    for (int g2 = 0; g2 < NG; ++g2) qzl[qd][g2] = qz[h][g2];
+    for (int g2 = 0; g2 < NG; ++g2) z_l[g2] = qz[0][g2];
+#pragma unroll
+    for (int h = 1; h < GQ; ++h) {
+      const bool mine = h == qd * 4 + kb;
+      qe_l = mine ? qexp[h] : qe_l;
+#pragma unroll
+      for (int g2 = 0; g2 < NG; ++g2) z_l[g2] = mine ? qz[h][g2] : z_l[g2];
+    }
+    qscale[qd] = ldexpf(1.f, -qe_l) * p.sm_log2;
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) qzl[qd][g2] = z_l[g2];
   }
 
   int hl = p.hist_len[b];
@@ -203,8 +243,9 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
   const int p0 = split * p.pages_per_split;
   int p1 = p0 + p.pages_per_split;
   p1 = p1 > npages ? npages : p1;
+  const int nk = p1 > p0 ? p1 - p0 : 0;           // pages of this wave's chunk
 
-  // running state; QK layout: lane = (head kb [+4 qd], token r16)
+  // running state; QK layout: lane = (head 4*qd + kb, token r16)
   float m_run[NQ], lsum[NQ], zacc[NQ][NG];
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
@@ -220,63 +261,70 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
     for (int h2 = 0; h2 < NH; ++h2) acc[qd][h2] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // ---------------- page loop: 4-stage register ring ----------------
+  // ---------------- page loop: register ring of NS pages ----------------
   // stage data of one page for this lane: K words of token r16 / lane group kb,
   // K and V (scale, zero) words of token r16, and the V words of channels
   // lane + 64*h2 (adjacent in the record).
-  constexpr int NS = 4;
-  constexpr int VPL = D / 64;
+#ifndef OSCAR_INT2_STAGES
+#define OSCAR_INT2_STAGES 4
+#endif
+  constexpr int NS = OSCAR_INT2_STAGES;   // pages in the register ring (NS-1 in flight)
+  constexpr int SW = D / 32;             // words of a lane slot: NBLK K words, NH V words
   struct Stage {
-    uint32_t k[NBLK], ks[NG], vs[NG], v[VPL];
+    uint32_t c[SW];                      // K words of (token r16, part kb), V words of channels lane + 64*h2
+    uint32_t sz[2 * NG];                 // token r16: K (scale, zero) per group, then V
     int ok;
   };
   Stage st[NS];
-  const int nk = p1 - p0 - w > 0 ? (p1 - p0 - w + 3) / 4 : 0;   // pages of this wave
-  const int32_t *ptab = p.hist_pages + (size_t)b * p.hist_stride;
+  // page ids through the constant address space: wave-uniform scalar loads,
+  // counted apart from the vector loads so reading one never drains the ring
+  using cint32 = const __attribute__((address_space(4))) int32_t;
+  cint32 *ptab = (cint32 *)(p.hist_pages + (size_t)b * p.hist_stride + p0);
   const size_t rec_stride = (size_t)p.Hkv * RL.bytes();
   const uint8_t *pool_j = p.int2_pool + (size_t)j * RL.bytes();
-  int pid_vec = 0, pid_base = -64;
 
-  auto page_id = [&](int k) -> int {           // wave-uniform k
-    if (k - pid_base >= 64) {
-      pid_base = k;
-      const int kk = k + lane;
-      pid_vec = kk < nk ? ptab[p0 + w + 4 * kk] : -1;
-    }
-    return __builtin_amdgcn_readlane(pid_vec, k - pid_base);
-  };
-  auto issue = [&](Stage &sg, int k) {
-    int phys = k < nk ? page_id(k) : -1;
-    sg.ok = phys >= 0 && phys < p.num_int2_pages;
+  // per-lane byte offsets inside a record: lane slot `lane` (= 16*kb + r16)
+  // and token slot r16
+  const uint32_t off_c = (uint32_t)RL.kword(lane, 0);
+  const uint32_t off_sz = (uint32_t)RL.tok_sz(r16);
+  const int npool = p.num_int2_pages < 0x7fffffff ? (int)p.num_int2_pages : 0x7fffffff;
+
+  auto issue = [&](Stage &sg, int k) {         // wave-uniform k
+    const int phys = k < nk ? ptab[k] : -1;
+    sg.ok = phys >= 0 && phys < npool;
     // out-of-range stages still load (from page 0) so every lane issues the
     // same load sequence; their data is never used
     const uint8_t *rec = pool_j + (sg.ok ? (size_t)phys : 0) * rec_stride;
-    load_words<NBLK>(sg.k, reinterpret_cast<const uint32_t *>(rec + RL.kcodes()) + r16 * (D / 16) + kb * NBLK);
-    load_words<NG>(sg.ks, reinterpret_cast<const uint32_t *>(rec + RL.ksz()) + r16 * NG);
-    load_words<NG>(sg.vs, reinterpret_cast<const uint32_t *>(rec + RL.vsz()) + r16 * NG);
-    load_words<VPL>(sg.v, reinterpret_cast<const uint32_t *>(rec + RL.vcodes()) + lane * VPL);
+    load_words<SW>(sg.c, reinterpret_cast<const uint32_t *>(rec + off_c));
+    load_words<2 * NG>(sg.sz, reinterpret_cast<const uint32_t *>(rec + off_sz));
   };
+
   // code -> f16 (1 + code/4) masks, held in registers (opaque to the compiler)
   // so that (x & m) | c selects one v_and_or_b32
-  uint32_t m_code, f16one;
-  asm volatile("s_mov_b32 %0, 0x3000300" : "=s"(m_code));
+  uint32_t m4, m6, m8, f16one;
+  asm volatile("s_mov_b32 %0, 0x300030" : "=s"(m4));
+  asm volatile("s_mov_b32 %0, 0xc000c0" : "=s"(m6));
+  asm volatile("s_mov_b32 %0, 0x3000300" : "=s"(m8));
   asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(f16one));
   const int pvs = pv_slot(r16);
+  const float pvf = pv_factor(r16);
+  constexpr float kLazy = 2.f;                 // log2 headroom of the running max
+  float m_thr[NQ];
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) m_thr[qd] = -INFINITY;
 
   auto process = [&](Stage &sg, int k) {
     if (!sg.ok) return;
-    const int pg = p0 + w + 4 * k;
+    const int pg = p0 + k;
     const int ntok = hl - pg * kPage < kPage ? hl - pg * kPage : kPage;
     // tokens past the history length (only on a sequence's last, partial page):
     // logit -inf and (scale, zero) read as 0, since unwritten record bytes may
     // hold any bit pattern
-    const bool partial = ntok < kPage;           // wave-uniform
-    if (partial) {
+    if (ntok < kPage) {
       const uint32_t vmask = r16 < ntok ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-      for (int g2 = 0; g2 < NG; ++g2) { sg.ks[g2] &= vmask; sg.vs[g2] &= vmask; }
+      for (int g2 = 0; g2 < 2 * NG; ++g2) sg.sz[g2] &= vmask;
     }
-    const float sinv = r16 < ntok ? 0.f : -INFINITY;
 
     // ---------------- QK on int8 MFMA ----------------
     v4i qacc[NQ][NG];
@@ -286,7 +334,7 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
       for (int g2 = 0; g2 < NG; ++g2) qacc[qd][g2] = v4i{0, 0, 0, 0};
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) {
-      const uint32_t d = sg.k[blk];
+      const uint32_t d = sg.c[blk];
       const v4i bq = v4i{(int)(d & 0x03030303u), (int)((d >> 2) & 0x03030303u),
                          (int)((d >> 4) & 0x03030303u), (int)((d >> 6) & 0x03030303u)};
 #pragma unroll
@@ -305,26 +353,28 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
       for (int g2 = 0; g2 < NG; ++g2) {
         const int dint = ((qacc[qd][g2][0] << 7) + qacc[qd][g2][1]) * 128 + qacc[qd][g2][2];
-        sc = fmaf(bf16_lo(sg.ks[g2]), (float)dint, sc);
-        zt = fmaf(bf16_hi(sg.ks[g2]), qzl[qd][g2], zt);
+        sc = fmaf(bf16_lo(sg.sz[g2]), (float)dint, sc);
+        zt = fmaf(bf16_hi(sg.sz[g2]), qzl[qd][g2], zt);
       }
-      s_[qd] = fmaf(sc, qscale[qd], zt) + sinv;
+      s_[qd] = fmaf(sc, qscale[qd], zt);
+    }
+    if (__builtin_expect(ntok < kPage, 0)) {
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) s_[qd] = r16 < ntok ? s_[qd] : -INFINITY;
     }
 
-    // ---------------- online softmax (exact running max per head) ----------------
+    // ---------------- online softmax (lazy running max per head) ----------------
     bool grow = false;
-    float mnew[NQ];
 #pragma unroll
-    for (int qd = 0; qd < NQ; ++qd) {
-      mnew[qd] = max_raw(m_run[qd], row_max(s_[qd]));
-      grow |= mnew[qd] > m_run[qd];
-    }
+    for (int qd = 0; qd < NQ; ++qd) grow |= s_[qd] > m_thr[qd];
     if (__builtin_expect(__any(grow), 0)) {
       float alpha[NQ];
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
-        alpha[qd] = m_run[qd] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qd] - mnew[qd]);
-        m_run[qd] = mnew[qd];
+        const float mnew = max_raw(m_run[qd], row_max(s_[qd]));
+        alpha[qd] = m_run[qd] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qd] - mnew);
+        m_run[qd] = mnew;
+        m_thr[qd] = mnew + kLazy;
         lsum[qd] *= alpha[qd];
 #pragma unroll
         for (int g2 = 0; g2 < NG; ++g2) zacc[qd][g2] *= alpha[qd];
@@ -343,38 +393,52 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
     float pr[NQ];
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
-      pr[qd] = __builtin_amdgcn_exp2f(s_[qd] - m_run[qd]);   // 0 for masked tokens
+      pr[qd] = __builtin_amdgcn_exp2f(s_[qd] - m_run[qd]);   // < 4; 0 for masked tokens
       lsum[qd] += pr[qd];
     }
+    float pa[NQ];                                 // A weights carry the factor 2^(8-b)
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) pa[qd] = pr[qd] * pvf;
 
     // ---------------- PV weights to LDS ----------------
 #pragma unroll
     for (int g2 = 0; g2 < NG; ++g2) {
-      const float vs = bf16_lo(sg.vs[g2]), vz = bf16_hi(sg.vs[g2]);
+      const float vs = bf16_lo(sg.sz[NG + g2]), vz = bf16_hi(sg.sz[NG + g2]);
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
-        const _Float16 wh = (_Float16)(pr[qd] * vs);
+        const _Float16 wh = (_Float16)(pa[qd] * vs);
         zacc[qd][g2] = fmaf(pr[qd], vz, zacc[qd][g2]);
         zacc[qd][g2] = fmaf(-4.f, (float)wh, zacc[qd][g2]);
-        wbuf[w][g2][qd * 4 + kb][pvs] = wh;
+        wbuf[g2][qd * 4 + kb][pvs] = wh;
       }
     }
     wave_lds_sync();
 
     // ---------------- PV on f16 MFMA, 4 token quads ----------------
-    // quad ti: tokens (ti, ti+8, ti+4, ti+12) as k = 0..3; token t of a V word
-    // sits in bits 2t, so v << (8 - 2ti) and v >> 2ti put each pair at f16
-    // mantissa bits 8..9 / 24..25
+    // token t of a V word sits in bits 2t; B register u holds tokens (u, u+8)
+    // in its two halves at the mantissa bit given by pv_factor
+    uint32_t bw[NH][8];
+#pragma unroll
+    for (int h2 = 0; h2 < NH; ++h2) {
+      const uint32_t x0 = sg.c[NBLK + h2], x1 = x0 << 4, x2 = x0 >> 6;
+      bw[h2][0] = (x1 & m4) | f16one;
+      bw[h2][1] = (x1 & m6) | f16one;
+      bw[h2][2] = (x1 & m8) | f16one;
+      bw[h2][3] = (x0 & m6) | f16one;
+      bw[h2][4] = (x0 & m8) | f16one;
+      bw[h2][5] = (x2 & m4) | f16one;
+      bw[h2][6] = (x2 & m6) | f16one;
+      bw[h2][7] = (x2 & m8) | f16one;
+    }
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
 #pragma unroll
       for (int h2 = 0; h2 < NH; ++h2) {
-        const uint32_t v = sg.v[h2];
-        const v4h bv = as_v4h(((v << (8 - 2 * ti)) & m_code) | f16one, ((v >> (2 * ti)) & m_code) | f16one);
+        const v4h bv = as_v4h(bw[h2][2 * ti], bw[h2][2 * ti + 1]);
         const int g2 = (lane + 64 * h2) / G;
 #pragma unroll
         for (int qd = 0; qd < NQ; ++qd) {
-          const uint2 u = *reinterpret_cast<const uint2 *>(&wbuf[w][g2][qd * 4 + (lane & 3)][4 * ti]);
+          const uint2 u = *reinterpret_cast<const uint2 *>(&wbuf[g2][qd * 4 + (lane & 3)][4 * ti]);
           acc[qd][h2] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_v4h(u.x, u.y), bv, acc[qd][h2], 0, 0, 0);
         }
       }
@@ -394,76 +458,46 @@ __global__ __launch_bounds__(256) void k_int2_mfma(DecodeParams p) {
     }
   }
 
-  // ---------------- wave epilogue ----------------
-  // head h's sums: row sums over the 16 token lanes of quad h/4, lane group h%4
+  // ---------------- epilogue: this wave's chunk partial ----------------
+  float *po = reinterpret_cast<float *>(p.ws + p.L.part_o);
+  float *pml = reinterpret_cast<float *>(p.ws + p.L.part_ml);
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
+    // head 4*qd + kb's sums over its 16 token lanes
     const float L = row_sum(lsum[qd]);
     float Z[NG];
 #pragma unroll
     for (int g2 = 0; g2 < NG; ++g2) Z[g2] = row_sum(zacc[qd][g2]);
-    const int h = qd * 4 + kb;
     if (r16 == 0) {
-      wm[w][h] = m_run[qd];
-      wl[w][h] = L;
-    }
-    // the zero-point / offset part is added to every channel of its group
-    if (r16 < NG) {
-      float zz = Z[0];
-#pragma unroll
-      for (int g2 = 1; g2 < NG; ++g2) zz = r16 == g2 ? Z[g2] : zz;
-      wo[w][h][0 + r16] = zz;          // staged in the first NG channels, moved below
-    }
-  }
-  wave_lds_sync();
-  float zst[GQ][NG];
-#pragma unroll
-  for (int h = 0; h < GQ; ++h)
-#pragma unroll
-    for (int g2 = 0; g2 < NG; ++g2) zst[h][g2] = wo[w][h][g2];
-  wave_lds_sync();
-  // accumulator element i of quad qd, half h2: head 4*qd + i, channel lane + 64*h2
-#pragma unroll
-  for (int qd = 0; qd < NQ; ++qd)
-#pragma unroll
-    for (int h2 = 0; h2 < NH; ++h2) {
-      const int c = lane + 64 * h2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wo[w][4 * qd + i][c] = 4.f * acc[qd][h2][i] + zst[4 * qd + i][c / G];
-    }
-  __syncthreads();
-
-  // ---------------- combine the 4 waves, write the chunk partial ----------------
-  float *po = reinterpret_cast<float *>(p.ws + p.L.part_o);
-  float *pml = reinterpret_cast<float *>(p.ws + p.L.part_ml);
-  for (int i = tid; i < GQ * D; i += 256) {
-    const int h = i / D, c = i % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) M = fmaxf(M, wm[k][h]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (wm[k][h] == -INFINITY) continue;
-        const float a = exp2f(wm[k][h] - M);
-        L = fmaf(wl[k][h], a, L);
-        O = fmaf(wo[k][h][c], a, O);
-      }
-    }
-    const int hq = p.q_of_kv[j * GQ + h];
-    const size_t row = ((size_t)b * p.Hq + hq) * S + split;
-    po[row * D + c] = O;
-    if (c == 0) {
-      pml[row * 2 + 0] = M;
+      const size_t row = ((size_t)b * p.Hq + p.q_of_kv[j * GQ + qd * 4 + kb]) * S + split;
+      pml[row * 2 + 0] = m_run[qd];
       pml[row * 2 + 1] = L;
+    }
+    // accumulator element i: head 4*qd + i, channel lane + 64*h2; the zero-point
+    // and offset part of head 4*qd + i is uniform over lanes 16*i ..
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t row = ((size_t)b * p.Hq + p.q_of_kv[j * GQ + qd * 4 + i]) * S + split;
+#pragma unroll
+      for (int h2 = 0; h2 < NH; ++h2) {
+        const int c = lane + 64 * h2;
+        float zz = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < NG; ++g2) {
+          const float zg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Z[g2]), 16 * i));
+          zz = (c / G == g2) ? zg : zz;
+        }
+        po[row * D + c] = 4.f * acc[qd][h2][i] + zz;
+      }
     }
   }
 }
 
 template <int D, int G>
 static void launch_mfma_dg(const DecodeParams &p, hipStream_t s) {
-  const dim3 grid(p.B * p.Hkv * p.splits), blk(256);
+  const int hb = p.Hkv < kMfmaHeadsPerBlock ? p.Hkv : kMfmaHeadsPerBlock;
+  const int ngrp = (p.Hkv + hb - 1) / hb;
+  const dim3 grid(p.B * p.splits * ngrp), blk(64 * hb);
   if (p.g == 8) hipLaunchKernelGGL((k_int2_mfma<D, G, 8>), grid, blk, 0, s, p);
   else hipLaunchKernelGGL((k_int2_mfma<D, G, 4>), grid, blk, 0, s, p);
 }

@@ -243,41 +243,47 @@ def k_row_words(codes_row) -> np.ndarray:
     return out
 
 
-def v_word_order(D: int) -> np.ndarray:
-    """Channel stored at each V-code word position: position (c % 64)*(D/64) + c//64
-    holds channel c, so the D/64 channels c, c+64, ... of one reader lane are
-    adjacent.  For D = 64 this is channel order."""
-    nh = max(1, D // 64)
-    pos = np.empty(D, dtype=np.int64)
-    for c in range(D):
-        pos[(c % 64) * nh + c // 64] = c
-    return pos
-
-
 # ----------------------------------------------------------------------------
 # INT2 page record (layout of one (physical page, KV head) record in HBM)
 # ----------------------------------------------------------------------------
 
 def record_bytes(D: int, G: int) -> int:
-    """K codes [16][D/16 words] | V codes [D words] | K (scale,zero) [16][D/G][2]
-    bf16 | V (scale,zero) [16][D/G][2] bf16."""
+    """Code region of 64 lane slots x D/32 words (2*16*D/4 bytes) | scale/zero
+    region of 16 token slots x 2*D/G words (2*16*(D/G)*4 bytes)."""
     return 2 * 16 * (D // 4) + 2 * 16 * (D // G) * 4
 
 
 def encode_record(kc, ks, kz, vc, vs, vz, D: int, G: int) -> np.ndarray:
     """Bytes of one page record (16 tokens of one KV head) from codes [16, D]
-    and bf16 scale/zero [16, D/G] for K and V.  Words are little-endian.
-    Token rows not yet written are all-zero (pass zeros)."""
-    def sz(s, z):
-        sb = f64_to_bf16_bits(s).astype(np.uint16)
-        zb = f64_to_bf16_bits(z).astype(np.uint16)
-        pair = np.stack([sb, zb], axis=-1)        # [16][D/G][2]
-        return pair.astype("<u2").view(np.uint8).reshape(-1)
-    kwords = np.concatenate([k_row_words(kc[t]) for t in range(16)])
-    vwords = pack_channel_major(vc)[v_word_order(D)]
-    parts = [kwords.astype("<u4").view(np.uint8), vwords.astype("<u4").view(np.uint8),
-             sz(ks, kz), sz(vs, vz)]
-    out = np.concatenate(parts)
+    and bf16 scale/zero [16, D/G] for K and V.  Words are little-endian; D is a
+    multiple of 64.  Token rows not yet written are all-zero (pass zeros).
+
+    Code region: lane slot l = 16*kb + t (kb = 0..3, t = 0..15) holds, in this
+    order, the D/64 K words of token t for part kb (word blk = k_row_words word
+    kb*(D/64) + blk: channels 64*blk + 16*kb + i in bits 2i), then the D/64 V
+    words of channels l, l + 64, ... (pack_channel_major: token t in bits 2t).
+    Scale/zero region: token slot t holds the K words of groups 0..D/G-1, then
+    the V words; each word is scale (bf16) | zero (bf16) << 16."""
+    nblk, ng = D // 64, D // G
+    sw = D // 32
+    vw = pack_channel_major(vc)
+    codes = np.zeros(64 * sw, dtype=np.uint32)
+    for t in range(16):
+        krow = k_row_words(kc[t])
+        for kb in range(4):
+            l = 16 * kb + t
+            for blk in range(nblk):
+                codes[l * sw + blk] = krow[kb * nblk + blk]
+    for l in range(64):
+        for h2 in range(nblk):
+            codes[l * sw + nblk + h2] = vw[l + 64 * h2]
+
+    def szw(s, z):
+        sb = f64_to_bf16_bits(s).astype(np.uint32)
+        zb = f64_to_bf16_bits(z).astype(np.uint32)
+        return sb | (zb << np.uint32(16))            # [16][D/G]
+    sz = np.concatenate([szw(ks, kz), szw(vs, vz)], axis=1).reshape(-1)   # [16][2*D/G]
+    out = np.concatenate([codes.astype("<u4").view(np.uint8), sz.astype("<u4").view(np.uint8)])
     assert out.size == record_bytes(D, G)
     return out
 
@@ -285,27 +291,26 @@ def encode_record(kc, ks, kz, vc, vs, vz, D: int, G: int) -> np.ndarray:
 def decode_record(rec, D: int, G: int):
     """Inverse of encode_record: (kc, ks, kz, vc, vs, vz)."""
     rec = np.asarray(rec, dtype=np.uint8)
-    nw = D // 16
-    kw = rec[:16 * nw * 4].view("<u4").reshape(16, nw)
-    o = 16 * nw * 4
-    vw = rec[o:o + D * 4].view("<u4"); o += D * 4
-    nblk = max(1, D // 64)
+    nblk, ng = D // 64, D // G
+    sw = D // 32
+    codes = rec[:64 * sw * 4].view("<u4").reshape(64, sw)
     kc = np.zeros((16, D), np.uint8)
-    for kb in range(min(4, nw)):
-        for blk in range(nblk):
-            w = kw[:, kb * nblk + blk]
-            for i in range(16):
-                kc[:, 64 * blk + 16 * kb + i] = (w >> np.uint32(2 * i)) & 3
-    vchan = np.zeros(D, np.uint32)
-    vchan[v_word_order(D)] = vw
     vc = np.zeros((16, D), np.uint8)
-    for t in range(16):
-        vc[t] = (vchan >> np.uint32(2 * t)) & 3
-    ng = D // G
-    ksz = rec[o:o + 16 * ng * 4].view("<u2").reshape(16, ng, 2); o += 16 * ng * 4
-    vsz = rec[o:o + 16 * ng * 4].view("<u2").reshape(16, ng, 2); o += 16 * ng * 4
-    return (kc, bf16_bits_to_f64(ksz[..., 0]), bf16_bits_to_f64(ksz[..., 1]),
-            vc, bf16_bits_to_f64(vsz[..., 0]), bf16_bits_to_f64(vsz[..., 1]))
+    for l in range(64):
+        kb, t = l >> 4, l & 15
+        for blk in range(nblk):
+            w = int(codes[l, blk])
+            for i in range(16):
+                kc[t, 64 * blk + 16 * kb + i] = (w >> (2 * i)) & 3
+        for h2 in range(nblk):
+            w = int(codes[l, nblk + h2])
+            for tt in range(16):
+                vc[tt, l + 64 * h2] = (w >> (2 * tt)) & 3
+    sz = rec[64 * sw * 4:].view("<u4").reshape(16, 2 * ng)
+    lo = (sz & np.uint32(0xFFFF)).astype(np.uint16)
+    hi = (sz >> np.uint32(16)).astype(np.uint16)
+    return (kc, bf16_bits_to_f64(lo[:, :ng]), bf16_bits_to_f64(hi[:, :ng]),
+            vc, bf16_bits_to_f64(lo[:, ng:]), bf16_bits_to_f64(hi[:, ng:]))
 
 
 def quantize_tokens(kv_bf16_vals, R, G: int, clip: float):

@@ -226,10 +226,6 @@ def test_channel_major_layout():
     c[5, 2] = 3          # token 5, channel 2 -> channel 2's word, bits 10..11
     w = orc.pack_channel_major(c)
     assert w.shape == (8,) and w[2] == 3 << 10 and w.sum() == 3 << 10
-    # V words: channel c at position (c % 64) * (D/64) + c // 64
-    order = orc.v_word_order(128)
-    assert order[0] == 0 and order[1] == 64 and order[2] == 1 and order[35] == 81
-    assert list(orc.v_word_order(64)) == list(range(64))
 
 
 def test_k_row_word_order():
@@ -415,24 +411,48 @@ def test_bits_per_element_printed_values():
 
 
 def test_record_layout_hand_placed():
-    """Byte positions of the page-record layout for D=64, G=32 (record = K words
-    [16][4] | V words [64] (channel order at D = 64) | K (scale,zero) [16][2][2] bf16 | V (scale,zero)
-    [16][2][2] bf16 = 256 + 256 + 128 + 128 bytes), worked by hand."""
+    """Byte positions of the page-record layout for D=64, G=32, worked by hand:
+    64 lane slots of 2 words (K word of token t = l % 16, part kb = l // 16;
+    V word of channel l) = 512 bytes, then 16 token slots of 4 words (K groups
+    0, 1; V groups 0, 1; scale | zero << 16) = 256 bytes."""
     D, G = 64, 32
     kc = np.zeros((16, D), np.uint8); vc = np.zeros((16, D), np.uint8)
     ks = np.zeros((16, 2)); kz = np.zeros((16, 2)); vs = np.zeros((16, 2)); vz = np.zeros((16, 2))
-    kc[3, 37] = 2         # token 3, channel 37: word 3*4 + 2, bits 10..11 -> byte 57 = 0x08
-    vc[9, 6] = 3          # channel 6 at word 6, token 9 bits 18..19 -> byte 256+24+2 = 0x0C
-    vc[0, 17] = 1         # channel 17 at word 17, token 0 -> byte 256+68 = 0x01
-    ks[2, 1] = 1.0        # K (s, z) of token 2 group 1 at 512 + (2*2+1)*4 -> 0x3F80
-    kz[2, 1] = -2.0       # zero -> 0xC000 right after
-    vz[15, 0] = 0.5       # V block: 640 + (15*2+0)*4 + 2 -> 0x3F00
+    kc[3, 37] = 2         # channel 37 = 16*2 + 5: slot 35 word 0 (byte 280), bits 10..11 -> byte 281 = 0x08
+    vc[9, 6] = 3          # channel 6: slot 6 word 1 (byte 52), token 9 bits 18..19 -> byte 54 = 0x0C
+    vc[0, 17] = 1         # channel 17: slot 17 word 1 (byte 140), token 0 -> 0x01
+    ks[2, 1] = 1.0        # token 2 slot at 512 + 32, K group 1 word at +4 -> 0x3F80
+    kz[2, 1] = -2.0       # zero in the high half -> 0xC000
+    vz[15, 0] = 0.5       # token 15 slot at 512 + 240, V group 0 word at +8, high half -> 0x3F00
     rec = orc.encode_record(kc, ks, kz, vc, vs, vz, D, G)
     assert rec.size == 768
     want = np.zeros(768, np.uint8)
-    want[57] = 0x08
-    want[256 + 24 + 2] = 0x0C
-    want[256 + 68] = 0x01
-    want[532:536] = [0x80, 0x3F, 0x00, 0xC0]
-    want[640 + 120 + 2:640 + 120 + 4] = [0x00, 0x3F]
+    want[281] = 0x08
+    want[54] = 0x0C
+    want[140] = 0x01
+    want[548:552] = [0x80, 0x3F, 0x00, 0xC0]
+    want[762:764] = [0x00, 0x3F]
+    assert np.array_equal(rec, want)
+
+
+def test_record_layout_hand_placed_d128():
+    """D=128, G=64: lane slots of 4 words (K blocks 0, 1 of token t part kb;
+    V channels l, l + 64) = 1024 bytes, then token slots of 4 words (K groups 0, 1;
+    V groups 0, 1) = 256 bytes; worked by hand."""
+    D, G = 128, 64
+    kc = np.zeros((16, D), np.uint8); vc = np.zeros((16, D), np.uint8)
+    z2 = np.zeros((16, 2))
+    kc[5, 70] = 1         # channel 70 = 64 + 16*0 + 6: slot 5 word 1 (byte 84), bits 12..13 -> byte 85 = 0x10
+    kc[12, 127] = 3       # channel 127 = 64 + 16*3 + 15: slot 60 word 1 (byte 964), bits 30..31 -> byte 967 = 0xC0
+    vc[1, 65] = 2         # channel 65: slot 1 word 3 (byte 28), token 1 bits 2..3 -> 0x08
+    vc[15, 0] = 1         # channel 0: slot 0 word 2 (byte 8), token 15 bits 30..31 -> byte 11 = 0x40
+    vs = z2.copy(); vs[7, 1] = 2.0   # token 7 slot at 1024 + 112, V group 1 word at +12 -> 0x4000
+    rec = orc.encode_record(kc, z2, z2, vc, vs, z2, D, G)
+    assert rec.size == 1280
+    want = np.zeros(1280, np.uint8)
+    want[85] = 0x10
+    want[967] = 0xC0
+    want[28] = 0x08
+    want[11] = 0x40
+    want[1024 + 112 + 12:1024 + 112 + 14] = [0x00, 0x40]
     assert np.array_equal(rec, want)
