@@ -122,7 +122,8 @@ typedef struct {
   int32_t max_hist_len;      /* [host] upper bound on every hist_len; sizes the
                                 grid without a device-to-host read               */
   float sm_scale;            /* softmax scale; 0 means 1/sqrt(D)                */
-  int32_t num_splits;        /* history chunks per (sequence, KV head); 0 = auto */
+  int32_t num_splits;        /* history chunks per (sequence, KV head); 0 = auto;
+                                at most 1024 are used                          */
   int32_t int2_kernel;       /* OSCAR_INT2_AUTO / _VALU / _MFMA                  */
   uint32_t phases;           /* oscar_decode_attn work: OR of OSCAR_PHASE_*; 0 means
                                 all.  Phases may be issued in separate calls (e.g.

@@ -159,6 +159,7 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
       S = S < 1 ? 1 : S;
     }
   }
+  S = S > kMaxSplits ? kMaxSplits : S;
   const int pps = npages > 0 ? (npages + S - 1) / S : 0;
   if (npages > 0) S = (npages + pps - 1) / pps;
   p->splits = S;

@@ -12,6 +12,7 @@ namespace oscar {
 constexpr int kPage = OSCAR_PAGE_TOKENS;
 constexpr int kMaxBf16 = OSCAR_MAX_BF16_TOKENS;
 constexpr int kBf16PagesPerSplit = 4;                              // one wave per page
+constexpr int kMaxSplits = 1024;        // history chunks per (sequence, KV head)
 constexpr int kBf16Splits = kMaxBf16 / (kPage * kBf16PagesPerSplit); // 5 BF16 partials
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

@@ -17,26 +17,54 @@ namespace oscar {
 // so (q . R_k) . (k . R_k) = q . k for an orthogonal R_k.  fp64 accumulation,
 // one rounding to fp32.
 // ---------------------------------------------------------------------------
+// 256 threads per (sequence, q head): thread (group gi, column quad c4) sums
+// rows gi*RPG .. +RPG-1 of R for columns 4*c4 .. +3 (one 16-byte load per row,
+// all issued together); the row groups are added in LDS.
 template <int D>
-__global__ __launch_bounds__(D) void k_qrot(DecodeParams p, const uint16_t *__restrict__ q,
-                                            const float *__restrict__ Rk) {
+__global__ __launch_bounds__(256) void k_qrot(DecodeParams p, const uint16_t *__restrict__ q,
+                                              const float *__restrict__ Rk) {
+  constexpr int NC4 = D / 4;             // column quads
+  constexpr int NGR = 256 / NC4;         // row groups
+  constexpr int RPG = D / NGR;           // rows per group
   const int bh = blockIdx.x;
   const int h = bh % p.Hq;
   const int j = p.kv_of_q[h];
-  const int c = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int c4 = tid % NC4, gi = tid / NC4;
   __shared__ double qs[D];
-  qs[c] = (double)bf16_to_f32(q[(size_t)bh * D + c]);
+  __shared__ double part[NGR][D];
+  if (tid < D) qs[tid] = (double)bf16_to_f32(q[(size_t)bh * D + tid]);
   __syncthreads();
-  const float *R = Rk + (size_t)j * D * D;
-  double acc = 0.0;
-  for (int i = 0; i < D; ++i) acc = fma(qs[i], (double)R[(size_t)i * D + c], acc);
-  reinterpret_cast<float *>(p.ws + p.L.qrot)[(size_t)bh * D + c] = (float)acc;
+  const float4 *R = reinterpret_cast<const float4 *>(Rk + (size_t)j * D * D) + c4;
+  float4 r[RPG];
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) r[i] = R[(size_t)(gi * RPG + i) * NC4];
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) {
+    const double qi = qs[gi * RPG + i];
+    a0 = fma(qi, (double)r[i].x, a0);
+    a1 = fma(qi, (double)r[i].y, a1);
+    a2 = fma(qi, (double)r[i].z, a2);
+    a3 = fma(qi, (double)r[i].w, a3);
+  }
+  part[gi][4 * c4 + 0] = a0;
+  part[gi][4 * c4 + 1] = a1;
+  part[gi][4 * c4 + 2] = a2;
+  part[gi][4 * c4 + 3] = a3;
+  __syncthreads();
+  if (tid < D) {
+    double acc = 0.0;
+#pragma unroll
+    for (int g2 = 0; g2 < NGR; ++g2) acc += part[g2][tid];
+    reinterpret_cast<float *>(p.ws + p.L.qrot)[(size_t)bh * D + tid] = (float)acc;
+  }
 }
 
 hipError_t launch_qrot(const DecodeParams &p, const uint16_t *q, const float *Rk, hipStream_t s) {
   const int nb = p.B * p.Hq;
-  if (p.D == 64) hipLaunchKernelGGL(k_qrot<64>, dim3(nb), dim3(64), 0, s, p, q, Rk);
-  else hipLaunchKernelGGL(k_qrot<128>, dim3(nb), dim3(128), 0, s, p, q, Rk);
+  if (p.D == 64) hipLaunchKernelGGL(k_qrot<64>, dim3(nb), dim3(256), 0, s, p, q, Rk);
+  else hipLaunchKernelGGL(k_qrot<128>, dim3(nb), dim3(256), 0, s, p, q, Rk);
   return hipGetLastError();
 }
 

@@ -93,7 +93,21 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
 
   double x[T];
   const float *R = isv ? Rv : Rk;
-  if (R != nullptr) {
+  if (R != nullptr && T == 1) {
+    // one token: all D loads of column c are issued before the dot product
+    R += (size_t)j * D * D;
+    float r[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) r[i] = R[(size_t)i * D + c];
+    double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+    for (int i = 0; i < D; i += 2) {
+      const double2 kk = *reinterpret_cast<const double2 *>(&xs[0][i]);
+      a0 = fma(kk.x, (double)r[i], a0);
+      a1 = fma(kk.y, (double)r[i + 1], a1);
+    }
+    x[0] = a0 + a1;
+  } else if (R != nullptr) {
     R += (size_t)j * D * D;
 #pragma unroll
     for (int t = 0; t < T; ++t) x[t] = 0.0;
