@@ -27,7 +27,7 @@ What it computes, and where the pages state it (page titles abbreviated:
   from per-chunk partials merged by online softmax ([thmotor], decode stage:
   the BF16 and INT2 segments are merged by an online-softmax merge).
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   clip ratio c scales the group min and max: range [c*mn, c*mx]; scale =
   (c*mx - c*mn)/3, zero = c*mn, both rounded to bf16 directly from fp64 (round
   to nearest even); codes = clamp(rint((x - zero_b)/scale_b), 0, 3) with
