@@ -365,13 +365,13 @@ def main(argv=None):
     timed = range(a.warmup, a.warmup + a.steps)
     ms_step = 1000.0 * r["wall_s"] / a.steps
     kvth = np.mean([int(st.hl_h[s].sum() + st.bl_h[s].sum()) * wl.Hkv for s in timed])
-    splits = ob.decode_plan(st.sc.cache, r["args"][a.warmup])[0]
+    splits, _, _, kind = ob.decode_plan(st.sc.cache, r["args"][a.warmup])
     step_bytes = np.mean([step_alg_bytes(wl, st.hl_h[s], st.bl_h[s], splits) for s in timed])
     seg = r["seg_ms"]
     int2_ms = float(seg[:, 2].mean())
     i2_last = int2_alg_bytes(wl, st.hl_h[r["int2_only_step"]], splits)[0]
     achieved = i2_last / (r["int2_only_ms"] * 1e-3) / 1e9
-    kname = "k_int2_mfma" if kern == ob.INT2_MFMA else "k_int2_valu"
+    kname = "k_int2_mfma" if kind == ob.INT2_MFMA else "k_int2_valu"
     tr = traffic_from_profile(kname, wl.name)
     out = {
         "metric": "decode attention: KV-tokens·heads/s and achieved HBM TB/s (% of peak) at 100K ctx",

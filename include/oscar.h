@@ -177,13 +177,15 @@ int oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_ar
 /*
  * oscar_decode_plan - the history chunking oscar_decode_attn will use for these
  * arguments (host only): num_splits chunks of pages_per_split pages per
- * (sequence, KV head), and the workspace size.  Any output may be NULL.
+ * (sequence, KV head), the workspace size, and the INT2 kernel that runs
+ * (OSCAR_INT2_VALU or OSCAR_INT2_MFMA, AUTO resolved).  Any output may be NULL.
  * Automatic chunking (num_splits == 0) aims at 8192 (MFMA kernel) or 2048
  * (VALU kernel) (sequence, KV head, chunk) units while keeping every chunk at
  * least 50x the bytes of its partial result and 16 pages long.
  */
 int oscar_decode_plan(const oscar_cache *cache, const oscar_decode_args *args,
-                      int32_t *num_splits, int32_t *pages_per_split, size_t *workspace_bytes);
+                      int32_t *num_splits, int32_t *pages_per_split, size_t *workspace_bytes,
+                      int32_t *int2_kernel);
 
 /*
  * oscar_decode_attn - attend every q head over both segments, producing partial

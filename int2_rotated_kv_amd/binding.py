@@ -84,7 +84,7 @@ _SIGS = {
                                                     ctypes.POINTER(ctypes.c_size_t)]),
     "oscar_decode_plan": (ctypes.c_int, [ctypes.POINTER(OscarCache), ctypes.POINTER(OscarDecodeArgs),
                                          ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
-                                         ctypes.POINTER(ctypes.c_size_t)]),
+                                         ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int32)]),
     "oscar_decode_attn": (ctypes.c_int, [ctypes.POINTER(OscarCache), ctypes.POINTER(OscarDecodeArgs),
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]),
@@ -217,12 +217,13 @@ def workspace_bytes(cache: Cache, args: DecodeArgs) -> int:
 
 
 def decode_plan(cache: Cache, args: DecodeArgs):
-    """(num_splits, pages_per_split, workspace_bytes) oscar_decode_attn will use."""
+    """(num_splits, pages_per_split, workspace_bytes, int2_kernel) oscar_decode_attn
+    will use; int2_kernel is INT2_VALU or INT2_MFMA."""
     d = cache.desc()
-    s, p, w = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_size_t(0)
+    s, p, w, k = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_size_t(0), ctypes.c_int32(0)
     check(lib().oscar_decode_plan(ctypes.byref(d), ctypes.byref(args.c), ctypes.byref(s),
-                                  ctypes.byref(p), ctypes.byref(w)))
-    return int(s.value), int(p.value), int(w.value)
+                                  ctypes.byref(p), ctypes.byref(w), ctypes.byref(k)))
+    return int(s.value), int(p.value), int(w.value), int(k.value)
 
 
 def alloc_workspace(cache: Cache, args: DecodeArgs, device="cuda"):

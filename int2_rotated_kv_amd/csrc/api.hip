@@ -240,13 +240,15 @@ int oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_ar
 }
 
 int oscar_decode_plan(const oscar_cache *cache, const oscar_decode_args *args,
-                      int32_t *num_splits, int32_t *pages_per_split, size_t *workspace_bytes) {
+                      int32_t *num_splits, int32_t *pages_per_split, size_t *workspace_bytes,
+                      int32_t *int2_kernel) {
   DecodeParams p{};
   int st = check_args(cache, args, &p);
   if (st) return st;
   if (num_splits) *num_splits = p.splits;
   if (pages_per_split) *pages_per_split = p.pages_per_split;
   if (workspace_bytes) *workspace_bytes = p.L.total;
+  if (int2_kernel) *int2_kernel = p.int2_kind;
   return OSCAR_OK;
 }
 

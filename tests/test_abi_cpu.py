@@ -146,3 +146,42 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ob, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         ob.lib()
+
+
+def _plan(c, a):
+    s, p, w, k = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_size_t(0), ctypes.c_int32(-1)
+    st = ob.lib().oscar_decode_plan(ctypes.byref(c), ctypes.byref(a), ctypes.byref(s),
+                                    ctypes.byref(p), ctypes.byref(w), ctypes.byref(k))
+    return st, s.value, p.value, w.value, k.value
+
+
+def test_plan_resolves_int2_kernel():
+    # 4 q heads per KV head: matrix-core kernel unless asked otherwise
+    st, *_, k = _plan(_cache(), _args())
+    assert st == ob.OSCAR_OK and k == ob.INT2_MFMA
+    st, *_, k = _plan(_cache(), _args(int2_kernel=ob.INT2_VALU))
+    assert st == ob.OSCAR_OK and k == ob.INT2_VALU
+    # 2 q heads per KV head: vector-ALU kernel; asking for MFMA is unsupported
+    st, *_, k = _plan(_cache(), _args(num_q_heads=16))
+    assert st == ob.OSCAR_OK and k == ob.INT2_VALU
+    st, *_ = _plan(_cache(), _args(num_q_heads=16, int2_kernel=ob.INT2_MFMA))
+    assert st == ob.OSCAR_EUNSUPPORTED
+    assert "4 or 8" in ob.lib().oscar_last_error().decode()
+
+
+def test_plan_chunking_rules():
+    # batch 32 x 8 KV heads, 6000 history pages: the matrix-core kernel aims at
+    # 8192 (sequence, KV head, chunk) units -> 32 chunks; the VALU kernel at 2048
+    big = dict(batch=32, hist_stride=6000, max_hist_len=6000 * 16)
+    st, s, p, w, k = _plan(_cache(), _args(**big))
+    assert st == 0 and k == ob.INT2_MFMA and s == 32 and p * s >= 6000 and p * (s - 1) < 6000
+    st, s, *_ = _plan(_cache(), _args(int2_kernel=ob.INT2_VALU, **big))
+    assert st == 0 and s == 8
+    # explicit chunk counts are capped by the page count and by 1024
+    st, s, p, *_ = _plan(_cache(), _args(num_splits=5000, **big))
+    assert st == 0 and s <= 1024 and p == 6
+    st, s, p, *_ = _plan(_cache(), _args(num_splits=50, hist_stride=10, max_hist_len=100))
+    assert st == 0 and s == 7 and p == 1
+    # no history: one (empty) chunk
+    st, s, p, *_ = _plan(_cache(), _args(max_hist_len=0))
+    assert st == 0 and s == 1 and p == 0
