@@ -179,9 +179,15 @@ int oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_ar
  * arguments (host only): num_splits chunks of pages_per_split pages per
  * (sequence, KV head), the workspace size, and the INT2 kernel that runs
  * (OSCAR_INT2_VALU or OSCAR_INT2_MFMA, AUTO resolved).  Any output may be NULL.
- * Automatic chunking (num_splits == 0) aims at 8192 (MFMA kernel) or 2048
+ * Automatic chunking (num_splits == 0) aims at 4096 (MFMA kernel) or 2048
  * (VALU kernel) (sequence, KV head, chunk) units while keeping every chunk at
- * least 50x the bytes of its partial result and 16 pages long.
+ * least 8x the bytes of its partial result and 16 pages long.  The VALU kernel
+ * gives chunk c pages [c*pages_per_split, (c+1)*pages_per_split) and drops
+ * empty chunks.  The MFMA kernel rounds the chunk count up to a multiple of 8:
+ * each group of 8 chunks is one block of 8 waves that takes the pages of one
+ * equal part of the history in batches from a shared counter, so which pages a
+ * chunk partial covers depends on timing (the merged result does not, up to
+ * fp32 rounding order) and pages_per_split is nominal.
  */
 int oscar_decode_plan(const oscar_cache *cache, const oscar_decode_args *args,
                       int32_t *num_splits, int32_t *pages_per_split, size_t *workspace_bytes,

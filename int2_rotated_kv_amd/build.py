@@ -39,7 +39,10 @@ def common_flags(debug: bool = False):
          "-munsafe-fp-atomics",
          # keep matrix-core accumulators in VGPRs: the online-softmax rescale
          # multiplies them with VALU ops, which cannot read AGPRs
-         "-mllvm", "-amdgpu-mfma-vgpr-form"]
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
+         # keep uniform-address atomics as written: the optimiser's lane
+         # aggregation waits for each result right after issuing it
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
     f += ["-O1", "-g"] if debug else ["-O3"]
     return f
 

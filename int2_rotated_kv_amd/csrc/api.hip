@@ -11,6 +11,7 @@
 #include "common.hpp"
 
 namespace oscar {
+static_assert(kMaxSplits % kMfmaWaves == 0, "chunk cap must be a multiple of the MFMA waves per head");
 namespace {
 
 thread_local std::string g_err;
@@ -138,30 +139,39 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
                 "matrix-core INT2 kernel needs 4 or 8 q heads per KV head (got %d)", p->g);
   p->int2_kind = kind;
 
-  // history split: enough waves to fill the chip (the vector-ALU kernel runs
-  // 4 waves per (sequence, KV head, chunk), the matrix-core one 1), but each
-  // chunk streams enough pages that its partials stay ~2% of its history bytes
+  // history split: enough waves to fill the chip once (the vector-ALU kernel
+  // runs 4 waves per (sequence, KV head, chunk), the matrix-core one 1), while
+  // each chunk streams at least 8x the bytes of its partial result (read and
+  // written once more by the merge) and 16 pages.  The matrix-core kernel runs
+  // blocks of kMfmaWaves waves over up to 8 KV heads of one sequence, the waves
+  // of a head sharing the pages of one part of its history, so its chunk count
+  // is a multiple of the waves per head; its pages_per_split is nominal.
   const int npages = need_hist;
   int S = 1;
   if (npages > 0) {
     if (a->num_splits > 0) {
-      S = a->num_splits < npages ? a->num_splits : npages;
+      S = a->num_splits;
+      if (kind != OSCAR_INT2_MFMA && S > npages) S = npages;
     } else {
       const int units = a->batch * c->num_kv_heads;
-      const int target_blocks = kind == OSCAR_INT2_MFMA ? 8192 : 2048;
+      const int target = kind == OSCAR_INT2_MFMA ? 4096 : 2048;
       const double rec = (double)RecLayout(p->D, p->G).bytes();
       const double part_bytes = 2.0 * p->g * (p->D + 2) * 4.0;   // write + read back
-      int min_pages = (int)std::ceil(50.0 * part_bytes / rec);
+      int min_pages = (int)std::ceil(8.0 * part_bytes / rec);
       min_pages = min_pages < 16 ? 16 : min_pages;
-      int s_fill = (target_blocks + units - 1) / units;
+      int s_fill = (target + units - 1) / units;
       int s_cap = npages / min_pages;
       S = s_fill < s_cap ? s_fill : s_cap;
       S = S < 1 ? 1 : S;
     }
   }
   S = S > kMaxSplits ? kMaxSplits : S;
+  if (kind == OSCAR_INT2_MFMA) {
+    const int wh = kMfmaWaves / mfma_heads_per_block(c->num_kv_heads);   // waves per head
+    S = (S + wh - 1) / wh * wh;
+  }
   const int pps = npages > 0 ? (npages + S - 1) / S : 0;
-  if (npages > 0) S = (npages + pps - 1) / pps;
+  if (npages > 0 && kind != OSCAR_INT2_MFMA) S = (npages + pps - 1) / pps;
   p->splits = S;
   p->pages_per_split = pps;
 
@@ -169,8 +179,6 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   const size_t BH = (size_t)a->batch * a->num_q_heads;
   size_t off = 0;
   L.qrot = off; off = align256(off + BH * p->D * 4);
-  L.qpiece = off; off = align256(off + BH * 4 * p->D);
-  L.qexp = off; off = align256(off + BH * 4);
   L.part_o = off; off = align256(off + BH * S * p->D * 4);
   L.part_ml = off; off = align256(off + BH * S * 2 * 4);
   L.bf_o = off; off = align256(off + BH * kBf16Splits * p->D * 4);

@@ -13,6 +13,15 @@ constexpr int kPage = OSCAR_PAGE_TOKENS;
 constexpr int kMaxBf16 = OSCAR_MAX_BF16_TOKENS;
 constexpr int kBf16PagesPerSplit = 4;                              // one wave per page
 constexpr int kMaxSplits = 1024;        // history chunks per (sequence, KV head)
+#ifndef OSCAR_INT2_WAVES
+#define OSCAR_INT2_WAVES 16
+#endif
+constexpr int kMfmaWaves = OSCAR_INT2_WAVES;   // matrix-core INT2 kernel: waves per block
+// KV heads per block of the matrix-core INT2 kernel: Hkv rounded up to a power
+// of two, at most 8; the block's waves are split evenly over them
+__host__ __device__ constexpr int mfma_heads_per_block(int hkv) {
+  return hkv >= 8 ? 8 : hkv > 4 ? 8 : hkv > 2 ? 4 : hkv > 1 ? 2 : 1;
+}
 constexpr int kBf16Splits = kMaxBf16 / (kPage * kBf16PagesPerSplit); // 5 BF16 partials
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -46,8 +55,6 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 // Workspace partition used by decode_attn and merge.
 struct WsLayout {
   size_t qrot;      // fp32 [B][Hq][D]     q . R_k (unscaled)
-  size_t qpiece;    // int8 [B][Hq][4][D] + per-head exponent (MFMA path)
-  size_t qexp;      // int32 [B][Hq]
   size_t part_o;    // fp32 [B][Hq][S][D]  history chunk partial outputs (rotated basis)
   size_t part_ml;   // fp32 [B][Hq][S][2]  (max logit in log2 units, sum of exponentials)
   size_t bf_o;      // fp32 [B][Hq][kBf16Splits][D]  BF16 segment partial outputs

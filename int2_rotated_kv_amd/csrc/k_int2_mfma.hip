@@ -21,14 +21,15 @@
 //     shifted copies; A = w * 2^(8-b) in f16, so A * B = A + w * code / 4;
 //     fp32 accumulation; the A part is removed with sum_t A (same f16 values).
 //
-// One block per (sequence, chunk of pages, group of up to 8 KV heads), one wave
-// per KV head.  The waves of a block walk the same pages, so the records of all
-// KV heads of a page (adjacent in the pool) are read together; each wave keeps
-// 3 pages in flight in a register ring and writes its own chunk partial.  The
-// running max per head is lazy: it is raised (16-lane DPP reductions, rescale
-// of the partial sums) only when a logit exceeds it by more than 2 (log2
-// units), so unnormalised weights stay below 4.  Requires 4 or 8 q heads per KV
-// head and V group scales below 1024 (A = w * 16 must stay in f16 range).
+// One block of 8 waves per (sequence, KV head, equal part of its history);
+// each wave is one chunk and writes one partial.  The waves take batches of 4
+// consecutive pages of the part from an LDS counter: the SIMD arbiter favours
+// older waves, so fixed page ranges per wave would finish unevenly.  Each wave
+// keeps 3 pages in flight in a register ring.  The running max per head is
+// lazy: it is raised (16-lane DPP reductions, rescale of the partial sums) only
+// when a logit exceeds it by more than 2 (log2 units), so unnormalised weights
+// stay below 4.  Requires 4 or 8 q heads per KV head and V group scales below
+// 1024 (A = w * 16 must stay in f16 range).
 #include "common.hpp"
 
 namespace oscar {
@@ -111,12 +112,31 @@ __device__ __forceinline__ void load_words(uint32_t (&dst)[NW], const uint32_t *
   }
 }
 
+// NW consecutive words at byte offset `off` of a buffer resource (16- or
+// 8-byte loads); the resource's base and bounds live in scalar registers, so
+// a wave-uniform base costs no vector instructions
+template <int NW>
+__device__ __forceinline__ void buf_words(uint32_t (&dst)[NW], __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  if constexpr (NW % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+      const u4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * i, 0, 0);
+      dst[4 * i] = v.x; dst[4 * i + 1] = v.y; dst[4 * i + 2] = v.z; dst[4 * i + 3] = v.w;
+    }
+  } else {
+    static_assert(NW == 2, "2 or a multiple of 4 words");
+    const u2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+    dst[0] = v.x; dst[1] = v.y;
+  }
+}
+
 }  // namespace
 
-constexpr int kMfmaHeadsPerBlock = 8;
 
 template <int D, int G, int GQ>
-__global__ __launch_bounds__(64 * kMfmaHeadsPerBlock) void k_int2_mfma(DecodeParams p) {
+__global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   constexpr RecLayout RL(D, G);
   constexpr int NG = D / G;            // groups per token
   constexpr int NBLK = D / 64;         // 64-channel blocks (one int8 MFMA K each)
@@ -124,20 +144,122 @@ __global__ __launch_bounds__(64 * kMfmaHeadsPerBlock) void k_int2_mfma(DecodePar
   constexpr int NQK = NBLK * GPB;      // QK MFMAs per head quad per page
   constexpr int NH = D / 64;           // 64-channel halves of PV (lane owns l + 64*h2)
   constexpr int NQ = GQ / 4;           // head quads
-  constexpr int HB = kMfmaHeadsPerBlock;
+  constexpr int HB = kMfmaWaves;
   static_assert(GQ == 4 || GQ == 8, "4 or 8 q heads per KV head");
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave (uniform)
-  const int nwav = blockDim.x >> 6;
-  const int ngrp = (p.Hkv + nwav - 1) / nwav;
-  const int S = p.splits;
-  const int hg = blockIdx.x % ngrp;
-  const int split = (blockIdx.x / ngrp) % S;
-  const int b = blockIdx.x / (ngrp * S);
-  const int j = hg * nwav + w;                    // this wave's KV head
-  if (j >= p.Hkv) return;                         // no block-level barrier follows
+  // block = (sequence, group of HG KV heads, part of the history); WH waves
+  // per head, each one chunk with its own partial
+  const int HG = mfma_heads_per_block(p.Hkv);
+  const int WH = HB / HG;
+  const int S = p.splits;                         // WH waves x P parts per (sequence, KV head)
+  const int P = S / WH;
+  const int ngrp = (p.Hkv + HG - 1) / HG;
+  const int part = blockIdx.x % P;
+  const int hg = (blockIdx.x / P) % ngrp;
+  const int b = blockIdx.x / (P * ngrp);
+  // waves 4k .. 4k+3 sit in issue slot k of the CU's four SIMDs, and the
+  // arbiter favours lower slots; with 8 heads the two waves of a head are
+  // taken from slots 0 and 3, or 1 and 2, so every head gets about the same
+  // issue share
+  const int wq = w >> 2;                          // issue slot of this wave
+  const int wpos = (HG == 8 && (wq == 2 || wq == 3)) ? (w ^ 4) : w;
+  const int jl = wpos % HG;                       // head within the group
+  const int j = hg * HG + jl;                     // this wave's KV head
+  const int split = part * WH + wpos / HG;        // this wave's partial
   const int r16 = lane & 15, kb = lane >> 4;      // row-in-16 and lane group
+  __shared__ int batch_ctr[8];                    // per head: next batch of the part
+  if (threadIdx.x < 8) batch_ctr[threadIdx.x] = 0;
+  __syncthreads();                                // the only block-level barrier
+  if (j >= p.Hkv) return;
+
+  int hl = p.hist_len[b];
+  hl = hl < 0 ? 0 : hl;
+  hl = hl > p.max_hist_len ? p.max_hist_len : hl;
+  hl = hl > kPage * p.hist_stride ? kPage * p.hist_stride : hl;
+  const int npages = (hl + kPage - 1) / kPage;
+  // this block's pages [pbeg, pend): part `part` of P equal parts
+  const int pbeg = (int)((long long)npages * part / P);
+  const int pend = (int)((long long)npages * (part + 1) / P);
+
+  // ---------------- page loop: register ring of NS pages ----------------
+  // stage data of one page for this lane: K words of token r16 / lane group kb,
+  // K and V (scale, zero) words of token r16, and the V words of channels
+  // lane + 64*h2 (adjacent in the record).
+#ifndef OSCAR_INT2_STAGES
+#define OSCAR_INT2_STAGES 4
+#endif
+  constexpr int NS = OSCAR_INT2_STAGES;   // pages in the register ring (NS-1 in flight)
+  constexpr int SW = D / 32;             // words of a lane slot: NBLK K words, NH V words
+  struct Stage {
+    uint32_t c[SW];                      // K words of (token r16, part kb), V words of channels lane + 64*h2
+    uint32_t sz[2 * NG];                 // token r16: K (scale, zero) per group, then V
+    int ok;
+  };
+  Stage st[NS];
+  // page ids through the constant address space: wave-uniform scalar loads,
+  // counted apart from the vector loads so reading one never drains the ring
+  using cint32 = const __attribute__((address_space(4))) int32_t;
+  cint32 *ptab = (cint32 *)(p.hist_pages + (size_t)b * p.hist_stride);
+  const size_t rec_stride = (size_t)p.Hkv * RL.bytes();
+  const uint8_t *pool_j = p.int2_pool + (size_t)j * RL.bytes();
+
+  // per-lane byte offsets inside a record: lane slot `lane` (= 16*kb + r16)
+  // and token slot r16
+  const uint32_t off_c = (uint32_t)RL.kword(lane, 0);
+  const uint32_t off_sz = (uint32_t)RL.tok_sz(r16);
+  const int npool = p.num_int2_pages < 0x7fffffff ? (int)p.num_int2_pages : 0x7fffffff;
+
+  // page id of history page k (wave-uniform); pages outside [pbeg, pend) are
+  // -1 and the table is never read there
+  auto page_id = [&](int k) -> int {
+    const int id = ptab[k >= pbeg && k < pend ? k : pbeg];
+    return (k >= pbeg && k < pend) ? id : -1;
+  };
+
+  // Work distribution: the WH waves of a head take batches of NS consecutive
+  // pages of the block's part from that head's LDS counter, so waves the SIMD
+  // arbiter favours (older waves) take more pages and a head's waves finish
+  // together.
+  auto grab = [&]() -> int {                      // start page of the next batch
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&batch_ctr[jl], NS);
+    return pbeg + __builtin_amdgcn_readfirstlane(v);
+  };
+
+  auto issue = [&](Stage &sg, int phys) {      // wave-uniform phys
+    sg.ok = phys >= 0 && phys < npool;
+    // out-of-range stages still load (from page 0) so every lane issues the
+    // same load sequence; their data is never used
+    const uint8_t *rec = pool_j + (sg.ok ? (size_t)phys : 0) * rec_stride;
+    // one record as a buffer resource (word 3: 32-bit data format, required
+    // non-zero for buffer loads on this family); reads past it return 0
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(rec), (short)0, RL.bytes(), 0x00020000);
+    buf_words<SW>(sg.c, rs, off_c);
+    buf_words<2 * NG>(sg.sz, rs, off_sz);
+  };
+
+  // the rotated query is loaded first, then the first pages are requested, so
+  // the query prologue runs while the pages are in flight (vector loads return
+  // in order); the page ids an outer iteration issues are read one iteration
+  // earlier
+  float qv[GQ][D / 64];
+  {
+    const float *qrot = reinterpret_cast<const float *>(p.ws + p.L.qrot);
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k)
+        qv[h][k] = qrot[((size_t)b * p.Hq + p.q_of_kv[j * GQ + h]) * D + lane + 64 * k];
+  }
+  int bcur = pend;                                // batch being processed
+  if (pend > pbeg) {
+    bcur = grab();
+#pragma unroll
+    for (int s2 = 0; s2 < NS - 1; ++s2) issue(st[s2], page_id(bcur + s2));
+  }
 
   __shared__ float qf_all[HB][GQ][D];             // per wave: q_rot (unscaled)
   __shared__ __align__(16) _Float16 wbuf_all[HB][NG][GQ][16];   // per wave: w[grp][head][slot]
@@ -145,19 +267,17 @@ __global__ __launch_bounds__(64 * kMfmaHeadsPerBlock) void k_int2_mfma(DecodePar
   _Float16 (*wbuf)[GQ][16] = wbuf_all[w];
 
   // ---------------- prologue: the wave's q heads as integer pieces ----------------
-  const float *qrot = reinterpret_cast<const float *>(p.ws + p.L.qrot);
   int qexp[GQ];
   float qz[GQ][NG];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
-    const float *src = qrot + ((size_t)b * p.Hq + p.q_of_kv[j * GQ + h]) * D;
     float mx = 0.f;
     float gs[NG];
 #pragma unroll
     for (int g2 = 0; g2 < NG; ++g2) gs[g2] = 0.f;
 #pragma unroll
     for (int k = 0; k < D / 64; ++k) {
-      const float v = src[lane + 64 * k];
+      const float v = qv[h][k];
       qf[h][lane + 64 * k] = v;
       mx = fmaxf(mx, fabsf(v));
       gs[(lane + 64 * k) / G] += v;
@@ -235,16 +355,6 @@ __global__ __launch_bounds__(64 * kMfmaHeadsPerBlock) void k_int2_mfma(DecodePar
     for (int g2 = 0; g2 < NG; ++g2) qzl[qd][g2] = z_l[g2];
   }
 
-  int hl = p.hist_len[b];
-  hl = hl < 0 ? 0 : hl;
-  hl = hl > p.max_hist_len ? p.max_hist_len : hl;
-  hl = hl > kPage * p.hist_stride ? kPage * p.hist_stride : hl;
-  const int npages = (hl + kPage - 1) / kPage;
-  const int p0 = split * p.pages_per_split;
-  int p1 = p0 + p.pages_per_split;
-  p1 = p1 > npages ? npages : p1;
-  const int nk = p1 > p0 ? p1 - p0 : 0;           // pages of this wave's chunk
-
   // running state; QK layout: lane = (head 4*qd + kb, token r16)
   float m_run[NQ], lsum[NQ], zacc[NQ][NG];
 #pragma unroll
@@ -261,44 +371,6 @@ __global__ __launch_bounds__(64 * kMfmaHeadsPerBlock) void k_int2_mfma(DecodePar
 #pragma unroll
     for (int h2 = 0; h2 < NH; ++h2) acc[qd][h2] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // ---------------- page loop: register ring of NS pages ----------------
-  // stage data of one page for this lane: K words of token r16 / lane group kb,
-  // K and V (scale, zero) words of token r16, and the V words of channels
-  // lane + 64*h2 (adjacent in the record).
-#ifndef OSCAR_INT2_STAGES
-#define OSCAR_INT2_STAGES 4
-#endif
-  constexpr int NS = OSCAR_INT2_STAGES;   // pages in the register ring (NS-1 in flight)
-  constexpr int SW = D / 32;             // words of a lane slot: NBLK K words, NH V words
-  struct Stage {
-    uint32_t c[SW];                      // K words of (token r16, part kb), V words of channels lane + 64*h2
-    uint32_t sz[2 * NG];                 // token r16: K (scale, zero) per group, then V
-    int ok;
-  };
-  Stage st[NS];
-  // page ids through the constant address space: wave-uniform scalar loads,
-  // counted apart from the vector loads so reading one never drains the ring
-  using cint32 = const __attribute__((address_space(4))) int32_t;
-  cint32 *ptab = (cint32 *)(p.hist_pages + (size_t)b * p.hist_stride + p0);
-  const size_t rec_stride = (size_t)p.Hkv * RL.bytes();
-  const uint8_t *pool_j = p.int2_pool + (size_t)j * RL.bytes();
-
-  // per-lane byte offsets inside a record: lane slot `lane` (= 16*kb + r16)
-  // and token slot r16
-  const uint32_t off_c = (uint32_t)RL.kword(lane, 0);
-  const uint32_t off_sz = (uint32_t)RL.tok_sz(r16);
-  const int npool = p.num_int2_pages < 0x7fffffff ? (int)p.num_int2_pages : 0x7fffffff;
-
-  auto issue = [&](Stage &sg, int k) {         // wave-uniform k
-    const int phys = k < nk ? ptab[k] : -1;
-    sg.ok = phys >= 0 && phys < npool;
-    // out-of-range stages still load (from page 0) so every lane issues the
-    // same load sequence; their data is never used
-    const uint8_t *rec = pool_j + (sg.ok ? (size_t)phys : 0) * rec_stride;
-    load_words<SW>(sg.c, reinterpret_cast<const uint32_t *>(rec + off_c));
-    load_words<2 * NG>(sg.sz, reinterpret_cast<const uint32_t *>(rec + off_sz));
-  };
-
   // code -> f16 (1 + code/4) masks, held in registers (opaque to the compiler)
   // so that (x & m) | c selects one v_and_or_b32
   uint32_t m4, m6, m8, f16one;
@@ -313,9 +385,8 @@ __global__ __launch_bounds__(64 * kMfmaHeadsPerBlock) void k_int2_mfma(DecodePar
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) m_thr[qd] = -INFINITY;
 
-  auto process = [&](Stage &sg, int k) {
+  auto process = [&](Stage &sg, int pg) {          // pg: history page index
     if (!sg.ok) return;
-    const int pg = p0 + k;
     const int ntok = hl - pg * kPage < kPage ? hl - pg * kPage : kPage;
     // tokens past the history length (only on a sequence's last, partial page):
     // logit -inf and (scale, zero) read as 0, since unwritten record bytes may
@@ -352,7 +423,11 @@ __global__ __launch_bounds__(64 * kMfmaHeadsPerBlock) void k_int2_mfma(DecodePar
       float sc = 0.f, zt = 0.f;
 #pragma unroll
       for (int g2 = 0; g2 < NG; ++g2) {
-        const int dint = ((qacc[qd][g2][0] << 7) + qacc[qd][g2][1]) * 128 + qacc[qd][g2][2];
+        // p0*2^14 + p1*2^7 + p2 as two shift-adds (the empty asm keeps the
+        // compiler from re-associating them into two shifts and an add3)
+        int dhi = (qacc[qd][g2][0] << 7) + qacc[qd][g2][1];
+        asm volatile("" : "+v"(dhi));
+        const int dint = (dhi << 7) + qacc[qd][g2][2];
         sc = fmaf(bf16_lo(sg.sz[g2]), (float)dint, sc);
         zt = fmaf(bf16_hi(sg.sz[g2]), qzl[qd][g2], zt);
       }
@@ -446,16 +521,22 @@ __global__ __launch_bounds__(64 * kMfmaHeadsPerBlock) void k_int2_mfma(DecodePar
     wave_lds_sync();
   };
 
-  if (nk > 0) {
+  // the ring holds pages bcur .. bcur + NS - 2 on entry; each step issues one
+  // page (the rest of this batch, then the start of the next) and processes one
+  while (bcur < pend) {
+    const int bnext = grab();
+    int idc[NS];
 #pragma unroll
-    for (int s2 = 0; s2 < NS - 1; ++s2) issue(st[s2], s2);
-    for (int k = 0; k < nk; k += NS) {
-#pragma unroll
-      for (int s2 = 0; s2 < NS; ++s2) {
-        issue(st[(s2 + NS - 1) % NS], k + s2 + NS - 1);
-        if (k + s2 < nk) process(st[s2], k + s2);
-      }
+    for (int s2 = 0; s2 < NS; ++s2) {
+      const int ipos = s2 + NS - 1;
+      idc[s2] = ipos < NS ? page_id(bcur + ipos) : page_id(bnext + ipos - NS);
     }
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2) {
+      issue(st[(s2 + NS - 1) % NS], idc[s2]);
+      if (bcur + s2 < pend) process(st[s2], bcur + s2);
+    }
+    bcur = bnext;
   }
 
   // ---------------- epilogue: this wave's chunk partial ----------------
@@ -495,9 +576,10 @@ __global__ __launch_bounds__(64 * kMfmaHeadsPerBlock) void k_int2_mfma(DecodePar
 
 template <int D, int G>
 static void launch_mfma_dg(const DecodeParams &p, hipStream_t s) {
-  const int hb = p.Hkv < kMfmaHeadsPerBlock ? p.Hkv : kMfmaHeadsPerBlock;
-  const int ngrp = (p.Hkv + hb - 1) / hb;
-  const dim3 grid(p.B * p.splits * ngrp), blk(64 * hb);
+  // splits is a multiple of the waves per head (argument checking rounds it up)
+  const int hg = mfma_heads_per_block(p.Hkv);
+  const int ngrp = (p.Hkv + hg - 1) / hg;
+  const dim3 grid(p.B * ngrp * (p.splits / (kMfmaWaves / hg))), blk(64 * kMfmaWaves);
   if (p.g == 8) hipLaunchKernelGGL((k_int2_mfma<D, G, 8>), grid, blk, 0, s, p);
   else hipLaunchKernelGGL((k_int2_mfma<D, G, 4>), grid, blk, 0, s, p);
 }
