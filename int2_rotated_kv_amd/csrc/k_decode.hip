@@ -12,6 +12,8 @@
 
 namespace oscar {
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 // ---------------------------------------------------------------------------
 // q . R_k for every (sequence, q head): the history keys are stored as k . R_k,
 // so (q . R_k) . (k . R_k) = q . k for an orthogonal R_k.  fp64 accumulation,
@@ -70,108 +72,123 @@ hipError_t launch_qrot(const DecodeParams &p, const uint16_t *q, const float *Rk
 
 // ---------------------------------------------------------------------------
 // BF16 segment: up to 320 unrotated tokens per sequence in BF16 pages.  Grid
-// (sequence x KV head, 5 splits of 4 pages); one wave per page, the g q heads
-// of the KV head share every load.  Per page:
-//   QK: lane (t = lane%16, part = lane/16) dots channels 32*part .. +31 of token
-//       t with q; the parts are summed across lanes.
-//   PV: lane owns channels D/64*lane .. +D/64-1 and accumulates p * v over the
-//       16 tokens.
-// Each split writes one partial (m, l, o) per q head.
+// (sequence x KV head, 5 chunks of 4 pages); one wave per page, the g q heads
+// of the KV head share every load.  Per page (16 tokens):
+//   QK on v_mfma_f32_16x16x32_bf16: A = 16 K rows (lane (kb, t) holds channels
+//      32m + 8kb .. +7 of token t: one 16-byte load), B = the q heads (bf16,
+//      exact products, fp32 accumulation); lane (kb, h) receives tokens
+//      4kb .. 4kb+3 of head h.
+//   softmax per head over the 16 tokens (4 in-lane, 4 lane groups).
+//   PV on the vector ALU: lane owns channels D/64*lane .. +D/64-1 and
+//      accumulates p * v over the 16 tokens, p from LDS.
+// Every load of the page is issued before any of it is used.  Each chunk
+// writes one partial per q head.
 // ---------------------------------------------------------------------------
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
 template <int D, int GQ>
 __global__ __launch_bounds__(256) void k_bf16_seg(DecodeParams p, const uint16_t *__restrict__ q) {
-  constexpr int CP = D / 4;            // channels per QK part
+  constexpr int NM = D / 32;           // QK matrix instructions (32 channels each)
   constexpr int NCH = D / 64;          // PV channels per lane
+  static_assert(GQ <= 16, "q heads are the 16 columns of the QK product");
   const int b = blockIdx.x / p.Hkv;
   const int j = blockIdx.x % p.Hkv;
   const int split = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int t = lane & 15, part = lane >> 4;
+  const int r16 = lane & 15, kb = lane >> 4;
 
-  __shared__ float qs[D][GQ];
-  __shared__ float pb[4][16][GQ];
+  __shared__ __align__(16) float pb[4][kPage][GQ];   // per wave: p[token][head]
   __shared__ float wm[4][GQ], wl[4][GQ];
   __shared__ float wo[4][GQ][D];
 
+  // segment length and this wave's page id, then every load
+  const int pgi = split * kBf16PagesPerSplit + w;     // page index in the table
   int T = p.bf16_len[b];
+  const int64_t page = pgi < p.bf16_stride ? p.bf16_pages[(size_t)b * p.bf16_stride + pgi] : -1;
   T = T < 0 ? 0 : T;
   T = T > kMaxBf16 ? kMaxBf16 : T;
   T = T > kPage * p.bf16_stride ? kPage * p.bf16_stride : T;
+  const int ntok = T - pgi * kPage;
+  const bool live = ntok > 0 && page >= 0 && page < p.num_bf16_pages;
 
-  for (int i = tid; i < GQ * D; i += 256) {
-    const int h = i / D, c = i % D;
-    qs[c][h] = bf16_to_f32(q[((size_t)b * p.Hq + p.q_of_kv[j * GQ + h]) * D + c]) * p.sm_log2;
-  }
-  __syncthreads();
-
-  const int pgi = split * kBf16PagesPerSplit + w;     // page index in the table
-  float m[GQ], o[GQ][NCH], lsum[GQ];
+  // q operands: lane (kb, h) holds channels 32m + 8kb .. +7 of q head h
+  v8bf qb[NM];
+  {
+    const int hq = r16 < GQ ? p.q_of_kv[j * GQ + r16] : 0;
+    const uint4 *qp = reinterpret_cast<const uint4 *>(q + ((size_t)b * p.Hq + hq) * D + 8 * kb);
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    m[h] = -INFINITY;
-    lsum[h] = 0.f;
+    for (int m = 0; m < NM; ++m) {
+      const uint4 v = r16 < GQ ? qp[4 * m] : make_uint4(0u, 0u, 0u, 0u);
+      __builtin_memcpy(&qb[m], &v, 16);
+    }
+  }
+  v8bf ka[NM];
+  uint32_t vraw[kPage];
+  if (live) {
+    const size_t base = ((page * p.Hkv + j) * kPage) * D;
+    const uint4 *kp = reinterpret_cast<const uint4 *>(p.bf16_k + base + (size_t)r16 * D + 8 * kb);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const uint4 v = kp[4 * m];
+      __builtin_memcpy(&ka[m], &v, 16);
+    }
+    const uint16_t *vp = p.bf16_v + base;
+#pragma unroll
+    for (int tt = 0; tt < kPage; ++tt) {
+      if constexpr (NCH == 2) vraw[tt] = reinterpret_cast<const uint32_t *>(vp)[(size_t)tt * (D / 2) + lane];
+      else vraw[tt] = vp[(size_t)tt * D + lane];
+    }
+  }
+
+  float m_h = -INFINITY, l_h = 0.f;
+  float o[GQ][NCH];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h)
 #pragma unroll
     for (int k = 0; k < NCH; ++k) o[h][k] = 0.f;
-  }
-  const int ntok = T - pgi * kPage;
-  if (ntok > 0) {
-    const int64_t page = p.bf16_pages[(size_t)b * p.bf16_stride + pgi];
-    if (page >= 0 && page < p.num_bf16_pages) {
-      const size_t base = ((page * p.Hkv + j) * kPage) * D;
-      // ---- QK ----
-      const uint4 *kp = reinterpret_cast<const uint4 *>(p.bf16_k + base + (size_t)t * D + part * CP);
-      float dot[GQ];
+  if (live) {
+    // ---- QK ----
+    v4f sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h = 0; h < GQ; ++h) dot[h] = 0.f;
+    for (int m = 0; m < NM; ++m) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], qb[m], sacc, 0, 0, 0);
+    // lane (kb, h): tokens 4kb + i of head h; slots past the segment length
+    // (any bits) get logit -inf
+    float sv[4];
 #pragma unroll
-      for (int c8 = 0; c8 < CP / 8; ++c8) {
-        const uint4 v = kp[c8];
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    for (int i = 0; i < 4; ++i) sv[i] = (4 * kb + i < ntok) ? sacc[i] * p.sm_log2 : -INFINITY;
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));           // >= one valid token: finite
+    float pr[4], l = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = part * CP + c8 * 8 + 2 * e;
-          const float k0 = bf16_lo(w4[e]), k1 = bf16_hi(w4[e]);
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = exp2f(sv[i] - mx);                    // 0 for masked slots
+      l += pr[i];
+    }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    m_h = mx;
+    l_h = l;
+    if (r16 < GQ) {
 #pragma unroll
-          for (int h = 0; h < GQ; ++h) dot[h] = fmaf(qs[c + 1][h], k1, fmaf(qs[c][h], k0, dot[h]));
-        }
+      for (int i = 0; i < 4; ++i) pb[w][4 * kb + i][r16] = pr[i];
+    }
+    wave_lds_sync();
+    // ---- PV ----  (slots past the segment length may hold any bits: 0)
+#pragma unroll
+    for (int tt = 0; tt < kPage; ++tt) {
+      float v[NCH];
+      if constexpr (NCH == 2) {
+        v[0] = tt < ntok ? bf16_lo(vraw[tt]) : 0.f;
+        v[1] = tt < ntok ? bf16_hi(vraw[tt]) : 0.f;
+      } else {
+        v[0] = tt < ntok ? bf16_to_f32((uint16_t)vraw[tt]) : 0.f;
       }
-      const bool valid = t < ntok;
 #pragma unroll
       for (int h = 0; h < GQ; ++h) {
-        float s = dot[h];
-        s += __shfl_xor(s, 16);
-        s += __shfl_xor(s, 32);
-        s = valid ? s : -INFINITY;
-        float mx = s;
+        const float ph = pb[w][tt][h];
 #pragma unroll
-        for (int o2 = 1; o2 < 16; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
-        const float pr = valid ? exp2f(s - mx) : 0.f;
-        float l = pr;
-#pragma unroll
-        for (int o2 = 1; o2 < 16; o2 <<= 1) l += __shfl_xor(l, o2);
-        m[h] = mx;
-        lsum[h] = l;
-        if (part == 0) pb[w][t][h] = pr;
-      }
-      wave_lds_sync();
-      // ---- PV ----
-      const uint16_t *vp = p.bf16_v + base;
-      const int tmax = ntok < kPage ? ntok : kPage;
-      for (int tt = 0; tt < tmax; ++tt) {
-        float v[NCH];
-        if constexpr (NCH == 2) {
-          const uint32_t vv = reinterpret_cast<const uint32_t *>(vp)[(size_t)tt * (D / 2) + lane];
-          v[0] = bf16_lo(vv);
-          v[1] = bf16_hi(vv);
-        } else {
-          v[0] = bf16_to_f32(vp[(size_t)tt * D + lane]);
-        }
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-          const float pr = pb[w][tt][h];
-#pragma unroll
-          for (int k = 0; k < NCH; ++k) o[h][k] = fmaf(pr, v[k], o[h][k]);
-        }
+        for (int k = 0; k < NCH; ++k) o[h][k] = fmaf(ph, v[k], o[h][k]);
       }
     }
   }
@@ -179,8 +196,8 @@ __global__ __launch_bounds__(256) void k_bf16_seg(DecodeParams p, const uint16_t
   for (int h = 0; h < GQ; ++h) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) wo[w][h][lane * NCH + k] = o[h][k];
-    if (lane == 0) { wm[w][h] = m[h]; wl[w][h] = lsum[h]; }
   }
+  if (kb == 0 && r16 < GQ) { wm[w][r16] = m_h; wl[w][r16] = l_h; }
   __syncthreads();
   float *bo = reinterpret_cast<float *>(p.ws + p.L.bf_o);
   float *bml = reinterpret_cast<float *>(p.ws + p.L.bf_ml);
