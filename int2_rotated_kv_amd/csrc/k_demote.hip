@@ -65,6 +65,18 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
   __shared__ int s_src[T], s_dst[T];
   __shared__ double red_mx[2][T], red_mn[2][T];
 
+  // one token: the D loads of this thread's R column do not depend on the
+  // token, so they are issued first
+  const float *R = isv ? Rv : Rk;
+  float rcol[T == 1 ? D : 1];
+  if constexpr (T == 1) {
+    if (R != nullptr) {
+      const float *Rj = R + (size_t)j * D * D;
+#pragma unroll
+      for (int i = 0; i < D; ++i) rcol[i] = Rj[(size_t)i * D + c];
+    }
+  }
+
   if (c < T) {
     const int e = e0 + c;
     int sv = -1, dv = -1;
@@ -92,19 +104,13 @@ __global__ __launch_bounds__(D) void k_demote(const uint16_t *__restrict__ bf_k,
   __syncthreads();
 
   double x[T];
-  const float *R = isv ? Rv : Rk;
   if (R != nullptr && T == 1) {
-    // one token: all D loads of column c are issued before the dot product
-    R += (size_t)j * D * D;
-    float r[D];
-#pragma unroll
-    for (int i = 0; i < D; ++i) r[i] = R[(size_t)i * D + c];
     double a0 = 0.0, a1 = 0.0;
 #pragma unroll
     for (int i = 0; i < D; i += 2) {
       const double2 kk = *reinterpret_cast<const double2 *>(&xs[0][i]);
-      a0 = fma(kk.x, (double)r[i], a0);
-      a1 = fma(kk.y, (double)r[i + 1], a1);
+      a0 = fma(kk.x, (double)rcol[i], a0);
+      a1 = fma(kk.y, (double)rcol[i + 1], a1);
     }
     x[0] = a0 + a1;
   } else if (R != nullptr) {

@@ -12,16 +12,19 @@
 namespace oscar {
 
 constexpr int kMergeThreads = 256;
+constexpr int kMergeRegChunks = 8;       // chunk outputs per thread loaded up front
 
-// One block (4 waves) per (sequence, q head).  Phase 1 (wave 0) reduces the
-// chunk maxima and sums and stages the chunk weights in LDS; phase 2 splits
-// the chunks over 256 / D thread groups that sum weighted chunk outputs with
-// independent loads; phase 3 un-rotates (the same groups split the R_v row)
-// and merges the BF16 segment.
+// One block (4 waves) per (sequence, q head).  Every load the block needs is
+// issued first (chunk maxima and sums, the first chunk outputs of each thread,
+// its slice of the R_v row, the BF16 partials), so the block waits for memory
+// about once; the rest is LDS exchanges.  Thread (group gi, channel c) sums
+// chunks gi, gi + NGR, ... for channel c and multiplies the slice gi of the
+// R_v row c.
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeParams p, const float *__restrict__ Rv,
                                                          float *__restrict__ out, float *__restrict__ lse) {
   constexpr int NGR = kMergeThreads / D;         // thread groups (2 or 4)
+  constexpr int KPG = D / NGR / 4;               // float4 of an R_v row per group
   const size_t bh = blockIdx.x;
   const int j = p.kv_of_q[bh % p.Hq];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -34,19 +37,48 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeParams p, const f
 
   const float *ml = reinterpret_cast<const float *>(p.ws + p.L.part_ml) + bh * S * 2;
   const float *po = reinterpret_cast<const float *>(p.ws + p.L.part_o) + bh * S * D;
+  const float *bml = reinterpret_cast<const float *>(p.ws + p.L.bf_ml) + bh * kBf16Splits * 2;
+  const float *bo = reinterpret_cast<const float *>(p.ws + p.L.bf_o) + bh * kBf16Splits * D + c;
 
-  // phase 1: M = max_s m_s, L = sum_s l_s 2^(m_s - M)
+  // ---- every load up front ----
+  float ov[kMergeRegChunks];                     // chunk outputs gi + NGR*k, channel c
+#pragma unroll
+  for (int k = 0; k < kMergeRegChunks; ++k) {
+    const int s2 = gi + NGR * k;
+    ov[k] = s2 < S ? po[(size_t)s2 * D + c] : 0.f;
+  }
+  float4 r[KPG];
+  if (Rv != nullptr) {
+    const float4 *row = reinterpret_cast<const float4 *>(Rv + ((size_t)j * D + c) * D) + gi * KPG;
+#pragma unroll
+    for (int k = 0; k < KPG; ++k) r[k] = row[k];
+  }
+  float bm[kBf16Splits], bl[kBf16Splits], bov[kBf16Splits];
+#pragma unroll
+  for (int s2 = 0; s2 < kBf16Splits; ++s2) {
+    bm[s2] = bml[2 * s2];
+    bl[s2] = bml[2 * s2 + 1];
+    bov[s2] = gi == 0 ? bo[(size_t)s2 * D] : 0.f;
+  }
+  float mv = -INFINITY, lv = 0.f;                // wave 0: chunk lane
+  if (tid < 64 && lane < S) {
+    mv = ml[2 * lane];
+    lv = ml[2 * lane + 1];
+  }
+
+  // ---- chunk weights (wave 0): M = max m_s, L = sum l_s 2^(m_s - M) ----
   if (tid < 64) {
-    float M = -INFINITY;
-    for (int s2 = lane; s2 < S; s2 += 64) M = fmaxf(M, ml[2 * s2]);
+    float M = mv;
+    for (int s2 = lane + 64; s2 < S; s2 += 64) M = fmaxf(M, ml[2 * s2]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     float L = 0.f;
     for (int s2 = lane; s2 < S; s2 += 64) {
-      const float m = ml[2 * s2];
+      const float m = s2 == lane ? mv : ml[2 * s2];
+      const float l = s2 == lane ? lv : ml[2 * s2 + 1];
       const float a = (m == -INFINITY) ? 0.f : exp2f(m - M);
       a_s[s2] = a;
-      L = fmaf(ml[2 * s2 + 1], a, L);
+      L = fmaf(l, a, L);
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
@@ -54,25 +86,22 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeParams p, const f
   }
   __syncthreads();
 
-  // phase 2: O[c] = sum_s a_s o_s[c]; chunks gi, gi + NGR, ...  A chunk with
-  // weight 0 (no tokens) contributes 0 whatever its stored output holds.
+  // ---- O[c] = sum_s a_s o_s[c]; a chunk with weight 0 (no tokens) adds 0
+  // whatever its stored output holds ----
   {
-    float O0 = 0.f, O1 = 0.f, O2 = 0.f, O3 = 0.f;
-    int s2 = gi;
-    for (; s2 + 3 * NGR < S; s2 += 4 * NGR) {
-      const float v0 = po[(size_t)s2 * D + c], v1 = po[(size_t)(s2 + NGR) * D + c];
-      const float v2 = po[(size_t)(s2 + 2 * NGR) * D + c], v3 = po[(size_t)(s2 + 3 * NGR) * D + c];
-      const float w0 = a_s[s2], w1 = a_s[s2 + NGR], w2 = a_s[s2 + 2 * NGR], w3 = a_s[s2 + 3 * NGR];
-      O0 = fmaf(w0, w0 != 0.f ? v0 : 0.f, O0);
-      O1 = fmaf(w1, w1 != 0.f ? v1 : 0.f, O1);
-      O2 = fmaf(w2, w2 != 0.f ? v2 : 0.f, O2);
-      O3 = fmaf(w3, w3 != 0.f ? v3 : 0.f, O3);
+    float O0 = 0.f, O1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMergeRegChunks; ++k) {
+      const int s2 = gi + NGR * k;
+      const float wgt = s2 < S ? a_s[s2] : 0.f;
+      float &O = (k & 1) ? O1 : O0;
+      O = fmaf(wgt, wgt != 0.f ? ov[k] : 0.f, O);
     }
-    for (; s2 < S; s2 += NGR) {
-      const float v0 = po[(size_t)s2 * D + c], w0 = a_s[s2];
-      O0 = fmaf(w0, w0 != 0.f ? v0 : 0.f, O0);
+    for (int s2 = gi + NGR * kMergeRegChunks; s2 < S; s2 += NGR) {
+      const float v = po[(size_t)s2 * D + c], wgt = a_s[s2];
+      O0 = fmaf(wgt, wgt != 0.f ? v : 0.f, O0);
     }
-    red[gi][c] = (O0 + O1) + (O2 + O3);
+    red[gi][c] = O0 + O1;
   }
   __syncthreads();
   if (tid < D) {
@@ -83,16 +112,10 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeParams p, const f
   }
   __syncthreads();
 
-  // phase 3: un-rotation O_hist[c] = sum_k O[k] R_v[j][c][k], group gi taking
-  // k in [gi*D/NGR, (gi+1)*D/NGR)
+  // ---- un-rotation O_hist[c] = sum_k O[k] R_v[j][c][k] ----
   float oh;
   if (Rv != nullptr) {
-    constexpr int KPG = D / NGR / 4;             // float4 per group
-    const float4 *row = reinterpret_cast<const float4 *>(Rv + ((size_t)j * D + c) * D) + gi * KPG;
     const float4 *o4 = reinterpret_cast<const float4 *>(Os) + gi * KPG;
-    float4 r[KPG];
-#pragma unroll
-    for (int k = 0; k < KPG; ++k) r[k] = row[k];
     float x0 = 0.f, x1 = 0.f;
 #pragma unroll
     for (int k = 0; k < KPG; ++k) {
@@ -110,21 +133,18 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeParams p, const f
   }
   if (gi != 0) return;
 
-  // BF16 segment partials of this head, then the final merge
-  const float *bml = reinterpret_cast<const float *>(p.ws + p.L.bf_ml) + bh * kBf16Splits * 2;
-  const float *bo = reinterpret_cast<const float *>(p.ws + p.L.bf_o) + bh * kBf16Splits * D + c;
+  // ---- merge with the BF16 segment ----
   float mb = -INFINITY;
 #pragma unroll
-  for (int s2 = 0; s2 < kBf16Splits; ++s2) mb = fmaxf(mb, bml[2 * s2]);
+  for (int s2 = 0; s2 < kBf16Splits; ++s2) mb = fmaxf(mb, bm[s2]);
   float lb = 0.f, obv = 0.f;
   if (mb != -INFINITY) {
 #pragma unroll
     for (int s2 = 0; s2 < kBf16Splits; ++s2) {
-      const float ms = bml[2 * s2];
-      if (ms == -INFINITY) continue;
-      const float a = exp2f(ms - mb);
-      lb = fmaf(bml[2 * s2 + 1], a, lb);
-      obv = fmaf(bo[(size_t)s2 * D], a, obv);
+      if (bm[s2] == -INFINITY) continue;
+      const float a = exp2f(bm[s2] - mb);
+      lb = fmaf(bl[s2], a, lb);
+      obv = fmaf(bov[s2], a, obv);
     }
   }
   const float M = ML[0], L = ML[1];
