@@ -202,85 +202,101 @@ def step_alg_bytes(wl, hl_row, bl_row, splits):
 # CPU baseline: the oracle, timed on this host
 # --------------------------------------------------------------------------
 
-def cpu_baseline(st, first_out, budget_s=12.0, max_seqs=4, log=print):
-    """Time the CPU oracle on the first decode step of a few sequences: unpack
-    every INT2 page record of the sequence, dequantise, quantise the demoted
-    token, and attend all q heads over the split cache.  The oracle's records
-    come from its own quantisation of the generated tokens.  Returns the
-    baseline dict and the oracle-vs-GPU error of the sampled sequences."""
+def oracle_step0(st, b, timed=True):
+    """The oracle's view of sequence b after the first decode step: it quantises
+    the sequence's history from the generated BF16 tokens and encodes its own
+    page records (set-up), then - the part that is timed - unpacks and
+    dequantises every record, quantises the demoted token and attends all q
+    heads over the split cache.  Returns (out [Hq][D], lse [Hq], records
+    {kv_head: [pages] uint8 records}, seconds timed, KV-token-heads)."""
     import torch
     from oracle import oscar_oracle as orc
 
+    wl, gen = st.wl, st.gen
+    D, G, Hkv, g = wl.D, wl.G, wl.Hkv, wl.g
+    ppb = synth.LargeGen.PAGES_PER_BLOCK
+    knew0, vnew0, q0 = gen.step_tokens(0)
+    hl0 = int(gen.hist_len0[b])
+    npg = -(-hl0 // PAGE)
+    us = gen.unique_of[b, :npg]
+    blocks = {}
+    kh = np.empty((npg * PAGE, Hkv, D), np.uint16)
+    vh = np.empty_like(kh)
+    for i, u in enumerate(us):
+        blk = int(u) // ppb
+        if blk not in blocks:
+            blocks.clear()
+            k, v = gen.history_block(blk)
+            blocks[blk] = (k.view(torch.int16).cpu().numpy().view(np.uint16),
+                           v.view(torch.int16).cpu().numpy().view(np.uint16))
+        k, v = blocks[blk]
+        o = (int(u) % ppb) * PAGE
+        kh[i * PAGE:(i + 1) * PAGE] = k[o:o + PAGE]
+        vh[i * PAGE:(i + 1) * PAGE] = v[o:o + PAGE]
+    kh, vh = kh[:hl0], vh[:hl0]
+    kb, vb = gen.bf16_tokens(b)
+    kb = kb.view(torch.int16).cpu().numpy().view(np.uint16)
+    vb = vb.view(torch.int16).cpu().numpy().view(np.uint16)
+    # after step 0: token 64 (the oldest recent) is demoted, the new token appended
+    dem_k, dem_v = kb[SINK], vb[SINK]
+    u16 = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    bf_k = np.concatenate([kb[:SINK], kb[SINK + 1:], u16(knew0[b:b + 1])])
+    bf_v = np.concatenate([vb[:SINK], vb[SINK + 1:], u16(vnew0[b:b + 1])])
+    q = synth.bf16_bits_to_f64(u16(q0[b]))
+    out_ref = np.zeros((wl.Hq, D))
+    lse_ref = np.zeros(wl.Hq)
+    records = {}
+    spent = 0.0
+    for j in range(Hkv):
+        K = synth.bf16_bits_to_f64(kh[:, j])
+        V = synth.bf16_bits_to_f64(vh[:, j])
+        kc, ks, kz = orc.quantize_tokens(K, gen.R_k[j], G, float(gen.clip_k[j]))
+        vc, vs, vz = orc.quantize_tokens(V, gen.R_v[j], G, float(gen.clip_v[j]))
+        recs = []
+        for pg in range(npg):
+            a_, e_ = pg * PAGE, min(hl0, pg * PAGE + PAGE)
+            pad = lambda x, w: np.concatenate([x[a_:e_], np.zeros((PAGE - (e_ - a_), w), x.dtype)])
+            recs.append(orc.encode_record(pad(kc, D), pad(ks, D // G), pad(kz, D // G),
+                                          pad(vc, D), pad(vs, D // G), pad(vz, D // G), D, G))
+        records[j] = recs
+        heads = [h for h in range(wl.Hq) if h // g == j]
+        t0 = time.perf_counter()
+        dk = orc.quantize_tokens(synth.bf16_bits_to_f64(dem_k[j])[None], gen.R_k[j], G, float(gen.clip_k[j]))
+        dv = orc.quantize_tokens(synth.bf16_bits_to_f64(dem_v[j])[None], gen.R_v[j], G, float(gen.clip_v[j]))
+        parts = [orc.decode_record(r, D, G) for r in recs]
+        khat = np.concatenate([orc.dequant(p_[0], p_[1], p_[2], G) for p_ in parts])[:hl0]
+        vhat = np.concatenate([orc.dequant(p_[3], p_[4], p_[5], G) for p_ in parts])[:hl0]
+        khat = np.concatenate([khat, orc.dequant(*dk, G)])
+        vhat = np.concatenate([vhat, orc.dequant(*dv, G)])
+        o, l = orc.decode_attention(q[heads], np.zeros(len(heads), int),
+                                    synth.bf16_bits_to_f64(bf_k[:, j])[:, None],
+                                    synth.bf16_bits_to_f64(bf_v[:, j])[:, None],
+                                    khat[:, None], vhat[:, None], gen.R_k[j:j + 1], gen.R_v[j:j + 1])
+        spent += time.perf_counter() - t0
+        out_ref[heads] = o
+        lse_ref[heads] = l
+    return out_ref, lse_ref, records, spent, (hl0 + 1 + SINK + RECENT) * Hkv
+
+
+def cpu_baseline(st, first_out, budget_s=12.0, max_seqs=4, log=print):
+    """Time the CPU oracle on the first decode step of a few sequences (see
+    oracle_step0: the timed part unpacks and dequantises every INT2 record,
+    quantises the demoted token and attends all q heads over the split cache).
+    Returns the baseline dict and the oracle-vs-GPU error of the sampled
+    sequences."""
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
-    wl, gen = st.wl, st.gen
-    D, G, Hkv, g = wl.D, wl.G, wl.Hkv, wl.g
-    ppb = synth.LargeGen.PAGES_PER_BLOCK
-    knew0, vnew0, q0 = gen.step_tokens(0)
-    timed, units, worst = 0.0, 0, 0.0
-    seqs = 0
+    wl = st.wl
+    timed, units, worst, seqs = 0.0, 0, 0.0, 0
     for b in range(wl.B):
         if seqs >= max_seqs or (seqs > 0 and timed >= budget_s):
             break
-        hl0 = int(gen.hist_len0[b])
-        npg = -(-hl0 // PAGE)
-        us = gen.unique_of[b, :npg]
-        blocks = {}
-        kh = np.empty((npg * PAGE, Hkv, D), np.uint16)
-        vh = np.empty_like(kh)
-        for i, u in enumerate(us):
-            blk = int(u) // ppb
-            if blk not in blocks:
-                blocks.clear()
-                k, v = gen.history_block(blk)
-                blocks[blk] = (k.view(torch.int16).cpu().numpy().view(np.uint16),
-                               v.view(torch.int16).cpu().numpy().view(np.uint16))
-            k, v = blocks[blk]
-            o = (int(u) % ppb) * PAGE
-            kh[i * PAGE:(i + 1) * PAGE] = k[o:o + PAGE]
-            vh[i * PAGE:(i + 1) * PAGE] = v[o:o + PAGE]
-        kh, vh = kh[:hl0], vh[:hl0]
-        kb, vb = gen.bf16_tokens(b)
-        kb = kb.view(torch.int16).cpu().numpy().view(np.uint16)
-        vb = vb.view(torch.int16).cpu().numpy().view(np.uint16)
-        # after step 0: token 64 (oldest recent) is demoted, the new token appended
-        dem_k, dem_v = kb[SINK], vb[SINK]
-        bf_k = np.concatenate([kb[:SINK], kb[SINK + 1:], knew0[b:b + 1].view(torch.int16).cpu().numpy().view(np.uint16)])
-        bf_v = np.concatenate([vb[:SINK], vb[SINK + 1:], vnew0[b:b + 1].view(torch.int16).cpu().numpy().view(np.uint16)])
-        q = synth.bf16_bits_to_f64(q0[b].view(torch.int16).cpu().numpy().view(np.uint16))
-        out_ref = np.zeros((wl.Hq, D))
-        for j in range(Hkv):
-            # oracle-side cache: records of its own quantisation (setup, untimed)
-            K = synth.bf16_bits_to_f64(kh[:, j])
-            V = synth.bf16_bits_to_f64(vh[:, j])
-            kc, ks, kz = orc.quantize_tokens(K, gen.R_k[j], G, float(gen.clip_k[j]))
-            vc, vs, vz = orc.quantize_tokens(V, gen.R_v[j], G, float(gen.clip_v[j]))
-            recs = []
-            for p in range(npg):
-                a, e = p * PAGE, min(hl0, p * PAGE + PAGE)
-                pad = lambda x, w: np.concatenate([x[a:e], np.zeros((PAGE - (e - a), w), x.dtype)])
-                recs.append(orc.encode_record(pad(kc, D), pad(ks, D // G), pad(kz, D // G),
-                                              pad(vc, D), pad(vs, D // G), pad(vz, D // G), D, G))
-            heads = [h for h in range(wl.Hq) if h // g == j]
-            t0 = time.perf_counter()
-            # --- timed: one decode step of this (sequence, KV head) ---
-            dk = orc.quantize_tokens(synth.bf16_bits_to_f64(dem_k[j])[None], gen.R_k[j], G, float(gen.clip_k[j]))
-            dv = orc.quantize_tokens(synth.bf16_bits_to_f64(dem_v[j])[None], gen.R_v[j], G, float(gen.clip_v[j]))
-            parts = [orc.decode_record(r, D, G) for r in recs]
-            khat = np.concatenate([orc.dequant(p_[0], p_[1], p_[2], G) for p_ in parts])[:hl0]
-            vhat = np.concatenate([orc.dequant(p_[3], p_[4], p_[5], G) for p_ in parts])[:hl0]
-            khat = np.concatenate([khat, orc.dequant(*dk, G)])
-            vhat = np.concatenate([vhat, orc.dequant(*dv, G)])
-            o, _ = orc.decode_attention(q[heads], np.zeros(len(heads), int),
-                                        synth.bf16_bits_to_f64(bf_k[:, j])[:, None],
-                                        synth.bf16_bits_to_f64(bf_v[:, j])[:, None],
-                                        khat[:, None], vhat[:, None], gen.R_k[j:j + 1], gen.R_v[j:j + 1])
-            timed += time.perf_counter() - t0
-            out_ref[heads] = o
-        units += (hl0 + 1 + SINK + RECENT) * Hkv
+        out_ref, _, _, spent, u = oracle_step0(st, b)
+        timed += spent
+        units += u
         seqs += 1
         if first_out is not None:
             got = first_out[0][b].astype(np.float64)
@@ -288,7 +304,7 @@ def cpu_baseline(st, first_out, budget_s=12.0, max_seqs=4, log=print):
             worst = max(worst, float((np.abs(got - out_ref).max(axis=1) / den).max()))
         log(f"[bench] cpu oracle: sequence {b} done, {timed:.1f}s timed so far")
     return dict(value=units / timed, unit="KV-token-heads/s", cores=int(blas_threads), kind="oracle",
-                sample=f"first decode step of {seqs} of {wl.B} sequences (all {Hkv} KV heads, "
+                sample=f"first decode step of {seqs} of {wl.B} sequences (all {wl.Hkv} KV heads, "
                        f"{wl.Hq} q heads): unpack + dequantise every INT2 record, quantise the "
                        f"demoted token, fp64 attention; {timed:.1f}s timed",
                 seconds=timed), worst

@@ -1,0 +1,118 @@
+"""GPU parity at full size: the large caches (the batch-32 Qwen3-8B-shaped cache
+at ~96K context that bench.py measures, a single 102400-token sequence, and the
+Qwen3-32B-shaped shared-prefix batch), built and run in the configuration
+bench.py times (automatic kernel choice and chunking), one decode step.
+Checked against the oracle on sampled outputs:
+
+* every q head of the first and the last sequence: outputs within 2e-3 row
+  relative error, lse within 1e-3 (the oracle quantises the sequence's
+  history from the same generated tokens, in fp64, and attends it);
+* the bytes of 48 sampled history pages of those sequences (all KV heads)
+  equal the oracle's encoded records."""
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+PAGE, SINK = 16, 64
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _u16(t):
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _history_tokens(gen, b, hl0):
+    """BF16 history tokens [hl0][Hkv][D] of sequence b as generated."""
+    ppb = synth.LargeGen.PAGES_PER_BLOCK
+    npg = -(-hl0 // PAGE)
+    us = gen.unique_of[b, :npg]
+    kh = np.empty((npg * PAGE, gen.wl.Hkv, gen.wl.D), np.uint16)
+    vh = np.empty_like(kh)
+    cur, kv = -1, None
+    for i, u in enumerate(us):
+        blk = int(u) // ppb
+        if blk != cur:
+            k, v = gen.history_block(blk)
+            kv, cur = (_u16(k), _u16(v)), blk
+        o = (int(u) % ppb) * PAGE
+        kh[i * PAGE:(i + 1) * PAGE] = kv[0][o:o + PAGE]
+        vh[i * PAGE:(i + 1) * PAGE] = kv[1][o:o + PAGE]
+    return kh[:hl0], vh[:hl0]
+
+
+def _check_sequence(st, first_out, pool, b, rng):
+    from oracle import oscar_oracle as orc
+    wl, gen = st.wl, st.gen
+    D, G, Hkv, g = wl.D, wl.G, wl.Hkv, wl.g
+    hl0 = int(gen.hist_len0[b])
+    npg = -(-hl0 // PAGE)
+    kh, vh = _history_tokens(gen, b, hl0)
+    kb, vb = gen.bf16_tokens(b)
+    kb, vb = _u16(kb), _u16(vb)
+    knew, vnew, q0 = gen.step_tokens(0)
+    # step 0: the oldest recent token (position 64) is demoted, the new token appended
+    bf_k = np.concatenate([kb[:SINK], kb[SINK + 1:], _u16(knew[b:b + 1])])
+    bf_v = np.concatenate([vb[:SINK], vb[SINK + 1:], _u16(vnew[b:b + 1])])
+    hist_k = np.concatenate([kh, kb[SINK:SINK + 1]])
+    hist_v = np.concatenate([vh, vb[SINK:SINK + 1]])
+    q = synth.bf16_bits_to_f64(_u16(q0[b]))
+    sample = np.sort(rng.choice(npg - 1, size=min(48, npg - 1), replace=False))   # full prompt pages
+    phys = st.gen.hist_table[b, sample]
+    out_ref = np.zeros((wl.Hq, D))
+    lse_ref = np.zeros(wl.Hq)
+    for j in range(Hkv):
+        K = synth.bf16_bits_to_f64(hist_k[:, j])
+        V = synth.bf16_bits_to_f64(hist_v[:, j])
+        kc, ks, kz = orc.quantize_tokens(K, gen.R_k[j], G, float(gen.clip_k[j]))
+        vc, vs, vz = orc.quantize_tokens(V, gen.R_v[j], G, float(gen.clip_v[j]))
+        for pg, ph in zip(sample, phys):
+            sl = slice(pg * PAGE, (pg + 1) * PAGE)
+            want = orc.encode_record(kc[sl], ks[sl], kz[sl], vc[sl], vs[sl], vz[sl], D, G)
+            got = pool[ph, j]
+            assert np.array_equal(got, want), f"seq {b} page {pg} (physical {ph}) head {j}: bytes differ"
+        heads = [h for h in range(wl.Hq) if h // g == j]
+        o, l = orc.decode_attention(q[heads], np.zeros(len(heads), int),
+                                    synth.bf16_bits_to_f64(bf_k[:, j])[:, None],
+                                    synth.bf16_bits_to_f64(bf_v[:, j])[:, None],
+                                    orc.dequant(kc, ks, kz, G)[:, None], orc.dequant(vc, vs, vz, G)[:, None],
+                                    gen.R_k[j:j + 1], gen.R_v[j:j + 1])
+        out_ref[heads], lse_ref[heads] = o, l
+    got = first_out[0][b].astype(np.float64)
+    den = np.maximum(np.abs(out_ref).max(axis=1), 1e-30)
+    err = np.abs(got - out_ref).max(axis=1) / den
+    assert np.all(err <= TOL), f"seq {b}: row errors {np.sort(err)[-4:]}"
+    lerr = np.abs(first_out[1][b] - lse_ref).max()
+    assert lerr < 1e-3, f"seq {b}: lse error {lerr}"
+    return float(err.max())
+
+
+@pytest.mark.parametrize("workload", ["qwen3-8b-b32-100k", "qwen3-8b-100k-b1", "qwen3-32b-b16-128k"])
+def test_full_size_sampled(workload):
+    """Batch-32 ~96K (the benchmark workload), one 102400-token sequence, and
+    the Qwen3-32B-shaped batch 16 x 131072 with a shared 32768-token prefix
+    (8 q heads per KV head, group 128)."""
+    import bench
+    from int2_rotated_kv_amd import binding as ob
+    t0 = time.time()
+    _say(f"case: {workload}, one decode step (bench configuration)")
+    st = bench.build_workload(workload, 1, log=_say)
+    r = bench.run_steps(st, 0, 1, ob.INT2_AUTO, keep_first_out=True)
+    plan = ob.decode_plan(st.sc.cache, r["args"][0])
+    _say(f"step done: chunks {plan[0]}, kernel {plan[3]}, {time.time() - t0:.1f}s")
+    pool = st.sc.cache.int2.cpu().numpy()
+    rng = np.random.default_rng(0)
+    for b in sorted({0, st.wl.B - 1}):
+        w = _check_sequence(st, r["first_out"], pool, b, rng)
+        _say(f"sequence {b}: bytes of sampled pages exact, worst row rel err {w:.3e} "
+             f"({time.time() - t0:.1f}s)")
