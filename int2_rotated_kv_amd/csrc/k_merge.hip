@@ -11,129 +11,174 @@
 
 namespace oscar {
 
-constexpr int kMergeThreads = 256;
-constexpr int kMergeRegChunks = 8;       // chunk outputs per thread loaded up front
+constexpr int kMergeRegChunks = 8;       // chunk rows per thread loaded up front
 
-// One block (4 waves) per (sequence, q head).  Every load the block needs is
-// issued first (chunk maxima and sums, the first chunk outputs of each thread,
-// its slice of the R_v row, the BF16 partials), so the block waits for memory
-// about once; the rest is LDS exchanges.  Thread (group gi, channel c) sums
-// chunks gi, gi + NGR, ... for channel c and multiplies the slice gi of the
-// R_v row c.
-template <int D>
-__global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeParams p, const float *__restrict__ Rv,
-                                                         float *__restrict__ out, float *__restrict__ lse) {
-  constexpr int NGR = kMergeThreads / D;         // thread groups (2 or 4)
-  constexpr int KPG = D / NGR / 4;               // float4 of an R_v row per group
+// Sum of RPT values per lane across the LPR lanes of a row group, folded so
+// that every exchange also halves the number of values: after log2(LPR) steps
+// lane l holds the full sum of value number `base`, with RPT <= LPR.
+template <int CNT, int O>
+__device__ __forceinline__ void fold_sum(float *v, int lane, int &base) {
+  if constexpr (O >= 1) {
+    if constexpr (CNT > 1) {
+      constexpr int H = CNT / 2;
+      const bool up = (lane & O) != 0;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float send = up ? v[i] : v[i + H];
+        const float keep = up ? v[i + H] : v[i];
+        v[i] = keep + __shfl_xor(send, O);
+      }
+      if (up) base += H;
+      fold_sum<H, O / 2>(v, lane, base);
+    } else {
+      v[0] += __shfl_xor(v[0], O);
+      fold_sum<1, O / 2>(v, lane, base);
+    }
+  }
+}
+
+// One block of NT threads per (sequence, q head).  A row of D floats (a chunk
+// output, a row of R_v) is read by D/4 consecutive lanes, 16 bytes each, so
+// every load is a contiguous row segment.  Every load the block needs is
+// issued first: the chunk (m, l) pairs (thread s holds chunk s), the first
+// kMergeRegChunks chunk rows of each row group, the thread's float4 of RPT
+// rows of R_v and the BF16 partials; the rest is shuffles and LDS exchanges.
+// NT = 1024 serves long chunk lists (a few sequences split many ways), 256
+// the rest.
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void k_merge(DecodeParams p, const float *__restrict__ Rv,
+                                              float *__restrict__ out, float *__restrict__ lse) {
+  constexpr int LPR = D / 4;                   // lanes per row (float4 each)
+  constexpr int RG = NT / LPR;                 // row groups
+  constexpr int NW = NT / 64;                  // waves
+  constexpr int RPT = D / RG;                  // R_v rows per thread
+  static_assert(RPT >= 1 && RPT <= LPR && (RPT & (RPT - 1)) == 0, "R_v row split");
   const size_t bh = blockIdx.x;
   const int j = p.kv_of_q[bh % p.Hq];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int c = tid % D, gi = tid / D;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int cq = tid % LPR, rg = tid / LPR;
   const int S = p.splits;
-  extern __shared__ float a_s[];                 // [S] chunk weights 2^(m_s - M)
-  __shared__ __align__(16) float Os[D];          // merged history output (rotated basis)
-  __shared__ float red[NGR][D];
-  __shared__ float ML[2];
+  extern __shared__ float a_s[];               // [S] chunk weights 2^(m_s - M)
+  __shared__ float4 red[NW][LPR];              // per-wave channel sums
+  __shared__ __align__(16) float Os[D];        // merged history output (rotated basis)
+  __shared__ float OH[D];                      // un-rotated history output
+  __shared__ float wred[2][NW];
 
-  const float *ml = reinterpret_cast<const float *>(p.ws + p.L.part_ml) + bh * S * 2;
-  const float *po = reinterpret_cast<const float *>(p.ws + p.L.part_o) + bh * S * D;
+  const float2 *ml = reinterpret_cast<const float2 *>(p.ws + p.L.part_ml) + bh * S;
+  const float4 *po = reinterpret_cast<const float4 *>(p.ws + p.L.part_o) + bh * S * LPR + cq;
   const float *bml = reinterpret_cast<const float *>(p.ws + p.L.bf_ml) + bh * kBf16Splits * 2;
-  const float *bo = reinterpret_cast<const float *>(p.ws + p.L.bf_o) + bh * kBf16Splits * D + c;
+  const float *bo = reinterpret_cast<const float *>(p.ws + p.L.bf_o) + bh * kBf16Splits * D + tid;
 
   // ---- every load up front ----
-  float ov[kMergeRegChunks];                     // chunk outputs gi + NGR*k, channel c
+  float2 mlv = make_float2(-INFINITY, 0.f);
+  if (tid < S) mlv = ml[tid];
+  float4 ov[kMergeRegChunks];                  // chunk rows rg + RG*k, channels 4cq..4cq+3
 #pragma unroll
   for (int k = 0; k < kMergeRegChunks; ++k) {
-    const int s2 = gi + NGR * k;
-    ov[k] = s2 < S ? po[(size_t)s2 * D + c] : 0.f;
+    const int s2 = rg + RG * k;
+    ov[k] = s2 < S ? po[(size_t)s2 * LPR] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  float4 r[KPG];
+  float4 r[RPT];                               // R_v[j] rows rg + RG*i, columns 4cq..4cq+3
   if (Rv != nullptr) {
-    const float4 *row = reinterpret_cast<const float4 *>(Rv + ((size_t)j * D + c) * D) + gi * KPG;
+    const float4 *rrow = reinterpret_cast<const float4 *>(Rv + (size_t)j * D * D) + cq;
 #pragma unroll
-    for (int k = 0; k < KPG; ++k) r[k] = row[k];
+    for (int i = 0; i < RPT; ++i) r[i] = rrow[(size_t)(rg + RG * i) * LPR];
   }
   float bm[kBf16Splits], bl[kBf16Splits], bov[kBf16Splits];
 #pragma unroll
   for (int s2 = 0; s2 < kBf16Splits; ++s2) {
     bm[s2] = bml[2 * s2];
     bl[s2] = bml[2 * s2 + 1];
-    bov[s2] = gi == 0 ? bo[(size_t)s2 * D] : 0.f;
-  }
-  float mv = -INFINITY, lv = 0.f;                // wave 0: chunk lane
-  if (tid < 64 && lane < S) {
-    mv = ml[2 * lane];
-    lv = ml[2 * lane + 1];
+    bov[s2] = tid < D ? bo[(size_t)s2 * D] : 0.f;
   }
 
-  // ---- chunk weights (wave 0): M = max m_s, L = sum l_s 2^(m_s - M) ----
-  if (tid < 64) {
-    float M = mv;
-    for (int s2 = lane + 64; s2 < S; s2 += 64) M = fmaxf(M, ml[2 * s2]);
+  // ---- chunk weights: M = max m_s, L = sum l_s 2^(m_s - M) ----
+  float M = mlv.x;
+  for (int s2 = tid + NT; s2 < S; s2 += NT) M = fmaxf(M, ml[s2].x);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float L = 0.f;
-    for (int s2 = lane; s2 < S; s2 += 64) {
-      const float m = s2 == lane ? mv : ml[2 * s2];
-      const float l = s2 == lane ? lv : ml[2 * s2 + 1];
-      const float a = (m == -INFINITY) ? 0.f : exp2f(m - M);
-      a_s[s2] = a;
-      L = fmaf(l, a, L);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-    if (lane == 0) { ML[0] = M; ML[1] = L; }
-  }
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) wred[0][wv] = M;
   __syncthreads();
-
-  // ---- O[c] = sum_s a_s o_s[c]; a chunk with weight 0 (no tokens) adds 0
-  // whatever its stored output holds ----
-  {
-    float O0 = 0.f, O1 = 0.f;
+  M = wred[0][0];
 #pragma unroll
-    for (int k = 0; k < kMergeRegChunks; ++k) {
-      const int s2 = gi + NGR * k;
-      const float wgt = s2 < S ? a_s[s2] : 0.f;
-      float &O = (k & 1) ? O1 : O0;
-      O = fmaf(wgt, wgt != 0.f ? ov[k] : 0.f, O);
-    }
-    for (int s2 = gi + NGR * kMergeRegChunks; s2 < S; s2 += NGR) {
-      const float v = po[(size_t)s2 * D + c], wgt = a_s[s2];
-      O0 = fmaf(wgt, wgt != 0.f ? v : 0.f, O0);
-    }
-    red[gi][c] = O0 + O1;
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, wred[0][w]);
+  float L = 0.f;
+  for (int s2 = tid; s2 < S; s2 += NT) {
+    const float2 t = s2 == tid ? mlv : ml[s2];
+    const float a = (t.x == -INFINITY) ? 0.f : exp2f(t.x - M);
+    a_s[s2] = a;
+    L = fmaf(t.y, a, L);
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  if (lane == 0) wred[1][wv] = L;
+  __syncthreads();
+  L = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) L += wred[1][w];
+
+  // ---- O = sum_s a_s o_s; a chunk with weight 0 (no tokens) adds 0 whatever
+  // its stored output holds ----
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < kMergeRegChunks; ++k) {
+    const int s2 = rg + RG * k;
+    const float wgt = s2 < S ? a_s[s2] : 0.f;
+    if (wgt != 0.f) {
+      acc.x = fmaf(wgt, ov[k].x, acc.x);
+      acc.y = fmaf(wgt, ov[k].y, acc.y);
+      acc.z = fmaf(wgt, ov[k].z, acc.z);
+      acc.w = fmaf(wgt, ov[k].w, acc.w);
+    }
+  }
+  for (int s2 = rg + RG * kMergeRegChunks; s2 < S; s2 += RG) {
+    const float wgt = a_s[s2];
+    if (wgt != 0.f) {
+      const float4 v = po[(size_t)s2 * LPR];
+      acc.x = fmaf(wgt, v.x, acc.x);
+      acc.y = fmaf(wgt, v.y, acc.y);
+      acc.z = fmaf(wgt, v.z, acc.z);
+      acc.w = fmaf(wgt, v.w, acc.w);
+    }
+  }
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) {         // row groups inside the wave
+    acc.x += __shfl_xor(acc.x, o);
+    acc.y += __shfl_xor(acc.y, o);
+    acc.z += __shfl_xor(acc.z, o);
+    acc.w += __shfl_xor(acc.w, o);
+  }
+  if (lane < LPR) red[wv][lane] = acc;
   __syncthreads();
   if (tid < D) {
+    const float *rf = reinterpret_cast<const float *>(&red[0][0]);
     float O = 0.f;
 #pragma unroll
-    for (int g2 = 0; g2 < NGR; ++g2) O += red[g2][tid];
+    for (int w = 0; w < NW; ++w) O += rf[w * D + tid];
     Os[tid] = O;
   }
   __syncthreads();
 
   // ---- un-rotation O_hist[c] = sum_k O[k] R_v[j][c][k] ----
-  float oh;
+  float oh = 0.f;
   if (Rv != nullptr) {
-    const float4 *o4 = reinterpret_cast<const float4 *>(Os) + gi * KPG;
-    float x0 = 0.f, x1 = 0.f;
+    const float4 o4 = reinterpret_cast<const float4 *>(Os)[cq];
+    float v[RPT];
 #pragma unroll
-    for (int k = 0; k < KPG; ++k) {
-      const float4 o = o4[k];
-      float &x = (k & 1) ? x1 : x0;
-      x = fmaf(o.x, r[k].x, fmaf(o.y, r[k].y, fmaf(o.z, r[k].z, fmaf(o.w, r[k].w, x))));
-    }
-    red[gi][c] = x0 + x1;
+    for (int i = 0; i < RPT; ++i)
+      v[i] = fmaf(o4.x, r[i].x, fmaf(o4.y, r[i].y, fmaf(o4.z, r[i].z, o4.w * r[i].w)));
+    int base = 0;
+    fold_sum<RPT, LPR / 2>(v, lane, base);
+    OH[rg + RG * base] = v[0];                 // the lanes of one row agree
     __syncthreads();
-    oh = 0.f;
-#pragma unroll
-    for (int g2 = 0; g2 < NGR; ++g2) oh += red[g2][c];
-  } else {
-    oh = Os[c];
+    if (tid < D) oh = OH[tid];
+  } else if (tid < D) {
+    oh = Os[tid];
   }
-  if (gi != 0) return;
+  if (tid >= D) return;
 
   // ---- merge with the BF16 segment ----
+  const int c = tid;
   float mb = -INFINITY;
 #pragma unroll
   for (int s2 = 0; s2 < kBf16Splits; ++s2) mb = fmaxf(mb, bm[s2]);
@@ -147,7 +192,6 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeParams p, const f
       obv = fmaf(bov[s2], a, obv);
     }
   }
-  const float M = ML[0], L = ML[1];
   const float M2 = fmaxf(M, mb);
   if (M2 == -INFINITY) {
     out[bh * D + c] = 0.f;
@@ -161,12 +205,19 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecodeParams p, const f
   if (c == 0 && lse != nullptr) lse[bh] = M2 * kLn2 + logf(den);
 }
 
+template <int D>
+static void launch_merge_d(const DecodeParams &p, const float *Rv, float *out, float *lse,
+                           size_t lds, hipStream_t s) {
+  const dim3 grid(p.B * p.Hq);
+  if (p.splits > 64) hipLaunchKernelGGL((k_merge<D, 1024>), grid, dim3(1024), lds, s, p, Rv, out, lse);
+  else hipLaunchKernelGGL((k_merge<D, 256>), grid, dim3(256), lds, s, p, Rv, out, lse);
+}
+
 hipError_t launch_merge(const DecodeParams &p, const float *Rv, float *out, float *lse,
                         hipStream_t s) {
-  const dim3 grid(p.B * p.Hq), blk(kMergeThreads);
   const size_t lds = (size_t)(p.splits > 0 ? p.splits : 1) * sizeof(float);
-  if (p.D == 64) hipLaunchKernelGGL(k_merge<64>, grid, blk, lds, s, p, Rv, out, lse);
-  else hipLaunchKernelGGL(k_merge<128>, grid, blk, lds, s, p, Rv, out, lse);
+  if (p.D == 64) launch_merge_d<64>(p, Rv, out, lse, lds, s);
+  else launch_merge_d<128>(p, Rv, out, lse, lds, s);
   return hipGetLastError();
 }
 
