@@ -119,10 +119,20 @@ def step_args(st, s: int, int2_kernel: int, num_splits: int = 0):
                          int(st.hl_h[s].max()), int2_kernel=int2_kernel, num_splits=num_splits)
 
 
+def breakdown_steps(steps):
+    """Extra steps run after the timed ones with an event between phases."""
+    return min(steps, 20)
+
+
 def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0):
+    """Warmup steps, then `steps` timed steps through the plain entry points
+    (demote_pack, write_bf16, one decode_attn, merge) with nothing else on the
+    stream, then breakdown_steps(steps) more with events between the phases
+    (decode_attn split into its QROT|BF16 and INT2 phases)."""
     import torch
     from int2_rotated_kv_amd import binding as ob
-    T = steps + warmup
+    E = breakdown_steps(steps)
+    T = steps + warmup + E
     args = [step_args(st, s, int2_kernel, num_splits) for s in range(T)]
     a_qb = [a.with_phases(ob.PHASE_QROT | ob.PHASE_BF16) for a in args]
     a_i2 = [a.with_phases(ob.PHASE_INT2) for a in args]
@@ -130,21 +140,27 @@ def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0
     wl = st.wl
     out = torch.zeros((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=st.q.device)
     lse = torch.zeros((wl.B, wl.Hq), dtype=torch.float32, device=st.q.device)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(E)]
     first_out = None
     cache = st.sc.cache
 
-    def one(s, e=None):
-        if e: e[0].record()
+    def one(s):
         ob.demote_pack(cache, st.dsrc[s], st.ddst[s], st.Rk, st.Rv, st.ck, st.cv)
         ob.write_bf16(cache, st.wdst[s], st.knew[s], st.vnew[s])
-        if e: e[1].record()
-        ob.decode_attn(cache, a_qb[s], st.q[s], st.Rk, ws)
-        if e: e[2].record()
-        ob.decode_attn(cache, a_i2[s], st.q[s], st.Rk, ws)
-        if e: e[3].record()
+        ob.decode_attn(cache, args[s], st.q[s], st.Rk, ws)
         ob.merge(cache, args[s], ws, st.Rv, out, lse)
-        if e: e[4].record()
+
+    def one_phased(s, e):
+        e[0].record()
+        ob.demote_pack(cache, st.dsrc[s], st.ddst[s], st.Rk, st.Rv, st.ck, st.cv)
+        ob.write_bf16(cache, st.wdst[s], st.knew[s], st.vnew[s])
+        e[1].record()
+        ob.decode_attn(cache, a_qb[s], st.q[s], st.Rk, ws)
+        e[2].record()
+        ob.decode_attn(cache, a_i2[s], st.q[s], st.Rk, ws)
+        e[3].record()
+        ob.merge(cache, args[s], ws, st.Rv, out, lse)
+        e[4].record()
 
     for s in range(warmup):
         one(s)
@@ -154,10 +170,13 @@ def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        one(warmup + i, ev[i])
+        one(warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    seg = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in ev])  # ms
+    for i in range(E):
+        one_phased(warmup + steps + i, ev[i])
+    torch.cuda.synchronize()
+    seg = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in ev]).reshape(E, 4)  # ms
     # the INT2 kernel alone: back-to-back launches of the last step's INT2 phase
     # (it only rewrites the workspace partials) between two events on the
     # stream it is launched on
@@ -371,7 +390,7 @@ def main(argv=None):
         return
     kern = {"auto": ob.INT2_AUTO, "valu": ob.INT2_VALU, "mfma": ob.INT2_MFMA}[a.int2_kernel]
     torch.cuda.set_device(0)
-    st = build_workload(a.workload, a.steps + a.warmup, log=log)
+    st = build_workload(a.workload, a.steps + a.warmup + breakdown_steps(a.steps), log=log)
     wl = st.wl
     r = run_steps(st, a.steps, a.warmup, kern, keep_first_out=not a.no_cpu_baseline,
                   num_splits=a.splits)

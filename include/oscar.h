@@ -123,7 +123,7 @@ typedef struct {
                                 grid without a device-to-host read               */
   float sm_scale;            /* softmax scale; 0 means 1/sqrt(D)                */
   int32_t num_splits;        /* history chunks per (sequence, KV head); 0 = auto;
-                                at most 1024 are used                          */
+                                at most min(1024, history pages) are used       */
   int32_t int2_kernel;       /* OSCAR_INT2_AUTO / _VALU / _MFMA                  */
   uint32_t phases;           /* oscar_decode_attn work: OR of OSCAR_PHASE_*; 0 means
                                 all.  Phases may be issued in separate calls (e.g.
@@ -179,15 +179,18 @@ int oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_ar
  * arguments (host only): num_splits chunks of pages_per_split pages per
  * (sequence, KV head), the workspace size, and the INT2 kernel that runs
  * (OSCAR_INT2_VALU or OSCAR_INT2_MFMA, AUTO resolved).  Any output may be NULL.
- * Automatic chunking (num_splits == 0) aims at 4096 (MFMA kernel) or 2048
- * (VALU kernel) (sequence, KV head, chunk) units while keeping every chunk at
- * least 8x the bytes of its partial result and 16 pages long.  The VALU kernel
- * gives chunk c pages [c*pages_per_split, (c+1)*pages_per_split) and drops
- * empty chunks.  The MFMA kernel rounds the chunk count up to a multiple of 8:
- * each group of 8 chunks is one block of 8 waves that takes the pages of one
- * equal part of the history in batches from a shared counter, so which pages a
- * chunk partial covers depends on timing (the merged result does not, up to
- * fp32 rounding order) and pages_per_split is nominal.
+ * VALU kernel: automatic chunking (num_splits == 0) aims at 2048 (sequence,
+ * KV head, chunk) units while keeping every chunk at least 8x the bytes of its
+ * partial result and 16 pages long; chunk c covers pages
+ * [c*pages_per_split, (c+1)*pages_per_split) and empty chunks are dropped.
+ * MFMA kernel: a chunk is one of num_splits equal parts of each sequence's
+ * history.  One block of 16 waves serves one part for a group of up to 8 KV
+ * heads; the waves of a head take its pages in batches from a shared counter
+ * and their results are combined into one partial per (q head, part).
+ * Automatic chunking aims at 256 blocks (one per compute unit) while keeping
+ * every part at least 4x its partial bytes and 16 pages per head;
+ * pages_per_split is nominal.  An explicit num_splits is capped at the page
+ * count and at 1024.
  */
 int oscar_decode_plan(const oscar_cache *cache, const oscar_decode_args *args,
                       int32_t *num_splits, int32_t *pages_per_split, size_t *workspace_bytes,

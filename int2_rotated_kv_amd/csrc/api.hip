@@ -11,7 +11,6 @@
 #include "common.hpp"
 
 namespace oscar {
-static_assert(kMaxSplits % kMfmaWaves == 0, "chunk cap must be a multiple of the MFMA waves per head");
 namespace {
 
 thread_local std::string g_err;
@@ -139,25 +138,27 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
                 "matrix-core INT2 kernel needs 4 or 8 q heads per KV head (got %d)", p->g);
   p->int2_kind = kind;
 
-  // history split: enough waves to fill the chip once (the vector-ALU kernel
-  // runs 4 waves per (sequence, KV head, chunk), the matrix-core one 1), while
-  // each chunk streams at least 8x the bytes of its partial result (read and
-  // written once more by the merge) and 16 pages.  The matrix-core kernel runs
-  // blocks of kMfmaWaves waves over up to 8 KV heads of one sequence, the waves
-  // of a head sharing the pages of one part of its history, so its chunk count
-  // is a multiple of the waves per head; its pages_per_split is nominal.
+  // history split.  Vector-ALU kernel: enough waves to fill the chip once (4
+  // waves per (sequence, KV head, chunk)), each chunk streaming at least 8x
+  // the bytes of its partial result (read and written once more by the merge)
+  // and 16 pages.  Matrix-core kernel: one block of kMfmaWaves waves per
+  // (sequence, group of up to 8 KV heads, part), the group's waves combining
+  // their results into one partial per (q head, part); enough parts for one
+  // block per compute unit, each part at least 4x its partial bytes and 16
+  // pages per head; its pages_per_split is nominal.
   const int npages = need_hist;
   int S = 1;
   if (npages > 0) {
     if (a->num_splits > 0) {
-      S = a->num_splits;
-      if (kind != OSCAR_INT2_MFMA && S > npages) S = npages;
+      S = a->num_splits > npages ? npages : a->num_splits;
     } else {
-      const int units = a->batch * c->num_kv_heads;
-      const int target = kind == OSCAR_INT2_MFMA ? 4096 : 2048;
+      const bool mf = kind == OSCAR_INT2_MFMA;
+      const int hg = mfma_heads_per_block(c->num_kv_heads);
+      const int units = mf ? a->batch * ((c->num_kv_heads + hg - 1) / hg) : a->batch * c->num_kv_heads;
+      const int target = mf ? kMfmaTargetBlocks : 2048;
       const double rec = (double)RecLayout(p->D, p->G).bytes();
       const double part_bytes = 2.0 * p->g * (p->D + 2) * 4.0;   // write + read back
-      int min_pages = (int)std::ceil(8.0 * part_bytes / rec);
+      int min_pages = (int)std::ceil((mf ? 4.0 : 8.0) * part_bytes / rec);
       min_pages = min_pages < 16 ? 16 : min_pages;
       int s_fill = (target + units - 1) / units;
       int s_cap = npages / min_pages;
@@ -166,10 +167,6 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
     }
   }
   S = S > kMaxSplits ? kMaxSplits : S;
-  if (kind == OSCAR_INT2_MFMA) {
-    const int wh = kMfmaWaves / mfma_heads_per_block(c->num_kv_heads);   // waves per head
-    S = (S + wh - 1) / wh * wh;
-  }
   const int pps = npages > 0 ? (npages + S - 1) / S : 0;
   if (npages > 0 && kind != OSCAR_INT2_MFMA) S = (npages + pps - 1) / pps;
   p->splits = S;

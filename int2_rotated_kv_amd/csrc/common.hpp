@@ -17,6 +17,7 @@ constexpr int kMaxSplits = 1024;        // history chunks per (sequence, KV head
 #define OSCAR_INT2_WAVES 16
 #endif
 constexpr int kMfmaWaves = OSCAR_INT2_WAVES;   // matrix-core INT2 kernel: waves per block
+constexpr int kMfmaTargetBlocks = 256;          // its default grid: one block per compute unit
 // KV heads per block of the matrix-core INT2 kernel: Hkv rounded up to a power
 // of two, at most 8; the block's waves are split evenly over them
 __host__ __device__ constexpr int mfma_heads_per_block(int hkv) {

@@ -150,11 +150,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave (uniform)
   // block = (sequence, group of HG KV heads, part of the history); WH waves
-  // per head, each one chunk with its own partial
+  // per head share the part's pages and their results are combined into one
+  // partial per (q head, part)
   const int HG = mfma_heads_per_block(p.Hkv);
   const int WH = HB / HG;
-  const int S = p.splits;                         // WH waves x P parts per (sequence, KV head)
-  const int P = S / WH;
+  const int P = p.splits;                         // parts per (sequence, KV head)
   const int ngrp = (p.Hkv + HG - 1) / HG;
   const int part = blockIdx.x % P;
   const int hg = (blockIdx.x / P) % ngrp;
@@ -166,15 +166,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   const int wq = w >> 2;                          // issue slot of this wave
   const int wpos = (HG == 8 && (wq == 2 || wq == 3)) ? (w ^ 4) : w;
   const int jl = wpos % HG;                       // head within the group
-  const int j = hg * HG + jl;                     // this wave's KV head
-  const int split = part * WH + wpos / HG;        // this wave's partial
+  const bool live = hg * HG + jl < p.Hkv;         // a last group may be short
+  const int j = live ? hg * HG + jl : 0;          // this wave's KV head
   const int r16 = lane & 15, kb = lane >> 4;      // row-in-16 and lane group
   __shared__ int batch_ctr[8];                    // per head: next batch of the part
   if (threadIdx.x < 8) batch_ctr[threadIdx.x] = 0;
-  __syncthreads();                                // the only block-level barrier
-  if (j >= p.Hkv) return;
+  __syncthreads();
 
-  int hl = p.hist_len[b];
+  int hl = live ? p.hist_len[b] : 0;
   hl = hl < 0 ? 0 : hl;
   hl = hl > p.max_hist_len ? p.max_hist_len : hl;
   hl = hl > kPage * p.hist_stride ? kPage * p.hist_stride : hl;
@@ -539,9 +538,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     bcur = bnext;
   }
 
-  // ---------------- epilogue: this wave's chunk partial ----------------
-  float *po = reinterpret_cast<float *>(p.ws + p.L.part_o);
-  float *pml = reinterpret_cast<float *>(p.ws + p.L.part_ml);
+  // ---------------- epilogue: one partial per (q head, part) ----------------
+  // each wave leaves its unnormalised output and (max, sum) per head in LDS
+  // (its own query slot, no longer read), then the block combines the WH waves
+  // of every head:  M = max m_w, L = sum L_w 2^(m_w - M), O = sum O_w 2^(m_w - M)
+  __shared__ float mlw[HB][GQ][2];
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
     // head 4*qd + kb's sums over its 16 token lanes
@@ -550,15 +551,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
     for (int g2 = 0; g2 < NG; ++g2) Z[g2] = row_sum(zacc[qd][g2]);
     if (r16 == 0) {
-      const size_t row = ((size_t)b * p.Hq + p.q_of_kv[j * GQ + qd * 4 + kb]) * S + split;
-      pml[row * 2 + 0] = m_run[qd];
-      pml[row * 2 + 1] = L;
+      mlw[w][qd * 4 + kb][0] = m_run[qd];
+      mlw[w][qd * 4 + kb][1] = L;
     }
     // accumulator element i: head 4*qd + i, channel lane + 64*h2; the zero-point
     // and offset part of head 4*qd + i is uniform over lanes 16*i ..
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const size_t row = ((size_t)b * p.Hq + p.q_of_kv[j * GQ + qd * 4 + i]) * S + split;
 #pragma unroll
       for (int h2 = 0; h2 < NH; ++h2) {
         const int c = lane + 64 * h2;
@@ -568,18 +567,50 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
           const float zg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Z[g2]), 16 * i));
           zz = (c / G == g2) ? zg : zz;
         }
-        po[row * D + c] = 4.f * acc[qd][h2][i] + zz;
+        qf[qd * 4 + i][c] = 4.f * acc[qd][h2][i] + zz;
       }
+    }
+  }
+  __syncthreads();
+  float *po = reinterpret_cast<float *>(p.ws + p.L.part_o);
+  float *pml = reinterpret_cast<float *>(p.ws + p.L.part_ml);
+  for (int idx = threadIdx.x; idx < HG * GQ * D; idx += 64 * HB) {
+    const int c = idx % D, hh = (idx / D) % GQ, jl2 = idx / (D * GQ);
+    const int j2 = hg * HG + jl2;
+    if (j2 >= p.Hkv) break;                       // the rest of idx is past the group too
+    // the waves of head jl2: wpos = jl2 + HG*k, and the wpos map is its own inverse
+    auto wave_of = [&](int k) {
+      const int wp = jl2 + HG * k;
+      return (HG == 8 && ((wp >> 2) == 2 || (wp >> 2) == 3)) ? (wp ^ 4) : wp;
+    };
+    float M = -INFINITY;
+    for (int k = 0; k < WH; ++k) M = fmaxf(M, mlw[wave_of(k)][hh][0]);
+    float O = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+      for (int k = 0; k < WH; ++k) {
+        const int wk = wave_of(k);
+        const float m = mlw[wk][hh][0];
+        if (m == -INFINITY) continue;
+        const float a = exp2f(m - M);
+        O = fmaf(a, qf_all[wk][hh][c], O);
+        L = fmaf(a, mlw[wk][hh][1], L);
+      }
+    }
+    const size_t row = ((size_t)b * p.Hq + p.q_of_kv[j2 * GQ + hh]) * P + part;
+    po[row * D + c] = O;
+    if (c == 0) {
+      pml[row * 2 + 0] = M;
+      pml[row * 2 + 1] = L;
     }
   }
 }
 
 template <int D, int G>
 static void launch_mfma_dg(const DecodeParams &p, hipStream_t s) {
-  // splits is a multiple of the waves per head (argument checking rounds it up)
+  // one block per (sequence, group of KV heads, part); splits = parts
   const int hg = mfma_heads_per_block(p.Hkv);
   const int ngrp = (p.Hkv + hg - 1) / hg;
-  const dim3 grid(p.B * ngrp * (p.splits / (kMfmaWaves / hg))), blk(64 * kMfmaWaves);
+  const dim3 grid(p.B * ngrp * p.splits), blk(64 * kMfmaWaves);
   if (p.g == 8) hipLaunchKernelGGL((k_int2_mfma<D, G, 8>), grid, blk, 0, s, p);
   else hipLaunchKernelGGL((k_int2_mfma<D, G, 4>), grid, blk, 0, s, p);
 }

@@ -171,32 +171,34 @@ def test_plan_resolves_int2_kernel():
 
 def test_plan_chunking_rules():
     # batch 32 x 8 KV heads, 6000 history pages: the matrix-core kernel aims at
-    # 4096 (sequence, KV head, chunk) units -> 16 chunks; the VALU kernel at 2048
+    # 256 blocks of (sequence, 8 KV heads, part) -> 8 parts; the VALU kernel at
+    # 2048 (sequence, KV head, chunk) units -> 8 chunks
     big = dict(batch=32, hist_stride=6000, max_hist_len=6000 * 16)
     st, s, p, w, k = _plan(_cache(), _args(**big))
-    assert st == 0 and k == ob.INT2_MFMA and s == 16 and p * s >= 6000 and p * (s - 1) < 6000
+    assert st == 0 and k == ob.INT2_MFMA and s == 8 and p * s >= 6000 and p * (s - 1) < 6000
     st, s, *_ = _plan(_cache(), _args(int2_kernel=ob.INT2_VALU, **big))
     assert st == 0 and s == 8
-    # explicit chunk counts are capped by 1024 (and, for the VALU kernel, by the
-    # page count); the MFMA kernel rounds up to a multiple of its waves per KV
-    # head (16 waves per block over 8 KV heads: 2)
+    # explicit chunk counts are capped by 1024 and by the page count
     st, s, p, *_ = _plan(_cache(), _args(num_splits=5000, **big))
     assert st == 0 and s == 1024 and p == 6
     st, s, p, *_ = _plan(_cache(), _args(num_splits=51, hist_stride=10, max_hist_len=100))
-    assert st == 0 and s == 52 and p == 1
+    assert st == 0 and s == 7 and p == 1
     st, s, p, *_ = _plan(_cache(), _args(num_splits=50, hist_stride=10, max_hist_len=100,
                                           int2_kernel=ob.INT2_VALU))
     assert st == 0 and s == 7 and p == 1
     st, s, *_ = _plan(_cache(), _args(num_splits=3, **big))
-    assert st == 0 and s == 4
-    # one KV head: all 16 waves of a block serve it
-    st, s, *_ = _plan(_cache(num_kv_heads=1), _args(num_q_heads=4, num_splits=3, **big))
-    assert st == 0 and s == 16
-    # a single long sequence still fills the chip: chunks of >= 8x the partial bytes
+    assert st == 0 and s == 3
+    # one KV head per block: 32 sequences x 8 parts still fill 256 blocks
+    st, s, *_ = _plan(_cache(num_kv_heads=1), _args(num_q_heads=4, **big))
+    assert st == 0 and s == 8
+    # a single long sequence fills the chip: 256 parts of >= 16 pages
     st, s, p, *_ = _plan(_cache(), _args(batch=1, hist_stride=6400, max_hist_len=6400 * 16))
-    assert st == 0 and s % 2 == 0 and 200 <= s <= 256
-    # no history: one (empty) chunk, one per wave of a head for the MFMA kernel
+    assert st == 0 and s == 256 and p == 25
+    # ... unless its history is short: parts of at least 16 pages
+    st, s, p, *_ = _plan(_cache(), _args(batch=1, hist_stride=640, max_hist_len=640 * 16))
+    assert st == 0 and s == 40 and p == 16
+    # no history: one (empty) chunk
     st, s, p, *_ = _plan(_cache(), _args(max_hist_len=0))
-    assert st == 0 and s == 2 and p == 0
+    assert st == 0 and s == 1 and p == 0
     st, s, p, *_ = _plan(_cache(), _args(max_hist_len=0, int2_kernel=ob.INT2_VALU))
     assert st == 0 and s == 1 and p == 0
