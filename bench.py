@@ -42,10 +42,13 @@ class BenchState:
     pass
 
 
-def build_workload(name: str, total_steps: int, device="cuda", log=print):
+def build_workload(name: str, total_steps: int, device="cuda", log=print, bf16_history=False):
     """Build the split cache of a 100K-class workload on the device and plan
     `total_steps` decode steps.  History pages are quantised by
-    oscar_demote_pack from generated BF16 tokens."""
+    oscar_demote_pack from generated BF16 tokens.  With bf16_history, the same
+    tokens are also laid out as the comparison cache: every history page kept
+    in BF16 at its physical id (same page tables), the sink/recent pages after
+    them."""
     import torch
     from int2_rotated_kv_amd import binding as ob
     from int2_rotated_kv_amd.splitcache import SplitCache
@@ -66,6 +69,11 @@ def build_workload(name: str, total_steps: int, device="cuda", log=print):
         npg = -(-int(gen.hist_len0[b]) // PAGE)
         prompt[gen.unique_of[b, :npg]] = True
     ppb = synth.LargeGen.PAGES_PER_BLOCK
+    n_hist = sc.cache.num_int2_pages
+    if bf16_history:
+        shape = (n_hist + sc.cache.num_bf16_pages, wl.Hkv, PAGE, wl.D)
+        bk = torch.zeros(shape, dtype=torch.int16, device=device)
+        bv = torch.zeros(shape, dtype=torch.int16, device=device)
     for blk in range(-(-gen.n_unique // ppb)):
         us = np.arange(blk * ppb, min((blk + 1) * ppb, gen.n_unique))
         sel = us[prompt[us]]
@@ -76,6 +84,10 @@ def build_workload(name: str, total_steps: int, device="cuda", log=print):
         v = v.view(ppb, PAGE, wl.Hkv, wl.D)[torch.from_numpy(sel - blk * ppb).to(device)]
         sc.fill_history_pages(gen.phys_of_unique[sel], k.reshape(-1, wl.Hkv, wl.D),
                               v.reshape(-1, wl.Hkv, wl.D), Rk, Rv, ck, cv)
+        if bf16_history:
+            ph = torch.from_numpy(gen.phys_of_unique[sel].astype(np.int64)).to(device)
+            bk[ph] = k.view(torch.int16).permute(0, 2, 1, 3)
+            bv[ph] = v.view(torch.int16).permute(0, 2, 1, 3)
     for b in range(wl.B):
         k, v = gen.bf16_tokens(b)
         sc.load_bf16(b, k, v)
@@ -107,6 +119,16 @@ def build_workload(name: str, total_steps: int, device="cuda", log=print):
     st.dsrc, st.ddst, st.wdst, st.hl, st.bl = dev(dsrc), dev(ddst), dev(wdst), dev(hl), dev(bl)
     st.hl_h, st.bl_h = hl, bl
     toks = [gen.step_tokens(s) for s in range(T)]
+    if bf16_history:
+        # sink/recent pages after the history pages; window slot w -> n_hist*16 + w
+        bk[n_hist:] = sc.cache.bf16_k
+        bv[n_hist:] = sc.cache.bf16_v
+        st.cmp_cache = ob.Cache(wl.Hkv, wl.D, wl.G, 0, bk.shape[0], device=device,
+                                bf16_k=bk, bf16_v=bv)
+        st.cmp_win_pages = sc.bf16_pages + n_hist
+        st.cmp_off = n_hist * PAGE
+        log(f"[bench] comparison cache: {bk.shape[0]} BF16 pages "
+            f"({2 * bk.numel() * 2 / 1e9:.2f} GB)")
     st.knew = torch.stack([t[0] for t in toks]).view(torch.int16)
     st.vnew = torch.stack([t[1] for t in toks]).view(torch.int16)
     st.q = torch.stack([t[2] for t in toks]).view(torch.int16)
@@ -190,6 +212,52 @@ def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0
     int2_only_ms = e0.elapsed_time(e1) / n_i2
     return dict(wall_s=wall, seg_ms=seg, first_out=first_out, out=out, args=args,
                 int2_only_ms=int2_only_ms, int2_only_step=T - 1)
+
+
+def run_steps_bf16(st, steps, warmup):
+    """The same decode steps on the comparison cache (history in BF16 pages):
+    copy the oldest recent token into its history slot, write the new token
+    into the freed window slot, attend (BF16 window + BF16 history) and merge.
+    Returns the timed wall seconds and the per-launch time of the history
+    kernel alone."""
+    import torch
+    from int2_rotated_kv_amd import binding as ob
+    wl, cache = st.wl, st.cmp_cache
+    T = steps + warmup
+    args = [ob.DecodeArgs(wl.B, wl.Hq, st.sc.hist_pages, st.hl[s], st.cmp_win_pages, st.bl[s],
+                          int(st.hl_h[s].max()), int2_kernel=ob.HISTORY_BF16) for s in range(T)]
+    a_h = [a.with_phases(ob.PHASE_INT2) for a in args]
+    ws = ob.alloc_workspace(cache, args[-1])
+    out = torch.zeros((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=st.q.device)
+    lse = torch.zeros((wl.B, wl.Hq), dtype=torch.float32, device=st.q.device)
+    src = (st.dsrc.long() + st.cmp_off)
+    wdst = st.wdst + st.cmp_off
+    kp, vp = cache.bf16_k, cache.bf16_v
+
+    def one(s):
+        sp, so = src[s] // PAGE, src[s] % PAGE
+        kd, vd = kp[sp, :, so, :], vp[sp, :, so, :]       # [B, Hkv, D]
+        ob.write_bf16(cache, st.ddst[s], kd, vd)
+        ob.write_bf16(cache, wdst[s], st.knew[s], st.vnew[s])
+        ob.decode_attn(cache, args[s], st.q[s], None, ws)
+        ob.merge(cache, args[s], ws, None, out, lse)
+
+    for s in range(warmup):
+        one(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one(warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n = 10
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        ob.decode_attn(cache, a_h[T - 1], st.q[T - 1], None, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    return dict(wall_s=wall, hist_ms=e0.elapsed_time(e1) / n, out=out, lse=lse)
 
 
 # --------------------------------------------------------------------------
@@ -368,6 +436,9 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=0,
                     help="history chunks per (sequence, KV head); 0 = the library's choice")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-bf16-compare", action="store_true",
+                    help="skip the comparison run over the same tokens with the whole "
+                         "history kept in BF16 pages")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run 5 plain device-to-device copies of BYTES bytes (the "
                          "reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE) and exit")
@@ -390,7 +461,8 @@ def main(argv=None):
         return
     kern = {"auto": ob.INT2_AUTO, "valu": ob.INT2_VALU, "mfma": ob.INT2_MFMA}[a.int2_kernel]
     torch.cuda.set_device(0)
-    st = build_workload(a.workload, a.steps + a.warmup + breakdown_steps(a.steps), log=log)
+    st = build_workload(a.workload, a.steps + a.warmup + breakdown_steps(a.steps), log=log,
+                        bf16_history=not a.no_bf16_compare)
     wl = st.wl
     r = run_steps(st, a.steps, a.warmup, kern, keep_first_out=not a.no_cpu_baseline,
                   num_splits=a.splits)
@@ -434,6 +506,23 @@ def main(argv=None):
                      "traffic": tr, "kernel": kname,
                      "alg_bytes_per_launch": i2_last, "launch_ms": r["int2_only_ms"]},
     }
+    if not a.no_bf16_compare:
+        rb = run_steps_bf16(st, a.steps, a.warmup)
+        ms_b = 1000.0 * rb["wall_s"] / a.steps
+        hist_b = np.mean([int(st.hl_h[s].sum()) for s in timed]) * wl.Hkv * 2 * wl.D * 2
+        hl_last = st.hl_h[a.steps + a.warmup - 1]
+        out["bf16_history"] = {
+            "ms_per_step": ms_b, "value": kvth / (ms_b * 1e-3), "unit": "KV-token-heads/s",
+            "int2_speedup": ms_b / ms_step,
+            "hist_kernel": "k_bf16_hist", "hist_kernel_ms": rb["hist_ms"],
+            "hist_kernel_GBs": float(hl_last.sum()) * wl.Hkv * 2 * wl.D * 2 / (rb["hist_ms"] * 1e-3) / 1e9,
+            "hist_bytes_per_step": hist_b,
+            "what": "same steps, same tokens, whole history in BF16 pages (no rotation or "
+                    "quantisation): copy the demoted token into the BF16 history, write the "
+                    "new token, BF16 window + BF16 history attention, merge",
+        }
+        log(f"[bench] BF16-history comparison: {ms_b:.4f} ms/step, INT2 speed-up "
+            f"{ms_b / ms_step:.2f}x")
     if not a.no_cpu_baseline:
         cb, worst = cpu_baseline(st, r["first_out"], budget_s=a.cpu_budget, log=log)
         out["cpu_baseline"] = cb

@@ -89,7 +89,11 @@ enum {
 enum {
   OSCAR_INT2_AUTO = 0,
   OSCAR_INT2_VALU = 1,      /* vector-ALU dot products                         */
-  OSCAR_INT2_MFMA = 2       /* matrix-core contraction                         */
+  OSCAR_INT2_MFMA = 2,      /* matrix-core contraction                         */
+  OSCAR_HISTORY_BF16 = 3    /* comparison layout, no INT2: the history pages are
+                               BF16 pages of the BF16 pool (unrotated,
+                               unquantised); oscar_decode_attn skips the query
+                               rotation and oscar_merge ignores R_v            */
 };
 
 typedef struct {
@@ -124,7 +128,8 @@ typedef struct {
   float sm_scale;            /* softmax scale; 0 means 1/sqrt(D)                */
   int32_t num_splits;        /* history chunks per (sequence, KV head); 0 = auto;
                                 at most min(1024, history pages) are used       */
-  int32_t int2_kernel;       /* OSCAR_INT2_AUTO / _VALU / _MFMA                  */
+  int32_t int2_kernel;       /* OSCAR_INT2_AUTO / _VALU / _MFMA, or
+                                OSCAR_HISTORY_BF16                              */
   uint32_t phases;           /* oscar_decode_attn work: OR of OSCAR_PHASE_*; 0 means
                                 all.  Phases may be issued in separate calls (e.g.
                                 on two streams or between timing events); the
@@ -178,10 +183,11 @@ int oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_ar
  * oscar_decode_plan - the history chunking oscar_decode_attn will use for these
  * arguments (host only): num_splits chunks of pages_per_split pages per
  * (sequence, KV head), the workspace size, and the INT2 kernel that runs
- * (OSCAR_INT2_VALU or OSCAR_INT2_MFMA, AUTO resolved).  Any output may be NULL.
- * VALU kernel: automatic chunking (num_splits == 0) aims at 2048 (sequence,
- * KV head, chunk) units while keeping every chunk at least 8x the bytes of its
- * partial result and 16 pages long; chunk c covers pages
+ * (OSCAR_INT2_VALU, OSCAR_INT2_MFMA or OSCAR_HISTORY_BF16, AUTO resolved).
+ * Any output may be NULL.
+ * VALU kernel and BF16 history: automatic chunking (num_splits == 0) aims at
+ * 2048 (sequence, KV head, chunk) units while keeping every chunk at least 8x
+ * the bytes of its partial result and 16 pages long; chunk c covers pages
  * [c*pages_per_split, (c+1)*pages_per_split) and empty chunks are dropped.
  * MFMA kernel: a chunk is one of num_splits equal parts of each sequence's
  * history.  One block of 16 waves serves one part for a group of up to 8 KV
@@ -200,7 +206,8 @@ int oscar_decode_plan(const oscar_cache *cache, const oscar_decode_args *args,
  * oscar_decode_attn - attend every q head over both segments, producing partial
  * results in `workspace` (thmotor: decode stage of the split-cache paragraph).
  *   q          [B][Hq][D] bf16
- *   R_k        [Hkv][D][D] fp32: the history is attended with q . R_k
+ *   R_k        [Hkv][D][D] fp32: the history is attended with q . R_k (unused,
+ *              may be NULL, with OSCAR_HISTORY_BF16)
  *   workspace  >= oscar_decode_workspace_bytes; contents valid for a following
  *              oscar_merge with the same cache/args on the same stream
  * Partials per (sequence, q head): one for the BF16 segment (unrotated q and

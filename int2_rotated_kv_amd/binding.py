@@ -20,7 +20,7 @@ OSCAR_EUNSUPPORTED = -2
 OSCAR_EWORKSPACE = -3
 OSCAR_EHIP = -4
 
-INT2_AUTO, INT2_VALU, INT2_MFMA = 0, 1, 2
+INT2_AUTO, INT2_VALU, INT2_MFMA, HISTORY_BF16 = 0, 1, 2, 3
 PHASE_QROT, PHASE_BF16, PHASE_INT2, PHASE_ALL = 1, 2, 4, 7
 PAGE = 16
 SINK, RECENT = 64, 256
@@ -218,7 +218,7 @@ def workspace_bytes(cache: Cache, args: DecodeArgs) -> int:
 
 def decode_plan(cache: Cache, args: DecodeArgs):
     """(num_splits, pages_per_split, workspace_bytes, int2_kernel) oscar_decode_attn
-    will use; int2_kernel is INT2_VALU or INT2_MFMA."""
+    will use; int2_kernel is INT2_VALU, INT2_MFMA or HISTORY_BF16."""
     d = cache.desc()
     s, p, w, k = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_size_t(0), ctypes.c_int32(0)
     check(lib().oscar_decode_plan(ctypes.byref(d), ctypes.byref(args.c), ctypes.byref(s),

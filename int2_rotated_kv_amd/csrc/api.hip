@@ -98,15 +98,19 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
     if (a->hist_stride < need_hist)
       return fail(OSCAR_EINVAL, "hist_stride %d < ceil(max_hist_len/16) = %d", a->hist_stride,
                   need_hist);
-    if (c->num_int2_pages <= 0) return fail(OSCAR_EINVAL, "max_hist_len > 0 but no INT2 pages");
+    if (a->int2_kernel == OSCAR_HISTORY_BF16) {
+      if (c->num_bf16_pages <= 0) return fail(OSCAR_EINVAL, "max_hist_len > 0 but no BF16 pages");
+    } else if (c->num_int2_pages <= 0) {
+      return fail(OSCAR_EINVAL, "max_hist_len > 0 but no INT2 pages");
+    }
   }
   if (a->bf16_pages == nullptr || a->bf16_stride < 1)
     return fail(OSCAR_EINVAL, "bf16_pages is NULL or bf16_stride < 1");
   if (!(a->sm_scale >= 0.f) || !std::isfinite(a->sm_scale))
     return fail(OSCAR_EINVAL, "sm_scale must be finite and >= 0");
   if (a->num_splits < 0) return fail(OSCAR_EINVAL, "num_splits < 0");
-  if (a->int2_kernel < OSCAR_INT2_AUTO || a->int2_kernel > OSCAR_INT2_MFMA)
-    return fail(OSCAR_EINVAL, "int2_kernel must be 0, 1 or 2");
+  if (a->int2_kernel < OSCAR_INT2_AUTO || a->int2_kernel > OSCAR_HISTORY_BF16)
+    return fail(OSCAR_EINVAL, "int2_kernel must be 0, 1, 2 or 3");
   if (a->phases & ~(uint32_t)OSCAR_PHASE_ALL) return fail(OSCAR_EINVAL, "unknown phase bits");
 
   p->B = a->batch;
@@ -156,7 +160,9 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
       const int hg = mfma_heads_per_block(c->num_kv_heads);
       const int units = mf ? a->batch * ((c->num_kv_heads + hg - 1) / hg) : a->batch * c->num_kv_heads;
       const int target = mf ? kMfmaTargetBlocks : 2048;
-      const double rec = (double)RecLayout(p->D, p->G).bytes();
+      // bytes of one history page of one KV head
+      const double rec = kind == OSCAR_HISTORY_BF16 ? 2.0 * kPage * p->D * 2
+                                                    : (double)RecLayout(p->D, p->G).bytes();
       const double part_bytes = 2.0 * p->g * (p->D + 2) * 4.0;   // write + read back
       int min_pages = (int)std::ceil((mf ? 4.0 : 8.0) * part_bytes / rec);
       min_pages = min_pages < 16 ? 16 : min_pages;
@@ -263,7 +269,8 @@ int oscar_decode_attn(const oscar_cache *cache, const oscar_decode_args *args, c
   int st = check_args(cache, args, &p);
   if (st) return st;
   if (!q || !aligned(q, 16)) return fail(OSCAR_EINVAL, "q is NULL or not 16-byte aligned");
-  if (!R_k || !aligned(R_k, 16)) return fail(OSCAR_EINVAL, "R_k is NULL or not 16-byte aligned");
+  if (p.int2_kind != OSCAR_HISTORY_BF16 && (!R_k || !aligned(R_k, 16)))
+    return fail(OSCAR_EINVAL, "R_k is NULL or not 16-byte aligned");
   if (!workspace || !aligned(workspace, 256))
     return fail(OSCAR_EINVAL, "workspace is NULL or not 256-byte aligned");
   if (workspace_bytes < p.L.total)
@@ -273,7 +280,8 @@ int oscar_decode_attn(const oscar_cache *cache, const oscar_decode_args *args, c
   hipStream_t s = (hipStream_t)stream;
   const uint32_t ph = args->phases ? args->phases : (uint32_t)OSCAR_PHASE_ALL;
   hipError_t e = hipSuccess;
-  if (ph & OSCAR_PHASE_QROT) {
+  const bool bf16_hist = p.int2_kind == OSCAR_HISTORY_BF16;
+  if ((ph & OSCAR_PHASE_QROT) && !bf16_hist) {
     e = launch_qrot(p, q, R_k, s);
     if (e != hipSuccess) return hip_fail(e, "q rotation launch");
   }
@@ -282,8 +290,9 @@ int oscar_decode_attn(const oscar_cache *cache, const oscar_decode_args *args, c
     if (e != hipSuccess) return hip_fail(e, "BF16 segment launch");
   }
   if ((ph & OSCAR_PHASE_INT2) && args->max_hist_len > 0) {
-    e = p.int2_kind == OSCAR_INT2_MFMA ? launch_int2_mfma(p, s) : launch_int2_valu(p, s);
-    if (e != hipSuccess) return hip_fail(e, "INT2 segment launch");
+    e = bf16_hist ? launch_bf16_hist(p, q, s)
+        : p.int2_kind == OSCAR_INT2_MFMA ? launch_int2_mfma(p, s) : launch_int2_valu(p, s);
+    if (e != hipSuccess) return hip_fail(e, "history segment launch");
   }
   return OSCAR_OK;
 }
@@ -302,6 +311,7 @@ int oscar_merge(const oscar_cache *cache, const oscar_decode_args *args, const v
                 p.L.total);
   p.ws = static_cast<uint8_t *>(const_cast<void *>(workspace));
   if (args->max_hist_len == 0) p.splits = 0;   // no history chunk was produced
+  if (p.int2_kind == OSCAR_HISTORY_BF16) R_v = nullptr;   // unrotated history
   hipError_t e = launch_merge(p, R_v, out, lse, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return OSCAR_OK;

@@ -80,7 +80,7 @@ struct DecodeParams {
   const int32_t *bf16_len;
   int max_hist_len;
   float sm_log2;       // softmax scale * log2(e)
-  int int2_kind;       // resolved INT2 kernel: OSCAR_INT2_VALU or OSCAR_INT2_MFMA
+  int int2_kind;       // resolved history kernel: OSCAR_INT2_VALU, _MFMA or OSCAR_HISTORY_BF16
   int splits, pages_per_split;
   uint8_t *ws;
   WsLayout L;
@@ -105,6 +105,7 @@ hipError_t launch_qrot(const DecodeParams &p, const uint16_t *q, const float *Rk
 hipError_t launch_bf16_seg(const DecodeParams &p, const uint16_t *q, hipStream_t s);
 hipError_t launch_int2_valu(const DecodeParams &p, hipStream_t s);
 hipError_t launch_int2_mfma(const DecodeParams &p, hipStream_t s);
+hipError_t launch_bf16_hist(const DecodeParams &p, const uint16_t *q, hipStream_t s);
 hipError_t launch_merge(const DecodeParams &p, const float *Rv, float *out, float *lse,
                         hipStream_t s);
 

@@ -151,3 +151,70 @@ def row_rel_err(got, ref):
     """max_c |got - ref| / max_c |ref| per row (the last axis)."""
     den = np.maximum(np.abs(ref).max(axis=-1), 1e-30)
     return np.abs(got - ref).max(axis=-1) / den
+
+
+def build_bf16_history_and_attend(inp: synth.SmallInputs, num_splits=0, device="cuda"):
+    """The comparison layout: every sequence's history kept as BF16 pages of
+    the BF16 pool (no rotation, no quantisation), sink + recent in BF16 pages
+    of the same pool, every page at a seeded random physical id.  One
+    decode_attn (history kind HISTORY_BF16) + merge; returns (out, lse)."""
+    import torch
+    from int2_rotated_kv_amd import binding as ob
+
+    wl = inp.wl
+    B, Hkv, D = wl.B, wl.Hkv, wl.D
+    spl = [synth.split_lengths(L) for L in wl.lengths]
+    hp = [-(-h // PAGE) for (_, h, _) in spl]
+    wp = [-(-(s + r) // PAGE) for (s, _, r) in spl]
+    n = sum(hp) + sum(wp)
+    perm = synth.page_permutation(wl.seed + 11, n, extra=2)
+    kpool = np.zeros((n + 2, Hkv, PAGE, D), np.uint16)
+    vpool = np.zeros_like(kpool)
+    hstride, wstride = max(1, max(hp)), max(1, max(wp))
+    htab = np.zeros((B, hstride), np.int32)
+    wtab = np.zeros((B, wstride), np.int32)
+    o = 0
+    for b in range(B):
+        s, h, r = spl[b]
+        K, V = inp.K[b], inp.V[b]
+        for tab, idx, npg, col in ((htab, list(range(s, s + h)), hp[b], 0),
+                                   (wtab, list(range(0, s)) + list(range(s + h, wl.lengths[b])), wp[b], 0)):
+            for pgi in range(npg):
+                ph = perm[o]; o += 1
+                tab[b, pgi] = ph
+                tok = idx[pgi * PAGE:(pgi + 1) * PAGE]
+                kpool[ph, :, :len(tok)] = K[tok].transpose(1, 0, 2)
+                vpool[ph, :, :len(tok)] = V[tok].transpose(1, 0, 2)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(device)
+    cache = ob.Cache(Hkv, D, wl.G, 0, n + 2, device=device,
+                     bf16_k=dev(kpool.view(np.int16)), bf16_v=dev(vpool.view(np.int16)))
+    hl = np.array([h for (_, h, _) in spl], np.int32)
+    bl = np.array([s + r for (s, _, r) in spl], np.int32)
+    args = ob.DecodeArgs(B, wl.Hq, dev(htab), dev(hl), dev(wtab), dev(bl), int(hl.max()),
+                         num_splits=num_splits, int2_kernel=ob.HISTORY_BF16)
+    out = torch.zeros((B, wl.Hq, D), dtype=torch.float32, device=device)
+    lse = torch.zeros((B, wl.Hq), dtype=torch.float32, device=device)
+    q = to_dev_bf16(inp.q[0])
+    ob.decode(cache, args, q.view(torch.int16), None, None, out, lse)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def oracle_plain(inp: synth.SmallInputs):
+    """Oracle attention of q (step 0) over every token of each sequence, all
+    BF16 (the comparison layout): the split form with an unquantised history
+    and identity rotations."""
+    wl = inp.wl
+    hm = orc.default_head_map(wl.Hq, wl.Hkv)
+    eye = np.broadcast_to(np.eye(wl.D), (wl.Hkv, wl.D, wl.D))
+    res = {}
+    for b in range(wl.B):
+        L = wl.lengths[b]
+        s, h, r = synth.split_lengths(L)
+        K = synth.bf16_bits_to_f64(inp.K[b][:L])
+        V = synth.bf16_bits_to_f64(inp.V[b][:L])
+        bidx = list(range(0, s)) + list(range(s + h, L))
+        q = synth.bf16_bits_to_f64(inp.q[0][b])
+        out, lse = orc.decode_attention(q, hm, K[bidx], V[bidx], K[s:s + h], V[s:s + h], eye, None)
+        res[b] = dict(out=out, lse=lse)
+    return res

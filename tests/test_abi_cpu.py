@@ -202,3 +202,31 @@ def test_plan_chunking_rules():
     assert st == 0 and s == 1 and p == 0
     st, s, p, *_ = _plan(_cache(), _args(max_hist_len=0, int2_kernel=ob.INT2_VALU))
     assert st == 0 and s == 1 and p == 0
+
+
+def test_plan_bf16_history_comparison():
+    """HISTORY_BF16: the history pages are BF16 pool pages; chunking follows the
+    VALU rule with 8 KiB BF16 pages per head; no INT2 pool is needed."""
+    big = dict(batch=32, hist_stride=6000, max_hist_len=6000 * 16, int2_kernel=ob.HISTORY_BF16)
+    st, s, p, w, k = _plan(_cache(num_int2_pages=0, int2_pool=0), _args(**big))
+    assert st == ob.OSCAR_OK and k == ob.HISTORY_BF16 and s == 8 and p == 750
+    st, s, p, *_ = _plan(_cache(), _args(batch=1, hist_stride=6400, max_hist_len=6400 * 16,
+                                         int2_kernel=ob.HISTORY_BF16))
+    assert st == ob.OSCAR_OK and s == 256 and p == 25
+    # a history with no BF16 pool to hold it is rejected
+    st, *_ = _plan(_cache(num_bf16_pages=0, bf16_k_pool=0, bf16_v_pool=0), _args(**big))
+    assert st == ob.OSCAR_EINVAL and "BF16" in ob.last_error()
+    # an unknown kernel kind is rejected
+    st, *_ = _plan(_cache(), _args(int2_kernel=4))
+    assert st == ob.OSCAR_EINVAL
+
+
+def test_bf16_history_needs_no_rotation():
+    """decode_attn with HISTORY_BF16 accepts R_k = NULL (argument checks only:
+    workspace too small, so nothing is launched)."""
+    c, a = _cache(), _args(int2_kernel=ob.HISTORY_BF16)
+    st = ob.lib().oscar_decode_attn(ctypes.byref(c), ctypes.byref(a), 0x80000, None, 0x90000, 16, None)
+    assert st == ob.OSCAR_EWORKSPACE
+    a = _args()
+    st = ob.lib().oscar_decode_attn(ctypes.byref(c), ctypes.byref(a), 0x80000, None, 0x90000, 16, None)
+    assert st == ob.OSCAR_EINVAL and "R_k" in ob.last_error()

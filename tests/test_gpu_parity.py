@@ -110,3 +110,26 @@ def test_shapes(kernel, D, G, Hq, Hkv):
     _check_bytes(run, inp, ref)
     w = _check_out(run, ref)
     _say("worst row rel err", w)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("shape", ["tiny", "edge", "d128g4", "d128g8"])
+def test_bf16_history_comparison(shape, splits):
+    """The comparison layout (whole history in BF16 pages, HISTORY_BF16) equals
+    one softmax over all tokens of each sequence."""
+    _say("case: BF16 history", shape, "splits", splits)
+    if shape == "tiny":
+        wl = synth.workload("tiny", B=2, lengths=(1024, 777), steps=1, seed=21)
+    elif shape == "edge":
+        wl = synth.workload("tiny", B=5, Hkv=2, Hq=8, lengths=(10, 64, 320, 321, 400), steps=1, seed=22)
+    elif shape == "d128g4":
+        wl = synth.workload("tiny", B=2, Hkv=2, Hq=8, D=128, G=64, lengths=(3000, 1700), steps=1, seed=23)
+    else:
+        wl = synth.workload("tiny", B=2, Hkv=2, Hq=16, D=128, G=128, lengths=(2500, 999), steps=1, seed=24)
+    inp = synth.make_small(wl)
+    out, lse = sh.build_bf16_history_and_attend(inp, num_splits=splits)
+    ref = sh.oracle_plain(inp)
+    for b, r in ref.items():
+        e = sh.row_rel_err(out[b].astype(np.float64), r["out"])
+        assert np.all(e <= TOL), f"seq {b}: row errors {np.sort(e)[-4:]}"
+        assert np.abs(lse[b] - r["lse"]).max() < 1e-3
