@@ -233,6 +233,38 @@ int oscar_merge(const oscar_cache *cache, const oscar_decode_args *args,
                 const void *workspace, size_t workspace_bytes, const float *R_v,
                 float *out, float *lse, void *stream);
 
+/*
+ * oscar_decode_step - one whole decode step of a batch in three launches
+ * (m.th-motor.com repost of the OSCAR article, split-cache paragraph: the new
+ * token enters the recent window, the oldest recent token is rotated,
+ * clipped, quantised, packed and demoted, and decode attends the BF16 and
+ * INT2 segments and merges them).  Same result, bit for bit, as
+ *   oscar_demote_pack(cache, B, demote_src, demote_dst, R_k, R_v, clip_k, clip_v)
+ *   oscar_write_bf16(cache, B, new_slot, k_new, v_new)
+ *   oscar_decode_attn(cache, args, q, R_k, workspace)
+ *   oscar_merge(cache, args, workspace, R_v, out, lse)
+ * with the first launch doing the demotion, the token store, the query
+ * rotation and the BF16 segment side by side (the BF16 segment reads the new
+ * token from k_new/v_new), then the INT2 history chunks, then the merge.
+ *   demote_src, demote_dst [B] slots (page*16 + offset) of sequence b's
+ *              demoted token, -1 = no demotion for b
+ *   new_slot   [B] BF16 slot of sequence b's new token, -1 = none; it may be
+ *              demote_src[b] (the freed slot) but no other sequence's
+ *              demote_src, and must be one of the slots args lists for b
+ *   k_new, v_new [B][Hkv][D] bf16, 16-byte aligned
+ *   args       describes the cache after the step (lengths include the new
+ *              token and the demoted one); phases must be 0 (or
+ *              OSCAR_PHASE_ALL); the history kind must be an INT2 one
+ * Errors: as the four calls, plus EINVAL for phases != 0 and EUNSUPPORTED for
+ * OSCAR_HISTORY_BF16.  Nothing is launched on an error.
+ */
+int oscar_decode_step(const oscar_cache *cache, const oscar_decode_args *args,
+                      const int32_t *demote_src, const int32_t *demote_dst, const float *clip_k,
+                      const float *clip_v, const int32_t *new_slot, const uint16_t *k_new,
+                      const uint16_t *v_new, const uint16_t *q, const float *R_k, const float *R_v,
+                      void *workspace, size_t workspace_bytes, float *out, float *lse,
+                      void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -91,6 +91,12 @@ _SIGS = {
     "oscar_merge": (ctypes.c_int, [ctypes.POINTER(OscarCache), ctypes.POINTER(OscarDecodeArgs),
                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_void_p]),
+    "oscar_decode_step": (ctypes.c_int, [ctypes.POINTER(OscarCache), ctypes.POINTER(OscarDecodeArgs),
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 
@@ -241,6 +247,19 @@ def merge(cache: Cache, args: DecodeArgs, workspace, R_v, out, lse=None, stream=
     d = cache.desc()
     check(lib().oscar_merge(ctypes.byref(d), ctypes.byref(args.c), _ptr(workspace),
                             int(workspace.numel()), _ptr(R_v), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def decode_step(cache: Cache, args: DecodeArgs, demote_src, demote_dst, clip_k, clip_v, new_slot,
+                k_new, v_new, q, R_k, R_v, workspace, out, lse=None, stream=None):
+    """oscar_decode_step: demotion, new-token store, both segments and the merge
+    of one decode step (demote_src/demote_dst/new_slot int32 [B], -1 = none;
+    k_new/v_new [B, Hkv, D] bf16 bits)."""
+    d = cache.desc()
+    check(lib().oscar_decode_step(ctypes.byref(d), ctypes.byref(args.c), _ptr(demote_src),
+                                  _ptr(demote_dst), _ptr(clip_k), _ptr(clip_v), _ptr(new_slot),
+                                  _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(R_k), _ptr(R_v),
+                                  _ptr(workspace), int(workspace.numel()), _ptr(out), _ptr(lse),
+                                  _stream(stream)))
 
 
 def decode(cache: Cache, args: DecodeArgs, q, R_k, R_v, out, lse=None, workspace=None, stream=None):

@@ -317,4 +317,47 @@ int oscar_merge(const oscar_cache *cache, const oscar_decode_args *args, const v
   return OSCAR_OK;
 }
 
+int oscar_decode_step(const oscar_cache *cache, const oscar_decode_args *args,
+                      const int32_t *demote_src, const int32_t *demote_dst, const float *clip_k,
+                      const float *clip_v, const int32_t *new_slot, const uint16_t *k_new,
+                      const uint16_t *v_new, const uint16_t *q, const float *R_k, const float *R_v,
+                      void *workspace, size_t workspace_bytes, float *out, float *lse,
+                      void *stream) {
+  DecodeParams p{};
+  int st = check_args(cache, args, &p);
+  if (st) return st;
+  if (args->phases != 0 && args->phases != (uint32_t)OSCAR_PHASE_ALL)
+    return fail(OSCAR_EINVAL, "oscar_decode_step runs every phase (phases must be 0 or ALL)");
+  if (p.int2_kind == OSCAR_HISTORY_BF16)
+    return fail(OSCAR_EUNSUPPORTED, "oscar_decode_step needs an INT2 history");
+  if (!demote_src || !demote_dst || !new_slot) return fail(OSCAR_EINVAL, "NULL slot list");
+  if (!clip_k || !clip_v) return fail(OSCAR_EINVAL, "NULL clip ratios");
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(OSCAR_EINVAL, "k_new / v_new are NULL or not 16-byte aligned");
+  if (!q || !aligned(q, 16)) return fail(OSCAR_EINVAL, "q is NULL or not 16-byte aligned");
+  if (!R_k || !aligned(R_k, 16)) return fail(OSCAR_EINVAL, "R_k is NULL or not 16-byte aligned");
+  if (R_v && !aligned(R_v, 16)) return fail(OSCAR_EINVAL, "R_v is not 16-byte aligned");
+  if (!out) return fail(OSCAR_EINVAL, "out is NULL");
+  if (cache->num_bf16_pages <= 0) return fail(OSCAR_EINVAL, "cache has no BF16 pages");
+  if (!workspace || !aligned(workspace, 256))
+    return fail(OSCAR_EINVAL, "workspace is NULL or not 256-byte aligned");
+  if (workspace_bytes < p.L.total)
+    return fail(OSCAR_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
+                p.L.total);
+  p.ws = static_cast<uint8_t *>(workspace);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_step_pre(p, *cache, q, R_k, R_v, clip_k, clip_v, demote_src, demote_dst,
+                                 new_slot, k_new, v_new, s);
+  if (e != hipSuccess) return hip_fail(e, "decode-step prologue launch");
+  if (args->max_hist_len > 0) {
+    e = p.int2_kind == OSCAR_INT2_MFMA ? launch_int2_mfma(p, s) : launch_int2_valu(p, s);
+    if (e != hipSuccess) return hip_fail(e, "history segment launch");
+  } else {
+    p.splits = 0;                               // no history chunk was produced
+  }
+  e = launch_merge(p, R_v, out, lse, s);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return OSCAR_OK;
+}
+
 }  // extern "C"

@@ -108,5 +108,9 @@ hipError_t launch_int2_mfma(const DecodeParams &p, hipStream_t s);
 hipError_t launch_bf16_hist(const DecodeParams &p, const uint16_t *q, hipStream_t s);
 hipError_t launch_merge(const DecodeParams &p, const float *Rv, float *out, float *lse,
                         hipStream_t s);
+hipError_t launch_step_pre(const DecodeParams &p, const oscar_cache &c, const uint16_t *q,
+                           const float *Rk, const float *Rv, const float *ck, const float *cv,
+                           const int32_t *dsrc, const int32_t *ddst, const int32_t *new_slot,
+                           const uint16_t *k_new, const uint16_t *v_new, hipStream_t s);
 
 }  // namespace oscar

@@ -9,6 +9,7 @@
 // exponential is exp2.  Partials per (sequence, q head, chunk) are
 // (m = max s, l = sum 2^(s - m), o = sum 2^(s - m) v) in fp32.
 #include "common.hpp"
+#include "demote.hpp"
 
 namespace oscar {
 
@@ -23,19 +24,22 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // rows gi*RPG .. +RPG-1 of R for columns 4*c4 .. +3 (one 16-byte load per row,
 // all issued together); the row groups are added in LDS.
 template <int D>
-__global__ __launch_bounds__(256) void k_qrot(DecodeParams p, const uint16_t *__restrict__ q,
-                                              const float *__restrict__ Rk) {
+struct QrotShared {
+  double qs[D];
+  double part[256 / (D / 4)][D];
+};
+
+template <int D>
+__device__ __forceinline__ void qrot_body(const DecodeParams &p, const uint16_t *__restrict__ q,
+                                          const float *__restrict__ Rk, int bh, int tid,
+                                          QrotShared<D> &sh) {
   constexpr int NC4 = D / 4;             // column quads
   constexpr int NGR = 256 / NC4;         // row groups
   constexpr int RPG = D / NGR;           // rows per group
-  const int bh = blockIdx.x;
   const int h = bh % p.Hq;
   const int j = p.kv_of_q[h];
-  const int tid = threadIdx.x;
   const int c4 = tid % NC4, gi = tid / NC4;
-  __shared__ double qs[D];
-  __shared__ double part[NGR][D];
-  if (tid < D) qs[tid] = (double)bf16_to_f32(q[(size_t)bh * D + tid]);
+  if (tid < D) sh.qs[tid] = (double)bf16_to_f32(q[(size_t)bh * D + tid]);
   __syncthreads();
   const float4 *R = reinterpret_cast<const float4 *>(Rk + (size_t)j * D * D) + c4;
   float4 r[RPG];
@@ -44,23 +48,30 @@ __global__ __launch_bounds__(256) void k_qrot(DecodeParams p, const uint16_t *__
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
 #pragma unroll
   for (int i = 0; i < RPG; ++i) {
-    const double qi = qs[gi * RPG + i];
+    const double qi = sh.qs[gi * RPG + i];
     a0 = fma(qi, (double)r[i].x, a0);
     a1 = fma(qi, (double)r[i].y, a1);
     a2 = fma(qi, (double)r[i].z, a2);
     a3 = fma(qi, (double)r[i].w, a3);
   }
-  part[gi][4 * c4 + 0] = a0;
-  part[gi][4 * c4 + 1] = a1;
-  part[gi][4 * c4 + 2] = a2;
-  part[gi][4 * c4 + 3] = a3;
+  sh.part[gi][4 * c4 + 0] = a0;
+  sh.part[gi][4 * c4 + 1] = a1;
+  sh.part[gi][4 * c4 + 2] = a2;
+  sh.part[gi][4 * c4 + 3] = a3;
   __syncthreads();
   if (tid < D) {
     double acc = 0.0;
 #pragma unroll
-    for (int g2 = 0; g2 < NGR; ++g2) acc += part[g2][tid];
+    for (int g2 = 0; g2 < NGR; ++g2) acc += sh.part[g2][tid];
     reinterpret_cast<float *>(p.ws + p.L.qrot)[(size_t)bh * D + tid] = (float)acc;
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_qrot(DecodeParams p, const uint16_t *__restrict__ q,
+                                              const float *__restrict__ Rk) {
+  __shared__ QrotShared<D> sh;
+  qrot_body<D>(p, q, Rk, blockIdx.x, threadIdx.x, sh);
 }
 
 hipError_t launch_qrot(const DecodeParams &p, const uint16_t *q, const float *Rk, hipStream_t s) {
@@ -87,19 +98,32 @@ hipError_t launch_qrot(const DecodeParams &p, const uint16_t *q, const float *Rk
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 template <int D, int GQ>
-__global__ __launch_bounds__(256) void k_bf16_seg(DecodeParams p, const uint16_t *__restrict__ q) {
+struct SegShared {
+  __align__(16) float pb[4][kPage][GQ];   // per wave: p[token][head]
+  float wm[4][GQ], wl[4][GQ];
+  float wo[4][GQ][D];
+};
+
+// The token of this step, not yet in the pool: slot[b] (page * 16 + offset,
+// negative = none) of sequence b reads k[b][j][:], v[b][j][:] instead.
+struct NewTok {
+  const int32_t *slot;
+  const uint16_t *k, *v;               // [B][Hkv][D] bf16
+};
+
+template <int D, int GQ>
+__device__ __forceinline__ void bf16_seg_body(const DecodeParams &p, const uint16_t *__restrict__ q,
+                                              int b, int j, int split, int tid, const NewTok &nt,
+                                              SegShared<D, GQ> &sh) {
   constexpr int NM = D / 32;           // QK matrix instructions (32 channels each)
   constexpr int NCH = D / 64;          // PV channels per lane
   static_assert(GQ <= 16, "q heads are the 16 columns of the QK product");
-  const int b = blockIdx.x / p.Hkv;
-  const int j = blockIdx.x % p.Hkv;
-  const int split = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, kb = lane >> 4;
-
-  __shared__ __align__(16) float pb[4][kPage][GQ];   // per wave: p[token][head]
-  __shared__ float wm[4][GQ], wl[4][GQ];
-  __shared__ float wo[4][GQ][D];
+  auto &pb = sh.pb;
+  auto &wm = sh.wm;
+  auto &wl = sh.wl;
+  auto &wo = sh.wo;
 
   // segment length and this wave's page id, then every load
   const int pgi = split * kBf16PagesPerSplit + w;     // page index in the table
@@ -122,11 +146,19 @@ __global__ __launch_bounds__(256) void k_bf16_seg(DecodeParams p, const uint16_t
       __builtin_memcpy(&qb[m], &v, 16);
     }
   }
+  // this step's token sits at offset noff of this wave's page (noff = -1: not here)
+  int noff = -1;
+  if (nt.slot != nullptr && live) {
+    const int ns = nt.slot[b];
+    noff = (ns >= 0 && (ns >> 4) == page) ? (ns & 15) : -1;
+  }
   v8bf ka[NM];
   uint32_t vraw[kPage];
   if (live) {
     const size_t base = ((page * p.Hkv + j) * kPage) * D;
-    const uint4 *kp = reinterpret_cast<const uint4 *>(p.bf16_k + base + (size_t)r16 * D + 8 * kb);
+    const uint16_t *krow = r16 == noff ? nt.k + ((size_t)b * p.Hkv + j) * D
+                                       : p.bf16_k + base + (size_t)r16 * D;
+    const uint4 *kp = reinterpret_cast<const uint4 *>(krow + 8 * kb);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const uint4 v = kp[4 * m];
@@ -137,6 +169,14 @@ __global__ __launch_bounds__(256) void k_bf16_seg(DecodeParams p, const uint16_t
     for (int tt = 0; tt < kPage; ++tt) {
       if constexpr (NCH == 2) vraw[tt] = reinterpret_cast<const uint32_t *>(vp)[(size_t)tt * (D / 2) + lane];
       else vraw[tt] = vp[(size_t)tt * D + lane];
+    }
+    if (noff >= 0) {
+      const uint16_t *vn = nt.v + ((size_t)b * p.Hkv + j) * D;
+      uint32_t x;
+      if constexpr (NCH == 2) x = reinterpret_cast<const uint32_t *>(vn)[lane];
+      else x = vn[lane];
+#pragma unroll
+      for (int tt = 0; tt < kPage; ++tt) vraw[tt] = tt == noff ? x : vraw[tt];
     }
   }
 
@@ -225,6 +265,13 @@ __global__ __launch_bounds__(256) void k_bf16_seg(DecodeParams p, const uint16_t
   }
 }
 
+template <int D, int GQ>
+__global__ __launch_bounds__(256) void k_bf16_seg(DecodeParams p, const uint16_t *__restrict__ q) {
+  __shared__ SegShared<D, GQ> sh;
+  bf16_seg_body<D, GQ>(p, q, blockIdx.x / p.Hkv, blockIdx.x % p.Hkv, blockIdx.y, threadIdx.x,
+                       NewTok{nullptr, nullptr, nullptr}, sh);
+}
+
 template <int D>
 static void launch_bf16_d(const DecodeParams &p, const uint16_t *q, hipStream_t s) {
   const dim3 grid(p.B * p.Hkv, kBf16Splits), blk(256);
@@ -239,6 +286,83 @@ static void launch_bf16_d(const DecodeParams &p, const uint16_t *q, hipStream_t 
 hipError_t launch_bf16_seg(const DecodeParams &p, const uint16_t *q, hipStream_t s) {
   if (p.D == 64) launch_bf16_d<64>(p, q, s);
   else launch_bf16_d<128>(p, q, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Decode-step prologue in one launch: every block is one of
+//   [B*Hkv*5]  BF16 segment chunk (b, j, split), reading this step's token
+//              from the k_new/v_new inputs at its slot,
+//   [B*Hkv]    demotion of sequence b's oldest recent token for KV head j (K
+//              and V halves of the block), then the store of head j of b's new
+//              token into its BF16 slot (after every read of the demoted slot),
+//   [B*Hq]     q . R_k of one (sequence, q head).
+// The three kinds are independent, so they run side by side instead of in four
+// dependent launches.
+// ---------------------------------------------------------------------------
+template <int D, int G, int GQ>
+__global__ __launch_bounds__(256) void k_step_pre(DecodeParams p, const uint16_t *__restrict__ q,
+                                                  const float *__restrict__ Rk, DemoteArgs da,
+                                                  NewTok nt) {
+  const int tid = threadIdx.x;
+  int bid = blockIdx.x;
+  const int nseg = p.B * p.Hkv * kBf16Splits;
+  if (bid < nseg) {
+    __shared__ SegShared<D, GQ> sh;
+    const int bj = bid / kBf16Splits;
+    bf16_seg_body<D, GQ>(p, q, bj / p.Hkv, bj % p.Hkv, bid % kBf16Splits, tid, nt, sh);
+    return;
+  }
+  bid -= nseg;
+  const int ndem = p.B * p.Hkv;
+  if (bid < ndem) {
+    __shared__ DemoteShared<D, 1> sh;
+    const int b = bid / p.Hkv, j = bid % p.Hkv;
+    demote_body<D, G, 1>(da, b, j, tid / D, tid % D, tid < 2 * D, sh);
+    // the demoted slot has been read (demote_body's second barrier); b's new
+    // token may reuse it
+    const int ns = nt.slot[b];
+    if (ns >= 0 && (ns >> 4) < p.num_bf16_pages && tid < 2 * (D / 8)) {
+      const bool isv = tid >= D / 8;
+      const int c8 = tid % (D / 8);
+      const int64_t page = ns >> 4, off = ns & 15;
+      const uint4 *src = reinterpret_cast<const uint4 *>((isv ? nt.v : nt.k) + ((size_t)b * p.Hkv + j) * D);
+      uint4 *dst = reinterpret_cast<uint4 *>(const_cast<uint16_t *>(isv ? p.bf16_v : p.bf16_k) +
+                                             ((page * p.Hkv + j) * kPage + off) * D);
+      dst[c8] = src[c8];
+    }
+    return;
+  }
+  bid -= ndem;
+  __shared__ QrotShared<D> sh;
+  qrot_body<D>(p, q, Rk, bid, tid, sh);
+}
+
+template <int D, int G>
+static void launch_step_pre_dg(const DecodeParams &p, const uint16_t *q, const float *Rk,
+                               const DemoteArgs &da, const NewTok &nt, hipStream_t s) {
+  const dim3 grid(p.B * p.Hkv * kBf16Splits + p.B * p.Hkv + p.B * p.Hq), blk(256);
+  switch (p.g) {
+    case 1: hipLaunchKernelGGL((k_step_pre<D, G, 1>), grid, blk, 0, s, p, q, Rk, da, nt); break;
+    case 2: hipLaunchKernelGGL((k_step_pre<D, G, 2>), grid, blk, 0, s, p, q, Rk, da, nt); break;
+    case 4: hipLaunchKernelGGL((k_step_pre<D, G, 4>), grid, blk, 0, s, p, q, Rk, da, nt); break;
+    default: hipLaunchKernelGGL((k_step_pre<D, G, 8>), grid, blk, 0, s, p, q, Rk, da, nt); break;
+  }
+}
+
+hipError_t launch_step_pre(const DecodeParams &p, const oscar_cache &c, const uint16_t *q,
+                           const float *Rk, const float *Rv, const float *ck, const float *cv,
+                           const int32_t *dsrc, const int32_t *ddst, const int32_t *new_slot,
+                           const uint16_t *k_new, const uint16_t *v_new, hipStream_t s) {
+  const DemoteArgs da = demote_args(c, p.B, dsrc, ddst, Rk, Rv, ck, cv);
+  const NewTok nt{new_slot, k_new, v_new};
+  const int D = p.D, G = p.G;
+  if (D == 64 && G == 32) launch_step_pre_dg<64, 32>(p, q, Rk, da, nt, s);
+  else if (D == 64 && G == 64) launch_step_pre_dg<64, 64>(p, q, Rk, da, nt, s);
+  else if (D == 128 && G == 32) launch_step_pre_dg<128, 32>(p, q, Rk, da, nt, s);
+  else if (D == 128 && G == 64) launch_step_pre_dg<128, 64>(p, q, Rk, da, nt, s);
+  else if (D == 128 && G == 128) launch_step_pre_dg<128, 128>(p, q, Rk, da, nt, s);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -28,6 +28,8 @@ class DeviceRun:
     lse: np.ndarray       # [B][Hq]
     pool: np.ndarray      # INT2 pool bytes [pages][Hkv][rec]
     hist_len: np.ndarray  # per sequence after the steps
+    bf16_k: np.ndarray = None   # BF16 pools after the steps
+    bf16_v: np.ndarray = None
 
 
 def hist_capacity_pages(L: int, steps: int) -> int:
@@ -36,10 +38,11 @@ def hist_capacity_pages(L: int, steps: int) -> int:
 
 
 def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_splits=0,
-                   R_v_none=False, head_map=None, device="cuda", seed_perm=None):
+                   R_v_none=False, head_map=None, device="cuda", seed_perm=None, fused=False):
     """Build the initial split cache of every sequence, run `steps` decode steps
-    (demote oldest recent -> write new token -> attend -> merge), return the
-    outputs of the last step and the INT2 pool."""
+    (demote oldest recent -> write new token -> attend -> merge; with fused,
+    through the single oscar_decode_step call), return the outputs of the last
+    step and the INT2 pool."""
     import torch
     from int2_rotated_kv_amd import binding as ob
     from int2_rotated_kv_amd.splitcache import SplitCache
@@ -75,20 +78,25 @@ def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_sp
     lse = torch.zeros((B, wl.Hq), dtype=torch.float32, device=device)
     for st in range(steps):
         dsrc, ddst, wdst = sc.plan_step()
-        ob.demote_pack(sc.cache, torch.from_numpy(dsrc).to(device), torch.from_numpy(ddst).to(device),
-                       Rk, Rv, ck, cv)
         newk = np.stack([inp.K[b][wl.lengths[b] + st] for b in range(B)])
         newv = np.stack([inp.V[b][wl.lengths[b] + st] for b in range(B)])
-        ob.write_bf16(sc.cache, torch.from_numpy(wdst).to(device),
-                      to_dev_bf16(newk).view(torch.int16), to_dev_bf16(newv).view(torch.int16))
+        kn, vn = to_dev_bf16(newk).view(torch.int16), to_dev_bf16(newv).view(torch.int16)
+        d_src, d_dst, d_w = (torch.from_numpy(x).to(device) for x in (dsrc, ddst, wdst))
+        q = to_dev_bf16(inp.q[st]).view(torch.int16)
+        if not fused:
+            ob.demote_pack(sc.cache, d_src, d_dst, Rk, Rv, ck, cv)
+            ob.write_bf16(sc.cache, d_w, kn, vn)
         sc.commit_step()
         sc.sync_lengths()
         args = sc.decode_args(kv_head_of_q=head_map, num_splits=num_splits, int2_kernel=int2_kernel)
-        q = to_dev_bf16(inp.q[st])
-        ob.decode(sc.cache, args, q.view(torch.int16), Rk, Rv, out, lse)
+        if fused:
+            ws = ob.alloc_workspace(sc.cache, args, device=q.device)
+            ob.decode_step(sc.cache, args, d_src, d_dst, ck, cv, d_w, kn, vn, q, Rk, Rv, ws, out, lse)
+        else:
+            ob.decode(sc.cache, args, q, Rk, Rv, out, lse)
     torch.cuda.synchronize()
     return DeviceRun(sc, out.cpu().numpy(), lse.cpu().numpy(), sc.cache.int2.cpu().numpy(),
-                     sc.hist_len_h.copy())
+                     sc.hist_len_h.copy(), sc.cache.bf16_k.cpu().numpy(), sc.cache.bf16_v.cpu().numpy())
 
 
 def oracle_step(inp: synth.SmallInputs, steps: int = 1, R_v_none=False, head_map=None,

@@ -230,3 +230,30 @@ def test_bf16_history_needs_no_rotation():
     a = _args()
     st = ob.lib().oscar_decode_attn(ctypes.byref(c), ctypes.byref(a), 0x80000, None, 0x90000, 16, None)
     assert st == ob.OSCAR_EINVAL and "R_k" in ob.last_error()
+
+
+def _step(c, a, **kw):
+    p = dict(demote_src=0x1000, demote_dst=0x1100, clip_k=0x1200, clip_v=0x1300, new_slot=0x1400,
+             k_new=0x1500, v_new=0x1600, q=0x1700, R_k=0x1800, R_v=0x1900, ws=0x2000, ws_bytes=16,
+             out=0x2100, lse=0x2200)
+    p.update(kw)
+    return ob.lib().oscar_decode_step(ctypes.byref(c), ctypes.byref(a), p["demote_src"], p["demote_dst"],
+                                      p["clip_k"], p["clip_v"], p["new_slot"], p["k_new"], p["v_new"],
+                                      p["q"], p["R_k"], p["R_v"], p["ws"], p["ws_bytes"], p["out"],
+                                      p["lse"], None)
+
+
+def test_decode_step_argument_checks():
+    """oscar_decode_step validates everything on the host before launching
+    (all of these fail before any pointer is dereferenced)."""
+    c, a = _cache(), _args()
+    assert _step(c, a) == ob.OSCAR_EWORKSPACE
+    assert _step(c, a, new_slot=None) == ob.OSCAR_EINVAL
+    assert _step(c, a, demote_src=None) == ob.OSCAR_EINVAL
+    assert _step(c, a, clip_v=None) == ob.OSCAR_EINVAL
+    assert _step(c, a, k_new=0x1501) == ob.OSCAR_EINVAL and "k_new" in ob.last_error()
+    assert _step(c, a, R_k=None) == ob.OSCAR_EINVAL and "R_k" in ob.last_error()
+    assert _step(c, a, out=None) == ob.OSCAR_EINVAL
+    assert _step(c, _args(phases=ob.PHASE_INT2)) == ob.OSCAR_EINVAL and "phases" in ob.last_error()
+    assert _step(c, _args(int2_kernel=ob.HISTORY_BF16)) == ob.OSCAR_EUNSUPPORTED
+    assert _step(c, _args(phases=ob.PHASE_ALL)) == ob.OSCAR_EWORKSPACE

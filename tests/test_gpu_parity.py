@@ -133,3 +133,40 @@ def test_bf16_history_comparison(shape, splits):
         e = sh.row_rel_err(out[b].astype(np.float64), r["out"])
         assert np.all(e <= TOL), f"seq {b}: row errors {np.sort(e)[-4:]}"
         assert np.abs(lse[b] - r["lse"]).max() < 1e-3
+
+
+@pytest.mark.parametrize("shape", ["tiny", "edge", "d128g4", "d128g8"])
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_fused_step_matches_separate_calls(shape, kernel):
+    """oscar_decode_step over several steps gives the same INT2 and BF16 pool
+    bytes, bit for bit, and the same outputs as demote_pack + write_bf16 +
+    decode_attn + merge; and matches the oracle."""
+    _say("case: fused step", shape, "kernel", kernel)
+    if shape == "tiny":
+        wl = synth.workload("tiny", B=2, lengths=(1024, 777), steps=3, seed=31)
+    elif shape == "edge":
+        wl = synth.workload("tiny", B=5, Hkv=2, Hq=8, lengths=(10, 64, 320, 321, 400), steps=3, seed=32)
+    elif shape == "d128g4":
+        wl = synth.workload("tiny", B=2, Hkv=2, Hq=8, D=128, G=64, lengths=(3000, 1700), steps=3, seed=33)
+    else:
+        wl = synth.workload("tiny", B=2, Hkv=2, Hq=16, D=128, G=128, lengths=(2500, 999), steps=3, seed=34)
+    if kernel == 2 and wl.g not in (4, 8):
+        pytest.skip("matrix-core kernel needs 4 or 8 q heads per KV head")
+    inp = synth.make_small(wl, distinct_rv=True)
+    sep = sh.build_and_step(inp, steps=3, int2_kernel=kernel)
+    fus = sh.build_and_step(inp, steps=3, int2_kernel=kernel, fused=True)
+    assert np.array_equal(sep.pool, fus.pool), "INT2 pools differ"
+    assert np.array_equal(sep.bf16_k, fus.bf16_k) and np.array_equal(sep.bf16_v, fus.bf16_v), \
+        "BF16 pools differ"
+    if kernel == 1:
+        # static chunks: the same arithmetic in the same order
+        assert np.array_equal(sep.out.view(np.uint32), fus.out.view(np.uint32)), "outputs differ"
+        assert np.array_equal(sep.lse.view(np.uint32), fus.lse.view(np.uint32)), "lse differ"
+    else:
+        # the matrix-core kernel's waves share a part's pages dynamically, so
+        # two runs may sum in a different fp32 order
+        e = sh.row_rel_err(fus.out.astype(np.float64), sep.out.astype(np.float64))
+        assert e.max() < 1e-5 and np.abs(fus.lse - sep.lse).max() < 1e-5
+    ref = sh.oracle_step(inp, steps=3)
+    _check_bytes(fus, inp, ref)
+    _check_out(fus, ref)
