@@ -2,12 +2,13 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--int2-kernel auto|valu|mfma]
 
-One step = the whole hot path for every sequence of the batch: demote the
-oldest recent token into the INT2 history (oscar_demote_pack), write the new
-token into the freed BF16 slot (oscar_write_bf16), attend both segments
-(oscar_decode_attn: query rotation, BF16 segment, INT2 history chunks) and
-merge (oscar_merge).  Inputs are synthetic and already resident in HBM when
-timing starts.  Prints ONE JSON line.
+One step = the whole hot path for every sequence of the batch, one
+oscar_decode_step call: demote the oldest recent token into the INT2 history,
+write the new token into the freed BF16 slot, attend both segments (query
+rotation, BF16 segment, INT2 history chunks) and merge.  The same steps
+through the four separate entry points (oscar_demote_pack, oscar_write_bf16,
+oscar_decode_attn, oscar_merge) are timed alongside.  Inputs are synthetic and
+already resident in HBM when timing starts.  Prints ONE JSON line.
 
 The default workload is the Qwen3-8B-shaped batch-32 cache at ~100K context
 (8 KV heads, 32 q heads, head_dim 128, INT2 group 64, lengths uniform in
@@ -142,19 +143,23 @@ def step_args(st, s: int, int2_kernel: int, num_splits: int = 0):
 
 
 def breakdown_steps(steps):
-    """Extra steps run after the timed ones with an event between phases."""
-    return min(steps, 20)
+    """Extra steps run after the timed ones: as many through the separate
+    entry points with nothing else on the stream, then as many again with an
+    event between phases."""
+    return 2 * min(steps, 20)
 
 
 def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0):
-    """Warmup steps, then `steps` timed steps through the plain entry points
-    (demote_pack, write_bf16, one decode_attn, merge) with nothing else on the
-    stream, then breakdown_steps(steps) more with events between the phases
-    (decode_attn split into its QROT|BF16 and INT2 phases)."""
+    """Warmup steps, then `steps` timed steps through oscar_decode_step with
+    nothing else on the stream; then min(steps, 20) steps through the separate
+    entry points (demote_pack, write_bf16, decode_attn, merge), timed the same
+    way, and as many again with events between the phases (decode_attn split
+    into its QROT|BF16 and INT2 phases)."""
     import torch
     from int2_rotated_kv_amd import binding as ob
-    E = breakdown_steps(steps)
-    T = steps + warmup + E
+    E2 = breakdown_steps(steps)
+    E = E2 // 2
+    T = steps + warmup + E2
     args = [step_args(st, s, int2_kernel, num_splits) for s in range(T)]
     a_qb = [a.with_phases(ob.PHASE_QROT | ob.PHASE_BF16) for a in args]
     a_i2 = [a.with_phases(ob.PHASE_INT2) for a in args]
@@ -167,6 +172,10 @@ def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0
     cache = st.sc.cache
 
     def one(s):
+        ob.decode_step(cache, args[s], st.dsrc[s], st.ddst[s], st.ck, st.cv, st.wdst[s],
+                       st.knew[s], st.vnew[s], st.q[s], st.Rk, st.Rv, ws, out, lse)
+
+    def one_separate(s):
         ob.demote_pack(cache, st.dsrc[s], st.ddst[s], st.Rk, st.Rv, st.ck, st.cv)
         ob.write_bf16(cache, st.wdst[s], st.knew[s], st.vnew[s])
         ob.decode_attn(cache, args[s], st.q[s], st.Rk, ws)
@@ -195,8 +204,13 @@ def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0
         one(warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    t0 = time.perf_counter()
     for i in range(E):
-        one_phased(warmup + steps + i, ev[i])
+        one_separate(warmup + steps + i)
+    torch.cuda.synchronize()
+    wall_sep = time.perf_counter() - t0
+    for i in range(E):
+        one_phased(warmup + steps + E + i, ev[i])
     torch.cuda.synchronize()
     seg = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in ev]).reshape(E, 4)  # ms
     # the INT2 kernel alone: back-to-back launches of the last step's INT2 phase
@@ -211,7 +225,8 @@ def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0
     torch.cuda.synchronize()
     int2_only_ms = e0.elapsed_time(e1) / n_i2
     return dict(wall_s=wall, seg_ms=seg, first_out=first_out, out=out, args=args,
-                int2_only_ms=int2_only_ms, int2_only_step=T - 1)
+                int2_only_ms=int2_only_ms, int2_only_step=T - 1,
+                ms_separate=1000.0 * wall_sep / E if E else float("nan"))
 
 
 def run_steps_bf16(st, steps, warmup):
@@ -428,8 +443,8 @@ def traffic_from_profile(kernel_name: str, workload: str):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3-8b-b32-100k")
     ap.add_argument("--int2-kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -499,6 +514,7 @@ def main(argv=None):
                    "splits": splits, "parallelism": "single-gpu"},
         "hbm_tbps": step_bytes / (ms_step * 1e-3) / 1e12,
         "hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "ms_per_step_separate_calls": r["ms_separate"],
         "step_ms_breakdown": {"demote+write": float(seg[:, 0].mean()), "qrot+bf16": float(seg[:, 1].mean()),
                               "int2": int2_ms, "merge": float(seg[:, 3].mean())},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -245,6 +245,148 @@ __device__ __forceinline__ void demote_body(const DemoteArgs &a, int e0, int j, 
   }
 }
 
+template <int D>
+struct DemoteOneShared {
+  double ks[D];                        // the token's source values
+  double part[256 / (D / 4)][D];       // row-group partial sums of k . R
+  double red_mx[2], red_mn[2];         // per wave, groups wider than a wave
+  int src, dst;
+};
+
+// Demotion of one entry e of the slot lists for KV head j, K (half 0) or V
+// (half 1), by a block of 256 threads.  The rotation x = k . R is split like
+// the query rotation: thread (row group gi, column quad c4) sums rows
+// gi*RPG .. +RPG-1 for columns 4*c4 .. +3 (fp64 fma chain, its R loads issued
+// before the token is read), the row groups are added in order in LDS; then
+// threads c < D own channel c.  Every thread must call it (it has block
+// barriers); it returns once the entry's bytes are written, after every read
+// of the source slot.
+template <int D, int G>
+__device__ __forceinline__ void demote_one_body(const DemoteArgs &a, int e, int j, int half, int tid,
+                                                DemoteOneShared<D> &sh) {
+#pragma clang fp contract(off)
+  constexpr RecLayout RL(D, G);
+  constexpr int NC4 = D / 4;           // column quads
+  constexpr int NGR = 256 / NC4;       // row groups
+  constexpr int RPG = D / NGR;         // rows per group
+  constexpr int GW = G < 64 ? G : 64;  // lanes of a group inside one wave
+  const bool isv = half != 0;
+  const float *R = isv ? a.Rv : a.Rk;
+  const int c4 = tid % NC4, gi = tid / NC4;
+  float4 r[RPG];
+  if (R != nullptr) {
+    const float4 *Rp = reinterpret_cast<const float4 *>(R + (size_t)j * D * D) + c4;
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) r[i] = Rp[(size_t)(gi * RPG + i) * NC4];
+  }
+  if (tid == 0) {
+    int sv = -1, dv = -1;
+    if (e < a.n) { sv = a.src[e]; dv = a.dst[e]; }
+    // entries with a negative or out-of-range slot are skipped
+    if (sv < 0 || dv < 0 || (sv >> 4) >= a.n_bf16_pages || (dv >> 4) >= a.n_int2_pages) {
+      sv = -1;
+      dv = -1;
+    }
+    sh.src = sv;
+    sh.dst = dv;
+  }
+  __syncthreads();
+  const int s = sh.src, d = sh.dst;
+  if (d < 0) return;                   // uniform over the block
+  if (tid < D) {
+    const uint16_t *bf = isv ? a.bf_v : a.bf_k;
+    const int64_t page = s >> 4, off = s & 15;
+    sh.ks[tid] = (double)bf16_to_f32(bf[((page * a.Hkv + j) * kPage + off) * D + tid]);
+  }
+  __syncthreads();
+
+  double x = 0.0;
+  if (R != nullptr) {
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    // the R values are widened one row at a time, next to their use (the
+    // ordered conversions keep 4 doubles live instead of RPG*4)
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const double ki = sh.ks[gi * RPG + i];
+      double rx, ry, rz, rw;
+      asm volatile("v_cvt_f64_f32 %0, %1" : "=v"(rx) : "v"(r[i].x));
+      asm volatile("v_cvt_f64_f32 %0, %1" : "=v"(ry) : "v"(r[i].y));
+      asm volatile("v_cvt_f64_f32 %0, %1" : "=v"(rz) : "v"(r[i].z));
+      asm volatile("v_cvt_f64_f32 %0, %1" : "=v"(rw) : "v"(r[i].w));
+      a0 = fma(ki, rx, a0);
+      a1 = fma(ki, ry, a1);
+      a2 = fma(ki, rz, a2);
+      a3 = fma(ki, rw, a3);
+    }
+    sh.part[gi][4 * c4 + 0] = a0;
+    sh.part[gi][4 * c4 + 1] = a1;
+    sh.part[gi][4 * c4 + 2] = a2;
+    sh.part[gi][4 * c4 + 3] = a3;
+    __syncthreads();
+    if (tid < D) {
+#pragma unroll
+      for (int g2 = 0; g2 < NGR; ++g2) x += sh.part[g2][tid];
+    }
+  } else if (tid < D) {
+    x = sh.ks[tid];
+  }
+
+  // group max / min (threads c < D: whole waves)
+  const int c = tid;
+  double mx = x, mn = x;
+  if (c < D) {
+#pragma unroll
+    for (int o = 1; o < GW; o <<= 1) {
+      mx = fmax(mx, __shfl_xor(mx, o));
+      mn = fmin(mn, __shfl_xor(mn, o));
+    }
+  }
+  if constexpr (G > 64) {
+    if (c < D && (c & 63) == 0) { sh.red_mx[c >> 6] = mx; sh.red_mn[c >> 6] = mn; }
+    __syncthreads();
+    mx = fmax(sh.red_mx[0], sh.red_mx[1]);
+    mn = fmin(sh.red_mn[0], sh.red_mn[1]);
+  }
+  if (c >= D) return;
+
+  const double clip = (double)(isv ? a.clip_v[j] : a.clip_k[j]);
+  const double hi = clip * mx;
+  const double lo = clip * mn;
+  const double scale = (hi - lo) / 3.0;
+  const uint16_t sb = f64_to_bf16_rne(scale);
+  const uint16_t zb = f64_to_bf16_rne(lo);
+  const double sd = (double)bf16_to_f32(sb);
+  const double zd = (double)bf16_to_f32(zb);
+  uint32_t code = 0;
+  if (sd != 0.0) {
+    double qv = rint((x - zd) / sd);
+    qv = fmin(fmax(qv, 0.0), 3.0);
+    code = (uint32_t)qv;
+  }
+  const int64_t page = d >> 4, off = d & 15;
+  uint8_t *rec = a.pool + ((size_t)page * a.Hkv + j) * RL.bytes();
+  if ((c % G) == 0) {
+    const int o = isv ? RL.vsz((int)off, c / G) : RL.ksz((int)off, c / G);
+    *reinterpret_cast<uint32_t *>(rec + o) = (uint32_t)sb | ((uint32_t)zb << 16);
+  }
+  if (!isv) {
+    // K: word blk of lane slot 16*kb + t holds channels 64*blk + 16*kb + i of
+    // token t at bits 2i
+    const int kb = (c & 63) >> 4, blk = c >> 6;
+    uint32_t w = code << (2 * (c & 15));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) w |= __shfl_xor(w, o);
+    if ((c & 15) == 0) *reinterpret_cast<uint32_t *>(rec + RL.kword(16 * kb + (int)off, blk)) = w;
+  } else {
+    // V: channel-major, one dword per channel holds the 16 tokens of a page;
+    // this token's two bits only
+    uint32_t *wp = reinterpret_cast<uint32_t *>(rec + RL.vword(c & 63, c >> 6));
+    const int shf = 2 * (int)off;
+    atomicAnd(wp, ~(3u << shf));
+    atomicOr(wp, code << shf);
+  }
+}
+
 DemoteArgs demote_args(const oscar_cache &c, int n, const int32_t *src, const int32_t *dst,
                        const float *Rk, const float *Rv, const float *ck, const float *cv);
 

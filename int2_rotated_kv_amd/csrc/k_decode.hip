@@ -293,9 +293,9 @@ hipError_t launch_bf16_seg(const DecodeParams &p, const uint16_t *q, hipStream_t
 // Decode-step prologue in one launch: every block is one of
 //   [B*Hkv*5]  BF16 segment chunk (b, j, split), reading this step's token
 //              from the k_new/v_new inputs at its slot,
-//   [B*Hkv]    demotion of sequence b's oldest recent token for KV head j (K
-//              and V halves of the block), then the store of head j of b's new
-//              token into its BF16 slot (after every read of the demoted slot),
+//   [B*Hkv*2]  demotion of sequence b's oldest recent token for KV head j, K
+//              or V, then the store of that half of head j of b's new token
+//              into its BF16 slot (after every read of the demoted slot),
 //   [B*Hq]     q . R_k of one (sequence, q head).
 // The three kinds are independent, so they run side by side instead of in four
 // dependent launches.
@@ -314,17 +314,18 @@ __global__ __launch_bounds__(256) void k_step_pre(DecodeParams p, const uint16_t
     return;
   }
   bid -= nseg;
-  const int ndem = p.B * p.Hkv;
+  const int ndem = p.B * p.Hkv * 2;
   if (bid < ndem) {
-    __shared__ DemoteShared<D, 1> sh;
-    const int b = bid / p.Hkv, j = bid % p.Hkv;
-    demote_body<D, G, 1>(da, b, j, tid / D, tid % D, tid < 2 * D, sh);
-    // the demoted slot has been read (demote_body's second barrier); b's new
+    __shared__ DemoteOneShared<D> sh;
+    const int b = bid / (2 * p.Hkv), j = (bid / 2) % p.Hkv, half = bid % 2;
+    demote_one_body<D, G>(da, b, j, half, tid, sh);
+    __syncthreads();
+    // every read of the demoted slot (this half of head j) is done; b's new
     // token may reuse it
     const int ns = nt.slot[b];
-    if (ns >= 0 && (ns >> 4) < p.num_bf16_pages && tid < 2 * (D / 8)) {
-      const bool isv = tid >= D / 8;
-      const int c8 = tid % (D / 8);
+    if (ns >= 0 && (ns >> 4) < p.num_bf16_pages && tid < D / 8) {
+      const bool isv = half != 0;
+      const int c8 = tid;
       const int64_t page = ns >> 4, off = ns & 15;
       const uint4 *src = reinterpret_cast<const uint4 *>((isv ? nt.v : nt.k) + ((size_t)b * p.Hkv + j) * D);
       uint4 *dst = reinterpret_cast<uint4 *>(const_cast<uint16_t *>(isv ? p.bf16_v : p.bf16_k) +
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(256) void k_step_pre(DecodeParams p, const uint16_t
 template <int D, int G>
 static void launch_step_pre_dg(const DecodeParams &p, const uint16_t *q, const float *Rk,
                                const DemoteArgs &da, const NewTok &nt, hipStream_t s) {
-  const dim3 grid(p.B * p.Hkv * kBf16Splits + p.B * p.Hkv + p.B * p.Hq), blk(256);
+  const dim3 grid(p.B * p.Hkv * kBf16Splits + p.B * p.Hkv * 2 + p.B * p.Hq), blk(256);
   switch (p.g) {
     case 1: hipLaunchKernelGGL((k_step_pre<D, G, 1>), grid, blk, 0, s, p, q, Rk, da, nt); break;
     case 2: hipLaunchKernelGGL((k_step_pre<D, G, 2>), grid, blk, 0, s, p, q, Rk, da, nt); break;

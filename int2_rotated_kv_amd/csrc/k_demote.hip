@@ -13,6 +13,14 @@ __global__ __launch_bounds__(D) void k_demote(DemoteArgs a) {
   demote_body<D, G, T>(a, blockIdx.x * T, blockIdx.y, blockIdx.z, threadIdx.x, true, sh);
 }
 
+// The few tokens of a decode step: one (entry, KV head, K|V) per block of 256
+// threads (the body the fused decode-step kernel uses as well).
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_demote_one(DemoteArgs a) {
+  __shared__ DemoteOneShared<D> sh;
+  demote_one_body<D, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, sh);
+}
+
 __global__ void k_write_bf16(uint16_t *__restrict__ pk, uint16_t *__restrict__ pv, int Hkv, int D,
                              int64_t n_pages, const int32_t *__restrict__ dst,
                              const uint16_t *__restrict__ kn, const uint16_t *__restrict__ vn) {
@@ -42,7 +50,7 @@ static void launch_demote_t(const DemoteArgs &a, hipStream_t s) {
   // few tokens (a decode step): one token per block for parallelism; bulk
   // fills: 16 tokens per block so every R load serves 16 dot products
   if ((a.n + 15) / 16 * a.Hkv * 2 < 1024) {
-    hipLaunchKernelGGL((k_demote<D, G, 1>), dim3(a.n, a.Hkv, 2), dim3(D), 0, s, a);
+    hipLaunchKernelGGL((k_demote_one<D, G>), dim3(a.n, a.Hkv, 2), dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL((k_demote<D, G, 16>), dim3((a.n + 15) / 16, a.Hkv, 2), dim3(D), 0, s, a);
   }

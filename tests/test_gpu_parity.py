@@ -163,10 +163,11 @@ def test_fused_step_matches_separate_calls(shape, kernel):
         assert np.array_equal(sep.out.view(np.uint32), fus.out.view(np.uint32)), "outputs differ"
         assert np.array_equal(sep.lse.view(np.uint32), fus.lse.view(np.uint32)), "lse differ"
     else:
-        # the matrix-core kernel's waves share a part's pages dynamically, so
-        # two runs may sum in a different fp32 order
+        # the matrix-core kernel's waves share a part's pages dynamically:
+        # two runs sum in a different order, and the f16 PV weights are
+        # rounded relative to the running max at the time a page is taken
         e = sh.row_rel_err(fus.out.astype(np.float64), sep.out.astype(np.float64))
-        assert e.max() < 1e-5 and np.abs(fus.lse - sep.lse).max() < 1e-5
+        assert e.max() < 5e-4 and np.abs(fus.lse - sep.lse).max() < 1e-4
     ref = sh.oracle_step(inp, steps=3)
     _check_bytes(fus, inp, ref)
     _check_out(fus, ref)
