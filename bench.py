@@ -149,17 +149,23 @@ def breakdown_steps(steps):
     return 2 * min(steps, 20)
 
 
-def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0):
+COLD_SCRATCH = 512 << 20   # bytes written between cold steps (> the 256 MB last-level cache)
+
+
+def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0, cold_steps=0):
     """Warmup steps, then `steps` timed steps through oscar_decode_step with
     nothing else on the stream; then min(steps, 20) steps through the separate
     entry points (demote_pack, write_bf16, decode_attn, merge), timed the same
     way, and as many again with events between the phases (decode_attn split
-    into its QROT|BF16 and INT2 phases)."""
+    into its QROT|BF16 and INT2 phases).  With cold_steps, that many more
+    steps each preceded by a 512 MiB scratch write (nothing of the cache left
+    in any cache level), timed by events around the step alone."""
     import torch
     from int2_rotated_kv_amd import binding as ob
     E2 = breakdown_steps(steps)
     E = E2 // 2
-    T = steps + warmup + E2
+    T_hot = steps + warmup + E2
+    T = T_hot + 2 * cold_steps
     args = [step_args(st, s, int2_kernel, num_splits) for s in range(T)]
     a_qb = [a.with_phases(ob.PHASE_QROT | ob.PHASE_BF16) for a in args]
     a_i2 = [a.with_phases(ob.PHASE_INT2) for a in args]
@@ -220,13 +226,43 @@ def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(n_i2):
-        ob.decode_attn(cache, a_i2[T - 1], st.q[T - 1], st.Rk, ws)
+        ob.decode_attn(cache, a_i2[T_hot - 1], st.q[T_hot - 1], st.Rk, ws)
     e1.record()
     torch.cuda.synchronize()
     int2_only_ms = e0.elapsed_time(e1) / n_i2
-    return dict(wall_s=wall, seg_ms=seg, first_out=first_out, out=out, args=args,
-                int2_only_ms=int2_only_ms, int2_only_step=T - 1,
-                ms_separate=1000.0 * wall_sep / E if E else float("nan"))
+    res = dict(wall_s=wall, seg_ms=seg, first_out=first_out, out=out, args=args,
+               int2_only_ms=int2_only_ms, int2_only_step=T_hot - 1,
+               ms_separate=1000.0 * wall_sep / E if E else float("nan"))
+    if cold_steps:
+        # two cache-cold protocols, cold_steps steps each: 512 MiB of scratch
+        # read (clean eviction, as other layers' caches and weights do) or
+        # written (dirty eviction) on the stream before every step
+        scratch = torch.ones(COLD_SCRATCH // 4, dtype=torch.int32, device=st.q.device)
+        flush = {"read": lambda i: scratch.sum(), "write": lambda i: scratch.fill_(i)}
+        for k, (name, fl) in enumerate(flush.items()):
+            base = T_hot + k * cold_steps
+            ec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(cold_steps)]
+            for i in range(cold_steps):
+                fl(i)
+                ec[i][0].record()
+                one(base + i)
+                ec[i][1].record()
+            torch.cuda.synchronize()
+            last = base + cold_steps - 1
+            ci = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(10)]
+            for i in range(10):
+                fl(i)
+                ci[i][0].record()
+                ob.decode_attn(cache, a_i2[last], st.q[last], st.Rk, ws)
+                ci[i][1].record()
+            torch.cuda.synchronize()
+            res[f"cold_{name}"] = dict(
+                ms=float(np.mean([a.elapsed_time(b) for a, b in ec])),
+                int2_ms=float(np.mean([a.elapsed_time(b) for a, b in ci])),
+                int2_step=last, steps=range(base, base + cold_steps))
+    return res
 
 
 def run_steps_bf16(st, steps, warmup):
@@ -451,6 +487,10 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=0,
                     help="history chunks per (sequence, KV head); 0 = the library's choice")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cold", action="store_true",
+                    help="also time --steps steps each preceded by a 512 MiB scratch read, and "
+                         "as many preceded by a 512 MiB scratch write (cache-cold protocols for "
+                         "caches that fit the last-level cache)")
     ap.add_argument("--no-bf16-compare", action="store_true",
                     help="skip the comparison run over the same tokens with the whole "
                          "history kept in BF16 pages")
@@ -476,11 +516,12 @@ def main(argv=None):
         return
     kern = {"auto": ob.INT2_AUTO, "valu": ob.INT2_VALU, "mfma": ob.INT2_MFMA}[a.int2_kernel]
     torch.cuda.set_device(0)
-    st = build_workload(a.workload, a.steps + a.warmup + breakdown_steps(a.steps), log=log,
-                        bf16_history=not a.no_bf16_compare)
+    cold_steps = a.steps if a.cold else 0
+    st = build_workload(a.workload, a.steps + a.warmup + breakdown_steps(a.steps) + 2 * cold_steps,
+                        log=log, bf16_history=not a.no_bf16_compare)
     wl = st.wl
     r = run_steps(st, a.steps, a.warmup, kern, keep_first_out=not a.no_cpu_baseline,
-                  num_splits=a.splits)
+                  num_splits=a.splits, cold_steps=cold_steps)
     log(f"[bench] timed {a.steps} steps in {r['wall_s']:.3f}s")
 
     # per-step quantities over the timed steps
@@ -522,6 +563,20 @@ def main(argv=None):
                      "traffic": tr, "kernel": kname,
                      "alg_bytes_per_launch": i2_last, "launch_ms": r["int2_only_ms"]},
     }
+    if cold_steps:
+        for name in ("read", "write"):
+            c = r[f"cold_{name}"]
+            i2c = int2_alg_bytes(wl, st.hl_h[c["int2_step"]], splits)[0]
+            kv_c = np.mean([int(st.hl_h[s].sum() + st.bl_h[s].sum()) * wl.Hkv for s in c["steps"]])
+            out[f"cold_{name}"] = {
+                "ms_per_step": c["ms"], "value": kv_c / (c["ms"] * 1e-3),
+                "int2_kernel_ms": c["int2_ms"],
+                "int2_achieved_GBs": i2c / (c["int2_ms"] * 1e-3) / 1e9,
+                "int2_frac": i2c / (c["int2_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "protocol": f"each step (and each INT2 launch) preceded by a 512 MiB scratch {name} "
+                            "on the stream; HIP events around the step (launch) alone",
+            }
+            log(f"[bench] cold ({name}): {c['ms']:.4f} ms/step, INT2 {c['int2_ms'] * 1000:.1f} us")
     if not a.no_bf16_compare:
         rb = run_steps_bf16(st, a.steps, a.warmup)
         ms_b = 1000.0 * rb["wall_s"] / a.steps

@@ -182,6 +182,11 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   const size_t BH = (size_t)a->batch * a->num_q_heads;
   size_t off = 0;
   L.qrot = off; off = align256(off + BH * p->D * 4);
+  const bool mf = p->int2_kind == OSCAR_INT2_MFMA;
+  L.qpk = off;
+  off = align256(off + (mf ? (size_t)a->batch * c->num_kv_heads * (p->g / 4) *
+                                 mfma_qk_steps(p->D, p->G) * 64 * 4 * 4 : 0));
+  L.qhd = off; off = align256(off + (mf ? BH * 8 * 4 : 0));
   L.part_o = off; off = align256(off + BH * S * p->D * 4);
   L.part_ml = off; off = align256(off + BH * S * 2 * 4);
   L.bf_o = off; off = align256(off + BH * kBf16Splits * p->D * 4);

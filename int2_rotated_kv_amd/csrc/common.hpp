@@ -23,6 +23,9 @@ constexpr int kMfmaTargetBlocks = 256;          // its default grid: one block p
 __host__ __device__ constexpr int mfma_heads_per_block(int hkv) {
   return hkv >= 8 ? 8 : hkv > 4 ? 8 : hkv > 2 ? 4 : hkv > 1 ? 2 : 1;
 }
+// QK matrix instructions per page and head quad of the matrix-core INT2 kernel
+// (int8 K = 64 channels each, one per group inside a 64-channel block)
+__host__ __device__ constexpr int mfma_qk_steps(int d, int g) { return (d / 64) * (g < 64 ? 64 / g : 1); }
 constexpr int kBf16Splits = kMaxBf16 / (kPage * kBf16PagesPerSplit); // 5 BF16 partials
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -56,6 +59,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 // Workspace partition used by decode_attn and merge.
 struct WsLayout {
   size_t qrot;      // fp32 [B][Hq][D]     q . R_k (unscaled)
+  size_t qpk;       // matrix-core kernel only: int32 [B][Hkv][g/4][mfma_qk_steps][64][4]
+                    //   its QK A operands (the rotated query in 7-bit pieces)
+  size_t qhd;       // matrix-core kernel only: [B][Hq][8] per q head: int exponent
+                    //   (bits), then sum of q_rot over each group * sm_scale * log2(e)
   size_t part_o;    // fp32 [B][Hq][S][D]  history chunk partial outputs (rotated basis)
   size_t part_ml;   // fp32 [B][Hq][S][2]  (max logit in log2 units, sum of exponentials)
   size_t bf_o;      // fp32 [B][Hq][kBf16Splits][D]  BF16 segment partial outputs

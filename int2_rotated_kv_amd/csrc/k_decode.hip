@@ -27,6 +27,8 @@ template <int D>
 struct QrotShared {
   double qs[D];
   double part[256 / (D / 4)][D];
+  float qf[D];                           // q . R_k rounded to fp32
+  int qe;
 };
 
 template <int D>
@@ -64,6 +66,72 @@ __device__ __forceinline__ void qrot_body(const DecodeParams &p, const uint16_t 
 #pragma unroll
     for (int g2 = 0; g2 < NGR; ++g2) acc += sh.part[g2][tid];
     reinterpret_cast<float *>(p.ws + p.L.qrot)[(size_t)bh * D + tid] = (float)acc;
+    sh.qf[tid] = (float)acc;
+  }
+  if (p.int2_kind != OSCAR_INT2_MFMA) return;
+
+  // Operands of the matrix-core INT2 kernel for this q head (h_in-th of its
+  // KV head's g): q_rot as a 21-bit integer qi = rint(q * 2^qe) with
+  // |q| * 2^qe < 2^20, split into 7-bit pieces qi >> 14, (qi >> 7) & 127,
+  // qi & 127 that fill A rows 4*(h_in % 4) + piece of head quad h_in / 4 (row
+  // 4*(h_in % 4) + 3 is zero); per QK step m (64 channels of one group) lane
+  // (kb, row) holds in dword e, byte bb the piece of channel
+  // 64*blk + 16*kb + 4*bb + e.  Also the exponent and the group sums of q_rot
+  // (their zero-point term) times sm_scale*log2(e).
+  __syncthreads();
+  const int G = p.G, NG = D / G;
+  if (tid < 64) {
+    float mx = 0.f;
+    float gs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      const float v = sh.qf[tid + 64 * k];
+      mx = fmaxf(mx, fabsf(v));
+      gs[(tid + 64 * k) / G] += v;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+#pragma unroll
+    for (int g2 = 0; g2 < 4; ++g2)
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) gs[g2] += __shfl_xor(gs[g2], o);
+    int e = 0;
+    if (mx > 0.f) (void)frexpf(mx, &e);          // mx < 2^e
+    int qe = mx > 0.f ? 20 - e : 0;              // |q| * 2^qe < 2^20
+    qe = qe > 126 ? 126 : (qe < -100 ? -100 : qe);
+    if (tid == 0) {
+      sh.qe = qe;
+      float *hd = reinterpret_cast<float *>(p.ws + p.L.qhd) + (size_t)bh * 8;
+      hd[0] = __int_as_float(qe);
+      for (int g2 = 0; g2 < NG; ++g2) hd[1 + g2] = gs[g2] * p.sm_log2;
+    }
+  }
+  __syncthreads();
+  const int j2 = p.kv_of_q[h];
+  int h_in = 0;
+  for (int k = 0; k < p.g; ++k) h_in = p.q_of_kv[j2 * p.g + k] == h ? k : h_in;
+  const int gpb = G < 64 ? 64 / G : 1;
+  const int nqk = mfma_qk_steps(D, G);
+  const int nq = p.g / 4;
+  const float sc = ldexpf(1.f, sh.qe);
+  const int b = bh / p.Hq;
+  for (int t = tid; t < nqk * 64; t += 256) {
+    const int m = t >> 6, pc = (t >> 4) & 3, kb = (t >> 2) & 3, e = t & 3;
+    const int blk = m / gpb, g2 = (64 * blk) / G + m % gpb;
+    uint32_t word = 0;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      const int c = 64 * blk + 16 * kb + 4 * bb + e;
+      int piece = 0;
+      if (pc < 3 && c / G == g2) {
+        const int qi = (int)rintf(sh.qf[c] * sc);
+        piece = pc == 0 ? (qi >> 14) : pc == 1 ? ((qi >> 7) & 127) : (qi & 127);
+      }
+      word |= ((uint32_t)piece & 0xFFu) << (8 * bb);
+    }
+    const int lane = 16 * kb + 4 * (h_in & 3) + pc;
+    int32_t *dst = reinterpret_cast<int32_t *>(p.ws + p.L.qpk);
+    dst[((((size_t)b * p.Hkv + j2) * nq + (h_in >> 2)) * nqk + m) * 256 + lane * 4 + e] = (int32_t)word;
   }
 }
 

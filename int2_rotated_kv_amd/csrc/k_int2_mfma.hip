@@ -169,18 +169,29 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   const bool live = hg * HG + jl < p.Hkv;         // a last group may be short
   const int j = live ? hg * HG + jl : 0;          // this wave's KV head
   const int r16 = lane & 15, kb = lane >> 4;      // row-in-16 and lane group
-  __shared__ int batch_ctr[8];                    // per head: next batch of the part
-  if (threadIdx.x < 8) batch_ctr[threadIdx.x] = 0;
-  __syncthreads();
-
-  int hl = live ? p.hist_len[b] : 0;
+  int hl = p.hist_len[b];
   hl = hl < 0 ? 0 : hl;
   hl = hl > p.max_hist_len ? p.max_hist_len : hl;
   hl = hl > kPage * p.hist_stride ? kPage * p.hist_stride : hl;
   const int npages = (hl + kPage - 1) / kPage;
-  // this block's pages [pbeg, pend): part `part` of P equal parts
+  // this block's pages [pbeg, pend): part `part` of P equal parts (none for a
+  // wave without a head)
   const int pbeg = (int)((long long)npages * part / P);
-  const int pend = (int)((long long)npages * (part + 1) / P);
+  const int pend = live ? (int)((long long)npages * (part + 1) / P) : pbeg;
+
+  // the part's page ids (the first kPidCap of them) are staged in LDS once, so
+  // a batch's ids are an LDS read away rather than a scalar-cache miss
+  constexpr int kPidCap = 1024;
+  __shared__ int batch_ctr[8];                    // per head: next batch of the part
+  __shared__ int pid_lds[kPidCap];
+  {
+    const int pe = (int)((long long)npages * (part + 1) / P);
+    const int n = pe - pbeg < kPidCap ? pe - pbeg : kPidCap;
+    const int32_t *tab = p.hist_pages + (size_t)b * p.hist_stride + pbeg;
+    for (int i = threadIdx.x; i < n; i += 64 * HB) pid_lds[i] = tab[i];
+  }
+  if (threadIdx.x < 8) batch_ctr[threadIdx.x] = 0;
+  __syncthreads();
 
   // ---------------- page loop: register ring of NS pages ----------------
   // stage data of one page for this lane: K words of token r16 / lane group kb,
@@ -189,7 +200,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
 #ifndef OSCAR_INT2_STAGES
 #define OSCAR_INT2_STAGES 4
 #endif
+#ifndef OSCAR_INT2_BATCH
+#define OSCAR_INT2_BATCH 4
+#endif
   constexpr int NS = OSCAR_INT2_STAGES;   // pages in the register ring (NS-1 in flight)
+  constexpr int NB = OSCAR_INT2_BATCH;    // pages per batch taken from a head's counter
+  constexpr int NBT = NS / NB;            // batches per pass over the ring
+  static_assert(NS % NB == 0, "the ring holds whole batches");
   constexpr int SW = D / 32;             // words of a lane slot: NBLK K words, NH V words
   struct Stage {
     uint32_t c[SW];                      // K words of (token r16, part kb), V words of channels lane + 64*h2
@@ -197,8 +214,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     int ok;
   };
   Stage st[NS];
-  // page ids through the constant address space: wave-uniform scalar loads,
-  // counted apart from the vector loads so reading one never drains the ring
+  // page ids past the staged ones through the constant address space:
+  // wave-uniform scalar loads, counted apart from the vector loads so reading
+  // one never drains the ring
   using cint32 = const __attribute__((address_space(4))) int32_t;
   cint32 *ptab = (cint32 *)(p.hist_pages + (size_t)b * p.hist_stride);
   const size_t rec_stride = (size_t)p.Hkv * RL.bytes();
@@ -213,17 +231,19 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   // page id of history page k (wave-uniform); pages outside [pbeg, pend) are
   // -1 and the table is never read there
   auto page_id = [&](int k) -> int {
-    const int id = ptab[k >= pbeg && k < pend ? k : pbeg];
-    return (k >= pbeg && k < pend) ? id : -1;
+    if (k < pbeg || k >= pend) return -1;
+    const int i = k - pbeg;
+    if (i < kPidCap) return __builtin_amdgcn_readfirstlane(pid_lds[i]);
+    return ptab[k];
   };
 
-  // Work distribution: the WH waves of a head take batches of NS consecutive
+  // Work distribution: the WH waves of a head take batches of NB consecutive
   // pages of the block's part from that head's LDS counter, so waves the SIMD
   // arbiter favours (older waves) take more pages and a head's waves finish
-  // together.
+  // together.  A batch is taken when its first page is about to be requested.
   auto grab = [&]() -> int {                      // start page of the next batch
     int v = 0;
-    if (lane == 0) v = atomicAdd(&batch_ctr[jl], NS);
+    if (lane == 0) v = atomicAdd(&batch_ctr[jl], NB);
     return pbeg + __builtin_amdgcn_readfirstlane(v);
   };
 
@@ -240,114 +260,65 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     buf_words<2 * NG>(sg.sz, rs, off_sz);
   };
 
-  // the rotated query is loaded first, then the first pages are requested, so
-  // the query prologue runs while the pages are in flight (vector loads return
-  // in order); the page ids an outer iteration issues are read one iteration
-  // earlier
-  float qv[GQ][D / 64];
+  // the query operands (prepared with the q rotation) are loaded first, then
+  // the first pages are requested: A words of the wave's head quads, and per
+  // q head its exponent and group sums (wave-uniform scalar loads)
+  v4i aq[NQ][NQK];
   {
-    const float *qrot = reinterpret_cast<const float *>(p.ws + p.L.qrot);
+    const v4i *qpk = reinterpret_cast<const v4i *>(p.ws + p.L.qpk) +
+                     ((size_t)b * p.Hkv + j) * NQ * NQK * 64 + lane;
 #pragma unroll
-    for (int h = 0; h < GQ; ++h)
+    for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-      for (int k = 0; k < D / 64; ++k)
-        qv[h][k] = qrot[((size_t)b * p.Hq + p.q_of_kv[j * GQ + h]) * D + lane + 64 * k];
+      for (int m = 0; m < NQK; ++m) aq[qd][m] = qpk[(qd * NQK + m) * 64];
   }
-  int bcur = pend;                                // batch being processed
-  if (pend > pbeg) {
-    bcur = grab();
+  int qe_h[GQ];
+  float qz_h[GQ][NG];
+  {
+    using cf32 = const __attribute__((address_space(4))) float;
+    cf32 *qhd = (cf32 *)(p.ws + p.L.qhd);
 #pragma unroll
-    for (int s2 = 0; s2 < NS - 1; ++s2) issue(st[s2], page_id(bcur + s2));
+    for (int h = 0; h < GQ; ++h) {
+      cf32 *hd = qhd + ((size_t)b * p.Hq + p.q_of_kv[j * GQ + h]) * 8;
+      qe_h[h] = __float_as_int(hd[0]);
+#pragma unroll
+      for (int g2 = 0; g2 < NG; ++g2) qz_h[h][g2] = hd[1 + g2];
+    }
+  }
+  // batch starts: bq[0 .. NBT-1] are processed in the current pass over the
+  // ring, bq[NBT ..] are taken during it; pages of the wave's sequence of
+  // batches go to ring slots in order, NS - 1 requests ahead of processing
+  int bq[2 * NBT];
+#pragma unroll
+  for (int k = 0; k < 2 * NBT; ++k) bq[k] = pend;
+  if (pend > pbeg) {
+#pragma unroll
+    for (int idx = 0; idx < NS - 1; ++idx) {
+      if (idx % NB == 0) bq[idx / NB] = grab();
+      issue(st[idx], page_id(bq[idx / NB] + idx % NB));
+    }
   }
 
-  __shared__ float qf_all[HB][GQ][D];             // per wave: q_rot (unscaled)
+  __shared__ float qf_all[HB][GQ][D];             // per wave: its partial outputs at the end
   __shared__ __align__(16) _Float16 wbuf_all[HB][NG][GQ][16];   // per wave: w[grp][head][slot]
   float (*qf)[D] = qf_all[w];
   _Float16 (*wbuf)[GQ][16] = wbuf_all[w];
 
-  // ---------------- prologue: the wave's q heads as integer pieces ----------------
-  int qexp[GQ];
-  float qz[GQ][NG];
-#pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    float mx = 0.f;
-    float gs[NG];
-#pragma unroll
-    for (int g2 = 0; g2 < NG; ++g2) gs[g2] = 0.f;
-#pragma unroll
-    for (int k = 0; k < D / 64; ++k) {
-      const float v = qv[h][k];
-      qf[h][lane + 64 * k] = v;
-      mx = fmaxf(mx, fabsf(v));
-      gs[(lane + 64 * k) / G] += v;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-#pragma unroll
-    for (int g2 = 0; g2 < NG; ++g2) {
-      float t = gs[g2];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
-      qz[h][g2] = t * p.sm_log2;
-    }
-    int e = 0;
-    if (mx > 0.f) (void)frexpf(mx, &e);          // mx < 2^e
-    int qe = mx > 0.f ? 20 - e : 0;              // |q| * 2^qexp < 2^20
-    qexp[h] = qe > 126 ? 126 : (qe < -100 ? -100 : qe);
-  }
-  wave_lds_sync();
-
-  // A operands: row = 4*h + piece (piece 3 is zero), lane group kb, VGPR e,
-  // byte bb <-> channel 64*blk + 16*kb + 4*bb + e (the B unpack order).
-  v4i aq[NQ][NQK];
-  {
-    const int hrow = r16 >> 2, pc = r16 & 3;
-#pragma unroll
-    for (int qd = 0; qd < NQ; ++qd) {
-      int qe_row = qexp[0];
-#pragma unroll
-      for (int h = 1; h < GQ; ++h) qe_row = (h == qd * 4 + hrow) ? qexp[h] : qe_row;
-      const float sc = ldexpf(1.f, qe_row);
-      const int h = qd * 4 + hrow;
-#pragma unroll
-      for (int m = 0; m < NQK; ++m) {
-        const int blk = m / GPB, gsub = m % GPB;
-        const int g2 = (64 * blk) / G + gsub;
-        int vv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const int c = 64 * blk + 16 * kb + 4 * bb + e;
-            int piece = 0;
-            if (pc < 3 && c / G == g2) {
-              const int qi = (int)rintf(qf[h][c] * sc);
-              piece = pc == 0 ? (qi >> 14) : pc == 1 ? ((qi >> 7) & 127) : (qi & 127);
-            }
-            word |= ((uint32_t)piece & 0xFFu) << (8 * bb);
-          }
-          vv[e] = (int)word;
-        }
-        aq[qd][m] = v4i{vv[0], vv[1], vv[2], vv[3]};
-      }
-    }
-  }
   // per-lane constants of the (head, token) layout of the QK result:
   // lane (kb, r16) holds head 4*qd + kb, token r16
   float qscale[NQ], qzl[NQ][NG];
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
-    int qe_l = qexp[0];
+    int qe_l = qe_h[0];
     float z_l[NG];
 #pragma unroll
-    for (int g2 = 0; g2 < NG; ++g2) z_l[g2] = qz[0][g2];
+    for (int g2 = 0; g2 < NG; ++g2) z_l[g2] = qz_h[0][g2];
 #pragma unroll
     for (int h = 1; h < GQ; ++h) {
       const bool mine = h == qd * 4 + kb;
-      qe_l = mine ? qexp[h] : qe_l;
+      qe_l = mine ? qe_h[h] : qe_l;
 #pragma unroll
-      for (int g2 = 0; g2 < NG; ++g2) z_l[g2] = mine ? qz[h][g2] : z_l[g2];
+      for (int g2 = 0; g2 < NG; ++g2) z_l[g2] = mine ? qz_h[h][g2] : z_l[g2];
     }
     qscale[qd] = ldexpf(1.f, -qe_l) * p.sm_log2;
 #pragma unroll
@@ -520,22 +491,19 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     wave_lds_sync();
   };
 
-  // the ring holds pages bcur .. bcur + NS - 2 on entry; each step issues one
-  // page (the rest of this batch, then the start of the next) and processes one
-  while (bcur < pend) {
-    const int bnext = grab();
-    int idc[NS];
+  // each step requests the page NS - 1 ahead (taking a new batch when that
+  // page starts one) and processes one; a batch past the part is empty
+  while (bq[0] < pend) {
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2) {
-      const int ipos = s2 + NS - 1;
-      idc[s2] = ipos < NS ? page_id(bcur + ipos) : page_id(bnext + ipos - NS);
+      const int idx = s2 + NS - 1;                // request position in this pass
+      if (idx % NB == 0) bq[idx / NB] = grab();
+      issue(st[(s2 + NS - 1) % NS], page_id(bq[idx / NB] + idx % NB));
+      const int cur = bq[s2 / NB] + s2 % NB;
+      if (cur < pend) process(st[s2], cur);
     }
 #pragma unroll
-    for (int s2 = 0; s2 < NS; ++s2) {
-      issue(st[(s2 + NS - 1) % NS], idc[s2]);
-      if (bcur + s2 < pend) process(st[s2], bcur + s2);
-    }
-    bcur = bnext;
+    for (int k = 0; k < NBT; ++k) bq[k] = bq[k + NBT];
   }
 
   // ---------------- epilogue: one partial per (q head, part) ----------------
