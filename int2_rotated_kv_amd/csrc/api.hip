@@ -175,8 +175,17 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   S = S > kMaxSplits ? kMaxSplits : S;
   const int pps = npages > 0 ? (npages + S - 1) / S : 0;
   if (npages > 0 && kind != OSCAR_INT2_MFMA) S = (npages + pps - 1) / pps;
-  p->splits = S;
   p->pages_per_split = pps;
+  p->mfma_parts = S;
+  p->mfma_balanced = 0;
+  if (kind == OSCAR_INT2_MFMA) {
+    // S parts per sequence on average; with the blocks balanced across
+    // sequences one sequence may use up to 2S + 2 partial slots
+    p->mfma_balanced = a->batch > 1 && a->batch <= kMaxBalancedBatch &&
+                       (long long)a->batch * npages < (1LL << 31);
+    S = 2 * S + 2;
+  }
+  p->splits = S;
 
   WsLayout &L = p->L;
   const size_t BH = (size_t)a->batch * a->num_q_heads;
@@ -187,6 +196,7 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   off = align256(off + (mf ? (size_t)a->batch * c->num_kv_heads * (p->g / 4) *
                                  mfma_qk_steps(p->D, p->G) * 64 * 4 * 4 : 0));
   L.qhd = off; off = align256(off + (mf ? BH * 8 * 4 : 0));
+  L.nslots = off; off = align256(off + (mf ? (size_t)a->batch * 4 : 0));
   L.part_o = off; off = align256(off + BH * S * p->D * 4);
   L.part_ml = off; off = align256(off + BH * S * 2 * 4);
   L.bf_o = off; off = align256(off + BH * kBf16Splits * p->D * 4);
@@ -261,7 +271,7 @@ int oscar_decode_plan(const oscar_cache *cache, const oscar_decode_args *args,
   DecodeParams p{};
   int st = check_args(cache, args, &p);
   if (st) return st;
-  if (num_splits) *num_splits = p.splits;
+  if (num_splits) *num_splits = p.int2_kind == OSCAR_INT2_MFMA ? p.mfma_parts : p.splits;
   if (pages_per_split) *pages_per_split = p.pages_per_split;
   if (workspace_bytes) *workspace_bytes = p.L.total;
   if (int2_kernel) *int2_kernel = p.int2_kind;

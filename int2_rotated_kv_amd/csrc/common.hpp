@@ -18,6 +18,7 @@ constexpr int kMaxSplits = 1024;        // history chunks per (sequence, KV head
 #endif
 constexpr int kMfmaWaves = OSCAR_INT2_WAVES;   // matrix-core INT2 kernel: waves per block
 constexpr int kMfmaTargetBlocks = 256;          // its default grid: one block per compute unit
+constexpr int kMaxBalancedBatch = 64 * kMfmaWaves;   // sequences it balances across (one per thread)
 // KV heads per block of the matrix-core INT2 kernel: Hkv rounded up to a power
 // of two, at most 8; the block's waves are split evenly over them
 __host__ __device__ constexpr int mfma_heads_per_block(int hkv) {
@@ -61,6 +62,7 @@ struct WsLayout {
   size_t qrot;      // fp32 [B][Hq][D]     q . R_k (unscaled)
   size_t qpk;       // matrix-core kernel only: int32 [B][Hkv][g/4][mfma_qk_steps][64][4]
                     //   its QK A operands (the rotated query in 7-bit pieces)
+  size_t nslots;    // matrix-core kernel only: int32 [B] partial slots each sequence used
   size_t qhd;       // matrix-core kernel only: [B][Hq][8] per q head: int exponent
                     //   (bits), then sum of q_rot over each group * sm_scale * log2(e)
   size_t part_o;    // fp32 [B][Hq][S][D]  history chunk partial outputs (rotated basis)
@@ -88,7 +90,9 @@ struct DecodeParams {
   int max_hist_len;
   float sm_log2;       // softmax scale * log2(e)
   int int2_kind;       // resolved history kernel: OSCAR_INT2_VALU, _MFMA or OSCAR_HISTORY_BF16
-  int splits, pages_per_split;
+  int splits, pages_per_split;   // partial slots per (sequence, q head); nominal pages
+  int mfma_parts;      // matrix-core kernel: blocks per head group = B * mfma_parts
+  int mfma_balanced;   // matrix-core kernel: may balance blocks across sequences
   uint8_t *ws;
   WsLayout L;
   int16_t q_of_kv[OSCAR_MAX_Q_HEADS];  // [Hkv][g] q heads of each KV head

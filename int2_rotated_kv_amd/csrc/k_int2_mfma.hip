@@ -149,16 +149,17 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave (uniform)
-  // block = (sequence, group of HG KV heads, part of the history); WH waves
-  // per head share the part's pages and their results are combined into one
-  // partial per (q head, part)
+  // block = (group of HG KV heads, block index within the group); WH waves
+  // per head share the block's pages and their results are combined into one
+  // partial per (q head, segment)
   const int HG = mfma_heads_per_block(p.Hkv);
   const int WH = HB / HG;
-  const int P = p.splits;                         // parts per (sequence, KV head)
+  const int S = p.splits;                         // partial slots per (sequence, q head)
   const int ngrp = (p.Hkv + HG - 1) / HG;
-  const int part = blockIdx.x % P;
-  const int hg = (blockIdx.x / P) % ngrp;
-  const int b = blockIdx.x / (P * ngrp);
+  const int NBT = gridDim.x / ngrp;               // blocks per head group
+  const int hg = blockIdx.x / NBT;
+  const int ib = blockIdx.x % NBT;
+  const int P = NBT / p.B;                        // parts per sequence when not balanced
   // waves 4k .. 4k+3 sit in issue slot k of the CU's four SIMDs, and the
   // arbiter favours lower slots; with 8 heads the two waves of a head are
   // taken from slots 0 and 3, or 1 and 2, so every head gets about the same
@@ -169,24 +170,117 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   const bool live = hg * HG + jl < p.Hkv;         // a last group may be short
   const int j = live ? hg * HG + jl : 0;          // this wave's KV head
   const int r16 = lane & 15, kb = lane >> 4;      // row-in-16 and lane group
-  int hl = p.hist_len[b];
-  hl = hl < 0 ? 0 : hl;
-  hl = hl > p.max_hist_len ? p.max_hist_len : hl;
-  hl = hl > kPage * p.hist_stride ? kPage * p.hist_stride : hl;
-  const int npages = (hl + kPage - 1) / kPage;
-  // this block's pages [pbeg, pend): part `part` of P equal parts (none for a
-  // wave without a head)
-  const int pbeg = (int)((long long)npages * part / P);
-  const int pend = live ? (int)((long long)npages * (part + 1) / P) : pbeg;
 
-  // the part's page ids (the first kPidCap of them) are staged in LDS once, so
-  // a batch's ids are an LDS read away rather than a scalar-cache miss
+  // ---------------- schedule: this block's segments ----------------
+  // The histories of the batch laid end to end hold T pages; block ib of its
+  // head group covers pages [T*ib/NB, T*(ib+1)/NB) with NB = min(NBT, T/16)
+  // blocks at work, so blocks get equal page counts whatever the sequence
+  // lengths.  A range that crosses a sequence boundary is handled as one
+  // segment per sequence, each writing its own partial slot: the index of the
+  // block among the blocks that cover that sequence.  If some sequence would
+  // need more than S slots (lengths far from equal), or the batch is larger
+  // than the block, every block instead takes one of P equal parts of one
+  // sequence (slot = part).
+  auto clamp_len = [&](int v) {
+    v = v < 0 ? 0 : v;
+    v = v > p.max_hist_len ? p.max_hist_len : v;
+    return v > kPage * p.hist_stride ? kPage * p.hist_stride : v;
+  };
+  __shared__ int cum[kMaxBalancedBatch + 1];      // pages before sequence b
+  __shared__ int wsum[HB];
+  const bool scan = p.mfma_balanced != 0;         // B <= kMaxBalancedBatch and no overflow
+  int T = 0, NB = 1;
+  bool balanced = false;
+  if (scan) {
+    const int t = threadIdx.x;
+    const int v = t < p.B ? (clamp_len(p.hist_len[t]) + kPage - 1) / kPage : 0;
+    int x = v;                                    // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int before = 0;
+    for (int k = 0; k < w; ++k) before += wsum[k];
+    if (t < p.B) cum[t] = before + x - v;
+    if (t == p.B - 1) cum[p.B] = before + x;
+    __syncthreads();
+    T = cum[p.B];
+    NB = T / 16 < NBT ? T / 16 : NBT;
+    NB = NB < 1 ? 1 : NB;
+    // the block holding global page g: the largest i with T*i/NB <= g
+    bool bad = false;
+    if (t < p.B && v > 0 && T > 0) {
+      const int first = (int)(((long long)(cum[t] + 1) * NB - 1) / T);
+      const int last = (int)(((long long)(cum[t] + v) * NB - 1) / T);
+      bad = last - first + 1 > S;
+    }
+    balanced = T > 0 && !__syncthreads_or(bad);
+    // the merge reads each sequence's slot count
+    if (hg == 0 && ib == 0 && t < p.B) {
+      int n = P;
+      if (balanced) {
+        const int first = (int)(((long long)(cum[t] + 1) * NB - 1) / T);
+        const int last = (int)(((long long)(cum[t] + v) * NB - 1) / T);
+        n = v > 0 ? last - first + 1 : 0;
+      }
+      reinterpret_cast<int *>(p.ws + p.L.nslots)[t] = n;
+    }
+  }
+  const long long g0 = balanced && ib < NB ? (long long)T * ib / NB : 0;
+  const long long g1 = balanced && ib < NB ? (long long)T * (ib + 1) / NB : 0;
+  int bseg = 0;                                   // next sequence to look at
+  if (balanced) {
+    int lo = 0, hi = p.B - 1;                     // last b with cum[b] <= g0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cum[mid] <= g0) lo = mid; else hi = mid - 1;
+    }
+    bseg = lo;
+  } else {
+    bseg = ib / (P > 0 ? P : 1);
+  }
+  bool fallback_done = false;
+
+  // page ids (the first kPidCap of a segment) are staged in LDS, so a batch's
+  // ids are an LDS read away rather than a scalar-cache miss
   constexpr int kPidCap = 1024;
-  __shared__ int batch_ctr[8];                    // per head: next batch of the part
+  __shared__ int batch_ctr[8];                    // per head: next batch of the segment
   __shared__ int pid_lds[kPidCap];
+  __shared__ float qf_all[HB][GQ][D];             // per wave: its partial outputs at the end
+  __shared__ __align__(16) _Float16 wbuf_all[HB][NG][GQ][16];   // per wave: w[grp][head][slot]
+  __shared__ float mlw[HB][GQ][2];
+
+  for (;;) {
+  // ---------------- next segment: sequence b, its pages [pbeg, pend) ----------------
+  int b, pbeg, pend_all, slot;
+  if (balanced) {
+    while (bseg < p.B && cum[bseg] < g1 &&
+           (cum[bseg + 1] < g1 ? cum[bseg + 1] : g1) <= (cum[bseg] > g0 ? cum[bseg] : g0))
+      ++bseg;
+    if (bseg >= p.B || ib >= NB || cum[bseg] >= g1) break;
+    b = bseg++;
+    const long long lo = cum[b] > g0 ? cum[b] : g0;
+    const long long hi = cum[b + 1] < g1 ? cum[b + 1] : g1;
+    pbeg = (int)(lo - cum[b]);
+    pend_all = (int)(hi - cum[b]);
+    slot = ib - (int)(((long long)(cum[b] + 1) * NB - 1) / T);
+  } else {
+    if (fallback_done || bseg >= p.B || P == 0) break;
+    fallback_done = true;
+    b = bseg;
+    const int part = ib % P;
+    const int npg = (clamp_len(p.hist_len[b]) + kPage - 1) / kPage;
+    pbeg = (int)((long long)npg * part / P);
+    pend_all = (int)((long long)npg * (part + 1) / P);
+    slot = part;
+  }
+  const int hl = clamp_len(p.hist_len[b]);
+  const int pend = live ? pend_all : pbeg;        // no pages for a wave without a head
   {
-    const int pe = (int)((long long)npages * (part + 1) / P);
-    const int n = pe - pbeg < kPidCap ? pe - pbeg : kPidCap;
+    const int n = pend_all - pbeg < kPidCap ? pend_all - pbeg : kPidCap;
     const int32_t *tab = p.hist_pages + (size_t)b * p.hist_stride + pbeg;
     for (int i = threadIdx.x; i < n; i += 64 * HB) pid_lds[i] = tab[i];
   }
@@ -238,7 +332,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   };
 
   // Work distribution: the WH waves of a head take batches of NB consecutive
-  // pages of the block's part from that head's LDS counter, so waves the SIMD
+  // pages of the segment from that head's LDS counter, so waves the SIMD
   // arbiter favours (older waves) take more pages and a head's waves finish
   // together.  A batch is taken when its first page is about to be requested.
   auto grab = [&]() -> int {                      // start page of the next batch
@@ -299,8 +393,6 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     }
   }
 
-  __shared__ float qf_all[HB][GQ][D];             // per wave: its partial outputs at the end
-  __shared__ __align__(16) _Float16 wbuf_all[HB][NG][GQ][16];   // per wave: w[grp][head][slot]
   float (*qf)[D] = qf_all[w];
   _Float16 (*wbuf)[GQ][16] = wbuf_all[w];
 
@@ -492,7 +584,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   };
 
   // each step requests the page NS - 1 ahead (taking a new batch when that
-  // page starts one) and processes one; a batch past the part is empty
+  // page starts one) and processes one; a batch past the segment is empty
   while (bq[0] < pend) {
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2) {
@@ -506,11 +598,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     for (int k = 0; k < NBT; ++k) bq[k] = bq[k + NBT];
   }
 
-  // ---------------- epilogue: one partial per (q head, part) ----------------
+  // ---------------- epilogue: one partial per (q head, segment) ----------------
   // each wave leaves its unnormalised output and (max, sum) per head in LDS
   // (its own query slot, no longer read), then the block combines the WH waves
   // of every head:  M = max m_w, L = sum L_w 2^(m_w - M), O = sum O_w 2^(m_w - M)
-  __shared__ float mlw[HB][GQ][2];
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
     // head 4*qd + kb's sums over its 16 token lanes
@@ -564,21 +655,24 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
         L = fmaf(a, mlw[wk][hh][1], L);
       }
     }
-    const size_t row = ((size_t)b * p.Hq + p.q_of_kv[j2 * GQ + hh]) * P + part;
+    const size_t row = ((size_t)b * p.Hq + p.q_of_kv[j2 * GQ + hh]) * S + slot;
     po[row * D + c] = O;
     if (c == 0) {
       pml[row * 2 + 0] = M;
       pml[row * 2 + 1] = L;
     }
   }
+  __syncthreads();                                // LDS is reused by the next segment
+  }  // segments
 }
 
 template <int D, int G>
 static void launch_mfma_dg(const DecodeParams &p, hipStream_t s) {
-  // one block per (sequence, group of KV heads, part); splits = parts
+  // B * mfma_parts blocks per group of KV heads (balanced across sequences
+  // inside the kernel)
   const int hg = mfma_heads_per_block(p.Hkv);
   const int ngrp = (p.Hkv + hg - 1) / hg;
-  const dim3 grid(p.B * ngrp * p.splits), blk(64 * kMfmaWaves);
+  const dim3 grid(p.B * ngrp * p.mfma_parts), blk(64 * kMfmaWaves);
   if (p.g == 8) hipLaunchKernelGGL((k_int2_mfma<D, G, 8>), grid, blk, 0, s, p);
   else hipLaunchKernelGGL((k_int2_mfma<D, G, 4>), grid, blk, 0, s, p);
 }

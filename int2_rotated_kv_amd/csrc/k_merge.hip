@@ -57,7 +57,11 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeParams p, const float *__res
   const int j = p.kv_of_q[bh % p.Hq];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int cq = tid % LPR, rg = tid / LPR;
-  const int S = p.splits;
+  const int S = p.splits;                      // row stride of the partials
+  // chunks of this sequence: all S, or the slots the matrix-core kernel used
+  int n = S;
+  if (S > 0 && p.int2_kind == OSCAR_INT2_MFMA)
+    n = p.mfma_balanced ? reinterpret_cast<const int *>(p.ws + p.L.nslots)[bh / p.Hq] : p.mfma_parts;
   extern __shared__ float a_s[];               // [S] chunk weights 2^(m_s - M)
   __shared__ float4 red[NW][LPR];              // per-wave channel sums
   __shared__ __align__(16) float Os[D];        // merged history output (rotated basis)
@@ -71,12 +75,12 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeParams p, const float *__res
 
   // ---- every load up front ----
   float2 mlv = make_float2(-INFINITY, 0.f);
-  if (tid < S) mlv = ml[tid];
+  if (tid < n) mlv = ml[tid];
   float4 ov[kMergeRegChunks];                  // chunk rows rg + RG*k, channels 4cq..4cq+3
 #pragma unroll
   for (int k = 0; k < kMergeRegChunks; ++k) {
     const int s2 = rg + RG * k;
-    ov[k] = s2 < S ? po[(size_t)s2 * LPR] : make_float4(0.f, 0.f, 0.f, 0.f);
+    ov[k] = s2 < n ? po[(size_t)s2 * LPR] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float4 r[RPT];                               // R_v[j] rows rg + RG*i, columns 4cq..4cq+3
   if (Rv != nullptr) {
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeParams p, const float *__res
 
   // ---- chunk weights: M = max m_s, L = sum l_s 2^(m_s - M) ----
   float M = mlv.x;
-  for (int s2 = tid + NT; s2 < S; s2 += NT) M = fmaxf(M, ml[s2].x);
+  for (int s2 = tid + NT; s2 < n; s2 += NT) M = fmaxf(M, ml[s2].x);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   if (lane == 0) wred[0][wv] = M;
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeParams p, const float *__res
 #pragma unroll
   for (int w = 1; w < NW; ++w) M = fmaxf(M, wred[0][w]);
   float L = 0.f;
-  for (int s2 = tid; s2 < S; s2 += NT) {
+  for (int s2 = tid; s2 < n; s2 += NT) {
     const float2 t = s2 == tid ? mlv : ml[s2];
     const float a = (t.x == -INFINITY) ? 0.f : exp2f(t.x - M);
     a_s[s2] = a;
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeParams p, const float *__res
 #pragma unroll
   for (int k = 0; k < kMergeRegChunks; ++k) {
     const int s2 = rg + RG * k;
-    const float wgt = s2 < S ? a_s[s2] : 0.f;
+    const float wgt = s2 < n ? a_s[s2] : 0.f;
     if (wgt != 0.f) {
       acc.x = fmaf(wgt, ov[k].x, acc.x);
       acc.y = fmaf(wgt, ov[k].y, acc.y);
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeParams p, const float *__res
       acc.w = fmaf(wgt, ov[k].w, acc.w);
     }
   }
-  for (int s2 = rg + RG * kMergeRegChunks; s2 < S; s2 += RG) {
+  for (int s2 = rg + RG * kMergeRegChunks; s2 < n; s2 += RG) {
     const float wgt = a_s[s2];
     if (wgt != 0.f) {
       const float4 v = po[(size_t)s2 * LPR];

@@ -171,3 +171,31 @@ def test_fused_step_matches_separate_calls(shape, kernel):
     ref = sh.oracle_step(inp, steps=3)
     _check_bytes(fus, inp, ref)
     _check_out(fus, ref)
+
+
+@pytest.mark.parametrize("case", ["dominant_fallback", "dominant_balanced", "mixed_short", "batch_1025"])
+def test_block_balancing(case):
+    """The matrix-core kernel's block schedule: blocks take equal ranges of the
+    histories laid end to end (a block may cover several short sequences, a
+    long sequence many blocks); when one sequence would need more than
+    2*num_splits + 2 partial slots it falls back to equal parts per sequence;
+    batches above 1024 sequences always use parts."""
+    _say("case: block balancing", case)
+    if case.startswith("dominant"):
+        wl = synth.workload("tiny", B=8, Hkv=2, Hq=8, D=128, G=64,
+                            lengths=(6000, 400, 400, 400, 400, 400, 400, 400), steps=1, seed=41)
+        splits = 1 if case == "dominant_fallback" else 0
+    elif case == "mixed_short":
+        wl = synth.workload("tiny", B=8, Hkv=2, Hq=8, D=128, G=64,
+                            lengths=(2000, 330, 500, 340, 900, 1200, 321, 700), steps=1, seed=42)
+        splits = 1
+    else:
+        rng = np.random.default_rng(43)
+        wl = synth.workload("tiny", B=1025, lengths=tuple(int(x) for x in rng.integers(300, 420, 1025)),
+                            steps=1, seed=43)
+        splits = 0
+    inp = synth.make_small(wl)
+    run = sh.build_and_step(inp, steps=1, int2_kernel=2, num_splits=splits)
+    ref = sh.oracle_step(inp, steps=1)
+    _check_bytes(run, inp, ref)
+    _check_out(run, ref)
