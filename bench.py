@@ -233,6 +233,8 @@ def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0
     res = dict(wall_s=wall, seg_ms=seg, first_out=first_out, out=out, args=args,
                int2_only_ms=int2_only_ms, int2_only_step=T_hot - 1,
                ms_separate=1000.0 * wall_sep / E if E else float("nan"))
+    if steps:
+        res["graph"] = time_graph(one, T_hot - 1, steps, out)
     if cold_steps:
         # two cache-cold protocols, cold_steps steps each: 512 MiB of scratch
         # read (clean eviction, as other layers' caches and weights do) or
@@ -263,6 +265,38 @@ def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0
                 int2_ms=float(np.mean([a.elapsed_time(b) for a, b in ci])),
                 int2_step=last, steps=range(base, base + cold_steps))
     return res
+
+
+def time_graph(one, s, replays, out):
+    """The decode step `s` (already run once) captured in a HIP graph and
+    replayed: each replay repeats the same step (the demotion rewrites the
+    same bytes, the store the same token).  Three replays, each followed by a
+    synchronisation, are checked against an eager run of the step first; then
+    `replays` replays are timed back to back."""
+    import torch
+    try:
+        one(s)
+        torch.cuda.synchronize()
+        ref = out.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one(s)
+        worst = 0.0
+        for _ in range(3):
+            out.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            den = ref.abs().amax(dim=-1).clamp_min(1e-30)
+            worst = max(worst, float(((out - ref).abs().amax(dim=-1) / den).max()))
+        t0 = time.perf_counter()
+        for _ in range(replays):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = 1000.0 * (time.perf_counter() - t0) / replays
+        return dict(ms_per_step=ms, replay_vs_eager_max_rel=worst, ok=worst < 5e-4)
+    except Exception as e:  # a capture failure is reported, not fatal
+        return dict(ms_per_step=None, error=str(e)[:200], ok=False)
 
 
 def run_steps_bf16(st, steps, warmup):
@@ -556,6 +590,8 @@ def main(argv=None):
         "hbm_tbps": step_bytes / (ms_step * 1e-3) / 1e12,
         "hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "ms_per_step_separate_calls": r["ms_separate"],
+        "ms_per_step_graph": r.get("graph", {}).get("ms_per_step"),
+        "graph": r.get("graph"),
         "step_ms_breakdown": {"demote+write": float(seg[:, 0].mean()), "qrot+bf16": float(seg[:, 1].mean()),
                               "int2": int2_ms, "merge": float(seg[:, 3].mean())},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
