@@ -135,6 +135,19 @@ __device__ __forceinline__ void buf_words(uint32_t (&dst)[NW], __amdgpu_buffer_r
 }  // namespace
 
 
+constexpr int kPidCap = 1024;                   // page ids of a segment staged in LDS
+
+// LDS of the matrix-core kernel
+template <int D, int G, int GQ>
+struct Int2Shared {
+  int cum[kMaxBalancedBatch + 1];                 // pages before sequence b
+  int wsum[kMfmaWaves];
+  int batch_ctr[8];                               // per head: next batch of the segment
+  int pid_lds[kPidCap];
+  float qf_all[kMfmaWaves][GQ][D];                // per wave: its partial outputs at the end
+  __align__(16) _Float16 wbuf_all[kMfmaWaves][D / G][GQ][16];   // per wave: w[grp][head][slot]
+  float mlw[kMfmaWaves][GQ][2];
+};
 template <int D, int G, int GQ>
 __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   constexpr RecLayout RL(D, G);
@@ -147,6 +160,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   constexpr int HB = kMfmaWaves;
   static_assert(GQ == 4 || GQ == 8, "4 or 8 q heads per KV head");
 
+  __shared__ Int2Shared<D, G, GQ> lds;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave (uniform)
   // block = (group of HG KV heads, block index within the group); WH waves
@@ -186,8 +200,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     v = v > p.max_hist_len ? p.max_hist_len : v;
     return v > kPage * p.hist_stride ? kPage * p.hist_stride : v;
   };
-  __shared__ int cum[kMaxBalancedBatch + 1];      // pages before sequence b
-  __shared__ int wsum[HB];
+  auto &cum = lds.cum;                            // pages before sequence b
+  auto &wsum = lds.wsum;
   const bool scan = p.mfma_balanced != 0;         // B <= kMaxBalancedBatch and no overflow
   int T = 0, NB = 1;
   bool balanced = false;
@@ -246,12 +260,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
 
   // page ids (the first kPidCap of a segment) are staged in LDS, so a batch's
   // ids are an LDS read away rather than a scalar-cache miss
-  constexpr int kPidCap = 1024;
-  __shared__ int batch_ctr[8];                    // per head: next batch of the segment
-  __shared__ int pid_lds[kPidCap];
-  __shared__ float qf_all[HB][GQ][D];             // per wave: its partial outputs at the end
-  __shared__ __align__(16) _Float16 wbuf_all[HB][NG][GQ][16];   // per wave: w[grp][head][slot]
-  __shared__ float mlw[HB][GQ][2];
+  auto &batch_ctr = lds.batch_ctr;             // per head: next batch of the segment
+  auto &pid_lds = lds.pid_lds;
+  auto &qf_all = lds.qf_all;                   // per wave: its partial outputs at the end
+  auto &wbuf_all = lds.wbuf_all;               // per wave: w[grp][head][slot]
+  auto &mlw = lds.mlw;
 
   for (;;) {
   // ---------------- next segment: sequence b, its pages [pbeg, pend) ----------------

@@ -135,7 +135,7 @@ def test_bf16_history_comparison(shape, splits):
         assert np.abs(lse[b] - r["lse"]).max() < 1e-3
 
 
-@pytest.mark.parametrize("shape", ["tiny", "edge", "d128g4", "d128g8"])
+@pytest.mark.parametrize("shape", ["tiny", "edge", "d128g4", "d128g8", "b8"])
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_fused_step_matches_separate_calls(shape, kernel):
     """oscar_decode_step over several steps gives the same INT2 and BF16 pool
@@ -148,8 +148,12 @@ def test_fused_step_matches_separate_calls(shape, kernel):
         wl = synth.workload("tiny", B=5, Hkv=2, Hq=8, lengths=(10, 64, 320, 321, 400), steps=3, seed=32)
     elif shape == "d128g4":
         wl = synth.workload("tiny", B=2, Hkv=2, Hq=8, D=128, G=64, lengths=(3000, 1700), steps=3, seed=33)
-    else:
+    elif shape == "d128g8":
         wl = synth.workload("tiny", B=2, Hkv=2, Hq=16, D=128, G=128, lengths=(2500, 999), steps=3, seed=34)
+    else:
+        # batch >= 4: the BF16 segment runs in blocks appended to the INT2 launch
+        wl = synth.workload("tiny", B=8, Hkv=2, Hq=8, D=128, G=64,
+                            lengths=(2000, 330, 500, 340, 900, 1200, 321, 700), steps=3, seed=35)
     if kernel == 2 and wl.g not in (4, 8):
         pytest.skip("matrix-core kernel needs 4 or 8 q heads per KV head")
     inp = synth.make_small(wl, distinct_rv=True)
