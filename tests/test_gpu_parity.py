@@ -203,3 +203,20 @@ def test_block_balancing(case):
     ref = sh.oracle_step(inp, steps=1)
     _check_bytes(run, inp, ref)
     _check_out(run, ref)
+
+
+@pytest.mark.parametrize("Hkv,Hq,D,G", [(16, 64, 64, 32), (6, 24, 128, 64), (3, 24, 64, 64)])
+def test_head_groups(Hkv, Hq, D, G):
+    """KV-head counts other than 8 on the matrix-core kernel: two groups of 8
+    heads per sequence (16), a last group with dead heads (6 of 8), and a block
+    of 4 heads with one dead (3 heads, 8 q heads per KV head); several
+    sequences, so blocks are balanced across them; also through the fused
+    decode step."""
+    _say("case: head groups", Hkv, Hq, D, G)
+    wl = synth.workload("tiny", B=3, Hkv=Hkv, Hq=Hq, D=D, G=G, lengths=(1300, 700, 2100), steps=2, seed=51)
+    inp = synth.make_small(wl)
+    ref = sh.oracle_step(inp, steps=2)
+    for fused in (False, True):
+        run = sh.build_and_step(inp, steps=2, int2_kernel=2, fused=fused)
+        _check_bytes(run, inp, ref)
+        _check_out(run, ref)
