@@ -299,6 +299,32 @@ def time_graph(one, s, replays, out):
         return dict(ms_per_step=None, error=str(e)[:200], ok=False)
 
 
+def measure_bulk_quantize(st, n_calls=10):
+    """Throughput of the bulk path of oscar_demote_pack (prompt histories):
+    the BF16 staging pages of the cache (the last block of generated history
+    tokens) quantised into a scratch INT2 pool, 4096 tokens per call."""
+    import torch
+    from int2_rotated_kv_amd import binding as ob
+    wl, sc = st.wl, st.sc
+    n = sc.staging_pages * PAGE
+    scratch = ob.Cache(wl.Hkv, wl.D, wl.G, sc.staging_pages, sc.cache.num_bf16_pages,
+                       device=st.q.device, bf16_k=sc.cache.bf16_k, bf16_v=sc.cache.bf16_v)
+    base = sc.staging_base * PAGE
+    src = torch.arange(base, base + n, dtype=torch.int32, device=st.q.device)
+    dst = torch.arange(0, n, dtype=torch.int32, device=st.q.device)
+    ob.demote_pack(scratch, src, dst, st.Rk, st.Rv, st.ck, st.cv)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_calls):
+        ob.demote_pack(scratch, src, dst, st.Rk, st.Rv, st.ck, st.cv)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n_calls
+    return {"kernel": "k_demote_bulk", "tokens_per_call": n, "ms_per_call": ms,
+            "token_heads_per_s": n * wl.Hkv / (ms * 1e-3),
+            "fp64_fma_per_token_head": 2 * wl.D * wl.D}
+
+
 def run_steps_bf16(st, steps, warmup):
     """The same decode steps on the comparison cache (history in BF16 pages):
     copy the oldest recent token into its history slot, write the new token
@@ -613,6 +639,7 @@ def main(argv=None):
                             "on the stream; HIP events around the step (launch) alone",
             }
             log(f"[bench] cold ({name}): {c['ms']:.4f} ms/step, INT2 {c['int2_ms'] * 1000:.1f} us")
+    out["bulk_quantize"] = measure_bulk_quantize(st)
     if not a.no_bf16_compare:
         rb = run_steps_bf16(st, a.steps, a.warmup)
         ms_b = 1000.0 * rb["wall_s"] / a.steps

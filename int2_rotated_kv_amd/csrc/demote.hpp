@@ -50,201 +50,6 @@ struct DemoteArgs {
   const float *clip_k, *clip_v;    // [Hkv]
 };
 
-template <int D, int T>
-struct DemoteShared {
-  double xs[2][T][D];              // [K|V][entry][channel] source values
-  int s_src[T], s_dst[T];
-  double red_mx[2][2][T], red_mn[2][2][T];
-};
-
-// Demotion of up to T entries (e0 ..) of one KV head j, K (half 0) or V (half
-// 1), by the D threads c = 0 .. D-1 of that half.  Every thread of the block
-// calls it (inactive threads pass active = false) so that its barriers are
-// block-wide; the shared state is per half.
-template <int D, int G, int T>
-__device__ __forceinline__ void demote_body(const DemoteArgs &a, int e0, int j, int half, int c,
-                                            bool active, DemoteShared<D, T> &sh) {
-  // every fp64 operation below is rounded on its own, as specified: no fusion
-  // of the clip products into the subtraction
-#pragma clang fp contract(off)
-  constexpr RecLayout RL(D, G);
-  constexpr int GW = G < 64 ? G : 64;       // lanes of a group inside one wave
-  const bool isv = half != 0;
-
-  // one token: the D loads of this thread's R column do not depend on the
-  // token, so they are issued first
-  const float *R = isv ? a.Rv : a.Rk;
-  float rcol[T == 1 ? D : 1];
-  if constexpr (T == 1) {
-    if (active && R != nullptr) {
-      const float *Rj = R + (size_t)j * D * D;
-#pragma unroll
-      for (int i = 0; i < D; ++i) rcol[i] = Rj[(size_t)i * D + c];
-    }
-  }
-
-  if (active && c < T) {                   // both halves store the same values
-    const int e = e0 + c;
-    int sv = -1, dv = -1;
-    if (e < a.n) { sv = a.src[e]; dv = a.dst[e]; }
-    // entries with a negative or out-of-range slot are skipped
-    if (sv < 0 || dv < 0 || (sv >> 4) >= a.n_bf16_pages || (dv >> 4) >= a.n_int2_pages) {
-      sv = -1;
-      dv = -1;
-    }
-    sh.s_src[c] = sv;
-    sh.s_dst[c] = dv;
-  }
-  __syncthreads();
-
-  if (active) {
-    const uint16_t *bf = isv ? a.bf_v : a.bf_k;
-    for (int t = 0; t < T; ++t) {
-      const int s = sh.s_src[t];
-      double v = 0.0;
-      if (s >= 0) {
-        const int64_t page = s >> 4, off = s & 15;
-        v = (double)bf16_to_f32(bf[((page * a.Hkv + j) * kPage + off) * D + c]);
-      }
-      sh.xs[half][t][c] = v;
-    }
-  }
-  __syncthreads();
-  if (!active) {
-    if constexpr (G > 64) __syncthreads();
-    return;
-  }
-
-  double x[T];
-  if (R != nullptr && T == 1) {
-    double a0 = 0.0, a1 = 0.0;
-#pragma unroll
-    for (int i = 0; i < D; i += 2) {
-      const double2 kk = *reinterpret_cast<const double2 *>(&sh.xs[half][0][i]);
-      a0 = fma(kk.x, (double)rcol[i], a0);
-      a1 = fma(kk.y, (double)rcol[i + 1], a1);
-    }
-    x[0] = a0 + a1;
-  } else if (R != nullptr) {
-    R += (size_t)j * D * D;
-#pragma unroll
-    for (int t = 0; t < T; ++t) x[t] = 0.0;
-#pragma unroll 4
-    for (int i = 0; i < D; i += 2) {
-      const double r0 = (double)R[(size_t)i * D + c];
-      const double r1 = (double)R[(size_t)(i + 1) * D + c];
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const double2 kk = *reinterpret_cast<const double2 *>(&sh.xs[half][t][i]);
-        x[t] = fma(kk.y, r1, fma(kk.x, r0, x[t]));
-      }
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < T; ++t) x[t] = sh.xs[half][t][c];
-  }
-
-  // group max / min
-  double mx[T], mn[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    double u = x[t], l = x[t];
-#pragma unroll
-    for (int o = 1; o < GW; o <<= 1) {
-      u = fmax(u, __shfl_xor(u, o));
-      l = fmin(l, __shfl_xor(l, o));
-    }
-    mx[t] = u;
-    mn[t] = l;
-  }
-  if constexpr (G > 64) {
-    const int w = c >> 6;
-    if ((c & 63) == 0) {
-      for (int t = 0; t < T; ++t) { sh.red_mx[half][w][t] = mx[t]; sh.red_mn[half][w][t] = mn[t]; }
-    }
-    __syncthreads();
-    for (int t = 0; t < T; ++t) {
-      mx[t] = fmax(sh.red_mx[half][0][t], sh.red_mx[half][1][t]);
-      mn[t] = fmin(sh.red_mn[half][0][t], sh.red_mn[half][1][t]);
-    }
-  }
-
-  const double clip = (double)(isv ? a.clip_v[j] : a.clip_k[j]);
-  uint32_t codes[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const double hi = clip * mx[t];
-    const double lo = clip * mn[t];
-    const double scale = (hi - lo) / 3.0;
-    const uint16_t sb = f64_to_bf16_rne(scale);
-    const uint16_t zb = f64_to_bf16_rne(lo);
-    const double sd = (double)bf16_to_f32(sb);
-    const double zd = (double)bf16_to_f32(zb);
-    uint32_t code = 0;
-    if (sd != 0.0) {
-      double qv = rint((x[t] - zd) / sd);
-      qv = fmin(fmax(qv, 0.0), 3.0);
-      code = (uint32_t)qv;
-    }
-    codes[t] = code;
-    const int d = sh.s_dst[t];
-    if (d >= 0 && (c % G) == 0) {
-      const int64_t page = d >> 4, off = d & 15;
-      uint8_t *rec = a.pool + ((size_t)page * a.Hkv + j) * RL.bytes();
-      const int o = isv ? RL.vsz((int)off, c / G) : RL.ksz((int)off, c / G);
-      *reinterpret_cast<uint32_t *>(rec + o) = (uint32_t)sb | ((uint32_t)zb << 16);
-    }
-  }
-
-  if (!isv) {
-    // K: word blk of lane slot 16*kb + t holds channels 64*blk + 16*kb + i of
-    // token t at bits 2i
-    const int kb = (c & 63) >> 4, blk = c >> 6;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      uint32_t w = codes[t] << (2 * (c & 15));
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) w |= __shfl_xor(w, o);
-      const int d = sh.s_dst[t];
-      if (d >= 0 && (c & 15) == 0) {
-        const int64_t page = d >> 4, off = d & 15;
-        uint8_t *rec = a.pool + ((size_t)page * a.Hkv + j) * RL.bytes();
-        *reinterpret_cast<uint32_t *>(rec + RL.kword(16 * kb + (int)off, blk)) = w;
-      }
-    }
-  } else {
-    // V: channel-major, one dword per channel holds the 16 tokens of a page;
-    // entries of this block that share a page are combined first.
-    for (int t = 0; t < T; ++t) {
-      const int d = sh.s_dst[t];
-      if (d < 0) continue;
-      const int page = d >> 4;
-      bool leader = true;
-      for (int u = 0; u < t; ++u)
-        if (sh.s_dst[u] >= 0 && (sh.s_dst[u] >> 4) == page) leader = false;
-      if (!leader) continue;
-      uint32_t mask = 0, bits = 0;
-      for (int u = t; u < T; ++u) {
-        const int du = sh.s_dst[u];
-        if (du >= 0 && (du >> 4) == page) {
-          const int shf = 2 * (du & 15);
-          mask |= 3u << shf;
-          bits = (bits & ~(3u << shf)) | (codes[u] << shf);
-        }
-      }
-      uint8_t *rec = a.pool + ((size_t)page * a.Hkv + j) * RL.bytes();
-      // V word of channel c: lane slot c % 64, V word c / 64
-      uint32_t *wp = reinterpret_cast<uint32_t *>(rec + RL.vword(c & 63, c >> 6));
-      if (mask == 0xFFFFFFFFu) {
-        *wp = bits;
-      } else {
-        atomicAnd(wp, ~mask);
-        atomicOr(wp, bits);
-      }
-    }
-  }
-}
-
 template <int D>
 struct DemoteOneShared {
   double ks[D];                        // the token's source values

@@ -4,13 +4,162 @@
 
 namespace oscar {
 
-// One block: up to T entries of the slot lists (16 for bulk fills, 1 for the
-// few tokens of a decode step), one KV head (blockIdx.y), K or V (blockIdx.z).
-// Thread c owns rotated channel c of the block's tokens.
-template <int D, int G, int T>
-__global__ __launch_bounds__(D) void k_demote(DemoteArgs a) {
-  __shared__ DemoteShared<D, T> sh;
-  demote_body<D, G, T>(a, blockIdx.x * T, blockIdx.y, blockIdx.z, threadIdx.x, true, sh);
+// Bulk fills (prompt histories): one block = 16 consecutive entries of the
+// slot lists, one KV head (blockIdx.y), K or V (blockIdx.z); thread c owns
+// rotated channel c.  Every R load serves the 16 tokens: rows are walked in
+// order (fp64 fma chains, the same arithmetic per token as the single-token
+// routine's definition, x = sum_i k_i R_ic), with the next 8 rows' R values
+// requested while the current 8 are used.  The tokens are then quantised one
+// by one; a token's V bits are gathered per page word and a word is written
+// once all tokens of its page in this block are in (whole-page words with one
+// store, others with AND/OR atomics).
+template <int D, int G>
+__global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
+#pragma clang fp contract(off)
+  constexpr int T = 16;
+  constexpr int RB = 8;                        // R rows per pipeline step
+  constexpr RecLayout RL(D, G);
+  constexpr int GW = G < 64 ? G : 64;          // lanes of a group inside one wave
+  const int c = threadIdx.x;
+  const int j = blockIdx.y;
+  const bool isv = blockIdx.z != 0;
+  const int e0 = blockIdx.x * T;
+  __shared__ __align__(16) double xs[T][D];
+  __shared__ int s_src[T], s_dst[T];
+  __shared__ double red_mx[2], red_mn[2];
+
+  const float *R = isv ? a.Rv : a.Rk;
+  const float *Rj = R != nullptr ? R + (size_t)j * D * D : nullptr;
+  float rn[RB];
+  if (Rj != nullptr) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) rn[r] = Rj[(size_t)r * D + c];
+  }
+  if (c < T) {
+    const int e = e0 + c;
+    int sv = -1, dv = -1;
+    if (e < a.n) { sv = a.src[e]; dv = a.dst[e]; }
+    // entries with a negative or out-of-range slot are skipped
+    if (sv < 0 || dv < 0 || (sv >> 4) >= a.n_bf16_pages || (dv >> 4) >= a.n_int2_pages) {
+      sv = -1;
+      dv = -1;
+    }
+    s_src[c] = sv;
+    s_dst[c] = dv;
+  }
+  __syncthreads();
+  const uint16_t *bf = isv ? a.bf_v : a.bf_k;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int s = s_src[t];
+    double v = 0.0;
+    if (s >= 0) {
+      const int64_t page = s >> 4, off = s & 15;
+      v = (double)bf16_to_f32(bf[((page * a.Hkv + j) * kPage + off) * D + c]);
+    }
+    xs[t][c] = v;
+  }
+  __syncthreads();
+
+  double x[T];
+  if (Rj != nullptr) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) x[t] = 0.0;
+    for (int i0 = 0; i0 < D; i0 += RB) {
+      float rc[RB];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) rc[r] = rn[r];
+      if (i0 + RB < D) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r) rn[r] = Rj[(size_t)(i0 + RB + r) * D + c];
+      }
+#pragma unroll
+      for (int r = 0; r < RB; r += 2) {
+        const double r0 = (double)rc[r], r1 = (double)rc[r + 1];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const double2 kk = *reinterpret_cast<const double2 *>(&xs[t][i0 + r]);
+          x[t] = fma(kk.y, r1, fma(kk.x, r0, x[t]));
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < T; ++t) x[t] = xs[t][c];
+  }
+
+  const double clip = (double)(isv ? a.clip_v[j] : a.clip_k[j]);
+  int vpage = -1;                              // V word being gathered (uniform)
+  uint32_t vmask = 0, vbits = 0;
+  auto flush_v = [&]() {
+    if (vpage < 0) return;
+    uint8_t *rec = a.pool + ((size_t)vpage * a.Hkv + j) * RL.bytes();
+    // V word of channel c: lane slot c % 64, V word c / 64
+    uint32_t *wp = reinterpret_cast<uint32_t *>(rec + RL.vword(c & 63, c >> 6));
+    if (vmask == 0xFFFFFFFFu) {
+      *wp = vbits;
+    } else {
+      atomicAnd(wp, ~vmask);
+      atomicOr(wp, vbits);
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    double mx = x[t], mn = x[t];
+#pragma unroll
+    for (int o = 1; o < GW; o <<= 1) {
+      mx = fmax(mx, __shfl_xor(mx, o));
+      mn = fmin(mn, __shfl_xor(mn, o));
+    }
+    if constexpr (G > 64) {
+      if ((c & 63) == 0) { red_mx[c >> 6] = mx; red_mn[c >> 6] = mn; }
+      __syncthreads();
+      mx = fmax(red_mx[0], red_mx[1]);
+      mn = fmin(red_mn[0], red_mn[1]);
+      __syncthreads();
+    }
+    const int d = s_dst[t];
+    if (d < 0) continue;                       // uniform
+    const double hi = clip * mx;
+    const double lo = clip * mn;
+    const double scale = (hi - lo) / 3.0;
+    const uint16_t sb = f64_to_bf16_rne(scale);
+    const uint16_t zb = f64_to_bf16_rne(lo);
+    const double sd = (double)bf16_to_f32(sb);
+    const double zd = (double)bf16_to_f32(zb);
+    uint32_t code = 0;
+    if (sd != 0.0) {
+      double qv = rint((x[t] - zd) / sd);
+      qv = fmin(fmax(qv, 0.0), 3.0);
+      code = (uint32_t)qv;
+    }
+    const int64_t page = d >> 4, off = d & 15;
+    uint8_t *rec = a.pool + ((size_t)page * a.Hkv + j) * RL.bytes();
+    if ((c % G) == 0) {
+      const int o = isv ? RL.vsz((int)off, c / G) : RL.ksz((int)off, c / G);
+      *reinterpret_cast<uint32_t *>(rec + o) = (uint32_t)sb | ((uint32_t)zb << 16);
+    }
+    if (!isv) {
+      // K: word blk of lane slot 16*kb + t holds channels 64*blk + 16*kb + i of
+      // token t at bits 2i
+      const int kb = (c & 63) >> 4, blk = c >> 6;
+      uint32_t w = code << (2 * (c & 15));
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) w |= __shfl_xor(w, o);
+      if ((c & 15) == 0) *reinterpret_cast<uint32_t *>(rec + RL.kword(16 * kb + (int)off, blk)) = w;
+    } else {
+      if ((int)page != vpage) {
+        flush_v();
+        vpage = (int)page;
+        vmask = 0;
+        vbits = 0;
+      }
+      const int shf = 2 * (int)off;
+      vmask |= 3u << shf;
+      vbits = (vbits & ~(3u << shf)) | (code << shf);
+    }
+  }
+  if (isv) flush_v();
 }
 
 // The few tokens of a decode step: one (entry, KV head, K|V) per block of 256
@@ -52,7 +201,7 @@ static void launch_demote_t(const DemoteArgs &a, hipStream_t s) {
   if ((a.n + 15) / 16 * a.Hkv * 2 < 1024) {
     hipLaunchKernelGGL((k_demote_one<D, G>), dim3(a.n, a.Hkv, 2), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_demote<D, G, 16>), dim3((a.n + 15) / 16, a.Hkv, 2), dim3(D), 0, s, a);
+    hipLaunchKernelGGL((k_demote_bulk<D, G>), dim3((a.n + 15) / 16, a.Hkv, 2), dim3(D), 0, s, a);
   }
 }
 
