@@ -220,3 +220,54 @@ def test_head_groups(Hkv, Hq, D, G):
         run = sh.build_and_step(inp, steps=2, int2_kernel=2, fused=fused)
         _check_bytes(run, inp, ref)
         _check_out(run, ref)
+
+
+def test_bulk_quantise_order_and_splits():
+    """oscar_demote_pack on many tokens (the bulk kernel, 16 entries per block):
+    the pool bytes do not depend on the order of the entries or on how they
+    are split across calls (pages completed by several calls or blocks take
+    the AND/OR path for their V words), and equal the oracle's records."""
+    import torch
+    from int2_rotated_kv_amd import binding as ob
+    from oracle import oscar_oracle as orc
+    _say("case: bulk quantise order and splits")
+    wl = synth.workload("tiny", B=1, Hkv=2, Hq=8, D=128, G=64, lengths=(1000,), steps=1, seed=61)
+    inp = synth.make_small(wl)
+    n, npg = 1000, 63                              # 62 full pages and one of 8 tokens
+    K, V = inp.K[0][:n], inp.V[0][:n]              # [n][Hkv][D] bf16 bits
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+    Rk, Rv = dev(inp.R_k), dev(inp.R_v)
+    ck, cv = dev(inp.clip_k), dev(inp.clip_v)
+    phys = synth.page_permutation(61, npg, extra=2)
+    dst_all = (phys[np.arange(n) // 16].astype(np.int64) * 16 + np.arange(n) % 16).astype(np.int32)
+
+    def run(order, chunks):
+        cache = ob.Cache(wl.Hkv, wl.D, wl.G, npg + 2, npg + 1)
+        kb = np.zeros((npg + 1, wl.Hkv, 16, wl.D), np.uint16)
+        vb = np.zeros_like(kb)
+        for t in range(n):
+            kb[t // 16, :, t % 16] = K[t]
+            vb[t // 16, :, t % 16] = V[t]
+        cache.bf16_k.copy_(dev(kb.view(np.int16)))
+        cache.bf16_v.copy_(dev(vb.view(np.int16)))
+        src_all = np.arange(n, dtype=np.int32)
+        for part in np.array_split(order, chunks):
+            ob.demote_pack(cache, dev(src_all[part]), dev(dst_all[part]), Rk, Rv, ck, cv)
+        torch.cuda.synchronize()
+        return cache.int2.cpu().numpy()
+
+    rng = np.random.default_rng(61)
+    base = run(np.arange(n), 1)
+    assert np.array_equal(run(rng.permutation(n), 1), base), "entry order changed the bytes"
+    assert np.array_equal(run(np.arange(n), 7), base), "split calls changed the bytes"
+    inter = np.concatenate([np.arange(0, n, 2), np.arange(1, n, 2)])
+    assert np.array_equal(run(inter, 2), base), "interleaved calls changed the bytes"
+    Kf, Vf = synth.bf16_bits_to_f64(K), synth.bf16_bits_to_f64(V)
+    for j in range(wl.Hkv):
+        kc, ks, kz = orc.quantize_tokens(Kf[:, j], inp.R_k[j], wl.G, float(inp.clip_k[j]))
+        vc, vs, vz = orc.quantize_tokens(Vf[:, j], inp.R_v[j], wl.G, float(inp.clip_v[j]))
+        for pg in (0, 31, 62):
+            a, e = pg * 16, min(n, pg * 16 + 16)
+            pad = lambda x: np.concatenate([x[a:e], np.zeros((16 - (e - a),) + x.shape[1:], x.dtype)])
+            want = orc.encode_record(pad(kc), pad(ks), pad(kz), pad(vc), pad(vs), pad(vz), wl.D, wl.G)
+            assert np.array_equal(base[phys[pg], j], want), f"page {pg} head {j}"
