@@ -297,6 +297,31 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     const int32_t *tab = p.hist_pages + (size_t)b * p.hist_stride + pbeg;
     for (int i = threadIdx.x; i < n; i += 64 * HB) pid_lds[i] = tab[i];
   }
+  // the query operands (prepared with the q rotation) are requested before
+  // the staging barrier: A words of the wave's head quads, and per q head its
+  // exponent and group sums (wave-uniform scalar loads)
+  v4i aq[NQ][NQK];
+  {
+    const v4i *qpk = reinterpret_cast<const v4i *>(p.ws + p.L.qpk) +
+                     ((size_t)b * p.Hkv + j) * NQ * NQK * 64 + lane;
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+      for (int m = 0; m < NQK; ++m) aq[qd][m] = qpk[(qd * NQK + m) * 64];
+  }
+  int qe_h[GQ];
+  float qz_h[GQ][NG];
+  {
+    using cf32 = const __attribute__((address_space(4))) float;
+    cf32 *qhd = (cf32 *)(p.ws + p.L.qhd);
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      cf32 *hd = qhd + ((size_t)b * p.Hq + p.q_of_kv[j * GQ + h]) * 8;
+      qe_h[h] = __float_as_int(hd[0]);
+#pragma unroll
+      for (int g2 = 0; g2 < NG; ++g2) qz_h[h][g2] = hd[1 + g2];
+    }
+  }
   if (threadIdx.x < 8) batch_ctr[threadIdx.x] = 0;
   __syncthreads();
 
@@ -367,31 +392,6 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     buf_words<2 * NG>(sg.sz, rs, off_sz);
   };
 
-  // the query operands (prepared with the q rotation) are loaded first, then
-  // the first pages are requested: A words of the wave's head quads, and per
-  // q head its exponent and group sums (wave-uniform scalar loads)
-  v4i aq[NQ][NQK];
-  {
-    const v4i *qpk = reinterpret_cast<const v4i *>(p.ws + p.L.qpk) +
-                     ((size_t)b * p.Hkv + j) * NQ * NQK * 64 + lane;
-#pragma unroll
-    for (int qd = 0; qd < NQ; ++qd)
-#pragma unroll
-      for (int m = 0; m < NQK; ++m) aq[qd][m] = qpk[(qd * NQK + m) * 64];
-  }
-  int qe_h[GQ];
-  float qz_h[GQ][NG];
-  {
-    using cf32 = const __attribute__((address_space(4))) float;
-    cf32 *qhd = (cf32 *)(p.ws + p.L.qhd);
-#pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      cf32 *hd = qhd + ((size_t)b * p.Hq + p.q_of_kv[j * GQ + h]) * 8;
-      qe_h[h] = __float_as_int(hd[0]);
-#pragma unroll
-      for (int g2 = 0; g2 < NG; ++g2) qz_h[h][g2] = hd[1 + g2];
-    }
-  }
   // batch starts: bq[0 .. NBT-1] are processed in the current pass over the
   // ring, bq[NBT ..] are taken during it; pages of the wave's sequence of
   // batches go to ring slots in order, NS - 1 requests ahead of processing
