@@ -169,7 +169,10 @@ def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0
     args = [step_args(st, s, int2_kernel, num_splits) for s in range(T)]
     a_qb = [a.with_phases(ob.PHASE_QROT | ob.PHASE_BF16) for a in args]
     a_i2 = [a.with_phases(ob.PHASE_INT2) for a in args]
-    ws = ob.alloc_workspace(st.sc.cache, args[-1])
+    # the chunk count (and with it the workspace) need not grow monotonically
+    # with the history length: size the workspace for every planned step
+    ws = torch.empty(max(ob.workspace_bytes(st.sc.cache, a) for a in args), dtype=torch.uint8,
+                     device=st.q.device)
     wl = st.wl
     out = torch.zeros((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=st.q.device)
     lse = torch.zeros((wl.B, wl.Hq), dtype=torch.float32, device=st.q.device)
@@ -338,7 +341,8 @@ def run_steps_bf16(st, steps, warmup):
     args = [ob.DecodeArgs(wl.B, wl.Hq, st.sc.hist_pages, st.hl[s], st.cmp_win_pages, st.bl[s],
                           int(st.hl_h[s].max()), int2_kernel=ob.HISTORY_BF16) for s in range(T)]
     a_h = [a.with_phases(ob.PHASE_INT2) for a in args]
-    ws = ob.alloc_workspace(cache, args[-1])
+    ws = torch.empty(max(ob.workspace_bytes(cache, a) for a in args), dtype=torch.uint8,
+                     device=st.q.device)
     out = torch.zeros((wl.B, wl.Hq, wl.D), dtype=torch.float32, device=st.q.device)
     lse = torch.zeros((wl.B, wl.Hq), dtype=torch.float32, device=st.q.device)
     src = (st.dsrc.long() + st.cmp_off)
