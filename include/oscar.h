@@ -194,7 +194,7 @@ int oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_ar
  * heads; the waves of a head take its pages in batches from a shared counter
  * and their results are combined into one partial per (q head, part).
  * Automatic chunking aims at 256 blocks (one per compute unit) while keeping
- * every part at least 4x its partial bytes and 16 pages per head;
+ * every part at least 2x its partial bytes and 8 pages per head;
  * pages_per_split is nominal.  An explicit num_splits is capped at the page
  * count and at 1024.
  */

@@ -148,7 +148,7 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   // and 16 pages.  Matrix-core kernel: one block of kMfmaWaves waves per
   // (sequence, group of up to 8 KV heads, part), the group's waves combining
   // their results into one partial per (q head, part); enough parts for one
-  // block per compute unit, each part at least 4x its partial bytes and 16
+  // block per compute unit, each part at least 2x its partial bytes and 8
   // pages per head; its pages_per_split is nominal.
   const int npages = need_hist;
   int S = 1;
@@ -164,8 +164,9 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
       const double rec = kind == OSCAR_HISTORY_BF16 ? 2.0 * kPage * p->D * 2
                                                     : (double)RecLayout(p->D, p->G).bytes();
       const double part_bytes = 2.0 * p->g * (p->D + 2) * 4.0;   // write + read back
-      int min_pages = (int)std::ceil((mf ? 4.0 : 8.0) * part_bytes / rec);
-      min_pages = min_pages < 16 ? 16 : min_pages;
+      int min_pages = (int)std::ceil((mf ? 2.0 : 8.0) * part_bytes / rec);
+      const int floor_pages = mf ? 8 : 16;
+      min_pages = min_pages < floor_pages ? floor_pages : min_pages;
       int s_fill = (target + units - 1) / units;
       int s_cap = npages / min_pages;
       S = s_fill < s_cap ? s_fill : s_cap;

@@ -194,9 +194,9 @@ def test_plan_chunking_rules():
     # a single long sequence fills the chip: 256 parts of >= 16 pages
     st, s, p, *_ = _plan(_cache(), _args(batch=1, hist_stride=6400, max_hist_len=6400 * 16))
     assert st == 0 and s == 256 and p == 25
-    # ... unless its history is short: parts of at least 16 pages
+    # ... unless its history is short: parts of at least 8 pages
     st, s, p, *_ = _plan(_cache(), _args(batch=1, hist_stride=640, max_hist_len=640 * 16))
-    assert st == 0 and s == 40 and p == 16
+    assert st == 0 and s == 80 and p == 8
     # no history: one (empty) chunk
     st, s, p, *_ = _plan(_cache(), _args(max_hist_len=0))
     assert st == 0 and s == 1 and p == 0
