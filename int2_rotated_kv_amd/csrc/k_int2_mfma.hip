@@ -21,15 +21,18 @@
 //     shifted copies; A = w * 2^(8-b) in f16, so A * B = A + w * code / 4;
 //     fp32 accumulation; the A part is removed with sum_t A (same f16 values).
 //
-// One block of 8 waves per (sequence, KV head, equal part of its history);
-// each wave is one chunk and writes one partial.  The waves take batches of 4
-// consecutive pages of the part from an LDS counter: the SIMD arbiter favours
-// older waves, so fixed page ranges per wave would finish unevenly.  Each wave
-// keeps 3 pages in flight in a register ring.  The running max per head is
-// lazy: it is raised (16-lane DPP reductions, rescale of the partial sums) only
-// when a logit exceeds it by more than 2 (log2 units), so unnormalised weights
-// stay below 4.  Requires 4 or 8 q heads per KV head and V group scales below
-// 1024 (A = w * 16 must stay in f16 range).
+// One block of 16 waves covers up to 8 KV heads (two waves per head) and an
+// equal share of the batch's history pages (one or more segments, see the
+// schedule below); the two waves of a head take batches of 4 consecutive pages
+// of a segment from an LDS counter, since the SIMD arbiter favours older waves
+// and fixed page ranges per wave would finish unevenly, and the block combines
+// them into one partial per (q head, segment).  Each wave keeps 3 pages in
+// flight in a register ring.  The query operands (A words, exponents, group
+// sums) come from the workspace, written by the q rotation.  The running max
+// per head is lazy: it is raised (16-lane DPP reductions, rescale of the
+// partial sums) only when a logit exceeds it by more than 2 (log2 units), so
+// unnormalised weights stay below 4.  Requires 4 or 8 q heads per KV head and
+// V group scales below 1024 (A = w * 16 must stay in f16 range).
 #include "common.hpp"
 
 namespace oscar {
