@@ -116,3 +116,108 @@ def test_full_size_sampled(workload):
         w = _check_sequence(st, r["first_out"], pool, b, rng)
         _say(f"sequence {b}: bytes of sampled pages exact, worst row rel err {w:.3e} "
              f"({time.time() - t0:.1f}s)")
+
+
+CHECK_STEPS = (0, 1, 499, 999)
+
+
+def test_long_decode_1000_steps():
+    """The single 102400-token sequence over 1000 decode steps, each one
+    oscar_decode_step (demote the oldest recent token, store the new one,
+    attend, merge), in the configuration bench.py times.  At steps 0, 1, 499
+    and 999 every q head is checked against the oracle, which replays the same
+    steps: the token demoted at step s is the s-th of the window's tokens in
+    arrival order (the 256 prompt tokens of the recent window, then the new
+    tokens of steps 0, 1, ...), so after step s the history is the prompt
+    history followed by the first s+1 of them, and the BF16 segment is the sink
+    plus the next 256.  After the last step, the bytes of every page that the
+    steps filled, and of 16 sampled prompt pages, equal the oracle's records."""
+    import torch
+    import bench
+    from oracle import oscar_oracle as orc
+    from int2_rotated_kv_amd import binding as ob
+    t0 = time.time()
+    T = CHECK_STEPS[-1] + 1
+    _say(f"case: qwen3-8b-100k-b1, {T} decode steps, checks at {CHECK_STEPS}")
+    st = bench.build_workload("qwen3-8b-100k-b1", T, log=_say)
+    wl, gen, cache = st.wl, st.gen, st.sc.cache
+    D, G, Hkv, g = wl.D, wl.G, wl.Hkv, wl.g
+    args = [bench.step_args(st, s, ob.INT2_AUTO) for s in range(T)]
+    ws = torch.empty(max(ob.workspace_bytes(cache, a) for a in args), dtype=torch.uint8,
+                     device=st.q.device)
+    out = torch.zeros((wl.B, wl.Hq, D), dtype=torch.float32, device=st.q.device)
+    lse = torch.zeros((wl.B, wl.Hq), dtype=torch.float32, device=st.q.device)
+    got = {}
+    for s in range(T):
+        ob.decode_step(cache, args[s], st.dsrc[s], st.ddst[s], st.ck, st.cv, st.wdst[s],
+                       st.knew[s], st.vnew[s], st.q[s], st.Rk, st.Rv, ws, out, lse)
+        if s in CHECK_STEPS:
+            torch.cuda.synchronize()
+            got[s] = (out[0].cpu().numpy().astype(np.float64), lse[0].cpu().numpy().copy())
+    torch.cuda.synchronize()
+    _say(f"{T} steps done ({time.time() - t0:.1f}s)")
+
+    hl0 = int(gen.hist_len0[0])
+    kh, vh = _history_tokens(gen, 0, hl0)
+    kb, vb = gen.bf16_tokens(0)
+    kb, vb = _u16(kb), _u16(vb)
+    knew, vnew, qs = _u16(st.knew[:, 0]), _u16(st.vnew[:, 0]), _u16(st.q[:, 0])
+    # window tokens in arrival order: the prompt's recent window, then the new tokens
+    arr_k = np.concatenate([kb[SINK:], knew])
+    arr_v = np.concatenate([vb[SINK:], vnew])
+    f64 = synth.bf16_bits_to_f64
+    quant = {}
+    for j in range(Hkv):
+        K = f64(np.concatenate([kh[:, j], arr_k[:T, j]]))
+        V = f64(np.concatenate([vh[:, j], arr_v[:T, j]]))
+        quant[j] = (orc.quantize_tokens(K, gen.R_k[j], G, float(gen.clip_k[j])),
+                    orc.quantize_tokens(V, gen.R_v[j], G, float(gen.clip_v[j])))
+    worst = 0.0
+    for s in CHECK_STEPS:
+        nh = hl0 + s + 1                          # history tokens after step s
+        bf_k = np.concatenate([kb[:SINK], arr_k[s + 1:s + 1 + 256]])
+        bf_v = np.concatenate([vb[:SINK], arr_v[s + 1:s + 1 + 256]])
+        q = f64(qs[s])
+        out_ref = np.zeros((wl.Hq, D))
+        lse_ref = np.zeros(wl.Hq)
+        for j in range(Hkv):
+            (kc, ks, kz), (vc, vs, vz) = quant[j]
+            heads = [h for h in range(wl.Hq) if h // g == j]
+            o, l = orc.decode_attention(q[heads], np.zeros(len(heads), int),
+                                        f64(bf_k[:, j])[:, None], f64(bf_v[:, j])[:, None],
+                                        orc.dequant(kc[:nh], ks[:nh], kz[:nh], G)[:, None],
+                                        orc.dequant(vc[:nh], vs[:nh], vz[:nh], G)[:, None],
+                                        gen.R_k[j:j + 1], gen.R_v[j:j + 1])
+            out_ref[heads], lse_ref[heads] = o, l
+        o_gpu, l_gpu = got[s]
+        den = np.maximum(np.abs(out_ref).max(axis=1), 1e-30)
+        err = np.abs(o_gpu - out_ref).max(axis=1) / den
+        assert np.all(err <= TOL), f"step {s}: row errors {np.sort(err)[-4:]}"
+        lerr = np.abs(l_gpu - lse_ref).max()
+        assert lerr < 1e-3, f"step {s}: lse error {lerr}"
+        worst = max(worst, float(err.max()))
+        _say(f"step {s}: {nh} history tokens, worst row rel err {err.max():.3e}, "
+             f"lse err {lerr:.2e} ({time.time() - t0:.1f}s)")
+
+    # page bytes after the last step: the pages the steps filled (the last one
+    # partially: its written token rows are compared) and sampled prompt pages
+    pool = cache.int2.cpu().numpy()
+    nh = hl0 + T
+    rng = np.random.default_rng(1)
+    pages = list(range(hl0 // PAGE, -(-nh // PAGE)))
+    pages += sorted(rng.choice(hl0 // PAGE, size=16, replace=False).tolist())
+    for pg in pages:
+        ph = int(st.sc.hist_table_h[0, pg])
+        ntok = min(PAGE, nh - pg * PAGE)
+        sl = slice(pg * PAGE, pg * PAGE + ntok)
+        for j in range(Hkv):
+            (kc, ks, kz), (vc, vs, vz) = quant[j]
+            if ntok == PAGE:
+                want = orc.encode_record(kc[sl], ks[sl], kz[sl], vc[sl], vs[sl], vz[sl], D, G)
+                assert np.array_equal(pool[ph, j], want), f"page {pg} head {j}: bytes differ"
+            else:
+                dk = orc.decode_record(pool[ph, j], D, G)
+                for a, w in zip(dk, (kc[sl], ks[sl], kz[sl], vc[sl], vs[sl], vz[sl])):
+                    assert np.array_equal(a[:ntok], w), f"page {pg} head {j}: partial page differs"
+    _say(f"bytes of {len(pages)} pages x {Hkv} heads exact; worst row rel err {worst:.3e} "
+         f"({time.time() - t0:.1f}s)")
