@@ -527,15 +527,19 @@ def traffic_from_profile(kernel_name: str, workload: str):
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip().split()[0] if v.strip() else ""
-    src = os.path.join(ROOT, "int2_rotated_kv_amd", "csrc", kv.get("source", "-"))
-    if kv.get("workload") != workload or not os.path.isfile(src):
+            kv[k.strip()] = v.split("(")[0].split()
+    first = lambda k: kv.get(k, [""])[0] if kv.get(k) else ""
+    # the sources the kernel is built from, hashed in the order listed
+    srcs = [os.path.join(ROOT, "int2_rotated_kv_amd", "csrc", f) for f in kv.get("source", [])]
+    if first("workload") != workload or not srcs or not all(os.path.isfile(f) for f in srcs):
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if sha != kv.get("source_sha256_16"):
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(open(f, "rb").read())
+    if h.hexdigest()[:16] != first("source_sha256_16"):
         return None
     try:
-        return float(kv["hbm_bytes_per_dispatch"])
+        return float(first("hbm_bytes_per_dispatch"))
     except (KeyError, ValueError):
         return None
 

@@ -193,8 +193,8 @@ int oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_ar
  * the bytes of its partial result and 16 pages long; chunk c covers pages
  * [c*pages_per_split, (c+1)*pages_per_split) and empty chunks are dropped.
  * MFMA kernel: a chunk is one of num_splits equal parts of each sequence's
- * history.  One block of 16 waves serves one part for a group of up to 8 KV
- * heads; the waves of a head take its pages in batches from a shared counter
+ * history.  One block of 16 waves serves one part for a pair of KV heads
+ * (8 waves per head); the waves of a head take its pages in batches from a shared counter
  * and their results are combined into one partial per (q head, part).
  * Automatic chunking aims at 256 blocks (one per compute unit) while keeping
  * every part at least 2x its partial bytes and 8 pages per head;

@@ -146,7 +146,7 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   // waves per (sequence, KV head, chunk)), each chunk streaming at least 8x
   // the bytes of its partial result (read and written once more by the merge)
   // and 16 pages.  Matrix-core kernel: one block of kMfmaWaves waves per
-  // (sequence, group of up to 8 KV heads, part), the group's waves combining
+  // (sequence, pair of KV heads, part), the pair's waves combining
   // their results into one partial per (q head, part); enough parts for one
   // block per compute unit, each part at least 2x its partial bytes and 8
   // pages per head; its pages_per_split is nominal.

@@ -19,11 +19,12 @@ constexpr int kMaxSplits = 1024;        // history chunks per (sequence, KV head
 constexpr int kMfmaWaves = OSCAR_INT2_WAVES;   // matrix-core INT2 kernel: waves per block
 constexpr int kMfmaTargetBlocks = 256;          // its default grid: one block per compute unit
 constexpr int kMaxBalancedBatch = 64 * kMfmaWaves;   // sequences it balances across (one per thread)
-// KV heads per block of the matrix-core INT2 kernel: Hkv rounded up to a power
-// of two, at most 8; the block's waves are split evenly over them
-__host__ __device__ constexpr int mfma_heads_per_block(int hkv) {
-  return hkv >= 8 ? 8 : hkv > 4 ? 8 : hkv > 2 ? 4 : hkv > 1 ? 2 : 1;
-}
+// KV heads per block of the matrix-core INT2 kernel: 2 (1 for a single KV
+// head); the block's waves are split evenly over them.  Two heads per block
+// keep the partial results per (sequence, q head) few when a batch has only a
+// few sequences (each block still fills one compute unit), and measured at
+// least as fast as 4 or 8 heads per block on long batches.
+__host__ __device__ constexpr int mfma_heads_per_block(int hkv) { return hkv >= 2 ? 2 : 1; }
 // QK matrix instructions per page and head quad of the matrix-core INT2 kernel
 // (int8 K = 64 channels each, one per group inside a 64-channel block)
 __host__ __device__ constexpr int mfma_qk_steps(int d, int g) { return (d / 64) * (g < 64 ? 64 / g : 1); }

@@ -21,9 +21,9 @@
 //     shifted copies; A = w * 2^(8-b) in f16, so A * B = A + w * code / 4;
 //     fp32 accumulation; the A part is removed with sum_t A (same f16 values).
 //
-// One block of 16 waves covers up to 8 KV heads (two waves per head) and an
+// One block of 16 waves covers 2 KV heads (8 waves per head) and an
 // equal share of the batch's history pages (one or more segments, see the
-// schedule below); the two waves of a head take batches of 4 consecutive pages
+// schedule below); the waves of a head take batches of 4 consecutive pages
 // of a segment from an LDS counter, since the SIMD arbiter favours older waves
 // and fixed page ranges per wave would finish unevenly, and the block combines
 // them into one partial per (q head, segment).  Each wave keeps 3 pages in
@@ -178,12 +178,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   const int ib = blockIdx.x % NBT;
   const int P = NBT / p.B;                        // parts per sequence when not balanced
   // waves 4k .. 4k+3 sit in issue slot k of the CU's four SIMDs, and the
-  // arbiter favours lower slots; with 8 heads the two waves of a head are
-  // taken from slots 0 and 3, or 1 and 2, so every head gets about the same
-  // issue share
-  const int wq = w >> 2;                          // issue slot of this wave
-  const int wpos = (HG == 8 && (wq == 2 || wq == 3)) ? (w ^ 4) : w;
-  const int jl = wpos % HG;                       // head within the group
+  // arbiter favours lower slots; with at most 4 heads per block, wave w
+  // serving head w % HG puts every head's waves in every issue slot
+  const int jl = w % HG;                          // head within the group
   const bool live = hg * HG + jl < p.Hkv;         // a last group may be short
   const int j = live ? hg * HG + jl : 0;          // this wave's KV head
   const int r16 = lane & 15, kb = lane >> 4;      // row-in-16 and lane group
@@ -653,11 +650,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     const int c = idx % D, hh = (idx / D) % GQ, jl2 = idx / (D * GQ);
     const int j2 = hg * HG + jl2;
     if (j2 >= p.Hkv) break;                       // the rest of idx is past the group too
-    // the waves of head jl2: wpos = jl2 + HG*k, and the wpos map is its own inverse
-    auto wave_of = [&](int k) {
-      const int wp = jl2 + HG * k;
-      return (HG == 8 && ((wp >> 2) == 2 || (wp >> 2) == 3)) ? (wp ^ 4) : wp;
-    };
+    auto wave_of = [&](int k) { return jl2 + HG * k; };   // the waves of head jl2
     float M = -INFINITY;
     for (int k = 0; k < WH; ++k) M = fmaxf(M, mlw[wave_of(k)][hh][0]);
     float O = 0.f, L = 0.f;

@@ -171,11 +171,11 @@ def test_plan_resolves_int2_kernel():
 
 def test_plan_chunking_rules():
     # batch 32 x 8 KV heads, 6000 history pages: the matrix-core kernel aims at
-    # 256 blocks of (sequence, 8 KV heads, part) -> 8 parts; the VALU kernel at
-    # 2048 (sequence, KV head, chunk) units -> 8 chunks
+    # 256 blocks of (sequence, pair of KV heads, part) -> 2 parts; the VALU
+    # kernel at 2048 (sequence, KV head, chunk) units -> 8 chunks
     big = dict(batch=32, hist_stride=6000, max_hist_len=6000 * 16)
     st, s, p, w, k = _plan(_cache(), _args(**big))
-    assert st == 0 and k == ob.INT2_MFMA and s == 8 and p * s >= 6000 and p * (s - 1) < 6000
+    assert st == 0 and k == ob.INT2_MFMA and s == 2 and p * s >= 6000 and p * (s - 1) < 6000
     st, s, *_ = _plan(_cache(), _args(int2_kernel=ob.INT2_VALU, **big))
     assert st == 0 and s == 8
     # explicit chunk counts are capped by 1024 and by the page count
@@ -191,12 +191,12 @@ def test_plan_chunking_rules():
     # one KV head per block: 32 sequences x 8 parts still fill 256 blocks
     st, s, *_ = _plan(_cache(num_kv_heads=1), _args(num_q_heads=4, **big))
     assert st == 0 and s == 8
-    # a single long sequence fills the chip: 256 parts of >= 16 pages
+    # a single long sequence fills the chip: 4 pairs of KV heads x 64 parts
     st, s, p, *_ = _plan(_cache(), _args(batch=1, hist_stride=6400, max_hist_len=6400 * 16))
-    assert st == 0 and s == 256 and p == 25
+    assert st == 0 and s == 64 and p == 100
     # ... unless its history is short: parts of at least 8 pages
-    st, s, p, *_ = _plan(_cache(), _args(batch=1, hist_stride=640, max_hist_len=640 * 16))
-    assert st == 0 and s == 80 and p == 8
+    st, s, p, *_ = _plan(_cache(), _args(batch=1, hist_stride=320, max_hist_len=320 * 16))
+    assert st == 0 and s == 40 and p == 8
     # no history: one (empty) chunk
     st, s, p, *_ = _plan(_cache(), _args(max_hist_len=0))
     assert st == 0 and s == 1 and p == 0
