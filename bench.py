@@ -233,8 +233,16 @@ def run_steps(st, steps, warmup, int2_kernel, keep_first_out=False, num_splits=0
     e1.record()
     torch.cuda.synchronize()
     int2_only_ms = e0.elapsed_time(e1) / n_i2
+    # the same launches with the deterministic option (static page batches)
+    a_det = a_i2[T_hot - 1].with_flags(ob.FLAG_DETERMINISTIC)
+    e0.record()
+    for _ in range(n_i2):
+        ob.decode_attn(cache, a_det, st.q[T_hot - 1], st.Rk, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    int2_det_ms = e0.elapsed_time(e1) / n_i2
     res = dict(wall_s=wall, seg_ms=seg, first_out=first_out, out=out, args=args,
-               int2_only_ms=int2_only_ms, int2_only_step=T_hot - 1,
+               int2_only_ms=int2_only_ms, int2_det_ms=int2_det_ms, int2_only_step=T_hot - 1,
                ms_separate=1000.0 * wall_sep / E if E else float("nan"))
     if steps:
         res["graph"] = time_graph(one, T_hot - 1, steps, out)
@@ -632,6 +640,10 @@ def main(argv=None):
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": tr, "kernel": kname,
                      "alg_bytes_per_launch": i2_last, "launch_ms": r["int2_only_ms"]},
+        "int2_deterministic": {"launch_ms": r["int2_det_ms"],
+                               "frac": i2_last / (r["int2_det_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                               "what": "the INT2 launch with OSCAR_FLAG_DETERMINISTIC (static page "
+                                       "batches per wave: bitwise-repeatable outputs)"},
     }
     if cold_steps:
         for name in ("read", "write"):

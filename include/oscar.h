@@ -83,6 +83,16 @@ enum {
   OSCAR_PHASE_ALL = 7
 };
 
+/* Options of oscar_decode_attn / oscar_decode_step (bit mask). */
+enum {
+  OSCAR_FLAG_DETERMINISTIC = 1  /* the matrix-core INT2 kernel assigns history
+                                   pages to its waves statically instead of
+                                   from a shared counter, so a call's outputs
+                                   are bitwise the same on every run (the other
+                                   kernels always are); slower when the waves
+                                   of a compute unit progress unevenly        */
+};
+
 /* Which kernel computes the INT2 segment.  AUTO picks MFMA when every KV head
  * serves 4 or 8 q heads, else VALU; asking for MFMA with another ratio is
  * EUNSUPPORTED from every call that takes the arguments.  The MFMA kernel
@@ -138,6 +148,7 @@ typedef struct {
                                 on two streams or between timing events); the
                                 INT2 phase reads the rotated query that the QROT
                                 phase writes into the workspace                 */
+  uint32_t flags;            /* OR of OSCAR_FLAG_*; 0 = defaults                  */
 } oscar_decode_args;
 
 /* Bytes of one INT2 page record: 2*16*(D/4) + 2*16*(D/G)*4. */

@@ -22,6 +22,7 @@ OSCAR_EHIP = -4
 
 INT2_AUTO, INT2_VALU, INT2_MFMA, HISTORY_BF16 = 0, 1, 2, 3
 PHASE_QROT, PHASE_BF16, PHASE_INT2, PHASE_ALL = 1, 2, 4, 7
+FLAG_DETERMINISTIC = 1
 PAGE = 16
 SINK, RECENT = 64, 256
 MAX_BF16 = SINK + RECENT
@@ -59,6 +60,7 @@ class OscarDecodeArgs(ctypes.Structure):
         ("num_splits", ctypes.c_int32),
         ("int2_kernel", ctypes.c_int32),
         ("phases", ctypes.c_uint32),
+        ("flags", ctypes.c_uint32),
     ]
 
 
@@ -193,7 +195,7 @@ class DecodeArgs:
 
     def __init__(self, batch, num_q_heads, hist_pages, hist_len, bf16_pages, bf16_len,
                  max_hist_len, kv_head_of_q=None, sm_scale=0.0, num_splits=0, int2_kernel=INT2_AUTO,
-                 phases=0):
+                 phases=0, flags=0):
         self.hist_pages, self.hist_len = hist_pages, hist_len
         self.bf16_pages, self.bf16_len = bf16_pages, bf16_len
         self._map = None
@@ -204,7 +206,8 @@ class DecodeArgs:
             _ptr(hist_pages) if hist_pages is not None and hist_pages.numel() else None,
             int(hist_pages.shape[1]) if hist_pages is not None and hist_pages.dim() == 2 else 0,
             _ptr(hist_len), _ptr(bf16_pages), int(bf16_pages.shape[1]), _ptr(bf16_len),
-            int(max_hist_len), float(sm_scale), int(num_splits), int(int2_kernel), int(phases))
+            int(max_hist_len), float(sm_scale), int(num_splits), int(int2_kernel), int(phases),
+            int(flags))
 
     def with_phases(self, phases: int) -> "DecodeArgs":
         """A copy of these arguments restricted to some oscar_decode_attn phases."""
@@ -212,6 +215,12 @@ class DecodeArgs:
         other.__dict__.update(self.__dict__)
         other.c = OscarDecodeArgs.from_buffer_copy(self.c)
         other.c.phases = int(phases)
+        return other
+
+    def with_flags(self, flags: int) -> "DecodeArgs":
+        """A copy of these arguments with other OSCAR_FLAG_* options."""
+        other = self.with_phases(self.c.phases)
+        other.c.flags = int(flags)
         return other
 
 

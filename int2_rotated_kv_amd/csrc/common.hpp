@@ -94,6 +94,7 @@ struct DecodeParams {
   int splits, pages_per_split;   // partial slots per (sequence, q head); nominal pages
   int mfma_parts;      // matrix-core kernel: blocks per head group = B * mfma_parts
   int mfma_balanced;   // matrix-core kernel: may balance blocks across sequences
+  int deterministic;   // matrix-core kernel: static page batches per wave
   uint8_t *ws;
   WsLayout L;
   int16_t q_of_kv[OSCAR_MAX_Q_HEADS];  // [Hkv][g] q heads of each KV head

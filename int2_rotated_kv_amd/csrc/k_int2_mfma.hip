@@ -373,7 +373,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   // pages of the segment from that head's LDS counter, so waves the SIMD
   // arbiter favours (older waves) take more pages and a head's waves finish
   // together.  A batch is taken when its first page is about to be requested.
+  // With the deterministic option the k-th batch of the i-th wave of a head
+  // is batch i + WH*k of the segment: which pages a wave sums, and so every
+  // rounding, no longer depends on timing.
+  int ngrab = 0;                                  // batches this wave took (uniform)
+  const int wih = w / HG;                         // this wave's index among its head's
   auto grab = [&]() -> int {                      // start page of the next batch
+    if (p.deterministic) return pbeg + (wih + WH * ngrab++) * NB;
     int v = 0;
     if (lane == 0) v = atomicAdd(&batch_ctr[jl], NB);
     return pbeg + __builtin_amdgcn_readfirstlane(v);

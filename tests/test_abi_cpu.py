@@ -101,6 +101,7 @@ def test_workspace_bytes_valid():
     ({}, dict(num_splits=-2), ob.OSCAR_EINVAL),
     ({}, dict(int2_kernel=7), ob.OSCAR_EINVAL),
     ({}, dict(phases=8), ob.OSCAR_EINVAL),
+    ({}, dict(flags=2), ob.OSCAR_EINVAL),
 ])
 def test_invalid_arguments_rejected(ckw, akw, want):
     st, _ = _ws(_cache(**ckw), _args(**akw))

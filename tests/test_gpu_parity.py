@@ -151,7 +151,7 @@ def test_fused_step_matches_separate_calls(shape, kernel):
     elif shape == "d128g8":
         wl = synth.workload("tiny", B=2, Hkv=2, Hq=16, D=128, G=128, lengths=(2500, 999), steps=3, seed=34)
     else:
-        # batch >= 4: the BF16 segment runs in blocks appended to the INT2 launch
+        # batch 8, mixed lengths: blocks of the INT2 kernel cover several sequences
         wl = synth.workload("tiny", B=8, Hkv=2, Hq=8, D=128, G=64,
                             lengths=(2000, 330, 500, 340, 900, 1200, 321, 700), steps=3, seed=35)
     if kernel == 2 and wl.g not in (4, 8):
@@ -207,9 +207,9 @@ def test_block_balancing(case):
 
 @pytest.mark.parametrize("Hkv,Hq,D,G", [(16, 64, 64, 32), (6, 24, 128, 64), (3, 24, 64, 64)])
 def test_head_groups(Hkv, Hq, D, G):
-    """KV-head counts other than 8 on the matrix-core kernel: two groups of 8
-    heads per sequence (16), a last group with dead heads (6 of 8), and a block
-    of 4 heads with one dead (3 heads, 8 q heads per KV head); several
+    """KV-head counts other than 8 on the matrix-core kernel (blocks cover a
+    pair of KV heads): 8 pairs per sequence (16 heads), 3 pairs (6 heads), and
+    a last pair with a dead head (3 heads, 8 q heads per KV head); several
     sequences, so blocks are balanced across them; also through the fused
     decode step."""
     _say("case: head groups", Hkv, Hq, D, G)
@@ -271,3 +271,35 @@ def test_bulk_quantise_order_and_splits():
             pad = lambda x: np.concatenate([x[a:e], np.zeros((16 - (e - a),) + x.shape[1:], x.dtype)])
             want = orc.encode_record(pad(kc), pad(ks), pad(kz), pad(vc), pad(vs), pad(vz), wl.D, wl.G)
             assert np.array_equal(base[phys[pg], j], want), f"page {pg} head {j}"
+
+
+@pytest.mark.parametrize("shape", ["b8_mixed", "qwen3-8b-32k"])
+def test_deterministic_option(shape):
+    """OSCAR_FLAG_DETERMINISTIC: the matrix-core kernel's waves take static
+    page batches, so two runs on freshly built caches give bitwise the same
+    outputs, and the fused step gives bitwise the outputs of the separate
+    calls; both within the oracle bar, and within 5e-4 of the default
+    (dynamic) schedule.  Batch 8 with mixed lengths puts several sequences in
+    one block; the 32K layer gives each block long parts."""
+    from int2_rotated_kv_amd import binding as ob
+    _say("case: deterministic option", shape)
+    if shape == "b8_mixed":
+        wl = synth.workload("tiny", B=8, Hkv=2, Hq=8, D=128, G=64,
+                            lengths=(2000, 330, 500, 340, 900, 1200, 321, 700), steps=2, seed=61)
+    else:
+        wl = synth.workload("qwen3-8b-32k", steps=2)
+    inp = synth.make_small(wl)
+    det = dict(steps=2, int2_kernel=2, flags=ob.FLAG_DETERMINISTIC)
+    a = sh.build_and_step(inp, **det)
+    b = sh.build_and_step(inp, **det)
+    c = sh.build_and_step(inp, fused=True, **det)
+    for other, what in ((b, "second run"), (c, "fused step")):
+        assert np.array_equal(a.out.view(np.uint32), other.out.view(np.uint32)), f"{what}: outputs differ"
+        assert np.array_equal(a.lse.view(np.uint32), other.lse.view(np.uint32)), f"{what}: lse differ"
+    dyn = sh.build_and_step(inp, steps=2, int2_kernel=2)
+    e = sh.row_rel_err(a.out.astype(np.float64), dyn.out.astype(np.float64))
+    assert e.max() < 5e-4 and np.abs(a.lse - dyn.lse).max() < 1e-4
+    ref = sh.oracle_step(inp, steps=2)
+    _check_bytes(a, inp, ref)
+    w = _check_out(a, ref)
+    _say(f"deterministic: bitwise repeatable, worst row rel err {w:.3e}, vs dynamic {e.max():.2e}")
