@@ -4,11 +4,13 @@ Qwen3-32B-shaped shared-prefix batch), built and run in the configuration
 bench.py times (automatic kernel choice and chunking), one decode step.
 Checked against the oracle on sampled outputs:
 
-* every q head of the first and the last sequence: outputs within 2e-3 row
-  relative error, lse within 1e-3 (the oracle quantises the sequence's
-  history from the same generated tokens, in fp64, and attends it);
+* every q head of the first and the last sequence (of every sequence in the
+  shared-prefix batch): outputs within 2e-3 row relative error, lse within
+  1e-3 (the oracle quantises the sequence's history from the same generated
+  tokens, in fp64, and attends it);
 * the bytes of 48 sampled history pages of those sequences (all KV heads)
-  equal the oracle's encoded records."""
+  equal the oracle's encoded records, and so do the written token rows of the
+  page that received the step's demoted token."""
 import sys
 import time
 
@@ -51,50 +53,84 @@ def _history_tokens(gen, b, hl0):
     return kh[:hl0], vh[:hl0]
 
 
-def _check_sequence(st, first_out, pool, b, rng):
+def _check_sequences(st, first_out, pool, seqs, rng):
+    """Oracle check of step 0 for the sequences `seqs`: every q head's output
+    and lse, the bytes of 48 sampled prompt pages and of the page that
+    received the demoted token.  Prompt-history pages are quantised once per
+    unique page (sequences that share a prefix or a whole prompt alias the
+    same pages), one KV head at a time."""
     from oracle import oscar_oracle as orc
     wl, gen = st.wl, st.gen
     D, G, Hkv, g = wl.D, wl.G, wl.Hkv, wl.g
-    hl0 = int(gen.hist_len0[b])
-    npg = -(-hl0 // PAGE)
-    kh, vh = _history_tokens(gen, b, hl0)
-    kb, vb = gen.bf16_tokens(b)
-    kb, vb = _u16(kb), _u16(vb)
+    f64 = synth.bf16_bits_to_f64
+    ppb = synth.LargeGen.PAGES_PER_BLOCK
+    hl0 = {b: int(gen.hist_len0[b]) for b in seqs}
+    npg = {b: -(-hl0[b] // PAGE) for b in seqs}
+    us = np.unique(np.concatenate([gen.unique_of[b, :npg[b]] for b in seqs]))
+    # prompt-history tokens of those unique pages, rows 16*i + t for us[i]
+    kh = np.empty((us.size * PAGE, Hkv, D), np.uint16)
+    vh = np.empty_like(kh)
+    for blk in np.unique(us // ppb):
+        sel = np.nonzero(us // ppb == blk)[0]
+        k, v = gen.history_block(int(blk))
+        k, v = _u16(k).reshape(ppb, PAGE, Hkv, D), _u16(v).reshape(ppb, PAGE, Hkv, D)
+        kh.reshape(-1, PAGE, Hkv, D)[sel] = k[us[sel] % ppb]
+        vh.reshape(-1, PAGE, Hkv, D)[sel] = v[us[sel] % ppb]
+    rows = {b: (np.searchsorted(us, gen.unique_of[b, :npg[b]])[:, None] * PAGE
+                + np.arange(PAGE)[None, :]).reshape(-1)[:hl0[b]] for b in seqs}
     knew, vnew, q0 = gen.step_tokens(0)
-    # step 0: the oldest recent token (position 64) is demoted, the new token appended
-    bf_k = np.concatenate([kb[:SINK], kb[SINK + 1:], _u16(knew[b:b + 1])])
-    bf_v = np.concatenate([vb[:SINK], vb[SINK + 1:], _u16(vnew[b:b + 1])])
-    hist_k = np.concatenate([kh, kb[SINK:SINK + 1]])
-    hist_v = np.concatenate([vh, vb[SINK:SINK + 1]])
-    q = synth.bf16_bits_to_f64(_u16(q0[b]))
-    sample = np.sort(rng.choice(npg - 1, size=min(48, npg - 1), replace=False))   # full prompt pages
-    phys = st.gen.hist_table[b, sample]
-    out_ref = np.zeros((wl.Hq, D))
-    lse_ref = np.zeros(wl.Hq)
+    knew, vnew, q0 = _u16(knew), _u16(vnew), _u16(q0)
+    win = {}
+    for b in seqs:
+        kb, vb = gen.bf16_tokens(b)
+        win[b] = (_u16(kb), _u16(vb))
+    out_ref = {b: np.zeros((wl.Hq, D)) for b in seqs}
+    lse_ref = {b: np.zeros(wl.Hq) for b in seqs}
+    sample = {b: np.sort(rng.choice(npg[b] - 1, size=min(48, npg[b] - 1), replace=False)) for b in seqs}
     for j in range(Hkv):
-        K = synth.bf16_bits_to_f64(hist_k[:, j])
-        V = synth.bf16_bits_to_f64(hist_v[:, j])
-        kc, ks, kz = orc.quantize_tokens(K, gen.R_k[j], G, float(gen.clip_k[j]))
-        vc, vs, vz = orc.quantize_tokens(V, gen.R_v[j], G, float(gen.clip_v[j]))
-        for pg, ph in zip(sample, phys):
-            sl = slice(pg * PAGE, (pg + 1) * PAGE)
-            want = orc.encode_record(kc[sl], ks[sl], kz[sl], vc[sl], vs[sl], vz[sl], D, G)
-            got = pool[ph, j]
-            assert np.array_equal(got, want), f"seq {b} page {pg} (physical {ph}) head {j}: bytes differ"
+        qk = orc.quantize_tokens(f64(kh[:, j]), gen.R_k[j], G, float(gen.clip_k[j]))
+        qv = orc.quantize_tokens(f64(vh[:, j]), gen.R_v[j], G, float(gen.clip_v[j]))
+        xk, xv = orc.dequant(*qk, G), orc.dequant(*qv, G)
         heads = [h for h in range(wl.Hq) if h // g == j]
-        o, l = orc.decode_attention(q[heads], np.zeros(len(heads), int),
-                                    synth.bf16_bits_to_f64(bf_k[:, j])[:, None],
-                                    synth.bf16_bits_to_f64(bf_v[:, j])[:, None],
-                                    orc.dequant(kc, ks, kz, G)[:, None], orc.dequant(vc, vs, vz, G)[:, None],
-                                    gen.R_k[j:j + 1], gen.R_v[j:j + 1])
-        out_ref[heads], lse_ref[heads] = o, l
-    got = first_out[0][b].astype(np.float64)
-    den = np.maximum(np.abs(out_ref).max(axis=1), 1e-30)
-    err = np.abs(got - out_ref).max(axis=1) / den
-    assert np.all(err <= TOL), f"seq {b}: row errors {np.sort(err)[-4:]}"
-    lerr = np.abs(first_out[1][b] - lse_ref).max()
-    assert lerr < 1e-3, f"seq {b}: lse error {lerr}"
-    return float(err.max())
+        for b in seqs:
+            kb, vb = win[b]
+            # step 0: the oldest recent token (window position 64) is demoted
+            # to history position hl0, the new token appended to the window
+            dk = orc.quantize_tokens(f64(kb[SINK:SINK + 1, j]), gen.R_k[j], G, float(gen.clip_k[j]))
+            dv = orc.quantize_tokens(f64(vb[SINK:SINK + 1, j]), gen.R_v[j], G, float(gen.clip_v[j]))
+            r = rows[b]
+            hk = [np.concatenate([a[r], d]) for a, d in zip(qk, dk)]
+            hv = [np.concatenate([a[r], d]) for a, d in zip(qv, dv)]
+            for pg in sample[b]:
+                sl = slice(pg * PAGE, (pg + 1) * PAGE)
+                want = orc.encode_record(*(a[sl] for a in hk), *(a[sl] for a in hv), D, G)
+                ph = gen.hist_table[b, pg]
+                assert np.array_equal(pool[ph, j], want), \
+                    f"seq {b} page {pg} (physical {ph}) head {j}: bytes differ"
+            pg = hl0[b] // PAGE                   # the page that received the demoted token
+            n = hl0[b] + 1 - pg * PAGE
+            got = orc.decode_record(pool[gen.hist_table[b, pg], j], D, G)
+            for a, w in zip(got, (*hk, *hv)):
+                assert np.array_equal(a[:n], w[pg * PAGE:pg * PAGE + n]), \
+                    f"seq {b} page {pg} head {j}: demoted token's page differs"
+            bf_k = np.concatenate([kb[:SINK], kb[SINK + 1:], knew[b:b + 1]])[:, j]
+            bf_v = np.concatenate([vb[:SINK], vb[SINK + 1:], vnew[b:b + 1]])[:, j]
+            xhk = np.concatenate([xk[r], orc.dequant(*dk, G)])
+            xhv = np.concatenate([xv[r], orc.dequant(*dv, G)])
+            o, l = orc.decode_attention(f64(q0[b][heads]), np.zeros(len(heads), int),
+                                        f64(bf_k)[:, None], f64(bf_v)[:, None],
+                                        xhk[:, None], xhv[:, None], gen.R_k[j:j + 1], gen.R_v[j:j + 1])
+            out_ref[b][heads], lse_ref[b][heads] = o, l
+    worst = 0.0
+    for b in seqs:
+        got = first_out[0][b].astype(np.float64)
+        den = np.maximum(np.abs(out_ref[b]).max(axis=1), 1e-30)
+        err = np.abs(got - out_ref[b]).max(axis=1) / den
+        assert np.all(err <= TOL), f"seq {b}: row errors {np.sort(err)[-4:]}"
+        lerr = np.abs(first_out[1][b] - lse_ref[b]).max()
+        assert lerr < 1e-3, f"seq {b}: lse error {lerr}"
+        worst = max(worst, float(err.max()))
+    return worst
 
 
 @pytest.mark.parametrize("workload", ["qwen3-8b-b32-100k", "qwen3-8b-100k-b1", "qwen3-32b-b16-128k"])
@@ -112,10 +148,12 @@ def test_full_size_sampled(workload):
     _say(f"step done: chunks {plan[0]}, kernel {plan[3]}, {time.time() - t0:.1f}s")
     pool = st.sc.cache.int2.cpu().numpy()
     rng = np.random.default_rng(0)
-    for b in sorted({0, st.wl.B - 1}):
-        w = _check_sequence(st, r["first_out"], pool, b, rng)
-        _say(f"sequence {b}: bytes of sampled pages exact, worst row rel err {w:.3e} "
-             f"({time.time() - t0:.1f}s)")
+    # every sequence of the shared-prefix batch (its pages are quantised once),
+    # the first and the last of the others
+    seqs = list(range(st.wl.B)) if st.wl.shared_prefix else sorted({0, st.wl.B - 1})
+    w = _check_sequences(st, r["first_out"], pool, seqs, rng)
+    _say(f"sequences {seqs}: bytes of sampled and demoted-token pages exact, worst row rel err "
+         f"{w:.3e} ({time.time() - t0:.1f}s)")
 
 
 CHECK_STEPS = (0, 1, 499, 999)
