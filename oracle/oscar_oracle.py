@@ -21,6 +21,9 @@ What it computes, and where the pages state it (page titles abbreviated:
   channels with an asymmetric bf16 scale / zero point and a clipping ratio.
 * dequant: the INT2 kernel's unpack and scale/zero-point restore ([thmotor],
   same paragraph, decode stage).
+* lloyd_max_levels / quantize_groups_codebook / dequant_codebook: the Lloyd-Max
+  codebook variant ([thmotor], closing paragraph; reading in the section
+  comment above those functions).
 * decode_attention: one softmax over the BF16 sink/recent tokens and the INT2
   history together; the history contribution is computed in the rotated basis
   and un-rotated by R_v^T.  decode_attention_split + lse_merge: the same result
@@ -193,6 +196,92 @@ def dequant(codes, s_b, z_b, G: int) -> np.ndarray:
     n, D = codes.shape
     cg = codes.reshape(n, D // G, G)
     return (cg * s_b[:, :, None] + z_b[:, :, None]).reshape(n, D)
+
+
+# ----------------------------------------------------------------------------
+# Lloyd-Max codebook variant
+# ----------------------------------------------------------------------------
+# [thmotor], closing paragraph: the authors' latest code adds a Lloyd-Max
+# codebook to the attention-aware rotation.  The page says nothing more.
+# Reading taken: the group scale/zero and clipping stay as above; the 4 levels
+# of a code are not 0, 1, 2, 3 but a non-uniform codebook L (ascending, in
+# units of the group scale above the zero point) per (KV head, K|V), fixed by
+# offline calibration like R and the clip ratio:
+#     x_hat = zero_b + scale_b * L[code]
+# and a code is the nearest level, with the decision thresholds at the level
+# midpoints.  L = (0, 1, 2, 3) is the uniform quantiser.  Parity unpinned
+# against the pages (they give no level values); pinned by the uniform special
+# case, brute force, and Lloyd-Max's textbook solution for a Gaussian.
+
+def lloyd_max_levels(samples, n_levels: int = 4, init=None, iters: int = 200) -> np.ndarray:
+    """Lloyd's algorithm on 1-D samples (Lloyd 1957 / Max 1960): alternate
+    decision thresholds at the midpoints of adjacent levels and levels at the
+    mean of the samples between their thresholds, until the levels stop
+    moving.  Returns the ascending levels (float64).  A level whose cell is
+    empty keeps its value."""
+    x = np.sort(np.asarray(samples, dtype=np.float64).ravel())
+    if init is None:
+        lv = np.quantile(x, (np.arange(n_levels) + 0.5) / n_levels)
+    else:
+        lv = np.array(init, dtype=np.float64)
+    for _ in range(iters):
+        th = 0.5 * (lv[:-1] + lv[1:])
+        cell = np.searchsorted(th, x, side="left")      # x <= th[0] -> cell 0
+        new = lv.copy()
+        for k in range(n_levels):
+            sel = x[cell == k]
+            if sel.size:
+                new[k] = sel.mean()
+        if np.array_equal(new, lv):
+            break
+        lv = new
+    return lv
+
+
+def codebook_thresholds(levels) -> np.ndarray:
+    """Decision thresholds of a 4-level codebook given as float32 values:
+    (L_k + L_{k+1}) / 2 in fp64 (both exact, the sum and the halving exact
+    too for float32 inputs)."""
+    L = np.asarray(levels, dtype=np.float32).astype(np.float64)
+    return 0.5 * (L[:-1] + L[1:])
+
+
+def quantize_groups_codebook(x, G: int, clip: float, levels):
+    """The group quantiser with a codebook: scale, zero and their bf16 rounding
+    exactly as quantize_groups; then u = (x - zero_b) / scale_b (one fp64
+    division) and code = the number of thresholds strictly below u, i.e. the
+    nearest level, a tie going to the lower one; 0 when scale_b == 0.
+    Returns codes uint8 [n, D], scale and zero float64 [n, D/G]."""
+    x = np.asarray(x, dtype=np.float64)
+    n, D = x.shape
+    xg = x.reshape(n, D // G, G)
+    c = float(np.float32(clip))
+    mx = xg.max(axis=2)
+    mn = xg.min(axis=2)
+    scale = (c * mx - c * mn) / 3.0
+    zero = c * mn
+    s_b = bf16_round(scale)
+    z_b = bf16_round(zero)
+    th = codebook_thresholds(levels)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = (xg - z_b[:, :, None]) / s_b[:, :, None]
+    code = (u[..., None] > th).sum(axis=-1)
+    code = np.where(s_b[:, :, None] == 0, 0, code)
+    return code.reshape(n, D).astype(np.uint8), s_b, z_b
+
+
+def dequant_codebook(codes, s_b, z_b, G: int, levels) -> np.ndarray:
+    """x_hat = zero_b + scale_b * L[code], L the float32 levels (fp64 arithmetic)."""
+    L = np.asarray(levels, dtype=np.float32).astype(np.float64)
+    codes = np.asarray(codes)
+    n, D = codes.shape
+    lv = L[codes].reshape(n, D // G, G)
+    return (z_b[:, :, None] + s_b[:, :, None] * lv).reshape(n, D)
+
+
+def quantize_tokens_codebook(kv_bf16_vals, R, G: int, clip: float, levels):
+    """Rotate, then quantise with a codebook (see quantize_groups_codebook)."""
+    return quantize_groups_codebook(rotate(kv_bf16_vals, R), G, clip, levels)
 
 
 def pack_rows(codes) -> np.ndarray:

@@ -456,3 +456,80 @@ def test_record_layout_hand_placed_d128():
     want[11] = 0x40
     want[1024 + 112 + 12:1024 + 112 + 14] = [0x00, 0x40]
     assert np.array_equal(rec, want)
+
+
+# --------------------------------------------------------------------------
+# Lloyd-Max codebook variant
+# --------------------------------------------------------------------------
+
+def test_codebook_identity_levels_are_the_uniform_quantiser():
+    """Levels (0, 1, 2, 3) reproduce quantize_groups (same codes, scales,
+    zeros) on random groups; codebook dequantisation then equals dequant."""
+    rng = np.random.default_rng(71)
+    for G in (32, 64, 128):
+        X = rng.standard_normal((500, 128)) * np.exp2(rng.integers(-6, 6, (500, 1)))
+        a = orc.quantize_groups(X, G, 0.95)
+        b = orc.quantize_groups_codebook(X, G, 0.95, (0.0, 1.0, 2.0, 3.0))
+        for p, q in zip(a, b):
+            assert np.array_equal(p, q)
+        assert np.array_equal(orc.dequant(*a, G), orc.dequant_codebook(*b, G, (0.0, 1.0, 2.0, 3.0)))
+
+
+def test_codebook_hand_worked():
+    """One group worked by hand: x = 0..7 at G = 8, clip 1 -> scale 7/3
+    (bf16 2.328125), zero 0; with levels (0.5, 1.25, 2, 2.75) the thresholds
+    are 0.875, 1.625, 2.375, and u = x / 2.328125 = 0, 0.430, 0.859, 1.289,
+    1.718, 2.148, 2.577, 3.007 gives codes 0,0,0,1,2,2,3,3 (0.859 is just
+    below the first threshold); x_hat = 2.328125 * L[code]."""
+    x = np.arange(8, dtype=np.float64)[None, :]
+    L = (0.5, 1.25, 2.0, 2.75)
+    c, s, z = orc.quantize_groups_codebook(x, 8, 1.0, L)
+    assert s[0, 0] == 2.328125 and z[0, 0] == 0.0
+    assert c[0].tolist() == [0, 0, 0, 1, 2, 2, 3, 3]
+    assert np.array_equal(orc.dequant_codebook(c, s, z, 8, L)[0], 2.328125 * np.array(L)[c[0]])
+
+
+def test_codebook_nearest_level_brute_force():
+    """Every code is the level nearest to u = (x - zero_b)/scale_b (brute force
+    over the 4 levels), for random ascending codebooks."""
+    rng = np.random.default_rng(72)
+    for _ in range(20):
+        L = np.sort(rng.uniform(-0.2, 3.2, 4)).astype(np.float32)
+        X = rng.standard_normal((40, 64)) * 2.0
+        c, s, z = orc.quantize_groups_codebook(X, 32, 0.9, L)
+        u = (X.reshape(40, 2, 32) - z[:, :, None]) / s[:, :, None]
+        want = np.argmin(np.abs(u[..., None] - L.astype(np.float64)), axis=-1)
+        assert np.array_equal(c.reshape(40, 2, 32), want)
+
+
+def test_lloyd_max_gaussian_textbook_levels():
+    """4-level Lloyd-Max quantiser of a unit Gaussian: levels +-0.4528 and
+    +-1.510, thresholds 0 and +-0.9816, mean squared error 0.1175 (Max 1960,
+    the N = 4 row of the Gaussian table)."""
+    rng = np.random.default_rng(73)
+    x = rng.standard_normal(2_000_000)
+    x = np.concatenate([x, -x])                  # exactly symmetric sample
+    lv = orc.lloyd_max_levels(x)
+    assert np.allclose(lv, [-1.510, -0.4528, 0.4528, 1.510], atol=4e-3)
+    assert np.allclose(0.5 * (lv[:-1] + lv[1:]), [-0.9816, 0.0, 0.9816], atol=4e-3)
+    th = 0.5 * (lv[:-1] + lv[1:])
+    mse = np.mean((x - lv[np.searchsorted(th, x)]) ** 2)
+    assert abs(mse - 0.1175) < 1e-3
+
+
+def test_lloyd_max_uniform_and_distortion():
+    """On a uniform sample over [0, 3] the levels are the cell midpoints
+    3(2k+1)/8; started from the uniform levels on Gaussian-shaped group values,
+    the fitted codebook never has a larger quantisation error than the uniform
+    one (each Lloyd step lowers the distortion)."""
+    rng = np.random.default_rng(74)
+    lv = orc.lloyd_max_levels(rng.uniform(0.0, 3.0, 1_000_000))
+    assert np.allclose(lv, 3.0 * (2 * np.arange(4) + 1) / 8, atol=5e-3)
+    X = rng.standard_normal((4000, 64))
+    c, s, z = orc.quantize_groups(X, 64, 0.95)
+    u = ((X.reshape(4000, 1, 64) - z[:, :, None]) / s[:, :, None]).ravel()
+    L = orc.lloyd_max_levels(u, init=(0.0, 1.0, 2.0, 3.0)).astype(np.float32)
+    err_u = np.mean((orc.dequant(c, s, z, 64) - X) ** 2)
+    cb = orc.quantize_groups_codebook(X, 64, 0.95, L)
+    err_l = np.mean((orc.dequant_codebook(*cb, 64, L) - X) ** 2)
+    assert err_l < err_u
