@@ -43,13 +43,15 @@ class BenchState:
     pass
 
 
-def build_workload(name: str, total_steps: int, device="cuda", log=print, bf16_history=False):
+def build_workload(name: str, total_steps: int, device="cuda", log=print, bf16_history=False,
+                   codebook=False):
     """Build the split cache of a 100K-class workload on the device and plan
     `total_steps` decode steps.  History pages are quantised by
     oscar_demote_pack from generated BF16 tokens.  With bf16_history, the same
     tokens are also laid out as the comparison cache: every history page kept
     in BF16 at its physical id (same page tables), the sink/recent pages after
-    them."""
+    them.  With codebook, the cache uses the Lloyd-Max codebook variant (seeded
+    levels from synth.make_codebook)."""
     import torch
     from int2_rotated_kv_amd import binding as ob
     from int2_rotated_kv_amd.splitcache import SplitCache
@@ -57,8 +59,10 @@ def build_workload(name: str, total_steps: int, device="cuda", log=print, bf16_h
     wl = synth.workload(name, steps=total_steps)
     gen = synth.LargeGen(wl, device=device)
     t0 = time.time()
+    cb = synth.make_codebook(wl.seed, wl.Hkv) if codebook else None
     sc = SplitCache(wl.B, wl.Hkv, wl.Hq, wl.D, wl.G, gen.hist_table, gen.n_unique,
-                    staging_pages=synth.LargeGen.PAGES_PER_BLOCK, device=device)
+                    staging_pages=synth.LargeGen.PAGES_PER_BLOCK, device=device,
+                    codebook=None if cb is None else torch.from_numpy(cb).to(device))
     Rk = torch.from_numpy(gen.R_k).to(device)
     Rv = torch.from_numpy(gen.R_v).to(device)
     ck = torch.from_numpy(gen.clip_k).to(device)
@@ -115,6 +119,7 @@ def build_workload(name: str, total_steps: int, device="cuda", log=print, bf16_h
     sc.hist_len_h[:], sc.bf16_len_h[:], sc.ring_head[:] = h0, b0, r0
     st = BenchState()
     st.wl, st.gen, st.sc = wl, gen, sc
+    st.codebook_h = cb
     st.Rk, st.Rv, st.ck, st.cv = Rk, Rv, ck, cv
     dev = lambda x: torch.from_numpy(x).to(device)
     st.dsrc, st.ddst, st.wdst, st.hl, st.bl = dev(dsrc), dev(ddst), dev(wdst), dev(hl), dev(bl)
@@ -457,11 +462,19 @@ def oracle_step0(st, b, timed=True):
     lse_ref = np.zeros(wl.Hq)
     records = {}
     spent = 0.0
+    cb = getattr(st, "codebook_h", None)
     for j in range(Hkv):
+        # the uniform quantiser, or the Lloyd-Max codebook variant
+        if cb is None:
+            quant = lambda x, R, clip, kv: orc.quantize_tokens(x, R, G, clip)
+            deq = lambda c, s, z, kv: orc.dequant(c, s, z, G)
+        else:
+            quant = lambda x, R, clip, kv: orc.quantize_tokens_codebook(x, R, G, clip, cb[j, kv])
+            deq = lambda c, s, z, kv: orc.dequant_codebook(c, s, z, G, cb[j, kv])
         K = synth.bf16_bits_to_f64(kh[:, j])
         V = synth.bf16_bits_to_f64(vh[:, j])
-        kc, ks, kz = orc.quantize_tokens(K, gen.R_k[j], G, float(gen.clip_k[j]))
-        vc, vs, vz = orc.quantize_tokens(V, gen.R_v[j], G, float(gen.clip_v[j]))
+        kc, ks, kz = quant(K, gen.R_k[j], float(gen.clip_k[j]), 0)
+        vc, vs, vz = quant(V, gen.R_v[j], float(gen.clip_v[j]), 1)
         recs = []
         for pg in range(npg):
             a_, e_ = pg * PAGE, min(hl0, pg * PAGE + PAGE)
@@ -471,13 +484,13 @@ def oracle_step0(st, b, timed=True):
         records[j] = recs
         heads = [h for h in range(wl.Hq) if h // g == j]
         t0 = time.perf_counter()
-        dk = orc.quantize_tokens(synth.bf16_bits_to_f64(dem_k[j])[None], gen.R_k[j], G, float(gen.clip_k[j]))
-        dv = orc.quantize_tokens(synth.bf16_bits_to_f64(dem_v[j])[None], gen.R_v[j], G, float(gen.clip_v[j]))
+        dk = quant(synth.bf16_bits_to_f64(dem_k[j])[None], gen.R_k[j], float(gen.clip_k[j]), 0)
+        dv = quant(synth.bf16_bits_to_f64(dem_v[j])[None], gen.R_v[j], float(gen.clip_v[j]), 1)
         parts = [orc.decode_record(r, D, G) for r in recs]
-        khat = np.concatenate([orc.dequant(p_[0], p_[1], p_[2], G) for p_ in parts])[:hl0]
-        vhat = np.concatenate([orc.dequant(p_[3], p_[4], p_[5], G) for p_ in parts])[:hl0]
-        khat = np.concatenate([khat, orc.dequant(*dk, G)])
-        vhat = np.concatenate([vhat, orc.dequant(*dv, G)])
+        khat = np.concatenate([deq(p_[0], p_[1], p_[2], 0) for p_ in parts])[:hl0]
+        vhat = np.concatenate([deq(p_[3], p_[4], p_[5], 1) for p_ in parts])[:hl0]
+        khat = np.concatenate([khat, deq(*dk, 0)])
+        vhat = np.concatenate([vhat, deq(*dv, 1)])
         o, l = orc.decode_attention(q[heads], np.zeros(len(heads), int),
                                     synth.bf16_bits_to_f64(bf_k[:, j])[:, None],
                                     synth.bf16_bits_to_f64(bf_v[:, j])[:, None],
@@ -570,6 +583,9 @@ def main(argv=None):
     ap.add_argument("--no-bf16-compare", action="store_true",
                     help="skip the comparison run over the same tokens with the whole "
                          "history kept in BF16 pages")
+    ap.add_argument("--codebook", action="store_true",
+                    help="use the Lloyd-Max codebook variant of the INT2 history (seeded levels; "
+                         "attended by the vector-ALU kernel)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run 5 plain device-to-device copies of BYTES bytes (the "
                          "reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE) and exit")
@@ -594,7 +610,7 @@ def main(argv=None):
     torch.cuda.set_device(0)
     cold_steps = a.steps if a.cold else 0
     st = build_workload(a.workload, a.steps + a.warmup + breakdown_steps(a.steps) + 2 * cold_steps,
-                        log=log, bf16_history=not a.no_bf16_compare)
+                        log=log, bf16_history=not a.no_bf16_compare, codebook=a.codebook)
     wl = st.wl
     r = run_steps(st, a.steps, a.warmup, kern, keep_first_out=not a.no_cpu_baseline,
                   num_splits=a.splits, cold_steps=cold_steps)
@@ -628,7 +644,8 @@ def main(argv=None):
         "config": {"workload": wl.name, "batch": wl.B, "kv_heads": wl.Hkv, "q_heads": wl.Hq,
                    "head_dim": wl.D, "group": wl.G, "mean_context": float(np.mean(wl.lengths)),
                    "sink": SINK, "recent": RECENT, "page": PAGE, "int2_kernel": kname,
-                   "splits": splits, "parallelism": "single-gpu"},
+                   "splits": splits, "codebook": "lloyd-max" if a.codebook else "uniform",
+                   "parallelism": "single-gpu"},
         "hbm_tbps": step_bytes / (ms_step * 1e-3) / 1e12,
         "hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "ms_per_step_separate_calls": r["ms_separate"],

@@ -45,7 +45,8 @@
  *                   bits 0..15 and bf16 zero in bits 16..31
  *   A reader lane l takes slot l and token slot l % 16 with one 16-byte load
  *   each (D = 128, G = 64).
- *   Codes are in {0,1,2,3}; the dequantised rotated value is code*scale + zero.
+ *   Codes are in {0,1,2,3}; the dequantised rotated value is code*scale + zero
+ *   (zero + scale*level[code] with a codebook, see oscar_cache.codebook).
  *   BF16 pools: uint16 [num_bf16_pages][Hkv][16][D], one for K and one for V.
  *   A token slot is page*16 + offset within the page.
  */
@@ -119,6 +120,18 @@ typedef struct {
   uint16_t *bf16_k_pool;     /* [num_bf16_pages][Hkv][16][D]                    */
   uint16_t *bf16_v_pool;
   int64_t num_bf16_pages;
+  const float *codebook;     /* [Hkv][2][4] fp32 or NULL.  Lloyd-Max codebook
+                                variant (thmotor, closing paragraph): per KV
+                                head the 4 levels of the K codes, then of the V
+                                codes, ascending and finite, in units of the
+                                group scale above the zero point; a code then
+                                stands for zero + scale * level and is chosen
+                                as the nearest level (thresholds at the
+                                midpoints, a tie to the lower level).  NULL =
+                                the uniform levels 0, 1, 2, 3.  Only the vector-
+                                ALU INT2 kernel reads codebooks (AUTO picks it;
+                                asking for MFMA is EUNSUPPORTED).  Level order
+                                and finiteness are not checked (device memory) */
 } oscar_cache;
 
 typedef struct {

@@ -41,6 +41,7 @@ class OscarCache(ctypes.Structure):
         ("bf16_k_pool", ctypes.c_void_p),
         ("bf16_v_pool", ctypes.c_void_p),
         ("num_bf16_pages", ctypes.c_int64),
+        ("codebook", ctypes.c_void_p),
     ]
 
 
@@ -148,12 +149,19 @@ class Cache:
     int2   uint8  [num_int2_pages, Hkv, record_bytes(D, G)]
     bf16_k uint16 [num_bf16_pages, Hkv, 16, D]   (bf16 bit patterns; view as
     bf16_v uint16 [num_bf16_pages, Hkv, 16, D]    torch.bfloat16 when needed)
+    codebook float32 [Hkv, 2, 4] device tensor or None: the Lloyd-Max code levels
+           of K and V per KV head (None: the uniform levels 0, 1, 2, 3)
     """
 
     def __init__(self, Hkv: int, D: int, G: int, num_int2_pages: int, num_bf16_pages: int,
-                 device="cuda", int2=None, bf16_k=None, bf16_v=None):
+                 device="cuda", int2=None, bf16_k=None, bf16_v=None, codebook=None):
         import torch
         self.Hkv, self.D, self.G = Hkv, D, G
+        if codebook is not None:
+            if tuple(codebook.shape) != (Hkv, 2, 4) or codebook.dtype != torch.float32:
+                raise ValueError("codebook must be a float32 tensor of shape [Hkv, 2, 4]")
+            codebook = codebook.contiguous()
+        self.codebook = codebook
         self.rec = record_bytes(D, G)
         if self.rec == 0:
             raise OscarError(OSCAR_EUNSUPPORTED, f"no record layout for D={D}, G={G}")
@@ -168,7 +176,8 @@ class Cache:
     def desc(self) -> OscarCache:
         return OscarCache(self.Hkv, self.D, self.G, PAGE, _ptr(self.int2) if self.int2.numel() else 0,
                           self.num_int2_pages, _ptr(self.bf16_k) if self.bf16_k.numel() else 0,
-                          _ptr(self.bf16_v) if self.bf16_v.numel() else 0, self.num_bf16_pages)
+                          _ptr(self.bf16_v) if self.bf16_v.numel() else 0, self.num_bf16_pages,
+                          _ptr(self.codebook) if self.codebook is not None else None)
 
 
 def write_bf16(cache: Cache, dst_slots, k_new, v_new, stream=None):

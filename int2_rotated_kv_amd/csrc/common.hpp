@@ -95,6 +95,7 @@ struct DecodeParams {
   int mfma_parts;      // matrix-core kernel: blocks per head group = B * mfma_parts
   int mfma_balanced;   // matrix-core kernel: may balance blocks across sequences
   int deterministic;   // matrix-core kernel: static page batches per wave
+  const float *codebook;   // [Hkv][2][4] code levels (K, V) or nullptr = 0, 1, 2, 3
   uint8_t *ws;
   WsLayout L;
   int16_t q_of_kv[OSCAR_MAX_Q_HEADS];  // [Hkv][g] q heads of each KV head

@@ -10,7 +10,8 @@
 //   mx, mn = max, min over the G consecutive channels of a group
 //   scale = (c*mx - c*mn) / 3      zero = c*mn      (c = clipping ratio)
 //   s_b, z_b = bf16 round-to-nearest-even of scale, zero (directly from fp64)
-//   code = clamp(rint((x - z_b) / s_b), 0, 3), or 0 when s_b == 0
+//   code = clamp(rint((x - z_b) / s_b), 0, 3), or 0 when s_b == 0; with a
+//          Lloyd-Max codebook the nearest level (quant_code)
 #pragma once
 #include "common.hpp"
 
@@ -48,7 +49,25 @@ struct DemoteArgs {
   const int32_t *src, *dst;        // [n] slots page*16 + offset; negative = skip
   const float *Rk, *Rv;            // [Hkv][D][D]; Rv may be NULL (identity)
   const float *clip_k, *clip_v;    // [Hkv]
+  const float *codebook;           // [Hkv][2][4] code levels (K, V) or nullptr
 };
+
+// Code of rotated value x in a group with bf16 scale sd and zero zd (both as
+// fp64): with the uniform levels clamp(rint((x - zd) / sd), 0, 3); with a
+// codebook lv (4 ascending levels) the nearest level: the count of the
+// thresholds (lv[k] + lv[k+1]) / 2 strictly below u = (x - zd) / sd, every
+// step one fp64 operation.  0 when sd == 0.
+__device__ inline uint32_t quant_code(double x, double zd, double sd, const float *lv) {
+  if (sd == 0.0) return 0;
+  const double u = (x - zd) / sd;
+  if (lv == nullptr) {
+    const double qv = fmin(fmax(rint(u), 0.0), 3.0);
+    return (uint32_t)qv;
+  }
+  const double l0 = lv[0], l1 = lv[1], l2 = lv[2], l3 = lv[3];
+  return (uint32_t)(u > 0.5 * (l0 + l1)) + (uint32_t)(u > 0.5 * (l1 + l2)) +
+         (uint32_t)(u > 0.5 * (l2 + l3));
+}
 
 template <int D>
 struct DemoteOneShared {
@@ -162,12 +181,8 @@ __device__ __forceinline__ void demote_one_body(const DemoteArgs &a, int e, int 
   const uint16_t zb = f64_to_bf16_rne(lo);
   const double sd = (double)bf16_to_f32(sb);
   const double zd = (double)bf16_to_f32(zb);
-  uint32_t code = 0;
-  if (sd != 0.0) {
-    double qv = rint((x - zd) / sd);
-    qv = fmin(fmax(qv, 0.0), 3.0);
-    code = (uint32_t)qv;
-  }
+  const uint32_t code =
+      quant_code(x, zd, sd, a.codebook ? a.codebook + (j * 2 + (isv ? 1 : 0)) * 4 : nullptr);
   const int64_t page = d >> 4, off = d & 15;
   uint8_t *rec = a.pool + ((size_t)page * a.Hkv + j) * RL.bytes();
   if ((c % G) == 0) {

@@ -264,8 +264,17 @@ hipError_t launch_step_pre(const DecodeParams &p, const oscar_cache &c, const ui
 //   PV:  lane owns channels lane + 64k and accumulates
 //        sum_t (p*scale_v) * code_v; the zero-point part sum_t p*zero_v depends
 //        only on (head, group) and is accumulated on the token lanes.
+// With a Lloyd-Max codebook (CB) every code stands for its level L[code]
+// (x_hat = zero + scale * L[code]) and the same sums run over L[code].
 // ---------------------------------------------------------------------------
-template <int D, int G, int GQ>
+// level of a 2-bit code from 4 levels held in registers
+__device__ __forceinline__ float code_level(const float (&L)[4], uint32_t cd) {
+  const float lo = (cd & 1u) ? L[1] : L[0];
+  const float hi = (cd & 1u) ? L[3] : L[2];
+  return (cd & 2u) ? hi : lo;
+}
+
+template <int D, int G, int GQ, bool CB>
 __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
   constexpr RecLayout RL(D, G);
   constexpr int NG = D / G;       // groups per token (<= 4)
@@ -281,6 +290,14 @@ __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
   const int j = unit % p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int t = lane & 15, part = lane >> 4;
+  float lk[4] = {0.f, 1.f, 2.f, 3.f}, lvv[4] = {0.f, 1.f, 2.f, 3.f};   // K and V code levels
+  if constexpr (CB) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lk[i] = p.codebook[j * 8 + i];
+      lvv[i] = p.codebook[j * 8 + 4 + i];
+    }
+  }
 
   __shared__ float qs[D][GQ];                 // q_rot * sm_log2, heads innermost
   __shared__ float qword[D / 16][GQ];         // sum of q over each K word's 16 channels
@@ -358,7 +375,8 @@ __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
       for (int h = 0; h < GQ; ++h) dot[h] = 0.f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        const float cf = (float)((kw[i] >> (2 * k)) & 3u);
+        const uint32_t cd = (kw[i] >> (2 * k)) & 3u;
+        const float cf = CB ? code_level(lk, cd) : (float)cd;
 #pragma unroll
         for (int h = 0; h < GQ; ++h) dot[h] = fmaf(qs[c0 + k][h], cf, dot[h]);
       }
@@ -404,7 +422,8 @@ __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
       const int gc = c / G;
 #pragma unroll 4
       for (int tt = 0; tt < 16; ++tt) {
-        const float cf = (float)((vcw[k] >> (2 * tt)) & 3u);
+        const uint32_t cd = (vcw[k] >> (2 * tt)) & 3u;
+        const float cf = CB ? code_level(lvv, cd) : (float)cd;
 #pragma unroll
         for (int h = 0; h < GQ; ++h) o[h][k] = fmaf(pw[w][gc][tt][h], cf, o[h][k]);
       }
@@ -461,15 +480,21 @@ __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
   }
 }
 
-template <int D, int G>
-static void launch_int2_valu_dg(const DecodeParams &p, hipStream_t s) {
+template <int D, int G, bool CB>
+static void launch_int2_valu_cb(const DecodeParams &p, hipStream_t s) {
   const dim3 grid(p.B * p.Hkv * p.splits), blk(256);
   switch (p.g) {
-    case 1: hipLaunchKernelGGL((k_int2_valu<D, G, 1>), grid, blk, 0, s, p); break;
-    case 2: hipLaunchKernelGGL((k_int2_valu<D, G, 2>), grid, blk, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((k_int2_valu<D, G, 4>), grid, blk, 0, s, p); break;
-    default: hipLaunchKernelGGL((k_int2_valu<D, G, 8>), grid, blk, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((k_int2_valu<D, G, 1, CB>), grid, blk, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((k_int2_valu<D, G, 2, CB>), grid, blk, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((k_int2_valu<D, G, 4, CB>), grid, blk, 0, s, p); break;
+    default: hipLaunchKernelGGL((k_int2_valu<D, G, 8, CB>), grid, blk, 0, s, p); break;
   }
+}
+
+template <int D, int G>
+static void launch_int2_valu_dg(const DecodeParams &p, hipStream_t s) {
+  if (p.codebook != nullptr) launch_int2_valu_cb<D, G, true>(p, s);
+  else launch_int2_valu_cb<D, G, false>(p, s);
 }
 
 hipError_t launch_int2_valu(const DecodeParams &p, hipStream_t s) {

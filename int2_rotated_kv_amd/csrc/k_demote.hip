@@ -89,6 +89,7 @@ __global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
   }
 
   const double clip = (double)(isv ? a.clip_v[j] : a.clip_k[j]);
+  const float *lv = a.codebook ? a.codebook + (j * 2 + (isv ? 1 : 0)) * 4 : nullptr;
   int vpage = -1;                              // V word being gathered (uniform)
   uint32_t vmask = 0, vbits = 0;
   auto flush_v = [&]() {
@@ -127,12 +128,7 @@ __global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
     const uint16_t zb = f64_to_bf16_rne(lo);
     const double sd = (double)bf16_to_f32(sb);
     const double zd = (double)bf16_to_f32(zb);
-    uint32_t code = 0;
-    if (sd != 0.0) {
-      double qv = rint((x[t] - zd) / sd);
-      qv = fmin(fmax(qv, 0.0), 3.0);
-      code = (uint32_t)qv;
-    }
+    const uint32_t code = quant_code(x[t], zd, sd, lv);
     const int64_t page = d >> 4, off = d & 15;
     uint8_t *rec = a.pool + ((size_t)page * a.Hkv + j) * RL.bytes();
     if ((c % G) == 0) {
@@ -221,6 +217,7 @@ DemoteArgs demote_args(const oscar_cache &c, int n, const int32_t *src, const in
   a.Rv = Rv;
   a.clip_k = ck;
   a.clip_v = cv;
+  a.codebook = c.codebook;
   return a;
 }
 

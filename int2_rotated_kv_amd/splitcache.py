@@ -27,16 +27,18 @@ BF16_PAGES_PER_SEQ = MAXB // PAGE
 
 class SplitCache:
     def __init__(self, B: int, Hkv: int, Hq: int, D: int, G: int, hist_table: np.ndarray,
-                 num_int2_pages: int, staging_pages: int = 256, device="cuda"):
+                 num_int2_pages: int, staging_pages: int = 256, device="cuda", codebook=None):
         """hist_table: int32 [B][stride] physical INT2 page of each logical history
-        page (entries beyond a sequence's capacity are ignored)."""
+        page (entries beyond a sequence's capacity are ignored); codebook: float32
+        [Hkv][2][4] device tensor of Lloyd-Max code levels, or None (uniform)."""
         import torch
         self.torch = torch
         self.B, self.Hkv, self.Hq, self.D, self.G = B, Hkv, Hq, D, G
         self.device = device
         self.staging_base = B * BF16_PAGES_PER_SEQ
         self.staging_pages = staging_pages
-        self.cache = ob.Cache(Hkv, D, G, num_int2_pages, self.staging_base + staging_pages, device)
+        self.cache = ob.Cache(Hkv, D, G, num_int2_pages, self.staging_base + staging_pages, device,
+                              codebook=codebook)
         bf = np.arange(B * BF16_PAGES_PER_SEQ, dtype=np.int32).reshape(B, BF16_PAGES_PER_SEQ)
         self.bf16_pages_h = bf
         self.bf16_pages = torch.from_numpy(bf).to(device)

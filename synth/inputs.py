@@ -203,6 +203,17 @@ def _seed64(*parts) -> int:
     return int.from_bytes(h[:8], "little") & ((1 << 63) - 1)
 
 
+def make_codebook(seed: int, Hkv: int) -> np.ndarray:
+    """Lloyd-Max code levels float32 [Hkv][2][4] (K, V) for the codebook
+    variant, standing in for offline calibration: levels pulled towards the
+    middle of the group range, (0.35, 1.15, 1.85, 2.65) in units of the group
+    scale, each moved by a seeded offset in [-0.05, 0.05] so that heads and
+    K/V differ.  Ascending by construction."""
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    base = np.array([0.35, 1.15, 1.85, 2.65])
+    return (base + rng.uniform(-0.05, 0.05, (Hkv, 2, 4))).astype(np.float32)
+
+
 class LargeGen:
     """Device-side generator for 100K-class workloads.
 

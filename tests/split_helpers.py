@@ -39,7 +39,7 @@ def hist_capacity_pages(L: int, steps: int) -> int:
 
 def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_splits=0,
                    R_v_none=False, head_map=None, device="cuda", seed_perm=None, fused=False,
-                   flags=0):
+                   flags=0, codebook=None):
     """Build the initial split cache of every sequence, run `steps` decode steps
     (demote oldest recent -> write new token -> attend -> merge; with fused,
     through the single oscar_decode_step call), return the outputs of the last
@@ -59,7 +59,9 @@ def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_sp
     for b in range(B):
         table[b, :caps[b]] = perm[o:o + caps[b]]
         o += caps[b]
-    sc = SplitCache(B, wl.Hkv, wl.Hq, wl.D, wl.G, table, n_int2 + 3, staging_pages=64, device=device)
+    cb = None if codebook is None else torch.from_numpy(np.asarray(codebook, np.float32)).to(device)
+    sc = SplitCache(B, wl.Hkv, wl.Hq, wl.D, wl.G, table, n_int2 + 3, staging_pages=64, device=device,
+                    codebook=cb)
     Rk = torch.from_numpy(inp.R_k).to(device)
     Rv = None if R_v_none else torch.from_numpy(inp.R_v).to(device)
     ck = torch.from_numpy(inp.clip_k).to(device)
@@ -102,10 +104,11 @@ def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_sp
 
 
 def oracle_step(inp: synth.SmallInputs, steps: int = 1, R_v_none=False, head_map=None,
-                seqs=None, heads=None):
+                seqs=None, heads=None, codebook=None):
     """Oracle view after `steps` decode steps: history quantised from the
-    original tokens, BF16 = sink + current recent window.  Returns per sequence
-    (out [Hq][D], lse [Hq], quantised history dict)."""
+    original tokens (with codebook [Hkv][2][4]: the Lloyd-Max variant), BF16 =
+    sink + current recent window.  Returns per sequence (out [Hq][D], lse [Hq],
+    quantised history dict)."""
     wl = inp.wl
     D, G = wl.D, wl.G
     hm = np.array(head_map) if head_map is not None else orc.default_head_map(wl.Hq, wl.Hkv)
@@ -122,12 +125,20 @@ def oracle_step(inp: synth.SmallInputs, steps: int = 1, R_v_none=False, head_map
             if h == 0:
                 break
             Rv = np.eye(D) if R_v_none else inp.R_v[j]
-            c1, s1, z1 = orc.quantize_tokens(K[s:s + h, j], inp.R_k[j], G, float(inp.clip_k[j]))
-            c2, s2, z2 = orc.quantize_tokens(V[s:s + h, j], Rv, G, float(inp.clip_v[j]))
+            if codebook is None:
+                c1, s1, z1 = orc.quantize_tokens(K[s:s + h, j], inp.R_k[j], G, float(inp.clip_k[j]))
+                c2, s2, z2 = orc.quantize_tokens(V[s:s + h, j], Rv, G, float(inp.clip_v[j]))
+                khat[:, j] = orc.dequant(c1, s1, z1, G)
+                vhat[:, j] = orc.dequant(c2, s2, z2, G)
+            else:
+                lk, lv = codebook[j, 0], codebook[j, 1]
+                c1, s1, z1 = orc.quantize_tokens_codebook(K[s:s + h, j], inp.R_k[j], G,
+                                                          float(inp.clip_k[j]), lk)
+                c2, s2, z2 = orc.quantize_tokens_codebook(V[s:s + h, j], Rv, G, float(inp.clip_v[j]), lv)
+                khat[:, j] = orc.dequant_codebook(c1, s1, z1, G, lk)
+                vhat[:, j] = orc.dequant_codebook(c2, s2, z2, G, lv)
             kc[:, j], ks[:, j], kz[:, j] = c1, s1, z1
             vc[:, j], vs[:, j], vz[:, j] = c2, s2, z2
-            khat[:, j] = orc.dequant(c1, s1, z1, G)
-            vhat[:, j] = orc.dequant(c2, s2, z2, G)
         bidx = list(range(0, s)) + list(range(s + h, L))
         q = synth.bf16_bits_to_f64(inp.q[steps - 1][b])
         out, lse = orc.decode_attention(q, hm, K[bidx], V[bidx], khat, vhat, inp.R_k,

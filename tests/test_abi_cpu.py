@@ -258,3 +258,13 @@ def test_decode_step_argument_checks():
     assert _step(c, _args(phases=ob.PHASE_INT2)) == ob.OSCAR_EINVAL and "phases" in ob.last_error()
     assert _step(c, _args(int2_kernel=ob.HISTORY_BF16)) == ob.OSCAR_EUNSUPPORTED
     assert _step(c, _args(phases=ob.PHASE_ALL)) == ob.OSCAR_EWORKSPACE
+
+
+def test_codebook_cache_uses_the_valu_kernel():
+    """A cache with a Lloyd-Max codebook: AUTO resolves to the vector-ALU
+    kernel, an explicit matrix-core request is EUNSUPPORTED."""
+    st, *_, k = _plan(_cache(codebook=0x80000), _args())
+    assert st == ob.OSCAR_OK and k == ob.INT2_VALU
+    st, *_ = _plan(_cache(codebook=0x80000), _args(int2_kernel=ob.INT2_MFMA))
+    assert st == ob.OSCAR_EUNSUPPORTED
+    assert "codebook" in ob.last_error()

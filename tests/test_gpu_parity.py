@@ -303,3 +303,35 @@ def test_deterministic_option(shape):
     _check_bytes(a, inp, ref)
     w = _check_out(a, ref)
     _say(f"deterministic: bitwise repeatable, worst row rel err {w:.3e}, vs dynamic {e.max():.2e}")
+
+
+@pytest.mark.parametrize("shape", ["tiny", "d128g64", "d128g128"])
+def test_codebook_variant(shape):
+    """Lloyd-Max codebook variant: the prompt history quantised in bulk, then
+    two decode steps (one-token demotion, attention on the vector-ALU kernel,
+    which AUTO picks for a cache with a codebook), through the separate calls
+    and through oscar_decode_step.  INT2 page bytes bit-exact against the
+    oracle's nearest-level quantiser, outputs within the oracle bar, and the
+    fused step bitwise equal to the separate calls."""
+    from int2_rotated_kv_amd import binding as ob
+    _say("case: codebook variant", shape)
+    if shape == "tiny":
+        wl = synth.workload("tiny", B=2, lengths=(1024, 777), steps=2, seed=81)
+    elif shape == "d128g64":
+        wl = synth.workload("tiny", B=2, Hkv=2, Hq=8, D=128, G=64, lengths=(3000, 1700), steps=2, seed=82)
+    else:
+        wl = synth.workload("tiny", B=2, Hkv=2, Hq=16, D=128, G=128, lengths=(2500, 999), steps=2, seed=83)
+    inp = synth.make_small(wl, distinct_rv=True)
+    cb = synth.make_codebook(wl.seed, wl.Hkv)
+    sep = sh.build_and_step(inp, steps=2, int2_kernel=ob.INT2_AUTO, codebook=cb)
+    fus = sh.build_and_step(inp, steps=2, int2_kernel=ob.INT2_AUTO, codebook=cb, fused=True)
+    ref = sh.oracle_step(inp, steps=2, codebook=cb)
+    _check_bytes(sep, inp, ref)
+    _check_bytes(fus, inp, ref)
+    w = _check_out(sep, ref)
+    assert np.array_equal(sep.out.view(np.uint32), fus.out.view(np.uint32)), "fused outputs differ"
+    # the uniform quantiser would give other bytes: the codebook is really used
+    uni = sh.oracle_step(inp, steps=2)
+    assert not np.array_equal(sh.oracle_records(uni[0], wl.D, wl.G, wl.Hkv),
+                              sh.oracle_records(ref[0], wl.D, wl.G, wl.Hkv))
+    _say(f"codebook {shape}: bytes exact, worst row rel err {w:.3e}")
