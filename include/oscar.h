@@ -128,10 +128,10 @@ typedef struct {
                                 stands for zero + scale * level and is chosen
                                 as the nearest level (thresholds at the
                                 midpoints, a tie to the lower level).  NULL =
-                                the uniform levels 0, 1, 2, 3.  Only the vector-
-                                ALU INT2 kernel reads codebooks (AUTO picks it;
-                                asking for MFMA is EUNSUPPORTED).  Level order
-                                and finiteness are not checked (device memory) */
+                                the uniform levels 0, 1, 2, 3.  Both INT2
+                                kernels read it (the matrix-core one with two
+                                more bit-plane contractions).  Level order and
+                                finiteness are not checked (device memory)   */
 } oscar_cache;
 
 typedef struct {

@@ -135,15 +135,11 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   const float sm = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt((float)c->head_dim);
   p->sm_log2 = sm * kLog2e;
 
-  // INT2 kernel: the matrix-core one needs 4 or 8 q heads per KV head and
-  // the uniform code levels
+  // INT2 kernel: the matrix-core one needs 4 or 8 q heads per KV head
   p->codebook = c->codebook;
-  const bool mfma_ok = (p->g == 4 || p->g == 8) && c->codebook == nullptr;
+  const bool mfma_ok = p->g == 4 || p->g == 8;
   int kind = a->int2_kernel;
   if (kind == OSCAR_INT2_AUTO) kind = mfma_ok ? OSCAR_INT2_MFMA : OSCAR_INT2_VALU;
-  if (kind == OSCAR_INT2_MFMA && c->codebook != nullptr)
-    return fail(OSCAR_EUNSUPPORTED, "the matrix-core INT2 kernel reads uniform code levels only "
-                                    "(the cache has a codebook)");
   if (kind == OSCAR_INT2_MFMA && !mfma_ok)
     return fail(OSCAR_EUNSUPPORTED,
                 "matrix-core INT2 kernel needs 4 or 8 q heads per KV head (got %d)", p->g);

@@ -141,17 +141,18 @@ __device__ __forceinline__ void buf_words(uint32_t (&dst)[NW], __amdgpu_buffer_r
 constexpr int kPidCap = 1024;                   // page ids of a segment staged in LDS
 
 // LDS of the matrix-core kernel
-template <int D, int G, int GQ>
+template <int D, int G, int GQ, int NP>
 struct Int2Shared {
   int cum[kMaxBalancedBatch + 1];                 // pages before sequence b
   int wsum[kMfmaWaves];
   int batch_ctr[8];                               // per head: next batch of the segment
   int pid_lds[kPidCap];
   float qf_all[kMfmaWaves][GQ][D];                // per wave: its partial outputs at the end
-  __align__(16) _Float16 wbuf_all[kMfmaWaves][D / G][GQ][16];   // per wave: w[grp][head][slot]
+  // per wave and code plane: w[plane][grp][head][slot]
+  __align__(16) _Float16 wbuf_all[kMfmaWaves][NP][D / G][GQ][16];
   float mlw[kMfmaWaves][GQ][2];
 };
-template <int D, int G, int GQ>
+template <int D, int G, int GQ, bool CB>
 __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   constexpr RecLayout RL(D, G);
   constexpr int NG = D / G;            // groups per token
@@ -163,7 +164,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   constexpr int HB = kMfmaWaves;
   static_assert(GQ == 4 || GQ == 8, "4 or 8 q heads per KV head");
 
-  __shared__ Int2Shared<D, G, GQ> lds;
+  constexpr int NP = CB ? 3 : 1;       // code planes: the codes; with a codebook also b0, b0&b1
+  __shared__ Int2Shared<D, G, GQ, NP> lds;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave (uniform)
   // block = (group of HG KV heads, block index within the group); WH waves
@@ -184,6 +186,26 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   const bool live = hg * HG + jl < p.Hkv;         // a last group may be short
   const int j = live ? hg * HG + jl : 0;          // this wave's KV head
   const int r16 = lane & 15, kb = lane >> 4;      // row-in-16 and lane group
+
+  // Lloyd-Max codebook: the level of code c = b0 + 2*b1 is
+  //   L[c] = L0 + cA*c + cB*b0 + cC*b0*b1,
+  //   cA = (L2 - L0)/2, cB = (L1 - L0) - cA, cC = L3 - L2 - L1 + L0,
+  // so each contraction runs on the codes (as without a codebook) and on the
+  // b0 and b0&b1 bit planes, weighted by cA, cB, cC; the L0 part joins the
+  // zero point.  Without a codebook cA = 1 and the planes are not formed.
+  float kcA = 1.f, kcB = 0.f, kcC = 0.f, kL0 = 0.f;   // K levels
+  float vcA = 1.f, vcB = 0.f, vcC = 0.f, vL0 = 0.f;   // V levels
+  if constexpr (CB) {
+    const float *lk = p.codebook + j * 8, *lvv = lk + 4;
+    kL0 = lk[0];
+    kcA = 0.5f * (lk[2] - lk[0]);
+    kcB = (lk[1] - lk[0]) - kcA;
+    kcC = ((lk[3] - lk[2]) - lk[1]) + lk[0];
+    vL0 = lvv[0];
+    vcA = 0.5f * (lvv[2] - lvv[0]);
+    vcB = (lvv[1] - lvv[0]) - vcA;
+    vcC = ((lvv[3] - lvv[2]) - lvv[1]) + lvv[0];
+  }
 
   // ---------------- schedule: this block's segments ----------------
   // The histories of the batch laid end to end hold T pages; block ib of its
@@ -413,7 +435,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   }
 
   float (*qf)[D] = qf_all[w];
-  _Float16 (*wbuf)[GQ][16] = wbuf_all[w];
+  _Float16 (*wbuf)[D / G][GQ][16] = wbuf_all[w];     // [plane][grp][head][slot]
 
   // per-lane constants of the (head, token) layout of the QK result:
   // lane (kb, r16) holds head 4*qd + kb, token r16
@@ -459,6 +481,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   asm volatile("s_mov_b32 %0, 0xc000c0" : "=s"(m6));
   asm volatile("s_mov_b32 %0, 0x3000300" : "=s"(m8));
   asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(f16one));
+  uint32_t n4 = 0, n6 = 0, n8 = 0;             // one-bit masks of the codebook's planes
+  if constexpr (CB) {
+    asm volatile("s_mov_b32 %0, 0x100010" : "=s"(n4));
+    asm volatile("s_mov_b32 %0, 0x400040" : "=s"(n6));
+    asm volatile("s_mov_b32 %0, 0x1000100" : "=s"(n8));
+  }
   const int pvs = pv_slot(r16);
   const float pvf = pv_factor(r16);
   constexpr float kLazy = 2.f;                 // log2 headroom of the running max
@@ -479,24 +507,41 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     }
 
     // ---------------- QK on int8 MFMA ----------------
-    v4i qacc[NQ][NG];
+    // per plane (the codes; with a codebook also b0 and b0&b1): the group dot
+    // products, recombined from the three pieces as soon as they are done
+    float dv[NP][NQ][NG];
 #pragma unroll
-    for (int qd = 0; qd < NQ; ++qd)
+    for (int pl = 0; pl < NP; ++pl) {
+      v4i qacc[NQ][NG];
 #pragma unroll
-      for (int g2 = 0; g2 < NG; ++g2) qacc[qd][g2] = v4i{0, 0, 0, 0};
+      for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk) {
-      const uint32_t d = sg.c[blk];
-      const v4i bq = v4i{(int)(d & 0x03030303u), (int)((d >> 2) & 0x03030303u),
-                         (int)((d >> 4) & 0x03030303u), (int)((d >> 6) & 0x03030303u)};
+        for (int g2 = 0; g2 < NG; ++g2) qacc[qd][g2] = v4i{0, 0, 0, 0};
 #pragma unroll
-      for (int gs = 0; gs < GPB; ++gs) {
-        const int m = blk * GPB + gs;
-        const int g2 = (64 * blk) / G + gs;
+      for (int blk = 0; blk < NBLK; ++blk) {
+        const uint32_t d = sg.c[blk];
+        const uint32_t e = pl == 2 ? d & (d >> 1) : d;   // bit 2i of e: b0 & b1 of channel i
+        const uint32_t mk = pl == 0 ? 0x03030303u : 0x01010101u;
+        const v4i bq = v4i{(int)(e & mk), (int)((e >> 2) & mk), (int)((e >> 4) & mk), (int)((e >> 6) & mk)};
 #pragma unroll
-        for (int qd = 0; qd < NQ; ++qd)
-          qacc[qd][g2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[qd][m], bq, qacc[qd][g2], 0, 0, 0);
+        for (int gs = 0; gs < GPB; ++gs) {
+          const int m = blk * GPB + gs;
+          const int g2 = (64 * blk) / G + gs;
+#pragma unroll
+          for (int qd = 0; qd < NQ; ++qd)
+            qacc[qd][g2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[qd][m], bq, qacc[qd][g2], 0, 0, 0);
+        }
       }
+      // p0*2^14 + p1*2^7 + p2 as two shift-adds (the empty asm keeps the
+      // compiler from re-associating them into two shifts and an add3)
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+        for (int g2 = 0; g2 < NG; ++g2) {
+          int dhi = (qacc[qd][g2][0] << 7) + qacc[qd][g2][1];
+          asm volatile("" : "+v"(dhi));
+          dv[pl][qd][g2] = (float)((dhi << 7) + qacc[qd][g2][2]);
+        }
     }
     float s_[NQ];
 #pragma unroll
@@ -504,13 +549,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
       float sc = 0.f, zt = 0.f;
 #pragma unroll
       for (int g2 = 0; g2 < NG; ++g2) {
-        // p0*2^14 + p1*2^7 + p2 as two shift-adds (the empty asm keeps the
-        // compiler from re-associating them into two shifts and an add3)
-        int dhi = (qacc[qd][g2][0] << 7) + qacc[qd][g2][1];
-        asm volatile("" : "+v"(dhi));
-        const int dint = (dhi << 7) + qacc[qd][g2][2];
-        sc = fmaf(bf16_lo(sg.sz[g2]), (float)dint, sc);
-        zt = fmaf(bf16_hi(sg.sz[g2]), qzl[qd][g2], zt);
+        float dot = dv[0][qd][g2];
+        if constexpr (CB) dot = fmaf(kcC, dv[2][qd][g2], fmaf(kcB, dv[1][qd][g2], kcA * dot));
+        const float ks = bf16_lo(sg.sz[g2]);
+        sc = fmaf(ks, dot, sc);
+        // the zero point, and the codebook's L0 part of every level
+        zt = fmaf(CB ? fmaf(ks, kL0, bf16_hi(sg.sz[g2])) : bf16_hi(sg.sz[g2]), qzl[qd][g2], zt);
       }
       s_[qd] = fmaf(sc, qscale[qd], zt);
     }
@@ -560,12 +604,24 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
     for (int g2 = 0; g2 < NG; ++g2) {
       const float vs = bf16_lo(sg.sz[NG + g2]), vz = bf16_hi(sg.sz[NG + g2]);
+      // per plane the weight p * scale_v * coefficient; the codebook's L0
+      // part joins the zero point
+      float vsp[NP];
+      vsp[0] = CB ? vs * vcA : vs;
+      if constexpr (CB) {
+        vsp[1] = vs * vcB;
+        vsp[2] = vs * vcC;
+      }
+      const float vzl = CB ? fmaf(vL0, vs, vz) : vz;
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
-        const _Float16 wh = (_Float16)(pa[qd] * vs);
-        zacc[qd][g2] = fmaf(pr[qd], vz, zacc[qd][g2]);
-        zacc[qd][g2] = fmaf(-4.f, (float)wh, zacc[qd][g2]);
-        wbuf[g2][qd * 4 + kb][pvs] = wh;
+        zacc[qd][g2] = fmaf(pr[qd], vzl, zacc[qd][g2]);
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl) {
+          const _Float16 wh = (_Float16)(pa[qd] * vsp[pl]);
+          zacc[qd][g2] = fmaf(-4.f, (float)wh, zacc[qd][g2]);
+          wbuf[pl][g2][qd * 4 + kb][pvs] = wh;
+        }
       }
     }
     wave_lds_sync();
@@ -573,29 +629,41 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     // ---------------- PV on f16 MFMA, 4 token quads ----------------
     // token t of a V word sits in bits 2t; B register u holds tokens (u, u+8)
     // in its two halves at the mantissa bit given by pv_factor
-    uint32_t bw[NH][8];
+    // (codebook: the b0 plane keeps the low bit of each code, the b0&b1
+    // plane is the low bit of x0 & (x0 >> 1), both with one-bit masks)
+    uint32_t xs[NP][NH][3];                       // per plane the word and two shifted copies
 #pragma unroll
     for (int h2 = 0; h2 < NH; ++h2) {
-      const uint32_t x0 = sg.c[NBLK + h2], x1 = x0 << 4, x2 = x0 >> 6;
-      bw[h2][0] = (x1 & m4) | f16one;
-      bw[h2][1] = (x1 & m6) | f16one;
-      bw[h2][2] = (x1 & m8) | f16one;
-      bw[h2][3] = (x0 & m6) | f16one;
-      bw[h2][4] = (x0 & m8) | f16one;
-      bw[h2][5] = (x2 & m4) | f16one;
-      bw[h2][6] = (x2 & m6) | f16one;
-      bw[h2][7] = (x2 & m8) | f16one;
+      const uint32_t x0 = sg.c[NBLK + h2];
+#pragma unroll
+      for (int pl = 0; pl < NP; ++pl) {
+        const uint32_t y0 = pl == 2 ? x0 & (x0 >> 1) : x0;
+        xs[pl][h2][0] = y0;
+        xs[pl][h2][1] = y0 << 4;
+        xs[pl][h2][2] = y0 >> 6;
+      }
     }
+    // B register u (tokens u, u+8): copy (x1 x1 x1 x0 x0 x2 x2 x2)[u], mask
+    // at mantissa bit (4 6 8 6 8 4 6 8)[u]
+    auto breg = [&](int pl, int h2, int u) -> uint32_t {
+      const uint32_t x = u < 3 ? xs[pl][h2][1] : u < 5 ? xs[pl][h2][0] : xs[pl][h2][2];
+      const int b = (u == 0 || u == 5) ? 4 : (u == 1 || u == 3 || u == 6) ? 6 : 8;
+      const uint32_t mk = pl == 0 ? (b == 4 ? m4 : b == 6 ? m6 : m8) : (b == 4 ? n4 : b == 6 ? n6 : n8);
+      return (x & mk) | f16one;
+    };
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
 #pragma unroll
       for (int h2 = 0; h2 < NH; ++h2) {
-        const v4h bv = as_v4h(bw[h2][2 * ti], bw[h2][2 * ti + 1]);
         const int g2 = (lane + 64 * h2) / G;
 #pragma unroll
-        for (int qd = 0; qd < NQ; ++qd) {
-          const uint2 u = *reinterpret_cast<const uint2 *>(&wbuf[g2][qd * 4 + (lane & 3)][4 * ti]);
-          acc[qd][h2] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_v4h(u.x, u.y), bv, acc[qd][h2], 0, 0, 0);
+        for (int pl = 0; pl < NP; ++pl) {
+          const v4h bv = as_v4h(breg(pl, h2, 2 * ti), breg(pl, h2, 2 * ti + 1));
+#pragma unroll
+          for (int qd = 0; qd < NQ; ++qd) {
+            const uint2 u = *reinterpret_cast<const uint2 *>(&wbuf[pl][g2][qd * 4 + (lane & 3)][4 * ti]);
+            acc[qd][h2] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_v4h(u.x, u.y), bv, acc[qd][h2], 0, 0, 0);
+          }
         }
       }
     }
@@ -688,8 +756,11 @@ static void launch_mfma_dg(const DecodeParams &p, hipStream_t s) {
   const int hg = mfma_heads_per_block(p.Hkv);
   const int ngrp = (p.Hkv + hg - 1) / hg;
   const dim3 grid(p.B * ngrp * p.mfma_parts), blk(64 * kMfmaWaves);
-  if (p.g == 8) hipLaunchKernelGGL((k_int2_mfma<D, G, 8>), grid, blk, 0, s, p);
-  else hipLaunchKernelGGL((k_int2_mfma<D, G, 4>), grid, blk, 0, s, p);
+  const bool cb = p.codebook != nullptr;
+  if (p.g == 8 && cb) hipLaunchKernelGGL((k_int2_mfma<D, G, 8, true>), grid, blk, 0, s, p);
+  else if (p.g == 8) hipLaunchKernelGGL((k_int2_mfma<D, G, 8, false>), grid, blk, 0, s, p);
+  else if (cb) hipLaunchKernelGGL((k_int2_mfma<D, G, 4, true>), grid, blk, 0, s, p);
+  else hipLaunchKernelGGL((k_int2_mfma<D, G, 4, false>), grid, blk, 0, s, p);
 }
 
 hipError_t launch_int2_mfma(const DecodeParams &p, hipStream_t s) {

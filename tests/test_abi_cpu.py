@@ -260,11 +260,12 @@ def test_decode_step_argument_checks():
     assert _step(c, _args(phases=ob.PHASE_ALL)) == ob.OSCAR_EWORKSPACE
 
 
-def test_codebook_cache_uses_the_valu_kernel():
-    """A cache with a Lloyd-Max codebook: AUTO resolves to the vector-ALU
-    kernel, an explicit matrix-core request is EUNSUPPORTED."""
+def test_codebook_cache_kernel_choice():
+    """A cache with a Lloyd-Max codebook is read by both INT2 kernels: AUTO
+    resolves as without one (matrix cores at 4 or 8 q heads per KV head)."""
     st, *_, k = _plan(_cache(codebook=0x80000), _args())
+    assert st == ob.OSCAR_OK and k == ob.INT2_MFMA
+    st, *_, k = _plan(_cache(codebook=0x80000), _args(int2_kernel=ob.INT2_VALU))
     assert st == ob.OSCAR_OK and k == ob.INT2_VALU
-    st, *_ = _plan(_cache(codebook=0x80000), _args(int2_kernel=ob.INT2_MFMA))
-    assert st == ob.OSCAR_EUNSUPPORTED
-    assert "codebook" in ob.last_error()
+    st, *_, k = _plan(_cache(codebook=0x80000), _args(num_q_heads=16))
+    assert st == ob.OSCAR_OK and k == ob.INT2_VALU

@@ -305,16 +305,17 @@ def test_deterministic_option(shape):
     _say(f"deterministic: bitwise repeatable, worst row rel err {w:.3e}, vs dynamic {e.max():.2e}")
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("shape", ["tiny", "d128g64", "d128g128"])
-def test_codebook_variant(shape):
+def test_codebook_variant(shape, kernel):
     """Lloyd-Max codebook variant: the prompt history quantised in bulk, then
-    two decode steps (one-token demotion, attention on the vector-ALU kernel,
-    which AUTO picks for a cache with a codebook), through the separate calls
-    and through oscar_decode_step.  INT2 page bytes bit-exact against the
-    oracle's nearest-level quantiser, outputs within the oracle bar, and the
-    fused step bitwise equal to the separate calls."""
+    two decode steps (one-token demotion, attention on either INT2 kernel; the
+    matrix-core one with the deterministic option), through the separate
+    calls and through oscar_decode_step.  INT2 page bytes bit-exact against
+    the oracle's nearest-level quantiser, outputs within the oracle bar, and
+    the fused step bitwise equal to the separate calls."""
     from int2_rotated_kv_amd import binding as ob
-    _say("case: codebook variant", shape)
+    _say("case: codebook variant", shape, "kernel", kernel)
     if shape == "tiny":
         wl = synth.workload("tiny", B=2, lengths=(1024, 777), steps=2, seed=81)
     elif shape == "d128g64":
@@ -323,8 +324,9 @@ def test_codebook_variant(shape):
         wl = synth.workload("tiny", B=2, Hkv=2, Hq=16, D=128, G=128, lengths=(2500, 999), steps=2, seed=83)
     inp = synth.make_small(wl, distinct_rv=True)
     cb = synth.make_codebook(wl.seed, wl.Hkv)
-    sep = sh.build_and_step(inp, steps=2, int2_kernel=ob.INT2_AUTO, codebook=cb)
-    fus = sh.build_and_step(inp, steps=2, int2_kernel=ob.INT2_AUTO, codebook=cb, fused=True)
+    kw = dict(steps=2, int2_kernel=kernel, codebook=cb, flags=ob.FLAG_DETERMINISTIC)
+    sep = sh.build_and_step(inp, **kw)
+    fus = sh.build_and_step(inp, fused=True, **kw)
     ref = sh.oracle_step(inp, steps=2, codebook=cb)
     _check_bytes(sep, inp, ref)
     _check_bytes(fus, inp, ref)
@@ -334,4 +336,4 @@ def test_codebook_variant(shape):
     uni = sh.oracle_step(inp, steps=2)
     assert not np.array_equal(sh.oracle_records(uni[0], wl.D, wl.G, wl.Hkv),
                               sh.oracle_records(ref[0], wl.D, wl.G, wl.Hkv))
-    _say(f"codebook {shape}: bytes exact, worst row rel err {w:.3e}")
+    _say(f"codebook {shape} kernel {kernel}: bytes exact, worst row rel err {w:.3e}")
