@@ -627,7 +627,8 @@ def main(argv=None):
     i2_last = int2_alg_bytes(wl, st.hl_h[r["int2_only_step"]], splits)[0]
     achieved = i2_last / (r["int2_only_ms"] * 1e-3) / 1e9
     kname = "k_int2_mfma" if kind == ob.INT2_MFMA else "k_int2_valu"
-    tr = traffic_from_profile(kname, wl.name)
+    # the committed counter summaries are taken with uniform codes
+    tr = None if a.codebook else traffic_from_profile(kname, wl.name)
     out = {
         "metric": "decode attention: KV-tokens·heads/s and achieved HBM TB/s (% of peak) at 100K ctx",
         "value": kvth / (ms_step * 1e-3),
