@@ -53,7 +53,7 @@ def _history_tokens(gen, b, hl0):
     return kh[:hl0], vh[:hl0]
 
 
-def _check_sequences(st, first_out, pool, seqs, rng):
+def _check_sequences(st, first_out, pool, seqs, rng, codebook=None):
     """Oracle check of step 0 for the sequences `seqs`: every q head's output
     and lse, the bytes of 48 sampled prompt pages and of the page that
     received the demoted token.  Prompt-history pages are quantised once per
@@ -84,20 +84,26 @@ def _check_sequences(st, first_out, pool, seqs, rng):
     for b in seqs:
         kb, vb = gen.bf16_tokens(b)
         win[b] = (_u16(kb), _u16(vb))
+    if codebook is None:
+        quant = lambda x, R, clip, j, kv: orc.quantize_tokens(x, R, G, clip)
+        deq = lambda c, s, z, j, kv: orc.dequant(c, s, z, G)
+    else:
+        quant = lambda x, R, clip, j, kv: orc.quantize_tokens_codebook(x, R, G, clip, codebook[j, kv])
+        deq = lambda c, s, z, j, kv: orc.dequant_codebook(c, s, z, G, codebook[j, kv])
     out_ref = {b: np.zeros((wl.Hq, D)) for b in seqs}
     lse_ref = {b: np.zeros(wl.Hq) for b in seqs}
     sample = {b: np.sort(rng.choice(npg[b] - 1, size=min(48, npg[b] - 1), replace=False)) for b in seqs}
     for j in range(Hkv):
-        qk = orc.quantize_tokens(f64(kh[:, j]), gen.R_k[j], G, float(gen.clip_k[j]))
-        qv = orc.quantize_tokens(f64(vh[:, j]), gen.R_v[j], G, float(gen.clip_v[j]))
-        xk, xv = orc.dequant(*qk, G), orc.dequant(*qv, G)
+        qk = quant(f64(kh[:, j]), gen.R_k[j], float(gen.clip_k[j]), j, 0)
+        qv = quant(f64(vh[:, j]), gen.R_v[j], float(gen.clip_v[j]), j, 1)
+        xk, xv = deq(*qk, j, 0), deq(*qv, j, 1)
         heads = [h for h in range(wl.Hq) if h // g == j]
         for b in seqs:
             kb, vb = win[b]
             # step 0: the oldest recent token (window position 64) is demoted
             # to history position hl0, the new token appended to the window
-            dk = orc.quantize_tokens(f64(kb[SINK:SINK + 1, j]), gen.R_k[j], G, float(gen.clip_k[j]))
-            dv = orc.quantize_tokens(f64(vb[SINK:SINK + 1, j]), gen.R_v[j], G, float(gen.clip_v[j]))
+            dk = quant(f64(kb[SINK:SINK + 1, j]), gen.R_k[j], float(gen.clip_k[j]), j, 0)
+            dv = quant(f64(vb[SINK:SINK + 1, j]), gen.R_v[j], float(gen.clip_v[j]), j, 1)
             r = rows[b]
             hk = [np.concatenate([a[r], d]) for a, d in zip(qk, dk)]
             hv = [np.concatenate([a[r], d]) for a, d in zip(qv, dv)]
@@ -115,8 +121,8 @@ def _check_sequences(st, first_out, pool, seqs, rng):
                     f"seq {b} page {pg} head {j}: demoted token's page differs"
             bf_k = np.concatenate([kb[:SINK], kb[SINK + 1:], knew[b:b + 1]])[:, j]
             bf_v = np.concatenate([vb[:SINK], vb[SINK + 1:], vnew[b:b + 1]])[:, j]
-            xhk = np.concatenate([xk[r], orc.dequant(*dk, G)])
-            xhv = np.concatenate([xv[r], orc.dequant(*dv, G)])
+            xhk = np.concatenate([xk[r], deq(*dk, j, 0)])
+            xhv = np.concatenate([xv[r], deq(*dv, j, 1)])
             o, l = orc.decode_attention(f64(q0[b][heads]), np.zeros(len(heads), int),
                                         f64(bf_k)[:, None], f64(bf_v)[:, None],
                                         xhk[:, None], xhv[:, None], gen.R_k[j:j + 1], gen.R_v[j:j + 1])
@@ -133,16 +139,18 @@ def _check_sequences(st, first_out, pool, seqs, rng):
     return worst
 
 
-@pytest.mark.parametrize("workload", ["qwen3-8b-b32-100k", "qwen3-8b-100k-b1", "qwen3-32b-b16-128k"])
-def test_full_size_sampled(workload):
+@pytest.mark.parametrize("workload,codebook", [("qwen3-8b-b32-100k", False), ("qwen3-8b-100k-b1", False),
+                                               ("qwen3-32b-b16-128k", False), ("qwen3-8b-100k-b1", True)])
+def test_full_size_sampled(workload, codebook):
     """Batch-32 ~96K (the benchmark workload), one 102400-token sequence, and
     the Qwen3-32B-shaped batch 16 x 131072 with a shared 32768-token prefix
-    (8 q heads per KV head, group 128)."""
+    (8 q heads per KV head, group 128); and the 102400-token sequence with the
+    Lloyd-Max codebook variant (bench.py --codebook)."""
     import bench
     from int2_rotated_kv_amd import binding as ob
     t0 = time.time()
-    _say(f"case: {workload}, one decode step (bench configuration)")
-    st = bench.build_workload(workload, 1, log=_say)
+    _say(f"case: {workload}{' with codebook' if codebook else ''}, one decode step (bench configuration)")
+    st = bench.build_workload(workload, 1, log=_say, codebook=codebook)
     r = bench.run_steps(st, 0, 1, ob.INT2_AUTO, keep_first_out=True)
     plan = ob.decode_plan(st.sc.cache, r["args"][0])
     _say(f"step done: chunks {plan[0]}, kernel {plan[3]}, {time.time() - t0:.1f}s")
@@ -151,7 +159,7 @@ def test_full_size_sampled(workload):
     # every sequence of the shared-prefix batch (its pages are quantised once),
     # the first and the last of the others
     seqs = list(range(st.wl.B)) if st.wl.shared_prefix else sorted({0, st.wl.B - 1})
-    w = _check_sequences(st, r["first_out"], pool, seqs, rng)
+    w = _check_sequences(st, r["first_out"], pool, seqs, rng, codebook=st.codebook_h)
     _say(f"sequences {seqs}: bytes of sampled and demoted-token pages exact, worst row rel err "
          f"{w:.3e} ({time.time() - t0:.1f}s)")
 
