@@ -39,7 +39,7 @@ def hist_capacity_pages(L: int, steps: int) -> int:
 
 def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_splits=0,
                    R_v_none=False, head_map=None, device="cuda", seed_perm=None, fused=False,
-                   flags=0, codebook=None):
+                   flags=0, codebook=None, max_hist_len=None, extra_pages=0):
     """Build the initial split cache of every sequence, run `steps` decode steps
     (demote oldest recent -> write new token -> attend -> merge; with fused,
     through the single oscar_decode_step call), return the outputs of the last
@@ -50,7 +50,7 @@ def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_sp
 
     wl = inp.wl
     B = wl.B
-    caps = [hist_capacity_pages(L, steps) for L in wl.lengths]
+    caps = [hist_capacity_pages(L, steps) + extra_pages for L in wl.lengths]
     stride = max(caps)
     n_int2 = sum(caps)
     perm = synth.page_permutation(wl.seed if seed_perm is None else seed_perm, n_int2, extra=3)
@@ -91,8 +91,8 @@ def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_sp
             ob.write_bf16(sc.cache, d_w, kn, vn)
         sc.commit_step()
         sc.sync_lengths()
-        args = sc.decode_args(kv_head_of_q=head_map, num_splits=num_splits, int2_kernel=int2_kernel,
-                              flags=flags)
+        args = sc.decode_args(max_hist_len=max_hist_len, kv_head_of_q=head_map, num_splits=num_splits,
+                              int2_kernel=int2_kernel, flags=flags)
         if fused:
             ws = ob.alloc_workspace(sc.cache, args, device=q.device)
             ob.decode_step(sc.cache, args, d_src, d_dst, ck, cv, d_w, kn, vn, q, Rk, Rv, ws, out, lse)

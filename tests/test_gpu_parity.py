@@ -337,3 +337,20 @@ def test_codebook_variant(shape, kernel):
     assert not np.array_equal(sh.oracle_records(uni[0], wl.D, wl.G, wl.Hkv),
                               sh.oracle_records(ref[0], wl.D, wl.G, wl.Hkv))
     _say(f"codebook {shape} kernel {kernel}: bytes exact, worst row rel err {w:.3e}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_single_sequence_loose_length_bound(kernel):
+    """One sequence whose max_hist_len is the page table's whole capacity,
+    four times its history (the grid and the chunking are sized by the bound,
+    the pages walked by the length): outputs and bytes match the oracle."""
+    _say("case: single sequence, loose max_hist_len, kernel", kernel)
+    wl = synth.workload("tiny", B=1, Hkv=2, Hq=8, D=128, G=64, lengths=(1500,), steps=2, seed=91)
+    inp = synth.make_small(wl)
+    extra = 3 * sh.hist_capacity_pages(1500, 2)              # table rows 4x the history
+    bound = 16 * (sh.hist_capacity_pages(1500, 2) + extra)
+    run = sh.build_and_step(inp, steps=2, int2_kernel=kernel, max_hist_len=bound, num_splits=40,
+                            extra_pages=extra)
+    ref = sh.oracle_step(inp, steps=2)
+    _check_bytes(run, inp, ref)
+    _check_out(run, ref)
