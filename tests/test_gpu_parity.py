@@ -306,7 +306,7 @@ def test_deterministic_option(shape):
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
-@pytest.mark.parametrize("shape", ["tiny", "d128g64", "d128g128"])
+@pytest.mark.parametrize("shape", ["tiny", "d128g64", "d128g128", "d128g32", "d64g64g8"])
 def test_codebook_variant(shape, kernel):
     """Lloyd-Max codebook variant: the prompt history quantised in bulk, then
     two decode steps (one-token demotion, attention on either INT2 kernel; the
@@ -320,8 +320,12 @@ def test_codebook_variant(shape, kernel):
         wl = synth.workload("tiny", B=2, lengths=(1024, 777), steps=2, seed=81)
     elif shape == "d128g64":
         wl = synth.workload("tiny", B=2, Hkv=2, Hq=8, D=128, G=64, lengths=(3000, 1700), steps=2, seed=82)
-    else:
+    elif shape == "d128g128":
         wl = synth.workload("tiny", B=2, Hkv=2, Hq=16, D=128, G=128, lengths=(2500, 999), steps=2, seed=83)
+    elif shape == "d128g32":
+        wl = synth.workload("tiny", B=3, Hkv=2, Hq=8, D=128, G=32, lengths=(2000, 400, 1300), steps=2, seed=84)
+    else:
+        wl = synth.workload("tiny", B=2, Hkv=2, Hq=16, D=64, G=64, lengths=(1800, 700), steps=2, seed=85)
     inp = synth.make_small(wl, distinct_rv=True)
     cb = synth.make_codebook(wl.seed, wl.Hkv)
     kw = dict(steps=2, int2_kernel=kernel, codebook=cb, flags=ob.FLAG_DETERMINISTIC)
