@@ -5,36 +5,35 @@
 namespace oscar {
 
 // Bulk fills (prompt histories): one block = 16 consecutive entries of the
-// slot lists, one KV head (blockIdx.y), K or V (blockIdx.z); thread c owns
-// rotated channel c.  Every R load serves the 16 tokens: rows are walked in
-// order (fp64 fma chains, the same arithmetic per token as the single-token
-// routine's definition, x = sum_i k_i R_ic), with the next 8 rows' R values
-// requested while the current 8 are used.  The tokens are then quantised one
-// by one; a token's V bits are gathered per page word and a word is written
-// once all tokens of its page in this block are in (whole-page words with one
-// store, others with AND/OR atomics).
+// slot lists, one KV head (blockIdx.y), K or V (blockIdx.z).  The rotation of
+// the 16 tokens, X[16][D] = K[16][D] . R, runs on the fp64 matrix cores
+// (v_mfma_f64_16x16x4f64: every product of a bf16 value and an fp32 R entry is
+// exact in fp64, the sums are fp64): wave w computes the channels 64w..64w+63
+// as four 16-column tiles, tile ct holding channels 64w + 4j + ct (j = 0..15)
+// so that one 16-byte R load per lane and k-step feeds all four tiles.  The
+// token values come from LDS (rows padded to D + 4 doubles: at most 2-way
+// bank conflicts), the results go back to LDS, and thread c quantises channel
+// c of the 16 tokens one by one; a token's V bits are gathered per page word
+// and a word is written once all tokens of its page in this block are in
+// (whole-page words with one store, others with AND/OR atomics).
 template <int D, int G>
 __global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
 #pragma clang fp contract(off)
+  typedef double v4d __attribute__((ext_vector_type(4)));
   constexpr int T = 16;
-  constexpr int RB = 8;                        // R rows per pipeline step
+  constexpr int XS = D + 4;                    // padded row stride of xs (doubles)
   constexpr RecLayout RL(D, G);
   constexpr int GW = G < 64 ? G : 64;          // lanes of a group inside one wave
   const int c = threadIdx.x;
   const int j = blockIdx.y;
   const bool isv = blockIdx.z != 0;
   const int e0 = blockIdx.x * T;
-  __shared__ __align__(16) double xs[T][D];
+  __shared__ __align__(16) double xs[T][XS];   // token values, then rotated values
   __shared__ int s_src[T], s_dst[T];
   __shared__ double red_mx[2], red_mn[2];
 
   const float *R = isv ? a.Rv : a.Rk;
   const float *Rj = R != nullptr ? R + (size_t)j * D * D : nullptr;
-  float rn[RB];
-  if (Rj != nullptr) {
-#pragma unroll
-    for (int r = 0; r < RB; ++r) rn[r] = Rj[(size_t)r * D + c];
-  }
   if (c < T) {
     const int e = e0 + c;
     int sv = -1, dv = -1;
@@ -63,30 +62,34 @@ __global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
 
   double x[T];
   if (Rj != nullptr) {
+    // lane (ti, kq) = (l % 16, l / 16): A = token ti's value at k = 4s + kq,
+    // B = R[4s + kq][64w + 4ti + ct] for tile ct; the result of tile ct,
+    // element r, is X[token kq + 4r][channel 64w + 4ti + ct]
+    const int l = c & 63, w = c >> 6;
+    const int ti = l & 15, kq = l >> 4;
+    const float4 *R4 = reinterpret_cast<const float4 *>(Rj) + 16 * w + ti;
+    v4d acc[4];
 #pragma unroll
-    for (int t = 0; t < T; ++t) x[t] = 0.0;
-    for (int i0 = 0; i0 < D; i0 += RB) {
-      float rc[RB];
-#pragma unroll
-      for (int r = 0; r < RB; ++r) rc[r] = rn[r];
-      if (i0 + RB < D) {
-#pragma unroll
-        for (int r = 0; r < RB; ++r) rn[r] = Rj[(size_t)(i0 + RB + r) * D + c];
-      }
-#pragma unroll
-      for (int r = 0; r < RB; r += 2) {
-        const double r0 = (double)rc[r], r1 = (double)rc[r + 1];
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const double2 kk = *reinterpret_cast<const double2 *>(&xs[t][i0 + r]);
-          x[t] = fma(kk.y, r1, fma(kk.x, r0, x[t]));
-        }
-      }
+    for (int ct = 0; ct < 4; ++ct) acc[ct] = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+    for (int s = 0; s < D / 4; ++s) {
+      const int k = 4 * s + kq;
+      const double av = xs[ti][k];
+      const float4 rv = R4[(size_t)k * (D / 4)];
+      acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)rv.x, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)rv.y, acc[1], 0, 0, 0);
+      acc[2] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)rv.z, acc[2], 0, 0, 0);
+      acc[3] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)rv.w, acc[3], 0, 0, 0);
     }
-  } else {
+    __syncthreads();                           // every wave has read the token values
 #pragma unroll
-    for (int t = 0; t < T; ++t) x[t] = xs[t][c];
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) xs[kq + 4 * r][64 * w + 4 * ti + ct] = acc[ct][r];
+    __syncthreads();
   }
+#pragma unroll
+  for (int t = 0; t < T; ++t) x[t] = xs[t][c];
 
   const double clip = (double)(isv ? a.clip_v[j] : a.clip_k[j]);
   const float *lv = a.codebook ? a.codebook + (j * 2 + (isv ? 1 : 0)) * 4 : nullptr;
