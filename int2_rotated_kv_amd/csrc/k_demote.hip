@@ -12,10 +12,12 @@ namespace oscar {
 // as four 16-column tiles, tile ct holding channels 64w + 4j + ct (j = 0..15)
 // so that one 16-byte R load per lane and k-step feeds all four tiles.  The
 // token values come from LDS (rows padded to D + 4 doubles: at most 2-way
-// bank conflicts), the results go back to LDS, and thread c quantises channel
-// c of the 16 tokens one by one; a token's V bits are gathered per page word
-// and a word is written once all tokens of its page in this block are in
-// (whole-page words with one store, others with AND/OR atomics).
+// bank conflicts), the results go back to LDS.  The group statistics (max,
+// min, clipped range, bf16 scale and zero) are computed once per (token,
+// group) by a few threads each, and thread c then quantises channel c of the
+// 16 tokens one by one; a token's V bits are gathered per page word and a word
+// is written once all tokens of its page in this block are in (whole-page
+// words with one store, others with AND/OR atomics).
 template <int D, int G>
 __global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
 #pragma clang fp contract(off)
@@ -23,14 +25,16 @@ __global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
   constexpr int T = 16;
   constexpr int XS = D + 4;                    // padded row stride of xs (doubles)
   constexpr RecLayout RL(D, G);
-  constexpr int GW = G < 64 ? G : 64;          // lanes of a group inside one wave
+  constexpr int NG = D / G;                    // groups per token
+  constexpr int RT = D / (T * NG);             // threads per (token, group): 2, 4 or 8
+  constexpr int PG = G / RT;                   // channels each of them scans (16)
   const int c = threadIdx.x;
   const int j = blockIdx.y;
   const bool isv = blockIdx.z != 0;
   const int e0 = blockIdx.x * T;
   __shared__ __align__(16) double xs[T][XS];   // token values, then rotated values
   __shared__ int s_src[T], s_dst[T];
-  __shared__ double red_mx[2], red_mn[2];
+  __shared__ double s_sd[T][NG], s_zd[T][NG];  // bf16 scale and zero as fp64
 
   const float *R = isv ? a.Rv : a.Rk;
   const float *Rj = R != nullptr ? R + (size_t)j * D * D : nullptr;
@@ -93,6 +97,43 @@ __global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
 
   const double clip = (double)(isv ? a.clip_v[j] : a.clip_k[j]);
   const float *lv = a.codebook ? a.codebook + (j * 2 + (isv ? 1 : 0)) * 4 : nullptr;
+  // Per (token, group), once: max and min (RT consecutive threads scan PG
+  // channels each, then combine by shuffles), the clipped range, and the bf16
+  // scale and zero, which the first of them also stores in the record.
+  {
+    const int pr = c / RT, sub = c % RT;
+    const int t = pr / NG, g2 = pr % NG;
+    const double *row = &xs[t][g2 * G + sub * PG];
+    double mx = row[0], mn = row[0];
+#pragma unroll
+    for (int i = 1; i < PG; ++i) {
+      mx = fmax(mx, row[i]);
+      mn = fmin(mn, row[i]);
+    }
+#pragma unroll
+    for (int o = 1; o < RT; o <<= 1) {
+      mx = fmax(mx, __shfl_xor(mx, o));
+      mn = fmin(mn, __shfl_xor(mn, o));
+    }
+    if (sub == 0) {
+      const double hi = clip * mx;
+      const double lo = clip * mn;
+      const double scale = (hi - lo) / 3.0;
+      const uint16_t sb = f64_to_bf16_rne(scale);
+      const uint16_t zb = f64_to_bf16_rne(lo);
+      s_sd[t][g2] = (double)bf16_to_f32(sb);
+      s_zd[t][g2] = (double)bf16_to_f32(zb);
+      const int d = s_dst[t];
+      if (d >= 0) {
+        const int64_t page = d >> 4, off = d & 15;
+        uint8_t *rec = a.pool + ((size_t)page * a.Hkv + j) * RL.bytes();
+        const int o = isv ? RL.vsz((int)off, g2) : RL.ksz((int)off, g2);
+        *reinterpret_cast<uint32_t *>(rec + o) = (uint32_t)sb | ((uint32_t)zb << 16);
+      }
+    }
+  }
+  __syncthreads();
+
   int vpage = -1;                              // V word being gathered (uniform)
   uint32_t vmask = 0, vbits = 0;
   auto flush_v = [&]() {
@@ -109,35 +150,11 @@ __global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
   };
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    double mx = x[t], mn = x[t];
-#pragma unroll
-    for (int o = 1; o < GW; o <<= 1) {
-      mx = fmax(mx, __shfl_xor(mx, o));
-      mn = fmin(mn, __shfl_xor(mn, o));
-    }
-    if constexpr (G > 64) {
-      if ((c & 63) == 0) { red_mx[c >> 6] = mx; red_mn[c >> 6] = mn; }
-      __syncthreads();
-      mx = fmax(red_mx[0], red_mx[1]);
-      mn = fmin(red_mn[0], red_mn[1]);
-      __syncthreads();
-    }
     const int d = s_dst[t];
     if (d < 0) continue;                       // uniform
-    const double hi = clip * mx;
-    const double lo = clip * mn;
-    const double scale = (hi - lo) / 3.0;
-    const uint16_t sb = f64_to_bf16_rne(scale);
-    const uint16_t zb = f64_to_bf16_rne(lo);
-    const double sd = (double)bf16_to_f32(sb);
-    const double zd = (double)bf16_to_f32(zb);
-    const uint32_t code = quant_code(x[t], zd, sd, lv);
+    const uint32_t code = quant_code(x[t], s_zd[t][c / G], s_sd[t][c / G], lv);
     const int64_t page = d >> 4, off = d & 15;
     uint8_t *rec = a.pool + ((size_t)page * a.Hkv + j) * RL.bytes();
-    if ((c % G) == 0) {
-      const int o = isv ? RL.vsz((int)off, c / G) : RL.ksz((int)off, c / G);
-      *reinterpret_cast<uint32_t *>(rec + o) = (uint32_t)sb | ((uint32_t)zb << 16);
-    }
     if (!isv) {
       // K: word blk of lane slot 16*kb + t holds channels 64*blk + 16*kb + i of
       // token t at bits 2i
