@@ -358,3 +358,68 @@ def test_single_sequence_loose_length_bound(kernel):
     ref = sh.oracle_step(inp, steps=2)
     _check_bytes(run, inp, ref)
     _check_out(run, ref)
+
+
+def test_decode_step_in_hip_graph():
+    """oscar_decode_step captured in a HIP graph (the library allocates,
+    synchronises and memsets nothing, so a step can be captured) and replayed
+    three times, with eager work and a synchronisation between replays: with
+    the deterministic option every replay equals the eager run of the same
+    step bit for bit.  The step is re-run on the cache after it: its slot
+    lists are planned again from the state before it, so each run demotes the
+    token now in the freed slot (the new one) into the same history slot and
+    stores the same new token, the same bytes every time."""
+    import torch
+    from int2_rotated_kv_amd import binding as ob
+    from int2_rotated_kv_amd.splitcache import SplitCache
+    _say("case: decode step in a HIP graph")
+    wl = synth.workload("tiny", B=3, Hkv=2, Hq=8, D=128, G=64, lengths=(2000, 700, 1300), steps=1, seed=95)
+    inp = synth.make_small(wl)
+    run = sh.build_and_step(inp, steps=1, int2_kernel=2, flags=ob.FLAG_DETERMINISTIC)
+    sc = run.sc
+    dev = "cuda"
+    # plan the step build_and_step took again: the lengths and ring before it
+    sc.hist_len_h -= np.array([1 if L >= 320 else 0 for L in wl.lengths])
+    sc.bf16_len_h = np.minimum(np.array(wl.lengths), 320)
+    sc.ring_head[:] = 0
+    dsrc, ddst, wdst = (torch.from_numpy(x).to(dev) for x in sc.plan_step())
+    sc.commit_step()
+    sc.sync_lengths()
+    args = sc.decode_args(int2_kernel=2, flags=ob.FLAG_DETERMINISTIC)
+    B = wl.B
+    kn = sh.to_dev_bf16(np.stack([inp.K[b][wl.lengths[b]] for b in range(B)])).view(torch.int16)
+    vn = sh.to_dev_bf16(np.stack([inp.V[b][wl.lengths[b]] for b in range(B)])).view(torch.int16)
+    q = sh.to_dev_bf16(inp.q[0]).view(torch.int16)
+    Rk = torch.from_numpy(inp.R_k).to(dev)
+    Rv = torch.from_numpy(inp.R_v).to(dev)
+    ck = torch.from_numpy(inp.clip_k).to(dev)
+    cv = torch.from_numpy(inp.clip_v).to(dev)
+    ws = ob.alloc_workspace(sc.cache, args, device=dev)
+    out = torch.zeros((B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
+    lse = torch.zeros((B, wl.Hq), dtype=torch.float32, device=dev)
+
+    def step():
+        ob.decode_step(sc.cache, args, dsrc, ddst, ck, cv, wdst, kn, vn, q, Rk, Rv, ws, out, lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    pool0 = sc.cache.int2.clone()
+    step()                                            # the eager step repeats itself
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32))
+    assert torch.equal(sc.cache.int2, pool0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float(i + 1))                       # eager work between replays
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32)), f"replay {i}: outputs differ"
+        assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)), f"replay {i}: lse differ"
+        assert torch.equal(sc.cache.int2, pool0), f"replay {i}: INT2 pool differs"
+    _say("graph: 3 replays bitwise equal to the eager step")
