@@ -423,3 +423,39 @@ def test_decode_step_in_hip_graph():
         assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)), f"replay {i}: lse differ"
         assert torch.equal(sc.cache.int2, pool0), f"replay {i}: INT2 pool differs"
     _say("graph: 3 replays bitwise equal to the eager step")
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    D = int(rng.choice([64, 128]))
+    G = int(rng.choice([32, 64] if D == 64 else [32, 64, 128]))
+    Hkv = int(rng.choice([1, 2, 3, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(1, 7))
+    lengths = tuple(int(x) for x in rng.integers(1, 3000, B))
+    steps = int(rng.integers(1, 3))
+    kernel = int(rng.choice([0, 1, 2])) if g in (4, 8) else int(rng.choice([0, 1]))
+    codebook = bool(rng.integers(0, 2))
+    det = bool(rng.integers(0, 2))
+    return dict(D=D, G=G, Hkv=Hkv, Hq=g * Hkv, B=B, lengths=lengths, steps=steps, seed=2000 + seed), \
+        kernel, codebook, det
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_configurations(seed):
+    """Seeded random configurations (head_dim, group, KV heads, q heads per KV
+    head, batch, lengths from 1 to 3000 tokens, 1-2 steps, kernel choice,
+    codebook or not, deterministic option or not) against the oracle: page
+    bytes exact, outputs within the bar."""
+    from int2_rotated_kv_amd import binding as ob
+    kw, kernel, codebook, det = _random_case(seed)
+    _say(f"case: random configuration {seed}: {kw}, kernel {kernel}, codebook {codebook}, det {det}")
+    wl = synth.workload("tiny", **kw)
+    inp = synth.make_small(wl, distinct_rv=bool(seed % 2))
+    cb = synth.make_codebook(wl.seed, wl.Hkv) if codebook else None
+    run = sh.build_and_step(inp, steps=wl.steps, int2_kernel=kernel, codebook=cb,
+                            flags=ob.FLAG_DETERMINISTIC if det else 0)
+    ref = sh.oracle_step(inp, steps=wl.steps, codebook=cb)
+    _check_bytes(run, inp, ref)
+    w = _check_out(run, ref)
+    _say(f"random {seed}: bytes exact, worst row rel err {w:.3e}")
