@@ -98,8 +98,10 @@ enum {
  * serves 4 or 8 q heads, else VALU; asking for MFMA with another ratio is
  * EUNSUPPORTED from every call that takes the arguments.  The MFMA kernel
  * carries the PV weights p * scale_v * 16 (p < 4) in f16, so it requires V
- * group scales below 1024 (|V| up to ~3000 after rotation); the VALU kernel
- * has no such limit.  Neither is checked (the scales live on the device). */
+ * group scales below 1024 (|V| up to ~3000 after rotation; with a codebook,
+ * scale_v times the largest of |L2 - L0|/2, |L1 - L0 - (L2 - L0)/2| and
+ * |L3 - L2 - L1 + L0| below 1024); the VALU kernel has no such limit.  Neither
+ * is checked (the scales live on the device). */
 enum {
   OSCAR_INT2_AUTO = 0,
   OSCAR_INT2_VALU = 1,      /* vector-ALU dot products                         */
