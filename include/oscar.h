@@ -94,9 +94,11 @@ enum {
                                    of a compute unit progress unevenly        */
 };
 
-/* Which kernel computes the INT2 segment.  AUTO picks MFMA when every KV head
- * serves 4 or 8 q heads, else VALU; asking for MFMA with another ratio is
- * EUNSUPPORTED from every call that takes the arguments.  The MFMA kernel
+/* Which kernel computes the INT2 segment.  AUTO picks MFMA, which serves 1,
+ * 2, 4 or 8 q heads per KV head (with 1 or 2 the head quads are partly empty;
+ * it still reads the cache about 2.3 to 2.9 times faster than VALU there).
+ * VALU is the kernel to ask for when the V scales exceed what the MFMA
+ * kernel's f16 weights hold, as stated next.  The MFMA kernel
  * carries the PV weights p * scale_v * 16 (p < 4) in f16, so it requires V
  * group scales below 1024 (|V| up to ~3000 after rotation; with a codebook,
  * scale_v times the largest of |L2 - L0|/2, |L1 - L0 - (L2 - L0)/2| and

@@ -135,14 +135,11 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   const float sm = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt((float)c->head_dim);
   p->sm_log2 = sm * kLog2e;
 
-  // INT2 kernel: the matrix-core one needs 4 or 8 q heads per KV head
+  // INT2 kernel: the matrix-core one serves every supported ratio and reads
+  // the cache faster than the vector-ALU one at each of them
   p->codebook = c->codebook;
-  const bool mfma_ok = p->g == 4 || p->g == 8;
   int kind = a->int2_kernel;
-  if (kind == OSCAR_INT2_AUTO) kind = mfma_ok ? OSCAR_INT2_MFMA : OSCAR_INT2_VALU;
-  if (kind == OSCAR_INT2_MFMA && !mfma_ok)
-    return fail(OSCAR_EUNSUPPORTED,
-                "matrix-core INT2 kernel needs 4 or 8 q heads per KV head (got %d)", p->g);
+  if (kind == OSCAR_INT2_AUTO) kind = OSCAR_INT2_MFMA;
   p->int2_kind = kind;
 
   // history split.  Vector-ALU kernel: enough waves to fill the chip once (4
@@ -197,7 +194,7 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   L.qrot = off; off = align256(off + BH * p->D * 4);
   const bool mf = p->int2_kind == OSCAR_INT2_MFMA;
   L.qpk = off;
-  off = align256(off + (mf ? (size_t)a->batch * c->num_kv_heads * (p->g / 4) *
+  off = align256(off + (mf ? (size_t)a->batch * c->num_kv_heads * ((p->g + 3) / 4) *
                                  mfma_qk_steps(p->D, p->G) * 64 * 4 * 4 : 0));
   L.qhd = off; off = align256(off + (mf ? BH * 8 * 4 : 0));
   L.nslots = off; off = align256(off + (mf ? (size_t)a->batch * 4 : 0));

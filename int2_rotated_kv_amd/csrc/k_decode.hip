@@ -113,7 +113,7 @@ __device__ __forceinline__ void qrot_body(const DecodeParams &p, const uint16_t 
   for (int k = 0; k < p.g; ++k) h_in = p.q_of_kv[j2 * p.g + k] == h ? k : h_in;
   const int gpb = G < 64 ? 64 / G : 1;
   const int nqk = mfma_qk_steps(D, G);
-  const int nq = p.g / 4;
+  const int nq = (p.g + 3) / 4;          // head quads (the last one partly empty if g < 4)
   const float sc = ldexpf(1.f, sh.qe);
   const int b = bh / p.Hq;
   for (int t = tid; t < nqk * 64; t += 256) {
@@ -133,6 +133,17 @@ __device__ __forceinline__ void qrot_body(const DecodeParams &p, const uint16_t 
     const int lane = 16 * kb + 4 * (h_in & 3) + pc;
     int32_t *dst = reinterpret_cast<int32_t *>(p.ws + p.L.qpk);
     dst[((((size_t)b * p.Hkv + j2) * nq + (h_in >> 2)) * nqk + m) * 256 + lane * 4 + e] = (int32_t)word;
+  }
+  // with fewer than 4 q heads per KV head the rows of the quad's missing heads
+  // are zero (written by the last present head; nq == 1)
+  if (p.g < 4 && h_in == p.g - 1) {
+    int32_t *dst = reinterpret_cast<int32_t *>(p.ws + p.L.qpk);
+    for (int t = tid; t < nqk * 64 * (4 - p.g); t += 256) {
+      const int hh = p.g + t / (nqk * 64), u = t % (nqk * 64);
+      const int m = u >> 6, pc = (u >> 4) & 3, kb = (u >> 2) & 3, e = u & 3;
+      const int lane = 16 * kb + 4 * hh + pc;
+      dst[(((size_t)b * p.Hkv + j2) * nqk + m) * 256 + lane * 4 + e] = 0;
+    }
   }
 }
 

@@ -31,8 +31,10 @@
 // sums) come from the workspace, written by the q rotation.  The running max
 // per head is lazy: it is raised (16-lane DPP reductions, rescale of the
 // partial sums) only when a logit exceeds it by more than 2 (log2 units), so
-// unnormalised weights stay below 4.  Requires 4 or 8 q heads per KV head and
-// V group scales below 1024 (A = w * 16 must stay in f16 range).
+// unnormalised weights stay below 4.  Serves 1, 2, 4 or 8 q heads per KV head
+// (with fewer than 4 a head quad is partly empty: zero A rows, unused
+// accumulator heads) and needs V group scales below 1024 (A = w * 16 must stay
+// in f16 range).
 #include "common.hpp"
 
 namespace oscar {
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   constexpr int NH = D / 64;           // 64-channel halves of PV (lane owns l + 64*h2)
   constexpr int NQ = GQ / 4;           // head quads
   constexpr int HB = kMfmaWaves;
-  static_assert(GQ == 4 || GQ == 8, "4 or 8 q heads per KV head");
+  static_assert(GQ == 4 || GQ == 8, "one or two head quads (1, 2 or 4 q heads use one)");
 
   constexpr int NP = CB ? 3 : 1;       // code planes: the codes; with a codebook also b0, b0&b1
   __shared__ Int2Shared<D, G, GQ, NP> lds;
@@ -338,7 +340,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     cf32 *qhd = (cf32 *)(p.ws + p.L.qhd);
 #pragma unroll
     for (int h = 0; h < GQ; ++h) {
-      cf32 *hd = qhd + ((size_t)b * p.Hq + p.q_of_kv[j * GQ + h]) * 8;
+      // with fewer than GQ q heads per KV head the missing heads' A rows are
+      // zero; their per-head constants are taken from head 0 and never used
+      cf32 *hd = qhd + ((size_t)b * p.Hq + p.q_of_kv[j * p.g + (h < p.g ? h : 0)]) * 8;
       qe_h[h] = __float_as_int(hd[0]);
 #pragma unroll
       for (int g2 = 0; g2 < NG; ++g2) qz_h[h][g2] = hd[1 + g2];
@@ -738,7 +742,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
         L = fmaf(a, mlw[wk][hh][1], L);
       }
     }
-    const size_t row = ((size_t)b * p.Hq + p.q_of_kv[j2 * GQ + hh]) * S + slot;
+    if (hh >= p.g) continue;                      // a head the KV head does not have
+    const size_t row = ((size_t)b * p.Hq + p.q_of_kv[j2 * p.g + hh]) * S + slot;
     po[row * D + c] = O;
     if (c == 0) {
       pml[row * 2 + 0] = M;
@@ -764,7 +769,7 @@ static void launch_mfma_dg(const DecodeParams &p, hipStream_t s) {
 }
 
 hipError_t launch_int2_mfma(const DecodeParams &p, hipStream_t s) {
-  if (p.g != 4 && p.g != 8) return hipErrorInvalidValue;
+  if (p.g != 1 && p.g != 2 && p.g != 4 && p.g != 8) return hipErrorInvalidValue;
   if (p.D == 64 && p.G == 32) launch_mfma_dg<64, 32>(p, s);
   else if (p.D == 64 && p.G == 64) launch_mfma_dg<64, 64>(p, s);
   else if (p.D == 128 && p.G == 32) launch_mfma_dg<128, 32>(p, s);

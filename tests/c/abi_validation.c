@@ -92,8 +92,7 @@ int main(void) {
   a.int2_kernel = 9;      EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL); a = args();
   a.phases = 8;           EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL); a = args();
   a.flags = 2;            EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL); a = args();
-  a.num_q_heads = 16; a.int2_kernel = OSCAR_INT2_MFMA;
-  EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EUNSUPPORTED); a = args();
+  a.num_q_heads = 24;     EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EUNSUPPORTED); a = args();
   for (int h = 0; h < 32; ++h) head_map[h] = h % 8;   /* valid: 4 q heads per KV head */
   a.kv_head_of_q = head_map;
   EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_OK);

@@ -162,12 +162,15 @@ def test_plan_resolves_int2_kernel():
     assert st == ob.OSCAR_OK and k == ob.INT2_MFMA
     st, *_, k = _plan(_cache(), _args(int2_kernel=ob.INT2_VALU))
     assert st == ob.OSCAR_OK and k == ob.INT2_VALU
-    # 2 q heads per KV head: vector-ALU kernel; asking for MFMA is unsupported
-    st, *_, k = _plan(_cache(), _args(num_q_heads=16))
-    assert st == ob.OSCAR_OK and k == ob.INT2_VALU
-    st, *_ = _plan(_cache(), _args(num_q_heads=16, int2_kernel=ob.INT2_MFMA))
+    # 1 or 2 q heads per KV head (partly empty head quads): still matrix cores
+    for hq in (8, 16):
+        st, *_, k = _plan(_cache(), _args(num_q_heads=hq))
+        assert st == ob.OSCAR_OK and k == ob.INT2_MFMA
+        st, *_, k = _plan(_cache(), _args(num_q_heads=hq, int2_kernel=ob.INT2_VALU))
+        assert st == ob.OSCAR_OK and k == ob.INT2_VALU
+    # a ratio that is not 1, 2, 4 or 8 is unsupported by every kernel
+    st, *_ = _plan(_cache(), _args(num_q_heads=24))
     assert st == ob.OSCAR_EUNSUPPORTED
-    assert "4 or 8" in ob.lib().oscar_last_error().decode()
 
 
 def test_plan_chunking_rules():
@@ -262,10 +265,10 @@ def test_decode_step_argument_checks():
 
 def test_codebook_cache_kernel_choice():
     """A cache with a Lloyd-Max codebook is read by both INT2 kernels: AUTO
-    resolves as without one (matrix cores at 4 or 8 q heads per KV head)."""
+    resolves as without one (matrix cores)."""
     st, *_, k = _plan(_cache(codebook=0x80000), _args())
     assert st == ob.OSCAR_OK and k == ob.INT2_MFMA
     st, *_, k = _plan(_cache(codebook=0x80000), _args(int2_kernel=ob.INT2_VALU))
     assert st == ob.OSCAR_OK and k == ob.INT2_VALU
     st, *_, k = _plan(_cache(codebook=0x80000), _args(num_q_heads=16))
-    assert st == ob.OSCAR_OK and k == ob.INT2_VALU
+    assert st == ob.OSCAR_OK and k == ob.INT2_MFMA

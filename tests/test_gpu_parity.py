@@ -98,10 +98,13 @@ def test_qwen3_8b_32k_one_step(kernel):
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
-@pytest.mark.parametrize("D,G,Hq,Hkv", [(128, 128, 16, 2), (128, 32, 8, 2), (64, 64, 8, 1)])
+@pytest.mark.parametrize("D,G,Hq,Hkv", [(128, 128, 16, 2), (128, 32, 8, 2), (64, 64, 8, 1),
+                                       (128, 64, 4, 2), (128, 64, 4, 4), (64, 32, 6, 3)])
 def test_shapes(kernel, D, G, Hq, Hkv):
     """Other head_dim / group / GQA shapes: G = 128 with 8 q heads per KV head
-    (Qwen3-32B-shaped), G = 32 at D = 128, G = 64 at D = 64; ragged history."""
+    (Qwen3-32B-shaped), G = 32 at D = 128, G = 64 at D = 64; 2 and 1 q heads
+    per KV head (partly empty head quads on the matrix-core kernel), and 3 KV
+    heads with 2 q heads each; ragged history."""
     _say("case: shape", D, G, Hq, Hkv, "kernel", kernel)
     wl = synth.workload("tiny", B=2, Hkv=Hkv, Hq=Hq, D=D, G=G, lengths=(1500, 2077), steps=1, seed=11)
     inp = synth.make_small(wl)
@@ -154,8 +157,6 @@ def test_fused_step_matches_separate_calls(shape, kernel):
         # batch 8, mixed lengths: blocks of the INT2 kernel cover several sequences
         wl = synth.workload("tiny", B=8, Hkv=2, Hq=8, D=128, G=64,
                             lengths=(2000, 330, 500, 340, 900, 1200, 321, 700), steps=3, seed=35)
-    if kernel == 2 and wl.g not in (4, 8):
-        pytest.skip("matrix-core kernel needs 4 or 8 q heads per KV head")
     inp = synth.make_small(wl, distinct_rv=True)
     sep = sh.build_and_step(inp, steps=3, int2_kernel=kernel)
     fus = sh.build_and_step(inp, steps=3, int2_kernel=kernel, fused=True)
@@ -434,7 +435,7 @@ def _random_case(seed):
     B = int(rng.integers(1, 7))
     lengths = tuple(int(x) for x in rng.integers(1, 3000, B))
     steps = int(rng.integers(1, 3))
-    kernel = int(rng.choice([0, 1, 2])) if g in (4, 8) else int(rng.choice([0, 1]))
+    kernel = int(rng.choice([0, 1, 2]))
     codebook = bool(rng.integers(0, 2))
     det = bool(rng.integers(0, 2))
     return dict(D=D, G=G, Hkv=Hkv, Hq=g * Hkv, B=B, lengths=lengths, steps=steps, seed=2000 + seed), \
