@@ -52,10 +52,12 @@ __device__ __forceinline__ void bf16_seg_body(const DecodeParams &p, const uint1
   auto &wl = sh.wl;
   auto &wo = sh.wo;
 
-  // segment length and this wave's page id, then every load
+  // segment length, this wave's page id and the new token's slot (one round
+  // trip), then every load of the page (a second one)
   const int pgi = split * kBf16PagesPerSplit + w;     // page index in the table
   int T = p.bf16_len[b];
   const int64_t page = pgi < p.bf16_stride ? p.bf16_pages[(size_t)b * p.bf16_stride + pgi] : -1;
+  const int ns = nt.slot != nullptr ? nt.slot[b] : -1;
   T = T < 0 ? 0 : T;
   T = T > kMaxBf16 ? kMaxBf16 : T;
   T = T > kPage * p.bf16_stride ? kPage * p.bf16_stride : T;
@@ -74,22 +76,26 @@ __device__ __forceinline__ void bf16_seg_body(const DecodeParams &p, const uint1
     }
   }
   // this step's token sits at offset noff of this wave's page (noff = -1: not here)
-  int noff = -1;
-  if (nt.slot != nullptr && live) {
-    const int ns = nt.slot[b];
-    noff = (ns >= 0 && (ns >> 4) == page) ? (ns & 15) : -1;
-  }
+  const int noff = (live && ns >= 0 && (ns >> 4) == page) ? (ns & 15) : -1;
   v8bf ka[NM];
   uint32_t vraw[kPage];
   if (live) {
+    // the pool rows are read whatever the new token's slot holds (in bounds:
+    // the page is live); that token's K row then replaces the pool's one
     const size_t base = ((page * p.Hkv + j) * kPage) * D;
-    const uint16_t *krow = r16 == noff ? nt.k + ((size_t)b * p.Hkv + j) * D
-                                       : p.bf16_k + base + (size_t)r16 * D;
-    const uint4 *kp = reinterpret_cast<const uint4 *>(krow + 8 * kb);
+    const uint4 *kp = reinterpret_cast<const uint4 *>(p.bf16_k + base + (size_t)r16 * D + 8 * kb);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const uint4 v = kp[4 * m];
       __builtin_memcpy(&ka[m], &v, 16);
+    }
+    if (r16 == noff) {
+      const uint4 *kn = reinterpret_cast<const uint4 *>(nt.k + ((size_t)b * p.Hkv + j) * D + 8 * kb);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const uint4 v = kn[4 * m];
+        __builtin_memcpy(&ka[m], &v, 16);
+      }
     }
     const uint16_t *vp = p.bf16_v + base;
 #pragma unroll

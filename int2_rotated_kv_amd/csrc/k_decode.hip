@@ -196,25 +196,35 @@ hipError_t launch_bf16_seg(const DecodeParams &p, const uint16_t *q, hipStream_t
 // The three kinds are independent, so they run side by side instead of in four
 // dependent launches.
 // ---------------------------------------------------------------------------
+// The three block kinds share one LDS area (about 9.7 KB at D = 128 rather
+// than their 28 KB sum), so that LDS does not limit how many blocks a CU
+// holds: every kind is bound by the latency of a few dependent memory round
+// trips, so the number of blocks in flight sets the launch time.
+template <int D, int GQ>
+union StepPreShared {
+  SegShared<D, GQ> seg;
+  DemoteOneShared<D> dem;
+  QrotShared<D> qr;
+};
+
 template <int D, int G, int GQ>
 __global__ __launch_bounds__(256) void k_step_pre(DecodeParams p, const uint16_t *__restrict__ q,
                                                   const float *__restrict__ Rk, DemoteArgs da,
                                                   NewTok nt) {
+  __shared__ StepPreShared<D, GQ> sh;
   const int tid = threadIdx.x;
   int bid = blockIdx.x;
   const int nseg = p.B * p.Hkv * kBf16Splits;
   if (bid < nseg) {
-    __shared__ SegShared<D, GQ> sh;
     const int bj = bid / kBf16Splits;
-    bf16_seg_body<D, GQ>(p, q, bj / p.Hkv, bj % p.Hkv, bid % kBf16Splits, tid, nt, sh);
+    bf16_seg_body<D, GQ>(p, q, bj / p.Hkv, bj % p.Hkv, bid % kBf16Splits, tid, nt, sh.seg);
     return;
   }
   bid -= nseg;
   const int ndem = p.B * p.Hkv * 2;
   if (bid < ndem) {
-    __shared__ DemoteOneShared<D> sh;
     const int b = bid / (2 * p.Hkv), j = (bid / 2) % p.Hkv, half = bid % 2;
-    demote_one_body<D, G>(da, b, j, half, tid, sh);
+    demote_one_body<D, G>(da, b, j, half, tid, sh.dem);
     __syncthreads();
     // every read of the demoted slot (this half of head j) is done; b's new
     // token may reuse it
@@ -231,8 +241,7 @@ __global__ __launch_bounds__(256) void k_step_pre(DecodeParams p, const uint16_t
     return;
   }
   bid -= ndem;
-  __shared__ QrotShared<D> sh;
-  qrot_body<D>(p, q, Rk, bid, tid, sh);
+  qrot_body<D>(p, q, Rk, bid, tid, sh.qr);
 }
 
 template <int D, int G>
