@@ -97,11 +97,15 @@ __device__ __forceinline__ void demote_one_body(const DemoteArgs &a, int e, int 
   const bool isv = half != 0;
   const float *R = isv ? a.Rv : a.Rk;
   const int c4 = tid % NC4, gi = tid / NC4;
-  float4 r[RPG];
+  // the R rows in two halves (the second requested once the first is used),
+  // so that these blocks need fewer registers than the other block kinds of
+  // the decode-step prologue allow
+  constexpr int RH = RPG / 2;
+  float4 r[RH];
+  const float4 *Rp = reinterpret_cast<const float4 *>(R + (size_t)j * D * D) + c4;
   if (R != nullptr) {
-    const float4 *Rp = reinterpret_cast<const float4 *>(R + (size_t)j * D * D) + c4;
 #pragma unroll
-    for (int i = 0; i < RPG; ++i) r[i] = Rp[(size_t)(gi * RPG + i) * NC4];
+    for (int i = 0; i < RH; ++i) r[i] = Rp[(size_t)(gi * RPG + i) * NC4];
   }
   if (tid == 0) {
     int sv = -1, dv = -1;
@@ -131,12 +135,17 @@ __device__ __forceinline__ void demote_one_body(const DemoteArgs &a, int e, int 
     // ordered conversions keep 4 doubles live instead of RPG*4)
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
+      if (i == RH) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i2 = 0; i2 < RH; ++i2) r[i2] = Rp[(size_t)(gi * RPG + RH + i2) * NC4];
+      }
       const double ki = sh.ks[gi * RPG + i];
       double rx, ry, rz, rw;
-      asm volatile("v_cvt_f64_f32 %0, %1" : "=v"(rx) : "v"(r[i].x));
-      asm volatile("v_cvt_f64_f32 %0, %1" : "=v"(ry) : "v"(r[i].y));
-      asm volatile("v_cvt_f64_f32 %0, %1" : "=v"(rz) : "v"(r[i].z));
-      asm volatile("v_cvt_f64_f32 %0, %1" : "=v"(rw) : "v"(r[i].w));
+      asm volatile("v_cvt_f64_f32 %0, %1" : "=v"(rx) : "v"(r[i % RH].x));
+      asm volatile("v_cvt_f64_f32 %0, %1" : "=v"(ry) : "v"(r[i % RH].y));
+      asm volatile("v_cvt_f64_f32 %0, %1" : "=v"(rz) : "v"(r[i % RH].z));
+      asm volatile("v_cvt_f64_f32 %0, %1" : "=v"(rw) : "v"(r[i % RH].w));
       a0 = fma(ki, rx, a0);
       a1 = fma(ki, ry, a1);
       a2 = fma(ki, rz, a2);

@@ -44,18 +44,30 @@ __device__ __forceinline__ void qrot_body(const DecodeParams &p, const uint16_t 
   const int c4 = tid % NC4, gi = tid / NC4;
   if (tid < D) sh.qs[tid] = (double)bf16_to_f32(q[(size_t)bh * D + tid]);
   __syncthreads();
+  // the R rows in two halves (the second requested once the first is used),
+  // so that these blocks need fewer registers than the other block kinds of
+  // the decode-step prologue allow
   const float4 *R = reinterpret_cast<const float4 *>(Rk + (size_t)j * D * D) + c4;
-  float4 r[RPG];
+  constexpr int RH = RPG / 2;
+  float4 r[RH];
 #pragma unroll
-  for (int i = 0; i < RPG; ++i) r[i] = R[(size_t)(gi * RPG + i) * NC4];
+  for (int i = 0; i < RH; ++i) r[i] = R[(size_t)(gi * RPG + i) * NC4];
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
 #pragma unroll
-  for (int i = 0; i < RPG; ++i) {
-    const double qi = sh.qs[gi * RPG + i];
-    a0 = fma(qi, (double)r[i].x, a0);
-    a1 = fma(qi, (double)r[i].y, a1);
-    a2 = fma(qi, (double)r[i].z, a2);
-    a3 = fma(qi, (double)r[i].w, a3);
+  for (int hf = 0; hf < 2; ++hf) {
+    if (hf == 1) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < RH; ++i) r[i] = R[(size_t)(gi * RPG + RH + i) * NC4];
+    }
+#pragma unroll
+    for (int i = 0; i < RH; ++i) {
+      const double qi = sh.qs[gi * RPG + hf * RH + i];
+      a0 = fma(qi, (double)r[i].x, a0);
+      a1 = fma(qi, (double)r[i].y, a1);
+      a2 = fma(qi, (double)r[i].z, a2);
+      a3 = fma(qi, (double)r[i].w, a3);
+    }
   }
   sh.part[gi][4 * c4 + 0] = a0;
   sh.part[gi][4 * c4 + 1] = a1;
@@ -208,7 +220,8 @@ union StepPreShared {
 };
 
 template <int D, int G, int GQ>
-__global__ __launch_bounds__(256) void k_step_pre(DecodeParams p, const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6)))
+void k_step_pre(DecodeParams p, const uint16_t *__restrict__ q,
                                                   const float *__restrict__ Rk, DemoteArgs da,
                                                   NewTok nt) {
   __shared__ StepPreShared<D, GQ> sh;
