@@ -31,6 +31,14 @@ __host__ __device__ constexpr int mfma_qk_steps(int d, int g) { return (d / 64) 
 constexpr int kBf16Splits = kMaxBf16 / (kPage * kBf16PagesPerSplit); // 5 BF16 partials
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+#ifndef OSCAR_ROT_PARTS
+#define OSCAR_ROT_PARTS 2
+#endif
+#ifndef OSCAR_STEP_PRE_WAVES
+#define OSCAR_STEP_PRE_WAVES 6
+#endif
+constexpr int kRotParts = OSCAR_ROT_PARTS;         // R rows of a rotation thread, requested in parts
+constexpr int kStepPreWaves = OSCAR_STEP_PRE_WAVES; // decode-step prologue: waves per SIMD it must fit
 
 // Byte offsets of the four sections of one INT2 page record (16 tokens, one KV
 // head): K codes [16][D/4] | V codes [D][4] | K (s,z) [16][D/G] dwords | V (s,z).

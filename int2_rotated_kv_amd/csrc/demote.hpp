@@ -100,7 +100,7 @@ __device__ __forceinline__ void demote_one_body(const DemoteArgs &a, int e, int 
   // the R rows in two halves (the second requested once the first is used),
   // so that these blocks need fewer registers than the other block kinds of
   // the decode-step prologue allow
-  constexpr int RH = RPG / 2;
+  constexpr int RH = RPG / kRotParts;
   float4 r[RH];
   const float4 *Rp = reinterpret_cast<const float4 *>(R + (size_t)j * D * D) + c4;
   if (R != nullptr) {
@@ -135,10 +135,10 @@ __device__ __forceinline__ void demote_one_body(const DemoteArgs &a, int e, int 
     // ordered conversions keep 4 doubles live instead of RPG*4)
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
-      if (i == RH) {
+      if (i > 0 && i % RH == 0) {
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int i2 = 0; i2 < RH; ++i2) r[i2] = Rp[(size_t)(gi * RPG + RH + i2) * NC4];
+        for (int i2 = 0; i2 < RH; ++i2) r[i2] = Rp[(size_t)(gi * RPG + i + i2) * NC4];
       }
       const double ki = sh.ks[gi * RPG + i];
       double rx, ry, rz, rw;

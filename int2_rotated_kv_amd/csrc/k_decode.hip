@@ -48,17 +48,17 @@ __device__ __forceinline__ void qrot_body(const DecodeParams &p, const uint16_t 
   // so that these blocks need fewer registers than the other block kinds of
   // the decode-step prologue allow
   const float4 *R = reinterpret_cast<const float4 *>(Rk + (size_t)j * D * D) + c4;
-  constexpr int RH = RPG / 2;
+  constexpr int RH = RPG / kRotParts;
   float4 r[RH];
 #pragma unroll
   for (int i = 0; i < RH; ++i) r[i] = R[(size_t)(gi * RPG + i) * NC4];
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    if (hf == 1) {
+  for (int hf = 0; hf < kRotParts; ++hf) {
+    if (hf > 0) {
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int i = 0; i < RH; ++i) r[i] = R[(size_t)(gi * RPG + RH + i) * NC4];
+      for (int i = 0; i < RH; ++i) r[i] = R[(size_t)(gi * RPG + hf * RH + i) * NC4];
     }
 #pragma unroll
     for (int i = 0; i < RH; ++i) {
@@ -220,7 +220,7 @@ union StepPreShared {
 };
 
 template <int D, int G, int GQ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kStepPreWaves)))
 void k_step_pre(DecodeParams p, const uint16_t *__restrict__ q,
                                                   const float *__restrict__ Rk, DemoteArgs da,
                                                   NewTok nt) {
