@@ -50,8 +50,8 @@ def build_workload(name: str, total_steps: int, device="cuda", log=print, bf16_h
     oscar_demote_pack from generated BF16 tokens.  With bf16_history, the same
     tokens are also laid out as the comparison cache: every history page kept
     in BF16 at its physical id (same page tables), the sink/recent pages after
-    them.  With codebook, the cache uses the Lloyd-Max codebook variant (seeded
-    levels from synth.make_codebook)."""
+    them.  With codebook ("fit" or "symmetric"), the cache uses the Lloyd-Max
+    codebook variant (seeded levels from synth.make_codebook)."""
     import torch
     from int2_rotated_kv_amd import binding as ob
     from int2_rotated_kv_amd.splitcache import SplitCache
@@ -59,7 +59,7 @@ def build_workload(name: str, total_steps: int, device="cuda", log=print, bf16_h
     wl = synth.workload(name, steps=total_steps)
     gen = synth.LargeGen(wl, device=device)
     t0 = time.time()
-    cb = synth.make_codebook(wl.seed, wl.Hkv) if codebook else None
+    cb = synth.make_codebook(wl.seed, wl.Hkv, symmetric=codebook == "symmetric") if codebook else None
     sc = SplitCache(wl.B, wl.Hkv, wl.Hq, wl.D, wl.G, gen.hist_table, gen.n_unique,
                     staging_pages=synth.LargeGen.PAGES_PER_BLOCK, device=device,
                     codebook=None if cb is None else torch.from_numpy(cb).to(device))
@@ -583,9 +583,10 @@ def main(argv=None):
     ap.add_argument("--no-bf16-compare", action="store_true",
                     help="skip the comparison run over the same tokens with the whole "
                          "history kept in BF16 pages")
-    ap.add_argument("--codebook", action="store_true",
+    ap.add_argument("--codebook", nargs="?", const="fit", default=None, choices=["fit", "symmetric"],
                     help="use the Lloyd-Max codebook variant of the INT2 history (seeded levels; "
-                         "attended by the vector-ALU kernel)")
+                         "'symmetric': levels symmetric about the middle of the range, whose "
+                         "third code plane the matrix-core kernel skips)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run 5 plain device-to-device copies of BYTES bytes (the "
                          "reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE) and exit")
@@ -645,7 +646,8 @@ def main(argv=None):
         "config": {"workload": wl.name, "batch": wl.B, "kv_heads": wl.Hkv, "q_heads": wl.Hq,
                    "head_dim": wl.D, "group": wl.G, "mean_context": float(np.mean(wl.lengths)),
                    "sink": SINK, "recent": RECENT, "page": PAGE, "int2_kernel": kname,
-                   "splits": splits, "codebook": "lloyd-max" if a.codebook else "uniform",
+                   "splits": splits,
+                   "codebook": {"fit": "lloyd-max", "symmetric": "lloyd-max-symmetric"}.get(a.codebook, "uniform"),
                    "parallelism": "single-gpu"},
         "hbm_tbps": step_bytes / (ms_step * 1e-3) / 1e12,
         "hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,

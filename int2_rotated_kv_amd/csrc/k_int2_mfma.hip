@@ -208,6 +208,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     vcB = (lvv[1] - lvv[0]) - vcA;
     vcC = ((lvv[3] - lvv[2]) - lvv[1]) + lvv[0];
   }
+  // a symmetric codebook (L3 - L2 = L1 - L0 for K and V, as a Lloyd-Max fit
+  // of a symmetric distribution gives) has no b0&b1 term: its plane is
+  // skipped, which leaves every result bitwise the same (its weights and
+  // coefficients are 0); the test is uniform over the wave (one KV head)
+  const bool plane2 = CB && (kcC != 0.f || vcC != 0.f);
 
   // ---------------- schedule: this block's segments ----------------
   // The histories of the batch laid end to end hold T pages; block ib of its
@@ -516,6 +521,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     float dv[NP][NQ][NG];
 #pragma unroll
     for (int pl = 0; pl < NP; ++pl) {
+      if (pl == 2 && !plane2) {
+#pragma unroll
+        for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+          for (int g2 = 0; g2 < NG; ++g2) dv[2][qd][g2] = 0.f;
+        continue;
+      }
       v4i qacc[NQ][NG];
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd)
@@ -622,6 +634,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
         zacc[qd][g2] = fmaf(pr[qd], vzl, zacc[qd][g2]);
 #pragma unroll
         for (int pl = 0; pl < NP; ++pl) {
+          if (pl == 2 && !plane2) continue;
           const _Float16 wh = (_Float16)(pa[qd] * vsp[pl]);
           zacc[qd][g2] = fmaf(-4.f, (float)wh, zacc[qd][g2]);
           wbuf[pl][g2][qd * 4 + kb][pvs] = wh;
@@ -662,6 +675,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
         const int g2 = (lane + 64 * h2) / G;
 #pragma unroll
         for (int pl = 0; pl < NP; ++pl) {
+          if (pl == 2 && !plane2) continue;
           const v4h bv = as_v4h(breg(pl, h2, 2 * ti), breg(pl, h2, 2 * ti + 1));
 #pragma unroll
           for (int qd = 0; qd < NQ; ++qd) {

@@ -203,13 +203,24 @@ def _seed64(*parts) -> int:
     return int.from_bytes(h[:8], "little") & ((1 << 63) - 1)
 
 
-def make_codebook(seed: int, Hkv: int) -> np.ndarray:
+def make_codebook(seed: int, Hkv: int, symmetric: bool = False) -> np.ndarray:
     """Lloyd-Max code levels float32 [Hkv][2][4] (K, V) for the codebook
     variant, standing in for offline calibration: levels pulled towards the
     middle of the group range, (0.35, 1.15, 1.85, 2.65) in units of the group
     scale, each moved by a seeded offset in [-0.05, 0.05] so that heads and
-    K/V differ.  Ascending by construction."""
+    K/V differ.  Ascending by construction.
+
+    symmetric=True gives what a fit to a distribution symmetric about the
+    middle of the range gives: levels 1.5 -+ a, 1.5 -+ b (a near 1.15, b near
+    0.35, seeded offsets on a 1/1024 grid, so that every level and every
+    difference of levels is exact in float32 and L3 - L2 = L1 - L0 holds
+    exactly)."""
     rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    if symmetric:
+        off = np.round(rng.uniform(-0.05, 0.05, (Hkv, 2, 2)) * 1024) / 1024
+        a = np.round(1.15 * 1024) / 1024 + off[..., 0]
+        b = np.round(0.35 * 1024) / 1024 + off[..., 1]
+        return np.stack([1.5 - a, 1.5 - b, 1.5 + b, 1.5 + a], axis=-1).astype(np.float32)
     base = np.array([0.35, 1.15, 1.85, 2.65])
     return (base + rng.uniform(-0.05, 0.05, (Hkv, 2, 4))).astype(np.float32)
 

@@ -307,7 +307,7 @@ def test_deterministic_option(shape):
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
-@pytest.mark.parametrize("shape", ["tiny", "d128g64", "d128g128", "d128g32", "d64g64g8"])
+@pytest.mark.parametrize("shape", ["tiny", "d128g64", "d128g128", "d128g32", "d64g64g8", "d128g64sym"])
 def test_codebook_variant(shape, kernel):
     """Lloyd-Max codebook variant: the prompt history quantised in bulk, then
     two decode steps (one-token demotion, attention on either INT2 kernel; the
@@ -319,7 +319,7 @@ def test_codebook_variant(shape, kernel):
     _say("case: codebook variant", shape, "kernel", kernel)
     if shape == "tiny":
         wl = synth.workload("tiny", B=2, lengths=(1024, 777), steps=2, seed=81)
-    elif shape == "d128g64":
+    elif shape in ("d128g64", "d128g64sym"):
         wl = synth.workload("tiny", B=2, Hkv=2, Hq=8, D=128, G=64, lengths=(3000, 1700), steps=2, seed=82)
     elif shape == "d128g128":
         wl = synth.workload("tiny", B=2, Hkv=2, Hq=16, D=128, G=128, lengths=(2500, 999), steps=2, seed=83)
@@ -328,7 +328,11 @@ def test_codebook_variant(shape, kernel):
     else:
         wl = synth.workload("tiny", B=2, Hkv=2, Hq=16, D=64, G=64, lengths=(1800, 700), steps=2, seed=85)
     inp = synth.make_small(wl, distinct_rv=True)
-    cb = synth.make_codebook(wl.seed, wl.Hkv)
+    # "sym": levels symmetric about the middle of the range, whose b0&b1 term
+    # is exactly 0 (the matrix-core kernel then skips that code plane)
+    cb = synth.make_codebook(wl.seed, wl.Hkv, symmetric=shape.endswith("sym"))
+    if shape.endswith("sym"):
+        assert np.all(((cb[..., 3] - cb[..., 2]) - cb[..., 1]) + cb[..., 0] == 0)
     kw = dict(steps=2, int2_kernel=kernel, codebook=cb, flags=ob.FLAG_DETERMINISTIC)
     sep = sh.build_and_step(inp, **kw)
     fus = sh.build_and_step(inp, fused=True, **kw)

@@ -96,3 +96,21 @@ def test_merge_of_any_chunking_is_one_softmax(n, D, data):
     assert M == m
     assert math.isclose(L, e.sum(), rel_tol=1e-12)
     assert np.allclose(O / L, (e @ v) / e.sum(), rtol=1e-12, atol=1e-12)
+
+
+def test_symmetric_codebook_generator():
+    """The symmetric Lloyd-Max stand-in: ascending levels inside the group
+    range [0, 3], mirrored about 1.5, with L3 - L2 - L1 + L0 exactly 0 when
+    evaluated in float32 in the kernels' order (the condition under which the
+    matrix-core kernel skips its b0&b1 plane)."""
+    from synth import inputs as syn
+    for seed in range(5):
+        cb = syn.make_codebook(seed, 8, symmetric=True)
+        assert cb.dtype == np.float32 and cb.shape == (8, 2, 4)
+        assert np.all(np.diff(cb, axis=-1) > 0) and np.all(cb >= 0) and np.all(cb <= 3)
+        assert np.all(cb[..., 0] + cb[..., 3] == np.float32(3)) and np.all(cb[..., 1] + cb[..., 2] == np.float32(3))
+        cc = ((cb[..., 3] - cb[..., 2]) - cb[..., 1]) + cb[..., 0]
+        assert np.all(cc == 0)
+        # the fitted (asymmetric) stand-in keeps a non-zero term
+        fit = syn.make_codebook(seed, 8)
+        assert np.any(((fit[..., 3] - fit[..., 2]) - fit[..., 1]) + fit[..., 0] != 0)
