@@ -134,8 +134,11 @@ typedef struct {
                                 midpoints, a tie to the lower level).  NULL =
                                 the uniform levels 0, 1, 2, 3.  Both INT2
                                 kernels read it (the matrix-core one with two
-                                more bit-plane contractions).  Level order and
-                                finiteness are not checked (device memory)   */
+                                more bit-plane contractions, or one when a KV
+                                head's K and V levels are symmetric, i.e.
+                                L3 - L2 == L1 - L0 exactly in fp32).  Level
+                                order and finiteness are not checked (device
+                                memory)                                      */
 } oscar_cache;
 
 typedef struct {
