@@ -100,6 +100,9 @@ def build_workload(name: str, total_steps: int, device="cuda", log=print, bf16_h
     torch.cuda.synchronize()
     log(f"[bench] built {name}: {gen.n_unique} unique INT2 pages "
         f"({gen.n_unique * wl.Hkv * sc.cache.rec / 1e9:.2f} GB) in {time.time() - t0:.1f}s")
+    status = sc.cache.read_status()
+    if status:
+        raise RuntimeError(f"demotion reported status bits {status:#x} on {name}")
 
     # plan every step on the host; upload the slot lists and lengths once
     T = total_steps
@@ -641,7 +644,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32-accum (int8 QK pieces, f16 PV weights)",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "kv_heads": wl.Hkv, "q_heads": wl.Hq,
                    "head_dim": wl.D, "group": wl.G, "mean_context": float(np.mean(wl.lengths)),

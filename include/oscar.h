@@ -97,13 +97,15 @@ enum {
 /* Which kernel computes the INT2 segment.  AUTO picks MFMA, which serves 1,
  * 2, 4 or 8 q heads per KV head (with 1 or 2 the head quads are partly empty;
  * it still reads the cache about 2.3 to 2.9 times faster than VALU there).
- * VALU is the kernel to ask for when the V scales exceed what the MFMA
- * kernel's f16 weights hold, as stated next.  The MFMA kernel
- * carries the PV weights p * scale_v * 16 (p < 4) in f16, so it requires V
- * group scales below 1024 (|V| up to ~3000 after rotation; with a codebook,
- * scale_v times the largest of |L2 - L0|/2, |L1 - L0 - (L2 - L0)/2| and
- * |L3 - L2 - L1 + L0| below 1024); the VALU kernel has no such limit.  Neither
- * is checked (the scales live on the device). */
+ * The MFMA kernel carries the PV weights p * scale_v * c * 2^(8-b) (p <= 4,
+ * 2^(8-b) <= 16) in f16, so it needs every V group scale times the largest
+ * codebook coefficient magnitude c (1 without a codebook; with one, the
+ * largest of |L2 - L0|/2, |(L1 - L0) - (L2 - L0)/2| and |L3 - L2 - L1 + L0|,
+ * each computed in fp32) to stay below OSCAR_MFMA_V_SCALE_LIMIT.  The
+ * demotion paths check this for every group they write and set
+ * OSCAR_STATUS_MFMA_V_RANGE in oscar_cache.status when it fails; the caller
+ * must then ask for VALU, which has no such limit (its outputs over such a
+ * cache are correct, the MFMA kernel's may be inf or NaN). */
 enum {
   OSCAR_INT2_AUTO = 0,
   OSCAR_INT2_VALU = 1,      /* vector-ALU dot products                         */
@@ -112,6 +114,31 @@ enum {
                                BF16 pages of the BF16 pool (unrotated,
                                unquantised); oscar_decode_attn skips the query
                                rotation and oscar_merge ignores R_v            */
+};
+
+/* Largest V group scale (times the codebook coefficient, see above) that
+ * the MFMA kernel's f16 PV weights hold: 16 * 4 * 1023 = 65472 < 65504. */
+#define OSCAR_MFMA_V_SCALE_LIMIT 1023.0f
+
+/* Bits of the sticky device status word oscar_cache.status.  The demotion
+ * paths (oscar_demote_pack and the demotion inside oscar_decode_step) OR
+ * them in; nothing clears them but the caller (e.g. a hipMemsetAsync of 0).
+ * They report problems in device-resident inputs, which the host-side
+ * validation cannot see without a device-to-host read. */
+enum {
+  OSCAR_STATUS_CLIP_RANGE = 1,    /* a clip ratio outside (0, 1] (or NaN) was
+                                     met: the groups quantised with it were
+                                     written with scale 0, zero 0 and codes 0
+                                     (the token reads back as 0) instead of
+                                     from a clipped range                      */
+  OSCAR_STATUS_MFMA_V_RANGE = 2,  /* a V group scale (times the largest
+                                     codebook coefficient magnitude) reached
+                                     OSCAR_MFMA_V_SCALE_LIMIT: use
+                                     OSCAR_INT2_VALU for this cache            */
+  OSCAR_STATUS_NONFINITE = 4      /* a rotated value, scale or zero point was
+                                     inf or NaN (an inf/NaN input token, or
+                                     values near the fp32 range): its codes,
+                                     scale and zero are unspecified            */
 };
 
 typedef struct {
@@ -134,11 +161,16 @@ typedef struct {
                                 midpoints, a tie to the lower level).  NULL =
                                 the uniform levels 0, 1, 2, 3.  Both INT2
                                 kernels read it (the matrix-core one with two
-                                more bit-plane contractions, or one when a KV
-                                head's K and V levels are symmetric, i.e.
-                                L3 - L2 == L1 - L0 exactly in fp32).  Level
-                                order and finiteness are not checked (device
-                                memory)                                      */
+                                more bit-plane contractions, or one when the
+                                b0&b1 coefficient ((L3 - L2) - L1) + L0,
+                                evaluated in fp32 in that order, is 0 for K
+                                and V of a KV head, as for levels symmetric
+                                about their middle).  Level order and
+                                finiteness are not checked (device memory) */
+  uint32_t *status;          /* device word (4-byte aligned) or NULL: sticky
+                                OSCAR_STATUS_* bits set by the demotion paths
+                                (the calls that write records); NULL = not
+                                reported                                     */
 } oscar_cache;
 
 typedef struct {
@@ -190,28 +222,34 @@ int oscar_write_bf16(const oscar_cache *cache, int32_t n, const int32_t *dst_slo
 /*
  * oscar_demote_pack - rotate, clip, quantise and pack n tokens from BF16 slots
  * into INT2 history slots (thmotor: split-cache paragraph, rotate/clip/
- * quantize/pack at demotion, four 2-bit values per byte).
+ * quantize/pack at demotion, four 2-bit values per byte; the clipping
+ * threshold is per layer and head, calibration paragraph).
  *   src_slot [n]   BF16 slot (page*16+off) read for every KV head, or -1 to skip
  *   dst_slot [n]   INT2 slot (page*16+off) written for every KV head
  *   R_k, R_v       [Hkv][D][D] fp32, row-vector convention x = k . R;
  *                  R_v == NULL means identity (value rotation folded upstream)
- *   clip_k, clip_v [Hkv] fp32 clipping ratios in (0, 1]
+ *   clip_k, clip_v [Hkv] fp32 clipping ratios in (0, 1], per KV head
  * Per (token, KV head, K|V): x = k . R in fp64; per group of G consecutive
  * channels mx, mn = max, min; scale = (c*mx - c*mn)/3 and zero = c*mn rounded
  * to bf16 (nearest even, from fp64); code = clamp(rint((x - zero)/scale), 0, 3)
  * (0 when scale == 0).  The other tokens' bits in a shared record are
  * preserved, so any set of distinct destination slots may be demoted in one
  * call; two entries with the same destination race.
- * Errors: EINVAL (NULL pointers with n > 0, clip outside (0,1] is not checked
- * on the device: pass validated values), EUNSUPPORTED (D, G), EHIP.
+ * Device-side checks (reported through cache->status, see OSCAR_STATUS_*):
+ * a clip ratio outside (0, 1] is rejected (that head's K or V groups are
+ * written as scale 0, zero 0, codes 0), a V scale at the matrix-core limit
+ * and non-finite values are flagged.
+ * Errors: EINVAL (NULL pointers with n > 0, misaligned pointers), EUNSUPPORTED
+ * (D, G), EHIP.
  */
 int oscar_demote_pack(const oscar_cache *cache, int32_t n, const int32_t *src_slot,
                       const int32_t *dst_slot, const float *R_k, const float *R_v,
                       const float *clip_k, const float *clip_v, void *stream);
 
-/* Workspace bytes oscar_decode_attn needs for these arguments (host only). */
-int oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_args *args,
-                                 size_t *bytes);
+/* Workspace bytes oscar_decode_attn, oscar_merge and oscar_decode_step need
+ * for these arguments (host only).  0 when the arguments are invalid (the
+ * reason is in oscar_last_error()); never 0 for valid arguments. */
+size_t oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_args *args);
 
 /*
  * oscar_decode_plan - the history chunking oscar_decode_attn will use for these

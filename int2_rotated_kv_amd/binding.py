@@ -23,6 +23,8 @@ OSCAR_EHIP = -4
 INT2_AUTO, INT2_VALU, INT2_MFMA, HISTORY_BF16 = 0, 1, 2, 3
 PHASE_QROT, PHASE_BF16, PHASE_INT2, PHASE_ALL = 1, 2, 4, 7
 FLAG_DETERMINISTIC = 1
+STATUS_CLIP_RANGE, STATUS_MFMA_V_RANGE, STATUS_NONFINITE = 1, 2, 4
+MFMA_V_SCALE_LIMIT = 1023.0
 PAGE = 16
 SINK, RECENT = 64, 256
 MAX_BF16 = SINK + RECENT
@@ -42,6 +44,7 @@ class OscarCache(ctypes.Structure):
         ("bf16_v_pool", ctypes.c_void_p),
         ("num_bf16_pages", ctypes.c_int64),
         ("codebook", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
     ]
 
 
@@ -82,9 +85,8 @@ _SIGS = {
     "oscar_demote_pack": (ctypes.c_int, [ctypes.POINTER(OscarCache), ctypes.c_int32, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
-    "oscar_decode_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(OscarCache),
-                                                    ctypes.POINTER(OscarDecodeArgs),
-                                                    ctypes.POINTER(ctypes.c_size_t)]),
+    "oscar_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(OscarCache),
+                                                       ctypes.POINTER(OscarDecodeArgs)]),
     "oscar_decode_plan": (ctypes.c_int, [ctypes.POINTER(OscarCache), ctypes.POINTER(OscarDecodeArgs),
                                          ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                          ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int32)]),
@@ -151,11 +153,14 @@ class Cache:
     bf16_v uint16 [num_bf16_pages, Hkv, 16, D]    torch.bfloat16 when needed)
     codebook float32 [Hkv, 2, 4] device tensor or None: the Lloyd-Max code levels
            of K and V per KV head (None: the uniform levels 0, 1, 2, 3)
+    status int32 [1]: the sticky STATUS_* word the demotion paths set (zeroed
+           here; read_status() synchronises and returns it)
     """
 
     def __init__(self, Hkv: int, D: int, G: int, num_int2_pages: int, num_bf16_pages: int,
                  device="cuda", int2=None, bf16_k=None, bf16_v=None, codebook=None):
         import torch
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
         self.Hkv, self.D, self.G = Hkv, D, G
         if codebook is not None:
             if tuple(codebook.shape) != (Hkv, 2, 4) or codebook.dtype != torch.float32:
@@ -177,7 +182,15 @@ class Cache:
         return OscarCache(self.Hkv, self.D, self.G, PAGE, _ptr(self.int2) if self.int2.numel() else 0,
                           self.num_int2_pages, _ptr(self.bf16_k) if self.bf16_k.numel() else 0,
                           _ptr(self.bf16_v) if self.bf16_v.numel() else 0, self.num_bf16_pages,
-                          _ptr(self.codebook) if self.codebook is not None else None)
+                          _ptr(self.codebook) if self.codebook is not None else None,
+                          _ptr(self.status))
+
+    def read_status(self) -> int:
+        """The STATUS_* bits set so far (a device-to-host read)."""
+        return int(self.status.item()) & 0xFFFFFFFF
+
+    def clear_status(self):
+        self.status.zero_()
 
 
 def write_bf16(cache: Cache, dst_slots, k_new, v_new, stream=None):
@@ -235,9 +248,10 @@ class DecodeArgs:
 
 def workspace_bytes(cache: Cache, args: DecodeArgs) -> int:
     d = cache.desc()
-    out = ctypes.c_size_t(0)
-    check(lib().oscar_decode_workspace_bytes(ctypes.byref(d), ctypes.byref(args.c), ctypes.byref(out)))
-    return int(out.value)
+    n = int(lib().oscar_decode_workspace_bytes(ctypes.byref(d), ctypes.byref(args.c)))
+    if n == 0:
+        raise OscarError(OSCAR_EINVAL, last_error())
+    return n
 
 
 def decode_plan(cache: Cache, args: DecodeArgs):

@@ -54,6 +54,8 @@ int check_cache(const oscar_cache *c) {
       (c->bf16_k_pool == nullptr || c->bf16_v_pool == nullptr || !aligned(c->bf16_k_pool, 16) ||
        !aligned(c->bf16_v_pool, 16)))
     return fail(OSCAR_EINVAL, "bf16 pools are NULL or not 16-byte aligned");
+  if (c->status != nullptr && !aligned(c->status, 4))
+    return fail(OSCAR_EINVAL, "status word is not 4-byte aligned");
   return OSCAR_OK;
 }
 
@@ -256,14 +258,10 @@ int oscar_demote_pack(const oscar_cache *cache, int32_t n, const int32_t *src_sl
   return OSCAR_OK;
 }
 
-int oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_args *args,
-                                 size_t *bytes) {
+size_t oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode_args *args) {
   DecodeParams p{};
-  int st = check_args(cache, args, &p);
-  if (st) return st;
-  if (!bytes) return fail(OSCAR_EINVAL, "bytes is NULL");
-  *bytes = p.L.total;
-  return OSCAR_OK;
+  if (check_args(cache, args, &p) != OSCAR_OK) return 0;
+  return p.L.total;
 }
 
 int oscar_decode_plan(const oscar_cache *cache, const oscar_decode_args *args,

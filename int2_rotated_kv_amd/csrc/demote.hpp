@@ -50,7 +50,47 @@ struct DemoteArgs {
   const float *Rk, *Rv;            // [Hkv][D][D]; Rv may be NULL (identity)
   const float *clip_k, *clip_v;    // [Hkv]
   const float *codebook;           // [Hkv][2][4] code levels (K, V) or nullptr
+  uint32_t *status;                // sticky OSCAR_STATUS_* word or nullptr
 };
+
+// The clipped range [c*mn, c*mx] of a group (one fp64 product each) when the
+// ratio c is in (0, 1]; a ratio outside it (or NaN) is rejected: the range is
+// [+0, +0], so the group gets scale 0, zero 0 and codes 0, and the
+// OSCAR_STATUS_CLIP_RANGE bit is set.
+__device__ inline void clipped_range(float c, double mx, double mn, uint32_t &flags, double &hi,
+                                     double &lo) {
+#pragma clang fp contract(off)
+  if (c > 0.f && c <= 1.f) {
+    hi = (double)c * mx;
+    lo = (double)c * mn;
+  } else {
+    flags |= OSCAR_STATUS_CLIP_RANGE;
+    hi = 0.0;
+    lo = 0.0;
+  }
+}
+
+// Largest magnitude of the coefficients the matrix-core kernel multiplies a V
+// scale by: 1 for the uniform levels; with a codebook the b-plane
+// coefficients (L2 - L0)/2, (L1 - L0) - (L2 - L0)/2, L3 - L2 - L1 + L0, each
+// in fp32 as that kernel forms them.
+__device__ inline float v_coef_max(const float *lv) {
+  if (lv == nullptr) return 1.f;
+  const float cA = 0.5f * (lv[2] - lv[0]);
+  const float cB = (lv[1] - lv[0]) - cA;
+  const float cC = ((lv[3] - lv[2]) - lv[1]) + lv[0];
+  return fmaxf(fabsf(cA), fmaxf(fabsf(cB), fabsf(cC)));
+}
+
+// Status bits of one group's bf16 scale and zero (and, for V, the f16 range
+// of the matrix-core kernel's weights).
+__device__ inline uint32_t group_flags(double scale, double lo, uint16_t sb, bool isv, const float *lv) {
+  uint32_t f = 0;
+  if (!isfinite(scale) || !isfinite(lo)) f |= OSCAR_STATUS_NONFINITE;
+  if (isv && !(bf16_to_f32(sb) * v_coef_max(lv) < OSCAR_MFMA_V_SCALE_LIMIT))
+    f |= OSCAR_STATUS_MFMA_V_RANGE;
+  return f;
+}
 
 // Code of rotated value x in a group with bf16 scale sd and zero zd (both as
 // fp64): with the uniform levels clamp(rint((x - zd) / sd), 0, 3); with a
@@ -182,22 +222,24 @@ __device__ __forceinline__ void demote_one_body(const DemoteArgs &a, int e, int 
   }
   if (c >= D) return;
 
-  const double clip = (double)(isv ? a.clip_v[j] : a.clip_k[j]);
-  const double hi = clip * mx;
-  const double lo = clip * mn;
+  uint32_t flags = isfinite(x) ? 0u : (uint32_t)OSCAR_STATUS_NONFINITE;
+  double hi, lo;
+  clipped_range(isv ? a.clip_v[j] : a.clip_k[j], mx, mn, flags, hi, lo);
   const double scale = (hi - lo) / 3.0;
   const uint16_t sb = f64_to_bf16_rne(scale);
   const uint16_t zb = f64_to_bf16_rne(lo);
   const double sd = (double)bf16_to_f32(sb);
   const double zd = (double)bf16_to_f32(zb);
-  const uint32_t code =
-      quant_code(x, zd, sd, a.codebook ? a.codebook + (j * 2 + (isv ? 1 : 0)) * 4 : nullptr);
+  const float *lv = a.codebook ? a.codebook + (j * 2 + (isv ? 1 : 0)) * 4 : nullptr;
+  const uint32_t code = quant_code(x, zd, sd, lv);
   const int64_t page = d >> 4, off = d & 15;
   uint8_t *rec = a.pool + ((size_t)page * a.Hkv + j) * RL.bytes();
   if ((c % G) == 0) {
     const int o = isv ? RL.vsz((int)off, c / G) : RL.ksz((int)off, c / G);
     *reinterpret_cast<uint32_t *>(rec + o) = (uint32_t)sb | ((uint32_t)zb << 16);
+    flags |= group_flags(scale, lo, sb, isv, lv);
   }
+  if (flags != 0 && a.status != nullptr) atomicOr(a.status, flags);
   if (!isv) {
     // K: word blk of lane slot 16*kb + t holds channels 64*blk + 16*kb + i of
     // token t at bits 2i

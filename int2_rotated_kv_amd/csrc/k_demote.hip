@@ -95,7 +95,8 @@ __global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
 #pragma unroll
   for (int t = 0; t < T; ++t) x[t] = xs[t][c];
 
-  const double clip = (double)(isv ? a.clip_v[j] : a.clip_k[j]);
+  uint32_t flags = 0;
+  const float clip = isv ? a.clip_v[j] : a.clip_k[j];
   const float *lv = a.codebook ? a.codebook + (j * 2 + (isv ? 1 : 0)) * 4 : nullptr;
   // Per (token, group), once: max and min (RT consecutive threads scan PG
   // channels each, then combine by shuffles), the clipped range, and the bf16
@@ -116,8 +117,8 @@ __global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
       mn = fmin(mn, __shfl_xor(mn, o));
     }
     if (sub == 0) {
-      const double hi = clip * mx;
-      const double lo = clip * mn;
+      double hi, lo;
+      clipped_range(clip, mx, mn, flags, hi, lo);
       const double scale = (hi - lo) / 3.0;
       const uint16_t sb = f64_to_bf16_rne(scale);
       const uint16_t zb = f64_to_bf16_rne(lo);
@@ -129,6 +130,7 @@ __global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
         uint8_t *rec = a.pool + ((size_t)page * a.Hkv + j) * RL.bytes();
         const int o = isv ? RL.vsz((int)off, g2) : RL.ksz((int)off, g2);
         *reinterpret_cast<uint32_t *>(rec + o) = (uint32_t)sb | ((uint32_t)zb << 16);
+        flags |= group_flags(scale, lo, sb, isv, lv);
       }
     }
   }
@@ -152,6 +154,7 @@ __global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
   for (int t = 0; t < T; ++t) {
     const int d = s_dst[t];
     if (d < 0) continue;                       // uniform
+    if (!isfinite(x[t])) flags |= OSCAR_STATUS_NONFINITE;
     const uint32_t code = quant_code(x[t], s_zd[t][c / G], s_sd[t][c / G], lv);
     const int64_t page = d >> 4, off = d & 15;
     uint8_t *rec = a.pool + ((size_t)page * a.Hkv + j) * RL.bytes();
@@ -176,6 +179,7 @@ __global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
     }
   }
   if (isv) flush_v();
+  if (flags != 0 && a.status != nullptr) atomicOr(a.status, flags);
 }
 
 // The few tokens of a decode step: one (entry, KV head, K|V) per block of 256
@@ -238,6 +242,7 @@ DemoteArgs demote_args(const oscar_cache &c, int n, const int32_t *src, const in
   a.clip_k = ck;
   a.clip_v = cv;
   a.codebook = c.codebook;
+  a.status = c.status;
   return a;
 }
 

@@ -521,12 +521,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     float dv[NP][NQ][NG];
 #pragma unroll
     for (int pl = 0; pl < NP; ++pl) {
-      if (pl == 2 && !plane2) {
+      if constexpr (NP == 3) {
+        if (pl == 2 && !plane2) {
 #pragma unroll
-        for (int qd = 0; qd < NQ; ++qd)
+          for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-          for (int g2 = 0; g2 < NG; ++g2) dv[2][qd][g2] = 0.f;
-        continue;
+            for (int g2 = 0; g2 < NG; ++g2) dv[2][qd][g2] = 0.f;
+          continue;
+        }
       }
       v4i qacc[NQ][NG];
 #pragma unroll

@@ -50,6 +50,9 @@ class Workload:
     steps: int = 1
     shared_prefix: int = 0  # tokens of prefix whose history pages every sequence aliases
     distinct_frac: float = 0.0  # fraction of sequences with their own suffix (rest share one)
+    clip_set: tuple = ()    # per-KV-head clip ratios drawn from this set, K != V per head;
+                            # empty: `clip` for every head, K and V alike
+    v_range: float = 0.0    # > 0: V tokens uniform in [-v_range, v_range], no outliers
 
     @property
     def g(self) -> int:
@@ -61,19 +64,29 @@ def _lengths_uniform(seed: int, B: int, lo: int, hi: int) -> tuple:
     return tuple(int(x) for x in rng.integers(lo, hi + 1, size=B))
 
 
+# Clip ratios of the model-shaped workloads: one per (KV head, K|V), seeded,
+# from a set near 1 (the ratio is a per-layer, per-head calibration constant;
+# the tiny workload keeps the single 0.95 it is specified with).  The library
+# and the oracle both read the float32 nearest to each value.
+MODEL_CLIPS = (1.0, 0.95, 0.9, 0.85)
+# A wider set for parity cases, so that a mixed-up head or K/V index changes
+# bytes everywhere.
+WIDE_CLIPS = (1.0, 0.8, 0.5, 0.95)
+
 WORKLOADS: Dict[str, Workload] = {
     # 64 sink + 704 history + 256 recent, one decode step
     "tiny": Workload("tiny", B=1, Hkv=1, Hq=4, D=64, G=32, lengths=(1024,), seed=0,
                      n_outliers=4, outlier_scale=20.0),
     "qwen3-8b-32k": Workload("qwen3-8b-32k", B=1, Hkv=8, Hq=32, D=128, G=64,
-                             lengths=(32768,), seed=1),
+                             lengths=(32768,), seed=1, clip_set=MODEL_CLIPS),
     "qwen3-8b-100k-b1": Workload("qwen3-8b-100k-b1", B=1, Hkv=8, Hq=32, D=128, G=64,
-                                 lengths=(102400,), seed=2, steps=1000),
+                                 lengths=(102400,), seed=2, steps=1000, clip_set=MODEL_CLIPS),
     "qwen3-8b-b32-100k": Workload("qwen3-8b-b32-100k", B=32, Hkv=8, Hq=32, D=128, G=64,
-                                  lengths=_lengths_uniform(3, 32, 90000, 100000), seed=3),
+                                  lengths=_lengths_uniform(3, 32, 90000, 100000), seed=3,
+                                  clip_set=MODEL_CLIPS),
     "qwen3-32b-b16-128k": Workload("qwen3-32b-b16-128k", B=16, Hkv=8, Hq=64, D=128, G=128,
                                    lengths=(131072,) * 16, seed=4, shared_prefix=32768,
-                                   distinct_frac=0.2),
+                                   distinct_frac=0.2, clip_set=MODEL_CLIPS),
 }
 
 
@@ -169,6 +182,23 @@ class SmallInputs:
     out_v: np.ndarray
 
 
+def clip_ratios(wl: Workload):
+    """float32 [Hkv] clip ratios for K and for V.  With wl.clip_set: per KV
+    head a seeded pair of distinct values of the set (K != V); otherwise
+    wl.clip everywhere.  Drawn from their own generator, so the token streams
+    do not depend on it."""
+    if not wl.clip_set:
+        c = np.full(wl.Hkv, wl.clip, dtype=np.float32)
+        return c, c.copy()
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 31337))
+    vals = np.array(wl.clip_set, dtype=np.float64)
+    ck, cv = np.empty(wl.Hkv), np.empty(wl.Hkv)
+    for j in range(wl.Hkv):
+        a, b = rng.choice(len(vals), size=2, replace=False)
+        ck[j], cv[j] = vals[a], vals[b]
+    return ck.astype(np.float32), cv.astype(np.float32)
+
+
 def make_small(wl: Workload, distinct_rv: bool = False) -> SmallInputs:
     """All inputs of a small workload.  Token t of sequence b is K[b][t]; tokens
     L_b .. L_b+steps-1 are the new tokens appended by the decode steps."""
@@ -181,10 +211,28 @@ def make_small(wl: Workload, distinct_rv: bool = False) -> SmallInputs:
     for b in range(wl.B):
         n = wl.lengths[b] + wl.steps
         K.append(_gaussian_kv(rng, n, wl.Hkv, wl.D, out_k, wl.outlier_scale))
-        V.append(_gaussian_kv(rng, n, wl.Hkv, wl.D, out_v, wl.outlier_scale))
+        if wl.v_range > 0:
+            u = rng.uniform(-wl.v_range, wl.v_range, (n, wl.Hkv, wl.D)).astype(np.float32)
+            V.append(_f32_to_bf16_bits(u))
+        else:
+            V.append(_gaussian_kv(rng, n, wl.Hkv, wl.D, out_v, wl.outlier_scale))
     q = _f32_to_bf16_bits(rng.standard_normal((wl.steps, wl.B, wl.Hq, wl.D), dtype=np.float32))
-    clip = np.full(wl.Hkv, wl.clip, dtype=np.float32)
-    return SmallInputs(wl, q, K, V, R_k, R_v, clip, clip.copy(), out_k, out_v)
+    clip_k, clip_v = clip_ratios(wl)
+    return SmallInputs(wl, q, K, V, R_k, R_v, clip_k, clip_v, out_k, out_v)
+
+
+def plant_tokens(inp: SmallInputs, b: int, positions, kind: str, value: float = 0.0,
+                 which: str = "kv") -> SmallInputs:
+    """Overwrite tokens of sequence b (in place, token order positions) with
+    degenerate content: kind "zero" (every channel +0) or "const" (every
+    channel `value`, rounded to bf16); which = "k", "v" or "kv"."""
+    bits = _f32_to_bf16_bits(np.array([0.0 if kind == "zero" else value], np.float32))[0]
+    for t in positions:
+        if "k" in which:
+            inp.K[b][t] = bits
+        if "v" in which:
+            inp.V[b][t] = bits
+    return inp
 
 
 def page_permutation(seed: int, n_pages: int, extra: int = 0) -> np.ndarray:
@@ -247,8 +295,7 @@ class LargeGen:
         self.R_v = self.R_k.copy()
         self.out_k = _outliers(rng, wl.Hkv, wl.D, wl.n_outliers)
         self.out_v = _outliers(rng, wl.Hkv, wl.D, wl.n_outliers)
-        self.clip_k = np.full(wl.Hkv, wl.clip, dtype=np.float32)
-        self.clip_v = self.clip_k.copy()
+        self.clip_k, self.clip_v = clip_ratios(wl)
         self._build_page_map()
         self._scale_k = self._channel_scale(self.out_k)
         self._scale_v = self._channel_scale(self.out_v)

@@ -65,8 +65,22 @@ int main(void) {
   int32_t head_map[32];
 
   /* host-only queries with valid arguments */
-  EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_OK);
-  if (bytes == 0) { fprintf(stderr, "workspace of 0 bytes\n"); ++failures; }
+  EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_OK);
+  if (bytes == 0 || oscar_decode_workspace_bytes(&c, &a) != bytes) {
+    fprintf(stderr, "workspace bytes %zu vs %zu\n", bytes, oscar_decode_workspace_bytes(&c, &a));
+    ++failures;
+  }
+  /* the size query reports invalid arguments as 0 bytes, with an error text */
+  a.batch = 0;
+  if (oscar_decode_workspace_bytes(&c, &a) != 0 || oscar_last_error()[0] == '\0') {
+    fprintf(stderr, "workspace bytes of invalid arguments\n");
+    ++failures;
+  }
+  a = args();
+  if (oscar_decode_workspace_bytes(NULL, &a) != 0 || oscar_decode_workspace_bytes(&c, NULL) != 0) {
+    fprintf(stderr, "workspace bytes of NULL descriptors\n");
+    ++failures;
+  }
   EXPECT(oscar_decode_plan(&c, &a, &ns, &pps, &bytes, &kind), OSCAR_OK);
   if (kind != OSCAR_INT2_MFMA) { fprintf(stderr, "AUTO resolved to %d\n", kind); ++failures; }
   if (oscar_record_bytes(128, 64) != 1280 || oscar_record_bytes(100, 64) != 0) {
@@ -75,35 +89,41 @@ int main(void) {
   }
 
   /* cache descriptor errors */
-  c.head_dim = 96;   EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EUNSUPPORTED); c = cache();
-  c.group_size = 48; EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EUNSUPPORTED); c = cache();
-  c.page_size = 32;  EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL); c = cache();
-  c.num_kv_heads = 0; EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL); c = cache();
-  EXPECT(oscar_decode_workspace_bytes(NULL, &a, &bytes), OSCAR_EINVAL);
-  EXPECT(oscar_decode_workspace_bytes(&c, NULL, &bytes), OSCAR_EINVAL);
+  c.head_dim = 96;   EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EUNSUPPORTED); c = cache();
+  c.group_size = 48; EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EUNSUPPORTED); c = cache();
+  c.page_size = 32;  EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL); c = cache();
+  c.num_kv_heads = 0; EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL); c = cache();
+  c.status = (uint32_t *)dev(0x1002);   /* status word not 4-byte aligned */
+  EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL);
+  EXPECT(oscar_demote_pack(&c, 2, (const int32_t *)dev(0x800000), (const int32_t *)dev(0x800100),
+                           (const float *)dev(0x900000), NULL, (const float *)dev(0x900000),
+                           (const float *)dev(0x900000), NULL), OSCAR_EINVAL);
+  c = cache();
+  EXPECT(oscar_decode_plan(NULL, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL);
+  EXPECT(oscar_decode_plan(&c, NULL, NULL, NULL, &bytes, NULL), OSCAR_EINVAL);
 
   /* argument errors */
-  a.batch = 0;            EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL); a = args();
-  a.num_q_heads = 12;     EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL); a = args();
-  a.num_q_heads = 512;    EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL); a = args();
-  a.hist_stride = 6;      EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL); a = args();
-  a.max_hist_len = -1;    EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL); a = args();
-  a.sm_scale = -1.f;      EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL); a = args();
-  a.int2_kernel = 9;      EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL); a = args();
-  a.phases = 8;           EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL); a = args();
-  a.flags = 2;            EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL); a = args();
-  a.num_q_heads = 24;     EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EUNSUPPORTED); a = args();
+  a.batch = 0;            EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL); a = args();
+  a.num_q_heads = 12;     EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL); a = args();
+  a.num_q_heads = 512;    EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL); a = args();
+  a.hist_stride = 6;      EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL); a = args();
+  a.max_hist_len = -1;    EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL); a = args();
+  a.sm_scale = -1.f;      EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL); a = args();
+  a.int2_kernel = 9;      EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL); a = args();
+  a.phases = 8;           EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL); a = args();
+  a.flags = 2;            EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL); a = args();
+  a.num_q_heads = 24;     EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EUNSUPPORTED); a = args();
   for (int h = 0; h < 32; ++h) head_map[h] = h % 8;   /* valid: 4 q heads per KV head */
   a.kv_head_of_q = head_map;
-  EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_OK);
+  EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_OK);
   head_map[0] = 8;                                    /* out of range */
-  EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL);
+  EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL);
   head_map[0] = 1;                                    /* unequal group sizes */
-  EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_EINVAL);
+  EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_EINVAL);
   a = args();
 
   /* launching calls, each with one invalid argument: nothing is enqueued */
-  EXPECT(oscar_decode_workspace_bytes(&c, &a, &bytes), OSCAR_OK);
+  EXPECT(oscar_decode_plan(&c, &a, NULL, NULL, &bytes, NULL), OSCAR_OK);
   EXPECT(oscar_decode_attn(&c, &a, (const uint16_t *)dev(0x800000), (const float *)dev(0x900000),
                            dev(0xA00000), bytes - 1, NULL), OSCAR_EWORKSPACE);
   EXPECT(oscar_decode_attn(&c, &a, NULL, (const float *)dev(0x900000), dev(0xA00000), bytes, NULL),

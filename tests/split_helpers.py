@@ -30,6 +30,7 @@ class DeviceRun:
     hist_len: np.ndarray  # per sequence after the steps
     bf16_k: np.ndarray = None   # BF16 pools after the steps
     bf16_v: np.ndarray = None
+    status: int = 0             # the cache's sticky OSCAR_STATUS_* word
 
 
 def hist_capacity_pages(L: int, steps: int) -> int:
@@ -100,7 +101,8 @@ def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_sp
             ob.decode(sc.cache, args, q, Rk, Rv, out, lse)
     torch.cuda.synchronize()
     return DeviceRun(sc, out.cpu().numpy(), lse.cpu().numpy(), sc.cache.int2.cpu().numpy(),
-                     sc.hist_len_h.copy(), sc.cache.bf16_k.cpu().numpy(), sc.cache.bf16_v.cpu().numpy())
+                     sc.hist_len_h.copy(), sc.cache.bf16_k.cpu().numpy(), sc.cache.bf16_v.cpu().numpy(),
+                     sc.cache.read_status())
 
 
 def oracle_step(inp: synth.SmallInputs, steps: int = 1, R_v_none=False, head_map=None,

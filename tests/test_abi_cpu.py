@@ -67,8 +67,12 @@ def _args(**kw):
 
 
 def _ws(c, a):
+    """(status, workspace bytes) from oscar_decode_plan; oscar_decode_workspace_bytes
+    must agree (0 exactly when the status is not OK)."""
     out = ctypes.c_size_t(0)
-    st = ob.lib().oscar_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(a), ctypes.byref(out))
+    st = ob.lib().oscar_decode_plan(ctypes.byref(c), ctypes.byref(a), None, None, ctypes.byref(out), None)
+    n = ob.lib().oscar_decode_workspace_bytes(ctypes.byref(c), ctypes.byref(a))
+    assert n == (out.value if st == ob.OSCAR_OK else 0)
     return st, out.value
 
 
@@ -88,6 +92,7 @@ def test_workspace_bytes_valid():
     (dict(num_kv_heads=0), {}, ob.OSCAR_EINVAL),
     (dict(int2_pool=0x10001), {}, ob.OSCAR_EINVAL),
     (dict(bf16_v_pool=0), {}, ob.OSCAR_EINVAL),
+    (dict(status=0x10002), {}, ob.OSCAR_EINVAL),
     ({}, dict(batch=0), ob.OSCAR_EINVAL),
     ({}, dict(num_q_heads=30), ob.OSCAR_EINVAL),
     ({}, dict(num_q_heads=24), ob.OSCAR_EUNSUPPORTED),

@@ -4,10 +4,11 @@ Qwen3-32B-shaped shared-prefix batch), built and run in the configuration
 bench.py times (automatic kernel choice and chunking), one decode step.
 Checked against the oracle on sampled outputs:
 
-* every q head of the first and the last sequence (of every sequence in the
-  shared-prefix batch): outputs within 2e-3 row relative error, lse within
-  1e-3 (the oracle quantises the sequence's history from the same generated
-  tokens, in fp64, and attends it);
+* every q head of eight sequences spread over the batch of 32 (of the one
+  sequence of the 102400-token cache, of every sequence in the shared-prefix
+  batch): outputs within 2e-3 row relative error, lse within 1e-3 (the
+  oracle quantises the sequence's history from the same generated tokens, in
+  fp64, and attends it);
 * the bytes of 48 sampled history pages of those sequences (all KV heads)
   equal the oracle's encoded records, and so do the written token rows of the
   page that received the step's demoted token."""
@@ -153,12 +154,17 @@ def test_full_size_sampled(workload, codebook):
     st = bench.build_workload(workload, 1, log=_say, codebook=codebook)
     r = bench.run_steps(st, 0, 1, ob.INT2_AUTO, keep_first_out=True)
     plan = ob.decode_plan(st.sc.cache, r["args"][0])
+    assert st.sc.cache.read_status() == 0, f"cache status {st.sc.cache.read_status()}"
     _say(f"step done: chunks {plan[0]}, kernel {plan[3]}, {time.time() - t0:.1f}s")
     pool = st.sc.cache.int2.cpu().numpy()
     rng = np.random.default_rng(0)
-    # every sequence of the shared-prefix batch (its pages are quantised once),
-    # the first and the last of the others
-    seqs = list(range(st.wl.B)) if st.wl.shared_prefix else sorted({0, st.wl.B - 1})
+    # every sequence of the shared-prefix batch (its pages are quantised once);
+    # of the batch of 32, eight spread over the batch (the balanced schedule
+    # splits most sequences across two or three blocks, at different offsets)
+    if st.wl.shared_prefix:
+        seqs = list(range(st.wl.B))
+    else:
+        seqs = sorted({int(round(i * (st.wl.B - 1) / 7)) for i in range(8)})
     w = _check_sequences(st, r["first_out"], pool, seqs, rng, codebook=st.codebook_h)
     _say(f"sequences {seqs}: bytes of sampled and demoted-token pages exact, worst row rel err "
          f"{w:.3e} ({time.time() - t0:.1f}s)")

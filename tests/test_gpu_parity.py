@@ -224,17 +224,20 @@ def test_head_groups(Hkv, Hq, D, G):
 
 
 def test_bulk_quantise_order_and_splits():
-    """oscar_demote_pack on many tokens (the bulk kernel, 16 entries per block):
-    the pool bytes do not depend on the order of the entries or on how they
-    are split across calls (pages completed by several calls or blocks take
-    the AND/OR path for their V words), and equal the oracle's records."""
+    """oscar_demote_pack on many tokens: 4000 tokens of 8 KV heads in one call
+    run the 16-token-block kernel, the 7-way split the one-token kernel, the
+    2-way interleaved split the block kernel with pages completed by two
+    calls (their V words take the AND/OR path).  The pool bytes do not depend
+    on the order of the entries, on the split or on the kernel, and equal the
+    oracle's records."""
     import torch
     from int2_rotated_kv_amd import binding as ob
     from oracle import oscar_oracle as orc
     _say("case: bulk quantise order and splits")
-    wl = synth.workload("tiny", B=1, Hkv=2, Hq=8, D=128, G=64, lengths=(1000,), steps=1, seed=61)
+    wl = synth.workload("tiny", B=1, Hkv=8, Hq=32, D=128, G=64, lengths=(4000,), steps=1, seed=61,
+                        clip_set=synth.WIDE_CLIPS)
     inp = synth.make_small(wl)
-    n, npg = 1000, 63                              # 62 full pages and one of 8 tokens
+    n, npg = 3992, 250                             # 249 full pages and one of 8 tokens
     K, V = inp.K[0][:n], inp.V[0][:n]              # [n][Hkv][D] bf16 bits
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
     Rk, Rv = dev(inp.R_k), dev(inp.R_v)
@@ -267,7 +270,7 @@ def test_bulk_quantise_order_and_splits():
     for j in range(wl.Hkv):
         kc, ks, kz = orc.quantize_tokens(Kf[:, j], inp.R_k[j], wl.G, float(inp.clip_k[j]))
         vc, vs, vz = orc.quantize_tokens(Vf[:, j], inp.R_v[j], wl.G, float(inp.clip_v[j]))
-        for pg in (0, 31, 62):
+        for pg in (0, 31, 124, 249):
             a, e = pg * 16, min(n, pg * 16 + 16)
             pad = lambda x: np.concatenate([x[a:e], np.zeros((16 - (e - a),) + x.shape[1:], x.dtype)])
             want = orc.encode_record(pad(kc), pad(ks), pad(kz), pad(vc), pad(vs), pad(vz), wl.D, wl.G)
@@ -307,19 +310,23 @@ def test_deterministic_option(shape):
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
-@pytest.mark.parametrize("shape", ["tiny", "d128g64", "d128g128", "d128g32", "d64g64g8", "d128g64sym"])
+@pytest.mark.parametrize("shape", ["tiny", "d128g64", "d128g128", "d128g32", "d64g64g8", "d128g64sym",
+                                   "d128g64mixed"])
 def test_codebook_variant(shape, kernel):
     """Lloyd-Max codebook variant: the prompt history quantised in bulk, then
     two decode steps (one-token demotion, attention on either INT2 kernel; the
     matrix-core one with the deterministic option), through the separate
     calls and through oscar_decode_step.  INT2 page bytes bit-exact against
     the oracle's nearest-level quantiser, outputs within the oracle bar, and
-    the fused step bitwise equal to the separate calls."""
+    the fused step bitwise equal to the separate calls.  "mixed": KV head 0
+    has symmetric levels (the matrix-core kernel skips its third code plane),
+    head 1 fitted ones, under the default dynamic schedule (fused and
+    separate calls then agree within 5e-4, not bitwise)."""
     from int2_rotated_kv_amd import binding as ob
     _say("case: codebook variant", shape, "kernel", kernel)
     if shape == "tiny":
         wl = synth.workload("tiny", B=2, lengths=(1024, 777), steps=2, seed=81)
-    elif shape in ("d128g64", "d128g64sym"):
+    elif shape in ("d128g64", "d128g64sym", "d128g64mixed"):
         wl = synth.workload("tiny", B=2, Hkv=2, Hq=8, D=128, G=64, lengths=(3000, 1700), steps=2, seed=82)
     elif shape == "d128g128":
         wl = synth.workload("tiny", B=2, Hkv=2, Hq=16, D=128, G=128, lengths=(2500, 999), steps=2, seed=83)
@@ -333,14 +340,24 @@ def test_codebook_variant(shape, kernel):
     cb = synth.make_codebook(wl.seed, wl.Hkv, symmetric=shape.endswith("sym"))
     if shape.endswith("sym"):
         assert np.all(((cb[..., 3] - cb[..., 2]) - cb[..., 1]) + cb[..., 0] == 0)
-    kw = dict(steps=2, int2_kernel=kernel, codebook=cb, flags=ob.FLAG_DETERMINISTIC)
+    mixed = shape.endswith("mixed")
+    if mixed:
+        cb[0] = synth.make_codebook(wl.seed, wl.Hkv, symmetric=True)[0]
+        cterm = ((cb[..., 3] - cb[..., 2]) - cb[..., 1]) + cb[..., 0]
+        assert np.all(cterm[0] == 0) and np.all(cterm[1] != 0)
+    kw = dict(steps=2, int2_kernel=kernel, codebook=cb, flags=0 if mixed else ob.FLAG_DETERMINISTIC)
     sep = sh.build_and_step(inp, **kw)
     fus = sh.build_and_step(inp, fused=True, **kw)
     ref = sh.oracle_step(inp, steps=2, codebook=cb)
     _check_bytes(sep, inp, ref)
     _check_bytes(fus, inp, ref)
     w = _check_out(sep, ref)
-    assert np.array_equal(sep.out.view(np.uint32), fus.out.view(np.uint32)), "fused outputs differ"
+    _check_out(fus, ref)
+    if mixed and kernel == 2:
+        e = sh.row_rel_err(fus.out.astype(np.float64), sep.out.astype(np.float64))
+        assert e.max() < 5e-4 and np.abs(fus.lse - sep.lse).max() < 1e-4
+    else:
+        assert np.array_equal(sep.out.view(np.uint32), fus.out.view(np.uint32)), "fused outputs differ"
     # the uniform quantiser would give other bytes: the codebook is really used
     uni = sh.oracle_step(inp, steps=2)
     assert not np.array_equal(sh.oracle_records(uni[0], wl.D, wl.G, wl.Hkv),
@@ -442,16 +459,18 @@ def _random_case(seed):
     kernel = int(rng.choice([0, 1, 2]))
     codebook = bool(rng.integers(0, 2))
     det = bool(rng.integers(0, 2))
-    return dict(D=D, G=G, Hkv=Hkv, Hq=g * Hkv, B=B, lengths=lengths, steps=steps, seed=2000 + seed), \
-        kernel, codebook, det
+    clips = synth.WIDE_CLIPS if rng.integers(0, 2) else ()
+    return dict(D=D, G=G, Hkv=Hkv, Hq=g * Hkv, B=B, lengths=lengths, steps=steps, seed=2000 + seed,
+                clip_set=clips), kernel, codebook, det
 
 
 @pytest.mark.parametrize("seed", range(12))
 def test_random_configurations(seed):
     """Seeded random configurations (head_dim, group, KV heads, q heads per KV
     head, batch, lengths from 1 to 3000 tokens, 1-2 steps, kernel choice,
-    codebook or not, deterministic option or not) against the oracle: page
-    bytes exact, outputs within the bar."""
+    codebook or not, deterministic option or not, one clip ratio or per-head
+    K != V ratios) against the oracle: page bytes exact, outputs within the
+    bar, no status bit."""
     from int2_rotated_kv_amd import binding as ob
     kw, kernel, codebook, det = _random_case(seed)
     _say(f"case: random configuration {seed}: {kw}, kernel {kernel}, codebook {codebook}, det {det}")
@@ -463,4 +482,5 @@ def test_random_configurations(seed):
     ref = sh.oracle_step(inp, steps=wl.steps, codebook=cb)
     _check_bytes(run, inp, ref)
     w = _check_out(run, ref)
+    assert run.status == 0, f"status {run.status}"
     _say(f"random {seed}: bytes exact, worst row rel err {w:.3e}")
