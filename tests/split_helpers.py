@@ -40,11 +40,12 @@ def hist_capacity_pages(L: int, steps: int) -> int:
 
 def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_splits=0,
                    R_v_none=False, head_map=None, device="cuda", seed_perm=None, fused=False,
-                   flags=0, codebook=None, max_hist_len=None, extra_pages=0):
+                   flags=0, codebook=None, max_hist_len=None, extra_pages=0, noalloc=False):
     """Build the initial split cache of every sequence, run `steps` decode steps
     (demote oldest recent -> write new token -> attend -> merge; with fused,
-    through the single oscar_decode_step call), return the outputs of the last
-    step and the INT2 pool."""
+    through the single oscar_decode_step call, with noalloc through
+    oscar_decode_step_noalloc), return the outputs of the last step and the
+    INT2 pool."""
     import torch
     from int2_rotated_kv_amd import binding as ob
     from int2_rotated_kv_amd.splitcache import SplitCache
@@ -87,6 +88,13 @@ def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_sp
         kn, vn = to_dev_bf16(newk).view(torch.int16), to_dev_bf16(newv).view(torch.int16)
         d_src, d_dst, d_w = (torch.from_numpy(x).to(device) for x in (dsrc, ddst, wdst))
         q = to_dev_bf16(inp.q[st]).view(torch.int16)
+        if noalloc:
+            sc.commit_step()
+            sc.sync_lengths()
+            args = sc.decode_args(max_hist_len=max_hist_len, kv_head_of_q=head_map, num_splits=num_splits,
+                                  int2_kernel=int2_kernel, flags=flags)
+            ob.decode_step_noalloc(sc.cache, args, d_src, d_dst, ck, cv, d_w, kn, vn, q, Rk, Rv, out, lse)
+            continue
         if not fused:
             ob.demote_pack(sc.cache, d_src, d_dst, Rk, Rv, ck, cv)
             ob.write_bf16(sc.cache, d_w, kn, vn)
