@@ -30,8 +30,9 @@
  *     A failed kernel launch returns OSCAR_EHIP.  Device-side faults surface at
  *     the caller's next synchronisation (HIP semantics).
  *   - Calls are re-entrant; the only library state is a thread-local error
- *     string.  Calls that write the same cache records from several streams
- *     concurrently race.
+ *     string and, for oscar_decode_step_noalloc, its per-device workspace
+ *     array and that array's device addresses.  Calls that write the same
+ *     cache records from several streams concurrently race.
  *
  * Cache layout (HBM)
  *   INT2 history pool: uint8 [num_int2_pages][Hkv][oscar_record_bytes(D, G)].
@@ -336,6 +337,36 @@ int oscar_decode_step(const oscar_cache *cache, const oscar_decode_args *args,
                       const uint16_t *v_new, const uint16_t *q, const float *R_k, const float *R_v,
                       void *workspace, size_t workspace_bytes, float *out, float *lse,
                       void *stream);
+
+/* Bytes of the device workspace that oscar_decode_step_noalloc uses: one
+ * copy per device, part of the library's device code, held until the process
+ * ends (16 MiB: enough for a Qwen3-8B-shaped batch of 64 sequences at 100K
+ * context, or a Qwen3-32B-shaped batch of 16 at 128K). */
+#define OSCAR_NOALLOC_WORKSPACE_BYTES (16u << 20)
+
+/*
+ * oscar_decode_step_noalloc - oscar_decode_step with no workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc): the step's
+ * workspace is the library's own static device array.  It calls no
+ * hipMalloc, hipFree or allocating library routine.  Arguments, results and
+ * errors are those of oscar_decode_step, plus:
+ *   - OSCAR_EWORKSPACE when oscar_decode_workspace_bytes(cache, args) exceeds
+ *     OSCAR_NOALLOC_WORKSPACE_BYTES (nothing is launched);
+ *   - the work is enqueued for the current device, which must be the stream's
+ *     (EINVAL otherwise); the first call on a device looks up that device's
+ *     copy of the array (hipGetSymbolAddress), so make it outside a capture.
+ * Every call on a device shares that device's array, which keeps the last
+ * call's contents (nothing in it needs clearing: each step writes what it
+ * reads).  Calls that overlap on one device - on two streams, or from two
+ * threads without ordering - race on it.
+ */
+int oscar_decode_step_noalloc(const oscar_cache *cache, const oscar_decode_args *args,
+                              const int32_t *demote_src, const int32_t *demote_dst,
+                              const float *clip_k, const float *clip_v, const int32_t *new_slot,
+                              const uint16_t *k_new, const uint16_t *v_new, const uint16_t *q,
+                              const float *R_k, const float *R_v, float *out, float *lse,
+                              void *stream);
 
 #ifdef __cplusplus
 }

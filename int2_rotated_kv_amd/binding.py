@@ -23,6 +23,7 @@ OSCAR_EHIP = -4
 INT2_AUTO, INT2_VALU, INT2_MFMA, HISTORY_BF16 = 0, 1, 2, 3
 PHASE_QROT, PHASE_BF16, PHASE_INT2, PHASE_ALL = 1, 2, 4, 7
 FLAG_DETERMINISTIC = 1
+NOALLOC_WORKSPACE_BYTES = 16 << 20
 STATUS_CLIP_RANGE, STATUS_MFMA_V_RANGE, STATUS_NONFINITE = 1, 2, 4
 MFMA_V_SCALE_LIMIT = 1023.0
 PAGE = 16
@@ -102,6 +103,13 @@ _SIGS = {
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "oscar_decode_step_noalloc": (ctypes.c_int, [ctypes.POINTER(OscarCache),
+                                                 ctypes.POINTER(OscarDecodeArgs),
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p]),
 }
 
 
@@ -292,6 +300,17 @@ def decode_step(cache: Cache, args: DecodeArgs, demote_src, demote_dst, clip_k, 
                                   _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(R_k), _ptr(R_v),
                                   _ptr(workspace), int(workspace.numel()), _ptr(out), _ptr(lse),
                                   _stream(stream)))
+
+
+def decode_step_noalloc(cache: Cache, args: DecodeArgs, demote_src, demote_dst, clip_k, clip_v,
+                        new_slot, k_new, v_new, q, R_k, R_v, out, lse=None, stream=None):
+    """oscar_decode_step_noalloc: decode_step with the library's static device
+    workspace (no workspace argument; nothing is allocated)."""
+    d = cache.desc()
+    check(lib().oscar_decode_step_noalloc(ctypes.byref(d), ctypes.byref(args.c), _ptr(demote_src),
+                                          _ptr(demote_dst), _ptr(clip_k), _ptr(clip_v), _ptr(new_slot),
+                                          _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(R_k), _ptr(R_v),
+                                          _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def decode(cache: Cache, args: DecodeArgs, q, R_k, R_v, out, lse=None, workspace=None, stream=None):

@@ -6,14 +6,24 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "common.hpp"
+
+// Workspace of oscar_decode_step_noalloc: one copy per device, held until
+// the process ends.  In host code this name is only a stand-in for the
+// symbol; its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) uint8_t scratch[OSCAR_NOALLOC_WORKSPACE_BYTES];
 
 namespace oscar {
 namespace {
 
 thread_local std::string g_err;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t *g_scratch_dev[kMaxDevices];   // device address of `scratch` on each device
 
 int fail(int code, const char *fmt, ...) {
   char buf[512];
@@ -331,13 +341,17 @@ int oscar_merge(const oscar_cache *cache, const oscar_decode_args *args, const v
   return OSCAR_OK;
 }
 
-int oscar_decode_step(const oscar_cache *cache, const oscar_decode_args *args,
-                      const int32_t *demote_src, const int32_t *demote_dst, const float *clip_k,
-                      const float *clip_v, const int32_t *new_slot, const uint16_t *k_new,
-                      const uint16_t *v_new, const uint16_t *q, const float *R_k, const float *R_v,
-                      void *workspace, size_t workspace_bytes, float *out, float *lse,
-                      void *stream) {
-  DecodeParams p{};
+}  // extern "C"
+
+namespace oscar {
+namespace {
+
+// Host checks of a decode step's arguments other than the workspace.
+int check_step(const oscar_cache *cache, const oscar_decode_args *args, DecodeParams &p,
+               const int32_t *demote_src, const int32_t *demote_dst, const float *clip_k,
+               const float *clip_v, const int32_t *new_slot, const uint16_t *k_new,
+               const uint16_t *v_new, const uint16_t *q, const float *R_k, const float *R_v,
+               float *out) {
   int st = check_args(cache, args, &p);
   if (st) return st;
   if (args->phases != 0 && args->phases != (uint32_t)OSCAR_PHASE_ALL)
@@ -353,13 +367,15 @@ int oscar_decode_step(const oscar_cache *cache, const oscar_decode_args *args,
   if (R_v && !aligned(R_v, 16)) return fail(OSCAR_EINVAL, "R_v is not 16-byte aligned");
   if (!out) return fail(OSCAR_EINVAL, "out is NULL");
   if (cache->num_bf16_pages <= 0) return fail(OSCAR_EINVAL, "cache has no BF16 pages");
-  if (!workspace || !aligned(workspace, 256))
-    return fail(OSCAR_EINVAL, "workspace is NULL or not 256-byte aligned");
-  if (workspace_bytes < p.L.total)
-    return fail(OSCAR_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
-                p.L.total);
-  p.ws = static_cast<uint8_t *>(workspace);
-  hipStream_t s = (hipStream_t)stream;
+  return OSCAR_OK;
+}
+
+// The three launches of a decode step (arguments checked, p.ws set).
+int launch_step(DecodeParams &p, const oscar_cache *cache, const oscar_decode_args *args,
+                const int32_t *demote_src, const int32_t *demote_dst, const float *clip_k,
+                const float *clip_v, const int32_t *new_slot, const uint16_t *k_new,
+                const uint16_t *v_new, const uint16_t *q, const float *R_k, const float *R_v,
+                float *out, float *lse, hipStream_t s) {
   hipError_t e = launch_step_pre(p, *cache, q, R_k, R_v, clip_k, clip_v, demote_src, demote_dst,
                                  new_slot, k_new, v_new, s);
   if (e != hipSuccess) return hip_fail(e, "decode-step prologue launch");
@@ -372,6 +388,79 @@ int oscar_decode_step(const oscar_cache *cache, const oscar_decode_args *args,
   e = launch_merge(p, R_v, out, lse, s);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return OSCAR_OK;
+}
+
+// Device address of `scratch` on the device the work is enqueued on (the
+// current device, which must be the stream's).  Looked up once per device,
+// with that device current.
+int scratch_address(hipStream_t s, uint8_t **out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (s != nullptr) {
+    hipDevice_t sd = -1;
+    e = hipStreamGetDevice(s, &sd);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    if (sd != cur)
+      return fail(OSCAR_EINVAL, "stream belongs to device %d but device %d is current", (int)sd, cur);
+  }
+  if (cur < 0 || cur >= kMaxDevices) return fail(OSCAR_EUNSUPPORTED, "device %d out of range", cur);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_dev[cur] == nullptr) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_dev[cur] = static_cast<uint8_t *>(ptr);
+  }
+  *out = g_scratch_dev[cur];
+  return OSCAR_OK;
+}
+
+}  // namespace
+}  // namespace oscar
+
+extern "C" {
+
+int oscar_decode_step(const oscar_cache *cache, const oscar_decode_args *args,
+                      const int32_t *demote_src, const int32_t *demote_dst, const float *clip_k,
+                      const float *clip_v, const int32_t *new_slot, const uint16_t *k_new,
+                      const uint16_t *v_new, const uint16_t *q, const float *R_k, const float *R_v,
+                      void *workspace, size_t workspace_bytes, float *out, float *lse,
+                      void *stream) {
+  DecodeParams p{};
+  int st = check_step(cache, args, p, demote_src, demote_dst, clip_k, clip_v, new_slot, k_new,
+                      v_new, q, R_k, R_v, out);
+  if (st) return st;
+  if (!workspace || !aligned(workspace, 256))
+    return fail(OSCAR_EINVAL, "workspace is NULL or not 256-byte aligned");
+  if (workspace_bytes < p.L.total)
+    return fail(OSCAR_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
+                p.L.total);
+  p.ws = static_cast<uint8_t *>(workspace);
+  return launch_step(p, cache, args, demote_src, demote_dst, clip_k, clip_v, new_slot, k_new,
+                     v_new, q, R_k, R_v, out, lse, (hipStream_t)stream);
+}
+
+int oscar_decode_step_noalloc(const oscar_cache *cache, const oscar_decode_args *args,
+                              const int32_t *demote_src, const int32_t *demote_dst,
+                              const float *clip_k, const float *clip_v, const int32_t *new_slot,
+                              const uint16_t *k_new, const uint16_t *v_new, const uint16_t *q,
+                              const float *R_k, const float *R_v, float *out, float *lse,
+                              void *stream) {
+  DecodeParams p{};
+  int st = check_step(cache, args, p, demote_src, demote_dst, clip_k, clip_v, new_slot, k_new,
+                      v_new, q, R_k, R_v, out);
+  if (st) return st;
+  if (p.L.total > (size_t)OSCAR_NOALLOC_WORKSPACE_BYTES)
+    return fail(OSCAR_EWORKSPACE, "workspace of %zu bytes exceeds the %zu-byte static workspace",
+                p.L.total, (size_t)OSCAR_NOALLOC_WORKSPACE_BYTES);
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *ws = nullptr;
+  st = scratch_address(s, &ws);
+  if (st) return st;
+  p.ws = ws;
+  return launch_step(p, cache, args, demote_src, demote_dst, clip_k, clip_v, new_slot, k_new,
+                     v_new, q, R_k, R_v, out, lse, s);
 }
 
 }  // extern "C"

@@ -142,6 +142,29 @@ int main(void) {
                            dev(0xA00000), bytes, NULL, NULL, NULL), OSCAR_EINVAL);
   a = args();
 
+  /* the allocation-free step: argument errors, and a workspace larger than
+     its static array, are rejected before any HIP call */
+  {
+    const int32_t *sl = (const int32_t *)dev(0x800000);
+    const float *fp = (const float *)dev(0x900000);
+    const uint16_t *tk = (const uint16_t *)dev(0xC00000);
+    EXPECT(oscar_decode_step_noalloc(&c, &a, sl, sl, fp, fp, sl, tk, tk, tk, fp, fp, NULL, NULL, NULL),
+           OSCAR_EINVAL);                                         /* out is NULL */
+    EXPECT(oscar_decode_step_noalloc(&c, &a, NULL, sl, fp, fp, sl, tk, tk, tk, fp, fp,
+                                     (float *)dev(0xB00000), NULL, NULL), OSCAR_EINVAL);
+    oscar_decode_args big = args();
+    big.batch = 256;                                          /* 256 x 100K: > 16 MiB */
+    big.hist_stride = 6400;
+    big.max_hist_len = 6400 * 16;
+    EXPECT(oscar_decode_plan(&c, &big, NULL, NULL, &bytes, NULL), OSCAR_OK);
+    if (bytes <= OSCAR_NOALLOC_WORKSPACE_BYTES) {
+      fprintf(stderr, "expected a workspace above the static one, got %zu\n", bytes);
+      ++failures;
+    }
+    EXPECT(oscar_decode_step_noalloc(&c, &big, sl, sl, fp, fp, sl, tk, tk, tk, fp, fp,
+                                     (float *)dev(0xB00000), NULL, NULL), OSCAR_EWORKSPACE);
+  }
+
   if (failures) {
     fprintf(stderr, "%d check(s) failed\n", failures);
     return 1;

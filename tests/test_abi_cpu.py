@@ -277,3 +277,23 @@ def test_codebook_cache_kernel_choice():
     assert st == ob.OSCAR_OK and k == ob.INT2_VALU
     st, *_, k = _plan(_cache(codebook=0x80000), _args(num_q_heads=16))
     assert st == ob.OSCAR_OK and k == ob.INT2_MFMA
+
+
+def test_noalloc_step_rejects_before_launch():
+    """oscar_decode_step_noalloc checks its arguments like oscar_decode_step and
+    rejects a call whose workspace exceeds its static array, before any HIP
+    call (so no GPU is needed here)."""
+    lib = ob.lib()
+    c = _cache()
+    ptrs = [0x1000, 0x1100, 0x1200, 0x1300, 0x1400, 0x1500, 0x1600, 0x1700, 0x1800, 0x1900]
+    big = _args(batch=256, hist_stride=6400, max_hist_len=6400 * 16)
+    st, n = _ws(c, big)
+    assert st == ob.OSCAR_OK and n > ob.NOALLOC_WORKSPACE_BYTES
+    st = lib.oscar_decode_step_noalloc(ctypes.byref(c), ctypes.byref(big), *ptrs, 0x2100, None, None)
+    assert st == ob.OSCAR_EWORKSPACE and "static workspace" in ob.last_error()
+    a = _args()
+    st = lib.oscar_decode_step_noalloc(ctypes.byref(c), ctypes.byref(a), *ptrs, None, None, None)
+    assert st == ob.OSCAR_EINVAL and "out" in ob.last_error()
+    st = lib.oscar_decode_step_noalloc(ctypes.byref(c), ctypes.byref(_args(int2_kernel=ob.HISTORY_BF16)),
+                                       *ptrs, 0x2100, None, None)
+    assert st == ob.OSCAR_EUNSUPPORTED
