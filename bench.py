@@ -122,6 +122,9 @@ def build_workload(name: str, total_steps: int, device="cuda", log=print, bf16_h
     sc.hist_len_h[:], sc.bf16_len_h[:], sc.ring_head[:] = h0, b0, r0
     st = BenchState()
     st.wl, st.gen, st.sc = wl, gen, sc
+    # pages the page tables alias (a shared prompt prefix), as the caller's
+    # prefix cache would report them
+    st.shared = gen.shared_segments()
     st.codebook_h = cb
     st.Rk, st.Rv, st.ck, st.cv = Rk, Rv, ck, cv
     dev = lambda x: torch.from_numpy(x).to(device)
@@ -147,7 +150,8 @@ def build_workload(name: str, total_steps: int, device="cuda", log=print, bf16_h
 def step_args(st, s: int, int2_kernel: int, num_splits: int = 0):
     from int2_rotated_kv_amd import binding as ob
     return ob.DecodeArgs(st.wl.B, st.wl.Hq, st.sc.hist_pages, st.hl[s], st.sc.bf16_pages, st.bl[s],
-                         int(st.hl_h[s].max()), int2_kernel=int2_kernel, num_splits=num_splits)
+                         int(st.hl_h[s].max()), int2_kernel=int2_kernel, num_splits=num_splits,
+                         shared=st.shared)
 
 
 def breakdown_steps(steps):
@@ -653,6 +657,9 @@ def main(argv=None):
                     help="use the Lloyd-Max codebook variant of the INT2 history (seeded levels; "
                          "'symmetric': levels symmetric about the middle of the range, whose "
                          "third code plane the matrix-core kernel skips)")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="do not pass the shared-prefix pages to the library (every sequence then "
+                         "reads its aliased pages on its own)")
     ap.add_argument("--no-batch1", action="store_true",
                     help="skip the 102400-token batch-1 leg that the default run adds")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -681,6 +688,8 @@ def main(argv=None):
     st = build_workload(a.workload, a.steps + a.warmup + breakdown_steps(a.steps) + 2 * cold_steps,
                         log=log, bf16_history=not a.no_bf16_compare, codebook=a.codebook)
     wl = st.wl
+    if a.no_shared:
+        st.shared = []
     r = run_steps(st, a.steps, a.warmup, kern, keep_first_out=not a.no_cpu_baseline,
                   num_splits=a.splits, cold_steps=cold_steps, prewarm_s=0.3)
     log(f"[bench] timed {a.steps} steps in {r['wall_s']:.3f}s")
@@ -716,6 +725,7 @@ def main(argv=None):
                    "sink": SINK, "recent": RECENT, "page": PAGE, "int2_kernel": kname,
                    "splits": splits,
                    "codebook": {"fit": "lloyd-max", "symmetric": "lloyd-max-symmetric"}.get(a.codebook, "uniform"),
+                   "shared_pages": [list(x) for x in st.shared],
                    "parallelism": "single-gpu"},
         "hbm_tbps": step_bytes / (ms_step * 1e-3) / 1e12,
         "hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,

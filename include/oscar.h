@@ -74,7 +74,8 @@ enum {
   OSCAR_SINK_TOKENS = 64,
   OSCAR_RECENT_TOKENS = 256,
   OSCAR_MAX_BF16_TOKENS = 320,   /* sink + recent                              */
-  OSCAR_MAX_Q_HEADS = 256
+  OSCAR_MAX_Q_HEADS = 256,
+  OSCAR_MAX_SHARED = 16          /* shared page segments per call              */
 };
 
 /* Parts of oscar_decode_attn (bit mask). */
@@ -174,6 +175,28 @@ typedef struct {
                                 reported                                     */
 } oscar_cache;
 
+/* History pages that several sequences share (a common prompt prefix held
+ * once in a paged, prefix-aware cache: thmotor, split-cache paragraph - the
+ * method works with paged KV and radix prefix caching; Fig. 6 - throughput
+ * grows with the prefix-cache hit ratio).  Sequences seq_begin ..
+ * seq_begin + num_seqs - 1 list the same physical INT2 pages at logical
+ * history pages first_page .. first_page + num_pages - 1 (the pages are read
+ * from sequence seq_begin's table), and each of those pages holds 16 tokens
+ * for every one of them.  With the matrix-core INT2 kernel (AUTO or MFMA) and
+ * one group per token (G == D), the pages are attended once for all the
+ * sequences' q heads
+ * (up to num_seqs x Hq/Hkv query rows per KV head) and the result is merged
+ * with each sequence's own pages; otherwise every sequence reads them as its
+ * own.  The segments of one sequence must tile its first history pages:
+ * ordered by first_page, the first starts at page 0 and each next one where
+ * the previous ends. */
+typedef struct {
+  int32_t first_page;
+  int32_t num_pages;         /* >= 1                                            */
+  int32_t seq_begin;
+  int32_t num_seqs;          /* >= 2                                            */
+} oscar_shared_pages;
+
 typedef struct {
   int32_t batch;             /* B >= 1                                          */
   int32_t num_q_heads;       /* Hq, a multiple of Hkv, <= OSCAR_MAX_Q_HEADS     */
@@ -202,6 +225,8 @@ typedef struct {
                                 INT2 phase reads the rotated query that the QROT
                                 phase writes into the workspace                 */
   uint32_t flags;            /* OR of OSCAR_FLAG_*; 0 = defaults                  */
+  int32_t num_shared;        /* [host] entries of `shared`, 0..OSCAR_MAX_SHARED  */
+  const oscar_shared_pages *shared;  /* [host] shared history pages, or NULL    */
 } oscar_decode_args;
 
 /* Bytes of one INT2 page record: 2*16*(D/4) + 2*16*(D/G)*4. */

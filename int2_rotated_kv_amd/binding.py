@@ -49,6 +49,15 @@ class OscarCache(ctypes.Structure):
     ]
 
 
+class OscarSharedPages(ctypes.Structure):
+    _fields_ = [
+        ("first_page", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("seq_begin", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+    ]
+
+
 class OscarDecodeArgs(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32),
@@ -66,6 +75,8 @@ class OscarDecodeArgs(ctypes.Structure):
         ("int2_kernel", ctypes.c_int32),
         ("phases", ctypes.c_uint32),
         ("flags", ctypes.c_uint32),
+        ("num_shared", ctypes.c_int32),
+        ("shared", ctypes.c_void_p),
     ]
 
 
@@ -225,19 +236,26 @@ class DecodeArgs:
 
     def __init__(self, batch, num_q_heads, hist_pages, hist_len, bf16_pages, bf16_len,
                  max_hist_len, kv_head_of_q=None, sm_scale=0.0, num_splits=0, int2_kernel=INT2_AUTO,
-                 phases=0, flags=0):
+                 phases=0, flags=0, shared=None):
+        """shared: [(first_page, num_pages, seq_begin, num_seqs), ...] history
+        pages that those sequences' page tables share (oscar_shared_pages)."""
         self.hist_pages, self.hist_len = hist_pages, hist_len
         self.bf16_pages, self.bf16_len = bf16_pages, bf16_len
         self._map = None
         if kv_head_of_q is not None:
             self._map = (ctypes.c_int32 * len(kv_head_of_q))(*[int(x) for x in kv_head_of_q])
+        self._shared = None
+        if shared:
+            self._shared = (OscarSharedPages * len(shared))(
+                *[OscarSharedPages(*[int(v) for v in e]) for e in shared])
         self.c = OscarDecodeArgs(
             batch, num_q_heads, ctypes.cast(self._map, ctypes.c_void_p) if self._map else None,
             _ptr(hist_pages) if hist_pages is not None and hist_pages.numel() else None,
             int(hist_pages.shape[1]) if hist_pages is not None and hist_pages.dim() == 2 else 0,
             _ptr(hist_len), _ptr(bf16_pages), int(bf16_pages.shape[1]), _ptr(bf16_len),
             int(max_hist_len), float(sm_scale), int(num_splits), int(int2_kernel), int(phases),
-            int(flags))
+            int(flags), len(shared) if shared else 0,
+            ctypes.cast(self._shared, ctypes.c_void_p) if self._shared is not None else None)
 
     def with_phases(self, phases: int) -> "DecodeArgs":
         """A copy of these arguments restricted to some oscar_decode_attn phases."""

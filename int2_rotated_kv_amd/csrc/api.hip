@@ -154,6 +154,82 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   if (kind == OSCAR_INT2_AUTO) kind = OSCAR_INT2_MFMA;
   p->int2_kind = kind;
 
+  // shared history pages: validated whatever kernel runs; attended once for
+  // all their sequences (cascade) with the matrix-core kernel when a token's
+  // channels form one group (G == D)
+  if (a->num_shared < 0 || a->num_shared > OSCAR_MAX_SHARED)
+    return fail(OSCAR_EINVAL, "num_shared must be in [0, %d] (got %d)", OSCAR_MAX_SHARED,
+                a->num_shared);
+  if (a->num_shared > 0 && a->shared == nullptr) return fail(OSCAR_EINVAL, "shared is NULL");
+  for (int i = 0; i < a->num_shared; ++i) {
+    const oscar_shared_pages &e = a->shared[i];
+    if (e.first_page < 0 || e.num_pages < 1 || e.num_seqs < 2 || e.seq_begin < 0 ||
+        (long long)e.seq_begin + e.num_seqs > a->batch)
+      return fail(OSCAR_EINVAL, "shared[%d]: pages [%d, +%d) of sequences [%d, +%d) out of range",
+                  i, e.first_page, e.num_pages, e.seq_begin, e.num_seqs);
+    if ((long long)(e.first_page + (long long)e.num_pages) * OSCAR_PAGE_TOKENS > a->max_hist_len)
+      return fail(OSCAR_EINVAL, "shared[%d] ends beyond max_hist_len", i);
+  }
+  if (a->num_shared > 0) {
+    // the segments of every sequence tile its first pages, in page order
+    for (int b = 0; b < a->batch; ++b) {
+      int next = 0, left = 0;
+      for (int i = 0; i < a->num_shared; ++i)
+        left += (b >= a->shared[i].seq_begin && b < a->shared[i].seq_begin + a->shared[i].num_seqs);
+      while (left > 0) {
+        int found = -1;
+        for (int i = 0; i < a->num_shared; ++i) {
+          const oscar_shared_pages &e = a->shared[i];
+          if (b >= e.seq_begin && b < e.seq_begin + e.num_seqs && e.first_page == next) {
+            if (found >= 0) return fail(OSCAR_EINVAL, "sequence %d: two shared segments at page %d", b, next);
+            found = i;
+          }
+        }
+        if (found < 0)
+          return fail(OSCAR_EINVAL, "sequence %d: its shared segments do not tile pages from 0 (gap at %d)",
+                      b, next);
+        next += a->shared[found].num_pages;
+        --left;
+      }
+    }
+  }
+  p->n_shared = 0;
+  p->cas_slots = 0;
+  p->cas_blocks = 0;
+  if (a->num_shared > 0 && kind == OSCAR_INT2_MFMA && c->group_size == c->head_dim) {
+    // page ranges of about equal size so that the grid holds ~2 blocks per
+    // compute unit, each at least kCasMinPages pages (its partials, written
+    // and read back, stay well below the pages' bytes)
+    constexpr int kCasMinPages = 32, kCasTargetBlocks = 512;
+    long long work = 0;
+    const int g = p->g;
+    for (int i = 0; i < a->num_shared; ++i) {
+      const int rg = (a->shared[i].num_seqs * g + kCasRowsPerBlock - 1) / kCasRowsPerBlock;
+      work += (long long)a->shared[i].num_pages * rg * c->num_kv_heads;
+    }
+    long long pc = (work + kCasTargetBlocks - 1) / kCasTargetBlocks;
+    pc = pc < kCasMinPages ? kCasMinPages : pc;
+    int base = 0;
+    for (int i = 0; i < a->num_shared; ++i) {
+      const oscar_shared_pages &e = a->shared[i];
+      SharedSeg &sg = p->shared[i];
+      sg.first = e.first_page;
+      sg.num = e.num_pages;
+      sg.seq0 = e.seq_begin;
+      sg.nseq = e.num_seqs;
+      sg.parts = (int)((e.num_pages + pc - 1) / pc);
+      sg.rgroups = (e.num_seqs * g + kCasRowsPerBlock - 1) / kCasRowsPerBlock;
+      sg.block_base = base;
+      base += sg.parts * c->num_kv_heads * sg.rgroups;
+    }
+    p->n_shared = a->num_shared;
+    p->cas_blocks = base;
+    for (int b = 0; b < a->batch; ++b) {
+      const int n = cascade_slots(*p, b, nullptr);
+      p->cas_slots = n > p->cas_slots ? n : p->cas_slots;
+    }
+  }
+
   // history split.  Vector-ALU kernel: enough waves to fill the chip once (4
   // waves per (sequence, KV head, chunk)), each chunk streaming at least 8x
   // the bytes of its partial result (read and written once more by the merge)
@@ -198,6 +274,7 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
                        (long long)a->batch * npages < (1LL << 31);
     S = 2 * S + 2;
   }
+  S += p->cas_slots;                 // the cascade's slots come first in each row
   p->splits = S;
 
   WsLayout &L = p->L;
@@ -209,6 +286,7 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   off = align256(off + (mf ? (size_t)a->batch * c->num_kv_heads * ((p->g + 3) / 4) *
                                  mfma_qk_steps(p->D, p->G) * 64 * 4 * 4 : 0));
   L.qhd = off; off = align256(off + (mf ? BH * 8 * 4 : 0));
+  L.qcas = off; off = align256(off + (p->n_shared > 0 ? BH * 3 * p->D : 0));
   L.nslots = off; off = align256(off + (mf ? (size_t)a->batch * 4 : 0));
   L.part_o = off; off = align256(off + BH * S * p->D * 4);
   L.part_ml = off; off = align256(off + BH * S * 2 * 4);
@@ -314,6 +392,10 @@ int oscar_decode_attn(const oscar_cache *cache, const oscar_decode_args *args, c
     if (e != hipSuccess) return hip_fail(e, "BF16 segment launch");
   }
   if ((ph & OSCAR_PHASE_INT2) && args->max_hist_len > 0) {
+    if (p.n_shared > 0) {
+      e = launch_int2_cascade(p, s);
+      if (e != hipSuccess) return hip_fail(e, "shared history pages launch");
+    }
     e = bf16_hist ? launch_bf16_hist(p, q, s)
         : p.int2_kind == OSCAR_INT2_MFMA ? launch_int2_mfma(p, s) : launch_int2_valu(p, s);
     if (e != hipSuccess) return hip_fail(e, "history segment launch");
@@ -380,6 +462,10 @@ int launch_step(DecodeParams &p, const oscar_cache *cache, const oscar_decode_ar
                                  new_slot, k_new, v_new, s);
   if (e != hipSuccess) return hip_fail(e, "decode-step prologue launch");
   if (args->max_hist_len > 0) {
+    if (p.n_shared > 0) {
+      e = launch_int2_cascade(p, s);
+      if (e != hipSuccess) return hip_fail(e, "shared history pages launch");
+    }
     e = p.int2_kind == OSCAR_INT2_MFMA ? launch_int2_mfma(p, s) : launch_int2_valu(p, s);
     if (e != hipSuccess) return hip_fail(e, "history segment launch");
   } else {

@@ -66,6 +66,21 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
+// Shared history pages as the kernels see them (one oscar_shared_pages entry
+// plus its launch plan): `parts` equal page ranges, each one block per KV
+// head and group of up to kCasRowsPerBlock query rows; the segment's blocks
+// start at block_base of the cascade grid.
+constexpr int kMaxShared = OSCAR_MAX_SHARED;
+constexpr int kCasWaves = 4;                 // waves per cascade block
+constexpr int kCasRowsPerWave = 32;          // two 16-row MFMA tiles
+constexpr int kCasRowsPerBlock = kCasWaves * kCasRowsPerWave;
+struct SharedSeg {
+  int first, num;        // logical history pages [first, first + num)
+  int seq0, nseq;        // member sequences [seq0, seq0 + nseq)
+  int parts, rgroups;    // page ranges, row groups
+  int block_base;        // first block of the segment in the cascade grid
+};
+
 // Workspace partition used by decode_attn and merge.
 struct WsLayout {
   size_t qrot;      // fp32 [B][Hq][D]     q . R_k (unscaled)
@@ -74,6 +89,9 @@ struct WsLayout {
   size_t nslots;    // matrix-core kernel only: int32 [B] partial slots each sequence used
   size_t qhd;       // matrix-core kernel only: [B][Hq][8] per q head: int exponent
                     //   (bits), then sum of q_rot over each group * sm_scale * log2(e)
+  size_t qcas;      // shared pages only: int8 [B][Hq][3][D] the 7-bit pieces of the
+                    //   rotated query (piece-major), each 16-channel block stored
+                    //   4x4-transposed (byte 4i + j = channel 4j + i) for the MFMA
   size_t part_o;    // fp32 [B][Hq][S][D]  history chunk partial outputs (rotated basis)
   size_t part_ml;   // fp32 [B][Hq][S][2]  (max logit in log2 units, sum of exponentials)
   size_t bf_o;      // fp32 [B][Hq][kBf16Splits][D]  BF16 segment partial outputs
@@ -104,6 +122,13 @@ struct DecodeParams {
   int mfma_balanced;   // matrix-core kernel: may balance blocks across sequences
   int deterministic;   // matrix-core kernel: static page batches per wave
   const float *codebook;   // [Hkv][2][4] code levels (K, V) or nullptr = 0, 1, 2, 3
+  // shared history pages (cascade): the partial slots of a sequence are first
+  // its cascade slots (sum of `parts` over its segments, in page order), then
+  // those of the matrix-core kernel, which skips the shared pages
+  int n_shared;
+  int cas_slots;           // max over sequences of their cascade slots
+  int cas_blocks;          // cascade grid size
+  SharedSeg shared[kMaxShared];
   uint8_t *ws;
   WsLayout L;
   int16_t q_of_kv[OSCAR_MAX_Q_HEADS];  // [Hkv][g] q heads of each KV head
@@ -127,6 +152,22 @@ hipError_t launch_qrot(const DecodeParams &p, const uint16_t *q, const float *Rk
 hipError_t launch_bf16_seg(const DecodeParams &p, const uint16_t *q, hipStream_t s);
 hipError_t launch_int2_valu(const DecodeParams &p, hipStream_t s);
 hipError_t launch_int2_mfma(const DecodeParams &p, hipStream_t s);
+hipError_t launch_int2_cascade(const DecodeParams &p, hipStream_t s);
+
+// Cascade slots of sequence b (the partial slots its shared segments fill)
+// and the history pages they cover from page 0.
+__host__ __device__ inline int cascade_slots(const DecodeParams &p, int b, int *skip_pages) {
+  int n = 0, skip = 0;
+  for (int i = 0; i < p.n_shared; ++i) {
+    const SharedSeg &s = p.shared[i];
+    if (b >= s.seq0 && b < s.seq0 + s.nseq) {
+      n += s.parts;
+      skip = s.first + s.num > skip ? s.first + s.num : skip;
+    }
+  }
+  if (skip_pages) *skip_pages = skip;
+  return n;
+}
 hipError_t launch_bf16_hist(const DecodeParams &p, const uint16_t *q, hipStream_t s);
 hipError_t launch_merge(const DecodeParams &p, const float *Rv, float *out, float *lse,
                         hipStream_t s);

@@ -128,6 +128,19 @@ __device__ __forceinline__ void qrot_body(const DecodeParams &p, const uint16_t 
   const int nq = (p.g + 3) / 4;          // head quads (the last one partly empty if g < 4)
   const float sc = ldexpf(1.f, sh.qe);
   const int b = bh / p.Hq;
+  if (p.n_shared > 0) {
+    // the same pieces for the shared-page kernel, whose B operands hold one
+    // q row per column: [b][h][piece][D], channel 16k + 4j + i at byte
+    // 16k + 4i + j so that dword i of a 16-byte load is the MFMA's k-slot
+    // order (byte j of dword i = channel 4j + i, as the unpacked codes)
+    int8_t *dst = reinterpret_cast<int8_t *>(p.ws + p.L.qcas) + (size_t)bh * 3 * D;
+    for (int t = tid; t < 3 * D; t += 256) {
+      const int pc = t / D, c = t % D;
+      const int qi = (int)rintf(sh.qf[c] * sc);
+      const int piece = pc == 0 ? (qi >> 14) : pc == 1 ? ((qi >> 7) & 127) : (qi & 127);
+      dst[pc * D + (c & ~15) + 4 * (c & 3) + ((c >> 2) & 3)] = (int8_t)piece;
+    }
+  }
   for (int t = tid; t < nqk * 64; t += 256) {
     const int m = t >> 6, pc = (t >> 4) & 3, kb = (t >> 2) & 3, e = t & 3;
     const int blk = m / gpb, g2 = (64 * blk) / G + m % gpb;

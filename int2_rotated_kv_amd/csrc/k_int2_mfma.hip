@@ -176,6 +176,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   const int HG = mfma_heads_per_block(p.Hkv);
   const int WH = HB / HG;
   const int S = p.splits;                         // partial slots per (sequence, q head)
+  const int S_reg = S - p.cas_slots;              // of them this kernel's (after the cascade's)
   const int ngrp = (p.Hkv + HG - 1) / HG;
   const int NBT = gridDim.x / ngrp;               // blocks per head group
   const int hg = blockIdx.x / NBT;
@@ -229,6 +230,16 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     v = v > p.max_hist_len ? p.max_hist_len : v;
     return v > kPage * p.hist_stride ? kPage * p.hist_stride : v;
   };
+  // pages of sequence b this kernel reads: those after its shared pages,
+  // which the cascade kernel attends (with none shared: all of them)
+  auto own_pages = [&](int b, int *skip) {
+    const int npg = (clamp_len(p.hist_len[b]) + kPage - 1) / kPage;
+    int sk = 0;
+    if (p.n_shared > 0) cascade_slots(p, b, &sk);
+    sk = sk < npg ? sk : npg;
+    *skip = sk;
+    return npg - sk;
+  };
   auto &cum = lds.cum;                            // pages before sequence b
   auto &wsum = lds.wsum;
   const bool scan = p.mfma_balanced != 0;         // B <= kMaxBalancedBatch and no overflow
@@ -236,7 +247,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   bool balanced = false;
   if (scan) {
     const int t = threadIdx.x;
-    const int v = t < p.B ? (clamp_len(p.hist_len[t]) + kPage - 1) / kPage : 0;
+    int skip_t = 0;
+    const int v = t < p.B ? own_pages(t, &skip_t) : 0;
     int x = v;                                    // inclusive scan over the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -258,7 +270,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     if (t < p.B && v > 0 && T > 0) {
       const int first = (int)(((long long)(cum[t] + 1) * NB - 1) / T);
       const int last = (int)(((long long)(cum[t] + v) * NB - 1) / T);
-      bad = last - first + 1 > S;
+      bad = last - first + 1 > S_reg;
     }
     balanced = T > 0 && !__syncthreads_or(bad);
     // the merge reads each sequence's slot count
@@ -314,10 +326,23 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     fallback_done = true;
     b = bseg;
     const int part = ib % P;
-    const int npg = (clamp_len(p.hist_len[b]) + kPage - 1) / kPage;
+    int sk;
+    const int npg = own_pages(b, &sk);
     pbeg = (int)((long long)npg * part / P);
     pend_all = (int)((long long)npg * (part + 1) / P);
     slot = part;
+  }
+  {
+    // past the sequence's shared pages; its cascade slots come first
+    int sk = 0;
+    const int ncas = p.n_shared > 0 ? cascade_slots(p, b, &sk) : 0;
+    if (ncas > 0) {
+      const int npg = (clamp_len(p.hist_len[b]) + kPage - 1) / kPage;
+      sk = sk < npg ? sk : npg;
+      pbeg += sk;
+      pend_all += sk;
+      slot += ncas;
+    }
   }
   const int hl = clamp_len(p.hist_len[b]);
   const int pend = live ? pend_all : pbeg;        // no pages for a wave without a head

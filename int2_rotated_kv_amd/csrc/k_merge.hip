@@ -60,8 +60,12 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeParams p, const float *__res
   const int S = p.splits;                      // row stride of the partials
   // chunks of this sequence: all S, or the slots the matrix-core kernel used
   int n = S;
-  if (S > 0 && p.int2_kind == OSCAR_INT2_MFMA)
-    n = p.mfma_balanced ? reinterpret_cast<const int *>(p.ws + p.L.nslots)[bh / p.Hq] : p.mfma_parts;
+  if (S > 0 && p.int2_kind == OSCAR_INT2_MFMA) {
+    // the cascade slots of shared pages, then the matrix-core kernel's
+    const int b = (int)(bh / p.Hq);
+    n = p.mfma_balanced ? reinterpret_cast<const int *>(p.ws + p.L.nslots)[b] : p.mfma_parts;
+    if (p.n_shared > 0) n += cascade_slots(p, b, nullptr);
+  }
   extern __shared__ float a_s[];               // [S] chunk weights 2^(m_s - M)
   __shared__ float4 red[NW][LPR];              // per-wave channel sums
   __shared__ __align__(16) float Os[D];        // merged history output (rotated basis)

@@ -221,6 +221,21 @@ def make_small(wl: Workload, distinct_rv: bool = False) -> SmallInputs:
     return SmallInputs(wl, q, K, V, R_k, R_v, clip_k, clip_v, out_k, out_v)
 
 
+def share_history(inp: SmallInputs, segments) -> SmallInputs:
+    """Make sequences share history pages, as a prefix cache does for a
+    common prompt prefix: for each (first_page, num_pages, seq_begin,
+    num_seqs), the history tokens of pages first_page .. +num_pages-1 (token
+    positions 64 + 16*page ..) of sequences seq_begin+1 .. are overwritten (in
+    place) with those of sequence seq_begin."""
+    for (first, num, s0, n) in segments:
+        a, e = SINK + PAGE * first, SINK + PAGE * (first + num)
+        for b in range(s0 + 1, s0 + n):
+            assert e <= SINK + split_lengths(inp.wl.lengths[b])[1], "segment beyond the history"
+            inp.K[b][a:e] = inp.K[s0][a:e]
+            inp.V[b][a:e] = inp.V[s0][a:e]
+    return inp
+
+
 def plant_tokens(inp: SmallInputs, b: int, positions, kind: str, value: float = 0.0,
                  which: str = "kv") -> SmallInputs:
     """Overwrite tokens of sequence b (in place, token order positions) with
@@ -344,6 +359,22 @@ class LargeGen:
         self.hist_table = np.where(table >= 0, perm[np.maximum(table, 0)], 0).astype(np.int32)
         # a page's tokens that come from the shared prompt are identical across the
         # sequences aliasing it; partially-filled tail pages are private
+
+    def shared_segments(self):
+        """The aliasing of the page tables as shared-page segments
+        (first_page, num_pages, seq_begin, num_seqs): the prefix pages shared
+        by every sequence, then the rest of the prompt's full pages shared by
+        the sequences without a distinct suffix (those come last)."""
+        wl = self.wl
+        if not wl.shared_prefix:
+            return []
+        pre = max(0, wl.shared_prefix - SINK) // PAGE
+        n_distinct = int(round(wl.distinct_frac * wl.B))
+        segs = [(0, pre, 0, wl.B)] if pre > 0 and wl.B >= 2 else []
+        rest = int(min(self.hist_len0[n_distinct:] // PAGE)) - pre if n_distinct < wl.B else 0
+        if rest > 0 and wl.B - n_distinct >= 2:
+            segs.append((pre, rest, n_distinct, wl.B - n_distinct))
+        return segs
 
     def history_block(self, blk: int):
         """K, V bf16 tensors [PAGES_PER_BLOCK*16][Hkv][D] for unique pages of block blk."""

@@ -40,12 +40,16 @@ def hist_capacity_pages(L: int, steps: int) -> int:
 
 def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_splits=0,
                    R_v_none=False, head_map=None, device="cuda", seed_perm=None, fused=False,
-                   flags=0, codebook=None, max_hist_len=None, extra_pages=0, noalloc=False):
+                   flags=0, codebook=None, max_hist_len=None, extra_pages=0, noalloc=False,
+                   shared=None):
     """Build the initial split cache of every sequence, run `steps` decode steps
     (demote oldest recent -> write new token -> attend -> merge; with fused,
     through the single oscar_decode_step call, with noalloc through
     oscar_decode_step_noalloc), return the outputs of the last step and the
-    INT2 pool."""
+    INT2 pool.  shared: [(first_page, num_pages, seq_begin, num_seqs)], whose
+    member sequences' page tables then list seq_begin's physical pages there
+    (their tokens must be equal: synth.share_history); passed to the decode
+    calls as oscar_shared_pages."""
     import torch
     from int2_rotated_kv_amd import binding as ob
     from int2_rotated_kv_amd.splitcache import SplitCache
@@ -61,6 +65,9 @@ def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_sp
     for b in range(B):
         table[b, :caps[b]] = perm[o:o + caps[b]]
         o += caps[b]
+    for (first, num, s0, n) in (shared or []):
+        for b in range(s0 + 1, s0 + n):
+            table[b, first:first + num] = table[s0, first:first + num]
     cb = None if codebook is None else torch.from_numpy(np.asarray(codebook, np.float32)).to(device)
     sc = SplitCache(B, wl.Hkv, wl.Hq, wl.D, wl.G, table, n_int2 + 3, staging_pages=64, device=device,
                     codebook=cb)
@@ -92,7 +99,7 @@ def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_sp
             sc.commit_step()
             sc.sync_lengths()
             args = sc.decode_args(max_hist_len=max_hist_len, kv_head_of_q=head_map, num_splits=num_splits,
-                                  int2_kernel=int2_kernel, flags=flags)
+                                  int2_kernel=int2_kernel, flags=flags, shared=shared)
             ob.decode_step_noalloc(sc.cache, args, d_src, d_dst, ck, cv, d_w, kn, vn, q, Rk, Rv, out, lse)
             continue
         if not fused:
@@ -101,7 +108,7 @@ def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_sp
         sc.commit_step()
         sc.sync_lengths()
         args = sc.decode_args(max_hist_len=max_hist_len, kv_head_of_q=head_map, num_splits=num_splits,
-                              int2_kernel=int2_kernel, flags=flags)
+                              int2_kernel=int2_kernel, flags=flags, shared=shared)
         if fused:
             ws = ob.alloc_workspace(sc.cache, args, device=q.device)
             ob.decode_step(sc.cache, args, d_src, d_dst, ck, cv, d_w, kn, vn, q, Rk, Rv, ws, out, lse)

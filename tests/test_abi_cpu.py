@@ -297,3 +297,42 @@ def test_noalloc_step_rejects_before_launch():
     st = lib.oscar_decode_step_noalloc(ctypes.byref(c), ctypes.byref(_args(int2_kernel=ob.HISTORY_BF16)),
                                        *ptrs, 0x2100, None, None)
     assert st == ob.OSCAR_EUNSUPPORTED
+
+
+def _shared(*segs):
+    arr = (ob.OscarSharedPages * len(segs))(*[ob.OscarSharedPages(*s) for s in segs])
+    return len(segs), ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def test_shared_segments_validated_and_planned():
+    """oscar_shared_pages: segments must tile each member sequence's first
+    pages, stay inside the batch and below max_hist_len; with the matrix-core
+    kernel and one group per token they add cascade partial slots (a larger
+    workspace), with the vector-ALU kernel or G < D they are only validated."""
+    big = dict(batch=16, hist_stride=8200, max_hist_len=8172 * 16, num_q_heads=64)
+    c = _cache(group_size=128)
+    st0, n0 = _ws(c, _args(**big))
+    assert st0 == ob.OSCAR_OK
+    n, p, keep = _shared((0, 2044, 0, 16), (2044, 6128, 3, 13))
+    st, n1 = _ws(c, _args(num_shared=n, shared=p, **big))
+    assert st == ob.OSCAR_OK and n1 > n0
+    # the vector-ALU kernel, or groups smaller than head_dim: no cascade slots
+    st, n2 = _ws(c, _args(num_shared=n, shared=p, int2_kernel=ob.INT2_VALU, **big))
+    st0v, n0v = _ws(c, _args(int2_kernel=ob.INT2_VALU, **big))
+    assert st == ob.OSCAR_OK and n2 == n0v
+    st, n3 = _ws(_cache(group_size=64), _args(num_shared=n, shared=p, **big))
+    assert st == ob.OSCAR_OK and n3 == _ws(_cache(group_size=64), _args(**big))[1]
+    for segs, why in ((((1, 10, 0, 4),), "gap"),
+                      (((0, 10, 0, 4), (11, 5, 0, 4)), "gap"),
+                      (((0, 10, 0, 4), (0, 10, 2, 3)), "two shared segments"),
+                      (((0, 10, 14, 4),), "out of range"),
+                      (((0, 10, 0, 1),), "out of range"),
+                      (((0, 0, 0, 4),), "out of range"),
+                      (((0, 9000, 0, 4),), "max_hist_len")):
+        n, p, keep = _shared(*segs)
+        st, _ = _ws(c, _args(num_shared=n, shared=p, **big))
+        assert st == ob.OSCAR_EINVAL and why in ob.last_error(), (segs, ob.last_error())
+    st, _ = _ws(c, _args(num_shared=1, shared=None, **big))
+    assert st == ob.OSCAR_EINVAL
+    st, _ = _ws(c, _args(num_shared=17, shared=p, **big))
+    assert st == ob.OSCAR_EINVAL
