@@ -272,7 +272,25 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
     // sequences one sequence may use up to 2S + 2 partial slots
     p->mfma_balanced = a->batch > 1 && a->batch <= kMaxBalancedBatch &&
                        (long long)a->batch * npages < (1LL << 31);
-    S = 2 * S + 2;
+    int cap = 2 * S + 2;
+    if (p->n_shared > 0 && npages > 0) {
+      // the shared pages are skipped, so the pages left can sit in a few
+      // sequences (those with their own continuation): with every history at
+      // the length bound, the sequence with the most pages left is covered by
+      // about blocks * its pages / all pages left blocks, plus the ends
+      long long left = 0, most = 0;
+      for (int b = 0; b < a->batch; ++b) {
+        int skip = 0;
+        cascade_slots(*p, b, &skip);
+        const long long own = npages - skip > 0 ? npages - skip : 0;
+        left += own;
+        most = own > most ? own : most;
+      }
+      const long long blocks = (long long)a->batch * S;
+      const long long need = left > 0 ? (blocks * most + left - 1) / left + 2 : 2;
+      cap = need > cap ? (int)(need < kMaxSplits ? need : kMaxSplits) : cap;
+    }
+    S = cap;
   }
   S += p->cas_slots;                 // the cascade's slots come first in each row
   p->splits = S;

@@ -165,8 +165,20 @@ void k_int2_cascade(DecodeParams p) {
   const uint32_t off_k = (uint32_t)RL.kword(16 * g4 + cas_token(r16), 0);
   const uint32_t off_sz0 = (uint32_t)RL.tok_sz(2 * g4), off_sz1 = (uint32_t)RL.tok_sz(2 * g4 + 8);
 
-  auto issue = [&](Stage &sgi, int k) {      // k: logical page (uniform)
-    const int phys = k < pe ? ptab[k] : -1;
+  // The waves of a block read the same pages; each starts a quarter of the
+  // range further on (the softmax does not depend on the order), so that
+  // every wave leads the HBM reads of its own quarter and the others find
+  // those pages in the L2 or the last-level cache: four times the distinct
+  // pages in flight per block.
+  const int npg = pe - pb;
+  const int shift = npg > 0 ? (int)((long long)npg * w / kCasWaves) : 0;
+  auto issue = [&](Stage &sgi, int i) {      // i: position in this wave's order (uniform)
+    int k = -1;
+    if (i < npg) {
+      k = i + shift;
+      k = pb + (k >= npg ? k - npg : k);
+    }
+    const int phys = k >= 0 ? ptab[k] : -1;
     sgi.ok = phys >= 0 && phys < npool;
     // out-of-range stages still load (page 0) so every lane issues the same loads
     const uint8_t *rec = pool_j + (sgi.ok ? (size_t)phys : 0) * rec_stride;
@@ -320,14 +332,14 @@ void k_int2_cascade(DecodeParams p) {
     }
   };
 
-  if (pe > pb) {
+  if (npg > 0) {
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i) issue(st[i], pb + i);
-    for (int k0 = pb; k0 < pe; k0 += NS) {
+    for (int i = 0; i < NS - 1; ++i) issue(st[i], i);
+    for (int i0 = 0; i0 < npg; i0 += NS) {
 #pragma unroll
       for (int s2 = 0; s2 < NS; ++s2) {
-        issue(st[(s2 + NS - 1) % NS], k0 + s2 + NS - 1);
-        if (k0 + s2 < pe) process(st[s2]);
+        issue(st[(s2 + NS - 1) % NS], i0 + s2 + NS - 1);
+        if (i0 + s2 < npg) process(st[s2]);
       }
     }
   }

@@ -145,7 +145,8 @@ constexpr int kPidCap = 1024;                   // page ids of a segment staged 
 // LDS of the matrix-core kernel
 template <int D, int G, int GQ, int NP>
 struct Int2Shared {
-  int cum[kMaxBalancedBatch + 1];                 // pages before sequence b
+  int cum[kMaxBalancedBatch + 1];                 // work units before sequence b
+  int pst[kMaxBalancedBatch];                     // unit where sequence b's pages start
   int wsum[kMfmaWaves];
   int batch_ctr[8];                               // per head: next batch of the segment
   int pid_lds[kPidCap];
@@ -216,15 +217,18 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   const bool plane2 = CB && (kcC != 0.f || vcC != 0.f);
 
   // ---------------- schedule: this block's segments ----------------
-  // The histories of the batch laid end to end hold T pages; block ib of its
-  // head group covers pages [T*ib/NB, T*(ib+1)/NB) with NB = min(NBT, T/16)
-  // blocks at work, so blocks get equal page counts whatever the sequence
-  // lengths.  A range that crosses a sequence boundary is handled as one
-  // segment per sequence, each writing its own partial slot: the index of the
-  // block among the blocks that cover that sequence.  If some sequence would
-  // need more than S slots (lengths far from equal), or the batch is larger
-  // than the block, every block instead takes one of P equal parts of one
-  // sequence (slot = part).
+  // The histories of the batch laid end to end, each sequence counted as its
+  // pages plus kSegCost units for the fixed cost of a segment (query operands,
+  // page ids, the combine and the partial's stores), hold T units; block ib
+  // of its head group covers units [T*ib/NB, T*(ib+1)/NB) with
+  // NB = min(NBT, T/16) blocks at work, so blocks get about equal work
+  // whatever the sequence lengths (a block does not collect the fixed costs
+  // of many short sequences).  A range that crosses a sequence boundary is
+  // handled as one segment per sequence, each writing its own partial slot:
+  // the index of the block among the blocks that cover that sequence's pages.
+  // If some sequence would need more than S slots (lengths far from equal),
+  // or the batch is larger than the block, every block instead takes one of P
+  // equal parts of one sequence (slot = part).
   auto clamp_len = [&](int v) {
     v = v < 0 ? 0 : v;
     v = v > p.max_hist_len ? p.max_hist_len : v;
@@ -240,7 +244,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     *skip = sk;
     return npg - sk;
   };
-  auto &cum = lds.cum;                            // pages before sequence b
+  constexpr int kSegCost = 48;                    // units of a segment's fixed cost
+  auto &cum = lds.cum;                            // units before sequence b
+  auto &pst = lds.pst;                            // unit of sequence b's first page
   auto &wsum = lds.wsum;
   const bool scan = p.mfma_balanced != 0;         // B <= kMaxBalancedBatch and no overflow
   int T = 0, NB = 1;
@@ -249,7 +255,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     const int t = threadIdx.x;
     int skip_t = 0;
     const int v = t < p.B ? own_pages(t, &skip_t) : 0;
-    int x = v;                                    // inclusive scan over the wave
+    const int wv = v > 0 ? v + kSegCost : 0;      // work units of sequence t
+    int x = wv;                                   // inclusive scan over the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int y = __shfl_up(x, o);
@@ -259,30 +266,27 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     __syncthreads();
     int before = 0;
     for (int k = 0; k < w; ++k) before += wsum[k];
-    if (t < p.B) cum[t] = before + x - v;
+    if (t < p.B) {
+      cum[t] = before + x - wv;
+      pst[t] = before + x - v;                    // the pages are the sequence's last units
+    }
     if (t == p.B - 1) cum[p.B] = before + x;
     __syncthreads();
     T = cum[p.B];
     NB = T / 16 < NBT ? T / 16 : NBT;
     NB = NB < 1 ? 1 : NB;
-    // the block holding global page g: the largest i with T*i/NB <= g
+    // the block holding unit u: the largest i with T*i/NB <= u; the blocks
+    // covering sequence t's pages: those holding units pst .. pst + v - 1
     bool bad = false;
+    int first = 0, last = -1;
     if (t < p.B && v > 0 && T > 0) {
-      const int first = (int)(((long long)(cum[t] + 1) * NB - 1) / T);
-      const int last = (int)(((long long)(cum[t] + v) * NB - 1) / T);
+      first = (int)(((long long)(pst[t] + 1) * NB - 1) / T);
+      last = (int)(((long long)(pst[t] + v) * NB - 1) / T);
       bad = last - first + 1 > S_reg;
     }
     balanced = T > 0 && !__syncthreads_or(bad);
     // the merge reads each sequence's slot count
-    if (hg == 0 && ib == 0 && t < p.B) {
-      int n = P;
-      if (balanced) {
-        const int first = (int)(((long long)(cum[t] + 1) * NB - 1) / T);
-        const int last = (int)(((long long)(cum[t] + v) * NB - 1) / T);
-        n = v > 0 ? last - first + 1 : 0;
-      }
-      reinterpret_cast<int *>(p.ws + p.L.nslots)[t] = n;
-    }
+    if (hg == 0 && ib == 0 && t < p.B) reinterpret_cast<int *>(p.ws + p.L.nslots)[t] = balanced ? last - first + 1 : P;
   }
   const long long g0 = balanced && ib < NB ? (long long)T * ib / NB : 0;
   const long long g1 = balanced && ib < NB ? (long long)T * (ib + 1) / NB : 0;
@@ -311,16 +315,17 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   // ---------------- next segment: sequence b, its pages [pbeg, pend) ----------------
   int b, pbeg, pend_all, slot;
   if (balanced) {
+    // skip sequences whose pages [pst, cum[b + 1]) miss [g0, g1)
     while (bseg < p.B && cum[bseg] < g1 &&
-           (cum[bseg + 1] < g1 ? cum[bseg + 1] : g1) <= (cum[bseg] > g0 ? cum[bseg] : g0))
+           (cum[bseg + 1] < g1 ? cum[bseg + 1] : g1) <= (pst[bseg] > g0 ? pst[bseg] : g0))
       ++bseg;
     if (bseg >= p.B || ib >= NB || cum[bseg] >= g1) break;
     b = bseg++;
-    const long long lo = cum[b] > g0 ? cum[b] : g0;
+    const long long lo = pst[b] > g0 ? pst[b] : g0;
     const long long hi = cum[b + 1] < g1 ? cum[b + 1] : g1;
-    pbeg = (int)(lo - cum[b]);
-    pend_all = (int)(hi - cum[b]);
-    slot = ib - (int)(((long long)(cum[b] + 1) * NB - 1) / T);
+    pbeg = (int)(lo - pst[b]);
+    pend_all = (int)(hi - pst[b]);
+    slot = ib - (int)(((long long)(pst[b] + 1) * NB - 1) / T);
   } else {
     if (fallback_done || bseg >= p.B || P == 0) break;
     fallback_done = true;
