@@ -198,8 +198,8 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   p->cas_blocks = 0;
   if (a->num_shared > 0 && kind == OSCAR_INT2_MFMA && c->group_size == c->head_dim) {
     // page ranges of about equal size so that the grid holds ~2 blocks per
-    // compute unit, each at least kCasMinPages pages (its partials, written
-    // and read back, stay well below the pages' bytes)
+    // compute unit (as many as fit at once), each at least kCasMinPages pages
+    // (its partials, written and read back, stay well below the pages' bytes)
     constexpr int kCasMinPages = 32, kCasTargetBlocks = 512;
     long long work = 0;
     const int g = p->g;

@@ -36,6 +36,7 @@ namespace oscar {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 namespace {
@@ -44,6 +45,15 @@ __device__ __forceinline__ v4h as_v4h2(uint32_t a, uint32_t b) {
   v4h r;
   __builtin_memcpy(&r, &a, 4);
   __builtin_memcpy(reinterpret_cast<char *>(&r) + 4, &b, 4);
+  return r;
+}
+
+__device__ __forceinline__ v8h as_v8h(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  v8h r;
+  __builtin_memcpy(&r, &a, 4);
+  __builtin_memcpy(reinterpret_cast<char *>(&r) + 4, &b, 4);
+  __builtin_memcpy(reinterpret_cast<char *>(&r) + 8, &c, 4);
+  __builtin_memcpy(reinterpret_cast<char *>(&r) + 12, &d, 4);
   return r;
 }
 
@@ -80,16 +90,23 @@ __device__ __forceinline__ int cas_token(int r) { return 2 * (r >> 2) + ((r & 1)
 
 }  // namespace
 
+#ifndef OSCAR_CAS_STAGES
+#define OSCAR_CAS_STAGES 2   // ring of pairs of pages: one pair in flight
+#endif
+#ifndef OSCAR_CAS_WAVES_PER_SIMD
+#define OSCAR_CAS_WAVES_PER_SIMD 2
+#endif
 template <int D, int G>
-__global__ __launch_bounds__(64 * kCasWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * kCasWaves)
+__attribute__((amdgpu_waves_per_eu(OSCAR_CAS_WAVES_PER_SIMD, OSCAR_CAS_WAVES_PER_SIMD)))
 void k_int2_cascade(DecodeParams p) {
   constexpr RecLayout RL(D, G);
   constexpr int NG = D / G;                  // groups per token (1 or 2)
   constexpr int NBLK = D / 64;               // 64-channel blocks (K words per token slot)
   constexpr int NSL = D / 16;                // 16-channel PV slices
   constexpr int NT = kCasRowsPerWave / 16;   // 16-row tiles per wave
-  constexpr int NS = 3;                      // register ring: NS - 1 pages in flight
   constexpr float kLazy = 2.f;               // log2 headroom of the running max
+  constexpr float kOver = 2.f;               // a raised max sits this far above the logits
   // one group per token: with two (D = 128, G = 64) the doubled scale/zero
   // words and per-group accumulators no longer fit the register budget
   static_assert(G == D, "one group per token");
@@ -118,17 +135,23 @@ void k_int2_cascade(DecodeParams p) {
   // the page ring and the PV accumulators
   __shared__ v4i qlds[kCasWaves][NT][3][NBLK][64];
   float qsc[NT], qz[NT][NG];                 // 2^-qe * sm_scale * log2(e); group sums
-  size_t prow[NT];                           // partial row of (sequence, q head, slot)
+  // the (sequence, q head) of tile t's row of this lane, and whether it exists
+  auto row_of = [&](int t, int &b, size_t &bh) {
+    const int row = row0 + 16 * t + r16;
+    const bool ok = row < rows;
+    const int m = ok ? row / p.g : 0, hh = ok ? row % p.g : 0;
+    b = sg.seq0 + m;
+    int h = p.q_of_kv[j * p.g];
+    for (int k = 1; k < p.g; ++k) h = hh == k ? p.q_of_kv[j * p.g + k] : h;
+    bh = (size_t)b * p.Hq + h;
+    return ok;
+  };
   bool rv[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int row = row0 + 16 * t + r16;
-    rv[t] = row < rows;
-    const int m = rv[t] ? row / p.g : 0, hh = rv[t] ? row % p.g : 0;
-    const int b = sg.seq0 + m;
-    int h = p.q_of_kv[j * p.g];
-    for (int k = 1; k < p.g; ++k) h = hh == k ? p.q_of_kv[j * p.g + k] : h;
-    const size_t bh = (size_t)b * p.Hq + h;
+    int b;
+    size_t bh;
+    rv[t] = row_of(t, b, bh);
     const int8_t *qc = reinterpret_cast<const int8_t *>(p.ws + p.L.qcas) + bh * 3 * D;
 #pragma unroll
     for (int pc = 0; pc < 3; ++pc)
@@ -140,13 +163,6 @@ void k_int2_cascade(DecodeParams p) {
     qsc[t] = rv[t] ? ldexpf(1.f, -__float_as_int(hd[0])) * p.sm_log2 : 0.f;
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) qz[t][gg] = rv[t] ? hd[1 + gg] : 0.f;
-    // this part's slot: after the parts of the sequence's earlier segments
-    int slot = part;
-    for (int i = 0; i < p.n_shared; ++i) {
-      const SharedSeg &o = p.shared[i];
-      if (b >= o.seq0 && b < o.seq0 + o.nseq && o.first < sg.first) slot += o.parts;
-    }
-    prow[t] = bh * S + slot;
   }
 
   // ---- page ring ----
@@ -156,7 +172,6 @@ void k_int2_cascade(DecodeParams p) {
     uint32_t sz[8 * NG];                     // (scale, zero) words of tokens 2g4, 2g4+1, 2g4+8, 2g4+9
     int ok;
   };
-  Stage st[NS];
   using cint32 = const __attribute__((address_space(4))) int32_t;
   cint32 *ptab = (cint32 *)(p.hist_pages + (size_t)sg.seq0 * p.hist_stride);
   const size_t rec_stride = (size_t)p.Hkv * RL.bytes();
@@ -172,16 +187,34 @@ void k_int2_cascade(DecodeParams p) {
   // pages in flight per block.
   const int npg = pe - pb;
   const int shift = npg > 0 ? (int)((long long)npg * w / kCasWaves) : 0;
+  // page table entries in this wave's order, 64 positions per register:
+  // lane l of chunk c holds the physical page of position 64 c + l (a
+  // position past the range: the wave's first page).  The next chunk is
+  // loaded while the current one is used; pages are picked by readlane
+  auto ptab_chunk = [&](int c) -> int {
+    const int i = 64 * c + lane;
+    int k = (i < npg ? i : 0) + shift;
+    k = pb + (k >= npg ? k - npg : k);
+    return ptab[k];
+  };
+  int pt_cur = 0, pt_next = 0;
+  if (npg > 0) {
+    pt_cur = ptab_chunk(0);
+    pt_next = npg > 64 ? ptab_chunk(1) : 0;
+  }
   auto issue = [&](Stage &sgi, int i) {      // i: position in this wave's order (uniform)
-    int k = -1;
-    if (i < npg) {
-      k = i + shift;
-      k = pb + (k >= npg ? k - npg : k);
+    // a position past the range (the second page of a last, odd pair) loads
+    // the wave's first page again and is marked empty: its weights are 0,
+    // and the values they multiply are those of a written record
+    if ((i & 63) == 0 && i > 0) {            // uniform: the next chunk of the table
+      pt_cur = pt_next;
+      if (i + 64 < npg) pt_next = ptab_chunk((i >> 6) + 1);
     }
-    const int phys = k >= 0 ? ptab[k] : -1;
-    sgi.ok = phys >= 0 && phys < npool;
-    // out-of-range stages still load (page 0) so every lane issues the same loads
-    const uint8_t *rec = pool_j + (sgi.ok ? (size_t)phys : 0) * rec_stride;
+    const bool inr = i < npg;
+    const int phys = __builtin_amdgcn_readlane(pt_cur, i & 63);
+    const bool valid = phys >= 0 && phys < npool;
+    sgi.ok = inr && valid;
+    const uint8_t *rec = pool_j + (valid ? (size_t)phys : 0) * rec_stride;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(rec), (short)0, RL.bytes(), 0x00020000);
     rsrc_words<NBLK>(sgi.kw, rs, off_k);
@@ -196,150 +229,162 @@ void k_int2_cascade(DecodeParams p) {
     rsrc_words<4 * NG>(sgi.sz + 4 * NG, rs, off_sz1);
   };
 
-  float m_run[NT], m_thr[NT], lsum[NT], zacc[NT][NG];
-  v4f acc[NT][NSL], corr[NT][NG];
+  // running state per tile (the lane's row): m_run the row's running max,
+  // set exactly by the first pair of pages and raised lazily after that;
+  // lsum and zacc the lane's partial sums of p and p * zero_v; acc the PV
+  // accumulators (channels 16 sl + 4 g4 + i), corr the sum of the PV weights
+  float m_run[NT], lsum[NT], zacc[NT];
+  v4f acc[NT][NSL], corr[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    m_run[t] = -INFINITY;
-    m_thr[t] = -INFINITY;
+    m_run[t] = 0.f;
     lsum[t] = 0.f;
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-      zacc[t][gg] = 0.f;
-      corr[t][gg] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
+    zacc[t] = 0.f;
+    corr[t] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) acc[t][sl] = v4f{0.f, 0.f, 0.f, 0.f};
   }
+  bool started = false;                      // m_run holds a row maximum (uniform)
   const uint32_t rot = (uint32_t)(4 * g4 - 6) & 31u;   // token 2g4 of a V word to bit 6
   uint32_t f16one, mlo, mhi;
   asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(f16one));
   asm volatile("s_mov_b32 %0, 0xc000c0" : "=s"(mlo));
   asm volatile("s_mov_b32 %0, 0x3000300" : "=s"(mhi));
-  const v4h ones = as_v4h2(f16one, f16one);
-  // sz word base of value v (tokens 2g4, 2g4+8, 2g4+1, 2g4+9) and its PV factor
-  constexpr int kSzBase[4] = {0, 4 * NG, 2 * NG, 6 * NG};
+  const v8h ones = as_v8h(f16one, f16one, f16one, f16one);
+  // sz word of value v (tokens 2g4, 2g4+8, 2g4+1, 2g4+9): K (scale, zero),
+  // then V; the PV factor of value v (mantissa bit 6 or 8 of its code)
+  constexpr int kSzBase[4] = {0, 4, 2, 6};
+  constexpr float kPvf[4] = {16.f, 16.f, 4.f, 4.f};
 
-  auto process = [&](Stage &sgi) {
-    if (!sgi.ok) return;
-    // per value v (token) and group: K scale, zero; V scale (with the PV
-    // factor 16 or 4) and zero
-    float ks[4][NG], kz[4][NG], vsf[4][NG], vz[4][NG];
+  // A pair of pages per step: the PV contraction takes the 32 tokens of both
+  // in one v_mfma_f32_16x16x32_f16 (k slots 8 g4 .. 8 g4 + 3: the lane's 4
+  // tokens of page a, 8 g4 + 4 .. 8 g4 + 7: of page b; the A and B operands
+  // of a lane list the same tokens in the same order).  Logits are kept
+  // relative to the running max: s' = dot * (k_scale * qsc) + (k_zero * qz - m).
+  auto process = [&](Stage &sa, Stage &sb) {
+    if (!sa.ok && !sb.ok) return;
+    float sv[2][NT][4];                      // relative logits, -inf for an empty page
+    float vsf[2][4], vz[2][4];               // V scale * PV factor, V zero per value
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int gg = 0; gg < NG; ++gg) {
-        const uint32_t kw = sgi.sz[kSzBase[v] + gg], vw = sgi.sz[kSzBase[v] + NG + gg];
-        ks[v][gg] = bf16_lo(kw);
-        kz[v][gg] = bf16_hi(kw);
-        vsf[v][gg] = bf16_lo(vw) * (v < 2 ? 16.f : 4.f);
-        vz[v][gg] = bf16_hi(vw);
-      }
-    // QK A operands: the codes as bytes (byte j of dword i = channel 4j + i
-    // of the lane's 16 channels)
-    v4i kb[NBLK];
-#pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk) {
-      const uint32_t e = sgi.kw[blk];
-      kb[blk] = v4i{(int)(e & 0x03030303u), (int)((e >> 2) & 0x03030303u), (int)((e >> 4) & 0x03030303u),
-                    (int)((e >> 6) & 0x03030303u)};
-    }
-    float s_[NT][4];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      v4i qa[3][NG];
-#pragma unroll
-      for (int pc = 0; pc < 3; ++pc)
-#pragma unroll
-        for (int gg = 0; gg < NG; ++gg) qa[pc][gg] = v4i{0, 0, 0, 0};
-#pragma unroll
-      for (int pc = 0; pc < 3; ++pc)
-#pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk) {
-          const int gg = (64 * blk) / G;
-          qa[pc][gg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb[blk], qlds[w][t][pc][blk][lane],
-                                                             qa[pc][gg], 0, 0, 0);
-        }
+    for (int pg = 0; pg < 2; ++pg) {
+      Stage &sgi = pg ? sb : sa;
+      const float empty = sgi.ok ? 0.f : -INFINITY;   // uniform
+      float ks[4], kz[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        float sc = 0.f, zt = 0.f;
+        const uint32_t kw = sgi.sz[kSzBase[v]], vw = sgi.sz[kSzBase[v] + 1];
+        ks[v] = bf16_lo(kw);
+        kz[v] = bf16_hi(kw);
+        vsf[pg][v] = bf16_lo(vw) * kPvf[v];
+        vz[pg][v] = bf16_hi(vw);
+      }
+      // QK A operands: the codes as bytes (byte j of dword i = channel
+      // 4j + i of the lane's 16 channels)
+      v4i kb[NBLK];
 #pragma unroll
-        for (int gg = 0; gg < NG; ++gg) {
-          int dhi = (qa[0][gg][v] << 7) + qa[1][gg][v];
-          asm volatile("" : "+v"(dhi));
-          const float dot = (float)((dhi << 7) + qa[2][gg][v]);
-          sc = fmaf(ks[v][gg], dot, sc);
-          zt = fmaf(kz[v][gg], qz[t][gg], zt);
+      for (int blk = 0; blk < NBLK; ++blk) {
+        const uint32_t e = sgi.kw[blk];
+        kb[blk] = v4i{(int)(e & 0x03030303u), (int)((e >> 2) & 0x03030303u),
+                      (int)((e >> 4) & 0x03030303u), (int)((e >> 6) & 0x03030303u)};
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        v4i qa[3];
+#pragma unroll
+        for (int pc = 0; pc < 3; ++pc) {
+          qa[pc] = v4i{0, 0, 0, 0};
+#pragma unroll
+          for (int blk = 0; blk < NBLK; ++blk)
+            qa[pc] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb[blk], qlds[w][t][pc][blk][lane], qa[pc], 0, 0, 0);
         }
-        s_[t][v] = fmaf(sc, qsc[t], zt);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          int dhi = (qa[0][v] << 7) + qa[1][v];
+          asm volatile("" : "+v"(dhi));
+          const float dot = (float)((dhi << 7) + qa[2][v]);
+          sv[pg][t][v] = fmaf(dot, ks[v] * qsc[t], fmaf(kz[v], qz[t][0], empty - m_run[t]));
+        }
       }
     }
 
-    // ---- online softmax, lazy running max per row ----
-    bool grow = false;
+    // ---- lazy running max, per tile: raised when a logit of the tile's
+    // rows exceeds it by more than kLazy (log2 units), and set on the first
+    // pair; a raised row max is placed kOver above the new maximum, so that
+    // the next raise needs a rise of more than kLazy + kOver ----
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) grow |= s_[t][v] > m_thr[t];
-    if (__builtin_expect(__any(grow), 0)) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        float mx = fmaxf(fmaxf(s_[t][0], s_[t][1]), fmaxf(s_[t][2], s_[t][3]));
+    for (int t = 0; t < NT; ++t) {
+      float mx = fmaxf(fmaxf(fmaxf(sv[0][t][0], sv[0][t][1]), fmaxf(sv[0][t][2], sv[0][t][3])),
+                       fmaxf(fmaxf(sv[1][t][0], sv[1][t][1]), fmaxf(sv[1][t][2], sv[1][t][3])));
+      if (__builtin_expect(!started || __any(mx > kLazy), 0)) {
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m_run[t], mx);
-        const float alpha = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - mnew);
-        m_run[t] = mnew;
-        m_thr[t] = mnew + kLazy;
-        lsum[t] *= alpha;
+        // the rise of the row max (the first pair: the max itself)
+        const float delta = !started ? mx + kOver : (mx > kLazy ? mx + kOver : 0.f);
+        const float alpha = started ? __builtin_amdgcn_exp2f(-delta) : 0.f;
+        m_run[t] += delta;
 #pragma unroll
-        for (int gg = 0; gg < NG; ++gg) {
-          zacc[t][gg] *= alpha;
-          corr[t][gg] *= alpha;
-        }
+        for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sv[pg][t][v] -= delta;
+        lsum[t] *= alpha;
+        zacc[t] *= alpha;
+        corr[t] *= alpha;
 #pragma unroll
         for (int sl = 0; sl < NSL; ++sl) acc[t][sl] *= alpha;
       }
     }
-    // weights; PV B operands per group: p * scale_v * (16 or 4) in f16
-    v4h pbv[NT][NG];
+    started = true;
+    // weights (<= 4; 0 for a missing page) and the PV B operands
+    // p * scale_v * (16 or 4) in f16, page a then page b
+    v8h pbv[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      float pr[4];
+      float pr[2][4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        pr[v] = __builtin_amdgcn_exp2f(s_[t][v] - m_run[t]);   // <= 4
-        lsum[t] += pr[v];
-      }
+      for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
-      for (int gg = 0; gg < NG; ++gg) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) zacc[t][gg] = fmaf(pr[v], vz[v][gg], zacc[t][gg]);
-        pbv[t][gg] = as_v4h2(pack_f16(pr[0] * vsf[0][gg], pr[1] * vsf[1][gg]),
-                             pack_f16(pr[2] * vsf[2][gg], pr[3] * vsf[3][gg]));
-        corr[t][gg] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pbv[t][gg], corr[t][gg], 0, 0, 0);
-      }
+        for (int v = 0; v < 4; ++v) {
+          pr[pg][v] = __builtin_amdgcn_exp2f(sv[pg][t][v]);
+          lsum[t] += pr[pg][v];
+          zacc[t] = fmaf(pr[pg][v], vz[pg][v], zacc[t]);
+        }
+      pbv[t] = as_v8h(pack_f16(pr[0][0] * vsf[0][0], pr[0][1] * vsf[0][1]),
+                      pack_f16(pr[0][2] * vsf[0][2], pr[0][3] * vsf[0][3]),
+                      pack_f16(pr[1][0] * vsf[1][0], pr[1][1] * vsf[1][1]),
+                      pack_f16(pr[1][2] * vsf[1][2], pr[1][3] * vsf[1][3]));
+      corr[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pbv[t], corr[t], 0, 0, 0);
     }
-    // ---- PV: A = V codes of channels r16 + 16 sl, tokens (2g4, 2g4+8 | 2g4+1, 2g4+9) ----
+    // ---- PV: A = V codes of channel r16 + 16 sl, tokens (2g4, 2g4+8 | 2g4+1,
+    // 2g4+9) of page a, then of page b ----
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
-      const uint32_t x = __builtin_amdgcn_alignbit(sgi.vw[sl], sgi.vw[sl], rot);
-      const v4h av = as_v4h2((x & mlo) | f16one, (x & mhi) | f16one);
-      const int gg = (16 * sl) / G;
+      const uint32_t xa = __builtin_amdgcn_alignbit(sa.vw[sl], sa.vw[sl], rot);
+      const uint32_t xb = __builtin_amdgcn_alignbit(sb.vw[sl], sb.vw[sl], rot);
+      const v8h av = as_v8h((xa & mlo) | f16one, (xa & mhi) | f16one, (xb & mlo) | f16one,
+                            (xb & mhi) | f16one);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        acc[t][sl] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pbv[t][gg], acc[t][sl], 0, 0, 0);
+        acc[t][sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pbv[t], acc[t][sl], 0, 0, 0);
     }
   };
 
-  if (npg > 0) {
+  // ring of NSP pairs of pages (NSP - 1 pairs in flight)
+  constexpr int NSP = OSCAR_CAS_STAGES;
+  Stage st[NSP][2];
+  const int npair = (npg + 1) / 2;
+  if (npair > 0) {
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i) issue(st[i], i);
-    for (int i0 = 0; i0 < npg; i0 += NS) {
+    for (int i = 0; i < NSP - 1; ++i) {
+      issue(st[i][0], 2 * i);
+      issue(st[i][1], 2 * i + 1);
+    }
+    for (int i0 = 0; i0 < npair; i0 += NSP) {
 #pragma unroll
-      for (int s2 = 0; s2 < NS; ++s2) {
-        issue(st[(s2 + NS - 1) % NS], i0 + s2 + NS - 1);
-        if (i0 + s2 < npg) process(st[s2]);
+      for (int s2 = 0; s2 < NSP; ++s2) {
+        const int nx = i0 + s2 + NSP - 1;
+        issue(st[(s2 + NSP - 1) % NSP][0], 2 * nx);
+        issue(st[(s2 + NSP - 1) % NSP][1], 2 * nx + 1);
+        if (i0 + s2 < npair) process(st[s2][0], st[s2][1]);
       }
     }
   }
@@ -352,23 +397,27 @@ void k_int2_cascade(DecodeParams p) {
     float L = lsum[t];
     L += __shfl_xor(L, 16);
     L += __shfl_xor(L, 32);
-    float Z[NG];
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-      Z[gg] = zacc[t][gg];
-      Z[gg] += __shfl_xor(Z[gg], 16);
-      Z[gg] += __shfl_xor(Z[gg], 32);
+    float Z = zacc[t];
+    Z += __shfl_xor(Z, 16);
+    Z += __shfl_xor(Z, 32);
+    int b;
+    size_t bh;
+    if (!row_of(t, b, bh)) continue;
+    // this part's slot: after the parts of the sequence's earlier segments
+    int slot = part;
+    for (int i = 0; i < p.n_shared; ++i) {
+      const SharedSeg &o = p.shared[i];
+      if (b >= o.seq0 && b < o.seq0 + o.nseq && o.first < sg.first) slot += o.parts;
     }
-    if (!rv[t]) continue;
+    const size_t prow = bh * S + slot;
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
-      const int gg = (16 * sl) / G;
-      const v4f o = acc[t][sl] - corr[t][gg] + Z[gg];
-      *reinterpret_cast<v4f *>(po + prow[t] * D + 16 * sl + 4 * g4) = o;
+      const v4f o = acc[t][sl] - corr[t] + Z;
+      *reinterpret_cast<v4f *>(po + prow * D + 16 * sl + 4 * g4) = o;
     }
     if (g4 == 0) {
-      pml[prow[t] * 2 + 0] = m_run[t];
-      pml[prow[t] * 2 + 1] = L;
+      pml[prow * 2 + 0] = m_run[t];
+      pml[prow * 2 + 1] = L;
     }
   }
 }

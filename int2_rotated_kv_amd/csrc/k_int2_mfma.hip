@@ -244,7 +244,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     *skip = sk;
     return npg - sk;
   };
-  constexpr int kSegCost = 48;                    // units of a segment's fixed cost
+  constexpr int kSegCost = 128;                   // units of a segment's fixed cost
   auto &cum = lds.cum;                            // units before sequence b
   auto &pst = lds.pst;                            // unit of sequence b's first page
   auto &wsum = lds.wsum;

@@ -12,6 +12,7 @@
 namespace oscar {
 
 constexpr int kMergeRegChunks = 8;       // chunk rows per thread loaded up front
+constexpr int kMergeWideRows = 512;      // 1024-thread blocks below this many rows
 
 // Sum of RPT values per lane across the LPR lanes of a row group, folded so
 // that every exchange also halves the number of values: after log2(LPR) steps
@@ -43,8 +44,10 @@ __device__ __forceinline__ void fold_sum(float *v, int lane, int &base) {
 // issued first: the chunk (m, l) pairs (thread s holds chunk s), the first
 // kMergeRegChunks chunk rows of each row group, the thread's float4 of RPT
 // rows of R_v and the BF16 partials; the rest is shuffles and LDS exchanges.
-// NT = 1024 serves long chunk lists (a few sequences split many ways), 256
-// the rest.
+// NT = 1024 serves long chunk lists of a few (sequence, q head) rows (a
+// small batch split many ways), 256 the rest: with many rows, a longer list
+// is walked by the 256 threads in turn (a 1024-thread block per row costs
+// more in block turnover than the longer walk).
 template <int D, int NT>
 __global__ __launch_bounds__(NT) void k_merge(DecodeParams p, const float *__restrict__ Rv,
                                               float *__restrict__ out, float *__restrict__ lse) {
@@ -217,7 +220,8 @@ template <int D>
 static void launch_merge_d(const DecodeParams &p, const float *Rv, float *out, float *lse,
                            size_t lds, hipStream_t s) {
   const dim3 grid(p.B * p.Hq);
-  if (p.splits > 64) hipLaunchKernelGGL((k_merge<D, 1024>), grid, dim3(1024), lds, s, p, Rv, out, lse);
+  if (p.splits > 64 && p.B * p.Hq < kMergeWideRows)
+    hipLaunchKernelGGL((k_merge<D, 1024>), grid, dim3(1024), lds, s, p, Rv, out, lse);
   else hipLaunchKernelGGL((k_merge<D, 256>), grid, dim3(256), lds, s, p, Rv, out, lse);
 }
 
