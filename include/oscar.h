@@ -88,12 +88,11 @@ enum {
 
 /* Options of oscar_decode_attn / oscar_decode_step (bit mask). */
 enum {
-  OSCAR_FLAG_DETERMINISTIC = 1  /* the matrix-core INT2 kernel assigns history
-                                   pages to its waves statically instead of
-                                   from a shared counter, so a call's outputs
-                                   are bitwise the same on every run (the other
-                                   kernels always are); slower when the waves
-                                   of a compute unit progress unevenly        */
+  OSCAR_FLAG_DETERMINISTIC = 1  /* accepted and without effect: every kernel
+                                   assigns its work statically, so a call's
+                                   outputs are bitwise the same on every run
+                                   (and the fused step equals the separate
+                                   calls bit for bit)                          */
 };
 
 /* Which kernel computes the INT2 segment.  AUTO picks MFMA, which serves 1,
@@ -289,8 +288,9 @@ size_t oscar_decode_workspace_bytes(const oscar_cache *cache, const oscar_decode
  * [c*pages_per_split, (c+1)*pages_per_split) and empty chunks are dropped.
  * MFMA kernel: a chunk is one of num_splits equal parts of each sequence's
  * history.  One block of 16 waves serves one part for a pair of KV heads
- * (8 waves per head); the waves of a head take its pages in batches from a shared counter
- * and their results are combined into one partial per (q head, part).
+ * (8 waves per head); the waves of a head take fixed, interleaved batches of
+ * its pages and their results are combined in wave order into one partial per
+ * (q head, part).
  * Automatic chunking aims at 256 blocks (one per compute unit) while keeping
  * every part at least 2x its partial bytes and 8 pages per head;
  * pages_per_split is nominal.  An explicit num_splits is capped at the page

@@ -125,7 +125,6 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
     return fail(OSCAR_EINVAL, "int2_kernel must be 0, 1, 2 or 3");
   if (a->phases & ~(uint32_t)OSCAR_PHASE_ALL) return fail(OSCAR_EINVAL, "unknown phase bits");
   if (a->flags & ~(uint32_t)OSCAR_FLAG_DETERMINISTIC) return fail(OSCAR_EINVAL, "unknown flag bits");
-  p->deterministic = (a->flags & OSCAR_FLAG_DETERMINISTIC) != 0;
 
   p->B = a->batch;
   p->Hq = a->num_q_heads;

@@ -120,7 +120,6 @@ struct DecodeParams {
   int splits, pages_per_split;   // partial slots per (sequence, q head); nominal pages
   int mfma_parts;      // matrix-core kernel: blocks per head group = B * mfma_parts
   int mfma_balanced;   // matrix-core kernel: may balance blocks across sequences
-  int deterministic;   // matrix-core kernel: static page batches per wave
   const float *codebook;   // [Hkv][2][4] code levels (K, V) or nullptr = 0, 1, 2, 3
   // shared history pages (cascade): the partial slots of a sequence are first
   // its cascade slots (sum of `parts` over its segments, in page order), then

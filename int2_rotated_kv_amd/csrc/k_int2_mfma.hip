@@ -23,12 +23,13 @@
 //
 // One block of 16 waves covers 2 KV heads (8 waves per head) and an
 // equal share of the batch's history pages (one or more segments, see the
-// schedule below); the waves of a head take batches of 4 consecutive pages
-// of a segment from an LDS counter, since the SIMD arbiter favours older waves
-// and fixed page ranges per wave would finish unevenly, and the block combines
-// them into one partial per (q head, segment).  Each wave keeps 3 pages in
-// flight in a register ring.  The query operands (A words, exponents, group
-// sums) come from the workspace, written by the q rotation.  The running max
+// schedule below); the waves of a head take fixed, interleaved batches of 4
+// consecutive pages of a segment (a wave that falls behind its head's others
+// raises its issue priority, since the SIMD arbiter favours older waves), and
+// the block combines them in wave order into one partial per (q head,
+// segment): outputs are bitwise the same on every run.  Each wave keeps 3
+// pages in flight in a register ring.  The query operands (A words,
+// exponents, group sums) come from the workspace, written by the q rotation.  The running max
 // per head is lazy: it is raised (16-lane DPP reductions, rescale of the
 // partial sums) only when a logit exceeds it by more than 2 (log2 units), so
 // unnormalised weights stay below 4.  Serves 1, 2, 4 or 8 q heads per KV head
@@ -148,7 +149,7 @@ struct Int2Shared {
   int cum[kMaxBalancedBatch + 1];                 // work units before sequence b
   int pst[kMaxBalancedBatch];                     // unit where sequence b's pages start
   int wsum[kMfmaWaves];
-  int batch_ctr[8];                               // per head: next batch of the segment
+  int batch_ctr[8];                               // per head: batches its waves started
   int pid_lds[kPidCap];
   float qf_all[kMfmaWaves][GQ][D];                // per wave: its partial outputs at the end
   // per wave and code plane: w[plane][grp][head][slot]
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
 
   // page ids (the first kPidCap of a segment) are staged in LDS, so a batch's
   // ids are an LDS read away rather than a scalar-cache miss
-  auto &batch_ctr = lds.batch_ctr;             // per head: next batch of the segment
+  auto &batch_ctr = lds.batch_ctr;             // per head: batches its waves started
   auto &pid_lds = lds.pid_lds;
   auto &qf_all = lds.qf_all;                   // per wave: its partial outputs at the end
   auto &wbuf_all = lds.wbuf_all;               // per wave: w[grp][head][slot]
@@ -430,20 +431,24 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
     return ptab[k];
   };
 
-  // Work distribution: the WH waves of a head take batches of NB consecutive
-  // pages of the segment from that head's LDS counter, so waves the SIMD
-  // arbiter favours (older waves) take more pages and a head's waves finish
-  // together.  A batch is taken when its first page is about to be requested.
-  // With the deterministic option the k-th batch of the i-th wave of a head
-  // is batch i + WH*k of the segment: which pages a wave sums, and so every
-  // rounding, no longer depends on timing.
+  // Work distribution: the k-th batch of NB consecutive pages of the i-th
+  // wave of a head is batch i + WH*k of the segment, so which pages a wave
+  // sums, and so every rounding, is the same on every run.  The SIMD arbiter
+  // favours older waves, which would leave the younger ones finishing last;
+  // so a wave counts the batches its head's waves have started (an LDS
+  // counter, used for nothing else) and raises its issue priority while it
+  // is more than kPrioLag / WH batches behind their mean.  Priorities change
+  // only the timing.
+  constexpr int kPrioLag = 2;
   int ngrab = 0;                                  // batches this wave took (uniform)
   const int wih = w / HG;                         // this wave's index among its head's
   auto grab = [&]() -> int {                      // start page of the next batch
-    if (p.deterministic) return pbeg + (wih + WH * ngrab++) * NB;
     int v = 0;
-    if (lane == 0) v = atomicAdd(&batch_ctr[jl], NB);
-    return pbeg + __builtin_amdgcn_readfirstlane(v);
+    if (lane == 0) v = atomicAdd(&batch_ctr[jl], 1);
+    v = __builtin_amdgcn_readfirstlane(v);
+    if (v > WH * ngrab + kPrioLag) __builtin_amdgcn_s_setprio(2);
+    else __builtin_amdgcn_s_setprio(0);
+    return pbeg + (wih + WH * ngrab++) * NB;
   };
 
   auto issue = [&](Stage &sg, int phys) {      // wave-uniform phys
@@ -734,6 +739,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
     for (int k = 0; k < NBT; ++k) bq[k] = bq[k + NBT];
   }
+
+  __builtin_amdgcn_s_setprio(0);
 
   // ---------------- epilogue: one partial per (q head, segment) ----------------
   // each wave leaves its unnormalised output and (max, sum) per head in LDS

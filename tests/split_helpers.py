@@ -41,7 +41,7 @@ def hist_capacity_pages(L: int, steps: int) -> int:
 def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_splits=0,
                    R_v_none=False, head_map=None, device="cuda", seed_perm=None, fused=False,
                    flags=0, codebook=None, max_hist_len=None, extra_pages=0, noalloc=False,
-                   shared=None):
+                   shared=None, graph=False, on_step=None):
     """Build the initial split cache of every sequence, run `steps` decode steps
     (demote oldest recent -> write new token -> attend -> merge; with fused,
     through the single oscar_decode_step call, with noalloc through
@@ -49,7 +49,13 @@ def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_sp
     INT2 pool.  shared: [(first_page, num_pages, seq_begin, num_seqs)], whose
     member sequences' page tables then list seq_begin's physical pages there
     (their tokens must be equal: synth.share_history); passed to the decode
-    calls as oscar_shared_pages."""
+    calls as oscar_shared_pages.  graph: every step is one replay of a HIP
+    graph holding one oscar_decode_step, captured at the first step (its
+    arguments planned for max_hist_len or the lengths after the last step);
+    each step copies its slot lists, new token and query into the captured
+    buffers and the lengths into the cache first (every sequence must demote
+    at every step, so that the call's shape stays the same).  on_step(st,
+    out, lse) is called after each step with host copies."""
     import torch
     from int2_rotated_kv_amd import binding as ob
     from int2_rotated_kv_amd.splitcache import SplitCache
@@ -88,6 +94,45 @@ def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_sp
 
     out = torch.zeros((B, wl.Hq, wl.D), dtype=torch.float32, device=device)
     lse = torch.zeros((B, wl.Hq), dtype=torch.float32, device=device)
+    if graph:
+        assert all(L >= 320 for L in wl.lengths), "every sequence demotes at every step"
+        mh = int(sc.hist_len_h.max()) + steps if max_hist_len is None else max_hist_len
+        args = sc.decode_args(max_hist_len=mh, kv_head_of_q=head_map, num_splits=num_splits,
+                              int2_kernel=int2_kernel, flags=flags, shared=shared)
+        ws = ob.alloc_workspace(sc.cache, args, device=device)
+        bufs = None
+        g = None
+        for st in range(steps):
+            dsrc, ddst, wdst = sc.plan_step()
+            newk = np.stack([inp.K[b][wl.lengths[b] + st] for b in range(B)])
+            newv = np.stack([inp.V[b][wl.lengths[b] + st] for b in range(B)])
+            vals = [torch.from_numpy(x).to(device) for x in (dsrc, ddst, wdst)]
+            vals += [to_dev_bf16(newk).view(torch.int16), to_dev_bf16(newv).view(torch.int16),
+                     to_dev_bf16(inp.q[st]).view(torch.int16)]
+            if bufs is None:
+                bufs = [v.clone() for v in vals]
+            else:
+                for dst, v in zip(bufs, vals):
+                    dst.copy_(v)
+            sc.commit_step()
+            sc.sync_lengths()
+            d_src, d_dst, d_w, kn, vn, q = bufs
+            if g is None:
+                ob.decode(sc.cache, args, q, Rk, Rv, out, lse)      # warm-up, reads only
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    ob.decode_step(sc.cache, args, d_src, d_dst, ck, cv, d_w, kn, vn, q, Rk, Rv, ws, out, lse)
+                torch.cuda.synchronize()
+            out.fill_(float(st + 1))                                 # eager work between replays
+            lse.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if on_step is not None:
+                on_step(st, out.cpu().numpy(), lse.cpu().numpy())
+        return DeviceRun(sc, out.cpu().numpy(), lse.cpu().numpy(), sc.cache.int2.cpu().numpy(),
+                         sc.hist_len_h.copy(), sc.cache.bf16_k.cpu().numpy(), sc.cache.bf16_v.cpu().numpy(),
+                         sc.cache.read_status())
     for st in range(steps):
         dsrc, ddst, wdst = sc.plan_step()
         newk = np.stack([inp.K[b][wl.lengths[b] + st] for b in range(B)])
@@ -114,6 +159,9 @@ def build_and_step(inp: synth.SmallInputs, steps: int = 1, int2_kernel=1, num_sp
             ob.decode_step(sc.cache, args, d_src, d_dst, ck, cv, d_w, kn, vn, q, Rk, Rv, ws, out, lse)
         else:
             ob.decode(sc.cache, args, q, Rk, Rv, out, lse)
+        if on_step is not None:
+            torch.cuda.synchronize()
+            on_step(st, out.cpu().numpy(), lse.cpu().numpy())
     torch.cuda.synchronize()
     return DeviceRun(sc, out.cpu().numpy(), lse.cpu().numpy(), sc.cache.int2.cpu().numpy(),
                      sc.hist_len_h.copy(), sc.cache.bf16_k.cpu().numpy(), sc.cache.bf16_v.cpu().numpy(),
