@@ -136,10 +136,18 @@ enum {
                                      codebook coefficient magnitude) reached
                                      OSCAR_MFMA_V_SCALE_LIMIT: use
                                      OSCAR_INT2_VALU for this cache            */
-  OSCAR_STATUS_NONFINITE = 4      /* a rotated value, scale or zero point was
+  OSCAR_STATUS_NONFINITE = 4,     /* a rotated value, scale or zero point was
                                      inf or NaN (an inf/NaN input token, or
                                      values near the fp32 range): its codes,
                                      scale and zero are unspecified            */
+  OSCAR_STATUS_DEBUG_BOUNDS = 8   /* debug build only (liboscar_debug.so,
+                                     compiled with OSCAR_DEBUG): a kernel met
+                                     an index it otherwise clamps or skips
+                                     without a word - a page id outside the
+                                     pool, a history or BF16 length beyond its
+                                     bound, a demotion slot outside its pool -
+                                     or a merge row with more partial slots
+                                     than the workspace holds                  */
 };
 
 typedef struct {

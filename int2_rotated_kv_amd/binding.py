@@ -12,7 +12,9 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboscar.so")
+# OSCAR_LIB may name another build of the library (liboscar_debug.so: the
+# bounds-checking build); the default is the release build next to this file
+LIB_PATH = os.environ.get("OSCAR_LIB") or os.path.join(HERE, "liboscar.so")
 
 OSCAR_OK = 0
 OSCAR_EINVAL = -1
@@ -24,7 +26,7 @@ INT2_AUTO, INT2_VALU, INT2_MFMA, HISTORY_BF16 = 0, 1, 2, 3
 PHASE_QROT, PHASE_BF16, PHASE_INT2, PHASE_ALL = 1, 2, 4, 7
 FLAG_DETERMINISTIC = 1
 NOALLOC_WORKSPACE_BYTES = 16 << 20
-STATUS_CLIP_RANGE, STATUS_MFMA_V_RANGE, STATUS_NONFINITE = 1, 2, 4
+STATUS_CLIP_RANGE, STATUS_MFMA_V_RANGE, STATUS_NONFINITE, STATUS_DEBUG_BOUNDS = 1, 2, 4, 8
 MFMA_V_SCALE_LIMIT = 1023.0
 PAGE = 16
 SINK, RECENT = 64, 256

@@ -3,7 +3,10 @@
     python -m int2_rotated_kv_amd.build [--jobs N] [--debug]
 
 Every translation unit under csrc/ is compiled for gfx950 and linked into
-int2_rotated_kv_amd/liboscar.so next to this file.
+int2_rotated_kv_amd/liboscar.so next to this file.  With --debug the same
+sources are built with OSCAR_DEBUG (kernels report indices they would clamp
+or skip through the cache's status word, OSCAR_STATUS_DEBUG_BOUNDS) into
+liboscar_debug.so; the binding loads it when OSCAR_LIB names it.
 """
 from __future__ import annotations
 
@@ -20,6 +23,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liboscar.so")
+LIB_DEBUG = os.path.join(HERE, "liboscar_debug.so")
 
 ARCH = "gfx950"
 
@@ -43,7 +47,7 @@ def common_flags(debug: bool = False):
          # keep uniform-address atomics as written: the optimiser's lane
          # aggregation waits for each result right after issuing it
          "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
-    f += ["-O1", "-g"] if debug else ["-O3"]
+    f += ["-O2", "-g", "-DOSCAR_DEBUG"] if debug else ["-O3"]
     return f
 
 
@@ -52,8 +56,9 @@ def sources():
 
 
 def compile_one(src: str, debug: bool) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    bdir = os.path.join(BUILD, "debug") if debug else BUILD
+    os.makedirs(bdir, exist_ok=True)
+    obj = os.path.join(bdir, os.path.basename(src) + ".o")
     cmd = [hipcc()] + common_flags(debug) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -69,15 +74,16 @@ def build(jobs: int = 8, debug: bool = False, verbose: bool = True) -> str:
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(lambda s: compile_one(s, debug), srcs))
-    tmp = LIB + ".tmp"
+    lib = LIB_DEBUG if debug else LIB
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
-    return LIB
+        print(f"built {lib} from {len(srcs)} sources")
+    return lib
 
 
 def main(argv=None):

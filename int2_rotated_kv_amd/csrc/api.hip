@@ -149,6 +149,7 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   // INT2 kernel: the matrix-core one serves every supported ratio and reads
   // the cache faster than the vector-ALU one at each of them
   p->codebook = c->codebook;
+  p->status = c->status;
   int kind = a->int2_kernel;
   if (kind == OSCAR_INT2_AUTO) kind = OSCAR_INT2_MFMA;
   p->int2_kind = kind;

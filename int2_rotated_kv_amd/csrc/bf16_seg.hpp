@@ -57,6 +57,8 @@ __device__ __forceinline__ void bf16_seg_body(const DecodeParams &p, const uint1
   const int pgi = split * kBf16PagesPerSplit + w;     // page index in the table
   int T = p.bf16_len[b];
   const int64_t page = pgi < p.bf16_stride ? p.bf16_pages[(size_t)b * p.bf16_stride + pgi] : -1;
+  OSCAR_DCHECK(T >= 0 && T <= kMaxBf16, p.status);
+  OSCAR_DCHECK(pgi * kPage >= T || pgi >= p.bf16_stride || (page >= 0 && page < p.num_bf16_pages), p.status);
   const int ns = nt.slot != nullptr ? nt.slot[b] : -1;
   T = T < 0 ? 0 : T;
   T = T > kMaxBf16 ? kMaxBf16 : T;

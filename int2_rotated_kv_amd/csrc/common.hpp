@@ -81,6 +81,19 @@ struct SharedSeg {
   int block_base;        // first block of the segment in the cascade grid
 };
 
+// Debug build (OSCAR_DEBUG): report an index that a kernel clamps or skips
+// (it goes on as in the release build) through the status word.
+#ifdef OSCAR_DEBUG
+#define OSCAR_DCHECK(ok, status)                                                   \
+  do {                                                                            \
+    if (!(ok) && (status) != nullptr) atomicOr((status), (uint32_t)OSCAR_STATUS_DEBUG_BOUNDS); \
+  } while (0)
+#else
+#define OSCAR_DCHECK(ok, status) \
+  do {                           \
+  } while (0)
+#endif
+
 // Workspace partition used by decode_attn and merge.
 struct WsLayout {
   size_t qrot;      // fp32 [B][Hq][D]     q . R_k (unscaled)
@@ -121,6 +134,7 @@ struct DecodeParams {
   int mfma_parts;      // matrix-core kernel: blocks per head group = B * mfma_parts
   int mfma_balanced;   // matrix-core kernel: may balance blocks across sequences
   const float *codebook;   // [Hkv][2][4] code levels (K, V) or nullptr = 0, 1, 2, 3
+  uint32_t *status;        // the cache's sticky status word (debug-build checks) or nullptr
   // shared history pages (cascade): the partial slots of a sequence are first
   // its cascade slots (sum of `parts` over its segments, in page order), then
   // those of the matrix-core kernel, which skips the shared pages

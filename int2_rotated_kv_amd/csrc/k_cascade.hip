@@ -213,6 +213,7 @@ void k_int2_cascade(DecodeParams p) {
     const bool inr = i < npg;
     const int phys = __builtin_amdgcn_readlane(pt_cur, i & 63);
     const bool valid = phys >= 0 && phys < npool;
+    OSCAR_DCHECK(valid, p.status);
     sgi.ok = inr && valid;
     const uint8_t *rec = pool_j + (valid ? (size_t)phys : 0) * rec_stride;
     const __amdgpu_buffer_rsrc_t rs =

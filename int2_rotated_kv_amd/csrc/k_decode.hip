@@ -369,6 +369,7 @@ __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
   __syncthreads();
 
   int hl = p.hist_len[b];
+  OSCAR_DCHECK(hl >= 0 && hl <= p.max_hist_len && hl <= kPage * p.hist_stride, p.status);
   hl = hl < 0 ? 0 : hl;
   hl = hl > p.max_hist_len ? p.max_hist_len : hl;
   hl = hl > kPage * p.hist_stride ? kPage * p.hist_stride : hl;
@@ -389,6 +390,7 @@ __global__ __launch_bounds__(256) void k_int2_valu(DecodeParams p) {
 
   for (int pg = p0 + w; pg < p1; pg += 4) {
     const int phys = p.hist_pages[(size_t)b * p.hist_stride + pg];
+    OSCAR_DCHECK(phys >= 0 && phys < p.num_int2_pages, p.status);
     if (phys < 0 || phys >= p.num_int2_pages) continue;
     const uint8_t *rec = p.int2_pool + ((size_t)phys * p.Hkv + j) * RL.bytes();
     const int ntok = hl - pg * kPage < kPage ? hl - pg * kPage : kPage;

@@ -43,6 +43,9 @@ __global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
     int sv = -1, dv = -1;
     if (e < a.n) { sv = a.src[e]; dv = a.dst[e]; }
     // entries with a negative or out-of-range slot are skipped
+    // an entry is skipped by -1 in both lists
+    OSCAR_DCHECK((sv < 0 && dv < 0) || (sv >= 0 && dv >= 0 && (sv >> 4) < a.n_bf16_pages &&
+                                        (dv >> 4) < a.n_int2_pages), a.status);
     if (sv < 0 || dv < 0 || (sv >> 4) >= a.n_bf16_pages || (dv >> 4) >= a.n_int2_pages) {
       sv = -1;
       dv = -1;

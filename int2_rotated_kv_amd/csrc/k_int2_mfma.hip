@@ -231,6 +231,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   // or the batch is larger than the block, every block instead takes one of P
   // equal parts of one sequence (slot = part).
   auto clamp_len = [&](int v) {
+    OSCAR_DCHECK(v >= 0 && v <= p.max_hist_len && v <= kPage * p.hist_stride, p.status);
     v = v < 0 ? 0 : v;
     v = v > p.max_hist_len ? p.max_hist_len : v;
     return v > kPage * p.hist_stride ? kPage * p.hist_stride : v;
@@ -427,8 +428,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   auto page_id = [&](int k) -> int {
     if (k < pbeg || k >= pend) return -1;
     const int i = k - pbeg;
-    if (i < kPidCap) return __builtin_amdgcn_readfirstlane(pid_lds[i]);
-    return ptab[k];
+    const int id = i < kPidCap ? __builtin_amdgcn_readfirstlane(pid_lds[i]) : ptab[k];
+    OSCAR_DCHECK(id >= 0 && id < npool, p.status);
+    return id;
   };
 
   // Work distribution: the k-th batch of NB consecutive pages of the i-th

@@ -68,6 +68,8 @@ __global__ __launch_bounds__(NT) void k_merge(DecodeParams p, const float *__res
     const int b = (int)(bh / p.Hq);
     n = p.mfma_balanced ? reinterpret_cast<const int *>(p.ws + p.L.nslots)[b] : p.mfma_parts;
     if (p.n_shared > 0) n += cascade_slots(p, b, nullptr);
+    OSCAR_DCHECK(n <= S, p.status);
+    n = n < S ? n : S;
   }
   extern __shared__ float a_s[];               // [S] chunk weights 2^(m_s - M)
   __shared__ float4 red[NW][LPR];              // per-wave channel sums
