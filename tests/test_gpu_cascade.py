@@ -121,3 +121,53 @@ def test_shared_segments_rejected():
         with pytest.raises(ob.OscarError):
             ob.workspace_bytes(sc.cache, args)
     torch.cuda.synchronize()
+
+
+def _random_tree(seed):
+    """A seeded batch whose sequences share history pages as a prefix tree:
+    contiguous groups of the batch share a root prefix, and contiguous
+    subgroups of a group may share a continuation after it."""
+    rng = np.random.default_rng(3000 + seed)
+    D, G = [(128, 128), (64, 64)][seed % 2]
+    Hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([4, 8]))
+    B = int(rng.integers(3, 9))
+    lengths = [int(x) for x in rng.integers(900, 2600, B)]
+    pages = [(L - 320) // 16 for L in lengths]
+    segs = []
+    b = 0
+    while b < B:
+        n = int(rng.integers(2, B - b + 1)) if B - b >= 2 else 1
+        grp = list(range(b, b + n))
+        b += n
+        if n < 2:
+            continue
+        root = int(rng.integers(1, min(pages[i] for i in grp) + 1))
+        segs.append((0, root, grp[0], n))
+        if n >= 4:
+            k = int(rng.integers(2, n - 1))
+            for sub in (grp[:k], grp[k:]):
+                left = min(pages[i] for i in sub) - root
+                if len(sub) >= 2 and left > 0:
+                    segs.append((root, int(rng.integers(1, left + 1)), sub[0], len(sub)))
+    return dict(B=B, Hkv=Hkv, Hq=g * Hkv, D=D, G=G, lengths=tuple(lengths), seed=3100 + seed), segs
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_shared_pages_random_trees(seed):
+    """Seeded random prefix trees (group sizes, prefix and continuation
+    lengths, KV heads, 4 or 8 q heads per KV head, head_dim 64 or 128 with
+    one group per token): bytes exact and outputs within the bar against the
+    oracle, two steps through oscar_decode_step."""
+    from int2_rotated_kv_amd import binding as ob
+    kw, segs = _random_tree(seed)
+    _say(f"case: random shared tree {seed}: {kw}, segments {segs}")
+    if not segs:
+        pytest.skip("no group of two or more sequences drawn")
+    wl = synth.workload("tiny", steps=2, clip_set=synth.WIDE_CLIPS, **kw)
+    inp = synth.share_history(synth.make_small(wl, distinct_rv=True), segs)
+    ref = sh.oracle_step(inp, steps=2)
+    run = sh.build_and_step(inp, steps=2, int2_kernel=ob.INT2_MFMA, fused=True, shared=segs)
+    assert run.status == 0
+    w = _check(run, inp, ref)
+    _say(f"random tree {seed}: bytes exact, worst row rel err {w:.3e}")
