@@ -17,6 +17,7 @@ The default workload is the Qwen3-8B-shaped batch-32 cache at ~100K context
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -44,19 +45,28 @@ class BenchState:
 
 
 def build_workload(name: str, total_steps: int, device="cuda", log=print, bf16_history=False,
-                   codebook=False):
+                   codebook=False, group_size=0, q_heads=0):
     """Build the split cache of a 100K-class workload on the device and plan
     `total_steps` decode steps.  History pages are quantised by
     oscar_demote_pack from generated BF16 tokens.  With bf16_history, the same
     tokens are also laid out as the comparison cache: every history page kept
     in BF16 at its physical id (same page tables), the sink/recent pages after
     them.  With codebook ("fit" or "symmetric"), the cache uses the Lloyd-Max
-    codebook variant (seeded levels from synth.make_codebook)."""
+    codebook variant (seeded levels from synth.make_codebook).  group_size /
+    q_heads, when non-zero, replace the workload's G / Hq (the workload is then
+    named with them appended)."""
     import torch
     from int2_rotated_kv_amd import binding as ob
     from int2_rotated_kv_amd.splitcache import SplitCache
 
-    wl = synth.workload(name, steps=total_steps)
+    ov = {}
+    if group_size:
+        ov["G"] = group_size
+    if q_heads:
+        ov["Hq"] = q_heads
+    wl = synth.workload(name, steps=total_steps, **ov)
+    if ov:
+        wl = dataclasses.replace(wl, name=name + "".join(f"-{k}{v}" for k, v in sorted(ov.items())))
     gen = synth.LargeGen(wl, device=device)
     t0 = time.time()
     cb = synth.make_codebook(wl.seed, wl.Hkv, symmetric=codebook == "symmetric") if codebook else None
@@ -649,6 +659,10 @@ def main(argv=None):
                     help="use the Lloyd-Max codebook variant of the INT2 history (seeded levels; "
                          "'symmetric': levels symmetric about the middle of the range, whose "
                          "third code plane the matrix-core kernel skips)")
+    ap.add_argument("--group-size", type=int, default=0, metavar="G",
+                    help="replace the workload's quantisation group size (32, 64 or 128)")
+    ap.add_argument("--q-heads", type=int, default=0, metavar="HQ",
+                    help="replace the workload's number of q heads (a multiple of its KV heads)")
     ap.add_argument("--no-shared", action="store_true",
                     help="do not pass the shared-prefix pages to the library (every sequence then "
                          "reads its aliased pages on its own)")
@@ -678,7 +692,8 @@ def main(argv=None):
     torch.cuda.set_device(0)
     cold_steps = a.steps if a.cold else 0
     st = build_workload(a.workload, a.steps + a.warmup + breakdown_steps(a.steps) + 2 * cold_steps,
-                        log=log, bf16_history=not a.no_bf16_compare, codebook=a.codebook)
+                        log=log, bf16_history=not a.no_bf16_compare, codebook=a.codebook,
+                        group_size=a.group_size, q_heads=a.q_heads)
     wl = st.wl
     if a.no_shared:
         st.shared = []

@@ -233,7 +233,7 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   // history split.  Vector-ALU kernel: enough waves to fill the chip once (4
   // waves per (sequence, KV head, chunk)), each chunk streaming at least 8x
   // the bytes of its partial result (read and written once more by the merge)
-  // and 16 pages.  Matrix-core kernel: one block of kMfmaWaves waves per
+  // and 16 pages.  Matrix-core kernel: one block of 16 (or 8) waves per
   // (sequence, pair of KV heads, part), the pair's waves combining
   // their results into one partial per (q head, part); enough parts for one
   // block per compute unit, each part at least 2x its partial bytes and 8
@@ -270,7 +270,8 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   if (kind == OSCAR_INT2_MFMA) {
     // S parts per sequence on average; with the blocks balanced across
     // sequences one sequence may use up to 2S + 2 partial slots
-    p->mfma_balanced = a->batch > 1 && a->batch <= kMaxBalancedBatch &&
+    const int waves = mfma_waves(p->D, p->G, p->g == 8 ? 8 : 4, c->codebook != nullptr);
+    p->mfma_balanced = a->batch > 1 && a->batch <= mfma_max_balanced(waves) &&
                        (long long)a->batch * npages < (1LL << 31);
     int cap = 2 * S + 2;
     if (p->n_shared > 0 && npages > 0) {

@@ -13,12 +13,21 @@ constexpr int kPage = OSCAR_PAGE_TOKENS;
 constexpr int kMaxBf16 = OSCAR_MAX_BF16_TOKENS;
 constexpr int kBf16PagesPerSplit = 4;                              // one wave per page
 constexpr int kMaxSplits = 1024;        // history chunks per (sequence, KV head)
-#ifndef OSCAR_INT2_WAVES
-#define OSCAR_INT2_WAVES 16
-#endif
-constexpr int kMfmaWaves = OSCAR_INT2_WAVES;   // matrix-core INT2 kernel: waves per block
-constexpr int kMfmaTargetBlocks = 256;          // its default grid: one block per compute unit
-constexpr int kMaxBalancedBatch = 64 * kMfmaWaves;   // sequences it balances across (one per thread)
+constexpr int kMfmaTargetBlocks = 256;          // matrix-core INT2 kernel: default grid, one block per CU
+// Waves per block of the matrix-core INT2 kernel: 16 (four per SIMD, at most
+// 128 registers each), or 8 (two per SIMD, 256 registers) for the instances
+// whose page loop needs more than 128 registers: with D = 128 and G = 32
+// (four groups per token) at 8 q heads per KV head or with a codebook, and
+// with a codebook at 8 q heads per KV head and G = 32 or (D = 128) G = 64.
+// Spilled registers would be reloaded from scratch inside the page loop, and
+// each reload waits for every page load issued before it.  gq: 4 or 8, the q
+// heads of a wave (fewer than 4 per KV head use 4).
+__host__ __device__ constexpr int mfma_waves(int d, int g, int gq, bool cb) {
+  return ((d == 128 && g == 32 && (gq == 8 || cb)) || (cb && gq == 8 && (g == 32 || (d == 128 && g == 64))))
+             ? 8 : 16;
+}
+// sequences the kernel balances its blocks across (one per thread of a block)
+__host__ __device__ constexpr int mfma_max_balanced(int waves) { return 64 * waves; }
 // KV heads per block of the matrix-core INT2 kernel: 2 (1 for a single KV
 // head); the block's waves are split evenly over them.  Two heads per block
 // keep the partial results per (sequence, q head) few when a batch has only a

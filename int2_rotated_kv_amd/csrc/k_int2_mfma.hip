@@ -21,8 +21,9 @@
 //     shifted copies; A = w * 2^(8-b) in f16, so A * B = A + w * code / 4;
 //     fp32 accumulation; the A part is removed with sum_t A (same f16 values).
 //
-// One block of 16 waves covers 2 KV heads (8 waves per head) and an
-// equal share of the batch's history pages (one or more segments, see the
+// One block of 16 waves (8 for the instances that need more than 128
+// registers per wave, see mfma_waves) covers 2 KV heads (half the waves per
+// head each) and an equal share of the batch's history pages (one or more segments, see the
 // schedule below); the waves of a head take fixed, interleaved batches of 4
 // consecutive pages of a segment (a wave that falls behind its head's others
 // raises its issue priority, since the SIMD arbiter favours older waves), and
@@ -143,21 +144,21 @@ __device__ __forceinline__ void buf_words(uint32_t (&dst)[NW], __amdgpu_buffer_r
 
 constexpr int kPidCap = 1024;                   // page ids of a segment staged in LDS
 
-// LDS of the matrix-core kernel
-template <int D, int G, int GQ, int NP>
+// LDS of the matrix-core kernel (HB waves per block)
+template <int D, int G, int GQ, int NP, int HB>
 struct Int2Shared {
-  int cum[kMaxBalancedBatch + 1];                 // work units before sequence b
-  int pst[kMaxBalancedBatch];                     // unit where sequence b's pages start
-  int wsum[kMfmaWaves];
+  int cum[64 * HB + 1];                           // work units before sequence b
+  int pst[64 * HB];                               // unit where sequence b's pages start
+  int wsum[HB];
   int batch_ctr[8];                               // per head: batches its waves started
   int pid_lds[kPidCap];
-  float qf_all[kMfmaWaves][GQ][D];                // per wave: its partial outputs at the end
+  float qf_all[HB][GQ][D];                        // per wave: its partial outputs at the end
   // per wave and code plane: w[plane][grp][head][slot]
-  __align__(16) _Float16 wbuf_all[kMfmaWaves][NP][D / G][GQ][16];
-  float mlw[kMfmaWaves][GQ][2];
+  __align__(16) _Float16 wbuf_all[HB][NP][D / G][GQ][16];
+  float mlw[HB][GQ][2];
 };
-template <int D, int G, int GQ, bool CB>
-__global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
+template <int D, int G, int GQ, bool CB, int HB>
+__global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   constexpr RecLayout RL(D, G);
   constexpr int NG = D / G;            // groups per token
   constexpr int NBLK = D / 64;         // 64-channel blocks (one int8 MFMA K each)
@@ -165,11 +166,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   constexpr int NQK = NBLK * GPB;      // QK MFMAs per head quad per page
   constexpr int NH = D / 64;           // 64-channel halves of PV (lane owns l + 64*h2)
   constexpr int NQ = GQ / 4;           // head quads
-  constexpr int HB = kMfmaWaves;
   static_assert(GQ == 4 || GQ == 8, "one or two head quads (1, 2 or 4 q heads use one)");
 
   constexpr int NP = CB ? 3 : 1;       // code planes: the codes; with a codebook also b0, b0&b1
-  __shared__ Int2Shared<D, G, GQ, NP> lds;
+  __shared__ Int2Shared<D, G, GQ, NP, HB> lds;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave (uniform)
   // block = (group of HG KV heads, block index within the group); WH waves
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   auto &cum = lds.cum;                            // units before sequence b
   auto &pst = lds.pst;                            // unit of sequence b's first page
   auto &wsum = lds.wsum;
-  const bool scan = p.mfma_balanced != 0;         // B <= kMaxBalancedBatch and no overflow
+  const bool scan = p.mfma_balanced != 0;         // B <= 64 * HB and no overflow
   int T = 0, NB = 1;
   bool balanced = false;
   if (scan) {
@@ -809,18 +809,24 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_int2_mfma(DecodeParams p) {
   }  // segments
 }
 
-template <int D, int G>
-static void launch_mfma_dg(const DecodeParams &p, hipStream_t s) {
+template <int D, int G, int GQ, bool CB>
+static void launch_mfma_inst(const DecodeParams &p, hipStream_t s) {
   // B * mfma_parts blocks per group of KV heads (balanced across sequences
   // inside the kernel)
+  constexpr int HB = mfma_waves(D, G, GQ, CB);
   const int hg = mfma_heads_per_block(p.Hkv);
   const int ngrp = (p.Hkv + hg - 1) / hg;
-  const dim3 grid(p.B * ngrp * p.mfma_parts), blk(64 * kMfmaWaves);
+  const dim3 grid(p.B * ngrp * p.mfma_parts), blk(64 * HB);
+  hipLaunchKernelGGL((k_int2_mfma<D, G, GQ, CB, HB>), grid, blk, 0, s, p);
+}
+
+template <int D, int G>
+static void launch_mfma_dg(const DecodeParams &p, hipStream_t s) {
   const bool cb = p.codebook != nullptr;
-  if (p.g == 8 && cb) hipLaunchKernelGGL((k_int2_mfma<D, G, 8, true>), grid, blk, 0, s, p);
-  else if (p.g == 8) hipLaunchKernelGGL((k_int2_mfma<D, G, 8, false>), grid, blk, 0, s, p);
-  else if (cb) hipLaunchKernelGGL((k_int2_mfma<D, G, 4, true>), grid, blk, 0, s, p);
-  else hipLaunchKernelGGL((k_int2_mfma<D, G, 4, false>), grid, blk, 0, s, p);
+  if (p.g == 8 && cb) launch_mfma_inst<D, G, 8, true>(p, s);
+  else if (p.g == 8) launch_mfma_inst<D, G, 8, false>(p, s);
+  else if (cb) launch_mfma_inst<D, G, 4, true>(p, s);
+  else launch_mfma_inst<D, G, 4, false>(p, s);
 }
 
 hipError_t launch_int2_mfma(const DecodeParams &p, hipStream_t s) {

@@ -99,12 +99,14 @@ def test_qwen3_8b_32k_one_step(kernel):
 
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("D,G,Hq,Hkv", [(128, 128, 16, 2), (128, 32, 8, 2), (64, 64, 8, 1),
-                                       (128, 64, 4, 2), (128, 64, 4, 4), (64, 32, 6, 3)])
+                                       (128, 64, 4, 2), (128, 64, 4, 4), (64, 32, 6, 3),
+                                       (128, 32, 16, 2), (64, 32, 16, 2)])
 def test_shapes(kernel, D, G, Hq, Hkv):
     """Other head_dim / group / GQA shapes: G = 128 with 8 q heads per KV head
     (Qwen3-32B-shaped), G = 32 at D = 128, G = 64 at D = 64; 2 and 1 q heads
     per KV head (partly empty head quads on the matrix-core kernel), and 3 KV
-    heads with 2 q heads each; ragged history."""
+    heads with 2 q heads each; 8 q heads per KV head at G = 32 (at D = 128 the
+    matrix-core kernel runs it with 8 waves per block); ragged history."""
     _say("case: shape", D, G, Hq, Hkv, "kernel", kernel)
     wl = synth.workload("tiny", B=2, Hkv=Hkv, Hq=Hq, D=D, G=G, lengths=(1500, 2077), steps=1, seed=11)
     inp = synth.make_small(wl)
@@ -172,13 +174,15 @@ def test_fused_step_matches_separate_calls(shape, kernel):
     _check_out(fus, ref)
 
 
-@pytest.mark.parametrize("case", ["dominant_fallback", "dominant_balanced", "mixed_short", "batch_1025"])
+@pytest.mark.parametrize("case", ["dominant_fallback", "dominant_balanced", "mixed_short", "batch_1025",
+                                  "batch_512_8waves", "batch_513_8waves"])
 def test_block_balancing(case):
     """The matrix-core kernel's block schedule: blocks take equal ranges of the
     histories laid end to end (a block may cover several short sequences, a
     long sequence many blocks); when one sequence would need more than
     2*num_splits + 2 partial slots it falls back to equal parts per sequence;
-    batches above 1024 sequences always use parts."""
+    batches above one sequence per thread of a block (1024, or 512 for the
+    8-wave instances) always use parts."""
     _say("case: block balancing", case)
     if case.startswith("dominant"):
         wl = synth.workload("tiny", B=8, Hkv=2, Hq=8, D=128, G=64,
@@ -188,10 +192,17 @@ def test_block_balancing(case):
         wl = synth.workload("tiny", B=8, Hkv=2, Hq=8, D=128, G=64,
                             lengths=(2000, 330, 500, 340, 900, 1200, 321, 700), steps=1, seed=42)
         splits = 1
-    else:
+    elif case == "batch_1025":
         rng = np.random.default_rng(43)
         wl = synth.workload("tiny", B=1025, lengths=tuple(int(x) for x in rng.integers(300, 420, 1025)),
                             steps=1, seed=43)
+        splits = 0
+    else:
+        # D = 128, G = 32, 8 q heads per KV head: the 8-wave instance
+        n = 512 if case == "batch_512_8waves" else 513
+        rng = np.random.default_rng(44)
+        wl = synth.workload("tiny", B=n, Hkv=2, Hq=16, D=128, G=32,
+                            lengths=tuple(int(x) for x in rng.integers(300, 420, n)), steps=1, seed=44)
         splits = 0
     inp = synth.make_small(wl)
     run = sh.build_and_step(inp, steps=1, int2_kernel=2, num_splits=splits)
@@ -303,7 +314,7 @@ def test_bitwise_repeatable(shape):
 
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("shape", ["tiny", "d128g64", "d128g128", "d128g32", "d64g64g8", "d128g64sym",
-                                   "d128g64mixed"])
+                                   "d128g64mixed", "d128g32g8", "d128g64g8", "d64g32g8"])
 def test_codebook_variant(shape, kernel):
     """Lloyd-Max codebook variant: the prompt history quantised in bulk, then
     two decode steps (one-token demotion, attention on either INT2 kernel),
@@ -323,6 +334,11 @@ def test_codebook_variant(shape, kernel):
         wl = synth.workload("tiny", B=2, Hkv=2, Hq=16, D=128, G=128, lengths=(2500, 999), steps=2, seed=83)
     elif shape == "d128g32":
         wl = synth.workload("tiny", B=3, Hkv=2, Hq=8, D=128, G=32, lengths=(2000, 400, 1300), steps=2, seed=84)
+    elif shape in ("d128g32g8", "d128g64g8", "d64g32g8"):
+        # 8 q heads per KV head; the matrix-core kernel runs these with 8
+        # waves per block
+        D, G = {"d128g32g8": (128, 32), "d128g64g8": (128, 64), "d64g32g8": (64, 32)}[shape]
+        wl = synth.workload("tiny", B=3, Hkv=2, Hq=16, D=D, G=G, lengths=(2200, 500, 1400), steps=2, seed=86)
     else:
         wl = synth.workload("tiny", B=2, Hkv=2, Hq=16, D=64, G=64, lengths=(1800, 700), steps=2, seed=85)
     inp = synth.make_small(wl, distinct_rv=True)
