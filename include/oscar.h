@@ -98,12 +98,13 @@ enum {
 /* Which kernel computes the INT2 segment.  AUTO picks MFMA, which serves 1,
  * 2, 4 or 8 q heads per KV head (with 1 or 2 the head quads are partly empty;
  * it still reads the cache about 2.3 to 2.9 times faster than VALU there).
- * The MFMA kernel carries the PV weights p * scale_v * c * 2^(8-b) (p <= 4,
- * 2^(8-b) <= 16) in f16, so it needs every V group scale times the largest
- * codebook coefficient magnitude c (1 without a codebook; with one, the
- * largest of |L2 - L0|/2, |(L1 - L0) - (L2 - L0)/2| and |L3 - L2 - L1 + L0|,
- * each computed in fp32) to stay below OSCAR_MFMA_V_SCALE_LIMIT.  The
- * demotion paths check this for every group they write and set
+ * The MFMA kernel carries its PV operands in f16.  Without a codebook the
+ * weights are p * scale_v * 2^(8-b) (p <= 4, 2^(8-b) <= 16), so every V group
+ * scale must stay below OSCAR_MFMA_V_SCALE_LIMIT.  With a codebook the
+ * weights are p * scale_v and the V levels themselves (rounded to f16) are
+ * the other operand, so every V group scale times c = max(1, largest |V
+ * level|) / 16 must stay below the limit, and every |V level| below 16 times
+ * it.  The demotion paths check this for every group they write and set
  * OSCAR_STATUS_MFMA_V_RANGE in oscar_cache.status when it fails; the caller
  * must then ask for VALU, which has no such limit (its outputs over such a
  * cache are correct, the MFMA kernel's may be inf or NaN). */
@@ -117,8 +118,8 @@ enum {
                                rotation and oscar_merge ignores R_v            */
 };
 
-/* Largest V group scale (times the codebook coefficient, see above) that
- * the MFMA kernel's f16 PV weights hold: 16 * 4 * 1023 = 65472 < 65504. */
+/* Largest V group scale (times c with a codebook, see above) that the MFMA
+ * kernel's f16 PV weights hold: 16 * 4 * 1023 = 65472 < 65504. */
 #define OSCAR_MFMA_V_SCALE_LIMIT 1023.0f
 
 /* Bits of the sticky device status word oscar_cache.status.  The demotion
@@ -132,9 +133,9 @@ enum {
                                      written with scale 0, zero 0 and codes 0
                                      (the token reads back as 0) instead of
                                      from a clipped range                      */
-  OSCAR_STATUS_MFMA_V_RANGE = 2,  /* a V group scale (times the largest
-                                     codebook coefficient magnitude) reached
-                                     OSCAR_MFMA_V_SCALE_LIMIT: use
+  OSCAR_STATUS_MFMA_V_RANGE = 2,  /* a V group scale (times c with a
+                                     codebook) reached OSCAR_MFMA_V_SCALE_LIMIT,
+                                     or a V level its 16-fold: use
                                      OSCAR_INT2_VALU for this cache            */
   OSCAR_STATUS_NONFINITE = 4,     /* a rotated value, scale or zero point was
                                      inf or NaN (an inf/NaN input token, or
@@ -169,13 +170,14 @@ typedef struct {
                                 as the nearest level (thresholds at the
                                 midpoints, a tie to the lower level).  NULL =
                                 the uniform levels 0, 1, 2, 3.  Both INT2
-                                kernels read it (the matrix-core one with two
-                                more bit-plane contractions, or one when the
-                                b0&b1 coefficient ((L3 - L2) - L1) + L0,
-                                evaluated in fp32 in that order, is 0 for K
-                                and V of a KV head, as for levels symmetric
-                                about their middle).  Level order and
-                                finiteness are not checked (device memory) */
+                                kernels read it.  The matrix-core one runs QK
+                                on the codes and two more bit planes (one when
+                                the K b0&b1 coefficient ((L3 - L2) - L1) + L0,
+                                evaluated in fp32 in that order, is 0, as for
+                                levels symmetric about their middle) and PV
+                                on the V levels rounded to f16.  Level order
+                                and finiteness are not checked (device
+                                memory)                                      */
   uint32_t *status;          /* device word (4-byte aligned) or NULL: sticky
                                 OSCAR_STATUS_* bits set by the demotion paths
                                 (the calls that write records); NULL = not

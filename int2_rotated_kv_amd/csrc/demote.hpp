@@ -70,16 +70,21 @@ __device__ inline void clipped_range(float c, double mx, double mn, uint32_t &fl
   }
 }
 
-// Largest magnitude of the coefficients the matrix-core kernel multiplies a V
-// scale by: 1 for the uniform levels; with a codebook the b-plane
-// coefficients (L2 - L0)/2, (L1 - L0) - (L2 - L0)/2, L3 - L2 - L1 + L0, each
-// in fp32 as that kernel forms them.
+// Factor c of the matrix-core kernel's f16 PV range check on a V scale:
+// scale * c must stay below OSCAR_MFMA_V_SCALE_LIMIT.  Uniform levels: the
+// weights are p * scale * 2^(8-b) <= 64 * scale, c = 1.  Codebook: the
+// weights are p * scale <= 4 * scale and the V levels are f16 operands, c =
+// max(1, largest |level|) / 16; a level of magnitude 16 * limit or more (or
+// not finite) fails at any scale.
 __device__ inline float v_coef_max(const float *lv) {
   if (lv == nullptr) return 1.f;
-  const float cA = 0.5f * (lv[2] - lv[0]);
-  const float cB = (lv[1] - lv[0]) - cA;
-  const float cC = ((lv[3] - lv[2]) - lv[1]) + lv[0];
-  return fmaxf(fabsf(cA), fmaxf(fabsf(cB), fabsf(cC)));
+  float m = 1.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (!(fabsf(lv[k]) < 16.f * OSCAR_MFMA_V_SCALE_LIMIT)) return INFINITY;
+    m = fmaxf(m, fabsf(lv[k]));
+  }
+  return m * (1.f / 16.f);
 }
 
 // Status bits of one group's bf16 scale and zero (and, for V, the f16 range

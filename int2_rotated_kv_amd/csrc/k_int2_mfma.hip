@@ -145,7 +145,7 @@ __device__ __forceinline__ void buf_words(uint32_t (&dst)[NW], __amdgpu_buffer_r
 constexpr int kPidCap = 1024;                   // page ids of a segment staged in LDS
 
 // LDS of the matrix-core kernel (HB waves per block)
-template <int D, int G, int GQ, int NP, int HB>
+template <int D, int G, int GQ, int HB>
 struct Int2Shared {
   int cum[64 * HB + 1];                           // work units before sequence b
   int pst[64 * HB];                               // unit where sequence b's pages start
@@ -153,8 +153,8 @@ struct Int2Shared {
   int batch_ctr[8];                               // per head: batches its waves started
   int pid_lds[kPidCap];
   float qf_all[HB][GQ][D];                        // per wave: its partial outputs at the end
-  // per wave and code plane: w[plane][grp][head][slot]
-  __align__(16) _Float16 wbuf_all[HB][NP][D / G][GQ][16];
+  // per wave: the PV weights w[grp][head][slot]
+  __align__(16) _Float16 wbuf_all[HB][D / G][GQ][16];
   float mlw[HB][GQ][2];
 };
 template <int D, int G, int GQ, bool CB, int HB>
@@ -168,8 +168,8 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   constexpr int NQ = GQ / 4;           // head quads
   static_assert(GQ == 4 || GQ == 8, "one or two head quads (1, 2 or 4 q heads use one)");
 
-  constexpr int NP = CB ? 3 : 1;       // code planes: the codes; with a codebook also b0, b0&b1
-  __shared__ Int2Shared<D, G, GQ, NP, HB> lds;
+  constexpr int NP = CB ? 3 : 1;       // QK code planes: the codes; with a codebook also b0, b0&b1
+  __shared__ Int2Shared<D, G, GQ, HB> lds;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave (uniform)
   // block = (group of HG KV heads, block index within the group); WH waves
@@ -192,30 +192,39 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   const int j = live ? hg * HG + jl : 0;          // this wave's KV head
   const int r16 = lane & 15, kb = lane >> 4;      // row-in-16 and lane group
 
-  // Lloyd-Max codebook: the level of code c = b0 + 2*b1 is
+  // Lloyd-Max codebook.  QK: the level of code c = b0 + 2*b1 is
   //   L[c] = L0 + cA*c + cB*b0 + cC*b0*b1,
   //   cA = (L2 - L0)/2, cB = (L1 - L0) - cA, cC = L3 - L2 - L1 + L0,
-  // so each contraction runs on the codes (as without a codebook) and on the
-  // b0 and b0&b1 bit planes, weighted by cA, cB, cC; the L0 part joins the
-  // zero point.  Without a codebook cA = 1 and the planes are not formed.
+  // so the int8 contraction runs on the codes (as without a codebook) and on
+  // the b0 and b0&b1 bit planes, weighted by cA, cB, cC, and the L0 part
+  // joins the zero point.  PV: each code's V level itself, in f16, is looked
+  // up by byte permutes from a table of the 4 levels (their low bytes in one
+  // word, their high bytes in another), so PV runs once on the levels with the
+  // weights p * scale_v.  Without a codebook cA = 1 and no plane is formed.
   float kcA = 1.f, kcB = 0.f, kcC = 0.f, kL0 = 0.f;   // K levels
-  float vcA = 1.f, vcB = 0.f, vcC = 0.f, vL0 = 0.f;   // V levels
+  uint32_t vtab_lo = 0, vtab_hi = 0;                 // V levels in f16: low, high bytes
   if constexpr (CB) {
     const float *lk = p.codebook + j * 8, *lvv = lk + 4;
     kL0 = lk[0];
     kcA = 0.5f * (lk[2] - lk[0]);
     kcB = (lk[1] - lk[0]) - kcA;
     kcC = ((lk[3] - lk[2]) - lk[1]) + lk[0];
-    vL0 = lvv[0];
-    vcA = 0.5f * (lvv[2] - lvv[0]);
-    vcB = (lvv[1] - lvv[0]) - vcA;
-    vcC = ((lvv[3] - lvv[2]) - lvv[1]) + lvv[0];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const _Float16 h = (_Float16)lvv[k];
+      uint16_t hb;
+      __builtin_memcpy(&hb, &h, 2);
+      vtab_lo |= (uint32_t)(hb & 0xFF) << (8 * k);
+      vtab_hi |= (uint32_t)(hb >> 8) << (8 * k);
+    }
+    vtab_lo = __builtin_amdgcn_readfirstlane(vtab_lo);
+    vtab_hi = __builtin_amdgcn_readfirstlane(vtab_hi);
   }
-  // a symmetric codebook (L3 - L2 = L1 - L0 for K and V, as a Lloyd-Max fit
-  // of a symmetric distribution gives) has no b0&b1 term: its plane is
-  // skipped, which leaves every result bitwise the same (its weights and
-  // coefficients are 0); the test is uniform over the wave (one KV head)
-  const bool plane2 = CB && (kcC != 0.f || vcC != 0.f);
+  // a symmetric K codebook (L3 - L2 = L1 - L0, as a Lloyd-Max fit of a
+  // symmetric distribution gives) has no b0&b1 term: its QK plane is
+  // skipped, which leaves every result bitwise the same (its coefficient is
+  // 0); the test is uniform over the wave (one KV head)
+  const bool plane2 = CB && kcC != 0.f;
 
   // ---------------- schedule: this block's segments ----------------
   // The histories of the batch laid end to end, each sequence counted as its
@@ -481,7 +490,7 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   }
 
   float (*qf)[D] = qf_all[w];
-  _Float16 (*wbuf)[D / G][GQ][16] = wbuf_all[w];     // [plane][grp][head][slot]
+  _Float16 (*wbuf)[GQ][16] = wbuf_all[w];            // [grp][head][slot]
 
   // per-lane constants of the (head, token) layout of the QK result:
   // lane (kb, r16) holds head 4*qd + kb, token r16
@@ -527,14 +536,11 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   asm volatile("s_mov_b32 %0, 0xc000c0" : "=s"(m6));
   asm volatile("s_mov_b32 %0, 0x3000300" : "=s"(m8));
   asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(f16one));
-  uint32_t n4 = 0, n6 = 0, n8 = 0;             // one-bit masks of the codebook's planes
-  if constexpr (CB) {
-    asm volatile("s_mov_b32 %0, 0x100010" : "=s"(n4));
-    asm volatile("s_mov_b32 %0, 0x400040" : "=s"(n6));
-    asm volatile("s_mov_b32 %0, 0x1000100" : "=s"(n8));
-  }
-  const int pvs = pv_slot(r16);
-  const float pvf = pv_factor(r16);
+  // k slot of this lane's token in the PV A operands, and the A factor
+  // 2^(8-b) of its mantissa bit; with a codebook the slots of the level
+  // lookup (token t in slot 4 * (t % 4) + t / 4, no factor)
+  const int pvs = CB ? 4 * (r16 & 3) + (r16 >> 2) : pv_slot(r16);
+  const float pvf = CB ? 1.f : pv_factor(r16);
   constexpr float kLazy = 2.f;                 // log2 headroom of the running max
   float m_thr[NQ];
 #pragma unroll
@@ -659,66 +665,68 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
     for (int g2 = 0; g2 < NG; ++g2) {
       const float vs = bf16_lo(sg.sz[NG + g2]), vz = bf16_hi(sg.sz[NG + g2]);
-      // per plane the weight p * scale_v * coefficient; the codebook's L0
-      // part joins the zero point
-      float vsp[NP];
-      vsp[0] = CB ? vs * vcA : vs;
-      if constexpr (CB) {
-        vsp[1] = vs * vcB;
-        vsp[2] = vs * vcC;
-      }
-      const float vzl = CB ? fmaf(vL0, vs, vz) : vz;
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
-        zacc[qd][g2] = fmaf(pr[qd], vzl, zacc[qd][g2]);
-#pragma unroll
-        for (int pl = 0; pl < NP; ++pl) {
-          if (pl == 2 && !plane2) continue;
-          const _Float16 wh = (_Float16)(pa[qd] * vsp[pl]);
-          zacc[qd][g2] = fmaf(-4.f, (float)wh, zacc[qd][g2]);
-          wbuf[pl][g2][qd * 4 + kb][pvs] = wh;
-        }
+        zacc[qd][g2] = fmaf(pr[qd], vz, zacc[qd][g2]);
+        const _Float16 wh = (_Float16)(pa[qd] * vs);
+        // uniform codes: remove the implicit one of the f16 code values
+        if constexpr (!CB) zacc[qd][g2] = fmaf(-4.f, (float)wh, zacc[qd][g2]);
+        wbuf[g2][qd * 4 + kb][pvs] = wh;
       }
     }
     wave_lds_sync();
 
     // ---------------- PV on f16 MFMA, 4 token quads ----------------
-    // token t of a V word sits in bits 2t; B register u holds tokens (u, u+8)
-    // in its two halves at the mantissa bit given by pv_factor
-    // (codebook: the b0 plane keeps the low bit of each code, the b0&b1
-    // plane is the low bit of x0 & (x0 >> 1), both with one-bit masks)
-    uint32_t xs[NP][NH][3];                       // per plane the word and two shifted copies
-#pragma unroll
-    for (int h2 = 0; h2 < NH; ++h2) {
-      const uint32_t x0 = sg.c[NBLK + h2];
-#pragma unroll
-      for (int pl = 0; pl < NP; ++pl) {
-        const uint32_t y0 = pl == 2 ? x0 & (x0 >> 1) : x0;
-        xs[pl][h2][0] = y0;
-        xs[pl][h2][1] = y0 << 4;
-        xs[pl][h2][2] = y0 >> 6;
-      }
-    }
-    // B register u (tokens u, u+8): copy (x1 x1 x1 x0 x0 x2 x2 x2)[u], mask
-    // at mantissa bit (4 6 8 6 8 4 6 8)[u]
-    auto breg = [&](int pl, int h2, int u) -> uint32_t {
-      const uint32_t x = u < 3 ? xs[pl][h2][1] : u < 5 ? xs[pl][h2][0] : xs[pl][h2][2];
-      const int b = (u == 0 || u == 5) ? 4 : (u == 1 || u == 3 || u == 6) ? 6 : 8;
-      const uint32_t mk = pl == 0 ? (b == 4 ? m4 : b == 6 ? m6 : m8) : (b == 4 ? n4 : b == 6 ? n6 : n8);
-      return (x & mk) | f16one;
-    };
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
+    if constexpr (CB) {
+      // codebook: MFMA ti takes tokens ti, ti + 4, ti + 8, ti + 12 (token t
+      // of a V word sits in bits 2t); byte i of the selector is the code of
+      // token 4i + ti, the permutes give the low and the high bytes of the
+      // four tokens' f16 levels, and two more interleave them into f16 pairs
 #pragma unroll
       for (int h2 = 0; h2 < NH; ++h2) {
+        const uint32_t x0 = sg.c[NBLK + h2];
         const int g2 = (lane + 64 * h2) / G;
 #pragma unroll
-        for (int pl = 0; pl < NP; ++pl) {
-          if (pl == 2 && !plane2) continue;
-          const v4h bv = as_v4h(breg(pl, h2, 2 * ti), breg(pl, h2, 2 * ti + 1));
+        for (int ti = 0; ti < 4; ++ti) {
+          const uint32_t sel = (x0 >> (2 * ti)) & 0x03030303u;
+          const uint32_t lo = __builtin_amdgcn_perm(vtab_hi, vtab_lo, sel);
+          const uint32_t hi = __builtin_amdgcn_perm(vtab_lo, vtab_hi, sel);
+          const v4h bv = as_v4h(__builtin_amdgcn_perm(hi, lo, 0x05010400u),
+                                __builtin_amdgcn_perm(hi, lo, 0x07030602u));
 #pragma unroll
           for (int qd = 0; qd < NQ; ++qd) {
-            const uint2 u = *reinterpret_cast<const uint2 *>(&wbuf[pl][g2][qd * 4 + (lane & 3)][4 * ti]);
+            const uint2 u = *reinterpret_cast<const uint2 *>(&wbuf[g2][qd * 4 + (lane & 3)][4 * ti]);
+            acc[qd][h2] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_v4h(u.x, u.y), bv, acc[qd][h2], 0, 0, 0);
+          }
+        }
+      }
+    } else {
+      // token t of a V word sits in bits 2t; B register u holds tokens (u, u+8)
+      // in its two halves at the mantissa bit given by pv_factor
+      uint32_t xs[NH][3];                         // the word and two shifted copies
+#pragma unroll
+      for (int h2 = 0; h2 < NH; ++h2) {
+        const uint32_t x0 = sg.c[NBLK + h2];
+        xs[h2][0] = x0;
+        xs[h2][1] = x0 << 4;
+        xs[h2][2] = x0 >> 6;
+      }
+      // B register u (tokens u, u+8): copy (x1 x1 x1 x0 x0 x2 x2 x2)[u], mask
+      // at mantissa bit (4 6 8 6 8 4 6 8)[u]
+      auto breg = [&](int h2, int u) -> uint32_t {
+        const uint32_t x = u < 3 ? xs[h2][1] : u < 5 ? xs[h2][0] : xs[h2][2];
+        const int b = (u == 0 || u == 5) ? 4 : (u == 1 || u == 3 || u == 6) ? 6 : 8;
+        return (x & (b == 4 ? m4 : b == 6 ? m6 : m8)) | f16one;
+      };
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+        for (int h2 = 0; h2 < NH; ++h2) {
+          const int g2 = (lane + 64 * h2) / G;
+          const v4h bv = as_v4h(breg(h2, 2 * ti), breg(h2, 2 * ti + 1));
+#pragma unroll
+          for (int qd = 0; qd < NQ; ++qd) {
+            const uint2 u = *reinterpret_cast<const uint2 *>(&wbuf[g2][qd * 4 + (lane & 3)][4 * ti]);
             acc[qd][h2] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_v4h(u.x, u.y), bv, acc[qd][h2], 0, 0, 0);
           }
         }
@@ -772,7 +780,8 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
           const float zg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Z[g2]), 16 * i));
           zz = (c / G == g2) ? zg : zz;
         }
-        qf[qd * 4 + i][c] = 4.f * acc[qd][h2][i] + zz;
+        // uniform codes: the f16 code values carry a factor 1/4
+        qf[qd * 4 + i][c] = (CB ? 1.f : 4.f) * acc[qd][h2][i] + zz;
       }
     }
   }

@@ -143,21 +143,22 @@ def _v_range_inputs(v_range: float, seed: int):
 
 def _expected_v_flag(ref, codebook=None):
     """OSCAR_STATUS_MFMA_V_RANGE as the header defines it: some V group's bf16
-    scale times the largest codebook coefficient magnitude (1 without a
-    codebook; fp32 as written there) reaches OSCAR_MFMA_V_SCALE_LIMIT."""
+    scale times c reaches OSCAR_MFMA_V_SCALE_LIMIT, c = 1 without a codebook
+    and max(1, largest |V level|) / 16 with one (fp32), or a V level reaches
+    16 times the limit."""
     from int2_rotated_kv_amd import binding as ob
+    lim = np.float32(ob.MFMA_V_SCALE_LIMIT)
     flag = False
     for r in ref.values():
         for j in range(r["vs"].shape[1]):
             cm = np.float32(1.0)
             if codebook is not None:
-                L = codebook[j, 1].astype(np.float32)
-                cA = np.float32(0.5) * (L[2] - L[0])
-                cB = (L[1] - L[0]) - cA
-                cC = ((L[3] - L[2]) - L[1]) + L[0]
-                cm = max(abs(cA), abs(cB), abs(cC))
+                L = np.abs(codebook[j, 1].astype(np.float32))
+                if np.any(L >= np.float32(16.0) * lim):
+                    return True
+                cm = max(np.float32(1.0), L.max()) * np.float32(1.0 / 16.0)
             prod = r["vs"][:, j].astype(np.float32) * np.float32(cm)
-            flag |= bool(np.any(prod >= np.float32(ob.MFMA_V_SCALE_LIMIT)))
+            flag |= bool(np.any(prod >= lim))
     return flag
 
 
@@ -184,9 +185,10 @@ def test_v_scales_above_mfma_limit():
     """V group scales up to ~1260: the demotion sets OSCAR_STATUS_MFMA_V_RANGE
     (written both by the bulk path and the decode step's demotion), and the
     vector-ALU kernel, which the status word tells the caller to use, is
-    within the bar.  With a Lloyd-Max codebook whose largest V coefficient is
-    below 0.8 the same scales fit the f16 weights: no bit, and the
-    matrix-core kernel is within the bar too."""
+    within the bar.  With a Lloyd-Max codebook the matrix-core kernel's
+    weights are p * scale_v (its levels below 2.7 are the f16 operand), so the
+    same scales fit: no bit, and the matrix-core kernel is within the bar
+    too."""
     from int2_rotated_kv_amd import binding as ob
     _say("case: V scales above the MFMA limit")
     inp = _v_range_inputs(2000.0, 322)
@@ -265,3 +267,24 @@ def test_nonfinite_token_flagged():
     cache.clear_status()
     ob.demote_pack(cache, src[10:11], src[10:11], Rk, Rv, ck, cv)  # one-token path
     assert cache.read_status() == ob.STATUS_NONFINITE
+
+
+@pytest.mark.parametrize("v_range,flag", [(8000.0, False), (12500.0, True)])
+def test_v_scales_codebook_limit(v_range, flag):
+    """With a codebook (levels below 2.7) the limit sits at V scales of about
+    1023 * 16 / 2.7: scales up to ~5000 fit (no bit, the matrix-core kernel
+    within the bar), scales up to ~7900 set OSCAR_STATUS_MFMA_V_RANGE (the
+    vector-ALU kernel within the bar)."""
+    from int2_rotated_kv_amd import binding as ob
+    _say("case: codebook V scales, range", v_range)
+    inp = _v_range_inputs(v_range, 323)
+    cb = synth.make_codebook(323, inp.wl.Hkv)
+    ref = sh.oracle_step(inp, steps=1, R_v_none=True, codebook=cb)
+    assert _expected_v_flag(ref, cb) == flag
+    kernel = 1 if flag else 2
+    run = sh.build_and_step(inp, steps=1, int2_kernel=kernel, R_v_none=True, codebook=cb)
+    assert run.status == (ob.STATUS_MFMA_V_RANGE if flag else 0), f"status {run.status}"
+    _check_bytes(run, inp, ref)
+    w = _check_out(run, ref)
+    vmax = max(float(r["vs"].max()) for r in ref.values())
+    _say(f"largest V scale {vmax}: status {run.status}, worst row rel err {w:.3e}")
