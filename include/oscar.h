@@ -191,9 +191,9 @@ typedef struct {
  * seq_begin + num_seqs - 1 list the same physical INT2 pages at logical
  * history pages first_page .. first_page + num_pages - 1 (the pages are read
  * from sequence seq_begin's table), and each of those pages holds 16 tokens
- * for every one of them.  With the matrix-core INT2 kernel (AUTO or MFMA) and
- * one group per token (G == D), the pages are attended once for all the
- * sequences' q heads
+ * for every one of them.  With the matrix-core INT2 kernel (AUTO or MFMA),
+ * one group per token (G == D) and uniform codes (no codebook), the pages are
+ * attended once for all the sequences' q heads
  * (up to num_seqs x Hq/Hkv query rows per KV head) and the result is merged
  * with each sequence's own pages; otherwise every sequence reads them as its
  * own.  The segments of one sequence must tile its first history pages:

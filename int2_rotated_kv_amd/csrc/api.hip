@@ -156,7 +156,8 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
 
   // shared history pages: validated whatever kernel runs; attended once for
   // all their sequences (cascade) with the matrix-core kernel when a token's
-  // channels form one group (G == D)
+  // channels form one group (G == D) and the codes are uniform (the cascade
+  // has no codebook path: with one, every sequence reads its pages itself)
   if (a->num_shared < 0 || a->num_shared > OSCAR_MAX_SHARED)
     return fail(OSCAR_EINVAL, "num_shared must be in [0, %d] (got %d)", OSCAR_MAX_SHARED,
                 a->num_shared);
@@ -196,7 +197,8 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   p->n_shared = 0;
   p->cas_slots = 0;
   p->cas_blocks = 0;
-  if (a->num_shared > 0 && kind == OSCAR_INT2_MFMA && c->group_size == c->head_dim) {
+  if (a->num_shared > 0 && kind == OSCAR_INT2_MFMA && c->group_size == c->head_dim &&
+      c->codebook == nullptr) {
     // page ranges of about equal size so that the grid holds ~2 blocks per
     // compute unit (as many as fit at once), each at least kCasMinPages pages
     // (its partials, written and read back, stay well below the pages' bytes)

@@ -171,3 +171,22 @@ def test_shared_pages_random_trees(seed):
     assert run.status == 0
     w = _check(run, inp, ref)
     _say(f"random tree {seed}: bytes exact, worst row rel err {w:.3e}")
+
+
+def test_shared_pages_with_codebook():
+    """A Lloyd-Max codebook cache with shared pages: the cascade has no
+    codebook path, so every sequence reads its shared pages itself; bytes
+    exact and outputs within the bar against the oracle (which uses the
+    levels), through the separate calls and oscar_decode_step."""
+    from int2_rotated_kv_amd import binding as ob
+    kw, segs = CASES["d128_tree"]
+    _say("case: shared pages with a codebook")
+    wl = synth.workload("tiny", steps=2, **kw)
+    inp = synth.share_history(synth.make_small(wl, distinct_rv=True), segs)
+    cb = synth.make_codebook(wl.seed, wl.Hkv)
+    ref = sh.oracle_step(inp, steps=2, codebook=cb)
+    for fused in (False, True):
+        run = sh.build_and_step(inp, steps=2, int2_kernel=ob.INT2_AUTO, fused=fused, shared=segs, codebook=cb)
+        assert run.status == 0
+        w = _check(run, inp, ref)
+        _say(f"codebook with shared pages, fused {fused}: bytes exact, worst row rel err {w:.3e}")
