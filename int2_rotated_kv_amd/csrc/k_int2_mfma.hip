@@ -408,8 +408,7 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
 #define OSCAR_INT2_BATCH 4
 #endif
   constexpr int NS = OSCAR_INT2_STAGES;   // pages in the register ring (NS-1 in flight)
-  constexpr int NB = OSCAR_INT2_BATCH;    // pages per batch taken from a head's counter
-  constexpr int NBT = NS / NB;            // batches per pass over the ring
+  constexpr int NB = OSCAR_INT2_BATCH;    // pages per batch of a wave
   static_assert(NS % NB == 0, "the ring holds whole batches");
   constexpr int SW = D / 32;             // words of a lane slot: NBLK K words, NH V words
   struct Stage {
@@ -423,7 +422,7 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   // one never drains the ring
   using cint32 = const __attribute__((address_space(4))) int32_t;
   cint32 *ptab = (cint32 *)(p.hist_pages + (size_t)b * p.hist_stride);
-  const size_t rec_stride = (size_t)p.Hkv * RL.bytes();
+  const uint32_t rec_stride = (uint32_t)p.Hkv * (uint32_t)RL.bytes();   // bytes per page
   const uint8_t *pool_j = p.int2_pool + (size_t)j * RL.bytes();
 
   // per-lane byte offsets inside a record: lane slot `lane` (= 16*kb + r16)
@@ -432,41 +431,57 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   const uint32_t off_sz = (uint32_t)RL.tok_sz(r16);
   const int npool = p.num_int2_pages < 0x7fffffff ? (int)p.num_int2_pages : 0x7fffffff;
 
-  // page id of history page k (wave-uniform); pages outside [pbeg, pend) are
-  // -1 and the table is never read there
+  // page id of history page k in [pbeg, pend) (wave-uniform; the callers
+  // ask only for the pages of a wave's positions)
   auto page_id = [&](int k) -> int {
-    if (k < pbeg || k >= pend) return -1;
     const int i = k - pbeg;
     const int id = i < kPidCap ? __builtin_amdgcn_readfirstlane(pid_lds[i]) : ptab[k];
     OSCAR_DCHECK(id >= 0 && id < npool, p.status);
     return id;
   };
 
-  // Work distribution: the k-th batch of NB consecutive pages of the i-th
-  // wave of a head is batch i + WH*k of the segment, so which pages a wave
-  // sums, and so every rounding, is the same on every run.  The SIMD arbiter
-  // favours older waves, which would leave the younger ones finishing last;
-  // so a wave counts the batches its head's waves have started (an LDS
-  // counter, used for nothing else) and raises its issue priority while it
-  // is more than kPrioLag / WH batches behind their mean.  Priorities change
-  // only the timing.
+  // Work distribution: the n pages of the segment are dealt out as whole
+  // rounds of batches of NB consecutive pages (the k-th batch of the i-th
+  // wave of a head is batch i + WH*k), then the pages left after the last
+  // whole round (fewer than WH*NB) one at a time (page i, i + WH, ... of the
+  // rest), so that no wave of a short segment has a whole batch more than
+  // another.  Which pages a wave sums, and so every rounding, is the same on
+  // every run.  The SIMD arbiter favours older waves, which would leave the
+  // younger ones finishing last; so every NB pages a wave counts the pages
+  // its head's waves have started, in batches (an LDS counter, used for
+  // nothing else), and raises its issue priority while it is more than
+  // kPrioLag / WH batches behind their mean.  Priorities change only the
+  // timing.
   constexpr int kPrioLag = 2;
-  int ngrab = 0;                                  // batches this wave took (uniform)
+  int ngrab = 0;                                  // batches this wave started (uniform)
   const int wih = w / HG;                         // this wave's index among its head's
-  auto grab = [&]() -> int {                      // start page of the next batch
+  auto prio_tick = [&]() {
     int v = 0;
     if (lane == 0) v = atomicAdd(&batch_ctr[jl], 1);
     v = __builtin_amdgcn_readfirstlane(v);
     if (v > WH * ngrab + kPrioLag) __builtin_amdgcn_s_setprio(2);
     else __builtin_amdgcn_s_setprio(0);
-    return pbeg + (wih + WH * ngrab++) * NB;
+    ++ngrab;
+  };
+  const int nseg = pend - pbeg;                   // this head's pages (0 for a wave without one)
+  const int full = nseg / (WH * NB) * (WH * NB);  // pages in whole rounds of batches
+  const int rpos = full / WH;                     // this wave's positions in them (a multiple of NB)
+  const int ntail = nseg - full;
+  const int npos = rpos + (ntail > wih ? (ntail - wih + WH - 1) / WH : 0);   // positions of this wave
+  // pages of successive positions (uniform): +1 inside a batch, to the
+  // wave's next batch at a batch start, then the single pages WH apart
+  const int jump = (WH - 1) * NB + 1;
+  const int tail0 = pbeg + full + wih;            // page of position rpos
+  auto next_page = [&](int t, int pg, bool batch_start) -> int {   // page of position t after pg
+    return t < rpos ? (batch_start ? pg + jump : pg + 1) : (t == rpos ? tail0 : pg + WH);
   };
 
   auto issue = [&](Stage &sg, int phys) {      // wave-uniform phys
-    sg.ok = phys >= 0 && phys < npool;
+    // a negative id is a large unsigned one: one compare checks both ends
+    sg.ok = (uint32_t)phys < (uint32_t)npool;
     // out-of-range stages still load (from page 0) so every lane issues the
     // same load sequence; their data is never used
-    const uint8_t *rec = pool_j + (sg.ok ? (size_t)phys : 0) * rec_stride;
+    const uint8_t *rec = pool_j + (uint64_t)(sg.ok ? (uint32_t)phys : 0u) * rec_stride;
     // one record as a buffer resource (word 3: 32-bit data format, required
     // non-zero for buffer loads on this family); reads past it return 0
     const __amdgpu_buffer_rsrc_t rs =
@@ -475,17 +490,18 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
     buf_words<2 * NG>(sg.sz, rs, off_sz);
   };
 
-  // batch starts: bq[0 .. NBT-1] are processed in the current pass over the
-  // ring, bq[NBT ..] are taken during it; pages of the wave's sequence of
-  // batches go to ring slots in order, NS - 1 requests ahead of processing
-  int bq[2 * NBT];
-#pragma unroll
-  for (int k = 0; k < 2 * NBT; ++k) bq[k] = pend;
-  if (pend > pbeg) {
+  // the wave's positions go to ring slots in order, NS - 1 requests ahead of
+  // processing; a position past npos loads nothing that is used.  ipg is the
+  // page of the next position to request, pgr[slot] the page a stage holds.
+  int ipg = rpos > 0 ? pbeg + wih * NB : tail0;
+  int pgr[NS];
+  if (npos > 0) {
 #pragma unroll
     for (int idx = 0; idx < NS - 1; ++idx) {
-      if (idx % NB == 0) bq[idx / NB] = grab();
-      issue(st[idx], page_id(bq[idx / NB] + idx % NB));
+      if (idx % NB == 0) prio_tick();
+      pgr[idx] = ipg;
+      issue(st[idx], idx < npos ? page_id(ipg) : -1);
+      ipg = next_page(idx + 1, ipg, (idx + 1) % NB == 0);
     }
   }
 
@@ -546,9 +562,12 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) m_thr[qd] = -INFINITY;
 
-  auto process = [&](Stage &sg, int pg) {          // pg: history page index
+  // the sequence's last page when it is partial (else -1), and its tokens
+  const int tail_pg = (hl & (kPage - 1)) ? hl / kPage : -1;
+  const int tail_n = hl & (kPage - 1);
+  auto process = [&](Stage &sg, int pg) {          // pg: history page index (< ceil(hl / 16))
     if (!sg.ok) return;
-    const int ntok = hl - pg * kPage < kPage ? hl - pg * kPage : kPage;
+    const int ntok = pg == tail_pg ? tail_n : kPage;
     // tokens past the history length (only on a sequence's last, partial page):
     // logit -inf and (scale, zero) read as 0, since unwritten record bytes may
     // hold any bit pattern
@@ -735,19 +754,18 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
     wave_lds_sync();
   };
 
-  // each step requests the page NS - 1 ahead (taking a new batch when that
-  // page starts one) and processes one; a batch past the segment is empty
-  while (bq[0] < pend) {
+  // each step requests the position NS - 1 ahead and processes one
+  for (int t0 = 0; t0 < npos; t0 += NS) {
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2) {
-      const int idx = s2 + NS - 1;                // request position in this pass
-      if (idx % NB == 0) bq[idx / NB] = grab();
-      issue(st[(s2 + NS - 1) % NS], page_id(bq[idx / NB] + idx % NB));
-      const int cur = bq[s2 / NB] + s2 % NB;
-      if (cur < pend) process(st[s2], cur);
+      const int idx = t0 + s2 + NS - 1;           // request position (t0 is a multiple of NB)
+      const int slot = (s2 + NS - 1) % NS;
+      if ((s2 + NS - 1) % NB == 0) prio_tick();
+      pgr[slot] = ipg;
+      issue(st[slot], idx < npos ? page_id(ipg) : -1);
+      ipg = next_page(idx + 1, ipg, (s2 + NS) % NB == 0);
+      if (t0 + s2 < npos) process(st[s2], pgr[s2]);
     }
-#pragma unroll
-    for (int k = 0; k < NBT; ++k) bq[k] = bq[k + NBT];
   }
 
   __builtin_amdgcn_s_setprio(0);
