@@ -322,6 +322,33 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   auto &wbuf_all = lds.wbuf_all;               // per wave: w[grp][head][slot]
   auto &mlw = lds.mlw;
 
+  // the query operands (prepared with the q rotation), requested as soon as
+  // a segment's sequence is known, before its length and page ids: A words of
+  // the wave's head quads, and per q head its exponent and group sums
+  // (wave-uniform scalar loads)
+  v4i aq[NQ][NQK];
+  int qe_h[GQ];
+  float qz_h[GQ][NG];
+  auto load_query = [&](int b) {
+    const v4i *qpk = reinterpret_cast<const v4i *>(p.ws + p.L.qpk) +
+                     ((size_t)b * p.Hkv + j) * NQ * NQK * 64 + lane;
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+      for (int m = 0; m < NQK; ++m) aq[qd][m] = qpk[(qd * NQK + m) * 64];
+    using cf32 = const __attribute__((address_space(4))) float;
+    cf32 *qhd = (cf32 *)(p.ws + p.L.qhd);
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      // with fewer than GQ q heads per KV head the missing heads' A rows are
+      // zero; their per-head constants are taken from head 0 and never used
+      cf32 *hd = qhd + ((size_t)b * p.Hq + p.q_of_kv[j * p.g + (h < p.g ? h : 0)]) * 8;
+      qe_h[h] = __float_as_int(hd[0]);
+#pragma unroll
+      for (int g2 = 0; g2 < NG; ++g2) qz_h[h][g2] = hd[1 + g2];
+    }
+  };
+
   for (;;) {
   // ---------------- next segment: sequence b, its pages [pbeg, pend) ----------------
   int b, pbeg, pend_all, slot;
@@ -332,6 +359,7 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
       ++bseg;
     if (bseg >= p.B || ib >= NB || cum[bseg] >= g1) break;
     b = bseg++;
+    load_query(b);
     const long long lo = pst[b] > g0 ? pst[b] : g0;
     const long long hi = cum[b + 1] < g1 ? cum[b + 1] : g1;
     pbeg = (int)(lo - pst[b]);
@@ -341,6 +369,7 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
     if (fallback_done || bseg >= p.B || P == 0) break;
     fallback_done = true;
     b = bseg;
+    load_query(b);
     const int part = ib % P;
     int sk;
     const int npg = own_pages(b, &sk);
@@ -367,35 +396,6 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
     const int32_t *tab = p.hist_pages + (size_t)b * p.hist_stride + pbeg;
     for (int i = threadIdx.x; i < n; i += 64 * HB) pid_lds[i] = tab[i];
   }
-  // the query operands (prepared with the q rotation) are requested before
-  // the staging barrier: A words of the wave's head quads, and per q head its
-  // exponent and group sums (wave-uniform scalar loads)
-  v4i aq[NQ][NQK];
-  {
-    const v4i *qpk = reinterpret_cast<const v4i *>(p.ws + p.L.qpk) +
-                     ((size_t)b * p.Hkv + j) * NQ * NQK * 64 + lane;
-#pragma unroll
-    for (int qd = 0; qd < NQ; ++qd)
-#pragma unroll
-      for (int m = 0; m < NQK; ++m) aq[qd][m] = qpk[(qd * NQK + m) * 64];
-  }
-  int qe_h[GQ];
-  float qz_h[GQ][NG];
-  {
-    using cf32 = const __attribute__((address_space(4))) float;
-    cf32 *qhd = (cf32 *)(p.ws + p.L.qhd);
-#pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      // with fewer than GQ q heads per KV head the missing heads' A rows are
-      // zero; their per-head constants are taken from head 0 and never used
-      cf32 *hd = qhd + ((size_t)b * p.Hq + p.q_of_kv[j * p.g + (h < p.g ? h : 0)]) * 8;
-      qe_h[h] = __float_as_int(hd[0]);
-#pragma unroll
-      for (int g2 = 0; g2 < NG; ++g2) qz_h[h][g2] = hd[1 + g2];
-    }
-  }
-  if (threadIdx.x < 8) batch_ctr[threadIdx.x] = 0;
-  __syncthreads();
 
   // ---------------- page loop: register ring of NS pages ----------------
   // stage data of one page for this lane: K words of token r16 / lane group kb,
@@ -493,17 +493,22 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   // the wave's positions go to ring slots in order, NS - 1 requests ahead of
   // processing; a position past npos loads nothing that is used.  ipg is the
   // page of the next position to request, pgr[slot] the page a stage holds.
+  // The first NS - 1 requests take their page ids from the table itself, so
+  // they leave before the staging barrier.
   int ipg = rpos > 0 ? pbeg + wih * NB : tail0;
   int pgr[NS];
+  static_assert(NS - 1 <= NB, "the first requests lie in the first batch");
   if (npos > 0) {
 #pragma unroll
     for (int idx = 0; idx < NS - 1; ++idx) {
-      if (idx % NB == 0) prio_tick();
       pgr[idx] = ipg;
-      issue(st[idx], idx < npos ? page_id(ipg) : -1);
+      issue(st[idx], idx < npos ? ptab[ipg] : -1);
       ipg = next_page(idx + 1, ipg, (idx + 1) % NB == 0);
     }
   }
+  if (threadIdx.x < 8) batch_ctr[threadIdx.x] = 0;
+  __syncthreads();
+  if (npos > 0) prio_tick();                      // the first batch
 
   float (*qf)[D] = qf_all[w];
   _Float16 (*wbuf)[GQ][16] = wbuf_all[w];            // [grp][head][slot]
