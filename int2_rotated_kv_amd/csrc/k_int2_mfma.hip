@@ -439,6 +439,12 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
     OSCAR_DCHECK(id >= 0 && id < npool, p.status);
     return id;
   };
+  // the same from the table itself (before the ids are staged)
+  auto table_id = [&](int k) -> int {
+    const int id = ptab[k];
+    OSCAR_DCHECK(id >= 0 && id < npool, p.status);
+    return id;
+  };
 
   // Work distribution: the n pages of the segment are dealt out as whole
   // rounds of batches of NB consecutive pages (the k-th batch of the i-th
@@ -502,7 +508,7 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
     for (int idx = 0; idx < NS - 1; ++idx) {
       pgr[idx] = ipg;
-      issue(st[idx], idx < npos ? ptab[ipg] : -1);
+      issue(st[idx], idx < npos ? table_id(ipg) : -1);
       ipg = next_page(idx + 1, ipg, (idx + 1) % NB == 0);
     }
   }
