@@ -147,8 +147,10 @@ enum {
                                      without a word - a page id outside the
                                      pool, a history or BF16 length beyond its
                                      bound, a demotion slot outside its pool -
-                                     or a merge row with more partial slots
-                                     than the workspace holds                  */
+                                     a merge row with more partial slots than
+                                     the workspace holds, or a member of a
+                                     shared segment whose history ends inside
+                                     the segment's pages                       */
 };
 
 typedef struct {
@@ -198,7 +200,10 @@ typedef struct {
  * with each sequence's own pages; otherwise every sequence reads them as its
  * own.  The segments of one sequence must tile its first history pages:
  * ordered by first_page, the first starts at page 0 and each next one where
- * the previous ends. */
+ * the previous ends.  Every member's hist_len must cover its segments' pages
+ * whole (hist_len >= 16 * (first_page + num_pages)): they are attended whole
+ * for each member (device memory, not checked; the debug build reports a
+ * shorter history through OSCAR_STATUS_DEBUG_BOUNDS). */
 typedef struct {
   int32_t first_page;
   int32_t num_pages;         /* >= 1                                            */

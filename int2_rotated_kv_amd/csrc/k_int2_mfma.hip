@@ -248,9 +248,13 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   // pages of sequence b this kernel reads: those after its shared pages,
   // which the cascade kernel attends (with none shared: all of them)
   auto own_pages = [&](int b, int *skip) {
-    const int npg = (clamp_len(p.hist_len[b]) + kPage - 1) / kPage;
+    const int hlb = clamp_len(p.hist_len[b]);
+    const int npg = (hlb + kPage - 1) / kPage;
     int sk = 0;
     if (p.n_shared > 0) cascade_slots(p, b, &sk);
+    // the cascade attends every shared page whole for each member, so a
+    // member's history must cover them
+    OSCAR_DCHECK(sk * kPage <= hlb, p.status);
     sk = sk < npg ? sk : npg;
     *skip = sk;
     return npg - sk;

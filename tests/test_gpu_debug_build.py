@@ -5,9 +5,10 @@ an index they clamp or skip through the cache's status word
 Each case runs in a child process whose binding loads the debug library
 (OSCAR_LIB): valid inputs on both INT2 kernels and with shared pages keep the
 status word 0 and stay within the oracle bar; a history page id outside the
-pool (which every kernel skips) and a demotion entry with only one of its two
-slots set (skipped) set the bit, while the release build, given the same
-inputs in this process, skips them without a word."""
+pool (which every kernel skips), a demotion entry with only one of its two
+slots set (skipped) and a member of a shared segment whose history ends inside
+the segment's pages set the bit, while the release build, given the same
+inputs in this process, goes on without a word."""
 import os
 import subprocess
 import sys
@@ -46,10 +47,19 @@ CHILD = textwrap.dedent(r"""
                 assert np.all(e <= 2e-3), (kernel, b, e.max())
         print("debug build: valid inputs, status 0, within the bar")
     else:
-        run = sh.build_and_step(inp, steps=1, int2_kernel=ob.INT2_MFMA)
+        run = sh.build_and_step(inp, steps=1, int2_kernel=ob.INT2_MFMA,
+                                shared=segs if MODE == "shared" else None)
         sc = run.sc
         assert sc.cache.read_status() == 0
-        if MODE == "page":
+        if MODE == "shared":
+            # sequence 2's history made shorter than the 30 shared pages (480
+            # tokens) that the cascade attends whole for it
+            sc.hist_len[2] = 400
+            args = sc.decode_args(int2_kernel=ob.INT2_MFMA, shared=segs)
+            out = torch.zeros((wl.B, wl.Hq, wl.D), dtype=torch.float32, device="cuda")
+            ob.decode(sc.cache, args, sh.to_dev_bf16(inp.q[0]).view(torch.int16),
+                      torch.from_numpy(inp.R_k).cuda(), torch.from_numpy(inp.R_v).cuda(), out)
+        elif MODE == "page":
             # a history page id past the pool in sequence 1's table
             sc.hist_pages[1, 3] = int(sc.cache.int2.shape[0]) + 7
             args = sc.decode_args(int2_kernel=ob.INT2_MFMA)
@@ -85,19 +95,30 @@ def test_debug_build_valid_inputs():
     _child("valid")
 
 
-@pytest.mark.parametrize("mode", ["page", "demote"])
+@pytest.mark.parametrize("mode", ["page", "demote", "shared"])
 def test_debug_build_reports_skipped_indices(mode):
     _child(mode)
-    # the release build skips the same inputs without a word
+    # the release build skips the same inputs without a word (a member history
+    # shorter than its shared pages: they are still attended whole for it)
     import torch
     import synth
     import split_helpers as sh
     from int2_rotated_kv_amd import binding as ob
+    segs = [(0, 30, 0, 3)]
     wl = synth.workload("tiny", B=3, Hkv=2, Hq=16, D=128, G=128, lengths=(2400, 2400, 900), steps=1, seed=901)
     inp = synth.make_small(wl)
-    run = sh.build_and_step(inp, steps=1, int2_kernel=ob.INT2_MFMA)
+    if mode == "shared":
+        inp = synth.share_history(inp, segs)
+    run = sh.build_and_step(inp, steps=1, int2_kernel=ob.INT2_MFMA, shared=segs if mode == "shared" else None)
     sc = run.sc
-    if mode == "page":
+    if mode == "shared":
+        sc.hist_len[2] = 400
+        args = sc.decode_args(int2_kernel=ob.INT2_MFMA, shared=segs)
+        out = torch.zeros((wl.B, wl.Hq, wl.D), dtype=torch.float32, device="cuda")
+        ob.decode(sc.cache, args, sh.to_dev_bf16(inp.q[0]).view(torch.int16),
+                  torch.from_numpy(inp.R_k).cuda(), torch.from_numpy(inp.R_v).cuda(), out)
+        assert torch.isfinite(out).all()
+    elif mode == "page":
         sc.hist_pages[1, 3] = int(sc.cache.int2.shape[0]) + 7
         args = sc.decode_args(int2_kernel=ob.INT2_MFMA)
         out = torch.zeros((wl.B, wl.Hq, wl.D), dtype=torch.float32, device="cuda")
