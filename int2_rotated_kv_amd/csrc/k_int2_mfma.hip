@@ -169,6 +169,7 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   static_assert(GQ == 4 || GQ == 8, "one or two head quads (1, 2 or 4 q heads use one)");
 
   constexpr int NP = CB ? 3 : 1;       // QK code planes: the codes; with a codebook also b0, b0&b1
+  constexpr bool kPermPlanes = CB;    // the b0 and b0&b1 planes looked up from the code bytes
   __shared__ Int2Shared<D, G, GQ, HB> lds;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave (uniform)
@@ -594,8 +595,13 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
 
     // ---------------- QK on int8 MFMA ----------------
     // per plane (the codes; with a codebook also b0 and b0&b1): the group dot
-    // products, recombined from the three pieces as soon as they are done
+    // products, recombined from the three pieces as soon as they are done.
+    // With kPermPlanes the code bytes of the first plane are kept, and each
+    // byte of the other planes is looked up from them by one byte permute
+    // (tables b0 = c & 1 and b0&b1 = (c == 3)) instead of being extracted
+    // from the packed word again
     float dv[NP][NQ][NG];
+    v4i cbytes[NBLK];
 #pragma unroll
     for (int pl = 0; pl < NP; ++pl) {
       if constexpr (NP == 3) {
@@ -614,10 +620,18 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
         for (int g2 = 0; g2 < NG; ++g2) qacc[qd][g2] = v4i{0, 0, 0, 0};
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk) {
-        const uint32_t d = sg.c[blk];
-        const uint32_t e = pl == 2 ? d & (d >> 1) : d;   // bit 2i of e: b0 & b1 of channel i
-        const uint32_t mk = pl == 0 ? 0x03030303u : 0x01010101u;
-        const v4i bq = v4i{(int)(e & mk), (int)((e >> 2) & mk), (int)((e >> 4) & mk), (int)((e >> 6) & mk)};
+        v4i bq;
+        if (kPermPlanes && pl > 0) {
+          const uint32_t tab = pl == 1 ? 0x01000100u : 0x01000000u;   // byte c: plane value of code c
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bq[r] = (int)__builtin_amdgcn_perm(tab, tab, (uint32_t)cbytes[blk][r]);
+        } else {
+          const uint32_t d = sg.c[blk];
+          const uint32_t e = pl == 2 ? d & (d >> 1) : d;   // bit 2i of e: b0 & b1 of channel i
+          const uint32_t mk = pl == 0 ? 0x03030303u : 0x01010101u;
+          bq = v4i{(int)(e & mk), (int)((e >> 2) & mk), (int)((e >> 4) & mk), (int)((e >> 6) & mk)};
+          if constexpr (kPermPlanes) cbytes[blk] = bq;
+        }
 #pragma unroll
         for (int gs = 0; gs < GPB; ++gs) {
           const int m = blk * GPB + gs;
