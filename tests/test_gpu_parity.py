@@ -282,6 +282,67 @@ def test_bulk_quantise_order_and_splits():
             assert np.array_equal(base[phys[pg], j], want), f"page {pg} head {j}"
 
 
+@pytest.mark.parametrize("codebook", [False, True])
+@pytest.mark.parametrize("D,G", [(64, 32), (64, 64), (128, 32), (128, 64), (128, 128)])
+def test_bulk_quantise_every_shape(D, G, codebook):
+    """oscar_demote_pack in bulk (2000 entries of 8 KV heads: the
+    16-token-block kernel) for every head_dim and group size, with uniform
+    codes and with a Lloyd-Max codebook: 1995 tokens into randomly placed
+    pages, the last page partial (11 tokens), and 5 entries with both slots
+    -1 (skipped) at random positions.  Every page's record bytes equal the
+    oracle's (a partial page's unwritten token slots stay zero), and the
+    status word stays 0."""
+    import torch
+    from int2_rotated_kv_amd import binding as ob
+    from oracle import oscar_oracle as orc
+    _say(f"case: bulk quantise D{D} G{G} codebook {codebook}")
+    seed = 71 + D + G + (1 if codebook else 0)
+    wl = synth.workload("tiny", B=1, Hkv=8, Hq=32, D=D, G=G, lengths=(2100,), steps=1, seed=seed,
+                        clip_set=synth.WIDE_CLIPS)
+    inp = synth.make_small(wl)
+    n, npg = 1995, 125                             # 124 full pages and one of 11 tokens
+    K, V = inp.K[0][:n], inp.V[0][:n]              # [n][Hkv][D] bf16 bits
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+    Rk, Rv = dev(inp.R_k), dev(inp.R_v)
+    ck, cv = dev(inp.clip_k), dev(inp.clip_v)
+    cb = synth.make_codebook(seed, wl.Hkv) if codebook else None
+    phys = synth.page_permutation(seed, npg, extra=3)
+    dst = (phys[np.arange(n) // 16].astype(np.int64) * 16 + np.arange(n) % 16).astype(np.int32)
+    src = np.arange(n, dtype=np.int32)
+    rng = np.random.default_rng(seed)
+    at = np.sort(rng.choice(n, 5, replace=False))
+    src = np.insert(src, at, -1)
+    dst = np.insert(dst, at, -1)
+    assert src.shape == (2000,) and ((2000 + 15) // 16) * wl.Hkv * 2 >= 1024   # the bulk kernel
+    cache = ob.Cache(wl.Hkv, D, G, npg + 3, npg, codebook=dev(cb) if codebook else None)
+    kb = np.zeros((npg, wl.Hkv, 16, D), np.uint16)
+    vb = np.zeros_like(kb)
+    for t in range(n):
+        kb[t // 16, :, t % 16] = K[t]
+        vb[t // 16, :, t % 16] = V[t]
+    cache.bf16_k.copy_(dev(kb.view(np.int16)))
+    cache.bf16_v.copy_(dev(vb.view(np.int16)))
+    ob.demote_pack(cache, dev(src), dev(dst), Rk, Rv, ck, cv)
+    torch.cuda.synchronize()
+    pool = cache.int2.cpu().numpy()
+    assert cache.read_status() == 0
+    Kf, Vf = synth.bf16_bits_to_f64(K), synth.bf16_bits_to_f64(V)
+    for j in range(wl.Hkv):
+        if codebook:
+            kc, ks, kz = orc.quantize_tokens_codebook(Kf[:, j], inp.R_k[j], G, float(inp.clip_k[j]), cb[j, 0])
+            vc, vs, vz = orc.quantize_tokens_codebook(Vf[:, j], inp.R_v[j], G, float(inp.clip_v[j]), cb[j, 1])
+        else:
+            kc, ks, kz = orc.quantize_tokens(Kf[:, j], inp.R_k[j], G, float(inp.clip_k[j]))
+            vc, vs, vz = orc.quantize_tokens(Vf[:, j], inp.R_v[j], G, float(inp.clip_v[j]))
+        for pg in range(npg):
+            a, e = pg * 16, min(n, pg * 16 + 16)
+            pad = lambda x: np.concatenate([x[a:e], np.zeros((16 - (e - a),) + x.shape[1:], x.dtype)])
+            want = orc.encode_record(pad(kc), pad(ks), pad(kz), pad(vc), pad(vs), pad(vz), D, G)
+            assert np.array_equal(pool[phys[pg], j], want), f"page {pg} head {j}"
+    unused = np.setdiff1d(np.arange(npg + 3), phys)
+    assert not pool[unused].any(), "a page no entry names was written"
+
+
 @pytest.mark.parametrize("shape", ["b8_mixed", "qwen3-8b-32k"])
 def test_bitwise_repeatable(shape):
     """The matrix-core kernel's waves take fixed page batches (only their
