@@ -4,184 +4,253 @@
 
 namespace oscar {
 
-// Bulk fills (prompt histories): one block = 16 consecutive entries of the
-// slot lists, one KV head (blockIdx.y), K or V (blockIdx.z).  The rotation of
-// the 16 tokens, X[16][D] = K[16][D] . R, runs on the fp64 matrix cores
-// (v_mfma_f64_16x16x4f64: every product of a bf16 value and an fp32 R entry is
-// exact in fp64, the sums are fp64): wave w computes the channels 64w..64w+63
-// as four 16-column tiles, tile ct holding channels 64w + 4j + ct (j = 0..15)
-// so that one 16-byte R load per lane and k-step feeds all four tiles.  The
-// token values come from LDS (rows padded to D + 4 doubles: at most 2-way
-// bank conflicts), the results go back to LDS.  The group statistics (max,
-// min, clipped range, bf16 scale and zero) are computed once per (token,
-// group) by a few threads each, and thread c then quantises channel c of the
-// 16 tokens one by one; a token's V bits are gathered per page word and a word
-// is written once all tokens of its page in this block are in (whole-page
-// words with one store, others with AND/OR atomics).
+// Bulk fills (prompt histories): one wave = 16 consecutive entries of the
+// slot lists, one KV head (blockIdx.y), K or V (blockIdx.z), all D channels.
+// The rotation of the 16 tokens, X[16][D] = K[16][D] . R, runs on the fp64
+// matrix cores (v_mfma_f64_16x16x4f64: A[i][k] from lane i + 16k, B[k][j]
+// from lane j + 16k, D[i][j] in lane j + 16 (i mod 4), element i / 4; every
+// product of a bf16 value and an fp32 R entry is exact in fp64, the sums are
+// fp64) as 4 * D/64 tiles of 16 columns: tile (h, ct) holds channels
+// 64h + 4j + ct, so that one 16-byte R load per lane, k-step and half feeds
+// four tiles, and lane (ti, kq) = (l % 16, l / 16) ends up with token
+// kq + 4r (r = 0..3) at channels 64h + 4ti + ct.  Everything after the
+// rotation stays in registers: a group's max and min by reductions over the
+// 8 or 16 lanes of a row that hold it; its clipped range and bf16 scale and
+// zero computed once, by one of those lanes (which stores the record word),
+// and shuffled to the others; the codes; the K words by an OR over the 4
+// lanes of a quad, and the V words of a page by an OR over the 4 lanes that
+// hold a channel's tokens (whole-page words with one store, others with
+// AND/OR atomics).  No barrier after the token load, so the waves of a
+// compute unit drift out of phase and one wave's vector work runs under
+// another's matrix instructions.
 template <int D, int G>
-__global__ __launch_bounds__(D) void k_demote_bulk(DemoteArgs a) {
+__global__ __launch_bounds__(64) void k_demote_bulk(DemoteArgs a) {
 #pragma clang fp contract(off)
   typedef double v4d __attribute__((ext_vector_type(4)));
   constexpr int T = 16;
-  constexpr int XS = D + 4;                    // padded row stride of xs (doubles)
+  constexpr int XS = D + 4;                    // padded row stride of xs (floats)
   constexpr RecLayout RL(D, G);
-  constexpr int NG = D / G;                    // groups per token
-  constexpr int RT = D / (T * NG);             // threads per (token, group): 2, 4 or 8
-  constexpr int PG = G / RT;                   // channels each of them scans (16)
-  const int c = threadIdx.x;
+  constexpr int NH = D / 64;                   // 64-channel halves (tiles 4h .. 4h + 3)
+  constexpr int GL = G >= 64 ? 16 : G / 4;     // lanes of a row that share a group
+  constexpr int NGV = G > 64 ? 1 : NH;         // groups a lane holds per token (one per half, or one)
+  const int l = threadIdx.x;
+  const int ti = l & 15, kq = l >> 4;
   const int j = blockIdx.y;
   const bool isv = blockIdx.z != 0;
   const int e0 = blockIdx.x * T;
-  __shared__ __align__(16) double xs[T][XS];   // token values, then rotated values
-  __shared__ int s_src[T], s_dst[T];
-  __shared__ double s_sd[T][NG], s_zd[T][NG];  // bf16 scale and zero as fp64
+  __shared__ __align__(16) float xs[T][XS];    // the 16 tokens' values
 
-  const float *R = isv ? a.Rv : a.Rk;
-  const float *Rj = R != nullptr ? R + (size_t)j * D * D : nullptr;
-  if (c < T) {
-    const int e = e0 + c;
-    int sv = -1, dv = -1;
+  // entry e0 + t in lane t (t < 16); an entry with a negative or out-of-range
+  // slot is skipped (-1 in both lists)
+  int sv = -1, dv = -1;
+  if (l < T) {
+    const int e = e0 + l;
     if (e < a.n) { sv = a.src[e]; dv = a.dst[e]; }
-    // entries with a negative or out-of-range slot are skipped
-    // an entry is skipped by -1 in both lists
     OSCAR_DCHECK((sv < 0 && dv < 0) || (sv >= 0 && dv >= 0 && (sv >> 4) < a.n_bf16_pages &&
                                         (dv >> 4) < a.n_int2_pages), a.status);
     if (sv < 0 || dv < 0 || (sv >> 4) >= a.n_bf16_pages || (dv >> 4) >= a.n_int2_pages) {
       sv = -1;
       dv = -1;
     }
-    s_src[c] = sv;
-    s_dst[c] = dv;
   }
-  __syncthreads();
+  // the token values into LDS, 16 bytes (8 channels) per load; a skipped
+  // entry's token reads as 0
   const uint16_t *bf = isv ? a.bf_v : a.bf_k;
+  constexpr int CPT = D / 8;                   // 16-byte chunks per token
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const int s = s_src[t];
-    double v = 0.0;
+  for (int i = 0; i < T * CPT / 64; ++i) {
+    const int c = l + 64 * i;
+    const int t = c / CPT, pp = c % CPT;
+    const int s = __shfl(sv, t);
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
     if (s >= 0) {
       const int64_t page = s >> 4, off = s & 15;
-      v = (double)bf16_to_f32(bf[((page * a.Hkv + j) * kPage + off) * D + c]);
+      u = *reinterpret_cast<const uint4 *>(bf + ((page * a.Hkv + j) * kPage + off) * D + 8 * pp);
     }
-    xs[t][c] = v;
+    float4 *dst = reinterpret_cast<float4 *>(&xs[t][8 * pp]);
+    dst[0] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+    dst[1] = make_float4(bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w));
   }
   __syncthreads();
 
-  double x[T];
+  // x = k . R: acc[h][ct][r] = X[kq + 4r][64h + 4ti + ct]
+  const float *R = isv ? a.Rv : a.Rk;
+  const float *Rj = R != nullptr ? R + (size_t)j * D * D : nullptr;
+  v4d acc[NH][4];
   if (Rj != nullptr) {
-    // lane (ti, kq) = (l % 16, l / 16): A = token ti's value at k = 4s + kq,
-    // B = R[4s + kq][64w + 4ti + ct] for tile ct; the result of tile ct,
-    // element r, is X[token kq + 4r][channel 64w + 4ti + ct]
-    const int l = c & 63, w = c >> 6;
-    const int ti = l & 15, kq = l >> 4;
-    const float4 *R4 = reinterpret_cast<const float4 *>(Rj) + 16 * w + ti;
-    v4d acc[4];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[ct] = v4d{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 8
-    for (int s = 0; s < D / 4; ++s) {
-      const int k = 4 * s + kq;
-      const double av = xs[ti][k];
-      const float4 rv = R4[(size_t)k * (D / 4)];
-      acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)rv.x, acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)rv.y, acc[1], 0, 0, 0);
-      acc[2] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)rv.z, acc[2], 0, 0, 0);
-      acc[3] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)rv.w, acc[3], 0, 0, 0);
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[h][ct] = v4d{0.0, 0.0, 0.0, 0.0};
+    const float4 *R4 = reinterpret_cast<const float4 *>(Rj) + ti;
+#pragma unroll 4
+    for (int st = 0; st < D / 4; ++st) {
+      const int k = 4 * st + kq;
+      const double av = (double)xs[ti][k];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const float4 rv = R4[(size_t)k * (D / 4) + 16 * h];
+        acc[h][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)rv.x, acc[h][0], 0, 0, 0);
+        acc[h][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)rv.y, acc[h][1], 0, 0, 0);
+        acc[h][2] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)rv.z, acc[h][2], 0, 0, 0);
+        acc[h][3] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)rv.w, acc[h][3], 0, 0, 0);
+      }
     }
-    __syncthreads();                           // every wave has read the token values
+  } else {
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) xs[kq + 4 * r][64 * w + 4 * ti + ct] = acc[ct][r];
-    __syncthreads();
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[h][ct][r] = (double)xs[kq + 4 * r][64 * h + 4 * ti + ct];
   }
-#pragma unroll
-  for (int t = 0; t < T; ++t) x[t] = xs[t][c];
 
   uint32_t flags = 0;
   const float clip = isv ? a.clip_v[j] : a.clip_k[j];
   const float *lv = a.codebook ? a.codebook + (j * 2 + (isv ? 1 : 0)) * 4 : nullptr;
-  // Per (token, group), once: max and min (RT consecutive threads scan PG
-  // channels each, then combine by shuffles), the clipped range, and the bf16
-  // scale and zero, which the first of them also stores in the record.
-  {
-    const int pr = c / RT, sub = c % RT;
-    const int t = pr / NG, g2 = pr % NG;
-    const double *row = &xs[t][g2 * G + sub * PG];
-    double mx = row[0], mn = row[0];
+  // this lane's tokens kq + 4r: destination slot (-1 = skipped)
+  int dr[4];
 #pragma unroll
-    for (int i = 1; i < PG; ++i) {
-      mx = fmax(mx, row[i]);
-      mn = fmin(mn, row[i]);
-    }
+  for (int r = 0; r < 4; ++r) dr[r] = __shfl(dv, kq + 4 * r);
+  // the codes of the lane's tokens, 2 bits per token r, per tile
+  uint32_t cp[NH][4];
 #pragma unroll
-    for (int o = 1; o < RT; o <<= 1) {
-      mx = fmax(mx, __shfl_xor(mx, o));
-      mn = fmin(mn, __shfl_xor(mn, o));
-    }
-    if (sub == 0) {
-      double hi, lo;
-      clipped_range(clip, mx, mn, flags, hi, lo);
-      const double scale = (hi - lo) / 3.0;
-      const uint16_t sb = f64_to_bf16_rne(scale);
-      const uint16_t zb = f64_to_bf16_rne(lo);
-      s_sd[t][g2] = (double)bf16_to_f32(sb);
-      s_zd[t][g2] = (double)bf16_to_f32(zb);
-      const int d = s_dst[t];
-      if (d >= 0) {
-        const int64_t page = d >> 4, off = d & 15;
-        uint8_t *rec = a.pool + ((size_t)page * a.Hkv + j) * RL.bytes();
-        const int o = isv ? RL.vsz((int)off, g2) : RL.ksz((int)off, g2);
-        *reinterpret_cast<uint32_t *>(rec + o) = (uint32_t)sb | ((uint32_t)zb << 16);
-        flags |= group_flags(scale, lo, sb, isv, lv);
-      }
-    }
-  }
-  __syncthreads();
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) cp[h][ct] = 0;
 
-  int vpage = -1;                              // V word being gathered (uniform)
-  uint32_t vmask = 0, vbits = 0;
-  auto flush_v = [&]() {
-    if (vpage < 0) return;
-    uint8_t *rec = a.pool + ((size_t)vpage * a.Hkv + j) * RL.bytes();
-    // V word of channel c: lane slot c % 64, V word c / 64
-    uint32_t *wp = reinterpret_cast<uint32_t *>(rec + RL.vword(c & 63, c >> 6));
-    if (vmask == 0xFFFFFFFFu) {
-      *wp = vbits;
-    } else {
-      atomicAnd(wp, ~vmask);
-      atomicOr(wp, vbits);
-    }
-  };
+  // group max and min per (token r, group v of the lane) over the GL lanes
+  // of the row that hold the group
+  double gmx[4][NGV], gmn[4][NGV];
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const int d = s_dst[t];
-    if (d < 0) continue;                       // uniform
-    if (!isfinite(x[t])) flags |= OSCAR_STATUS_NONFINITE;
-    const uint32_t code = quant_code(x[t], s_zd[t][c / G], s_sd[t][c / G], lv);
-    const int64_t page = d >> 4, off = d & 15;
-    uint8_t *rec = a.pool + ((size_t)page * a.Hkv + j) * RL.bytes();
-    if (!isv) {
-      // K: word blk of lane slot 16*kb + t holds channels 64*blk + 16*kb + i of
-      // token t at bits 2i
-      const int kb = (c & 63) >> 4, blk = c >> 6;
-      uint32_t w = code << (2 * (c & 15));
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) w |= __shfl_xor(w, o);
-      if ((c & 15) == 0) *reinterpret_cast<uint32_t *>(rec + RL.kword(16 * kb + (int)off, blk)) = w;
-    } else {
-      if ((int)page != vpage) {
-        flush_v();
-        vpage = (int)page;
-        vmask = 0;
-        vbits = 0;
+    for (int v = 0; v < NGV; ++v) {
+      double mx = acc[v][0][r], mn = acc[v][0][r];
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          if (NGV > 1 && h != v) continue;
+          mx = fmax(mx, acc[h][ct][r]);
+          mn = fmin(mn, acc[h][ct][r]);
+        }
+#pragma unroll
+      for (int o = 1; o < GL; o <<= 1) {
+        mx = fmax(mx, __shfl_xor(mx, o));
+        mn = fmin(mn, __shfl_xor(mn, o));
       }
-      const int shf = 2 * (int)off;
-      vmask |= 3u << shf;
-      vbits = (vbits & ~(3u << shf)) | (code << shf);
+      gmx[r][v] = mx;
+      gmn[r][v] = mn;
+    }
+  // the bf16 scale and zero of (token r, group v) are computed once, by lane
+  // 4v + r of each GL-lane part of the row (which holds that group's max and
+  // min), which also stores the record word; then every lane of the part
+  // takes them from there
+  const int li = ti % GL;
+  double sd1 = 0.0, zd1 = 0.0;
+  if (li < 4 * NGV) {
+    const int r1 = li & 3, v1 = li >> 2;
+    double mx = gmx[0][0], mn = gmn[0][0];
+    int d = dr[0];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int v = 0; v < NGV; ++v)
+        if (r == r1 && v == v1) { mx = gmx[r][v]; mn = gmn[r][v]; d = dr[r]; }
+    double hi, lo;
+    clipped_range(clip, mx, mn, flags, hi, lo);
+    const double scale = (hi - lo) / 3.0;
+    const uint16_t sb = f64_to_bf16_rne(scale);
+    const uint16_t zb = f64_to_bf16_rne(lo);
+    sd1 = (double)bf16_to_f32(sb);
+    zd1 = (double)bf16_to_f32(zb);
+    if (d >= 0) {
+      flags |= group_flags(scale, lo, sb, isv, lv);
+      const int g2 = (64 * v1 + 4 * ti) / G;
+      const int off = d & 15;
+      uint8_t *rec = a.pool + ((size_t)(d >> 4) * a.Hkv + j) * RL.bytes();
+      const int o = isv ? RL.vsz(off, g2) : RL.ksz(off, g2);
+      *reinterpret_cast<uint32_t *>(rec + o) = (uint32_t)sb | ((uint32_t)zb << 16);
     }
   }
-  if (isv) flush_v();
+  const int part0 = l - li;                    // first lane of this lane's GL-lane part
+  double sd[4][NGV], zd[4][NGV];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int v = 0; v < NGV; ++v) {
+      sd[r][v] = __shfl(sd1, part0 + 4 * v + r);
+      zd[r][v] = __shfl(zd1, part0 + 4 * v + r);
+    }
+
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int d = dr[r];
+    const int off = d & 15;
+    uint8_t *rec = a.pool + ((size_t)(d >= 0 ? (d >> 4) : 0) * a.Hkv + j) * RL.bytes();
+    // codes of token kq + 4r at the lane's channels
+    uint32_t code[NH][4];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const double x = acc[h][ct][r];
+        if (d >= 0 && !isfinite(x)) flags |= OSCAR_STATUS_NONFINITE;
+        const int v = NGV > 1 ? h : 0;
+        code[h][ct] = quant_code(x, zd[r][v], sd[r][v], lv);
+        cp[h][ct] |= code[h][ct] << (2 * r);
+      }
+    if (!isv) {
+      // K word h of lane slot 16 kb + off holds channels 64h + 16kb + i at
+      // bits 2i: the 4 lanes of a quad (ti = 4kb .. 4kb + 3) hold 4 channels each
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        uint32_t w = (code[h][0] | (code[h][1] << 2) | (code[h][2] << 4) | (code[h][3] << 6)) << (8 * (ti & 3));
+        w |= __shfl_xor(w, 1);
+        w |= __shfl_xor(w, 2);
+        if (d >= 0 && (ti & 3) == 0)
+          *reinterpret_cast<uint32_t *>(rec + RL.kword(16 * (ti >> 2) + off, h)) = w;
+      }
+    }
+  }
+
+  if (isv) {
+    // V word of channel c (lane slot c % 64, word c / 64) holds token slot o
+    // of the page at bits 2o.  Per page named by the entries (in entry
+    // order): the lanes' bits of its tokens, ORed over the 4 lanes that hold
+    // a channel (kq = 0..3), stored by the kq = 0 lane.
+    uint32_t todo = (uint32_t)__ballot(l < T && dv >= 0);   // tokens not yet stored (uniform)
+    while (todo != 0) {
+      const int t0 = __builtin_ctz(todo);
+      const int P = __shfl(dv, t0) >> 4;                    // uniform
+      const uint32_t inp = (uint32_t)__ballot(l < T && dv >= 0 && (dv >> 4) == P);
+      todo &= ~inp;
+      uint32_t cov = 0;                                     // token slots of P written here
+      for (uint32_t m = inp; m != 0; m &= m - 1) cov |= 3u << (2 * (__shfl(dv, __builtin_ctz(m)) & 15));
+      uint8_t *rec = a.pool + ((size_t)P * a.Hkv + j) * RL.bytes();
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          uint32_t b = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (dr[r] >= 0 && (dr[r] >> 4) == P) b |= ((cp[h][ct] >> (2 * r)) & 3u) << (2 * (dr[r] & 15));
+          b |= __shfl_xor(b, 16);
+          b |= __shfl_xor(b, 32);
+          if (kq == 0) {
+            uint32_t *wp = reinterpret_cast<uint32_t *>(rec + RL.vword(4 * ti + ct, h));
+            if (cov == 0xFFFFFFFFu) {
+              *wp = b;
+            } else {
+              atomicAnd(wp, ~cov);
+              atomicOr(wp, b);
+            }
+          }
+        }
+    }
+  }
   if (flags != 0 && a.status != nullptr) atomicOr(a.status, flags);
 }
 
@@ -224,7 +293,7 @@ static void launch_demote_t(const DemoteArgs &a, hipStream_t s) {
   if ((a.n + 15) / 16 * a.Hkv * 2 < 1024) {
     hipLaunchKernelGGL((k_demote_one<D, G>), dim3(a.n, a.Hkv, 2), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_demote_bulk<D, G>), dim3((a.n + 15) / 16, a.Hkv, 2), dim3(D), 0, s, a);
+    hipLaunchKernelGGL((k_demote_bulk<D, G>), dim3((a.n + 15) / 16, a.Hkv, 2), dim3(64), 0, s, a);
   }
 }
 
