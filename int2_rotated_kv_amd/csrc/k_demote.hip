@@ -24,7 +24,7 @@ namespace oscar {
 // compute unit drift out of phase and one wave's vector work runs under
 // another's matrix instructions.
 template <int D, int G>
-__global__ __launch_bounds__(64) void k_demote_bulk(DemoteArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_demote_bulk(DemoteArgs a) {
 #pragma clang fp contract(off)
   typedef double v4d __attribute__((ext_vector_type(4)));
   constexpr int T = 16;
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(64) void k_demote_bulk(DemoteArgs a) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) acc[h][ct] = v4d{0.0, 0.0, 0.0, 0.0};
     const float4 *R4 = reinterpret_cast<const float4 *>(Rj) + ti;
-#pragma unroll 4
+#pragma unroll 1
     for (int st = 0; st < D / 4; ++st) {
       const int k = 4 * st + kq;
       const double av = (double)xs[ti][k];
@@ -119,9 +119,15 @@ __global__ __launch_bounds__(64) void k_demote_bulk(DemoteArgs a) {
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) cp[h][ct] = 0;
 
-  // group max and min per (token r, group v of the lane) over the GL lanes
-  // of the row that hold the group
-  double gmx[4][NGV], gmn[4][NGV];
+  // The bf16 scale and zero of (token r, group v of the lane) are computed
+  // once, by lane 4v + r of each GL-lane part of a row (the lanes holding
+  // that group), which also stores the record word; the other lanes of the
+  // part take them from there.  Group max and min by reductions over the
+  // part; each lane keeps those of its own (r, v).
+  const int li = ti % GL;
+  const int part0 = l - li;                    // first lane of this lane's GL-lane part
+  double mxs = 0.0, mns = 0.0;
+  int ds = -1;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -140,55 +146,38 @@ __global__ __launch_bounds__(64) void k_demote_bulk(DemoteArgs a) {
         mx = fmax(mx, __shfl_xor(mx, o));
         mn = fmin(mn, __shfl_xor(mn, o));
       }
-      gmx[r][v] = mx;
-      gmn[r][v] = mn;
+      if (li == 4 * v + r) { mxs = mx; mns = mn; ds = dr[r]; }
     }
-  // the bf16 scale and zero of (token r, group v) are computed once, by lane
-  // 4v + r of each GL-lane part of the row (which holds that group's max and
-  // min), which also stores the record word; then every lane of the part
-  // takes them from there
-  const int li = ti % GL;
   double sd1 = 0.0, zd1 = 0.0;
   if (li < 4 * NGV) {
-    const int r1 = li & 3, v1 = li >> 2;
-    double mx = gmx[0][0], mn = gmn[0][0];
-    int d = dr[0];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int v = 0; v < NGV; ++v)
-        if (r == r1 && v == v1) { mx = gmx[r][v]; mn = gmn[r][v]; d = dr[r]; }
     double hi, lo;
-    clipped_range(clip, mx, mn, flags, hi, lo);
+    clipped_range(clip, mxs, mns, flags, hi, lo);
     const double scale = (hi - lo) / 3.0;
     const uint16_t sb = f64_to_bf16_rne(scale);
     const uint16_t zb = f64_to_bf16_rne(lo);
     sd1 = (double)bf16_to_f32(sb);
     zd1 = (double)bf16_to_f32(zb);
-    if (d >= 0) {
+    if (ds >= 0) {
       flags |= group_flags(scale, lo, sb, isv, lv);
-      const int g2 = (64 * v1 + 4 * ti) / G;
-      const int off = d & 15;
-      uint8_t *rec = a.pool + ((size_t)(d >> 4) * a.Hkv + j) * RL.bytes();
+      const int g2 = (64 * (li >> 2) + 4 * ti) / G;
+      const int off = ds & 15;
+      uint8_t *rec = a.pool + ((size_t)(ds >> 4) * a.Hkv + j) * RL.bytes();
       const int o = isv ? RL.vsz(off, g2) : RL.ksz(off, g2);
       *reinterpret_cast<uint32_t *>(rec + o) = (uint32_t)sb | ((uint32_t)zb << 16);
     }
   }
-  const int part0 = l - li;                    // first lane of this lane's GL-lane part
-  double sd[4][NGV], zd[4][NGV];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int v = 0; v < NGV; ++v) {
-      sd[r][v] = __shfl(sd1, part0 + 4 * v + r);
-      zd[r][v] = __shfl(zd1, part0 + 4 * v + r);
-    }
 
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int d = dr[r];
     const int off = d & 15;
     uint8_t *rec = a.pool + ((size_t)(d >= 0 ? (d >> 4) : 0) * a.Hkv + j) * RL.bytes();
+    double sd[NGV], zd[NGV];                   // scale and zero of token kq + 4r's groups
+#pragma unroll
+    for (int v = 0; v < NGV; ++v) {
+      sd[v] = __shfl(sd1, part0 + 4 * v + r);
+      zd[v] = __shfl(zd1, part0 + 4 * v + r);
+    }
     // codes of token kq + 4r at the lane's channels
     uint32_t code[NH][4];
 #pragma unroll
@@ -198,7 +187,7 @@ __global__ __launch_bounds__(64) void k_demote_bulk(DemoteArgs a) {
         const double x = acc[h][ct][r];
         if (d >= 0 && !isfinite(x)) flags |= OSCAR_STATUS_NONFINITE;
         const int v = NGV > 1 ? h : 0;
-        code[h][ct] = quant_code(x, zd[r][v], sd[r][v], lv);
+        code[h][ct] = quant_code(x, zd[v], sd[v], lv);
         cp[h][ct] |= code[h][ct] << (2 * r);
       }
     if (!isv) {
