@@ -101,13 +101,14 @@ enum {
  * The MFMA kernel carries its PV operands in f16.  Without a codebook the
  * weights are p * scale_v * 2^(8-b) (p <= 4, 2^(8-b) <= 16), so every V group
  * scale must stay below OSCAR_MFMA_V_SCALE_LIMIT.  With a codebook the
- * weights are p * scale_v and the V levels themselves (rounded to f16) are
- * the other operand, so every V group scale times c = max(1, largest |V
- * level|) / 16 must stay below the limit, and every |V level| below 16 times
- * it.  The demotion paths check this for every group they write and set
- * OSCAR_STATUS_MFMA_V_RANGE in oscar_cache.status when it fails; the caller
- * must then ask for VALU, which has no such limit (its outputs over such a
- * cache are correct, the MFMA kernel's may be inf or NaN). */
+ * weights are p * scale_v and the other operand is each V level written as
+ * L0 + beta * h with a small integer h (exact in f16); the check keeps every
+ * V group scale times c = max(1, largest |V level|) / 16 below the limit, and
+ * every |V level| below 16 times it.  The demotion paths check this for
+ * every group they write and set OSCAR_STATUS_MFMA_V_RANGE in
+ * oscar_cache.status when it fails; the caller must then ask for VALU, which
+ * has no such limit (its outputs over such a cache are correct, the MFMA
+ * kernel's may be inf or NaN). */
 enum {
   OSCAR_INT2_AUTO = 0,
   OSCAR_INT2_VALU = 1,      /* vector-ALU dot products                         */
@@ -177,9 +178,13 @@ typedef struct {
                                 the K b0&b1 coefficient ((L3 - L2) - L1) + L0,
                                 evaluated in fp32 in that order, is 0, as for
                                 levels symmetric about their middle) and PV
-                                on the V levels rounded to f16.  Level order
-                                and finiteness are not checked (device
-                                memory)                                      */
+                                on the V levels written per KV head as
+                                L0 + beta * h[c] with integers h = (0, h1,
+                                h2, H), H in [1024, 2047] chosen for the
+                                closest fit (typically within 1e-5 of the
+                                level span; levels with L3 == L0 or far out of
+                                order are taken in f16).  Level order and
+                                finiteness are not checked (device memory) */
   uint32_t *status;          /* device word (4-byte aligned) or NULL: sticky
                                 OSCAR_STATUS_* bits set by the demotion paths
                                 (the calls that write records); NULL = not

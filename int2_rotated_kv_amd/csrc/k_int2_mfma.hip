@@ -198,21 +198,59 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   //   cA = (L2 - L0)/2, cB = (L1 - L0) - cA, cC = L3 - L2 - L1 + L0,
   // so the int8 contraction runs on the codes (as without a codebook) and on
   // the b0 and b0&b1 bit planes, weighted by cA, cB, cC, and the L0 part
-  // joins the zero point.  PV: each code's V level itself, in f16, is looked
-  // up by byte permutes from a table of the 4 levels (their low bytes in one
-  // word, their high bytes in another), so PV runs once on the levels with the
-  // weights p * scale_v.  Without a codebook cA = 1 and no plane is formed.
+  // joins the zero point.  PV: the V levels are written as
+  //   L[c] = vL0 + vbeta * h[c],  h = (0, h1, h2, H) integers, H in [1024, 2047],
+  // vL0 = L0, vbeta = (L3 - L0) / H, h1, h2 the nearest integers to
+  // H (L1 - L0) / (L3 - L0) and H (L2 - L0) / (L3 - L0), with H chosen over
+  // its 1024 values (16 per lane, a wave minimum) so that those two are
+  // closest; then |L[c] - vL0 - vbeta h[c]| stays far below the f16
+  // rounding of the levels themselves (typically ~1e-5 of L3 - L0; below
+  // ~3e-5 of it for any levels).  The h[c] are exact in f16: each code's h is
+  // looked up by byte permutes from a table of the 4 (low bytes in one word,
+  // high bytes in another), PV runs once on them with the weights
+  // p * scale_v, and the vL0 part joins the zero point.  Levels with
+  // L3 == L0 or far out of order (|L1 - L0| or |L2 - L0| > 8 |L3 - L0|)
+  // take h = the levels rounded to f16, vL0 = 0, vbeta = 1.  Without a
+  // codebook cA = 1 and no plane is formed.
   float kcA = 1.f, kcB = 0.f, kcC = 0.f, kL0 = 0.f;   // K levels
-  uint32_t vtab_lo = 0, vtab_hi = 0;                 // V levels in f16: low, high bytes
+  uint32_t vtab_lo = 0, vtab_hi = 0;                 // h[c] in f16: low, high bytes
+  float vL0 = 0.f, vbeta = 1.f;                      // V levels = vL0 + vbeta * h[c]
   if constexpr (CB) {
     const float *lk = p.codebook + j * 8, *lvv = lk + 4;
     kL0 = lk[0];
     kcA = 0.5f * (lk[2] - lk[0]);
     kcB = (lk[1] - lk[0]) - kcA;
     kcC = ((lk[3] - lk[2]) - lk[1]) + lk[0];
+    const double l0 = lvv[0], l1 = lvv[1], l2 = lvv[2], l3 = lvv[3];
+    const double sp = l3 - l0;
+    const double r1 = sp != 0.0 ? (l1 - l0) / sp : 0.0, r2 = sp != 0.0 ? (l2 - l0) / sp : 0.0;
+    float hv[4] = {(float)l0, (float)l1, (float)l2, (float)l3};
+    if (sp != 0.0 && fabs(r1) <= 8.0 && fabs(r2) <= 8.0) {   // uniform over the wave
+      double best = INFINITY;
+      int bh = 2047;
+      for (int i = 0; i < 16; ++i) {
+        const int H = 1024 + 16 * lane + i;
+        const double e = fmax(fabs(H * r1 - rint(H * r1)), fabs(H * r2 - rint(H * r2))) / H;
+        if (e < best) { best = e; bh = H; }
+      }
+      // the wave's smallest error, then the smallest H that reaches it
+      double bw = best;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) bw = fmin(bw, __shfl_xor(bw, o));
+      int hw = best == bw ? bh : 2048;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) hw = min(hw, __shfl_xor(hw, o));
+      const int H = __builtin_amdgcn_readfirstlane(hw);
+      hv[0] = 0.f;
+      hv[1] = (float)rint(H * r1);
+      hv[2] = (float)rint(H * r2);
+      hv[3] = (float)H;
+      vL0 = (float)l0;
+      vbeta = (float)(sp / H);
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const _Float16 h = (_Float16)lvv[k];
+      const _Float16 h = (_Float16)hv[k];
       uint16_t hb;
       __builtin_memcpy(&hb, &h, 2);
       vtab_lo |= (uint32_t)(hb & 0xFF) << (8 * k);
@@ -220,6 +258,8 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
     }
     vtab_lo = __builtin_amdgcn_readfirstlane(vtab_lo);
     vtab_hi = __builtin_amdgcn_readfirstlane(vtab_hi);
+    vL0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vL0)));
+    vbeta = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vbeta)));
   }
   // a symmetric K codebook (L3 - L2 = L1 - L0, as a Lloyd-Max fit of a
   // symmetric distribution gives) has no b0&b1 term: its QK plane is
@@ -717,8 +757,10 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
       for (int qd = 0; qd < NQ; ++qd) {
         zacc[qd][g2] = fmaf(pr[qd], vz, zacc[qd][g2]);
         const _Float16 wh = (_Float16)(pa[qd] * vs);
-        // uniform codes: remove the implicit one of the f16 code values
+        // uniform codes: remove the implicit one of the f16 code values;
+        // codebook: the vL0 part of the levels
         if constexpr (!CB) zacc[qd][g2] = fmaf(-4.f, (float)wh, zacc[qd][g2]);
+        else zacc[qd][g2] = fmaf(vL0, (float)wh, zacc[qd][g2]);
         wbuf[g2][qd * 4 + kb][pvs] = wh;
       }
     }
@@ -827,8 +869,9 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
           const float zg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Z[g2]), 16 * i));
           zz = (c / G == g2) ? zg : zz;
         }
-        // uniform codes: the f16 code values carry a factor 1/4
-        qf[qd * 4 + i][c] = (CB ? 1.f : 4.f) * acc[qd][h2][i] + zz;
+        // uniform codes: the f16 code values carry a factor 1/4; codebook:
+        // PV ran on h[c], the levels' integer part
+        qf[qd * 4 + i][c] = (CB ? vbeta : 4.f) * acc[qd][h2][i] + zz;
       }
     }
   }

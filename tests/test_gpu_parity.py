@@ -282,6 +282,39 @@ def test_bulk_quantise_order_and_splits():
             assert np.array_equal(base[phys[pg], j], want), f"page {pg} head {j}"
 
 
+@pytest.mark.parametrize("D,G,g", [(128, 32, 2), (128, 64, 4), (64, 64, 8)])
+def test_codebook_v_level_precision(D, G, g):
+    """A codebook whose V levels each lie just under half an f16 unit in the
+    last place from the nearest f16 value (the largest error a PV on f16
+    levels could make, the same for every token with that code): outputs of
+    the matrix-core kernel within a quarter of the bar against the oracle
+    (which uses the levels as given), bytes exact.  The kernel writes the
+    levels as L0 + beta * h with small integers h."""
+    from int2_rotated_kv_amd import binding as ob
+    _say(f"case: codebook V level precision D{D} G{G} g{g}")
+    wl = synth.workload("tiny", B=3, Hkv=2, Hq=2 * g, D=D, G=G, lengths=(2400, 1800, 2900), steps=1, seed=97 + g)
+    inp = synth.make_small(wl, distinct_rv=True)
+    cb = synth.make_codebook(wl.seed, wl.Hkv)
+    for j in range(wl.Hkv):
+        for k in range(4):
+            x = np.float32(cb[j, 1, k])
+            h = np.float16(x)
+            up = np.nextafter(h, np.float16(np.inf))            # the f16 value above
+            mid = (np.float64(h) + np.float64(up)) / 2
+            cb[j, 1, k] = np.float32(mid - (np.float64(up) - np.float64(h)) * 0.01)
+    assert np.all(np.diff(cb[:, 1], axis=-1) > 0)
+    ref = sh.oracle_step(inp, steps=1, codebook=cb)
+    run = sh.build_and_step(inp, steps=1, int2_kernel=ob.INT2_MFMA, codebook=cb)
+    _check_bytes(run, inp, ref)
+    worst = 0.0
+    for b, r in ref.items():
+        e = sh.row_rel_err(run.out[b].astype(np.float64), r["out"])
+        worst = max(worst, float(e.max()))
+    assert worst <= TOL / 4, f"worst row rel err {worst:.3e}"
+    assert run.status == 0
+    _say(f"codebook V level precision: worst row rel err {worst:.3e}")
+
+
 @pytest.mark.parametrize("codebook", [False, True])
 @pytest.mark.parametrize("D,G", [(64, 32), (64, 64), (128, 32), (128, 64), (128, 128)])
 def test_bulk_quantise_every_shape(D, G, codebook):
@@ -557,13 +590,15 @@ def _random_case(seed):
                 clip_set=clips), kernel, codebook, det
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", list(range(12)) + [41, 48, 52])
 def test_random_configurations(seed):
     """Seeded random configurations (head_dim, group, KV heads, q heads per KV
     head, batch, lengths from 1 to 3000 tokens, 1-2 steps, kernel choice,
     codebook or not, deterministic option or not, one clip ratio or per-head
     K != V ratios) against the oracle: page bytes exact, outputs within the
-    bar, no status bit."""
+    bar, no status bit.  Seeds 41, 48 and 52 (codebook, matrix-core kernel,
+    1 or 2 q heads per KV head) exceeded the bar (2.8e-3 to 5.6e-3) when PV
+    took the V levels rounded to f16."""
     from int2_rotated_kv_amd import binding as ob
     kw, kernel, codebook, det = _random_case(seed)
     _say(f"case: random configuration {seed}: {kw}, kernel {kernel}, codebook {codebook}, det {det}")
