@@ -102,9 +102,10 @@ enum {
  * weights are p * scale_v * 2^(8-b) (p <= 4, 2^(8-b) <= 16), so every V group
  * scale must stay below OSCAR_MFMA_V_SCALE_LIMIT.  With a codebook the
  * weights are p * scale_v and the other operand is each V level written as
- * L0 + beta * h with a small integer h (exact in f16); the check keeps every
- * V group scale times c = max(1, largest |V level|) / 16 below the limit, and
- * every |V level| below 16 times it.  The demotion paths check this for
+ * Lmin + beta * h with an integer 0 <= h <= 2047 (exact in f16); the check
+ * keeps every
+ * V group scale times c = max(1, largest |V level|) / 16 below the limit,
+ * and every |V level| below 16 times it.  The demotion paths check this for
  * every group they write and set OSCAR_STATUS_MFMA_V_RANGE in
  * oscar_cache.status when it fails; the caller must then ask for VALU, which
  * has no such limit (its outputs over such a cache are correct, the MFMA
@@ -179,12 +180,14 @@ typedef struct {
                                 evaluated in fp32 in that order, is 0, as for
                                 levels symmetric about their middle) and PV
                                 on the V levels written per KV head as
-                                L0 + beta * h[c] with integers h = (0, h1,
-                                h2, H), H in [1024, 2047] chosen for the
-                                closest fit (typically within 1e-5 of the
-                                level span; levels with L3 == L0 or far out of
-                                order are taken in f16).  Level order and
-                                finiteness are not checked (device memory) */
+                                Lmin + beta * h[c], Lmin the smallest level,
+                                with integers 0 <= h[c] <= H, H in
+                                [1024, 2047] chosen for the closest fit
+                                (typically within 1e-5 of the level span;
+                                non-finite levels are taken in f16).  Level
+                                order and finiteness are not checked (device
+                                memory); the quantiser counts the level
+                                midpoints below a value, whatever the order */
   uint32_t *status;          /* device word (4-byte aligned) or NULL: sticky
                                 OSCAR_STATUS_* bits set by the demotion paths
                                 (the calls that write records); NULL = not

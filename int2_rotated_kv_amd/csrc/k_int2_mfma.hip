@@ -199,19 +199,20 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   // so the int8 contraction runs on the codes (as without a codebook) and on
   // the b0 and b0&b1 bit planes, weighted by cA, cB, cC, and the L0 part
   // joins the zero point.  PV: the V levels are written as
-  //   L[c] = vL0 + vbeta * h[c],  h = (0, h1, h2, H) integers, H in [1024, 2047],
-  // vL0 = L0, vbeta = (L3 - L0) / H, h1, h2 the nearest integers to
-  // H (L1 - L0) / (L3 - L0) and H (L2 - L0) / (L3 - L0), with H chosen over
-  // its 1024 values (16 per lane, a wave minimum) so that those two are
-  // closest; then |L[c] - vL0 - vbeta h[c]| stays far below the f16
-  // rounding of the levels themselves (typically ~1e-5 of L3 - L0; below
-  // ~3e-5 of it for any levels).  The h[c] are exact in f16: each code's h is
-  // looked up by byte permutes from a table of the 4 (low bytes in one word,
-  // high bytes in another), PV runs once on them with the weights
-  // p * scale_v, and the vL0 part joins the zero point.  Levels with
-  // L3 == L0 or far out of order (|L1 - L0| or |L2 - L0| > 8 |L3 - L0|)
-  // take h = the levels rounded to f16, vL0 = 0, vbeta = 1.  Without a
-  // codebook cA = 1 and no plane is formed.
+  //   L[c] = vL0 + vbeta * h[c],  h[c] = rint(H (L[c] - vL0) / (Lmax - vL0)),
+  // vL0 = Lmin, the smallest of the four levels, Lmax the largest, so every
+  // h[c] lies in [0, H]: 0 and H exactly at the extremes, the two others the
+  // nearest integers; vbeta = (Lmax - Lmin) / H, with H in [1024, 2047]
+  // chosen over its 1024 values (16 per lane, a wave minimum) so that those
+  // two are closest.  Then |L[c] - vL0 - vbeta h[c]| stays far below the f16
+  // rounding of the levels themselves (typically ~1e-5 of Lmax - Lmin; below
+  // ~3e-5 of it for any levels).  The h[c] are integers up to 2047, exact in
+  // f16: each code's h is looked up by byte permutes from a table of the 4
+  // (low bytes in one word, high bytes in another), PV runs once on them with
+  // the weights p * scale_v, and the vL0 part joins the zero point.  Four
+  // equal levels take h = 0 (exact); non-finite levels take h = the levels
+  // rounded to f16, vL0 = 0, vbeta = 1.  Without a codebook cA = 1 and no
+  // plane is formed.
   float kcA = 1.f, kcB = 0.f, kcC = 0.f, kL0 = 0.f;   // K levels
   uint32_t vtab_lo = 0, vtab_hi = 0;                 // h[c] in f16: low, high bytes
   float vL0 = 0.f, vbeta = 1.f;                      // V levels = vL0 + vbeta * h[c]
@@ -221,32 +222,41 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
     kcA = 0.5f * (lk[2] - lk[0]);
     kcB = (lk[1] - lk[0]) - kcA;
     kcC = ((lk[3] - lk[2]) - lk[1]) + lk[0];
-    const double l0 = lvv[0], l1 = lvv[1], l2 = lvv[2], l3 = lvv[3];
-    const double sp = l3 - l0;
-    const double r1 = sp != 0.0 ? (l1 - l0) / sp : 0.0, r2 = sp != 0.0 ? (l2 - l0) / sp : 0.0;
-    float hv[4] = {(float)l0, (float)l1, (float)l2, (float)l3};
-    if (sp != 0.0 && fabs(r1) <= 8.0 && fabs(r2) <= 8.0) {   // uniform over the wave
-      double best = INFINITY;
-      int bh = 2047;
-      for (int i = 0; i < 16; ++i) {
-        const int H = 1024 + 16 * lane + i;
-        const double e = fmax(fabs(H * r1 - rint(H * r1)), fabs(H * r2 - rint(H * r2))) / H;
-        if (e < best) { best = e; bh = H; }
+    const double lv[4] = {lvv[0], lvv[1], lvv[2], lvv[3]};
+    const double lmin = fmin(fmin(lv[0], lv[1]), fmin(lv[2], lv[3]));
+    const double lmax = fmax(fmax(lv[0], lv[1]), fmax(lv[2], lv[3]));
+    const double sp = lmax - lmin;
+    float hv[4] = {(float)lv[0], (float)lv[1], (float)lv[2], (float)lv[3]};
+    if (isfinite(lv[0] + lv[1] + lv[2] + lv[3])) {   // uniform over the wave
+      vL0 = (float)lmin;
+      if (sp == 0.0) {
+        hv[0] = hv[1] = hv[2] = hv[3] = 0.f;
+      } else {
+        double r[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r[k] = (lv[k] - lmin) / sp;   // in [0, 1]
+        double best = INFINITY;
+        int bh = 2047;
+        for (int i = 0; i < 16; ++i) {
+          const int H = 1024 + 16 * lane + i;
+          double e = 0.0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) e = fmax(e, fabs(H * r[k] - rint(H * r[k])));
+          e /= H;
+          if (e < best) { best = e; bh = H; }
+        }
+        // the wave's smallest error, then the smallest H that reaches it
+        double bw = best;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) bw = fmin(bw, __shfl_xor(bw, o));
+        int hw = best == bw ? bh : 2048;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) hw = min(hw, __shfl_xor(hw, o));
+        const int H = __builtin_amdgcn_readfirstlane(hw);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) hv[k] = (float)rint(H * r[k]);
+        vbeta = (float)(sp / H);
       }
-      // the wave's smallest error, then the smallest H that reaches it
-      double bw = best;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) bw = fmin(bw, __shfl_xor(bw, o));
-      int hw = best == bw ? bh : 2048;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) hw = min(hw, __shfl_xor(hw, o));
-      const int H = __builtin_amdgcn_readfirstlane(hw);
-      hv[0] = 0.f;
-      hv[1] = (float)rint(H * r1);
-      hv[2] = (float)rint(H * r2);
-      hv[3] = (float)H;
-      vL0 = (float)l0;
-      vbeta = (float)(sp / H);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {

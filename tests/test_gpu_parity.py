@@ -282,16 +282,21 @@ def test_bulk_quantise_order_and_splits():
             assert np.array_equal(base[phys[pg], j], want), f"page {pg} head {j}"
 
 
-@pytest.mark.parametrize("D,G,g", [(128, 32, 2), (128, 64, 4), (64, 64, 8)])
-def test_codebook_v_level_precision(D, G, g):
+@pytest.mark.parametrize("D,G,g,order", [(128, 32, 2, None), (128, 64, 4, None), (64, 64, 8, None),
+                                         (128, 64, 2, (1, 0, 3, 2)), (64, 32, 4, (2, 3, 0, 1))])
+def test_codebook_v_level_precision(D, G, g, order):
     """A codebook whose V levels each lie just under half an f16 unit in the
     last place from the nearest f16 value (the largest error a PV on f16
     levels could make, the same for every token with that code): outputs of
     the matrix-core kernel within a quarter of the bar against the oracle
     (which uses the levels as given), bytes exact.  The kernel writes the
-    levels as L0 + beta * h with small integers h."""
+    levels as Lmin + beta * h with integers 0 <= h <= 2047.  With `order` the
+    V levels are given out of order (level k is the k-th of the ascending
+    ones' permutation), so that the smallest and largest are not L0 and L3:
+    the kernel's quantiser and the oracle's both count the midpoints below a
+    value, so the bytes still agree."""
     from int2_rotated_kv_amd import binding as ob
-    _say(f"case: codebook V level precision D{D} G{G} g{g}")
+    _say(f"case: codebook V level precision D{D} G{G} g{g} order {order}")
     wl = synth.workload("tiny", B=3, Hkv=2, Hq=2 * g, D=D, G=G, lengths=(2400, 1800, 2900), steps=1, seed=97 + g)
     inp = synth.make_small(wl, distinct_rv=True)
     cb = synth.make_codebook(wl.seed, wl.Hkv)
@@ -303,6 +308,8 @@ def test_codebook_v_level_precision(D, G, g):
             mid = (np.float64(h) + np.float64(up)) / 2
             cb[j, 1, k] = np.float32(mid - (np.float64(up) - np.float64(h)) * 0.01)
     assert np.all(np.diff(cb[:, 1], axis=-1) > 0)
+    if order is not None:
+        cb[:, 1] = cb[:, 1][:, list(order)]
     ref = sh.oracle_step(inp, steps=1, codebook=cb)
     run = sh.build_and_step(inp, steps=1, int2_kernel=ob.INT2_MFMA, codebook=cb)
     _check_bytes(run, inp, ref)
