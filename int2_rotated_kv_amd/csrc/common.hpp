@@ -26,6 +26,12 @@ __host__ __device__ constexpr int mfma_waves(int d, int g, int gq, bool cb) {
   return ((d == 128 && g == 32 && (gq == 8 || cb)) || (cb && gq == 8 && (g == 32 || (d == 128 && g == 64))))
              ? 8 : 16;
 }
+// Query A operand sets per QK step of the matrix-core INT2 kernel: with a
+// codebook and one head quad (g <= 4 q heads per KV head) one per code plane
+// (the query pieces times the plane's weight, all planes contracted into one
+// accumulator); otherwise one (with two head quads the three sets would not
+// fit the register budget, and the planes keep separate accumulators)
+__host__ __device__ constexpr int mfma_a_planes(int g, bool cb) { return cb && g <= 4 ? 3 : 1; }
 // sequences the kernel balances its blocks across (one per thread of a block)
 __host__ __device__ constexpr int mfma_max_balanced(int waves) { return 64 * waves; }
 // KV heads per block of the matrix-core INT2 kernel: 2 (1 for a single KV
@@ -106,8 +112,9 @@ struct SharedSeg {
 // Workspace partition used by decode_attn and merge.
 struct WsLayout {
   size_t qrot;      // fp32 [B][Hq][D]     q . R_k (unscaled)
-  size_t qpk;       // matrix-core kernel only: int32 [B][Hkv][g/4][mfma_qk_steps][64][4]
-                    //   its QK A operands (the rotated query in 7-bit pieces)
+  size_t qpk;       // matrix-core kernel only: int32 [B][Hkv][g/4][planes][mfma_qk_steps][64][4]
+                    //   its QK A operands (the rotated query in 7-bit pieces;
+                    //   planes: mfma_a_planes)
   size_t nslots;    // matrix-core kernel only: int32 [B] partial slots each sequence used
   size_t qhd;       // matrix-core kernel only: [B][Hq][8] per q head: int exponent
                     //   (bits), then sum of q_rot over each group * sm_scale * log2(e)

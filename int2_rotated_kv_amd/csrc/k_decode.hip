@@ -91,8 +91,22 @@ __device__ __forceinline__ void qrot_body(const DecodeParams &p, const uint16_t 
   // (kb, row) holds in dword e, byte bb the piece of channel
   // 64*blk + 16*kb + 4*bb + e.  Also the exponent and the group sums of q_rot
   // (their zero-point term) times sm_scale*log2(e).
+  // With a codebook the K level of code c = b0 + 2*b1 is
+  // L0 + cA*c + cB*b0 + cC*b0*b1 (cA = (L2 - L0)/2, cB = L1 - L0 - cA,
+  // cC = L3 - L2 - L1 + L0); with up to 4 q heads per KV head the kernel
+  // contracts the three planes c, b0, b0&b1 into one accumulator: plane pl
+  // gets the pieces of rint(fl(q * c_pl) * 2^qe), with
+  // |q| * max|c_pl| * 2^qe < 2^20 (with 8 it weights the planes itself).
   __syncthreads();
   const int G = p.G, NG = D / G;
+  const int NPc = mfma_a_planes(p.g, p.codebook != nullptr);   // A operand sets
+  float kc[3] = {1.f, 0.f, 0.f};
+  if (NPc == 3) {
+    const float *lk = p.codebook + (size_t)j * 8;
+    kc[0] = 0.5f * (lk[2] - lk[0]);
+    kc[1] = (lk[1] - lk[0]) - kc[0];
+    kc[2] = ((lk[3] - lk[2]) - lk[1]) + lk[0];
+  }
   if (tid < 64) {
     float mx = 0.f;
     float gs[4] = {0.f, 0.f, 0.f, 0.f};
@@ -108,6 +122,7 @@ __device__ __forceinline__ void qrot_body(const DecodeParams &p, const uint16_t 
     for (int g2 = 0; g2 < 4; ++g2)
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) gs[g2] += __shfl_xor(gs[g2], o);
+    if (NPc == 3) mx *= fmaxf(fmaxf(fabsf(kc[0]), fabsf(kc[1])), fabsf(kc[2]));
     int e = 0;
     if (mx > 0.f) (void)frexpf(mx, &e);          // mx < 2^e
     int qe = mx > 0.f ? 20 - e : 0;              // |q| * 2^qe < 2^20
@@ -141,33 +156,38 @@ __device__ __forceinline__ void qrot_body(const DecodeParams &p, const uint16_t 
       dst[pc * D + (c & ~15) + 4 * (c & 3) + ((c >> 2) & 3)] = (int8_t)piece;
     }
   }
-  for (int t = tid; t < nqk * 64; t += 256) {
-    const int m = t >> 6, pc = (t >> 4) & 3, kb = (t >> 2) & 3, e = t & 3;
+  // layout [b][Hkv][head quad][plane][m][lane][dword]
+  for (int t = tid; t < NPc * nqk * 64; t += 256) {
+    const int pl = t / (nqk * 64), u = t % (nqk * 64);
+    const int m = u >> 6, pc = (u >> 4) & 3, kb = (u >> 2) & 3, e = u & 3;
     const int blk = m / gpb, g2 = (64 * blk) / G + m % gpb;
+    const float kp = kc[pl];
     uint32_t word = 0;
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) {
       const int c = 64 * blk + 16 * kb + 4 * bb + e;
       int piece = 0;
       if (pc < 3 && c / G == g2) {
-        const int qi = (int)rintf(sh.qf[c] * sc);
+        const int qi = (int)rintf((NPc == 1 ? sh.qf[c] : sh.qf[c] * kp) * sc);
         piece = pc == 0 ? (qi >> 14) : pc == 1 ? ((qi >> 7) & 127) : (qi & 127);
       }
       word |= ((uint32_t)piece & 0xFFu) << (8 * bb);
     }
     const int lane = 16 * kb + 4 * (h_in & 3) + pc;
     int32_t *dst = reinterpret_cast<int32_t *>(p.ws + p.L.qpk);
-    dst[((((size_t)b * p.Hkv + j2) * nq + (h_in >> 2)) * nqk + m) * 256 + lane * 4 + e] = (int32_t)word;
+    dst[(((((size_t)b * p.Hkv + j2) * nq + (h_in >> 2)) * NPc + pl) * nqk + m) * 256 + lane * 4 + e] =
+        (int32_t)word;
   }
   // with fewer than 4 q heads per KV head the rows of the quad's missing heads
   // are zero (written by the last present head; nq == 1)
   if (p.g < 4 && h_in == p.g - 1) {
     int32_t *dst = reinterpret_cast<int32_t *>(p.ws + p.L.qpk);
-    for (int t = tid; t < nqk * 64 * (4 - p.g); t += 256) {
-      const int hh = p.g + t / (nqk * 64), u = t % (nqk * 64);
-      const int m = u >> 6, pc = (u >> 4) & 3, kb = (u >> 2) & 3, e = u & 3;
+    for (int t = tid; t < NPc * nqk * 64 * (4 - p.g); t += 256) {
+      const int hh = p.g + t / (NPc * nqk * 64), u = t % (NPc * nqk * 64);
+      const int pl = u / (nqk * 64), v = u % (nqk * 64);
+      const int m = v >> 6, pc = (v >> 4) & 3, kb = (v >> 2) & 3, e = v & 3;
       const int lane = 16 * kb + 4 * hh + pc;
-      dst[(((size_t)b * p.Hkv + j2) * nqk + m) * 256 + lane * 4 + e] = 0;
+      dst[((((size_t)b * p.Hkv + j2) * NPc + pl) * nqk + m) * 256 + lane * 4 + e] = 0;
     }
   }
 }

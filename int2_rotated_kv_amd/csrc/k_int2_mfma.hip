@@ -170,6 +170,8 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
 
   constexpr int NP = CB ? 3 : 1;       // QK code planes: the codes; with a codebook also b0, b0&b1
   constexpr bool kPermPlanes = CB;    // the b0 and b0&b1 planes looked up from the code bytes
+  constexpr int NPA = mfma_a_planes(GQ, CB);   // query A operand sets
+  constexpr bool kSepAcc = NP > NPA;  // planes in accumulators of their own, weighted here
   __shared__ Int2Shared<D, G, GQ, HB> lds;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave (uniform)
@@ -197,8 +199,12 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   //   L[c] = L0 + cA*c + cB*b0 + cC*b0*b1,
   //   cA = (L2 - L0)/2, cB = (L1 - L0) - cA, cC = L3 - L2 - L1 + L0,
   // so the int8 contraction runs on the codes (as without a codebook) and on
-  // the b0 and b0&b1 bit planes, weighted by cA, cB, cC, and the L0 part
-  // joins the zero point.  PV: the V levels are written as
+  // the b0 and b0&b1 bit planes, and the L0 part joins the zero point.  With
+  // one head quad the planes go into one accumulator, the A operand of each
+  // holding the pieces of the query times the plane's weight (formed with
+  // the q rotation); with two (three A sets would not fit the registers)
+  // each plane has its own accumulator, weighted by cA, cB, cC here.  PV: the
+  // V levels are written as
   //   L[c] = vL0 + vbeta * h[c],  h[c] = rint(H (L[c] - vL0) / (Lmax - vL0)),
   // vL0 = Lmin, the smallest of the four levels, Lmax the largest, so every
   // h[c] lies in [0, H]: 0 and H exactly at the extremes, the two others the
@@ -211,8 +217,8 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   // (low bytes in one word, high bytes in another), PV runs once on them with
   // the weights p * scale_v, and the vL0 part joins the zero point.  Four
   // equal levels take h = 0 (exact); non-finite levels take h = the levels
-  // rounded to f16, vL0 = 0, vbeta = 1.  Without a codebook cA = 1 and no
-  // plane is formed.
+  // rounded to f16, vL0 = 0, vbeta = 1.  Without a codebook no plane is
+  // formed.
   float kcA = 1.f, kcB = 0.f, kcC = 0.f, kL0 = 0.f;   // K levels
   uint32_t vtab_lo = 0, vtab_hi = 0;                 // h[c] in f16: low, high bytes
   float vL0 = 0.f, vbeta = 1.f;                      // V levels = vL0 + vbeta * h[c]
@@ -381,16 +387,18 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   // a segment's sequence is known, before its length and page ids: A words of
   // the wave's head quads, and per q head its exponent and group sums
   // (wave-uniform scalar loads)
-  v4i aq[NQ][NQK];
+  v4i aq[NQ][NPA][NQK];
   int qe_h[GQ];
   float qz_h[GQ][NG];
   auto load_query = [&](int b) {
     const v4i *qpk = reinterpret_cast<const v4i *>(p.ws + p.L.qpk) +
-                     ((size_t)b * p.Hkv + j) * NQ * NQK * 64 + lane;
+                     ((size_t)b * p.Hkv + j) * NQ * NPA * NQK * 64 + lane;
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-      for (int m = 0; m < NQK; ++m) aq[qd][m] = qpk[(qd * NQK + m) * 64];
+      for (int pl = 0; pl < NPA; ++pl)
+#pragma unroll
+        for (int m = 0; m < NQK; ++m) aq[qd][pl][m] = qpk[((qd * NPA + pl) * NQK + m) * 64];
     using cf32 = const __attribute__((address_space(4))) float;
     cf32 *qhd = (cf32 *)(p.ws + p.L.qhd);
 #pragma unroll
@@ -644,30 +652,45 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
     }
 
     // ---------------- QK on int8 MFMA ----------------
-    // per plane (the codes; with a codebook also b0 and b0&b1): the group dot
-    // products, recombined from the three pieces as soon as they are done.
-    // With kPermPlanes the code bytes of the first plane are kept, and each
-    // byte of the other planes is looked up from them by one byte permute
-    // (tables b0 = c & 1 and b0&b1 = (c == 3)) instead of being extracted
-    // from the packed word again
-    float dv[NP][NQ][NG];
+    // per group: the dot products of the query pieces with the codes (with a
+    // codebook also with the b0 and b0&b1 planes), recombined from the three
+    // pieces as p0*2^14 + p1*2^7 + p2 (two shift-adds; the empty asm keeps
+    // the compiler from re-associating them into two shifts and an add3).
+    // The planes share one accumulator when their A operands carry the plane
+    // weights (kSepAcc false), else each plane is recombined as soon as it is
+    // done.  With kPermPlanes the code bytes of the first plane are kept, and
+    // each byte of the other planes is looked up from them by one byte
+    // permute (tables b0 = c & 1 and b0&b1 = (c == 3)) instead of being
+    // extracted from the packed word again
+    auto recombine = [](const v4i &a) -> float {
+      int dhi = (a[0] << 7) + a[1];
+      asm volatile("" : "+v"(dhi));
+      return (float)((dhi << 7) + a[2]);
+    };
+    constexpr int NACC = kSepAcc ? NP : 1;
+    float dv[NACC][NQ][NG];
+    v4i qacc[NQ][NG];
     v4i cbytes[NBLK];
 #pragma unroll
     for (int pl = 0; pl < NP; ++pl) {
+      const int ap = kSepAcc ? 0 : pl;           // A operand set of this plane
       if constexpr (NP == 3) {
         if (pl == 2 && !plane2) {
+          if constexpr (kSepAcc) {
 #pragma unroll
-          for (int qd = 0; qd < NQ; ++qd)
+            for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-            for (int g2 = 0; g2 < NG; ++g2) dv[2][qd][g2] = 0.f;
+              for (int g2 = 0; g2 < NG; ++g2) dv[NACC - 1][qd][g2] = 0.f;
+          }
           continue;
         }
       }
-      v4i qacc[NQ][NG];
+      if (kSepAcc || pl == 0) {
 #pragma unroll
-      for (int qd = 0; qd < NQ; ++qd)
+        for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-        for (int g2 = 0; g2 < NG; ++g2) qacc[qd][g2] = v4i{0, 0, 0, 0};
+          for (int g2 = 0; g2 < NG; ++g2) qacc[qd][g2] = v4i{0, 0, 0, 0};
+      }
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk) {
         v4i bq;
@@ -688,19 +711,15 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
           const int g2 = (64 * blk) / G + gs;
 #pragma unroll
           for (int qd = 0; qd < NQ; ++qd)
-            qacc[qd][g2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[qd][m], bq, qacc[qd][g2], 0, 0, 0);
+            qacc[qd][g2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[qd][ap][m], bq, qacc[qd][g2], 0, 0, 0);
         }
       }
-      // p0*2^14 + p1*2^7 + p2 as two shift-adds (the empty asm keeps the
-      // compiler from re-associating them into two shifts and an add3)
+      if (kSepAcc || pl == NP - 1 || (NP == 3 && pl == 1 && !plane2)) {
 #pragma unroll
-      for (int qd = 0; qd < NQ; ++qd)
+        for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-        for (int g2 = 0; g2 < NG; ++g2) {
-          int dhi = (qacc[qd][g2][0] << 7) + qacc[qd][g2][1];
-          asm volatile("" : "+v"(dhi));
-          dv[pl][qd][g2] = (float)((dhi << 7) + qacc[qd][g2][2]);
-        }
+          for (int g2 = 0; g2 < NG; ++g2) dv[kSepAcc ? pl : 0][qd][g2] = recombine(qacc[qd][g2]);
+      }
     }
     float s_[NQ];
 #pragma unroll
@@ -709,7 +728,7 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
 #pragma unroll
       for (int g2 = 0; g2 < NG; ++g2) {
         float dot = dv[0][qd][g2];
-        if constexpr (CB) dot = fmaf(kcC, dv[2][qd][g2], fmaf(kcB, dv[1][qd][g2], kcA * dot));
+        if constexpr (kSepAcc) dot = fmaf(kcC, dv[NACC - 1][qd][g2], fmaf(kcB, dv[1 % NACC][qd][g2], kcA * dot));
         const float ks = bf16_lo(sg.sz[g2]);
         sc = fmaf(ks, dot, sc);
         // the zero point, and the codebook's L0 part of every level
