@@ -80,7 +80,9 @@ enum {
 
 /* Parts of oscar_decode_attn (bit mask). */
 enum {
-  OSCAR_PHASE_QROT = 1,     /* q . R_k into the workspace                        */
+  OSCAR_PHASE_QROT = 1,     /* q . R_k into the workspace (with the matrix-core
+                               kernel also its query operands and, with a
+                               codebook, each KV head's V grid)              */
   OSCAR_PHASE_BF16 = 2,     /* BF16 sink/recent segment partial                  */
   OSCAR_PHASE_INT2 = 4,     /* INT2 history chunk partials                       */
   OSCAR_PHASE_ALL = 7

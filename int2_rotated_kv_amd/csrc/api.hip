@@ -308,6 +308,7 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
                                  mfma_a_planes(p->g, c->codebook != nullptr) * mfma_qk_steps(p->D, p->G) *
                                  64 * 4 * 4 : 0));
   L.qhd = off; off = align256(off + (mf ? BH * 8 * 4 : 0));
+  L.vgrid = off; off = align256(off + (mf && c->codebook != nullptr ? (size_t)c->num_kv_heads * 16 : 0));
   L.qcas = off; off = align256(off + (p->n_shared > 0 ? BH * 3 * p->D : 0));
   L.nslots = off; off = align256(off + (mf ? (size_t)a->batch * 4 : 0));
   L.part_o = off; off = align256(off + BH * S * p->D * 4);

@@ -118,6 +118,9 @@ struct WsLayout {
   size_t nslots;    // matrix-core kernel only: int32 [B] partial slots each sequence used
   size_t qhd;       // matrix-core kernel only: [B][Hq][8] per q head: int exponent
                     //   (bits), then sum of q_rot over each group * sm_scale * log2(e)
+  size_t vgrid;     // matrix-core kernel with a codebook only: uint32 [Hkv][4] the
+                    //   V levels as Lmin + beta * h[c]: h[c] in f16 (low bytes,
+                    //   high bytes), Lmin and beta (fp32 bits)
   size_t qcas;      // shared pages only: int8 [B][Hq][3][D] the 7-bit pieces of the
                     //   rotated query (piece-major), each 16-channel block stored
                     //   4x4-transposed (byte 4i + j = channel 4j + i) for the MFMA

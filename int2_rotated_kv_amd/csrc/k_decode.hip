@@ -32,6 +32,73 @@ struct QrotShared {
   int qe;
 };
 
+// The V grid of a Lloyd-Max codebook for the matrix-core kernel's PV, by one
+// wave (64 lanes, all active): the four V levels lv as Lmin + beta * h[c],
+// h[c] = rint(H (L[c] - Lmin) / (Lmax - Lmin)) in [0, H], beta =
+// (Lmax - Lmin) / H, with H in [1024, 2047] the one whose h lie closest to
+// those quotients: lane l compares H = 1024 + 16 l + i (i < 16) in fp32 on
+// max |H r - rint(H r)| / H, the wave keeps the smallest (the smallest H on
+// a tie), and the h of that H are formed in fp64.  Four equal levels give
+// h = 0; non-finite levels give h = the levels rounded to f16, Lmin = 0 and
+// beta = 1.  out: h[c] in f16 as two words (byte c of out[0] the low byte,
+// of out[1] the high byte), Lmin and beta as fp32 bits.
+__device__ void v_grid_words(const float *lv4, int lane, uint32_t out[4]) {
+  const double lv[4] = {lv4[0], lv4[1], lv4[2], lv4[3]};
+  const double lmin = fmin(fmin(lv[0], lv[1]), fmin(lv[2], lv[3]));
+  const double lmax = fmax(fmax(lv[0], lv[1]), fmax(lv[2], lv[3]));
+  const double sp = lmax - lmin;
+  float hv[4] = {(float)lv[0], (float)lv[1], (float)lv[2], (float)lv[3]};
+  float base = 0.f, beta = 1.f;
+  if (isfinite(lv[0] + lv[1] + lv[2] + lv[3])) {
+    base = (float)lmin;
+    if (sp == 0.0) {
+      hv[0] = hv[1] = hv[2] = hv[3] = 0.f;
+    } else {
+      double r[4];
+      float rf[4];
+      for (int k = 0; k < 4; ++k) {
+        r[k] = (lv[k] - lmin) / sp;   // in [0, 1]
+        rf[k] = (float)r[k];
+      }
+      float best = INFINITY;
+      int bh = 2047;
+      for (int i = 0; i < 16; ++i) {
+        const int H = 1024 + 16 * lane + i;
+        const float hf = (float)H;
+        float e = 0.f;
+        for (int k = 0; k < 4; ++k) {
+          const float t = hf * rf[k];
+          e = fmaxf(e, fabsf(t - rintf(t)));
+        }
+        e *= __builtin_amdgcn_rcpf(hf);
+        if (e < best) {
+          best = e;
+          bh = H;
+        }
+      }
+      float bw = best;
+      for (int o = 32; o >= 1; o >>= 1) bw = fminf(bw, __shfl_xor(bw, o));
+      int hw = best == bw ? bh : 2048;
+      for (int o = 32; o >= 1; o >>= 1) hw = min(hw, __shfl_xor(hw, o));
+      const int H = __builtin_amdgcn_readfirstlane(hw);
+      for (int k = 0; k < 4; ++k) hv[k] = (float)rint(H * r[k]);
+      beta = (float)(sp / H);
+    }
+  }
+  uint32_t lo = 0, hi = 0;
+  for (int k = 0; k < 4; ++k) {
+    const _Float16 h = (_Float16)hv[k];
+    uint16_t hb;
+    __builtin_memcpy(&hb, &h, 2);
+    lo |= (uint32_t)(hb & 0xFF) << (8 * k);
+    hi |= (uint32_t)(hb >> 8) << (8 * k);
+  }
+  out[0] = lo;
+  out[1] = hi;
+  out[2] = __float_as_uint(base);
+  out[3] = __float_as_uint(beta);
+}
+
 template <int D>
 __device__ __forceinline__ void qrot_body(const DecodeParams &p, const uint16_t *__restrict__ q,
                                           const float *__restrict__ Rk, int bh, int tid,
@@ -143,6 +210,13 @@ __device__ __forceinline__ void qrot_body(const DecodeParams &p, const uint16_t 
   const int nq = (p.g + 3) / 4;          // head quads (the last one partly empty if g < 4)
   const float sc = ldexpf(1.f, sh.qe);
   const int b = bh / p.Hq;
+  // the V grid of the codebook, once per KV head (its first q head in
+  // sequence 0)
+  if (p.codebook != nullptr && b == 0 && h_in == 0 && tid < 64) {
+    uint32_t words[4];
+    v_grid_words(p.codebook + (size_t)j2 * 8 + 4, tid, words);
+    if (tid < 4) reinterpret_cast<uint32_t *>(p.ws + p.L.vgrid)[(size_t)j2 * 4 + tid] = words[tid];
+  }
   if (p.n_shared > 0) {
     // the same pieces for the shared-page kernel, whose B operands hold one
     // q row per column: [b][h][piece][D], channel 16k + 4j + i at byte

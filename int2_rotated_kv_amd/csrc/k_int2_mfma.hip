@@ -209,8 +209,9 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   // vL0 = Lmin, the smallest of the four levels, Lmax the largest, so every
   // h[c] lies in [0, H]: 0 and H exactly at the extremes, the two others the
   // nearest integers; vbeta = (Lmax - Lmin) / H, with H in [1024, 2047]
-  // chosen over its 1024 values (16 per lane, a wave minimum) so that those
-  // two are closest.  Then |L[c] - vL0 - vbeta h[c]| stays far below the f16
+  // chosen over its 1024 values so that those two are closest (formed once
+  // per KV head with the q rotation and read from the workspace; see
+  // v_grid_words).  Then |L[c] - vL0 - vbeta h[c]| stays far below the f16
   // rounding of the levels themselves (typically ~1e-5 of Lmax - Lmin; below
   // ~3e-5 of it for any levels).  The h[c] are integers up to 2047, exact in
   // f16: each code's h is looked up by byte permutes from a table of the 4
@@ -223,59 +224,18 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   uint32_t vtab_lo = 0, vtab_hi = 0;                 // h[c] in f16: low, high bytes
   float vL0 = 0.f, vbeta = 1.f;                      // V levels = vL0 + vbeta * h[c]
   if constexpr (CB) {
-    const float *lk = p.codebook + j * 8, *lvv = lk + 4;
+    const float *lk = p.codebook + j * 8;
     kL0 = lk[0];
     kcA = 0.5f * (lk[2] - lk[0]);
     kcB = (lk[1] - lk[0]) - kcA;
     kcC = ((lk[3] - lk[2]) - lk[1]) + lk[0];
-    const double lv[4] = {lvv[0], lvv[1], lvv[2], lvv[3]};
-    const double lmin = fmin(fmin(lv[0], lv[1]), fmin(lv[2], lv[3]));
-    const double lmax = fmax(fmax(lv[0], lv[1]), fmax(lv[2], lv[3]));
-    const double sp = lmax - lmin;
-    float hv[4] = {(float)lv[0], (float)lv[1], (float)lv[2], (float)lv[3]};
-    if (isfinite(lv[0] + lv[1] + lv[2] + lv[3])) {   // uniform over the wave
-      vL0 = (float)lmin;
-      if (sp == 0.0) {
-        hv[0] = hv[1] = hv[2] = hv[3] = 0.f;
-      } else {
-        double r[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) r[k] = (lv[k] - lmin) / sp;   // in [0, 1]
-        double best = INFINITY;
-        int bh = 2047;
-        for (int i = 0; i < 16; ++i) {
-          const int H = 1024 + 16 * lane + i;
-          double e = 0.0;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) e = fmax(e, fabs(H * r[k] - rint(H * r[k])));
-          e /= H;
-          if (e < best) { best = e; bh = H; }
-        }
-        // the wave's smallest error, then the smallest H that reaches it
-        double bw = best;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) bw = fmin(bw, __shfl_xor(bw, o));
-        int hw = best == bw ? bh : 2048;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) hw = min(hw, __shfl_xor(hw, o));
-        const int H = __builtin_amdgcn_readfirstlane(hw);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) hv[k] = (float)rint(H * r[k]);
-        vbeta = (float)(sp / H);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const _Float16 h = (_Float16)hv[k];
-      uint16_t hb;
-      __builtin_memcpy(&hb, &h, 2);
-      vtab_lo |= (uint32_t)(hb & 0xFF) << (8 * k);
-      vtab_hi |= (uint32_t)(hb >> 8) << (8 * k);
-    }
-    vtab_lo = __builtin_amdgcn_readfirstlane(vtab_lo);
-    vtab_hi = __builtin_amdgcn_readfirstlane(vtab_hi);
-    vL0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vL0)));
-    vbeta = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vbeta)));
+    // the V grid of this KV head, formed with the q rotation (scalar loads)
+    using cu32 = const __attribute__((address_space(4))) uint32_t;
+    cu32 *vg = (cu32 *)(p.ws + p.L.vgrid) + j * 4;
+    vtab_lo = vg[0];
+    vtab_hi = vg[1];
+    vL0 = __uint_as_float(vg[2]);
+    vbeta = __uint_as_float(vg[3]);
   }
   // a symmetric K codebook (L3 - L2 = L1 - L0, as a Lloyd-Max fit of a
   // symmetric distribution gives) has no b0&b1 term: its QK plane is
