@@ -305,7 +305,8 @@ int check_args(const oscar_cache *c, const oscar_decode_args *a, DecodeParams *p
   const bool mf = p->int2_kind == OSCAR_INT2_MFMA;
   L.qpk = off;
   off = align256(off + (mf ? (size_t)a->batch * c->num_kv_heads * ((p->g + 3) / 4) *
-                                 mfma_a_planes(p->g, c->codebook != nullptr) * mfma_qk_steps(p->D, p->G) *
+                                 mfma_a_planes(p->D, p->G, p->g == 8 ? 8 : 4, c->codebook != nullptr) *
+                                 mfma_qk_steps(p->D, p->G) *
                                  64 * 4 * 4 : 0));
   L.qhd = off; off = align256(off + (mf ? BH * 8 * 4 : 0));
   L.vgrid = off; off = align256(off + (mf && c->codebook != nullptr ? (size_t)c->num_kv_heads * 16 : 0));

@@ -26,12 +26,17 @@ __host__ __device__ constexpr int mfma_waves(int d, int g, int gq, bool cb) {
   return ((d == 128 && g == 32 && (gq == 8 || cb)) || (cb && gq == 8 && (g == 32 || (d == 128 && g == 64))))
              ? 8 : 16;
 }
-// Query A operand sets per QK step of the matrix-core INT2 kernel: with a
-// codebook and one head quad (g <= 4 q heads per KV head) one per code plane
-// (the query pieces times the plane's weight, all planes contracted into one
-// accumulator); otherwise one (with two head quads the three sets would not
-// fit the register budget, and the planes keep separate accumulators)
-__host__ __device__ constexpr int mfma_a_planes(int g, bool cb) { return cb && g <= 4 ? 3 : 1; }
+// Query A operand sets per QK step of the matrix-core INT2 kernel (gq: its
+// q-head slots, 4 or 8): with a codebook one per code plane (the query
+// pieces times the plane's weight, all planes contracted into one
+// accumulator), except at D = 128 with 8 q heads per KV head and G = 32 or
+// 128, where the three sets would not fit the registers of the instance's
+// waves (G = 128 at 8 waves per block instead of 16 measured slower than
+// the unfolded planes) and the planes keep separate accumulators; without a
+// codebook one
+__host__ __device__ constexpr int mfma_a_planes(int d, int g, int gq, bool cb) {
+  return cb && !(d == 128 && gq == 8 && (g == 32 || g == 128)) ? 3 : 1;
+}
 // sequences the kernel balances its blocks across (one per thread of a block)
 __host__ __device__ constexpr int mfma_max_balanced(int waves) { return 64 * waves; }
 // KV heads per block of the matrix-core INT2 kernel: 2 (1 for a single KV

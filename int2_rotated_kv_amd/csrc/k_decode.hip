@@ -160,13 +160,12 @@ __device__ __forceinline__ void qrot_body(const DecodeParams &p, const uint16_t 
   // (their zero-point term) times sm_scale*log2(e).
   // With a codebook the K level of code c = b0 + 2*b1 is
   // L0 + cA*c + cB*b0 + cC*b0*b1 (cA = (L2 - L0)/2, cB = L1 - L0 - cA,
-  // cC = L3 - L2 - L1 + L0); with up to 4 q heads per KV head the kernel
-  // contracts the three planes c, b0, b0&b1 into one accumulator: plane pl
-  // gets the pieces of rint(fl(q * c_pl) * 2^qe), with
-  // |q| * max|c_pl| * 2^qe < 2^20 (with 8 it weights the planes itself).
+  // cC = L3 - L2 - L1 + L0); the kernel contracts the three planes c, b0,
+  // b0&b1 into one accumulator (mfma_a_planes): plane pl gets the pieces of
+  // rint(fl(q * c_pl) * 2^qe), with |q| * max|c_pl| * 2^qe < 2^20.
   __syncthreads();
   const int G = p.G, NG = D / G;
-  const int NPc = mfma_a_planes(p.g, p.codebook != nullptr);   // A operand sets
+  const int NPc = mfma_a_planes(D, G, p.g == 8 ? 8 : 4, p.codebook != nullptr);   // A operand sets
   float kc[3] = {1.f, 0.f, 0.f};
   if (NPc == 3) {
     const float *lk = p.codebook + (size_t)j * 8;

@@ -170,7 +170,7 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
 
   constexpr int NP = CB ? 3 : 1;       // QK code planes: the codes; with a codebook also b0, b0&b1
   constexpr bool kPermPlanes = CB;    // the b0 and b0&b1 planes looked up from the code bytes
-  constexpr int NPA = mfma_a_planes(GQ, CB);   // query A operand sets
+  constexpr int NPA = mfma_a_planes(D, G, GQ, CB);   // query A operand sets
   constexpr bool kSepAcc = NP > NPA;  // planes in accumulators of their own, weighted here
   __shared__ Int2Shared<D, G, GQ, HB> lds;
   const int lane = threadIdx.x & 63;
@@ -199,12 +199,12 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   //   L[c] = L0 + cA*c + cB*b0 + cC*b0*b1,
   //   cA = (L2 - L0)/2, cB = (L1 - L0) - cA, cC = L3 - L2 - L1 + L0,
   // so the int8 contraction runs on the codes (as without a codebook) and on
-  // the b0 and b0&b1 bit planes, and the L0 part joins the zero point.  With
-  // one head quad the planes go into one accumulator, the A operand of each
-  // holding the pieces of the query times the plane's weight (formed with
-  // the q rotation); with two (three A sets would not fit the registers)
-  // each plane has its own accumulator, weighted by cA, cB, cC here.  PV: the
-  // V levels are written as
+  // the b0 and b0&b1 bit planes, and the L0 part joins the zero point.  The
+  // planes go into one accumulator, the A operand of each holding the pieces
+  // of the query times the plane's weight (formed with the q rotation);
+  // where three A sets would not fit the registers (mfma_a_planes) each
+  // plane has its own accumulator, weighted by cA, cB, cC here.  PV: the V
+  // levels are written as
   //   L[c] = vL0 + vbeta * h[c],  h[c] = rint(H (L[c] - vL0) / (Lmax - vL0)),
   // vL0 = Lmin, the smallest of the four levels, Lmax the largest, so every
   // h[c] lies in [0, H]: 0 and H exactly at the extremes, the two others the
