@@ -322,6 +322,44 @@ def test_codebook_v_level_precision(D, G, g, order):
     _say(f"codebook V level precision: worst row rel err {worst:.3e}")
 
 
+K_LEVEL_SETS = {
+    "b0b1-dominant": (0.0, 0.1, 0.2, 3.0),      # cA = 0.1, cB = 0, cC = 2.7
+    "b0-dominant": (0.0, 2.5, 0.05, 2.6),       # cB = 2.475, cC = -2.35
+    "negative": (-1.5, -0.4, 0.45, 1.5),
+    "out-of-order": (2.2, 0.3, 2.9, 0.8),
+}
+
+
+@pytest.mark.parametrize("levels", sorted(K_LEVEL_SETS))
+@pytest.mark.parametrize("D,G,g", [(128, 64, 4), (128, 64, 8), (128, 128, 8), (64, 32, 8)])
+def test_codebook_k_plane_weights(D, G, g, levels):
+    """K codebooks whose plane weights cA = (L2 - L0)/2, cB = L1 - L0 - cA,
+    cC = L3 - L2 - L1 + L0 differ widely (one plane dominant, negative
+    levels, levels out of order), on instances where the matrix-core kernel
+    takes the three planes in one accumulator with the weights in the query
+    pieces (D128/G64 at 4 and 8 q heads per KV head, D64/G32 at 8) and one
+    where each plane has its own (D128/G128 at 8): outputs within half the
+    bar against the oracle (the f16 PV weights alone give up to ~4e-4 on
+    these inputs, whatever the K levels), bytes exact, status 0."""
+    from int2_rotated_kv_amd import binding as ob
+    _say(f"case: codebook K plane weights D{D} G{G} g{g} {levels}")
+    wl = synth.workload("tiny", B=3, Hkv=2, Hq=2 * g, D=D, G=G, lengths=(2100, 1700, 2600), steps=1,
+                        seed=113 + g + D // 64)
+    inp = synth.make_small(wl, distinct_rv=True)
+    cb = synth.make_codebook(wl.seed, wl.Hkv)
+    cb[0, 0] = np.asarray(K_LEVEL_SETS[levels], dtype=np.float32)
+    ref = sh.oracle_step(inp, steps=1, codebook=cb)
+    run = sh.build_and_step(inp, steps=1, int2_kernel=ob.INT2_MFMA, codebook=cb)
+    _check_bytes(run, inp, ref)
+    worst = 0.0
+    for b, r in ref.items():
+        e = sh.row_rel_err(run.out[b].astype(np.float64), r["out"])
+        worst = max(worst, float(e.max()))
+    assert worst <= TOL / 2, f"worst row rel err {worst:.3e}"
+    assert run.status == 0
+    _say(f"codebook K plane weights: worst row rel err {worst:.3e}")
+
+
 @pytest.mark.parametrize("codebook", [False, True])
 @pytest.mark.parametrize("D,G", [(64, 32), (64, 64), (128, 32), (128, 64), (128, 128)])
 def test_bulk_quantise_every_shape(D, G, codebook):
