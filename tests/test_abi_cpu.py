@@ -84,6 +84,31 @@ def test_workspace_bytes_valid():
     assert st2 == 0 and n2 > n or n2 >= n
 
 
+@pytest.mark.parametrize("hq,g_size,kernel,extra", [
+    # matrix-core kernel, 4 q heads per KV head: two more query piece sets
+    # (the code planes' weights) of 2 x 8 x 1 quad x 2 QK steps x 64 lanes x
+    # 16 bytes each, and the V grid (8 KV heads x 16 bytes, one 256-byte
+    # aligned partition)
+    (32, 64, 2, 2 * (2 * 8 * 1 * 2 * 64 * 16) + 256),
+    # 8 q heads per KV head at G = 64: the same with two head quads
+    (64, 64, 2, 2 * (2 * 8 * 2 * 2 * 64 * 16) + 256),
+    # 8 q heads per KV head at G = 128: one set (the planes keep their own
+    # accumulators), only the V grid
+    (64, 128, 2, 256),
+    # vector-ALU kernel: nothing more
+    (32, 64, 1, 0),
+])
+def test_workspace_grows_with_codebook(hq, g_size, kernel, extra):
+    """With a codebook the matrix-core kernel's workspace holds the query
+    pieces once per code plane where it folds the plane weights into them,
+    and each KV head's V grid; the planner adds exactly those bytes."""
+    a = _args(num_q_heads=hq, int2_kernel=kernel)
+    st0, n0 = _ws(_cache(group_size=g_size), a)
+    st1, n1 = _ws(_cache(group_size=g_size, codebook=0x80000), a)
+    assert st0 == ob.OSCAR_OK and st1 == ob.OSCAR_OK
+    assert n1 - n0 == extra
+
+
 @pytest.mark.parametrize("ckw,akw,want", [
     (dict(page_size=32), {}, ob.OSCAR_EINVAL),
     (dict(head_dim=96), {}, ob.OSCAR_EUNSUPPORTED),
