@@ -185,11 +185,13 @@ typedef struct {
                                 Lmin + beta * h[c], Lmin the smallest level,
                                 with integers 0 <= h[c] <= H, H in
                                 [1024, 2047] chosen for the closest fit
-                                (typically within 1e-5 of the level span;
-                                non-finite levels are taken in f16).  Level
-                                order and finiteness are not checked (device
-                                memory); the quantiser counts the level
-                                midpoints below a value, whatever the order */
+                                (typically within 1e-5 of the level span,
+                                4e-5 at the 99th percentile of random level
+                                sets; non-finite levels are taken in f16).
+                                Level order and finiteness are not checked
+                                (device memory); the quantiser counts the
+                                level midpoints below a value, whatever the
+                                order                                        */
   uint32_t *status;          /* device word (4-byte aligned) or NULL: sticky
                                 OSCAR_STATUS_* bits set by the demotion paths
                                 (the calls that write records); NULL = not
