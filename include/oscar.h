@@ -104,7 +104,7 @@ enum {
  * weights are p * scale_v * 2^(8-b) (p <= 4, 2^(8-b) <= 16), so every V group
  * scale must stay below OSCAR_MFMA_V_SCALE_LIMIT.  With a codebook the
  * weights are p * scale_v and the other operand is each V level written as
- * Lmin + beta * h with an integer 0 <= h <= 2047 (exact in f16); the check
+ * base + beta * h with an integer |h| <= 2048 (exact in f16); the check
  * keeps every
  * V group scale times c = max(1, largest |V level|) / 16 below the limit,
  * and every |V level| below 16 times it.  The demotion paths check this for
@@ -182,11 +182,11 @@ typedef struct {
                                 evaluated in fp32 in that order, is 0, as for
                                 levels symmetric about their middle) and PV
                                 on the V levels written per KV head as
-                                Lmin + beta * h[c], Lmin the smallest level,
-                                with integers 0 <= h[c] <= H, H in
-                                [1024, 2047] chosen for the closest fit
-                                (typically within 1e-5 of the level span,
-                                4e-5 at the 99th percentile of random level
+                                base + beta * h[c] with integers
+                                -2048 <= h[c] <= 2048, beta = span / H, H in
+                                [2048, 4095], chosen for the closest fit
+                                (typically within 2e-6 of the level span,
+                                1e-5 at the 99th percentile of random level
                                 sets; non-finite levels are taken in f16).
                                 Level order and finiteness are not checked
                                 (device memory); the quantiser counts the

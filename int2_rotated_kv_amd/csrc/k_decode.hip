@@ -32,16 +32,51 @@ struct QrotShared {
   int qe;
 };
 
+// Largest circular gap among the fractional parts f[0..3] (in [0, 1)) and
+// the point that follows it: the four lie on an arc of length 1 - gap that
+// starts at that point.
+template <typename T>
+__device__ inline void arc_of(const T f[4], T &gap, T &start) {
+  T a[4] = {f[0], f[1], f[2], f[3]};
+  // sorting network for 4 values
+  auto cs = [](T &x, T &y) {
+    const T lo = x < y ? x : y, hi = x < y ? y : x;
+    x = lo;
+    y = hi;
+  };
+  cs(a[0], a[1]);
+  cs(a[2], a[3]);
+  cs(a[0], a[2]);
+  cs(a[1], a[3]);
+  cs(a[1], a[2]);
+  gap = a[0] + T(1) - a[3];        // the wrap-around gap, then the inner ones
+  start = a[0];
+  for (int k = 0; k < 3; ++k) {
+    const T g = a[k + 1] - a[k];
+    if (g > gap) {
+      gap = g;
+      start = a[k + 1];
+    }
+  }
+}
+
 // The V grid of a Lloyd-Max codebook for the matrix-core kernel's PV, by one
-// wave (64 lanes, all active): the four V levels lv as Lmin + beta * h[c],
-// h[c] = rint(H (L[c] - Lmin) / (Lmax - Lmin)) in [0, H], beta =
-// (Lmax - Lmin) / H, with H in [1024, 2047] the one whose h lie closest to
-// those quotients: lane l compares H = 1024 + 16 l + i (i < 16) in fp32 on
-// max |H r - rint(H r)| / H, the wave keeps the smallest (the smallest H on
-// a tie), and the h of that H are formed in fp64.  Four equal levels give
-// h = 0; non-finite levels give h = the levels rounded to f16, Lmin = 0 and
-// beta = 1.  out: h[c] in f16 as two words (byte c of out[0] the low byte,
-// of out[1] the high byte), Lmin and beta as fp32 bits.
+// wave (64 lanes, all active): the four V levels lv as base + beta * h[c]
+// with integers -2048 <= h[c] <= 2048 (exact in f16).  With Lmin, Lmax the
+// smallest and largest level, r[c] = (L[c] - Lmin) / (Lmax - Lmin) and H in
+// [2048, 4095]: beta = (Lmax - Lmin) / H, base = Lmin + (2048 - phi) * beta
+// with phi in [0, 1) placing the four values H r[c] + phi as close to
+// integers as a common shift can (the centre of the shortest arc that holds
+// their fractional parts goes to an integer: error (1 - largest gap) / 2),
+// and H the one with the smallest error / H: lane l compares
+// H = 2048 + 32 l + i (i < 32) in fp32 on the two inner ratios (those of
+// the extremes are 0 and 1, fractional part 0), the wave keeps the smallest
+// (the smallest H on a tie).  The chosen grid is formed in fp64: phi, then
+// base and beta rounded to fp32 (as the kernel uses them), then
+// h[c] = rint((L[c] - base) / beta).  Four equal levels give h = 0 and
+// base = Lmin; non-finite levels give h = the levels rounded to f16,
+// base = 0 and beta = 1.  out: h[c] in f16 as two words (byte c of out[0]
+// the low byte, of out[1] the high byte), base and beta as fp32 bits.
 __device__ void v_grid_words(const float *lv4, int lane, uint32_t out[4]) {
   const double lv[4] = {lv4[0], lv4[1], lv4[2], lv4[3]};
   const double lmin = fmin(fmin(lv[0], lv[1]), fmin(lv[2], lv[3]));
@@ -55,22 +90,26 @@ __device__ void v_grid_words(const float *lv4, int lane, uint32_t out[4]) {
       hv[0] = hv[1] = hv[2] = hv[3] = 0.f;
     } else {
       double r[4];
-      float rf[4];
-      for (int k = 0; k < 4; ++k) {
-        r[k] = (lv[k] - lmin) / sp;   // in [0, 1]
-        rf[k] = (float)r[k];
-      }
-      float best = INFINITY;
-      int bh = 2047;
-      for (int i = 0; i < 16; ++i) {
-        const int H = 1024 + 16 * lane + i;
-        const float hf = (float)H;
-        float e = 0.f;
-        for (int k = 0; k < 4; ++k) {
-          const float t = hf * rf[k];
-          e = fmaxf(e, fabsf(t - rintf(t)));
+      for (int k = 0; k < 4; ++k) r[k] = (lv[k] - lmin) / sp;   // in [0, 1]
+      // the two inner ratios: the middle two of the sorted four
+      double s4[4] = {r[0], r[1], r[2], r[3]};
+      for (int a = 0; a < 3; ++a)
+        for (int b = 0; b < 3 - a; ++b) {
+          const double x = fmin(s4[b], s4[b + 1]), y = fmax(s4[b], s4[b + 1]);
+          s4[b] = x;
+          s4[b + 1] = y;
         }
-        e *= __builtin_amdgcn_rcpf(hf);
+      const float r1 = (float)s4[1], r2 = (float)s4[2];
+      float best = INFINITY;
+      int bh = 4095;
+      for (int i = 0; i < 32; ++i) {
+        const int H = 2048 + 32 * lane + i;
+        const float hf = (float)H;
+        const float t1 = hf * r1, t2 = hf * r2;
+        const float f1 = t1 - floorf(t1), f2 = t2 - floorf(t2);
+        const float lo = fminf(f1, f2), hi = fmaxf(f1, f2);
+        const float gap = fmaxf(fmaxf(lo, hi - lo), 1.f - hi);   // points 0, lo, hi
+        const float e = 0.5f * (1.f - gap) * __builtin_amdgcn_rcpf(hf);
         if (e < best) {
           best = e;
           bh = H;
@@ -78,11 +117,24 @@ __device__ void v_grid_words(const float *lv4, int lane, uint32_t out[4]) {
       }
       float bw = best;
       for (int o = 32; o >= 1; o >>= 1) bw = fminf(bw, __shfl_xor(bw, o));
-      int hw = best == bw ? bh : 2048;
+      int hw = best == bw ? bh : 4096;
       for (int o = 32; o >= 1; o >>= 1) hw = min(hw, __shfl_xor(hw, o));
       const int H = __builtin_amdgcn_readfirstlane(hw);
-      for (int k = 0; k < 4; ++k) hv[k] = (float)rint(H * r[k]);
+      double f[4];
+      for (int k = 0; k < 4; ++k) {
+        const double t = H * r[k];
+        f[k] = t - floor(t);
+      }
+      double gap, start;
+      arc_of(f, gap, start);
+      double phi = -(start + 0.5 * (1.0 - gap));   // the arc's centre onto an integer
+      phi -= floor(phi);
       beta = (float)(sp / H);
+      base = (float)(lmin + (2048.0 - phi) * (sp / H));
+      for (int k = 0; k < 4; ++k) {
+        const double h = rint((lv[k] - (double)base) / (double)beta);
+        hv[k] = (float)fmin(fmax(h, -2048.0), 2048.0);
+      }
     }
   }
   uint32_t lo = 0, hi = 0;

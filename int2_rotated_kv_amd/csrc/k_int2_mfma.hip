@@ -205,22 +205,22 @@ __global__ __launch_bounds__(64 * HB) void k_int2_mfma(DecodeParams p) {
   // where three A sets would not fit the registers (mfma_a_planes) each
   // plane has its own accumulator, weighted by cA, cB, cC here.  PV: the V
   // levels are written as
-  //   L[c] = vL0 + vbeta * h[c],  h[c] = rint(H (L[c] - vL0) / (Lmax - vL0)),
-  // vL0 = Lmin, the smallest of the four levels, Lmax the largest, so every
-  // h[c] lies in [0, H]: 0 and H exactly at the extremes, the two others the
-  // nearest integers; vbeta = (Lmax - Lmin) / H, with H in [1024, 2047]
-  // chosen over its 1024 values so that those two are closest (formed once
-  // per KV head with the q rotation and read from the workspace; see
-  // v_grid_words).  Then |L[c] - vL0 - vbeta h[c]| is typically ~1e-5 of
-  // Lmax - Lmin (over random level sets: median 8e-6, 99th percentile 4e-5,
-  // worst of 20000 sets 2.4e-4), where rounding the levels to f16 errs by up
-  // to 2^-11 of |L[c]|.  The h[c] are integers up to 2047, exact in
-  // f16: each code's h is looked up by byte permutes from a table of the 4
-  // (low bytes in one word, high bytes in another), PV runs once on them with
-  // the weights p * scale_v, and the vL0 part joins the zero point.  Four
-  // equal levels take h = 0 (exact); non-finite levels take h = the levels
-  // rounded to f16, vL0 = 0, vbeta = 1.  Without a codebook no plane is
-  // formed.
+  //   L[c] = vL0 + vbeta * h[c],  h[c] integers in [-2048, 2048] (exact in
+  // f16), vbeta = (Lmax - Lmin) / H with H in [2048, 4095] and vL0 = Lmin +
+  // (2048 - phi) * vbeta with phi in [0, 1), Lmin and Lmax the smallest and
+  // largest level: the common shift phi brings the four values
+  // H (L[c] - Lmin) / (Lmax - Lmin) + phi as close to integers as it can,
+  // and H is the one of its 2048 values with the smallest resulting error
+  // (formed once per KV head with the q rotation and read from the
+  // workspace; see v_grid_words).  Then |L[c] - vL0 - vbeta h[c]| is
+  // typically ~2e-6 of Lmax - Lmin (over random level sets: 99th percentile
+  // 1e-5, worst seen 6e-5), where rounding the levels to f16 errs by up to
+  // 2^-11 of |L[c]|.  Each code's h is looked up
+  // by byte permutes from a table of the 4 (low bytes in one word, high
+  // bytes in another), PV runs once on them with the weights p * scale_v,
+  // and the vL0 part joins the zero point.  Four equal levels take h = 0
+  // (exact); non-finite levels take h = the levels rounded to f16, vL0 = 0,
+  // vbeta = 1.  Without a codebook no plane is formed.
   float kcA = 1.f, kcB = 0.f, kcC = 0.f, kL0 = 0.f;   // K levels
   uint32_t vtab_lo = 0, vtab_hi = 0;                 // h[c] in f16: low, high bytes
   float vL0 = 0.f, vbeta = 1.f;                      // V levels = vL0 + vbeta * h[c]
